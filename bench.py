@@ -1,0 +1,203 @@
+"""Throughput of the gen-tower denoise step on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
+
+Workload: the 36-layer Qwen3-8B-shaped gen tower at 2048x2048 (4096 image tokens per
+branch), CFG batch 2 (cond + uncond, each with its own 400-token prefix-KV cache per layer),
+cfg 4.0, shifted flow Euler update (shift 3.0, t_eps 0.02), step 0 of the 50-step schedule.
+One timed step = one gen_tower_step call: patch embed + 36 gen blocks over both branches +
+final norm + out head + CFG/Euler.  Inputs are synthetic (seeded device RNG, the weight and
+activation distributions of the test workloads) and resident in HBM before timing starts.
+
+Prints ONE JSON line with image tokens/s (both branches), the fraction of the bf16 MFMA peak,
+a roofline entry for the dominant kernel (the fused gate/up + SwiGLU GEMM, its launches timed
+with HIP events on the library's stream inside the timed region) and the CPU oracle's rate on
+a bounded sample (one full-size gen block, scaled to the 36-layer step).
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import platform
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2516.6     # MI355X dense bf16 MFMA: 256 CU x 2.4 GHz x 4096 FLOP/clk
+PEAK_HBM_GBS = 8000.0
+
+
+def step_flops(w) -> dict:
+    """Algorithmic FLOPs of one gen_tower_step (2 per multiply-add), by component."""
+    d = w.dims
+    B, N, P, D = w.batch, w.n_tokens, w.prefix_len, d.hidden
+    M = B * N
+    QD, KV = d.n_q_heads * d.head_dim, d.n_kv_heads * d.head_dim
+    L = P + N
+    f = {}
+    f["qkv"] = 2 * M * D * (QD + 2 * KV)
+    f["attention"] = 4 * B * d.n_q_heads * N * L * d.head_dim
+    f["o"] = 2 * M * QD * D
+    if d.is_moe:
+        f["router"] = 2 * M * D * d.n_experts
+        f["experts"] = 2 * M * d.top_k * 3 * D * d.expert_intermediate
+    else:
+        f["gate_up"] = 2 * M * D * 2 * d.mlp_intermediate
+        f["down"] = 2 * M * d.mlp_intermediate * D
+    if d.lora_rank:
+        ins = (D, D, D, QD, D, D, d.mlp_intermediate)
+        outs = (QD, KV, KV, D, d.mlp_intermediate, d.mlp_intermediate, D)
+        f["lora"] = sum(2 * M * d.lora_rank * (i + o) for i, o in zip(ins, outs))
+    per_layer = sum(f.values())
+    out = {k: v * w.n_layers for k, v in f.items()}
+    out["embed"] = 2 * w.n_img * N * 3072 * D
+    out["head"] = 2 * M * D * 3072
+    out["total"] = per_layer * w.n_layers + out["embed"] + out["head"]
+    return out
+
+
+def make_device_tower(psf, w, seed=0):
+    """Random-init tower weights and prefixes on the GPU (torch's seeded device RNG)."""
+    import torch
+    d = w.dims
+    g = torch.Generator(device="cuda")
+    g.manual_seed(seed)
+    bf = torch.bfloat16
+
+    def randn(*shape, std=1.0, mean=0.0):
+        t = torch.empty(*shape, device="cuda", dtype=torch.float32)
+        t.normal_(mean, std, generator=g)
+        return t.to(bf)
+
+    D, I = d.hidden, d.mlp_intermediate
+    QKV = (d.n_q_heads + 2 * d.n_kv_heads) * d.head_dim
+    layers_dev = []
+    for _ in range(w.n_layers):
+        lw = {"g_in": randn(D, std=0.1, mean=1.0), "w_qkv": randn(QKV, D, std=0.02),
+              "g_q": randn(d.head_dim, std=0.1, mean=1.0), "g_k": randn(d.head_dim, std=0.1, mean=1.0),
+              "w_o": randn(D, d.n_q_heads * d.head_dim, std=0.02), "g_post": randn(D, std=0.1, mean=1.0),
+              "w_gate_up": randn(2 * I, D, std=0.02), "w_down": randn(D, I, std=0.02)}
+        layers_dev.append(lw)
+    glob = {"w_in": randn(D, 3072, std=0.02), "temb_w1": randn(D, 256, std=0.02), "temb_w2": randn(D, D, std=0.02),
+            "g_final": randn(D, std=0.1, mean=1.0), "w_out": randn(3072, D, std=0.02)}
+    shp = (w.prefix_len, d.n_kv_heads, d.head_dim)
+    pk = [randn(*shp) for _ in range(w.n_layers * w.batch)]
+    pv = [randn(*shp) for _ in range(w.n_layers * w.batch)]
+    x = torch.empty(w.n_img, 3, w.height, w.width, device="cuda")
+    x.normal_(0.0, 1.0, generator=g)
+    return layers_dev, glob, pk, pv, x
+
+
+def cpu_baseline(w, seed=0):
+    """The oracle (numpy fp32, as it stands) on one full-size gen block of the workload (both
+    branches, all tokens), scaled to the 36-layer step; the patch embed and head are < 0.3 %
+    of the work and are not in the sample."""
+    import numpy as np
+    import oracle as O
+    import workloads as W
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max((p.get("num_threads", 1) for p in threadpool_info() if p.get("user_api") == "blas"), default=1)
+    except Exception:
+        threads = os.cpu_count() or 1
+    wts = W.layer_weights(w, 0, seed, "bf16")
+    h = W.block_hidden(w, seed, "bf16")
+    pk, pv = zip(*[W.prefix_kv(w, 0, s, seed, "bf16") for s in range(w.batch)])
+    t0 = time.perf_counter()
+    O.gen_block(h, wts, w.dims, list(pk), list(pv))
+    dt = time.perf_counter() - t0
+    step_s = dt * w.n_layers
+    return {"value": w.batch * w.n_tokens / step_s, "unit": "image tokens/s", "cores": int(threads),
+            "kind": "oracle",
+            "sample": (f"one gen block of the workload (2 branches x {w.n_tokens} tokens, prefix {w.prefix_len}) "
+                       f"in numpy fp32 took {dt:.2f} s; scaled x{w.n_layers} layers"),
+            "host": platform.processor() or platform.machine(), "numpy": np.__version__}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--config", type=int, default=2)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU: this build has no multi-GPU path (asked for --gpus {args.gpus}). "
+              "See the sharding notes in DESIGN.md.", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import pixel_space_flow_amd as psf
+    import workloads as W
+
+    w = W.CONFIGS[args.config]
+    assert w.unit == "tower" and not w.dims.is_moe and not w.dims.lora_rank, "bench times the dense CFG tower step"
+    torch.cuda.set_device(0)
+    dims = psf.make_dims(w.dims, psf.GEN_BF16)
+    layers_dev, glob, pk, pv, x = make_device_tower(psf, w)
+    layers = [psf.make_weights(l) for l in layers_dev]
+    ws = psf.alloc_workspace(psf.workspace_size(dims, w.n_img, w.n_br, w.n_tokens, w.prefix_len))
+    xo = torch.empty_like(x)
+    sched = psf.sigma_schedule(w.n_steps, w.shift)
+    plen = [w.prefix_len] * w.batch
+
+    def step():
+        psf.tower_step(dims, layers, glob, x, w.n_br, [sched[0]], [sched[1]], w.cfg_scale, w.t_eps, pk, pv, plen,
+                       xo, ws)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    psf.timing_begin("gate_up", w.n_layers * args.steps)
+    start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    start.record()
+    for _ in range(args.steps):
+        step()
+    stop.record()
+    torch.cuda.synchronize()
+    total_ms = start.elapsed_time(stop)
+    gu_ms, gu_n = psf.timing_end()
+    ms = total_ms / args.steps
+    fl = step_flops(w)
+    tokens = w.batch * w.n_tokens
+    tflops = fl["total"] / (ms * 1e-3) / 1e12
+    d = w.dims
+    gu_flops = 2 * tokens * d.hidden * 2 * d.mlp_intermediate
+    gu_avg_ms = gu_ms / max(gu_n, 1)
+    gu_tflops = gu_flops / (gu_avg_ms * 1e-3) / 1e12
+    props = torch.cuda.get_device_properties(0)
+    out = {
+        "metric": "gen-tower image tokens/s per denoise step at 2048^2 CFG; % bf16 MFMA peak",
+        "value": round(tokens / (ms * 1e-3), 1),
+        "unit": "image tokens/s",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(ms, 3),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": w.name, "layers": w.n_layers, "image_px": [w.height, w.width],
+                   "image_tokens_per_branch": w.n_tokens, "cfg_branches": w.n_br, "prefix_tokens": w.prefix_len,
+                   "hidden": d.hidden, "heads": [d.n_q_heads, d.n_kv_heads, d.head_dim],
+                   "mlp_intermediate": d.mlp_intermediate, "cfg_scale": w.cfg_scale, "shift": w.shift,
+                   "t_eps": w.t_eps, "schedule_step": "0 of 50", "global_batch": w.batch, "seq_len": w.n_tokens},
+        "pct_bf16_peak": round(100 * tflops / PEAK_BF16_TFLOPS, 2),
+        "tflops": round(tflops, 1),
+        "step_tflop": round(fl["total"] / 1e12, 3),
+        "image_tokens_per_s_per_output_image": round(w.n_tokens / (ms * 1e-3), 1),
+        "roofline": {"kernel": "gate_up SwiGLU GEMM (M=8192, N=2x12288, K=4096)", "bound": "mfma",
+                     "achieved": round(gu_tflops, 1), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(gu_tflops / PEAK_BF16_TFLOPS, 4), "traffic": None,
+                     "avg_launch_ms": round(gu_avg_ms, 4), "launches_timed": gu_n},
+        "device": {"name": props.name, "cus": props.multi_processor_count},
+    }
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(W.scaled(w, n_layers=w.n_layers))
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

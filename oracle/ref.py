@@ -13,7 +13,7 @@ import numpy as np
 __all__ = [
     "shift_sigma", "sigma_schedule", "rms_norm", "rope_cos_sin", "apply_rope", "attention",
     "silu", "swiglu", "lora_delta", "linear", "route_topk", "moe_mlp", "gen_block",
-    "patchify", "unpatchify", "timestep_features", "timestep_embed", "tower_x0",
+    "patchify", "unpatchify", "timestep_features", "timestep_embed", "tower_tokens", "tower_x0",
     "cfg_mix", "euler_step", "tower_step", "noisy_sample",
 ]
 
@@ -271,25 +271,37 @@ def timestep_embed(sigma: float, w1: np.ndarray, w2: np.ndarray) -> np.ndarray:
     return linear(silu(linear(feat[None], w1)), w2)[0]
 
 
-def tower_x0(x_t: np.ndarray, sigma: Sequence[float], glob: Dict[str, np.ndarray], layer_weights,
-             dims, n_layers: int, n_br: int, prefix_k, prefix_v, dtype=np.float32) -> np.ndarray:
-    """Gen tower forward: x0 prediction for every (image, branch).
+def tower_tokens(x_t: np.ndarray, sigma: Sequence[float], glob: Dict[str, np.ndarray], layer_weights,
+                 dims, n_layers: int, n_br: int, prefix_k, prefix_v, dtype=np.float32,
+                 rows: Optional[np.ndarray] = None) -> np.ndarray:
+    """Gen tower forward: x0 prediction of every (image, branch) as patch tokens.
 
     x_t [n_img, 3, H, W]; sigma[i] per image; ``layer_weights(l)`` returns layer
     l's tensors; prefix_k[l][s], prefix_v[l][s] for sample s = i*n_br + br.
       h0 = patchify(x_t) W_in^T + temb(sigma)   (shared by both branches)
       h  = gen_block^L(h0 per branch)
-      x0 = unpatchify(RMSNorm(h; g_final) W_out^T)
+      y  = RMSNorm(h; g_final) W_out^T           (x0 = unpatchify(y))
     Reading: the tower predicts clean pixels x0 ([lilting] default.yaml: x0
-    loss), also at inference.  Returns [n_img*n_br, 3, H, W]."""
-    n_img, _, H, W = x_t.shape
+    loss), also at inference.  ``rows`` restricts the last block and the head
+    to those token indices.  Returns [n_img*n_br, len(rows) or N, 3*32*32]."""
+    n_img = x_t.shape[0]
     tok = patchify(x_t.astype(dtype))
     h0 = np.stack([linear(tok[i], glob["w_in"]) + timestep_embed(sigma[i], glob["temb_w1"], glob["temb_w2"])
                    for i in range(n_img)])
     h = np.repeat(h0, n_br, axis=0)
+    if n_layers == 0 and rows is not None:
+        h = h[:, rows]
     for l in range(n_layers):
-        h = gen_block(h, layer_weights(l), dims, prefix_k[l], prefix_v[l])
-    y = linear(rms_norm(h, glob["g_final"], dims.rms_eps), glob["w_out"])
+        last = l == n_layers - 1
+        h = gen_block(h, layer_weights(l), dims, prefix_k[l], prefix_v[l], rows=rows if last else None)
+    return linear(rms_norm(h, glob["g_final"], dims.rms_eps), glob["w_out"])
+
+
+def tower_x0(x_t: np.ndarray, sigma: Sequence[float], glob: Dict[str, np.ndarray], layer_weights,
+             dims, n_layers: int, n_br: int, prefix_k, prefix_v, dtype=np.float32) -> np.ndarray:
+    """x0 prediction in pixels: unpatchify of ``tower_tokens``; [n_img*n_br, 3, H, W]."""
+    H, W = x_t.shape[2], x_t.shape[3]
+    y = tower_tokens(x_t, sigma, glob, layer_weights, dims, n_layers, n_br, prefix_k, prefix_v, dtype)
     return unpatchify(y, H, W)
 
 

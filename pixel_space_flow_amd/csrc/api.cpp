@@ -1,0 +1,714 @@
+// C ABI of the gen-tower denoise step: argument validation (host only, before any HIP
+// call), workspace layout, and the launch sequence of a gen block and a tower step.
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <string>
+
+#include "../../include/psf_gen.h"
+#include "gemm.h"
+#include "kernels.h"
+
+using namespace psf;
+
+namespace {
+
+thread_local std::string g_err;
+
+int fail(int code, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_err = buf;
+  return code;
+}
+int ok() {
+  g_err.clear();
+  return GEN_OK;
+}
+
+#define HIP_TRY(expr)                                                                       \
+  do {                                                                                      \
+    hipError_t e_ = (expr);                                                                 \
+    if (e_ != hipSuccess) return fail(GEN_EHIP, "%s: %s", #expr, hipGetErrorString(e_));   \
+  } while (0)
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15) == 0; }
+
+// ------------------------------------------------------------------ launch timing (measurement only)
+enum { FAM_GATE_UP = 0, FAM_ATTN = 1, FAM_QKV = 2, FAM_DOWN = 3, FAM_O = 4, FAM_EXPERT = 5 };
+struct Timing {
+  int family = -1, cap = 0, used = 0;
+  hipEvent_t* ev = nullptr;
+} g_timing;
+
+// Runs `launch` bracketed by event records when its family is being timed.
+template <typename F>
+hipError_t timed(int family, hipStream_t s, F&& launch) {
+  const bool on = g_timing.family == family && g_timing.used < g_timing.cap;
+  if (on) {
+    hipError_t e = hipEventRecord(g_timing.ev[2 * g_timing.used], s);
+    if (e != hipSuccess) return e;
+  }
+  hipError_t e = launch();
+  if (e != hipSuccess) return e;
+  if (on) {
+    e = hipEventRecord(g_timing.ev[2 * g_timing.used + 1], s);
+    ++g_timing.used;
+  }
+  return e;
+}
+
+// ------------------------------------------------------------------ validation
+int check_dims(const gen_block_dims* d) {
+  if (!d) return fail(GEN_EINVAL, "dims is NULL");
+  if (d->dtype != GEN_F32 && d->dtype != GEN_BF16) return fail(GEN_EINVAL, "dtype %d is not GEN_F32/GEN_BF16", d->dtype);
+  if (d->hidden_dtype != GEN_F32 && d->hidden_dtype != GEN_BF16)
+    return fail(GEN_EINVAL, "hidden_dtype %d is not GEN_F32/GEN_BF16", d->hidden_dtype);
+  if (d->dtype == GEN_F32 && d->hidden_dtype != GEN_F32) return fail(GEN_EUNSUPPORTED, "fp32 weights need an fp32 hidden_dtype");
+  if (d->hidden <= 0 || d->hidden % 64) return fail(GEN_EINVAL, "hidden %d must be a positive multiple of 64", d->hidden);
+  if (d->hidden > 8192) return fail(GEN_EUNSUPPORTED, "hidden %d > 8192", d->hidden);
+  if (d->head_dim != 64 && d->head_dim != 128) return fail(GEN_EINVAL, "head_dim %d must be 64 or 128", d->head_dim);
+  if (d->n_q_heads <= 0 || d->n_kv_heads <= 0 || d->n_q_heads % d->n_kv_heads)
+    return fail(GEN_EINVAL, "n_q_heads %d must be a positive multiple of n_kv_heads %d", d->n_q_heads, d->n_kv_heads);
+  if (!(d->rms_eps >= 0.f) || !std::isfinite(d->rms_eps)) return fail(GEN_EINVAL, "rms_eps must be finite and >= 0");
+  if (!(d->rope_theta > 0.f) || !std::isfinite(d->rope_theta)) return fail(GEN_EINVAL, "rope_theta must be finite and > 0");
+  const bool dense = d->mlp_intermediate > 0, moe = d->n_experts > 0;
+  if (dense == moe) return fail(GEN_EINVAL, "exactly one of mlp_intermediate and n_experts must be > 0");
+  if (dense && d->mlp_intermediate % 64) return fail(GEN_EINVAL, "mlp_intermediate %d must be a multiple of 64", d->mlp_intermediate);
+  if (moe) {
+    if (d->n_experts > 64) return fail(GEN_EUNSUPPORTED, "n_experts %d > 64", d->n_experts);
+    if (d->top_k < 1 || d->top_k > d->n_experts) return fail(GEN_EINVAL, "top_k %d not in [1, n_experts]", d->top_k);
+    if (d->expert_intermediate <= 0 || d->expert_intermediate % 64)
+      return fail(GEN_EINVAL, "expert_intermediate %d must be a positive multiple of 64", d->expert_intermediate);
+    if (d->dtype != GEN_BF16) return fail(GEN_EUNSUPPORTED, "expert MLP runs in bf16 only");
+    if (d->hidden > 4096) return fail(GEN_EUNSUPPORTED, "router supports hidden <= 4096");
+  }
+  if (d->lora_rank < 0) return fail(GEN_EINVAL, "lora_rank %d < 0", d->lora_rank);
+  if (d->lora_rank > 0) {
+    if (d->lora_rank % 8 || d->lora_rank > 128) return fail(GEN_EUNSUPPORTED, "lora_rank %d must be a multiple of 8, <= 128", d->lora_rank);
+    if (moe) return fail(GEN_EUNSUPPORTED, "LoRA is supported on dense blocks only");
+    if (d->dtype != GEN_BF16) return fail(GEN_EUNSUPPORTED, "LoRA runs in bf16 only");
+    if (!std::isfinite(d->lora_alpha)) return fail(GEN_EINVAL, "lora_alpha must be finite");
+  }
+  return GEN_OK;
+}
+
+int check_weights(const gen_block_dims* d, const gen_block_weights* w, int layer) {
+  if (!w) return fail(GEN_EINVAL, "weights of layer %d are NULL", layer);
+  const void* req[] = {w->g_in, w->w_qkv, w->g_q, w->g_k, w->w_o, w->g_post};
+  const char* names[] = {"g_in", "w_qkv", "g_q", "g_k", "w_o", "g_post"};
+  for (int i = 0; i < 6; ++i) {
+    if (!req[i]) return fail(GEN_EINVAL, "layer %d: %s is NULL", layer, names[i]);
+    if (!aligned16(req[i])) return fail(GEN_EINVAL, "layer %d: %s is not 16-byte aligned", layer, names[i]);
+  }
+  if (d->mlp_intermediate > 0) {
+    if (!w->w_gate_up || !w->w_down) return fail(GEN_EINVAL, "layer %d: w_gate_up/w_down is NULL", layer);
+    if (!aligned16(w->w_gate_up) || !aligned16(w->w_down)) return fail(GEN_EINVAL, "layer %d: MLP weights not 16-byte aligned", layer);
+  } else {
+    if (!w->w_router || !w->w_exp_gate_up || !w->w_exp_down) return fail(GEN_EINVAL, "layer %d: expert weights are NULL", layer);
+    if (!aligned16(w->w_exp_gate_up) || !aligned16(w->w_exp_down)) return fail(GEN_EINVAL, "layer %d: expert weights not 16-byte aligned", layer);
+  }
+  if (d->lora_rank > 0) {
+    for (int s = 0; s < 7; ++s) {
+      if ((w->lora_a[s] == nullptr) != (w->lora_b[s] == nullptr))
+        return fail(GEN_EINVAL, "layer %d: LoRA site %d has only one of lora_a/lora_b", layer, s);
+      if ((w->lora_a[s] && !aligned16(w->lora_a[s])) || (w->lora_b[s] && !aligned16(w->lora_b[s])))
+        return fail(GEN_EINVAL, "layer %d: LoRA site %d not 16-byte aligned", layer, s);
+    }
+  }
+  return GEN_OK;
+}
+
+int check_prefix(const gen_block_dims* d, int B, const void* const* pk, const void* const* pv, const int* plen,
+                 int* max_prefix) {
+  if (!plen) return fail(GEN_EINVAL, "prefix_len is NULL");
+  int mx = 0;
+  for (int b = 0; b < B; ++b) {
+    if (plen[b] < 0) return fail(GEN_EINVAL, "prefix_len[%d] = %d < 0", b, plen[b]);
+    mx = std::max(mx, plen[b]);
+  }
+  if (mx > 0 && (!pk || !pv)) return fail(GEN_EINVAL, "prefix_k/prefix_v arrays are NULL");
+  (void)d;
+  *max_prefix = mx;
+  return GEN_OK;
+}
+
+// ------------------------------------------------------------------ workspace
+constexpr size_t ALIGN = 256;
+size_t up(size_t x) { return (x + ALIGN - 1) / ALIGN * ALIGN; }
+
+struct Ws {
+  size_t hidden, patches, u, qkv, attn, kc, vt, z, rope, temb, h1, x0, lora_t, hmid;
+  size_t m_idx, m_w, m_counts, m_offsets, m_perm, m_pos, m_tiles, m_z, m_y;
+  size_t total;
+  int Lpad, max_tiles, n_pos;
+};
+
+Ws layout(const gen_block_dims& d, int n_img, int n_br, int N, int max_prefix) {
+  Ws w{};
+  const size_t es = d.dtype == GEN_BF16 ? 2 : 4;
+  const size_t B = (size_t)n_img * n_br, M = B * N, D = d.hidden;
+  const size_t qkv = (size_t)(d.n_q_heads + 2 * d.n_kv_heads) * d.head_dim;
+  w.Lpad = (int)((max_prefix + N + 63) / 64 * 64);
+  w.n_pos = max_prefix + N;
+  size_t o = 0;
+  auto take = [&](size_t bytes) { size_t at = o; o += up(bytes); return at; };
+  w.hidden = take(M * D * 4);   // tower residual stream (fp32)
+  w.patches = take((size_t)n_img * N * 3072 * es);
+  w.u = take(M * D * es);
+  w.hmid = take(M * D * 4);   // fp32 residual between attention and MLP
+  w.qkv = take(M * qkv * es);
+  w.attn = take(M * d.n_q_heads * d.head_dim * es);
+  w.kc = take(B * d.n_kv_heads * w.Lpad * d.head_dim * es);
+  w.vt = take(B * d.n_kv_heads * w.Lpad * d.head_dim * es);
+  w.z = take(d.mlp_intermediate > 0 ? M * d.mlp_intermediate * es : 0);
+  w.rope = take((size_t)w.n_pos * (d.head_dim / 2) * sizeof(float) * 2);
+  w.temb = take((size_t)n_img * D * 4);
+  w.h1 = take((size_t)n_img * D * 4);
+  w.x0 = take(B * 3 * (size_t)N * 1024 * 4);
+  w.lora_t = take(d.lora_rank > 0 ? M * 3 * d.lora_rank * es : 0);
+  if (d.n_experts > 0) {
+    const size_t A = M * d.top_k;
+    w.max_tiles = (int)(A / 256 + d.n_experts + 1);
+    w.m_idx = take(A * 4);
+    w.m_w = take(A * 4);
+    w.m_counts = take(d.n_experts * 4);
+    w.m_offsets = take((d.n_experts + 1) * 4);
+    w.m_perm = take(A * 4);
+    w.m_pos = take(A * 4);
+    w.m_tiles = take((size_t)w.max_tiles * 3 * 4);
+    w.m_z = take(A * d.expert_intermediate * es);
+    w.m_y = take(A * D * es);
+  }
+  w.total = o;
+  return w;
+}
+
+template <typename T> T* at(void* ws, size_t off) { return reinterpret_cast<T*>(static_cast<char*>(ws) + off); }
+
+GemmParams gp() {
+  GemmParams p;
+  std::memset(&p, 0, sizeof p);
+  p.scale = 1.f;
+  return p;
+}
+
+// ------------------------------------------------------------------ one gen block
+template <typename T>
+hipError_t gemm_any(const GemmParams& p, int epi, hipStream_t s) {
+  if (sizeof(T) == 2) return gemm_bf16(p, epi, s);
+  return gemm_f32(p, epi, s);
+}
+
+// LoRA down-projection of the sites listed: t[:, slot*r:(slot+1)*r] = (alpha/r) x A_site^T.
+// Returns the number of sites present; fills per-site column offsets (-1 if absent).
+template <typename T>
+hipError_t lora_down(const gen_block_dims& d, const gen_block_weights& w, const int* sites, int ns, const T* x, int K,
+                     int M, T* t, int* off, int& ldt, hipStream_t s) {
+  GemmParams p = gp();
+  int n = 0;
+  for (int i = 0; i < ns; ++i) {
+    off[i] = -1;
+    if (w.lora_a[sites[i]]) { p.Bs[n] = w.lora_a[sites[i]]; off[i] = n * d.lora_rank; ++n; }
+  }
+  ldt = std::max(n, 1) * d.lora_rank;
+  if (n == 0) return hipSuccess;
+  p.A = x; p.lda = K; p.B = p.Bs[0]; p.ldb = K;
+  p.M = M; p.N = n * d.lora_rank; p.K = K;
+  p.bmode = 2; p.seg_rows = d.lora_rank;
+  p.C = t; p.ldc = ldt; p.scale = d.lora_alpha / (float)d.lora_rank;
+  return gemm_bf16(p, EPI_SCALED, s);
+}
+
+// Attach the LoRA up-projection of the given sites as a K extension of p.
+void lora_ext(GemmParams& p, const gen_block_dims& d, const gen_block_weights& w, const int* sites, int ns,
+              const int* site_end, const void* t, int ldt, const int* off) {
+  p.X = t; p.ldx = ldt; p.xk = ldt; p.xr = d.lora_rank;
+  for (int i = 0; i < 3; ++i) {
+    const int si = std::min(i, ns - 1);
+    p.XB[i] = (i < ns && off[i] >= 0) ? w.lora_b[sites[i]] : nullptr;
+    p.xsite_end[i] = site_end[si];
+    p.xoff[i] = (i < ns && off[i] >= 0) ? off[i] : 0;
+  }
+}
+
+// T: operand dtype (weights, GEMM/attention inputs); TH: residual-stream dtype of `hidden`.
+// With an fp32 residual the O and down projections accumulate into `hidden` in place; with a
+// bf16 residual the mid-block residual lives in the fp32 buffer hmid and `hidden` is rounded
+// once, at the block output.
+template <typename T, typename TH>
+int run_block(const gen_block_dims& d, const gen_block_weights& w, TH* hidden, const SeqInfo& si, void* ws,
+              const Ws& L, int32_t* topk_out, hipStream_t s) {
+  constexpr bool f32res = sizeof(TH) == 4;
+  const int B = si.B, N = si.N, M = B * N, D = d.hidden;
+  const int Hq = d.n_q_heads, Hkv = d.n_kv_heads, hd = d.head_dim;
+  const int QKV = (Hq + 2 * Hkv) * hd, QD = Hq * hd;
+  const bool lora = d.lora_rank > 0;
+  T* u = at<T>(ws, L.u);
+  T* qkv = at<T>(ws, L.qkv);
+  T* attn = at<T>(ws, L.attn);
+  T* Kc = at<T>(ws, L.kc);
+  T* Vt = at<T>(ws, L.vt);
+  T* lt = at<T>(ws, L.lora_t);
+  const float2* rope = at<float2>(ws, L.rope);
+
+  float* hmid = f32res ? (float*)hidden : at<float>(ws, L.hmid);
+  HIP_TRY((rmsnorm<TH, T>(hidden, (const T*)w.g_in, u, M, D, d.rms_eps, s)));
+  {
+    GemmParams p = gp();
+    p.A = u; p.lda = D; p.B = w.w_qkv; p.ldb = D; p.M = M; p.N = QKV; p.K = D;
+    p.C = qkv; p.ldc = QKV;
+    if (lora) {
+      const int sites[3] = {0, 1, 2}, ends[3] = {QD, QD + Hkv * hd, QKV};
+      int off[3], ldt;
+      HIP_TRY(lora_down<T>(d, w, sites, 3, u, D, M, lt, off, ldt, s));
+      if (off[0] >= 0 || off[1] >= 0 || off[2] >= 0) lora_ext(p, d, w, sites, 3, ends, lt, ldt, off);
+    }
+    HIP_TRY(timed(FAM_QKV, s, [&] { return gemm_any<T>(p, EPI_STORE, s); }));
+  }
+  HIP_TRY(qknorm_rope<T>(qkv, QKV, si, Hq, Hkv, hd, (const T*)w.g_q, (const T*)w.g_k, rope, d.rms_eps, s));
+  HIP_TRY(pack_kv<T>(qkv, QKV, si, Hq, Hkv, hd, L.Lpad, Kc, Vt, s));
+  HIP_TRY(timed(FAM_ATTN, s, [&] {
+    if (sizeof(T) == 2)
+      return attention_bf16((const bf16*)qkv, QKV, si, Hq, Hkv, hd, L.Lpad, (const bf16*)Kc, (const bf16*)Vt, (bf16*)attn, QD, s);
+    return attention_f32((const float*)qkv, QKV, si, Hq, Hkv, hd, L.Lpad, (const float*)Kc, (const float*)Vt, (float*)attn, QD, s);
+  }));
+  {
+    GemmParams p = gp();
+    p.A = attn; p.lda = QD; p.B = w.w_o; p.ldb = QD; p.M = M; p.N = D; p.K = QD;
+    p.C = hmid; p.ldc = D; p.R = hidden; p.ldr = D;
+    if (lora) {
+      const int sites[1] = {3}, ends[1] = {D};
+      int off[1], ldt;
+      HIP_TRY(lora_down<T>(d, w, sites, 1, attn, QD, M, lt, off, ldt, s));
+      if (off[0] >= 0) lora_ext(p, d, w, sites, 1, ends, lt, ldt, off);
+    }
+    HIP_TRY(timed(FAM_O, s, [&] { return gemm_any<T>(p, f32res ? EPI_RESID_F32 : EPI_RESID_TO_F32, s); }));
+  }
+  HIP_TRY((rmsnorm<float, T>(hmid, (const T*)w.g_post, u, M, D, d.rms_eps, s)));
+  if (d.mlp_intermediate > 0) {
+    const int I = d.mlp_intermediate;
+    T* z = at<T>(ws, L.z);
+    {
+      GemmParams p = gp();
+      p.A = u; p.lda = D; p.B = w.w_gate_up; p.ldb = D; p.M = M; p.N = 2 * I; p.K = D;
+      p.bmode = 1; p.swiglu_I = I; p.C = z; p.ldc = I;
+      if (lora) {
+        const int sites[2] = {4, 5}, ends[2] = {I, 2 * I};
+        int off[2], ldt;
+        HIP_TRY(lora_down<T>(d, w, sites, 2, u, D, M, lt, off, ldt, s));
+        if (off[0] >= 0 || off[1] >= 0) lora_ext(p, d, w, sites, 2, ends, lt, ldt, off);
+      }
+      HIP_TRY(timed(FAM_GATE_UP, s, [&] { return gemm_any<T>(p, EPI_SWIGLU, s); }));
+    }
+    {
+      GemmParams p = gp();
+      p.A = z; p.lda = I; p.B = w.w_down; p.ldb = I; p.M = M; p.N = D; p.K = I;
+      p.C = hidden; p.ldc = D; p.R = hmid; p.ldr = D;
+      if (lora) {
+        const int sites[1] = {6}, ends[1] = {D};
+        int off[1], ldt;
+        HIP_TRY(lora_down<T>(d, w, sites, 1, z, I, M, lt, off, ldt, s));
+        if (off[0] >= 0) lora_ext(p, d, w, sites, 1, ends, lt, ldt, off);
+      }
+      HIP_TRY(timed(FAM_DOWN, s, [&] { return gemm_any<T>(p, f32res ? EPI_RESID_F32 : EPI_RESID_FROM_F32, s); }));
+    }
+  } else {
+    const int E = d.n_experts, k = d.top_k, Ie = d.expert_intermediate;
+    int* idx = at<int>(ws, L.m_idx);
+    float* wt = at<float>(ws, L.m_w);
+    int* perm = at<int>(ws, L.m_perm);
+    int* pos = at<int>(ws, L.m_pos);
+    int* tiles = at<int>(ws, L.m_tiles);
+    bf16* zp = at<bf16>(ws, L.m_z);
+    bf16* yp = at<bf16>(ws, L.m_y);
+    HIP_TRY(moe_route<bf16>((const bf16*)u, (const bf16*)w.w_router, M, D, E, k, idx, wt, s));
+    HIP_TRY(moe_sort(idx, M, k, E, at<int>(ws, L.m_counts), at<int>(ws, L.m_offsets), perm, pos, tiles, L.max_tiles, 256, s));
+    {
+      GemmParams p = gp();
+      p.A = u; p.lda = D; p.a_rows = perm; p.B = w.w_exp_gate_up; p.ldb = D; p.N = 2 * Ie; p.K = D; p.M = M * k;
+      p.bmode = 1; p.swiglu_I = Ie; p.C = zp; p.ldc = Ie;
+      p.tiles = tiles; p.max_tiles = L.max_tiles; p.b_expert_stride = (int64_t)2 * Ie * D;
+      HIP_TRY(timed(FAM_EXPERT, s, [&] { return gemm_bf16_grouped(p, EPI_SWIGLU, (Ie + 127) / 128, s); }));
+    }
+    {
+      GemmParams p = gp();
+      p.A = zp; p.lda = Ie; p.B = w.w_exp_down; p.ldb = Ie; p.N = D; p.K = Ie; p.M = M * k;
+      p.C = yp; p.ldc = D;
+      p.tiles = tiles; p.max_tiles = L.max_tiles; p.b_expert_stride = (int64_t)D * Ie;
+      HIP_TRY(timed(FAM_EXPERT, s, [&] { return gemm_bf16_grouped(p, EPI_STORE, (D + 255) / 256, s); }));
+    }
+    HIP_TRY(moe_combine(hidden, hmid, yp, wt, pos, M, k, D, s));
+    if (topk_out) HIP_TRY(hipMemcpyAsync(topk_out, idx, (size_t)M * k * 4, hipMemcpyDeviceToDevice, s));
+  }
+  return GEN_OK;
+}
+
+SeqInfo make_seq(int B, int N, const void* const* pk, const void* const* pv, const int* plen) {
+  SeqInfo si;
+  std::memset(&si, 0, sizeof si);
+  si.B = B; si.N = N;
+  for (int b = 0; b < B; ++b) {
+    si.plen[b] = plen[b];
+    si.pk[b] = plen[b] > 0 ? pk[b] : nullptr;
+    si.pv[b] = plen[b] > 0 ? pv[b] : nullptr;
+  }
+  return si;
+}
+
+int check_prefix_ptrs(const SeqInfo& si, int layer) {
+  for (int b = 0; b < si.B; ++b)
+    if (si.plen[b] > 0) {
+      if (!si.pk[b] || !si.pv[b]) return fail(GEN_EINVAL, "layer %d: prefix pointer of sequence %d is NULL", layer, b);
+      if (!aligned16(si.pk[b]) || !aligned16(si.pv[b]))
+        return fail(GEN_EINVAL, "layer %d: prefix pointer of sequence %d not 16-byte aligned", layer, b);
+    }
+  return GEN_OK;
+}
+
+}  // namespace
+
+// ==================================================================== exported
+extern "C" {
+
+const char* gen_last_error(void) { return g_err.c_str(); }
+
+int gen_sigma_schedule(int steps, double shift, double* sigmas) {
+  if (steps < 1) return fail(GEN_EINVAL, "steps %d < 1", steps);
+  if (!sigmas) return fail(GEN_EINVAL, "sigmas is NULL");
+  if (!(shift > 0.0) || !std::isfinite(shift)) return fail(GEN_EINVAL, "shift must be finite and > 0");
+  for (int k = 0; k <= steps; ++k) {
+    const double sgrid = 1.0 - (double)k / (double)steps;
+    sigmas[k] = shift * sgrid / (1.0 + (shift - 1.0) * sgrid);
+  }
+  return ok();
+}
+
+size_t gen_workspace_size(const gen_block_dims* dims, int n_img, int n_br, int n_tokens, int max_prefix) {
+  if (check_dims(dims) != GEN_OK) return 0;
+  if (n_img < 1 || n_br < 1 || n_tokens < 1 || max_prefix < 0) {
+    fail(GEN_EINVAL, "sizes must be positive");
+    return 0;
+  }
+  g_err.clear();
+  return layout(*dims, n_img, n_br, n_tokens, max_prefix).total;
+}
+
+int flow_euler_cfg(float* x, const float* x0_cond, const float* x0_uncond, size_t n, float cfg_scale, float sigma,
+                   float sigma_next, float t_eps, void* stream) {
+  if (!x || !x0_cond) return fail(GEN_EINVAL, "x and x0_cond must be non-NULL");
+  if (!x0_uncond && cfg_scale != 1.0f) return fail(GEN_EINVAL, "x0_uncond is NULL but cfg_scale != 1");
+  if (!aligned16(x) || !aligned16(x0_cond) || (x0_uncond && !aligned16(x0_uncond)))
+    return fail(GEN_EINVAL, "pointers must be 16-byte aligned");
+  if (!std::isfinite(cfg_scale) || !std::isfinite(sigma) || !std::isfinite(sigma_next) || !std::isfinite(t_eps))
+    return fail(GEN_EINVAL, "scalars must be finite");
+  if (!(std::max(sigma, t_eps) > 0.f)) return fail(GEN_EINVAL, "max(sigma, t_eps) must be > 0");
+  HIP_TRY(cfg_euler(x, x, x0_cond, x0_uncond, n, cfg_scale, sigma, sigma_next, t_eps, (hipStream_t)stream));
+  return ok();
+}
+
+int gen_moe_route(const void* u, const void* w_router, int T, int D, int E, int top_k, int dtype, int32_t* idx_out,
+                  float* w_out, void* stream) {
+  if (!u || !w_router || !idx_out || !w_out) return fail(GEN_EINVAL, "NULL pointer argument");
+  if (T < 0 || D <= 0 || D > 4096 || E < 1 || E > 64 || top_k < 1 || top_k > E)
+    return fail(GEN_EINVAL, "bad sizes T=%d D=%d E=%d top_k=%d", T, D, E, top_k);
+  hipStream_t s = (hipStream_t)stream;
+  if (dtype == GEN_BF16) HIP_TRY(moe_route<bf16>((const bf16*)u, (const bf16*)w_router, T, D, E, top_k, idx_out, w_out, s));
+  else if (dtype == GEN_F32) HIP_TRY(moe_route<float>((const float*)u, (const float*)w_router, T, D, E, top_k, idx_out, w_out, s));
+  else return fail(GEN_EINVAL, "bad dtype %d", dtype);
+  return ok();
+}
+
+int gen_block_forward(const gen_block_dims* dims, const gen_block_weights* w, void* hidden, int B, int N,
+                      const void* const* prefix_k, const void* const* prefix_v, const int* prefix_len,
+                      int32_t* topk_idx_out, void* workspace, size_t workspace_bytes, void* stream) {
+  int rc = check_dims(dims);
+  if (rc) return rc;
+  if ((rc = check_weights(dims, w, 0))) return rc;
+  if (!hidden || !aligned16(hidden)) return fail(GEN_EINVAL, "hidden is NULL or not 16-byte aligned");
+  if (B < 1 || N < 1) return fail(GEN_EINVAL, "B=%d and N=%d must be >= 1", B, N);
+  if (B > MAXB) return fail(GEN_EUNSUPPORTED, "B=%d > %d sequences per call", B, MAXB);
+  int maxp = 0;
+  if ((rc = check_prefix(dims, B, prefix_k, prefix_v, prefix_len, &maxp))) return rc;
+  const SeqInfo si = make_seq(B, N, prefix_k, prefix_v, prefix_len);
+  if ((rc = check_prefix_ptrs(si, 0))) return rc;
+  if (!workspace || !aligned16(workspace)) return fail(GEN_EINVAL, "workspace is NULL or not 16-byte aligned");
+  const Ws L = layout(*dims, 1, B, N, maxp);
+  if (workspace_bytes < L.total)
+    return fail(GEN_EWORKSPACE, "workspace %zu bytes < %zu required", workspace_bytes, L.total);
+  hipStream_t s = (hipStream_t)stream;
+  HIP_TRY(rope_table(at<float2>(workspace, L.rope), L.n_pos, dims->head_dim, dims->rope_theta, s));
+  if (dims->dtype == GEN_BF16 && dims->hidden_dtype == GEN_F32)
+    rc = run_block<bf16, float>(*dims, *w, (float*)hidden, si, workspace, L, topk_idx_out, s);
+  else if (dims->dtype == GEN_BF16)
+    rc = run_block<bf16, bf16>(*dims, *w, (bf16*)hidden, si, workspace, L, topk_idx_out, s);
+  else
+    rc = run_block<float, float>(*dims, *w, (float*)hidden, si, workspace, L, topk_idx_out, s);
+  return rc ? rc : ok();
+}
+
+int gen_tower_step(const gen_block_dims* dims, int n_layers, const gen_block_weights* layers, const void* w_in,
+                   const void* temb_w1, const void* temb_w2, const void* g_final, const void* w_out, const float* x_t,
+                   int n_img, int n_br, int H, int W, const float* sigma, const float* sigma_next, float cfg_scale,
+                   int cfg_norm, float t_eps, const void* const* prefix_k, const void* const* prefix_v,
+                   const int* prefix_len, float* x_out, float* x0_out, void* workspace, size_t workspace_bytes,
+                   void* stream) {
+  int rc = check_dims(dims);
+  if (rc) return rc;
+  if (n_layers < 0) return fail(GEN_EINVAL, "n_layers %d < 0", n_layers);
+  if (n_layers > 0 && !layers) return fail(GEN_EINVAL, "layers is NULL");
+  for (int l = 0; l < n_layers; ++l)
+    if ((rc = check_weights(dims, &layers[l], l))) return rc;
+  const void* glob[] = {w_in, temb_w1, temb_w2, g_final, w_out, x_t, x_out};
+  const char* gname[] = {"w_in", "temb_w1", "temb_w2", "g_final", "w_out", "x_t", "x_out"};
+  for (int i = 0; i < 7; ++i) {
+    if (!glob[i]) return fail(GEN_EINVAL, "%s is NULL", gname[i]);
+    if (!aligned16(glob[i])) return fail(GEN_EINVAL, "%s is not 16-byte aligned", gname[i]);
+  }
+  if (x0_out && !aligned16(x0_out)) return fail(GEN_EINVAL, "x0_out is not 16-byte aligned");
+  if (n_img < 1) return fail(GEN_EINVAL, "n_img %d < 1", n_img);
+  if (n_br != 1 && n_br != 2) return fail(GEN_EINVAL, "n_br %d must be 1 or 2", n_br);
+  if (n_img * n_br > MAXB) return fail(GEN_EUNSUPPORTED, "n_img*n_br = %d > %d", n_img * n_br, MAXB);
+  if (H <= 0 || W <= 0 || H % 32 || W % 32) return fail(GEN_EINVAL, "H=%d and W=%d must be positive multiples of 32", H, W);
+  if (!sigma) return fail(GEN_EINVAL, "sigma is NULL");
+  if (cfg_norm != 0) return fail(GEN_EUNSUPPORTED, "cfg_norm %d: only 0 (\"none\") is supported", cfg_norm);
+  if (!sigma_next && n_br != 1) return fail(GEN_EINVAL, "x0-only output (sigma_next NULL) needs n_br == 1");
+  if (!std::isfinite(cfg_scale) || !std::isfinite(t_eps)) return fail(GEN_EINVAL, "cfg_scale and t_eps must be finite");
+  for (int i = 0; i < n_img; ++i) {
+    if (!std::isfinite(sigma[i])) return fail(GEN_EINVAL, "sigma[%d] is not finite", i);
+    if (sigma_next) {
+      if (!std::isfinite(sigma_next[i])) return fail(GEN_EINVAL, "sigma_next[%d] is not finite", i);
+      if (!(std::max(sigma[i], t_eps) > 0.f)) return fail(GEN_EINVAL, "max(sigma[%d], t_eps) must be > 0", i);
+    }
+  }
+  const int B = n_img * n_br, N = (H / 32) * (W / 32);
+  int maxp = 0;
+  if ((rc = check_prefix(dims, B, prefix_k ? prefix_k : nullptr, prefix_v, prefix_len, &maxp))) return rc;
+  if (n_layers > 0 && maxp > 0 && (!prefix_k || !prefix_v)) return fail(GEN_EINVAL, "prefix arrays are NULL");
+  for (int l = 0; l < n_layers; ++l) {
+    const SeqInfo si = make_seq(B, N, prefix_k + (size_t)l * B, prefix_v + (size_t)l * B, prefix_len);
+    if ((rc = check_prefix_ptrs(si, l))) return rc;
+  }
+  if (!workspace || !aligned16(workspace)) return fail(GEN_EINVAL, "workspace is NULL or not 16-byte aligned");
+  const Ws L = layout(*dims, n_img, n_br, N, maxp);
+  if (workspace_bytes < L.total)
+    return fail(GEN_EWORKSPACE, "workspace %zu bytes < %zu required", workspace_bytes, L.total);
+
+  hipStream_t s = (hipStream_t)stream;
+  const bool bf = dims->dtype == GEN_BF16;
+  const int D = dims->hidden;
+  const int M = B * N;
+  void* hidden = at<char>(workspace, L.hidden);
+  void* patches = at<char>(workspace, L.patches);
+  float* temb = at<float>(workspace, L.temb);
+  // timestep embedding, patch embedding (+ temb, copied to every branch)
+  if (bf) HIP_TRY(timestep_embed<bf16>(sigma, (const bf16*)temb_w1, (const bf16*)temb_w2, at<float>(workspace, L.h1), temb, n_img, D, s));
+  else HIP_TRY(timestep_embed<float>(sigma, (const float*)temb_w1, (const float*)temb_w2, at<float>(workspace, L.h1), temb, n_img, D, s));
+  if (bf) HIP_TRY(patchify<bf16>(x_t, (bf16*)patches, n_img, H, W, s));
+  else HIP_TRY(patchify<float>(x_t, (float*)patches, n_img, H, W, s));
+  {
+    GemmParams p = gp();
+    p.A = patches; p.lda = 3072; p.B = w_in; p.ldb = 3072; p.M = n_img * N; p.N = D; p.K = 3072;
+    p.C = hidden; p.ldc = D; p.bias = temb; p.rows_per = N; p.n_bcast = n_br;
+    if (bf) HIP_TRY(gemm_bf16(p, EPI_BIAS_BCAST_F32, s));
+    else HIP_TRY(gemm_f32(p, EPI_BIAS_BCAST_F32, s));
+  }
+  HIP_TRY(rope_table(at<float2>(workspace, L.rope), L.n_pos, dims->head_dim, dims->rope_theta, s));
+  for (int l = 0; l < n_layers; ++l) {
+    const SeqInfo si = make_seq(B, N, prefix_k + (size_t)l * B, prefix_v + (size_t)l * B, prefix_len);
+    if (bf) rc = run_block<bf16, float>(*dims, layers[l], (float*)hidden, si, workspace, L, nullptr, s);
+    else rc = run_block<float, float>(*dims, layers[l], (float*)hidden, si, workspace, L, nullptr, s);
+    if (rc) return rc;
+  }
+  // final norm + out head (fp32, unpatchified)
+  void* u = at<char>(workspace, L.u);
+  if (bf) HIP_TRY((rmsnorm<float, bf16>((const float*)hidden, (const bf16*)g_final, (bf16*)u, M, D, dims->rms_eps, s)));
+  else HIP_TRY((rmsnorm<float, float>((const float*)hidden, (const float*)g_final, (float*)u, M, D, dims->rms_eps, s)));
+  float* x0 = x0_out ? x0_out : (sigma_next ? at<float>(workspace, L.x0) : x_out);
+  {
+    GemmParams p = gp();
+    p.A = u; p.lda = D; p.B = w_out; p.ldb = D; p.M = M; p.N = 3072; p.K = D;
+    p.C = x0; p.rows_per = N; p.img_H = H; p.img_W = W;
+    if (bf) HIP_TRY(gemm_bf16(p, EPI_F32_IMG, s));
+    else HIP_TRY(gemm_f32(p, EPI_F32_IMG, s));
+  }
+  const size_t img = (size_t)3 * H * W;
+  if (!sigma_next) {
+    if (x0 != x_out) HIP_TRY(hipMemcpyAsync(x_out, x0, (size_t)n_img * img * 4, hipMemcpyDeviceToDevice, s));
+    return ok();
+  }
+  for (int i = 0; i < n_img; ++i) {
+    const float* xc = x0 + (size_t)i * n_br * img;
+    const float* xu = n_br == 2 ? xc + img : nullptr;
+    HIP_TRY(cfg_euler(x_out + i * img, x_t + i * img, xc, xu, img, n_br == 2 ? cfg_scale : 1.0f, sigma[i],
+                      sigma_next[i], t_eps, s));
+  }
+  return ok();
+}
+
+}  // extern "C"
+
+// ==================================================================== step-level entry points
+#include "../../include/psf_gen_ops.h"
+
+namespace {
+int check_dtype(int dtype) {
+  if (dtype != GEN_F32 && dtype != GEN_BF16) return fail(GEN_EINVAL, "bad dtype %d", dtype);
+  return GEN_OK;
+}
+size_t op_ws(int B, int N, int Hkv, int d, int maxp, int dtype, size_t* kc, size_t* vt, size_t* rope) {
+  const size_t es = dtype == GEN_BF16 ? 2 : 4;
+  const size_t Lpad = (size_t)(maxp + N + 63) / 64 * 64;
+  size_t o = 0;
+  *kc = o; o += up((size_t)B * Hkv * Lpad * d * es);
+  *vt = o; o += up((size_t)B * Hkv * Lpad * d * es);
+  *rope = o; o += up((size_t)(maxp + N) * (d / 2) * 8);
+  return o;
+}
+}  // namespace
+
+extern "C" {
+
+size_t gen_op_workspace_size(int B, int N, int Hkv, int d, int max_prefix, int dtype) {
+  size_t a, b, c;
+  if (B < 1 || N < 1 || Hkv < 1 || d < 1 || max_prefix < 0 || check_dtype(dtype)) return 0;
+  return op_ws(B, N, Hkv, d, max_prefix, dtype, &a, &b, &c);
+}
+
+int gen_op_rmsnorm(const void* x, const void* g, void* y, int rows, int D, float eps, int dtype, void* stream) {
+  if (check_dtype(dtype)) return GEN_EINVAL;
+  if (!x || !g || !y || !aligned16(x) || !aligned16(g) || !aligned16(y)) return fail(GEN_EINVAL, "NULL or unaligned pointer");
+  if (rows < 0 || D <= 0 || D % 64) return fail(GEN_EINVAL, "rows %d, D %d (D must be a positive multiple of 64)", rows, D);
+  if (D > 8192) return fail(GEN_EUNSUPPORTED, "D %d > 8192", D);
+  hipStream_t s = (hipStream_t)stream;
+  if (dtype == GEN_BF16) HIP_TRY((rmsnorm<bf16, bf16>((const bf16*)x, (const bf16*)g, (bf16*)y, rows, D, eps, s)));
+  else HIP_TRY((rmsnorm<float, float>((const float*)x, (const float*)g, (float*)y, rows, D, eps, s)));
+  return ok();
+}
+
+int gen_op_linear(const void* x, const void* w, void* y, const void* resid, int M, int N, int K, int epi, int dtype,
+                  void* stream) {
+  if (check_dtype(dtype)) return GEN_EINVAL;
+  if (!x || !w || !y || !aligned16(x) || !aligned16(w) || !aligned16(y)) return fail(GEN_EINVAL, "NULL or unaligned pointer");
+  if (M < 0 || N <= 0 || K <= 0 || K % 64) return fail(GEN_EINVAL, "M %d N %d K %d (K must be a positive multiple of 64)", M, N, K);
+  if (epi < 0 || epi > 2) return fail(GEN_EINVAL, "epi %d not in 0..2", epi);
+  if (epi == 1 && !resid) return fail(GEN_EINVAL, "epi 1 needs resid");
+  if (epi == 2 && N % 8) return fail(GEN_EINVAL, "epi 2 needs N %% 8 == 0");
+  GemmParams p = gp();
+  p.A = x; p.lda = K; p.B = w; p.ldb = K; p.M = M; p.K = K; p.C = y;
+  int e = EPI_STORE;
+  if (epi == 0) { p.N = N; p.ldc = N; }
+  if (epi == 1) { p.N = N; p.ldc = N; p.R = resid; p.ldr = N; e = EPI_RESID; }
+  if (epi == 2) { p.N = 2 * N; p.ldc = N; p.bmode = 1; p.swiglu_I = N; e = EPI_SWIGLU; }
+  hipStream_t s = (hipStream_t)stream;
+  if (dtype == GEN_BF16) HIP_TRY(gemm_bf16(p, e, s));
+  else HIP_TRY(gemm_f32(p, e, s));
+  return ok();
+}
+
+int gen_op_qknorm_rope(void* qkv, int B, int N, int Hq, int Hkv, int d, const int* prefix_len, const void* g_q,
+                       const void* g_k, float eps, float theta, void* workspace, size_t workspace_bytes, int dtype,
+                       void* stream) {
+  if (check_dtype(dtype)) return GEN_EINVAL;
+  if (!qkv || !g_q || !g_k || !prefix_len || !workspace) return fail(GEN_EINVAL, "NULL pointer argument");
+  if (B < 1 || B > MAXB || N < 1 || Hq < 1 || Hkv < 1 || Hq % Hkv || (d != 64 && d != 128))
+    return fail(GEN_EINVAL, "bad sizes B=%d N=%d Hq=%d Hkv=%d d=%d", B, N, Hq, Hkv, d);
+  int maxp = 0;
+  for (int b = 0; b < B; ++b) {
+    if (prefix_len[b] < 0) return fail(GEN_EINVAL, "prefix_len[%d] < 0", b);
+    maxp = std::max(maxp, prefix_len[b]);
+  }
+  size_t kc, vt, ro;
+  const size_t need = op_ws(B, N, Hkv, d, maxp, dtype, &kc, &vt, &ro);
+  if (workspace_bytes < need) return fail(GEN_EWORKSPACE, "workspace %zu < %zu", workspace_bytes, need);
+  SeqInfo si;
+  std::memset(&si, 0, sizeof si);
+  si.B = B; si.N = N;
+  for (int b = 0; b < B; ++b) si.plen[b] = prefix_len[b];
+  hipStream_t s = (hipStream_t)stream;
+  float2* table = at<float2>(workspace, ro);
+  HIP_TRY(rope_table(table, maxp + N, d, theta, s));
+  const int64_t ld = (int64_t)(Hq + 2 * Hkv) * d;
+  if (dtype == GEN_BF16) HIP_TRY(qknorm_rope<bf16>((bf16*)qkv, ld, si, Hq, Hkv, d, (const bf16*)g_q, (const bf16*)g_k, table, eps, s));
+  else HIP_TRY(qknorm_rope<float>((float*)qkv, ld, si, Hq, Hkv, d, (const float*)g_q, (const float*)g_k, table, eps, s));
+  return ok();
+}
+
+int gen_op_attention(const void* qkv, int B, int N, int Hq, int Hkv, int d, const void* const* prefix_k,
+                     const void* const* prefix_v, const int* prefix_len, void* out, void* workspace,
+                     size_t workspace_bytes, int dtype, void* stream) {
+  if (check_dtype(dtype)) return GEN_EINVAL;
+  if (!qkv || !out || !prefix_len || !workspace) return fail(GEN_EINVAL, "NULL pointer argument");
+  if (B < 1 || B > MAXB || N < 1 || Hq < 1 || Hkv < 1 || Hq % Hkv || (d != 64 && d != 128))
+    return fail(GEN_EINVAL, "bad sizes B=%d N=%d Hq=%d Hkv=%d d=%d", B, N, Hq, Hkv, d);
+  int maxp = 0, rc;
+  if ((rc = check_prefix(nullptr, B, prefix_k, prefix_v, prefix_len, &maxp))) return rc;
+  const SeqInfo si = make_seq(B, N, prefix_k, prefix_v, prefix_len);
+  if ((rc = check_prefix_ptrs(si, 0))) return rc;
+  size_t kc, vt, ro;
+  const size_t need = op_ws(B, N, Hkv, d, maxp, dtype, &kc, &vt, &ro);
+  if (workspace_bytes < need) return fail(GEN_EWORKSPACE, "workspace %zu < %zu", workspace_bytes, need);
+  const int Lpad = (maxp + N + 63) / 64 * 64;
+  const int64_t ld = (int64_t)(Hq + 2 * Hkv) * d;
+  hipStream_t s = (hipStream_t)stream;
+  if (dtype == GEN_BF16) {
+    HIP_TRY(pack_kv<bf16>((const bf16*)qkv, ld, si, Hq, Hkv, d, Lpad, at<bf16>(workspace, kc), at<bf16>(workspace, vt), s));
+    HIP_TRY(attention_bf16((const bf16*)qkv, ld, si, Hq, Hkv, d, Lpad, at<bf16>(workspace, kc), at<bf16>(workspace, vt), (bf16*)out, (int64_t)Hq * d, s));
+  } else {
+    HIP_TRY(pack_kv<float>((const float*)qkv, ld, si, Hq, Hkv, d, Lpad, at<float>(workspace, kc), at<float>(workspace, vt), s));
+    HIP_TRY(attention_f32((const float*)qkv, ld, si, Hq, Hkv, d, Lpad, at<float>(workspace, kc), at<float>(workspace, vt), (float*)out, (int64_t)Hq * d, s));
+  }
+  return ok();
+}
+
+}  // extern "C"
+
+extern "C" {
+
+int gen_timing_begin(int family, int capacity) {
+  if (family < 0 || family > 5 || capacity < 1) return fail(GEN_EINVAL, "bad family %d or capacity %d", family, capacity);
+  if (g_timing.ev) return fail(GEN_EINVAL, "timing already active");
+  g_timing.ev = new hipEvent_t[2 * capacity];
+  for (int i = 0; i < 2 * capacity; ++i) {
+    hipError_t e = hipEventCreate(&g_timing.ev[i]);
+    if (e != hipSuccess) {
+      for (int j = 0; j < i; ++j) (void)hipEventDestroy(g_timing.ev[j]);
+      delete[] g_timing.ev;
+      g_timing.ev = nullptr;
+      return fail(GEN_EHIP, "hipEventCreate: %s", hipGetErrorString(e));
+    }
+  }
+  g_timing.family = family;
+  g_timing.cap = capacity;
+  g_timing.used = 0;
+  return ok();
+}
+
+int gen_timing_end(double* total_ms, int* n_launches) {
+  if (!g_timing.ev) return fail(GEN_EINVAL, "timing not active");
+  double tot = 0.0;
+  hipError_t err = hipSuccess;
+  if (g_timing.used > 0) err = hipEventSynchronize(g_timing.ev[2 * g_timing.used - 1]);
+  for (int i = 0; i < g_timing.used && err == hipSuccess; ++i) {
+    float ms = 0.f;
+    err = hipEventElapsedTime(&ms, g_timing.ev[2 * i], g_timing.ev[2 * i + 1]);
+    tot += ms;
+  }
+  const int n = g_timing.used;
+  for (int i = 0; i < 2 * g_timing.cap; ++i) (void)hipEventDestroy(g_timing.ev[i]);
+  delete[] g_timing.ev;
+  g_timing = Timing();
+  if (err != hipSuccess) return fail(GEN_EHIP, "event timing: %s", hipGetErrorString(err));
+  if (total_ms) *total_ms = tot;
+  if (n_launches) *n_launches = n;
+  return ok();
+}
+
+}  // extern "C"

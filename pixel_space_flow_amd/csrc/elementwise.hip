@@ -1,0 +1,368 @@
+// Memory-bound kernels of the gen-tower step: RMSNorm, fused QK-norm + RoPE, RoPE table,
+// K/V packing for attention, patchify, timestep embedding and the CFG + Euler update.
+// All use 16-byte vector accesses along the contiguous axis; arithmetic is fp32.
+#include "common.h"
+#include "kernels.h"
+
+namespace psf {
+namespace {
+
+// ---- 16-byte vectors of T: 8 bf16 or 4 float
+template <typename T> struct V16;
+template <> struct V16<bf16> {
+  static constexpr int N = 8;
+  static DEVI void unpack(const u32x4& v, float* f) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      f[2 * i] = __uint_as_float(v[i] << 16);
+      f[2 * i + 1] = __uint_as_float(v[i] & 0xffff0000u);
+    }
+  }
+  static DEVI u32x4 pack(const float* f) {
+    u32x4 v;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const uint32_t lo = __builtin_bit_cast(uint16_t, static_cast<bf16>(f[2 * i]));
+      const uint32_t hi = __builtin_bit_cast(uint16_t, static_cast<bf16>(f[2 * i + 1]));
+      v[i] = lo | (hi << 16);
+    }
+    return v;
+  }
+};
+template <> struct V16<float> {
+  static constexpr int N = 4;
+  static DEVI void unpack(const u32x4& v, float* f) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) f[i] = __uint_as_float(v[i]);
+  }
+  static DEVI u32x4 pack(const float* f) {
+    u32x4 v;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) v[i] = __float_as_uint(f[i]);
+    return v;
+  }
+};
+
+// ---------------------------------------------------------------- RMSNorm
+// One 256-thread workgroup per row; the row stays in registers between the two passes.
+// Input chunks are 16 bytes of Tin; when Tin is wider than T (fp32 residual in, bf16 out)
+// a chunk covers 4 elements and is written as 8 bytes.
+template <typename Tin, typename T, int CH>
+__global__ __launch_bounds__(256) void rmsnorm_kernel(const Tin* __restrict__ x, const T* __restrict__ g,
+                                                      T* __restrict__ y, int D, float eps) {
+  using V = V16<Tin>;
+  const int nch = D / V::N;
+  const int64_t base = (int64_t)blockIdx.x * D;
+  u32x4 buf[CH];
+  float ss = 0.f;
+#pragma unroll
+  for (int c = 0; c < CH; ++c) {
+    const int i = threadIdx.x + c * 256;
+    if (i < nch) {
+      buf[c] = *(const u32x4*)(x + base + i * V::N);
+      float f[V::N];
+      V::unpack(buf[c], f);
+#pragma unroll
+      for (int e = 0; e < V::N; ++e) ss += f[e] * f[e];
+    }
+  }
+  __shared__ float red[4];
+  ss = warp_sum(ss);
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = ss;
+  __syncthreads();
+  const float tot = red[0] + red[1] + red[2] + red[3];
+  const float r = 1.0f / sqrtf(tot / (float)D + eps);
+#pragma unroll
+  for (int c = 0; c < CH; ++c) {
+    const int i = threadIdx.x + c * 256;
+    if (i < nch) {
+      float f[V::N];
+      V::unpack(buf[c], f);
+#pragma unroll
+      for (int e = 0; e < V::N; ++e) f[e] = f[e] * r * to_f(g[i * V::N + e]);
+      if constexpr (sizeof(Tin) == sizeof(T)) {
+        *(u32x4*)(y + base + i * V::N) = V::pack(f);
+      } else {
+#pragma unroll
+        for (int e = 0; e < V::N; ++e) y[base + i * V::N + e] = from_f<T>(f[e]);
+      }
+    }
+  }
+}
+
+// ---------------------------------------------------------------- RoPE table
+__global__ void rope_table_kernel(float2* table, int n_pos, int half, double theta) {
+  const int i = blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= n_pos * half) return;
+  const int pos = i / half, j = i - pos * half;
+  const double w = pow(theta, -2.0 * (double)j / (double)(2 * half));
+  double sn, cs;
+  sincos((double)pos * w, &sn, &cs);
+  table[i] = make_float2((float)cs, (float)sn);
+}
+
+// ---------------------------------------------------------------- QK-norm + RoPE
+// A head vector of d elements is spread over L = d / V::N lanes (16-byte chunks); a wave
+// covers 64 / L head vectors.  Rotate-half pairs element j with j + d/2, which lives in
+// lane ^ (L/2).
+template <typename T, int D>
+__global__ __launch_bounds__(256) void qknorm_rope_kernel(T* __restrict__ qkv, int64_t ld, SeqInfo si, int Hq, int Hkv,
+                                                          const T* __restrict__ gq, const T* __restrict__ gk,
+                                                          const float2* __restrict__ table, float eps, int64_t total) {
+  using V = V16<T>;
+  constexpr int L = D / V::N;
+  constexpr int HPW = 64 / L;
+  const int lane = threadIdx.x & 63;
+  const int64_t hv = ((int64_t)blockIdx.x * 4 + (threadIdx.x >> 6)) * HPW + lane / L;
+  const int sub = lane % L;
+  const bool active = hv < total;
+  const int64_t hvc = active ? hv : 0;
+  const int H = Hq + Hkv;
+  const int64_t tok = hvc / H;
+  const int head = (int)(hvc - tok * H);
+  const int b = (int)(tok / si.N), n = (int)(tok - (int64_t)b * si.N);
+  const int pos = si.plen[b] + n;
+  T* p = qkv + tok * ld + (int64_t)head * D + sub * V::N;
+  const T* g = (head < Hq ? gq : gk) + sub * V::N;
+  float x[V::N], gg[V::N];
+  V::unpack(*(const u32x4*)p, x);
+  V::unpack(*(const u32x4*)g, gg);
+  float ss = 0.f;
+#pragma unroll
+  for (int e = 0; e < V::N; ++e) ss += x[e] * x[e];
+#pragma unroll
+  for (int o = L / 2; o > 0; o >>= 1) ss += __shfl_xor(ss, o, 64);
+  const float r = 1.0f / sqrtf(ss / (float)D + eps);
+#pragma unroll
+  for (int e = 0; e < V::N; ++e) x[e] = x[e] * r * gg[e];
+  float pr[V::N];
+#pragma unroll
+  for (int e = 0; e < V::N; ++e) pr[e] = __shfl_xor(x[e], L / 2, 64);
+  const bool first = sub < L / 2;
+  const int j0 = (sub % (L / 2)) * V::N;
+  const float2* tb = table + (int64_t)pos * (D / 2) + j0;
+  float out[V::N];
+#pragma unroll
+  for (int e = 0; e < V::N; ++e) {
+    const float2 cs = tb[e];
+    out[e] = first ? (x[e] * cs.x - pr[e] * cs.y) : (x[e] * cs.x + pr[e] * cs.y);
+  }
+  if (active && head < H) *(u32x4*)p = V::pack(out);
+}
+
+// ---------------------------------------------------------------- K/V packing
+template <typename T>
+__global__ __launch_bounds__(256) void pack_k_kernel(const T* __restrict__ qkv, int64_t ld, SeqInfo si, int Hq,
+                                                     int Hkv, int d, int Lpad, T* __restrict__ Kc) {
+  using V = V16<T>;
+  const int cpr = d / V::N;                        // chunks per row
+  const int b = blockIdx.z, g = blockIdx.y;
+  const int t = blockIdx.x * 256 + threadIdx.x;
+  const int j = t / cpr, c = t - j * cpr;
+  if (j >= Lpad) return;
+  const int P = si.plen[b];
+  u32x4 v = {0, 0, 0, 0};
+  if (j < P) v = *(const u32x4*)((const T*)si.pk[b] + ((int64_t)j * Hkv + g) * d + c * V::N);
+  else if (j < P + si.N) v = *(const u32x4*)(qkv + ((int64_t)b * si.N + j - P) * ld + (int64_t)(Hq + g) * d + c * V::N);
+  *(u32x4*)(Kc + (((int64_t)b * Hkv + g) * Lpad + j) * d + c * V::N) = v;
+}
+
+// Vt[b][g][dd][j0..j0+8): each lane gathers 8 keys of one head-dim column; a wave's loads
+// of one key row are 64 consecutive elements.
+template <typename T>
+__global__ __launch_bounds__(256) void pack_vt_kernel(const T* __restrict__ qkv, int64_t ld, SeqInfo si, int Hq,
+                                                      int Hkv, int d, int Lpad, T* __restrict__ Vt) {
+  using V = V16<T>;
+  const int b = blockIdx.z, g = blockIdx.y;
+  const int t = blockIdx.x * 256 + threadIdx.x;
+  const int dd = t % d, jc = t / d;
+  const int j0 = jc * V::N;
+  if (j0 >= Lpad) return;
+  const int P = si.plen[b];
+  float f[V::N];
+#pragma unroll
+  for (int e = 0; e < V::N; ++e) {
+    const int j = j0 + e;
+    float v = 0.f;
+    if (j < P) v = to_f(((const T*)si.pv[b])[((int64_t)j * Hkv + g) * d + dd]);
+    else if (j < P + si.N) v = to_f(qkv[((int64_t)b * si.N + j - P) * ld + (int64_t)(Hq + Hkv + g) * d + dd]);
+    f[e] = v;
+  }
+  *(u32x4*)(Vt + (((int64_t)b * Hkv + g) * d + dd) * Lpad + j0) = V::pack(f);
+}
+
+// ---------------------------------------------------------------- patchify
+template <typename T>
+__global__ __launch_bounds__(256) void patchify_kernel(const float* __restrict__ x, T* __restrict__ out, int n_img,
+                                                       int H, int W, int64_t total) {
+  const int64_t t = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (t >= total) return;
+  const int64_t tok = t / 384;
+  const int f0 = (int)(t - tok * 384) * 8;
+  const int pw = W >> 5, N = (H >> 5) * pw;
+  const int i = (int)(tok / N), n = (int)(tok - (int64_t)i * N);
+  const int py = n / pw, px = n - py * pw;
+  const int c = f0 >> 10, iy = (f0 >> 5) & 31, ix = f0 & 31;
+  const float* src = x + (((int64_t)i * 3 + c) * H + py * 32 + iy) * W + px * 32 + ix;
+  const float4 a = *(const float4*)src, bq = *(const float4*)(src + 4);
+  T* dst = out + tok * 3072 + f0;
+  const float v[8] = {a.x, a.y, a.z, a.w, bq.x, bq.y, bq.z, bq.w};
+#pragma unroll
+  for (int e = 0; e < 8; ++e) dst[e] = from_f<T>(v[e]);
+}
+
+// ---------------------------------------------------------------- timestep embedding
+struct Sigmas { float s[MAXB]; };
+
+template <typename T>
+__global__ __launch_bounds__(256) void temb1_kernel(Sigmas sg, const T* __restrict__ w1, float* __restrict__ h1, int D) {
+  __shared__ float feat[256];
+  const int i = blockIdx.y;
+  {
+    const int k = threadIdx.x;
+    const int j = k & 127;
+    const double f = exp(-log(10000.0) * (double)j / 128.0);
+    const double a = 1000.0 * (double)sg.s[i] * f;
+    feat[k] = (float)(k < 128 ? cos(a) : sin(a));
+  }
+  __syncthreads();
+  const int lane = threadIdx.x & 63;
+  const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (row >= D) return;
+  float acc = 0.f;
+  for (int k = lane; k < 256; k += 64) acc += to_f(w1[(int64_t)row * 256 + k]) * feat[k];
+  acc = warp_sum(acc);
+  if (lane == 0) h1[(int64_t)i * D + row] = acc / (1.0f + expf(-acc));
+}
+
+template <typename T>
+__global__ __launch_bounds__(256) void temb2_kernel(const T* __restrict__ w2, const float* __restrict__ h1,
+                                                    float* __restrict__ temb, int D) {
+  const int i = blockIdx.y;
+  const int lane = threadIdx.x & 63;
+  const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (row >= D) return;
+  float acc = 0.f;
+  for (int k = lane; k < D; k += 64) acc += to_f(w2[(int64_t)row * D + k]) * h1[(int64_t)i * D + k];
+  acc = warp_sum(acc);
+  if (lane == 0) temb[(int64_t)i * D + row] = acc;
+}
+
+// ---------------------------------------------------------------- CFG + Euler
+template <bool MIX>
+__global__ __launch_bounds__(256) void cfg_euler_kernel(float* xo, const float* xi, const float* __restrict__ xc,
+                                                        const float* __restrict__ xu, size_t n, float scale, float dt,
+                                                        float den) {
+  const size_t i = ((size_t)blockIdx.x * 256 + threadIdx.x) * 4;
+  if (i + 4 <= n) {
+    float4 a = *(const float4*)(xi + i);
+    const float4 c = *(const float4*)(xc + i);
+    float4 g = c;
+    if (MIX) {
+      const float4 u = *(const float4*)(xu + i);
+      g = make_float4(u.x + scale * (c.x - u.x), u.y + scale * (c.y - u.y), u.z + scale * (c.z - u.z),
+                      u.w + scale * (c.w - u.w));
+    }
+    a.x = a.x + dt * ((a.x - g.x) / den);
+    a.y = a.y + dt * ((a.y - g.y) / den);
+    a.z = a.z + dt * ((a.z - g.z) / den);
+    a.w = a.w + dt * ((a.w - g.w) / den);
+    *(float4*)(xo + i) = a;
+  } else {
+    for (size_t k = i; k < n; ++k) {
+      const float g = MIX ? xu[k] + scale * (xc[k] - xu[k]) : xc[k];
+      xo[k] = xi[k] + dt * ((xi[k] - g) / den);
+    }
+  }
+}
+
+}  // namespace
+
+// ================================================================== launchers
+template <typename Tin, typename T>
+hipError_t rmsnorm(const Tin* x, const T* g, T* y, int rows, int D, float eps, hipStream_t s) {
+  if (rows <= 0) return hipSuccess;
+  const int nch = D / V16<Tin>::N;
+  if (nch <= 256) hipLaunchKernelGGL((rmsnorm_kernel<Tin, T, 1>), dim3(rows), dim3(256), 0, s, x, g, y, D, eps);
+  else if (nch <= 512) hipLaunchKernelGGL((rmsnorm_kernel<Tin, T, 2>), dim3(rows), dim3(256), 0, s, x, g, y, D, eps);
+  else if (nch <= 1024) hipLaunchKernelGGL((rmsnorm_kernel<Tin, T, 4>), dim3(rows), dim3(256), 0, s, x, g, y, D, eps);
+  else if (nch <= 2048) hipLaunchKernelGGL((rmsnorm_kernel<Tin, T, 8>), dim3(rows), dim3(256), 0, s, x, g, y, D, eps);
+  else return hipErrorInvalidValue;
+  return hipGetLastError();
+}
+template hipError_t rmsnorm<bf16, bf16>(const bf16*, const bf16*, bf16*, int, int, float, hipStream_t);
+template hipError_t rmsnorm<float, float>(const float*, const float*, float*, int, int, float, hipStream_t);
+template hipError_t rmsnorm<float, bf16>(const float*, const bf16*, bf16*, int, int, float, hipStream_t);
+
+hipError_t rope_table(float2* table, int n_pos, int head_dim, float theta, hipStream_t s) {
+  const int half = head_dim / 2;
+  const int total = n_pos * half;
+  hipLaunchKernelGGL(rope_table_kernel, dim3((total + 255) / 256), dim3(256), 0, s, table, n_pos, half, (double)theta);
+  return hipGetLastError();
+}
+
+template <typename T>
+hipError_t qknorm_rope(T* qkv, int64_t ld, const SeqInfo& si, int Hq, int Hkv, int d, const T* gq, const T* gk,
+                       const float2* table, float eps, hipStream_t s) {
+  const int64_t total = (int64_t)si.B * si.N * (Hq + Hkv);
+  if (total == 0) return hipSuccess;
+  const int L = d / V16<T>::N;
+  const int64_t per_block = 4 * (64 / L);
+  const dim3 grid((unsigned)((total + per_block - 1) / per_block));
+  if (d == 128) hipLaunchKernelGGL((qknorm_rope_kernel<T, 128>), grid, dim3(256), 0, s, qkv, ld, si, Hq, Hkv, gq, gk, table, eps, total);
+  else if (d == 64) hipLaunchKernelGGL((qknorm_rope_kernel<T, 64>), grid, dim3(256), 0, s, qkv, ld, si, Hq, Hkv, gq, gk, table, eps, total);
+  else return hipErrorInvalidValue;
+  return hipGetLastError();
+}
+template hipError_t qknorm_rope<bf16>(bf16*, int64_t, const SeqInfo&, int, int, int, const bf16*, const bf16*, const float2*, float, hipStream_t);
+template hipError_t qknorm_rope<float>(float*, int64_t, const SeqInfo&, int, int, int, const float*, const float*, const float2*, float, hipStream_t);
+
+template <typename T>
+hipError_t pack_kv(const T* qkv, int64_t ld, const SeqInfo& si, int Hq, int Hkv, int d, int Lpad, T* Kc, T* Vt,
+                   hipStream_t s) {
+  const int cpr = d / V16<T>::N;
+  dim3 gk((Lpad * cpr + 255) / 256, Hkv, si.B);
+  hipLaunchKernelGGL(pack_k_kernel<T>, gk, dim3(256), 0, s, qkv, ld, si, Hq, Hkv, d, Lpad, Kc);
+  dim3 gv((d * (Lpad / V16<T>::N) + 255) / 256, Hkv, si.B);
+  hipLaunchKernelGGL(pack_vt_kernel<T>, gv, dim3(256), 0, s, qkv, ld, si, Hq, Hkv, d, Lpad, Vt);
+  return hipGetLastError();
+}
+template hipError_t pack_kv<bf16>(const bf16*, int64_t, const SeqInfo&, int, int, int, int, bf16*, bf16*, hipStream_t);
+template hipError_t pack_kv<float>(const float*, int64_t, const SeqInfo&, int, int, int, int, float*, float*, hipStream_t);
+
+template <typename T>
+hipError_t patchify(const float* x, T* patches, int n_img, int H, int W, hipStream_t s) {
+  const int64_t total = (int64_t)n_img * (H / 32) * (W / 32) * 384;
+  hipLaunchKernelGGL(patchify_kernel<T>, dim3((unsigned)((total + 255) / 256)), dim3(256), 0, s, x, patches, n_img, H, W, total);
+  return hipGetLastError();
+}
+template hipError_t patchify<bf16>(const float*, bf16*, int, int, int, hipStream_t);
+template hipError_t patchify<float>(const float*, float*, int, int, int, hipStream_t);
+
+template <typename T>
+hipError_t timestep_embed(const float* sigma_host, const T* w1, const T* w2, float* h1, float* temb, int n_img, int D,
+                          hipStream_t s) {
+  Sigmas sg;
+  for (int i = 0; i < MAXB; ++i) sg.s[i] = i < n_img ? sigma_host[i] : 0.f;
+  dim3 grid((D + 3) / 4, n_img);
+  hipLaunchKernelGGL(temb1_kernel<T>, grid, dim3(256), 0, s, sg, w1, h1, D);
+  hipLaunchKernelGGL(temb2_kernel<T>, grid, dim3(256), 0, s, w2, h1, temb, D);
+  return hipGetLastError();
+}
+template hipError_t timestep_embed<bf16>(const float*, const bf16*, const bf16*, float*, float*, int, int, hipStream_t);
+template hipError_t timestep_embed<float>(const float*, const float*, const float*, float*, float*, int, int, hipStream_t);
+
+hipError_t cfg_euler(float* xo, const float* x, const float* xc, const float* xu, size_t n, float scale, float sigma,
+                     float sigma_next, float t_eps, hipStream_t s) {
+  if (n == 0) return hipSuccess;
+  const float dt = sigma_next - sigma;
+  const float den = sigma > t_eps ? sigma : t_eps;
+  const unsigned grid = (unsigned)((n + 1023) / 1024);
+  if (xu && scale != 1.0f)
+    hipLaunchKernelGGL(cfg_euler_kernel<true>, dim3(grid), dim3(256), 0, s, xo, x, xc, xu, n, scale, dt, den);
+  else
+    hipLaunchKernelGGL(cfg_euler_kernel<false>, dim3(grid), dim3(256), 0, s, xo, x, xc, xu, n, scale, dt, den);
+  return hipGetLastError();
+}
+
+}  // namespace psf

@@ -1,0 +1,397 @@
+// bf16 MFMA GEMM family for the gen block's projections (QKV, O, gate/up, down, patch
+// embed, out head, LoRA, expert GEMMs) on gfx950, plus a plain fp32 GEMM for fp32 runs.
+//
+// C = epilogue(A B^T), A [M, K] and B [N, K] both K-contiguous (Linear weights are
+// [out, in]), fp32 accumulation.  Tile 256 x 256 x 64, 4 waves in a 2 x 2 grid, each
+// wave owning 128 x 128 outputs as 4 x 4 blocks of v_mfma_f32_32x32x16_bf16.  Global
+// tiles are staged through registers into LDS (double buffered); LDS rows are 64 bf16
+// (128 B) with 16-byte chunks XOR-swizzled by (row & 7) so that MFMA fragment reads
+// (8 rows per LDS cycle) and chunk writes are bank-conflict free.
+#include "common.h"
+#include "gemm.h"
+
+namespace psf {
+namespace {
+
+constexpr int BM = 256, BN = 256, BK = 64, NT = 256;
+constexpr int STAGE_BYTES = (BM + BN) * BK * 2;  // 64 KiB per stage
+
+DEVI int swz(int row, int chunk) { return row * (BK * 2) + ((chunk ^ (row & 7)) << 4); }
+
+// Row pointer of B-tile row r (tile column base n0) for the three B modes.
+DEVI const bf16* b_row_ptr(const GemmParams& p, const bf16* Bbase, int tn, int r, int& valid) {
+  if (p.bmode == 1) {
+    // 32-column blocks alternate gate / up: block nb covers output columns
+    // tn*128 + (nb/2)*32 + [0, 32).
+    const int nb = r >> 5;
+    const int j = tn * (BN / 2) + (nb >> 1) * 32 + (r & 31);
+    valid = j < p.swiglu_I;
+    const int jj = valid ? j : 0;
+    return Bbase + (int64_t)((nb & 1) ? p.swiglu_I + jj : jj) * p.ldb;
+  }
+  int n = tn * BN + r;
+  valid = n < p.N;
+  if (!valid) n = 0;
+  if (p.bmode == 2) {
+    const int s = n / p.seg_rows;
+    return (const bf16*)p.Bs[s] + (int64_t)(n - s * p.seg_rows) * p.ldb;
+  }
+  return Bbase + (int64_t)n * p.ldb;
+}
+
+// B-row -> output column used by the K extension's site lookup.
+DEVI int b_row_outcol(const GemmParams& p, int tn, int r) {
+  if (p.bmode == 1) {
+    const int nb = r >> 5;
+    const int j = tn * (BN / 2) + (nb >> 1) * 32 + (r & 31);
+    return (nb & 1) ? p.swiglu_I + j : j;   // gate columns first, then up columns
+  }
+  return tn * BN + r;
+}
+
+template <int EPI>
+DEVI void store_one(const GemmParams& p, int row, int col, float v) {
+  if (EPI == EPI_STORE) {
+    ((bf16*)p.C)[(int64_t)row * p.ldc + col] = from_f<bf16>(v);
+  } else if (EPI == EPI_SCALED) {
+    ((bf16*)p.C)[(int64_t)row * p.ldc + col] = from_f<bf16>(v * p.scale);
+  } else if (EPI == EPI_RESID) {
+    const float r = to_f(((const bf16*)p.R)[(int64_t)row * p.ldr + col]);
+    ((bf16*)p.C)[(int64_t)row * p.ldc + col] = from_f<bf16>(r + v);
+  } else if (EPI == EPI_RESID_TO_F32) {
+    const float r = to_f(((const bf16*)p.R)[(int64_t)row * p.ldr + col]);
+    ((float*)p.C)[(int64_t)row * p.ldc + col] = r + v;
+  } else if (EPI == EPI_RESID_FROM_F32) {
+    const float r = ((const float*)p.R)[(int64_t)row * p.ldr + col];
+    ((bf16*)p.C)[(int64_t)row * p.ldc + col] = from_f<bf16>(r + v);
+  } else if (EPI == EPI_RESID_F32) {
+    const float r = ((const float*)p.R)[(int64_t)row * p.ldr + col];
+    ((float*)p.C)[(int64_t)row * p.ldc + col] = r + v;
+  } else if (EPI == EPI_BIAS_BCAST_F32) {
+    const int img = row / p.rows_per, t = row - img * p.rows_per;
+    const float x = v + p.bias[(int64_t)img * p.N + col];
+    for (int br = 0; br < p.n_bcast; ++br)
+      ((float*)p.C)[((int64_t)(img * p.n_bcast + br) * p.rows_per + t) * p.ldc + col] = x;
+  } else if (EPI == EPI_F32_IMG) {
+    // token row -> (image, patch row, patch col); feature col -> (channel, iy, ix)
+    const int img = row / p.rows_per, t = row - img * p.rows_per;
+    const int pw = p.img_W >> 5;
+    const int py = t / pw, px = t - py * pw;
+    const int c = col >> 10, iy = (col >> 5) & 31, ix = col & 31;
+    float* out = (float*)p.C;
+    out[(((int64_t)img * 3 + c) * p.img_H + py * 32 + iy) * p.img_W + px * 32 + ix] = v;
+  } else if (EPI == EPI_BIAS_BCAST) {
+    const int img = row / p.rows_per, t = row - img * p.rows_per;
+    const float x = v + p.bias[(int64_t)img * p.N + col];
+    const bf16 xb = from_f<bf16>(x);
+    for (int br = 0; br < p.n_bcast; ++br)
+      ((bf16*)p.C)[((int64_t)(img * p.n_bcast + br) * p.rows_per + t) * p.ldc + col] = xb;
+  }
+}
+
+template <int EPI, bool GROUPED, bool EXT>
+__global__ __launch_bounds__(NT, 1) void gemm_bf16_kernel(GemmParams p, int n_col_tiles) {
+  extern __shared__ __attribute__((aligned(16))) char smem[];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int wm = wave >> 1, wn = wave & 1;
+
+  // ---- tile coordinates
+  int tm, tn, row0, rows, expert = 0;
+  if (GROUPED) {
+    const int t = blockIdx.x / n_col_tiles;
+    tn = blockIdx.x - t * n_col_tiles;
+    expert = p.tiles[3 * t];
+    if (expert < 0) return;                      // unused slot of the tile table
+    row0 = p.tiles[3 * t + 1];
+    rows = p.tiles[3 * t + 2];
+    tm = 0;
+  } else {
+    const int n_m = (p.M + BM - 1) / BM;
+    const int n_t = n_m * n_col_tiles;
+    const int id = xcd_remap(blockIdx.x, n_t);
+    // grouped ordering: 8 m-tiles walk together so concurrently running tiles share A and B panels
+    const int GROUP = 8;
+    const int per_group = GROUP * n_col_tiles;
+    const int g = id / per_group;
+    const int first_m = g * GROUP;
+    const int gsz = min(n_m - first_m, GROUP);
+    const int r_in = id - g * per_group;
+    tm = first_m + r_in % gsz;
+    tn = r_in / gsz;
+    row0 = tm * BM;
+    rows = min(BM, p.M - row0);
+  }
+  const bf16* Bbase = (const bf16*)p.B + (GROUPED ? (int64_t)expert * p.b_expert_stride : 0);
+
+  // ---- per-thread load rows: chunk (tid & 7) of rows (tid >> 3) + 32 i
+  const int chunk = tid & 7;
+  const bf16* arow[8];
+  const bf16* brow[8];
+  int bvalid_mask = 0;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const int r = (tid >> 3) + 32 * i;
+    const int rr = min(r, rows - 1);
+    int prow = row0 + rr;
+    if (p.a_rows) prow = p.a_rows[prow];
+    arow[i] = (const bf16*)p.A + (int64_t)prow * p.lda + chunk * 8;
+    int v;
+    brow[i] = b_row_ptr(p, Bbase, tn, r, v) + chunk * 8;
+    bvalid_mask |= v << i;
+  }
+  const int KT0 = p.K / BK;
+  const int KT = KT0 + (EXT ? (p.xk + BK - 1) / BK : 0);
+
+  u32x4 ra[8], rb[8];
+  auto load = [&](int kt) {
+    if (!EXT || kt < KT0) {
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        ra[i] = *(const u32x4*)(arow[i] + kt * BK);
+        rb[i] = *(const u32x4*)(brow[i] + kt * BK);
+      }
+    } else {
+      // LoRA extension: k in [0, xk) of X and of the site's up-projection rows
+      const int k = (kt - KT0) * BK + chunk * 8;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const int r = (tid >> 3) + 32 * i;
+        const int rr = min(r, rows - 1);
+        int prow = row0 + rr;
+        ra[i] = (k < p.xk) ? *(const u32x4*)((const bf16*)p.X + (int64_t)prow * p.ldx + k) : u32x4{0, 0, 0, 0};
+        const int col = b_row_outcol(p, tn, r);
+        const int s = col < p.xsite_end[0] ? 0 : (col < p.xsite_end[1] ? 1 : 2);
+        const int start = s == 0 ? 0 : p.xsite_end[s - 1];
+        const int kk = k - p.xoff[s];
+        const bool ok = ((bvalid_mask >> i) & 1) && p.XB[s] != nullptr && kk >= 0 && kk < p.xr;
+        rb[i] = ok ? *(const u32x4*)((const bf16*)p.XB[s] + (int64_t)(col - start) * p.xr + kk) : u32x4{0, 0, 0, 0};
+      }
+    }
+  };
+  auto store = [&](int stage) {
+    char* As = smem + stage * STAGE_BYTES;
+    char* Bs = As + BM * BK * 2;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int r = (tid >> 3) + 32 * i;
+      *(u32x4*)(As + swz(r, chunk)) = ra[i];
+      *(u32x4*)(Bs + swz(r, chunk)) = rb[i];
+    }
+  };
+
+  f32x16 acc[4][4];
+#pragma unroll
+  for (int a = 0; a < 4; ++a)
+#pragma unroll
+    for (int b = 0; b < 4; ++b)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) acc[a][b][e] = 0.f;
+
+  load(0);
+  store(0);
+  __syncthreads();
+  const int lr = lane & 31, lh = lane >> 5;
+  for (int kt = 0; kt < KT; ++kt) {
+    const int cur = kt & 1;
+    if (kt + 1 < KT) load(kt + 1);
+    const char* As = smem + cur * STAGE_BYTES;
+    const char* Bs = As + BM * BK * 2;
+#pragma unroll
+    for (int ks = 0; ks < BK / 16; ++ks) {
+      bf16x8 af[4], bfr[4];
+#pragma unroll
+      for (int mb = 0; mb < 4; ++mb) af[mb] = *(const bf16x8*)(As + swz(wm * 128 + mb * 32 + lr, ks * 2 + lh));
+#pragma unroll
+      for (int nb = 0; nb < 4; ++nb) bfr[nb] = *(const bf16x8*)(Bs + swz(wn * 128 + nb * 32 + lr, ks * 2 + lh));
+#pragma unroll
+      for (int mb = 0; mb < 4; ++mb)
+#pragma unroll
+        for (int nb = 0; nb < 4; ++nb)
+          acc[mb][nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[mb], bfr[nb], acc[mb][nb], 0, 0, 0);
+    }
+    if (kt + 1 < KT) store(cur ^ 1);
+    __syncthreads();
+  }
+
+  // ---- epilogue.  Lane holds column (lane & 31) and rows (e/4)*8 + (lane/32)*4 + e%4 of each block.
+  const int orow0 = (GROUPED ? 0 : 0);
+  (void)orow0;
+  if (EPI == EPI_SWIGLU) {
+#pragma unroll
+    for (int mb = 0; mb < 4; ++mb)
+#pragma unroll
+      for (int pr = 0; pr < 2; ++pr) {
+        const int j = tn * (BN / 2) + (wn * 2 + pr) * 32 + lr;
+        if (j >= p.swiglu_I) continue;
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
+          const int r = wm * 128 + mb * 32 + (e >> 2) * 8 + lh * 4 + (e & 3);
+          if (r >= rows) continue;
+          const float g = acc[mb][2 * pr][e], u = acc[mb][2 * pr + 1][e];
+          ((bf16*)p.C)[(int64_t)(row0 + r) * p.ldc + j] = from_f<bf16>(silu_f(g) * u);
+        }
+      }
+  } else {
+#pragma unroll
+    for (int mb = 0; mb < 4; ++mb)
+#pragma unroll
+      for (int nb = 0; nb < 4; ++nb) {
+        const int col = tn * BN + wn * 128 + nb * 32 + lr;
+        if (col >= p.N) continue;
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
+          const int r = wm * 128 + mb * 32 + (e >> 2) * 8 + lh * 4 + (e & 3);
+          if (r >= rows) continue;
+          store_one<EPI>(p, row0 + r, col, acc[mb][nb][e]);
+        }
+      }
+  }
+}
+
+// ------------------------------------------------------------------ plain fp32 GEMM
+// 64 x 64 tiles, 256 threads, 4 x 4 outputs per thread.  Used by fp32 runs only.
+template <int EPI>
+__global__ __launch_bounds__(256) void gemm_f32_kernel(GemmParams p) {
+  __shared__ float As[16][64 + 1];
+  __shared__ float Bs[2][16][64 + 1];
+  const int tx = threadIdx.x & 15, ty = threadIdx.x >> 4;
+  const int m0 = blockIdx.y * 64;
+  const int nout = (EPI == EPI_SWIGLU) ? p.swiglu_I : p.N;
+  const int n0 = blockIdx.x * 64;
+  const float* A = (const float*)p.A;
+  const float* B = (const float*)p.B;
+  float acc[2][4][4] = {};
+  for (int k0 = 0; k0 < p.K; k0 += 16) {
+    for (int i = threadIdx.x; i < 16 * 64; i += 256) {
+      const int kk = i & 15, r = i >> 4;
+      const int m = m0 + r, k = k0 + kk;
+      int pm = m < p.M ? m : p.M - 1;
+      if (p.a_rows) pm = p.a_rows[pm];
+      As[kk][r] = (k < p.K) ? A[(int64_t)pm * p.lda + k] : 0.f;
+      const int n = n0 + r;
+      const bool nv = n < nout;
+      float b0 = 0.f, b1 = 0.f;
+      if (nv && k < p.K) {
+        if (EPI == EPI_SWIGLU) {
+          b0 = B[(int64_t)n * p.ldb + k];
+          b1 = B[(int64_t)(p.swiglu_I + n) * p.ldb + k];
+        } else if (p.bmode == 2) {
+          const int s = n / p.seg_rows;
+          b0 = ((const float*)p.Bs[s])[(int64_t)(n - s * p.seg_rows) * p.ldb + k];
+        } else {
+          b0 = B[(int64_t)n * p.ldb + k];
+        }
+      }
+      Bs[0][kk][r] = b0;
+      Bs[1][kk][r] = b1;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int kk = 0; kk < 16; ++kk) {
+      float a[4], b[4], b2[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) a[i] = As[kk][ty * 4 + i];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) { b[j] = Bs[0][kk][tx * 4 + j]; b2[j] = Bs[1][kk][tx * 4 + j]; }
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          acc[0][i][j] += a[i] * b[j];
+          if (EPI == EPI_SWIGLU) acc[1][i][j] += a[i] * b2[j];
+        }
+    }
+    __syncthreads();
+  }
+  for (int i = 0; i < 4; ++i)
+    for (int j = 0; j < 4; ++j) {
+      const int m = m0 + ty * 4 + i, n = n0 + tx * 4 + j;
+      if (m >= p.M || n >= nout) continue;
+      const float v = acc[0][i][j];
+      float* C = (float*)p.C;
+      if (EPI == EPI_STORE) C[(int64_t)m * p.ldc + n] = v;
+      else if (EPI == EPI_SCALED) C[(int64_t)m * p.ldc + n] = v * p.scale;
+      else if (EPI == EPI_RESID || EPI == EPI_RESID_TO_F32 || EPI == EPI_RESID_FROM_F32 || EPI == EPI_RESID_F32)
+        C[(int64_t)m * p.ldc + n] = ((const float*)p.R)[(int64_t)m * p.ldr + n] + v;
+      else if (EPI == EPI_SWIGLU) C[(int64_t)m * p.ldc + n] = silu_f(v) * acc[1][i][j];
+      else if (EPI == EPI_F32_IMG) {
+        const int img = m / p.rows_per, t = m - img * p.rows_per;
+        const int pw = p.img_W >> 5;
+        const int py = t / pw, px = t - py * pw;
+        const int c = n >> 10, iy = (n >> 5) & 31, ix = n & 31;
+        C[(((int64_t)img * 3 + c) * p.img_H + py * 32 + iy) * p.img_W + px * 32 + ix] = v;
+      } else if (EPI == EPI_BIAS_BCAST || EPI == EPI_BIAS_BCAST_F32) {
+        const int img = m / p.rows_per, t = m - img * p.rows_per;
+        const float x = v + p.bias[(int64_t)img * p.N + n];
+        for (int br = 0; br < p.n_bcast; ++br)
+          C[((int64_t)(img * p.n_bcast + br) * p.rows_per + t) * p.ldc + n] = x;
+      }
+    }
+}
+
+template <bool GROUPED, bool EXT>
+hipError_t launch_bf16(const GemmParams& p, int epi, int grid, int n_col_tiles, hipStream_t s) {
+  const size_t lds = 2 * STAGE_BYTES;
+#define PSF_L(E)                                                                                  \
+  case E: {                                                                                        \
+    auto k = gemm_bf16_kernel<E, GROUPED, EXT>;                                                    \
+    hipError_t e = hipFuncSetAttribute((const void*)k, hipFuncAttributeMaxDynamicSharedMemorySize, \
+                                       (int)lds);                                                  \
+    if (e != hipSuccess) return e;                                                                 \
+    hipLaunchKernelGGL(k, dim3(grid), dim3(NT), lds, s, p, n_col_tiles);                           \
+    return hipGetLastError();                                                                      \
+  }
+  switch (epi) {
+    PSF_L(EPI_STORE)
+    PSF_L(EPI_RESID)
+    PSF_L(EPI_SWIGLU)
+    PSF_L(EPI_F32_IMG)
+    PSF_L(EPI_BIAS_BCAST)
+    PSF_L(EPI_SCALED)
+    PSF_L(EPI_RESID_TO_F32)
+    PSF_L(EPI_RESID_FROM_F32)
+    PSF_L(EPI_RESID_F32)
+    PSF_L(EPI_BIAS_BCAST_F32)
+  }
+#undef PSF_L
+  return hipErrorInvalidValue;
+}
+
+}  // namespace
+
+hipError_t gemm_bf16(const GemmParams& p, int epi, hipStream_t s) {
+  if (p.M <= 0) return hipSuccess;
+  const int n_cols = (epi == EPI_SWIGLU) ? (p.swiglu_I + BN / 2 - 1) / (BN / 2) : (p.N + BN - 1) / BN;
+  const int n_m = (p.M + BM - 1) / BM;
+  if (p.X && p.xk > 0) return launch_bf16<false, true>(p, epi, n_m * n_cols, n_cols, s);
+  return launch_bf16<false, false>(p, epi, n_m * n_cols, n_cols, s);
+}
+
+hipError_t gemm_bf16_grouped(const GemmParams& p, int epi, int n_col_tiles, hipStream_t s) {
+  if (p.max_tiles <= 0) return hipSuccess;
+  return launch_bf16<true, false>(p, epi, p.max_tiles * n_col_tiles, n_col_tiles, s);
+}
+
+hipError_t gemm_f32(const GemmParams& p, int epi, hipStream_t s) {
+  if (p.M <= 0) return hipSuccess;
+  const int nout = (epi == EPI_SWIGLU) ? p.swiglu_I : p.N;
+  dim3 grid((nout + 63) / 64, (p.M + 63) / 64);
+#define PSF_F(E) \
+  case E: hipLaunchKernelGGL(gemm_f32_kernel<E>, grid, dim3(256), 0, s, p); return hipGetLastError();
+  switch (epi) {
+    PSF_F(EPI_STORE)
+    PSF_F(EPI_RESID)
+    PSF_F(EPI_SWIGLU)
+    PSF_F(EPI_F32_IMG)
+    PSF_F(EPI_BIAS_BCAST)
+    PSF_F(EPI_SCALED)
+    PSF_F(EPI_RESID_TO_F32)
+    PSF_F(EPI_RESID_FROM_F32)
+    PSF_F(EPI_RESID_F32)
+    PSF_F(EPI_BIAS_BCAST_F32)
+  }
+#undef PSF_F
+  return hipErrorInvalidValue;
+}
+
+}  // namespace psf

@@ -1,0 +1,73 @@
+// Host launchers of the gen-tower kernels (everything except the GEMMs).
+#pragma once
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime.h>
+#include "common.h"
+
+namespace psf {
+
+constexpr int MAXB = 32;  // sequences per block call (prefix pointers travel in kernel arguments)
+
+struct SeqInfo {
+  int B, N;                 // sequences, image tokens per sequence
+  int plen[MAXB];           // prefix tokens of each sequence
+  const void* pk[MAXB];     // prefix K [plen, Hkv, d]
+  const void* pv[MAXB];     // prefix V [plen, Hkv, d]
+};
+
+// y[r, :] = x[r, :] / sqrt(mean(x^2) + eps) * g   (x: Tin, g/y: T; D % (16/sizeof(Tin)) == 0)
+template <typename Tin, typename T>
+hipError_t rmsnorm(const Tin* x, const T* g, T* y, int rows, int D, float eps, hipStream_t s);
+
+// table[pos][j] = (cos(pos w_j), sin(pos w_j)), w_j = theta^(-2j/d), pos < n_pos (fp64 math, fp32 out)
+hipError_t rope_table(float2* table, int n_pos, int head_dim, float theta, hipStream_t s);
+
+// In place on the q and k heads of qkv [B*N, ld]: per-head RMSNorm (gain g_q / g_k) then
+// rotate-half RoPE at position plen[b] + n.
+template <typename T>
+hipError_t qknorm_rope(T* qkv, int64_t ld, const SeqInfo& si, int Hq, int Hkv, int d, const T* gq, const T* gk,
+                       const float2* table, float eps, hipStream_t s);
+
+// Pack keys and transposed values of every (sequence, kv head) contiguously:
+//   Kc[b][g][j][:] = j < P_b ? prefix K : (j < P_b + N ? k of token j - P_b : 0)     [B, Hkv, Lpad, d]
+//   Vt[b][g][:][j] = same for V, transposed                                          [B, Hkv, d, Lpad]
+template <typename T>
+hipError_t pack_kv(const T* qkv, int64_t ld, const SeqInfo& si, int Hq, int Hkv, int d, int Lpad, T* Kc, T* Vt,
+                   hipStream_t s);
+
+// O[b*N + n, h*d:(h+1)*d] = softmax(q k^T / sqrt(d)) v over the L_b = P_b + N keys of Kc/Vt.
+hipError_t attention_bf16(const bf16* qkv, int64_t ldq, const SeqInfo& si, int Hq, int Hkv, int d, int Lpad,
+                          const bf16* Kc, const bf16* Vt, bf16* O, int64_t ldo, hipStream_t s);
+hipError_t attention_f32(const float* qkv, int64_t ldq, const SeqInfo& si, int Hq, int Hkv, int d, int Lpad,
+                         const float* Kc, const float* Vt, float* O, int64_t ldo, hipStream_t s);
+
+// patches[(i*N + t), f] from x [n_img, 3, H, W] (32x32 patches, raster tokens, (c, iy, ix) features)
+template <typename T>
+hipError_t patchify(const float* x, T* patches, int n_img, int H, int W, hipStream_t s);
+
+// temb[i, :] = w2 silu(w1 feat(sigma_i)); feat = [cos(1000 sigma f_j), sin(1000 sigma f_j)], j < 128
+template <typename T>
+hipError_t timestep_embed(const float* sigma_dev, const T* w1, const T* w2, float* h1, float* temb, int n_img, int D,
+                          hipStream_t s);
+
+// xo = x + (sn - s) (x - x0g) / max(s, t_eps), x0g the CFG mix (xu may be null iff scale == 1);
+// xo may equal x.
+hipError_t cfg_euler(float* xo, const float* x, const float* xc, const float* xu, size_t n, float scale, float sigma,
+                     float sigma_next, float t_eps, hipStream_t s);
+
+// Router: idx/w [T, k]; u [T, D], wr [E, D]
+template <typename T>
+hipError_t moe_route(const T* u, const T* wr, int T_, int D, int E, int k, int* idx, float* w, hipStream_t s);
+
+// Counting sort of the T*k assignments by expert (stable in token order), tile table for the
+// grouped GEMM (BM-row tiles), and each assignment's position in the sorted order.
+hipError_t moe_sort(const int* idx, int T_, int k, int E, int* counts, int* offsets, int* perm_tok, int* pos_of,
+                    int* tiles, int max_tiles, int bm, hipStream_t s);
+
+// h[t, :] = bf16(r[t, :] + sum_j w[t, j] y[pos_of[t*k + j], :])   (fp32 residual r, fixed j order)
+template <typename TH>
+hipError_t moe_combine(TH* h, const float* r, const bf16* y, const float* w, const int* pos_of, int T_, int k, int D,
+                       hipStream_t s);
+
+}  // namespace psf

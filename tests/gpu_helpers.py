@@ -1,0 +1,67 @@
+"""Shared helpers of the GPU parity tests: move seeded numpy inputs to the device and
+compare GPU results with the oracle."""
+from __future__ import annotations
+
+import sys
+
+import numpy as np
+
+import workloads as W
+
+
+def log(msg: str):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+def dev(a: np.ndarray, dtype: str):
+    import torch
+    t = torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32))
+    t = t.to(torch.bfloat16) if dtype == "bf16" else t
+    return t.cuda()
+
+
+def host(t) -> np.ndarray:
+    import torch
+    return t.detach().float().cpu().numpy()
+
+
+def rms(x: np.ndarray) -> float:
+    return float(np.sqrt(np.mean(np.asarray(x, np.float64) ** 2)))
+
+
+def rel_max_err(got: np.ndarray, ref: np.ndarray) -> float:
+    """max |got - ref| / RMS(ref): the per-block parity metric."""
+    return float(np.max(np.abs(np.asarray(got, np.float64) - ref)) / max(rms(ref), 1e-30))
+
+
+def cosine(a: np.ndarray, b: np.ndarray) -> float:
+    a = np.asarray(a, np.float64).ravel()
+    b = np.asarray(b, np.float64).ravel()
+    return float(a @ b / (np.linalg.norm(a) * np.linalg.norm(b)))
+
+
+def bf16_faithful(got: np.ndarray, ref: np.ndarray, slack: float = 1.05) -> float:
+    """Largest |got - ref| in units of the bf16 rounding bound 2^-8 |ref| (plus 1e-4 RMS(ref)
+    for values near zero).  A bf16 result computed exactly and rounded once scores <= 1."""
+    ref = np.asarray(ref, np.float64)
+    bound = 2.0 ** -8 * np.abs(ref) + 1e-4 * rms(ref)
+    return float(np.max(np.abs(np.asarray(got, np.float64) - ref) / bound)) / slack
+
+
+BLOCK_TOL = 2e-2          # max abs error <= 2e-2 x RMS(reference) per block (bf16 runs)
+BLOCK_TOL_F32 = 1e-4      # fp32 runs: only summation order differs
+TOWER_COS = 0.999         # cosine similarity after the full tower
+
+
+def weights_to_dev(wts: dict, dtype: str) -> dict:
+    return {k: dev(v, dtype) for k, v in wts.items()}
+
+
+def block_inputs(w: W.Workload, layer: int, seed: int, dtype: str, hidden=None):
+    """Seeded block inputs: (numpy weights, numpy hidden, numpy prefix K/V lists)."""
+    wts = W.layer_weights(w, layer, seed, dtype)
+    h = W.block_hidden(w, seed, dtype) if hidden is None else hidden
+    slots = W.cache_slots(w, seed)
+    pk, pv = zip(*[W.prefix_kv(w, layer, s, seed, dtype) for s in slots])
+    return wts, h, list(pk), list(pv)

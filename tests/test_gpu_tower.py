@@ -1,0 +1,149 @@
+"""gen_tower_step on the GPU against the oracle's tower step: config 0 end to end over its
+2-step schedule (bf16 and fp32), and the full-width 2048^2 CFG tower (config 2) and 4-sample
+LoRA tower (config 3) at reduced depth with the last block and head checked on sampled tokens."""
+import os
+
+import numpy as np
+import pytest
+
+import oracle as O
+import workloads as W
+from gpu_helpers import BLOCK_TOL, TOWER_COS, cosine, dev, host, log, rel_max_err, weights_to_dev
+
+pytestmark = pytest.mark.gpu
+
+
+class GpuTower:
+    """Device copies of a workload's tower weights and prefixes (seeded) + the GPU step."""
+
+    def __init__(self, lib, w: W.Workload, dtype: str, seed: int = 0):
+        self.lib, self.w, self.dtype = lib, w, dtype
+        gdt = lib.GEN_BF16 if dtype == "bf16" else lib.GEN_F32
+        self.dims = lib.make_dims(w.dims, gdt)
+        self.np_glob = W.tower_globals(w, seed, dtype)
+        self.glob = weights_to_dev(self.np_glob, dtype)
+        self.np_layers, self.layers_dev, self.layers = [], [], []
+        for l in range(w.n_layers):
+            wts = W.layer_weights(w, l, seed, dtype)
+            self.np_layers.append(wts)
+            dv = weights_to_dev(wts, dtype)
+            self.layers_dev.append(dv)
+            self.layers.append(lib.make_weights(dv))
+        slots = W.cache_slots(w, seed)
+        self.np_pk = [[W.prefix_kv(w, l, s, seed, dtype)[0] for s in slots] for l in range(w.n_layers)]
+        self.np_pv = [[W.prefix_kv(w, l, s, seed, dtype)[1] for s in slots] for l in range(w.n_layers)]
+        self.pk = [dev(p, dtype) for layer in self.np_pk for p in layer]
+        self.pv = [dev(p, dtype) for layer in self.np_pv for p in layer]
+        self.plen = [w.prefix_len] * w.batch
+        self.ws = lib.alloc_workspace(lib.workspace_size(self.dims, w.n_img, w.n_br, w.n_tokens, w.prefix_len))
+
+    def step(self, x_np, sigma, sigma_next, cfg_scale):
+        import torch
+        w = self.w
+        x = torch.from_numpy(np.ascontiguousarray(x_np)).cuda()
+        xo = torch.empty_like(x)
+        x0 = torch.empty(w.batch, 3, w.height, w.width, device="cuda")
+        self.lib.tower_step(self.dims, self.layers, self.glob, x, w.n_br, sigma, sigma_next, cfg_scale, w.t_eps,
+                            self.pk, self.pv, self.plen, xo, self.ws, x0_out=x0)
+        torch.cuda.synchronize()
+        return host(xo), host(x0)
+
+    def oracle_tokens(self, x_np, sigma, rows=None):
+        w = self.w
+        return O.tower_tokens(x_np, sigma, self.np_glob, lambda l: self.np_layers[l], w.dims, w.n_layers, w.n_br,
+                              self.np_pk, self.np_pv, np.float32, rows=rows)
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_config0_two_step_denoise(lib, dtype):
+    w = W.CONFIGS[0]
+    t = GpuTower(lib, w, dtype)
+    sched = O.sigma_schedule(w.n_steps, w.shift)
+    x = W.noise_image(w)
+    cos_min = TOWER_COS if dtype == "bf16" else 0.99999
+    for k in range(w.n_steps):
+        log(f"config 0 {dtype} step {k}: sigma {sched[k]:.4f} -> {sched[k + 1]:.4f}")
+        xn, x0 = t.step(x, [sched[k]], [sched[k + 1]], w.cfg_scale)
+        rn, r0 = O.tower_step(x, k, sched, t.np_glob, lambda l: t.np_layers[l], w.dims, w.n_layers, w.n_br,
+                              t.np_pk, t.np_pv, w.cfg_scale, w.t_eps, np.float32)
+        cs = [cosine(x0[b], r0[b]) for b in range(w.batch)]
+        gg = O.cfg_mix(x0[0], x0[1], w.cfg_scale)
+        gr = O.cfg_mix(r0[0], r0[1], w.cfg_scale)
+        cg = cosine(gg, gr)
+        cd = cosine(xn - x, rn - x)
+        log(f"  cos x0 per branch {cs}, guided {cg:.6f}, dx {cd:.6f}")
+        assert min(cs) >= cos_min and cg >= cos_min and cd >= cos_min
+        x = xn
+    # the schedule ends at sigma = 0, where the update returns the guided prediction
+    np.testing.assert_allclose(x, O.cfg_mix(x0[0], x0[1], w.cfg_scale), rtol=1e-4, atol=1e-4)
+
+
+def test_config0_single_branch_cfg1(lib):
+    """cfg 1 runs one branch; the step must equal the Euler step on the cond prediction."""
+    w = W.scaled(W.CONFIGS[0], n_br=1, cfg_scale=1.0)
+    t = GpuTower(lib, w, "bf16")
+    x = W.noise_image(w)
+    xn, x0 = t.step(x, [0.75], [0.5], 1.0)
+    np.testing.assert_allclose(xn, O.euler_step(x, x0[0], 0.75, 0.5, w.t_eps), rtol=1e-5, atol=1e-5)
+    r = O.unpatchify(t.oracle_tokens(x, [0.75]), w.height, w.width)
+    assert cosine(x0, r) >= TOWER_COS
+
+
+def sampled_tower_check(lib, w, x, sigma, sigma_next, n_rows, seed_tag):
+    t = GpuTower(lib, w, "bf16")
+    xn, x0 = t.step(x, sigma, sigma_next, w.cfg_scale)
+    rows = np.sort(W.rng(w.config_id, 0, seed_tag).choice(w.n_tokens, n_rows, replace=False))
+    ref = t.oracle_tokens(x, sigma, rows=rows)
+    got = O.patchify(x0)[:, rows]
+    for b in range(w.batch):
+        c, e = cosine(got[b], ref[b]), rel_max_err(got[b], ref[b])
+        log(f"  sample {b}: cos {c:.6f}, max|err|/RMS {e:.3e}")
+        assert c >= TOWER_COS
+    return xn, x0, got, ref
+
+
+def test_config2_width_2048px_cfg_one_layer(lib):
+    """2048^2, 2 branches, cfg 4, step 0 of the 50-step schedule, at depth 1 (the depth only
+    repeats the same launches)."""
+    w = W.scaled(W.CONFIGS[2], n_layers=1)
+    sched = O.sigma_schedule(w.n_steps, w.shift)
+    x = W.noise_image(w)
+    log("config 2 at depth 1")
+    xn, x0, got, ref = sampled_tower_check(lib, w, x, [sched[0]], [sched[1]], 256, "rows")
+    # the Euler update is checked exactly on every pixel against the GPU's own x0
+    g = O.cfg_mix(x0[0], x0[1], w.cfg_scale)
+    np.testing.assert_allclose(xn[0], O.euler_step(x[0], g, sched[0], sched[1], w.t_eps), rtol=1e-5, atol=1e-5)
+
+
+def test_config3_lora_tower_x0_one_layer(lib):
+    """4 samples x 1024 tokens, each its own prefix from the 56-sample cache, LoRA r32, no CFG,
+    x0 output (sigma_next NULL)."""
+    import torch
+    w = W.scaled(W.CONFIGS[3], n_layers=1)
+    tt = W.train_timesteps(w)
+    x = O.noisy_sample(W.clean_image(w), W.noise_image(w), tt)
+    sig = [float(v) for v in tt]
+    t = GpuTower(lib, w, "bf16")
+    xd = torch.from_numpy(x).cuda()
+    xo = torch.empty_like(xd)
+    t.lib.tower_step(t.dims, t.layers, t.glob, xd, 1, sig, None, 1.0, w.t_eps, t.pk, t.pv, t.plen, xo, t.ws)
+    torch.cuda.synchronize()
+    rows = np.sort(W.rng(3, 0, "rows").choice(w.n_tokens, 256, replace=False))
+    ref = t.oracle_tokens(x, sig, rows=rows)
+    got = O.patchify(host(xo))[:, rows]
+    for b in range(w.n_img):
+        c = cosine(got[b], ref[b])
+        log(f"  sample {b} (t={sig[b]:.3f}): cos {c:.6f}")
+        assert c >= TOWER_COS
+
+
+@pytest.mark.slow
+@pytest.mark.skipif(os.environ.get("PSF_FULL_TOWER") != "1", reason="full 36-layer oracle run; set PSF_FULL_TOWER=1")
+def test_config2_full_tower_36_layers(lib):
+    """Full config 2: 36 layers, 2048^2, CFG 4, step 0.  The oracle runs the whole tower in fp32
+    on the host (minutes); the last block and the head are evaluated on 512 sampled tokens."""
+    w = W.CONFIGS[2]
+    sched = O.sigma_schedule(w.n_steps, w.shift)
+    x = W.noise_image(w)
+    log("config 2, 36 layers")
+    sampled_tower_check(lib, w, x, [sched[0]], [sched[1]], 512, "rows36")

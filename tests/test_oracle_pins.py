@@ -489,3 +489,13 @@ def test_prefix_cache_bytes_match_400_tokens_at_36_layers():
     d, w = W.CONFIGS[2].dims, W.CONFIGS[2]
     b = w.prefix_len * w.n_layers * d.n_kv_heads * d.head_dim * 2 * 2
     assert abs(b / 1e6 - 59.0) < 0.05
+
+
+def test_tower_tokens_rows_match_full():
+    w, d, glob, lw, pk, pv, x = tiny_tower(2)
+    full = O.tower_tokens(x, [0.7], glob, lambda l: lw[l], d, 2, 2, pk, pv, np.float64)
+    rows = np.array([1, 3])
+    sub = O.tower_tokens(x, [0.7], glob, lambda l: lw[l], d, 2, 2, pk, pv, np.float64, rows=rows)
+    np.testing.assert_allclose(sub, full[:, rows], rtol=1e-12, atol=1e-13)
+    np.testing.assert_allclose(O.unpatchify(full, 64, 64),
+                               O.tower_x0(x, [0.7], glob, lambda l: lw[l], d, 2, 2, pk, pv, np.float64), rtol=0)
