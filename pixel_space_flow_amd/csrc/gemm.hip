@@ -248,6 +248,318 @@ __global__ __launch_bounds__(NT, 1) void gemm_bf16_kernel(GemmParams p, int n_co
   }
 }
 
+// ------------------------------------------------------------------ fast path
+// Same tile, wave layout, LDS layout and epilogues as gemm_bf16_kernel, but the global->LDS
+// copy uses gfx950's buffer loads straight into LDS (16 bytes per lane): no staging VGPRs and
+// no ds_write instructions, which leaves registers for the MFMA fragments.  One load
+// instruction of a wave fills 8 consecutive LDS rows (1 KiB); lane l lands at base + 16 l,
+// i.e. row l/8, physical chunk l%8, so it fetches logical chunk (l%8) ^ (l/8) of its row and
+// the XOR swizzle comes out of the address arithmetic.  Buffer resources cover only the
+// tile's valid rows, so rows past M (or past N) read as zero.
+typedef __attribute__((address_space(3))) void* lds_ptr_t;
+
+DEVI __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
+}
+
+// 16 bytes per lane from a buffer straight into LDS at lds + 16*lane (kept out of the kernel
+// body: the builtin inside a kernel-local lambda stops clang from emitting the host stub).
+DEVI void dma16(__amdgpu_buffer_rsrc_t r, char* lds, uint32_t voff, uint32_t soff) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_ptr_t)lds, 16, voff, soff, 0, 0);
+}
+
+// Epilogue of 16 consecutive columns [col0, col0+16) of one output row.  Vector path when
+// all 16 columns are valid (col0 is a multiple of 16; leading dimensions are multiples of 8).
+template <int EPI>
+DEVI void epi_row16(const GemmParams& p, int row, int col0, int ncols, float* v) {
+  const bool full = col0 + 16 <= ncols;
+  if (EPI == EPI_F32_IMG) {
+    const int img = row / p.rows_per, t = row - img * p.rows_per;
+    const int pw = p.img_W >> 5;
+    const int py = t / pw, px = t - py * pw;
+    const int c = col0 >> 10, iy = (col0 >> 5) & 31, ix = col0 & 31;
+    float* out = (float*)p.C + (((int64_t)img * 3 + c) * p.img_H + py * 32 + iy) * p.img_W + px * 32 + ix;
+    if (full) {
+#pragma unroll
+      for (int q = 0; q < 4; ++q) *(float4*)(out + 4 * q) = make_float4(v[4 * q], v[4 * q + 1], v[4 * q + 2], v[4 * q + 3]);
+    } else {
+      for (int j = 0; j < 16 && col0 + j < ncols; ++j) out[j] = v[j];
+    }
+    return;
+  }
+  if (EPI == EPI_BIAS_BCAST || EPI == EPI_BIAS_BCAST_F32) {
+    const int img = row / p.rows_per, t = row - img * p.rows_per;
+    const float* bias = p.bias + (int64_t)img * p.N + col0;
+    for (int j = 0; j < 16; ++j) v[j] += (col0 + j < ncols) ? bias[j] : 0.f;
+    for (int br = 0; br < p.n_bcast; ++br) {
+      const int64_t o = ((int64_t)(img * p.n_bcast + br) * p.rows_per + t) * p.ldc + col0;
+      if (EPI == EPI_BIAS_BCAST_F32) {
+        float* C = (float*)p.C + o;
+        if (full) {
+#pragma unroll
+          for (int q = 0; q < 4; ++q) *(float4*)(C + 4 * q) = make_float4(v[4 * q], v[4 * q + 1], v[4 * q + 2], v[4 * q + 3]);
+        } else {
+          for (int j = 0; j < 16 && col0 + j < ncols; ++j) C[j] = v[j];
+        }
+      } else {
+        bf16* C = (bf16*)p.C + o;
+        if (full) {
+          bf16x8 a, b;
+#pragma unroll
+          for (int j = 0; j < 8; ++j) { a[j] = from_f<bf16>(v[j]); b[j] = from_f<bf16>(v[8 + j]); }
+          *(bf16x8*)C = a;
+          *(bf16x8*)(C + 8) = b;
+        } else {
+          for (int j = 0; j < 16 && col0 + j < ncols; ++j) C[j] = from_f<bf16>(v[j]);
+        }
+      }
+    }
+    return;
+  }
+  // residual input
+  if (EPI == EPI_RESID || EPI == EPI_RESID_TO_F32) {
+    const bf16* R = (const bf16*)p.R + (int64_t)row * p.ldr + col0;
+    if (full) {
+      const bf16x8 a = *(const bf16x8*)R, b = *(const bf16x8*)(R + 8);
+#pragma unroll
+      for (int j = 0; j < 8; ++j) { v[j] += static_cast<float>(a[j]); v[8 + j] += static_cast<float>(b[j]); }
+    } else {
+      for (int j = 0; j < 16 && col0 + j < ncols; ++j) v[j] += to_f(R[j]);
+    }
+  } else if (EPI == EPI_RESID_FROM_F32 || EPI == EPI_RESID_F32) {
+    const float* R = (const float*)p.R + (int64_t)row * p.ldr + col0;
+    if (full) {
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const float4 f = *(const float4*)(R + 4 * q);
+        v[4 * q] += f.x; v[4 * q + 1] += f.y; v[4 * q + 2] += f.z; v[4 * q + 3] += f.w;
+      }
+    } else {
+      for (int j = 0; j < 16 && col0 + j < ncols; ++j) v[j] += R[j];
+    }
+  } else if (EPI == EPI_SCALED) {
+#pragma unroll
+    for (int j = 0; j < 16; ++j) v[j] *= p.scale;
+  }
+  // output
+  if (EPI == EPI_RESID_TO_F32 || EPI == EPI_RESID_F32) {
+    float* C = (float*)p.C + (int64_t)row * p.ldc + col0;
+    if (full) {
+#pragma unroll
+      for (int q = 0; q < 4; ++q) *(float4*)(C + 4 * q) = make_float4(v[4 * q], v[4 * q + 1], v[4 * q + 2], v[4 * q + 3]);
+    } else {
+      for (int j = 0; j < 16 && col0 + j < ncols; ++j) C[j] = v[j];
+    }
+  } else {
+    bf16* C = (bf16*)p.C + (int64_t)row * p.ldc + col0;
+    if (full) {
+      bf16x8 a, b;
+#pragma unroll
+      for (int j = 0; j < 8; ++j) { a[j] = from_f<bf16>(v[j]); b[j] = from_f<bf16>(v[8 + j]); }
+      *(bf16x8*)C = a;
+      *(bf16x8*)(C + 8) = b;
+    } else {
+      for (int j = 0; j < 16 && col0 + j < ncols; ++j) C[j] = from_f<bf16>(v[j]);
+    }
+  }
+}
+
+template <int EPI, bool GROUPED, bool GATHER>
+__global__ __launch_bounds__(NT, 1) void gemm_fast_kernel(GemmParams p, int n_col_tiles) {
+  extern __shared__ __attribute__((aligned(16))) char smem[];
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wm = wave >> 1, wn = wave & 1;
+
+  int tn, row0, rows, expert = 0;
+  if (GROUPED) {
+    const int t = blockIdx.x / n_col_tiles;
+    tn = blockIdx.x - t * n_col_tiles;
+    expert = p.tiles[3 * t];
+    if (expert < 0) return;
+    row0 = p.tiles[3 * t + 1];
+    rows = p.tiles[3 * t + 2];
+  } else {
+    const int n_m = (p.M + BM - 1) / BM;
+    const int n_t = n_m * n_col_tiles;
+    const int id = xcd_remap(blockIdx.x, n_t);
+    const int GROUP = 8;
+    const int per_group = GROUP * n_col_tiles;
+    const int g = id / per_group;
+    const int first_m = g * GROUP;
+    const int gsz = min(n_m - first_m, GROUP);
+    const int r_in = id - g * per_group;
+    tn = r_in / gsz;
+    row0 = (first_m + r_in % gsz) * BM;
+    rows = min(BM, p.M - row0);
+  }
+  const int lrow = lane >> 3;                       // row within a group of 8
+  const int lch = (lane & 7) ^ (lane >> 3);         // logical 16-byte chunk this lane fetches
+  const uint32_t lda2 = (uint32_t)p.lda * 2, ldb2 = (uint32_t)p.ldb * 2;
+
+  // A operand
+  __amdgpu_buffer_rsrc_t ra;
+  uint32_t avoff[GATHER ? 8 : 1];
+  if (GATHER) {
+    ra = make_rsrc(p.A, 0x7fffffff);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int r = (wave * 8 + i) * 8 + lrow;
+      avoff[i] = (uint32_t)p.a_rows[row0 + min(r, rows - 1)] * lda2 + lch * 16;
+    }
+  } else {
+    ra = make_rsrc((const bf16*)p.A + (int64_t)row0 * p.lda, (uint32_t)rows * lda2);
+    avoff[0] = lrow * lda2 + lch * 16;
+  }
+  // B operand
+  const bf16* Bexp = (const bf16*)p.B + (GROUPED ? (int64_t)expert * p.b_expert_stride : 0);
+  __amdgpu_buffer_rsrc_t rb;
+  uint32_t bsoff[8];
+  if (p.bmode == 1) {
+    rb = make_rsrc(Bexp, (uint32_t)(2 * p.swiglu_I) * ldb2);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int r0 = (wave * 8 + i) * 8;
+      const int nb = r0 >> 5;
+      const int brow = ((nb & 1) ? p.swiglu_I : 0) + tn * (BN / 2) + (nb >> 1) * 32 + (r0 & 31);
+      bsoff[i] = (uint32_t)brow * ldb2;
+    }
+  } else {
+    const int nvalid = min(BN, p.N - tn * BN);
+    rb = make_rsrc(Bexp + (int64_t)tn * BN * p.ldb, (uint32_t)nvalid * ldb2);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) bsoff[i] = (uint32_t)((wave * 8 + i) * 8) * ldb2;
+  }
+  const uint32_t bvoff = lrow * ldb2 + lch * 16;
+
+  auto issue = [&](int kt, int stage) {
+    char* As = smem + stage * STAGE_BYTES;
+    char* Bs = As + BM * BK * 2;
+    const uint32_t kb = (uint32_t)kt * (BK * 2);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int grp = wave * 8 + i;
+      if (GATHER)
+        dma16(ra, As + grp * 1024, avoff[i], kb);
+      else
+        dma16(ra, As + grp * 1024, avoff[0], grp * 8 * lda2 + kb);
+      dma16(rb, Bs + grp * 1024, bvoff, bsoff[i] + kb);
+    }
+  };
+
+  f32x16 acc[4][4];
+#pragma unroll
+  for (int a = 0; a < 4; ++a)
+#pragma unroll
+    for (int b = 0; b < 4; ++b)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) acc[a][b][e] = 0.f;
+
+  const int KT = p.K / BK;
+  const int lr = lane & 31, lh = lane >> 5;
+  // LDS byte offsets of this lane's fragment rows (chunk XOR folded in per k-step below)
+  const int arow0 = (wm * 128 + lr) * (BK * 2), brow0 = (wn * 128 + lr) * (BK * 2);
+  const int sw = lr & 7;   // (row & 7) is the same for all 4 blocks: rows differ by multiples of 32
+
+  // Software pipeline.  Two register sets of fragments: the reads for k-step ks+1 are issued
+  // before the 16 MFMAs of step ks.  In the last step of a tile every wave waits for its
+  // outstanding LDS-DMA and LDS reads and meets the others at the barrier: the next tile's
+  // stage is then complete and this tile's stage is free, so the DMA of tile kt+2 goes out,
+  // the next tile's first fragments are read, and the last 16 MFMAs hide both.  The
+  // sched_barrier(0) fences keep the compiler from moving reads next to their MFMAs.
+  bf16x8 fa[2][4], fb[2][4];
+  auto rd = [&](int set, int stage, int ks) {
+    const char* As = smem + stage * STAGE_BYTES;
+    const char* Bs = As + BM * BK * 2;
+    const int ch = ((ks * 2 + lh) ^ sw) << 4;
+#pragma unroll
+    for (int mb = 0; mb < 4; ++mb) fa[set][mb] = *(const bf16x8*)(As + arow0 + mb * 32 * (BK * 2) + ch);
+#pragma unroll
+    for (int nb = 0; nb < 4; ++nb) fb[set][nb] = *(const bf16x8*)(Bs + brow0 + nb * 32 * (BK * 2) + ch);
+  };
+  auto mma = [&](int set) {
+#pragma unroll
+    for (int mb = 0; mb < 4; ++mb)
+#pragma unroll
+      for (int nb = 0; nb < 4; ++nb)
+        acc[mb][nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[set][mb], fb[set][nb], acc[mb][nb], 0, 0, 0);
+  };
+
+  issue(0, 0);
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+  if (KT > 1) issue(1, 1);
+  rd(0, 0, 0);
+  for (int kt = 0; kt < KT; ++kt) {
+    const int st = kt & 1;
+#pragma unroll
+    for (int ks = 0; ks < BK / 16; ++ks) {
+      const int cur = ks & 1;
+      if (ks + 1 < BK / 16) {
+        rd(cur ^ 1, st, ks + 1);
+      } else if (kt + 1 < KT) {
+        __builtin_amdgcn_s_waitcnt(0);
+        __syncthreads();
+        if (kt + 2 < KT) issue(kt + 2, st);
+        rd(cur ^ 1, st ^ 1, 0);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+      mma(cur);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  }
+
+  // ---- epilogue through LDS: each wave stages one 32x32 fp32 block at a time, then every lane
+  // owns 16 consecutive columns of one row (lanes 2r, 2r+1 cover row r), so global accesses are
+  // 16-byte vectors and the per-row index math runs once per block.
+  __syncthreads();   // every wave is done with the LDS stages
+  constexpr int TS = 36;                                   // padded fp32 row stride of a staged block
+  float* T0 = (float*)smem + wave * (2 * 32 * TS);
+  float* T1 = T0 + 32 * TS;
+  const int rr = lane >> 1, cc = (lane & 1) * 16;
+#pragma unroll
+  for (int mb = 0; mb < 4; ++mb) {
+#pragma unroll
+    for (int nb = 0; nb < 4; ++nb) {
+      if (EPI == EPI_SWIGLU && (nb & 1)) continue;       // consumed together with its gate block
+#pragma unroll
+      for (int e = 0; e < 16; ++e) T0[((e >> 2) * 8 + lh * 4 + (e & 3)) * TS + lr] = acc[mb][nb][e];
+      if (EPI == EPI_SWIGLU) {
+#pragma unroll
+        for (int e = 0; e < 16; ++e) T1[((e >> 2) * 8 + lh * 4 + (e & 3)) * TS + lr] = acc[mb][nb + 1][e];
+      }
+      __builtin_amdgcn_s_waitcnt(0xc07f);                   // lgkmcnt(0): staged values written
+      __builtin_amdgcn_wave_barrier();
+      float v[16];
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const float4 f = *(const float4*)(T0 + rr * TS + cc + 4 * q);
+        v[4 * q] = f.x; v[4 * q + 1] = f.y; v[4 * q + 2] = f.z; v[4 * q + 3] = f.w;
+      }
+      if (EPI == EPI_SWIGLU) {
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const float4 f = *(const float4*)(T1 + rr * TS + cc + 4 * q);
+          v[4 * q] = silu_f(v[4 * q]) * f.x;
+          v[4 * q + 1] = silu_f(v[4 * q + 1]) * f.y;
+          v[4 * q + 2] = silu_f(v[4 * q + 2]) * f.z;
+          v[4 * q + 3] = silu_f(v[4 * q + 3]) * f.w;
+        }
+      }
+      __builtin_amdgcn_s_waitcnt(0xc07f);                   // reads done before the next block overwrites
+      __builtin_amdgcn_wave_barrier();
+      const int r = wm * 128 + mb * 32 + rr;
+      if (r < rows) {
+        const int row = row0 + r;
+        const int col0 = (EPI == EPI_SWIGLU) ? tn * (BN / 2) + (wn * 2 + (nb >> 1)) * 32 + cc
+                                             : tn * BN + wn * 128 + nb * 32 + cc;
+        const int ncols = (EPI == EPI_SWIGLU) ? p.swiglu_I : p.N;
+        epi_row16<EPI>(p, row, col0, ncols, v);
+      }
+    }
+  }
+}
+
 // ------------------------------------------------------------------ plain fp32 GEMM
 // 64 x 64 tiles, 256 threads, 4 x 4 outputs per thread.  Used by fp32 runs only.
 template <int EPI>
@@ -329,6 +641,34 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(GemmParams p) {
     }
 }
 
+template <bool GROUPED, bool GATHER>
+hipError_t launch_fast(const GemmParams& p, int epi, int grid, int n_col_tiles, hipStream_t s) {
+  const size_t lds = 2 * STAGE_BYTES;
+#define PSF_L(E)                                                                                  \
+  case E: {                                                                                        \
+    auto k = gemm_fast_kernel<E, GROUPED, GATHER>;                                                 \
+    hipError_t e = hipFuncSetAttribute((const void*)k, hipFuncAttributeMaxDynamicSharedMemorySize, \
+                                       (int)lds);                                                  \
+    if (e != hipSuccess) return e;                                                                 \
+    hipLaunchKernelGGL(k, dim3(grid), dim3(NT), lds, s, p, n_col_tiles);                           \
+    return hipGetLastError();                                                                      \
+  }
+  switch (epi) {
+    PSF_L(EPI_STORE)
+    PSF_L(EPI_RESID)
+    PSF_L(EPI_SWIGLU)
+    PSF_L(EPI_F32_IMG)
+    PSF_L(EPI_BIAS_BCAST)
+    PSF_L(EPI_SCALED)
+    PSF_L(EPI_RESID_TO_F32)
+    PSF_L(EPI_RESID_FROM_F32)
+    PSF_L(EPI_RESID_F32)
+    PSF_L(EPI_BIAS_BCAST_F32)
+  }
+#undef PSF_L
+  return hipErrorInvalidValue;
+}
+
 template <bool GROUPED, bool EXT>
 hipError_t launch_bf16(const GemmParams& p, int epi, int grid, int n_col_tiles, hipStream_t s) {
   const size_t lds = 2 * STAGE_BYTES;
@@ -364,12 +704,15 @@ hipError_t gemm_bf16(const GemmParams& p, int epi, hipStream_t s) {
   const int n_cols = (epi == EPI_SWIGLU) ? (p.swiglu_I + BN / 2 - 1) / (BN / 2) : (p.N + BN - 1) / BN;
   const int n_m = (p.M + BM - 1) / BM;
   if (p.X && p.xk > 0) return launch_bf16<false, true>(p, epi, n_m * n_cols, n_cols, s);
-  return launch_bf16<false, false>(p, epi, n_m * n_cols, n_cols, s);
+  if (p.bmode == 2) return launch_bf16<false, false>(p, epi, n_m * n_cols, n_cols, s);
+  if (p.a_rows) return launch_fast<false, true>(p, epi, n_m * n_cols, n_cols, s);
+  return launch_fast<false, false>(p, epi, n_m * n_cols, n_cols, s);
 }
 
 hipError_t gemm_bf16_grouped(const GemmParams& p, int epi, int n_col_tiles, hipStream_t s) {
   if (p.max_tiles <= 0) return hipSuccess;
-  return launch_bf16<true, false>(p, epi, p.max_tiles * n_col_tiles, n_col_tiles, s);
+  if (p.a_rows) return launch_fast<true, true>(p, epi, p.max_tiles * n_col_tiles, n_col_tiles, s);
+  return launch_fast<true, false>(p, epi, p.max_tiles * n_col_tiles, n_col_tiles, s);
 }
 
 hipError_t gemm_f32(const GemmParams& p, int epi, hipStream_t s) {

@@ -75,7 +75,7 @@ def test_config0_two_step_denoise(lib, dtype):
         assert min(cs) >= cos_min and cg >= cos_min and cd >= cos_min
         x = xn
     # the schedule ends at sigma = 0, where the update returns the guided prediction
-    np.testing.assert_allclose(x, O.cfg_mix(x0[0], x0[1], w.cfg_scale), rtol=1e-4, atol=1e-4)
+    np.testing.assert_allclose(x[0], O.cfg_mix(x0[0], x0[1], w.cfg_scale), rtol=1e-4, atol=1e-4)
 
 
 def test_config0_single_branch_cfg1(lib):
