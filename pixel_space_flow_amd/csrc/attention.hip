@@ -18,6 +18,10 @@
 #include "common.h"
 #include "kernels.h"
 
+#ifndef ATTN_QB
+#define ATTN_QB 1
+#endif
+
 namespace psf {
 namespace {
 
@@ -175,6 +179,219 @@ __global__ __launch_bounds__(256, 2) void attn_bf16_kernel(const bf16* __restric
   }
 }
 
+// ------------------------------------------------------------------ v2
+// One workgroup = 4 waves x QB 32-query blocks of one q head.  K/V tiles of 64 keys come in by
+// LDS-DMA (buffer loads straight into LDS, double buffered, one barrier per tile).  Every K
+// fragment and V^T fragment read from LDS feeds QB MFMAs.  V^T is packed with the keys of each
+// 16-key group stored in the order [0-3, 8-11, 4-7, 12-15], which is exactly the order in which
+// the S^T accumulators hand P^T to the second MFMA, so each P.V fragment is one 16-byte read.
+// The running max is only moved when a tile's max exceeds it by more than 2^8 (in exp2 units):
+// probabilities stay below 256 and the final normalisation uses the same reference, so the
+// result is the plain softmax; most tiles skip the O rescale entirely.
+typedef __attribute__((address_space(3))) void* lds_ptr_t;
+
+DEVI __amdgpu_buffer_rsrc_t make_rsrc_a(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
+}
+DEVI void dma16_a(__amdgpu_buffer_rsrc_t r, char* lds, uint32_t voff, uint32_t soff) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_ptr_t)lds, 16, voff, soff, 0, 0);
+}
+
+template <int D, int QB>
+__global__ __launch_bounds__(256, QB == 1 ? 2 : 1) void attn_v2_kernel(const bf16* __restrict__ qkv, int64_t ldq,
+                                                                     SeqInfo si, int Hq, int Hkv, int Lpad,
+                                                                     const bf16* __restrict__ Kc,
+                                                                     const bf16* __restrict__ Vt, bf16* __restrict__ O,
+                                                                     int64_t ldo, float scale_log2, int n_qb) {
+  constexpr int KT = 64;                  // keys per tile
+  constexpr int KROW = D * 2;             // bytes per K row
+  constexpr int KCH = D / 8;              // 16-byte chunks per K row
+  constexpr int NDB = D / 32;
+  constexpr int STAGE = KT * KROW + D * KT * 2;
+  constexpr int QW = 32 * QB;             // queries per wave
+  constexpr float RESCALE_TH = 8.0f;
+  __shared__ __attribute__((aligned(16))) char smem[2 * STAGE];
+  // ds_read_b128 serves 16 lanes per cycle over a 256 B window: 256 B K rows (d = 128) swizzle
+  // chunks by (r & 15); 128 B rows (K at d = 64, V^T) pair up in a window and use ((r >> 1) & 7).
+  auto kswz = [](int r) { return D == 128 ? (r & 15) : ((r >> 1) & 7); };
+
+  const int G = Hq / Hkv;
+  const int total = si.B * Hkv * n_qb * G;
+  const int id = xcd_remap(blockIdx.x, total);
+  const int hh = id % G;
+  int rest = id / G;
+  const int qbk = rest % n_qb;
+  rest /= n_qb;
+  const int g = rest % Hkv;
+  const int b = rest / Hkv;
+  const int h = g * G + hh;
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int lr = lane & 31, lh = lane >> 5;
+  const int N = si.N;
+  const int L = si.plen[b] + N;
+  const int qbase = qbk * (4 * QW) + wave * QW;
+
+  bf16x8 qf[QB][D / 16];
+#pragma unroll
+  for (int qb = 0; qb < QB; ++qb) {
+    const int64_t tok = (int64_t)b * N + min(qbase + qb * 32 + lr, N - 1);
+    const bf16* qp = qkv + tok * ldq + (int64_t)h * D + lh * 8;
+#pragma unroll
+    for (int ks = 0; ks < D / 16; ++ks) qf[qb][ks] = *(const bf16x8*)(qp + ks * 16);
+  }
+  f32x16 o[QB][NDB];
+#pragma unroll
+  for (int qb = 0; qb < QB; ++qb)
+#pragma unroll
+    for (int i = 0; i < NDB; ++i)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) o[qb][i][e] = 0.f;
+  float m[QB], l[QB];
+#pragma unroll
+  for (int qb = 0; qb < QB; ++qb) { m[qb] = -INFINITY; l[qb] = 0.f; }
+
+  // DMA sources: K rows of this (b, g) and V^T rows, both with Lpad keys
+  const __amdgpu_buffer_rsrc_t rk = make_rsrc_a(Kc + ((int64_t)b * Hkv + g) * Lpad * D, (uint32_t)Lpad * KROW);
+  const __amdgpu_buffer_rsrc_t rv = make_rsrc_a(Vt + ((int64_t)b * Hkv + g) * D * Lpad, (uint32_t)D * Lpad * 2);
+  // K: one wave-load = 64 lanes x 16 B = (1024 / KROW) rows; lane -> row lane / KCH, chunk lane % KCH
+  constexpr int KRPL = 1024 / KROW;                 // K rows per wave-load
+  constexpr int KLOADS = KT / KRPL / 4;             // wave-loads per wave per tile (K)
+  const int krow_l = lane / KCH, kch_p = lane % KCH;
+  // V^T: rows of 128 B (64 keys); one wave-load = 8 rows; lane -> row lane/8, chunk lane%8
+  constexpr int VLOADS = D / 8 / 4;                 // wave-loads per wave per tile (V)
+  const int vrow_l = lane >> 3, vch_p = lane & 7;
+
+  auto issue = [&](int t, int stage) {
+    char* Ks = smem + stage * STAGE;
+    char* Vs = Ks + KT * KROW;
+#pragma unroll
+    for (int i = 0; i < KLOADS; ++i) {
+      const int r0 = (wave * KLOADS + i) * KRPL;
+      const int row = r0 + krow_l;
+      const int lch = kch_p ^ kswz(row);
+      dma16_a(rk, Ks + r0 * KROW, (uint32_t)(row * KROW + lch * 16), (uint32_t)t * KT * KROW);
+    }
+#pragma unroll
+    for (int i = 0; i < VLOADS; ++i) {
+      const int r0 = (wave * VLOADS + i) * 8;
+      const int row = r0 + vrow_l;
+      const int lch = vch_p ^ ((row >> 1) & 7);
+      dma16_a(rv, Vs + r0 * 128, (uint32_t)(row * Lpad * 2 + lch * 16), (uint32_t)t * KT * 2);
+    }
+  };
+
+  const int ntiles = (L + KT - 1) / KT;
+  issue(0, 0);
+  for (int t = 0; t < ntiles; ++t) {
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+    if (t + 1 < ntiles) issue(t + 1, (t + 1) & 1);
+    const char* Ks = smem + (t & 1) * STAGE;
+    const char* Vs = Ks + KT * KROW;
+    const int j0 = t * KT;
+
+    f32x16 sc[QB][2];
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb)
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) sc[qb][kb][e] = 0.f;
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+      const int r = kb * 32 + lr;
+#pragma unroll
+      for (int ks = 0; ks < D / 16; ++ks) {
+        const bf16x8 a = *(const bf16x8*)(Ks + r * KROW + (((ks * 2 + lh) ^ kswz(r)) << 4));
+#pragma unroll
+        for (int qb = 0; qb < QB; ++qb)
+          sc[qb][kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[qb][ks], sc[qb][kb], 0, 0, 0);
+      }
+    }
+    const bool tail = j0 + KT > L;
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb) {
+      if (tail) {
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+          for (int e = 0; e < 16; ++e) {
+            const int key = j0 + kb * 32 + (e >> 2) * 8 + lh * 4 + (e & 3);
+            if (key >= L) sc[qb][kb][e] = -INFINITY;
+          }
+      }
+      float mx = -INFINITY;
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) mx = fmaxf(mx, sc[qb][kb][e]);
+      mx = fmaxf(mx, __shfl_xor(mx, 32, 64)) * scale_log2;
+      const bool move = mx > m[qb] + RESCALE_TH;
+      if (__builtin_amdgcn_ballot_w64(move)) {          // wave-uniform: some query moves its max
+        const float mn = move ? mx : m[qb];
+        const float alpha = exp2f(m[qb] - mn);
+        m[qb] = mn;
+        l[qb] *= alpha;
+#pragma unroll
+        for (int i = 0; i < NDB; ++i)
+#pragma unroll
+          for (int e = 0; e < 16; ++e) o[qb][i][e] *= alpha;
+      }
+      const float nm = -m[qb];
+      float rs = 0.f;
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
+          const float pv = exp2f(fmaf(sc[qb][kb][e], scale_log2, nm));
+          sc[qb][kb][e] = pv;
+          rs += pv;
+        }
+      l[qb] += rs;
+    }
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int st = 0; st < 2; ++st) {
+        bf16x8 pb[QB];
+#pragma unroll
+        for (int qb = 0; qb < QB; ++qb)
+#pragma unroll
+          for (int e = 0; e < 8; ++e) pb[qb][e] = static_cast<bf16>(sc[qb][kb][st * 8 + e]);
+        const int ch = kb * 4 + st * 2 + lh;            // 16-byte chunk of keys in permuted order
+#pragma unroll
+        for (int db = 0; db < NDB; ++db) {
+          const int r = db * 32 + lr;
+          const bf16x8 av = *(const bf16x8*)(Vs + r * 128 + ((ch ^ ((r >> 1) & 7)) << 4));
+#pragma unroll
+          for (int qb = 0; qb < QB; ++qb)
+            o[qb][db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, pb[qb], o[qb][db], 0, 0, 0);
+        }
+      }
+  }
+
+#pragma unroll
+  for (int qb = 0; qb < QB; ++qb) {
+    const float lt = l[qb] + __shfl_xor(l[qb], 32, 64);
+    const float inv = 1.0f / lt;
+    const int query = qbase + qb * 32 + lr;
+    if (query < N) {
+      bf16* op = O + ((int64_t)b * N + query) * ldo + (int64_t)h * D;
+#pragma unroll
+      for (int db = 0; db < NDB; ++db)
+#pragma unroll
+        for (int e4 = 0; e4 < 4; ++e4) {
+          bf16x4 v;
+#pragma unroll
+          for (int i = 0; i < 4; ++i) v[i] = static_cast<bf16>(o[qb][db][e4 * 4 + i] * inv);
+          *(bf16x4*)(op + db * 32 + e4 * 8 + lh * 4) = v;
+        }
+    }
+  }
+}
+
 // fp32 path (small problems): one thread per (query, head), online softmax over all keys.
 template <int D>
 __global__ __launch_bounds__(128) void attn_f32_kernel(const float* __restrict__ qkv, int64_t ldq, SeqInfo si, int Hq,
@@ -217,12 +434,17 @@ hipError_t attention_bf16(const bf16* qkv, int64_t ldq, const SeqInfo& si, int H
   const int total = si.B * Hkv * n_qb * (Hq / Hkv);
   if (total == 0) return hipSuccess;
   const float scale_log2 = 1.4426950408889634f / sqrtf((float)d);
+  // 4 waves x ATTN_QB*32 queries per workgroup
+  constexpr int QB = ATTN_QB;
+  const int n_qb2 = (si.N + 128 * QB - 1) / (128 * QB);
+  const int total2 = si.B * Hkv * n_qb2 * (Hq / Hkv);
   if (d == 128)
-    hipLaunchKernelGGL(attn_bf16_kernel<128>, dim3(total), dim3(256), 0, s, qkv, ldq, si, Hq, Hkv, Lpad, Kc, Vt, O, ldo, scale_log2, n_qb);
+    hipLaunchKernelGGL((attn_v2_kernel<128, QB>), dim3(total2), dim3(256), 0, s, qkv, ldq, si, Hq, Hkv, Lpad, Kc, Vt, O, ldo, scale_log2, n_qb2);
   else if (d == 64)
-    hipLaunchKernelGGL(attn_bf16_kernel<64>, dim3(total), dim3(256), 0, s, qkv, ldq, si, Hq, Hkv, Lpad, Kc, Vt, O, ldo, scale_log2, n_qb);
+    hipLaunchKernelGGL((attn_v2_kernel<64, QB>), dim3(total2), dim3(256), 0, s, qkv, ldq, si, Hq, Hkv, Lpad, Kc, Vt, O, ldo, scale_log2, n_qb2);
   else
     return hipErrorInvalidValue;
+  (void)total;
   return hipGetLastError();
 }
 

@@ -182,7 +182,10 @@ __global__ __launch_bounds__(256) void pack_vt_kernel(const T* __restrict__ qkv,
   float f[V::N];
 #pragma unroll
   for (int e = 0; e < V::N; ++e) {
-    const int j = j0 + e;
+    // bf16 V^T stores each 16-key group as keys [0-3, 8-11, 4-7, 12-15]: the order in which the
+    // attention kernel's P^T fragments arrive.  fp32 V^T keeps the natural order.
+    const int pos = j0 + e;
+    const int j = sizeof(T) == 2 ? (pos & ~15) | (((pos >> 2) & 1) << 3) | (((pos >> 3) & 1) << 2) | (pos & 3) : pos;
     float v = 0.f;
     if (j < P) v = to_f(((const T*)si.pv[b])[((int64_t)j * Hkv + g) * d + dd]);
     else if (j < P + si.N) v = to_f(qkv[((int64_t)b * si.N + j - P) * ld + (int64_t)(Hq + Hkv + g) * d + dd]);

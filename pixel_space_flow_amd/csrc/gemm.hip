@@ -9,6 +9,7 @@
 // (8 rows per LDS cycle) and chunk writes are bank-conflict free.
 #include "common.h"
 #include "gemm.h"
+#include <cstdlib>
 
 namespace psf {
 namespace {
@@ -364,12 +365,17 @@ DEVI void epi_row16(const GemmParams& p, int row, int col0, int ncols, float* v)
   }
 }
 
-template <int EPI, bool GROUPED, bool GATHER>
-__global__ __launch_bounds__(NT, 1) void gemm_fast_kernel(GemmParams p, int n_col_tiles) {
+template <int EPI, bool GROUPED, bool GATHER, int NW>
+__global__ __launch_bounds__(64 * NW, 1) void gemm_fast_kernel(GemmParams p, int n_col_tiles) {
+  // NW = 4: 2 x 2 waves of 128 x 128 (one wave per SIMD); NW = 8: 2 x 4 waves of 128 x 64 (two
+  // waves per SIMD, so one wave's DMA issue or barrier wait is covered by the other's MFMAs).
+  constexpr int WN = NW / 2;                 // waves along n
+  constexpr int NBW = (BN / WN) / 32;        // 32-column MFMA blocks per wave (4 or 2)
+  constexpr int GPW = 32 / NW;               // 8-row load groups per wave per operand
   extern __shared__ __attribute__((aligned(16))) char smem[];
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int wm = wave >> 1, wn = wave & 1;
+  const int wm = wave / WN, wn = wave % WN;
 
   int tn, row0, rows, expert = 0;
   if (GROUPED) {
@@ -393,33 +399,39 @@ __global__ __launch_bounds__(NT, 1) void gemm_fast_kernel(GemmParams p, int n_co
     row0 = (first_m + r_in % gsz) * BM;
     rows = min(BM, p.M - row0);
   }
+  // LDS rows are 128 B; ds_read_b128 serves 16 lanes per cycle over a 256 B (64-bank) window, so a
+  // row pair shares a window and chunk c of row r sits at c ^ ((r >> 1) & 7): the 16 rows read
+  // together land on 16 distinct (half, chunk) slots.  A group of 8 rows starting at a multiple of
+  // 8 has ((r >> 1) & 7) = 4 (g & 1) + (lrow >> 1) for group index g.
   const int lrow = lane >> 3;                       // row within a group of 8
-  const int lch = (lane & 7) ^ (lane >> 3);         // logical 16-byte chunk this lane fetches
+  const int lch0 = (lane & 7) ^ (lrow >> 1);        // logical chunk fetched, even groups
+  const int lch1 = (lane & 7) ^ (4 + (lrow >> 1));  // odd groups
   const uint32_t lda2 = (uint32_t)p.lda * 2, ldb2 = (uint32_t)p.ldb * 2;
 
   // A operand
   __amdgpu_buffer_rsrc_t ra;
-  uint32_t avoff[GATHER ? 8 : 1];
+  uint32_t avoff[GATHER ? GPW : 2];
   if (GATHER) {
     ra = make_rsrc(p.A, 0x7fffffff);
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const int r = (wave * 8 + i) * 8 + lrow;
-      avoff[i] = (uint32_t)p.a_rows[row0 + min(r, rows - 1)] * lda2 + lch * 16;
+    for (int i = 0; i < GPW; ++i) {
+      const int r = (wave * GPW + i) * 8 + lrow;
+      avoff[i] = (uint32_t)p.a_rows[row0 + min(r, rows - 1)] * lda2 + (((wave * GPW + i) & 1) ? lch1 : lch0) * 16;
     }
   } else {
     ra = make_rsrc((const bf16*)p.A + (int64_t)row0 * p.lda, (uint32_t)rows * lda2);
-    avoff[0] = lrow * lda2 + lch * 16;
+    avoff[0] = lrow * lda2 + lch0 * 16;
+    avoff[1] = lrow * lda2 + lch1 * 16;
   }
   // B operand
   const bf16* Bexp = (const bf16*)p.B + (GROUPED ? (int64_t)expert * p.b_expert_stride : 0);
   __amdgpu_buffer_rsrc_t rb;
-  uint32_t bsoff[8];
+  uint32_t bsoff[GPW];
   if (p.bmode == 1) {
     rb = make_rsrc(Bexp, (uint32_t)(2 * p.swiglu_I) * ldb2);
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const int r0 = (wave * 8 + i) * 8;
+    for (int i = 0; i < GPW; ++i) {
+      const int r0 = (wave * GPW + i) * 8;
       const int nb = r0 >> 5;
       const int brow = ((nb & 1) ? p.swiglu_I : 0) + tn * (BN / 2) + (nb >> 1) * 32 + (r0 & 31);
       bsoff[i] = (uint32_t)brow * ldb2;
@@ -428,38 +440,38 @@ __global__ __launch_bounds__(NT, 1) void gemm_fast_kernel(GemmParams p, int n_co
     const int nvalid = min(BN, p.N - tn * BN);
     rb = make_rsrc(Bexp + (int64_t)tn * BN * p.ldb, (uint32_t)nvalid * ldb2);
 #pragma unroll
-    for (int i = 0; i < 8; ++i) bsoff[i] = (uint32_t)((wave * 8 + i) * 8) * ldb2;
+    for (int i = 0; i < GPW; ++i) bsoff[i] = (uint32_t)((wave * GPW + i) * 8) * ldb2;
   }
-  const uint32_t bvoff = lrow * ldb2 + lch * 16;
+  const uint32_t bvoff0 = lrow * ldb2 + lch0 * 16, bvoff1 = lrow * ldb2 + lch1 * 16;
 
   auto issue = [&](int kt, int stage) {
     char* As = smem + stage * STAGE_BYTES;
     char* Bs = As + BM * BK * 2;
     const uint32_t kb = (uint32_t)kt * (BK * 2);
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const int grp = wave * 8 + i;
+    for (int i = 0; i < GPW; ++i) {
+      const int grp = wave * GPW + i;
       if (GATHER)
         dma16(ra, As + grp * 1024, avoff[i], kb);
       else
-        dma16(ra, As + grp * 1024, avoff[0], grp * 8 * lda2 + kb);
-      dma16(rb, Bs + grp * 1024, bvoff, bsoff[i] + kb);
+        dma16(ra, As + grp * 1024, avoff[i & 1], grp * 8 * lda2 + kb);
+      dma16(rb, Bs + grp * 1024, (i & 1) ? bvoff1 : bvoff0, bsoff[i] + kb);
     }
   };
 
-  f32x16 acc[4][4];
+  f32x16 acc[4][NBW];
 #pragma unroll
   for (int a = 0; a < 4; ++a)
 #pragma unroll
-    for (int b = 0; b < 4; ++b)
+    for (int b = 0; b < NBW; ++b)
 #pragma unroll
       for (int e = 0; e < 16; ++e) acc[a][b][e] = 0.f;
 
   const int KT = p.K / BK;
   const int lr = lane & 31, lh = lane >> 5;
   // LDS byte offsets of this lane's fragment rows (chunk XOR folded in per k-step below)
-  const int arow0 = (wm * 128 + lr) * (BK * 2), brow0 = (wn * 128 + lr) * (BK * 2);
-  const int sw = lr & 7;   // (row & 7) is the same for all 4 blocks: rows differ by multiples of 32
+  const int arow0 = (wm * 128 + lr) * (BK * 2), brow0 = (wn * (BN / WN) + lr) * (BK * 2);
+  const int sw = (lr >> 1) & 7;   // the same for all 4 blocks: their rows differ by multiples of 32
 
   // Software pipeline.  Two register sets of fragments: the reads for k-step ks+1 are issued
   // before the 16 MFMAs of step ks.  In the last step of a tile every wave waits for its
@@ -467,7 +479,7 @@ __global__ __launch_bounds__(NT, 1) void gemm_fast_kernel(GemmParams p, int n_co
   // stage is then complete and this tile's stage is free, so the DMA of tile kt+2 goes out,
   // the next tile's first fragments are read, and the last 16 MFMAs hide both.  The
   // sched_barrier(0) fences keep the compiler from moving reads next to their MFMAs.
-  bf16x8 fa[2][4], fb[2][4];
+  bf16x8 fa[2][4], fb[2][NBW];
   auto rd = [&](int set, int stage, int ks) {
     const char* As = smem + stage * STAGE_BYTES;
     const char* Bs = As + BM * BK * 2;
@@ -475,13 +487,13 @@ __global__ __launch_bounds__(NT, 1) void gemm_fast_kernel(GemmParams p, int n_co
 #pragma unroll
     for (int mb = 0; mb < 4; ++mb) fa[set][mb] = *(const bf16x8*)(As + arow0 + mb * 32 * (BK * 2) + ch);
 #pragma unroll
-    for (int nb = 0; nb < 4; ++nb) fb[set][nb] = *(const bf16x8*)(Bs + brow0 + nb * 32 * (BK * 2) + ch);
+    for (int nb = 0; nb < NBW; ++nb) fb[set][nb] = *(const bf16x8*)(Bs + brow0 + nb * 32 * (BK * 2) + ch);
   };
   auto mma = [&](int set) {
 #pragma unroll
     for (int mb = 0; mb < 4; ++mb)
 #pragma unroll
-      for (int nb = 0; nb < 4; ++nb)
+      for (int nb = 0; nb < NBW; ++nb)
         acc[mb][nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[set][mb], fb[set][nb], acc[mb][nb], 0, 0, 0);
   };
 
@@ -520,7 +532,7 @@ __global__ __launch_bounds__(NT, 1) void gemm_fast_kernel(GemmParams p, int n_co
 #pragma unroll
   for (int mb = 0; mb < 4; ++mb) {
 #pragma unroll
-    for (int nb = 0; nb < 4; ++nb) {
+    for (int nb = 0; nb < NBW; ++nb) {
       if (EPI == EPI_SWIGLU && (nb & 1)) continue;       // consumed together with its gate block
 #pragma unroll
       for (int e = 0; e < 16; ++e) T0[((e >> 2) * 8 + lh * 4 + (e & 3)) * TS + lr] = acc[mb][nb][e];
@@ -551,8 +563,8 @@ __global__ __launch_bounds__(NT, 1) void gemm_fast_kernel(GemmParams p, int n_co
       const int r = wm * 128 + mb * 32 + rr;
       if (r < rows) {
         const int row = row0 + r;
-        const int col0 = (EPI == EPI_SWIGLU) ? tn * (BN / 2) + (wn * 2 + (nb >> 1)) * 32 + cc
-                                             : tn * BN + wn * 128 + nb * 32 + cc;
+        const int col0 = (EPI == EPI_SWIGLU) ? tn * (BN / 2) + (wn * (NBW / 2) + (nb >> 1)) * 32 + cc
+                                             : tn * BN + wn * (BN / WN) + nb * 32 + cc;
         const int ncols = (EPI == EPI_SWIGLU) ? p.swiglu_I : p.N;
         epi_row16<EPI>(p, row, col0, ncols, v);
       }
@@ -641,16 +653,26 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(GemmParams p) {
     }
 }
 
+// 8 waves (two per SIMD) by default; PSF_GEMM_WAVES=4 selects one wave per SIMD with 128 x 128
+// wave tiles (kept for comparison runs).
+int fast_waves() {
+  static const int w = [] {
+    const char* e = getenv("PSF_GEMM_WAVES");
+    return (e && atoi(e) == 4) ? 4 : 8;
+  }();
+  return w;
+}
+
 template <bool GROUPED, bool GATHER>
 hipError_t launch_fast(const GemmParams& p, int epi, int grid, int n_col_tiles, hipStream_t s) {
   const size_t lds = 2 * STAGE_BYTES;
 #define PSF_L(E)                                                                                  \
   case E: {                                                                                        \
-    auto k = gemm_fast_kernel<E, GROUPED, GATHER>;                                                 \
+    auto k = fast_waves() == 4 ? gemm_fast_kernel<E, GROUPED, GATHER, 4> : gemm_fast_kernel<E, GROUPED, GATHER, 8>; \
     hipError_t e = hipFuncSetAttribute((const void*)k, hipFuncAttributeMaxDynamicSharedMemorySize, \
                                        (int)lds);                                                  \
     if (e != hipSuccess) return e;                                                                 \
-    hipLaunchKernelGGL(k, dim3(grid), dim3(NT), lds, s, p, n_col_tiles);                           \
+    hipLaunchKernelGGL(k, dim3(grid), dim3(64 * fast_waves()), lds, s, p, n_col_tiles);            \
     return hipGetLastError();                                                                      \
   }
   switch (epi) {

@@ -139,17 +139,31 @@ def test_lora_block_sampled_rows(lib):
     rows = np.sort(W.rng(3, 0, "rows").choice(w.n_tokens, 256, replace=False))
     ref = O.gen_block(h, wts, w.dims, pk, pv, rows=rows)
     check(got[:, rows], ref, h[:, rows], BLOCK_TOL, "LoRA block")
-    # the LoRA delta itself must be reproduced, not just drowned by the base output
-    base_d = W.BlockDims(**{**W.dataclasses.asdict(w.dims), "lora_rank": 0, "lora_alpha": 0.0})
-    base = O.gen_block(h, {k: v for k, v in wts.items() if not k.startswith("lora")}, base_d, pk, pv, rows=rows)
-    dl_ref = ref - base
-    gbase = run_gpu_block(lib, W.scaled(w, dims=base_d), {k: v for k, v in wts.items() if not k.startswith("lora")},
-                          h, pk, pv, "bf16")
-    dl_got = got[:, rows] - gbase[:, rows]
+
+
+def test_lora_strong_adapter_delta(lib):
+    """With config 3's B ~ N(0, 1e-3) the LoRA delta is below the base path's bf16 noise, so the
+    adapter path is pinned separately with B ~ N(0, 0.05): the GPU's (LoRA - no LoRA) delta must
+    match the oracle's."""
     from gpu_helpers import cosine
-    c = cosine(dl_got, dl_ref)
-    log(f"  LoRA delta cosine {c:.5f}, RMS delta {rms(dl_ref):.3e}")
-    assert c > 0.95
+    w, wts, h, pk, pv = lora_case()
+    h = h[:2, :512]
+    w = W.scaled(w, n_img=2, height=512, width=1024)
+    pk, pv = pk[:2], pv[:2]
+    strong = dict(wts)
+    for s in W.LORA_SITES:
+        strong[f"lora_b_{s}"] = W.maybe_bf16(W.normal(3, 0, f"strong_b_{s}", wts[f"lora_b_{s}"].shape, 0.05), "bf16")
+    base_d = W.BlockDims(**{**W.dataclasses.asdict(w.dims), "lora_rank": 0, "lora_alpha": 0.0})
+    base_w = {k: v for k, v in wts.items() if not k.startswith("lora")}
+    got = run_gpu_block(lib, w, strong, h, pk, pv, "bf16")
+    gbase = run_gpu_block(lib, W.scaled(w, dims=base_d), base_w, h, pk, pv, "bf16")
+    rows = np.arange(0, 512, 7)
+    ref = O.gen_block(h, strong, w.dims, pk, pv, rows=rows)
+    base = O.gen_block(h, base_w, base_d, pk, pv, rows=rows)
+    check(got[:, rows], ref, h[:, rows], BLOCK_TOL, "strong LoRA block")
+    c = cosine(got[:, rows] - gbase[:, rows], ref - base)
+    log(f"  LoRA delta cosine {c:.5f}, RMS delta {rms(ref - base):.3e} vs RMS(y) {rms(ref):.3f}")
+    assert c > 0.999
 
 
 def test_lora_zero_up_is_bitwise_base(lib):

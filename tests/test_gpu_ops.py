@@ -128,8 +128,13 @@ def test_attention(lib, dtype, d, Hq, Hkv, N, plen):
         ref = O.attention(xr[b, :, :Hq], K, V)
         err = rel_max_err(got[b], ref)
         if dtype == "bf16":
-            # bf16 output rounding (2^-8 |ref|) plus the bf16 rounding of P ahead of the P.V MFMA
-            bound = 2.0 ** -8 * np.abs(ref) + 1e-2 * np.sqrt(np.mean(ref.astype(np.float64) ** 2))
+            # Rounding P to bf16 ahead of the P.V product perturbs each weight by at most 2^-9 of
+            # itself, so an output element moves by at most 2^-9 sum_j a_j |v_j| (the same attention
+            # applied to |V|); the output itself is rounded once (2^-8 |ref|).  Slack 1e-3 RMS covers
+            # fp32 summation order.
+            pv_bound = O.attention(xr[b, :, :Hq], K, np.abs(V))
+            bound = (2.0 ** -8 * np.abs(ref) + 2.0 ** -9 * pv_bound
+                     + 1e-3 * np.sqrt(np.mean(ref.astype(np.float64) ** 2)))
             worst = float(np.max(np.abs(got[b] - ref) / bound))
             log(f"  b={b} err={err:.3e} worst/bound={worst:.3f}")
             assert worst <= 1.0
