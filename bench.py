@@ -28,6 +28,30 @@ sys.path.insert(0, ROOT)
 
 PEAK_BF16_TFLOPS = 2516.6     # MI355X dense bf16 MFMA: 256 CU x 2.4 GHz x 4096 FLOP/clk
 PEAK_HBM_GBS = 8000.0
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "gate_up_gemm_2048px_tower.traffic.json")
+GEMM_SOURCES = ("pixel_space_flow_amd/csrc/gemm.hip", "pixel_space_flow_amd/csrc/gemm.h",
+                "pixel_space_flow_amd/csrc/common.h")
+
+
+def gemm_source_hash() -> str:
+    import hashlib
+    h = hashlib.sha256()
+    for f in GEMM_SOURCES:
+        h.update(open(os.path.join(ROOT, f), "rb").read())
+    return h.hexdigest()
+
+
+def measured_traffic():
+    """HBM-side bytes per launch of the gate/up GEMM from the committed rocprofv3 FETCH_SIZE /
+    WRITE_SIZE runs (each scaled by the same counter's reading for a copy of known size), or
+    None when the GEMM sources changed after the counters were taken."""
+    try:
+        t = json.load(open(TRAFFIC_FILE))
+    except (OSError, ValueError):
+        return None
+    if t.get("source_sha256") != gemm_source_hash():
+        return None
+    return int((t["fetch_kib"] * t["fetch_scale"] + t["write_kib"] * t["write_scale"]) * 1024)
 
 
 def step_flops(w) -> dict:
@@ -117,6 +141,39 @@ def cpu_baseline(w, seed=0):
             "host": platform.processor() or platform.machine(), "numpy": np.__version__}
 
 
+def run_kernel_only(psf, w, which: str, reps: int):
+    """One kernel family of the step at the workload's shapes, `reps` launches (rocprofv3 counter
+    runs); "copy" is a plain 256 MiB device copy used to calibrate the byte counters."""
+    import torch
+    d = w.dims
+    M, D, I = w.batch * w.n_tokens, d.hidden, d.mlp_intermediate
+    bf = torch.bfloat16
+    g = torch.Generator(device="cuda")
+    g.manual_seed(0)
+    if which == "gate_up":
+        x = torch.randn(M, D, device="cuda", generator=g).to(bf)
+        wt = (0.02 * torch.randn(2 * I, D, device="cuda", generator=g)).to(bf)
+        y = torch.empty(M, I, device="cuda", dtype=bf)
+        for _ in range(reps):
+            psf.op_linear(x, wt, y, None, 2)
+    elif which == "attention":
+        Hq, Hkv, hd, P, N = d.n_q_heads, d.n_kv_heads, d.head_dim, w.prefix_len, w.n_tokens
+        qkv = torch.randn(M, (Hq + 2 * Hkv) * hd, device="cuda", generator=g).to(bf)
+        pk = [torch.randn(P, Hkv, hd, device="cuda", generator=g).to(bf) for _ in range(w.batch)]
+        pv = [torch.randn(P, Hkv, hd, device="cuda", generator=g).to(bf) for _ in range(w.batch)]
+        out = torch.empty(M, Hq * hd, device="cuda", dtype=bf)
+        ws = torch.empty(psf.op_workspace_size(w.batch, N, Hkv, hd, P, psf.GEN_BF16), dtype=torch.uint8, device="cuda")
+        for _ in range(reps):
+            psf.op_attention(qkv, w.batch, N, Hq, Hkv, hd, pk, pv, [P] * w.batch, out, ws)
+    else:
+        a = torch.randn(64 * 1024 * 1024, device="cuda", generator=g)    # 256 MiB
+        b = torch.empty_like(a)
+        for _ in range(reps):
+            b.copy_(a)
+    torch.cuda.synchronize()
+    print(json.dumps({"kernel": which, "launches": reps, "workload": w.name}), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -124,6 +181,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--config", type=int, default=2)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--kernel", choices=("gate_up", "attention", "copy"),
+                    help="run only this kernel at the workload's shapes, --steps times (for counter runs)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU: this build has no multi-GPU path (asked for --gpus {args.gpus}). "
@@ -137,6 +196,9 @@ def main():
     w = W.CONFIGS[args.config]
     assert w.unit == "tower" and not w.dims.is_moe and not w.dims.lora_rank, "bench times the dense CFG tower step"
     torch.cuda.set_device(0)
+    if args.kernel:
+        run_kernel_only(psf, w, args.kernel, args.steps)
+        return
     dims = psf.make_dims(w.dims, psf.GEN_BF16)
     layers_dev, glob, pk, pv, x = make_device_tower(psf, w)
     layers = [psf.make_weights(l) for l in layers_dev]
@@ -190,7 +252,9 @@ def main():
         "image_tokens_per_s_per_output_image": round(w.n_tokens / (ms * 1e-3), 1),
         "roofline": {"kernel": "gate_up SwiGLU GEMM (M=8192, N=2x12288, K=4096)", "bound": "mfma",
                      "achieved": round(gu_tflops, 1), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-                     "frac": round(gu_tflops / PEAK_BF16_TFLOPS, 4), "traffic": None,
+                     "frac": round(gu_tflops / PEAK_BF16_TFLOPS, 4), "traffic": measured_traffic(),
+                     "algorithmic_bytes": 2 * (tokens * d.hidden + 2 * d.mlp_intermediate * d.hidden
+                                               + tokens * d.mlp_intermediate),
                      "avg_launch_ms": round(gu_avg_ms, 4), "launches_timed": gu_n},
         "device": {"name": props.name, "cus": props.multi_processor_count},
     }
