@@ -185,8 +185,8 @@ def main():
                     help="run only this kernel at the workload's shapes, --steps times (for counter runs)")
     args = ap.parse_args()
     if args.gpus != 1:
-        print(f"bench.py measures one GPU: this build has no multi-GPU path (asked for --gpus {args.gpus}). "
-              "See the sharding notes in DESIGN.md.", file=sys.stderr)
+        print(f"bench.py measures one GPU only: the denoise step here runs on a single GPU and has no "
+              f"multi-GPU path (asked for --gpus {args.gpus}).", file=sys.stderr)
         sys.exit(2)
 
     import torch

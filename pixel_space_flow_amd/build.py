@@ -17,7 +17,7 @@ SOURCES = ["gemm.hip", "attention.hip", "elementwise.hip", "moe.hip", "api.cpp"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 FLAGS = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}",
-         # keep the compiler from emitting packed fp32 VALU ops (see DESIGN.md)
+         # keep the compiler from emitting packed fp32 VALU ops
          "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
          "-Wno-unused-result"]
 
