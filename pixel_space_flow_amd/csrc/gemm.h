@@ -38,7 +38,6 @@ struct GemmParams {
   int img_H, img_W;                  // EPI_F32_IMG: images of img_H x img_W pixels, rows_per tokens each
   // grouped GEMM (MoE experts): tiles[3*t] = expert, first row, rows
   const int* tiles; int max_tiles; int64_t b_expert_stride;
-  int pfd;                           // fast kernel: L2 prefetch distance in tiles beyond the DMA (0 = off)
 };
 
 // Launchers (return hipError_t of the launch).

@@ -269,11 +269,6 @@ DEVI void dma16(__amdgpu_buffer_rsrc_t r, char* lds, uint32_t voff, uint32_t sof
   __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_ptr_t)lds, 16, voff, soff, 0, 0);
 }
 
-// 4 bytes per lane into LDS at lds + 4*lane: used only to pull lines into L2 ahead of the DMA.
-DEVI void dma4(__amdgpu_buffer_rsrc_t r, char* lds, uint32_t voff, uint32_t soff) {
-  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_ptr_t)lds, 4, voff, soff, 0, 0);
-}
-
 // Epilogue of 16 consecutive columns [col0, col0+16) of one output row.  Vector path when
 // all 16 columns are valid (col0 is a multiple of 16; leading dimensions are multiples of 8).
 template <int EPI>
@@ -370,7 +365,7 @@ DEVI void epi_row16(const GemmParams& p, int row, int col0, int ncols, float* v)
   }
 }
 
-template <int EPI, bool GROUPED, bool GATHER, int NW, bool PF>
+template <int EPI, bool GROUPED, bool GATHER, int NW>
 __global__ __launch_bounds__(64 * NW, 1) void gemm_fast_kernel(GemmParams p, int n_col_tiles) {
   // NW = 4: 2 x 2 waves of 128 x 128 (one wave per SIMD); NW = 8: 2 x 4 waves of 128 x 64 (two
   // waves per SIMD, so one wave's DMA issue or barrier wait is covered by the other's MFMAs).
@@ -464,37 +459,6 @@ __global__ __launch_bounds__(64 * NW, 1) void gemm_fast_kernel(GemmParams p, int
     }
   };
 
-  // L2 prefetch.  The LDS-DMA of tile kt+2 is issued one tile ahead of its use; under full load an
-  // L2 miss takes longer than one tile's MFMAs.  So each tile's DMA is paired with a 4-byte load of
-  // every 128-byte row segment of tile kt+2+p.pfd (A rows then B rows, one row per thread slot),
-  // landing in a per-wave scratch slot of LDS that nothing reads: the later DMA then hits L2.
-  constexpr int PF_PER = 512 / (64 * NW);    // prefetch loads per thread per tile
-  uint32_t pfoff[PF_PER];
-#pragma unroll
-  for (int i = 0; i < PF_PER; ++i) {
-    const int q = tid + i * 64 * NW;          // 0..255 A rows, 256..511 B rows (wave-uniform split)
-    const int r = q & 255;
-    if (q < 256) {
-      pfoff[i] = GATHER ? (uint32_t)p.a_rows[row0 + min(r, rows - 1)] * lda2 : (uint32_t)r * lda2;
-    } else if (p.bmode == 1) {
-      const int nb = r >> 5;
-      pfoff[i] = (uint32_t)(((nb & 1) ? p.swiglu_I : 0) + tn * (BN / 2) + (nb >> 1) * 32 + (r & 31)) * ldb2;
-    } else {
-      pfoff[i] = (uint32_t)r * ldb2;
-    }
-  }
-  char* pf_slot = smem + 2 * STAGE_BYTES + wave * 256;
-
-  const int KT = p.K / BK;
-  auto prefetch = [&](int kt) {
-    const uint32_t kb = (uint32_t)min(kt, KT - 1) * (BK * 2);   // clamped: the count per tile stays fixed
-#pragma unroll
-    for (int i = 0; i < PF_PER; ++i) {
-      if ((wave + i * NW) < 4) dma4(ra, pf_slot, pfoff[i], kb);   // wave-uniform operand choice
-      else dma4(rb, pf_slot, pfoff[i], kb);
-    }
-  };
-
   f32x16 acc[4][NBW];
 #pragma unroll
   for (int a = 0; a < 4; ++a)
@@ -503,30 +467,27 @@ __global__ __launch_bounds__(64 * NW, 1) void gemm_fast_kernel(GemmParams p, int
 #pragma unroll
       for (int e = 0; e < 16; ++e) acc[a][b][e] = 0.f;
 
+  const int KT = p.K / BK;
   const int lr = lane & 31, lh = lane >> 5;
   // LDS byte offsets of this lane's fragment rows (chunk XOR folded in per k-step below)
   const int arow0 = (wm * 128 + lr) * (BK * 2), brow0 = (wn * (BN / WN) + lr) * (BK * 2);
   const int sw = (lr >> 1) & 7;   // the same for all 4 blocks: their rows differ by multiples of 32
 
   // Software pipeline.  Two register sets of fragments: the reads for k-step ks+1 are issued
-  // before the 16 MFMAs of step ks.  At the last k-step of a tile every wave waits for the DMA of
-  // the next tile (the prefetch loads issued after it may stay in flight) and for its own LDS
-  // reads, and meets the others at the barrier: the next tile's stage is then complete and this
-  // tile's stage is free.  The next tile's first fragments are read, the DMA of tile kt+2 goes
-  // out, and the last k-step's MFMAs (whose fragments are already in registers) hide both.  The
-  // last tile is peeled so that every in-loop path has the same outstanding-read count.  The
+  // before the 16 MFMAs of step ks.  In the last step of a tile every wave waits for its
+  // outstanding LDS-DMA and LDS reads and meets the others at the barrier: the next tile's
+  // stage is then complete and this tile's stage is free, so the DMA of tile kt+2 goes out,
+  // the next tile's first fragments are read, and the last 16 MFMAs hide both.  The
   // sched_barrier(0) fences keep the compiler from moving reads next to their MFMAs.
   bf16x8 fa[2][4], fb[2][NBW];
   auto rd = [&](int set, int stage, int ks) {
     const char* As = smem + stage * STAGE_BYTES;
     const char* Bs = As + BM * BK * 2;
     const int ch = ((ks * 2 + lh) ^ sw) << 4;
-    // in the order the MFMAs consume them
-    fa[set][0] = *(const bf16x8*)(As + arow0 + ch);
+#pragma unroll
+    for (int mb = 0; mb < 4; ++mb) fa[set][mb] = *(const bf16x8*)(As + arow0 + mb * 32 * (BK * 2) + ch);
 #pragma unroll
     for (int nb = 0; nb < NBW; ++nb) fb[set][nb] = *(const bf16x8*)(Bs + brow0 + nb * 32 * (BK * 2) + ch);
-#pragma unroll
-    for (int mb = 1; mb < 4; ++mb) fa[set][mb] = *(const bf16x8*)(As + arow0 + mb * 32 * (BK * 2) + ch);
   };
   auto mma = [&](int set) {
 #pragma unroll
@@ -535,71 +496,34 @@ __global__ __launch_bounds__(64 * NW, 1) void gemm_fast_kernel(GemmParams p, int
       for (int nb = 0; nb < NBW; ++nb)
         acc[mb][nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[set][mb], fb[set][nb], acc[mb][nb], 0, 0, 0);
   };
-  // vmcnt(PF_PER) lgkmcnt(0): everything but the last PF_PER vector loads, and every LDS access
-  constexpr int WAIT_DMA = (PF_PER & 15) | ((PF_PER >> 4) << 14) | (7 << 4);
-
-  // Interleaving within a k-step: one MFMA, then one of the step's LDS reads (or LDS-DMA
-  // issues), so the MFMA pipe never waits behind a burst of memory instructions.
-  constexpr int NMF = 4 * NBW, NRD = 4 + NBW;
-  auto interleave_reads = [&]() {
-#pragma unroll
-    for (int i = 0; i < NRD; ++i) {
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // MFMA
-      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);   // DS read
-    }
-    __builtin_amdgcn_sched_group_barrier(0x008, NMF - NRD, 0);
-  };
 
   issue(0, 0);
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
-  if (KT > 1) {
-    issue(1, 1);
-    if (PF) prefetch(1 + p.pfd);
-  }
+  if (KT > 1) issue(1, 1);
   rd(0, 0, 0);
-  for (int kt = 0; kt + 1 < KT; ++kt) {
+  for (int kt = 0; kt < KT; ++kt) {
     const int st = kt & 1;
 #pragma unroll
-    for (int ks = 0; ks + 1 < BK / 16; ++ks) {
-      rd((ks & 1) ^ 1, st, ks + 1);
-      mma(ks & 1);
-      interleave_reads();
+    for (int ks = 0; ks < BK / 16; ++ks) {
+      const int cur = ks & 1;
+      if (ks + 1 < BK / 16) {
+        rd(cur ^ 1, st, ks + 1);
+      } else if (kt + 1 < KT) {
+        __builtin_amdgcn_s_waitcnt(0);
+        __syncthreads();
+        if (kt + 2 < KT) issue(kt + 2, st);
+        rd(cur ^ 1, st ^ 1, 0);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+      mma(cur);
       __builtin_amdgcn_sched_barrier(0);
     }
-    __builtin_amdgcn_s_waitcnt(PF ? WAIT_DMA : 0);
-    __builtin_amdgcn_s_barrier();   // no fence: the waitcnt above is the one needed
-    rd(0, st ^ 1, 0);
-    // The DMA of tile kt+2 into the stage just freed (clamped to the last tile, which is then
-    // loaded twice into a stage nobody reads again, so the loop body has no branch).
-    issue(min(kt + 2, KT - 1), st);
-    if (PF) prefetch(kt + 2 + p.pfd);
-    mma(1);
-#pragma unroll
-    for (int i = 0; i < NRD; ++i) {
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // MFMA
-      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);   // DS read
-      __builtin_amdgcn_sched_group_barrier(0x020, 2, 0);   // LDS-DMA issue
-    }
-    __builtin_amdgcn_sched_group_barrier(0x008, NMF - NRD, 0);
-    __builtin_amdgcn_sched_barrier(0);
-  }
-  {
-    const int st = (KT - 1) & 1;
-#pragma unroll
-    for (int ks = 0; ks + 1 < BK / 16; ++ks) {
-      rd((ks & 1) ^ 1, st, ks + 1);
-      mma(ks & 1);
-      interleave_reads();
-      __builtin_amdgcn_sched_barrier(0);
-    }
-    mma(1);
   }
 
   // ---- epilogue through LDS: each wave stages one 32x32 fp32 block at a time, then every lane
   // owns 16 consecutive columns of one row (lanes 2r, 2r+1 cover row r), so global accesses are
   // 16-byte vectors and the per-row index math runs once per block.
-  __builtin_amdgcn_s_waitcnt(0);   // no prefetch load still in flight
   __syncthreads();   // every wave is done with the LDS stages
   constexpr int TS = 36;                                   // padded fp32 row stride of a staged block
   float* T0 = (float*)smem + wave * (2 * 32 * TS);
@@ -729,27 +653,26 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(GemmParams p) {
     }
 }
 
-// L2 prefetch distance in tiles beyond the DMA (0 = off).
-int gemm_pfd() {
-  static const int d = [] {
-    const char* e = getenv("PSF_GEMM_PFD");
-    return e ? atoi(e) : 0;
+// 8 waves (two per SIMD) by default; PSF_GEMM_WAVES=4 selects one wave per SIMD with 128 x 128
+// wave tiles (kept for comparison runs).
+int fast_waves() {
+  static const int w = [] {
+    const char* e = getenv("PSF_GEMM_WAVES");
+    return (e && atoi(e) == 4) ? 4 : 8;
   }();
-  return d;
+  return w;
 }
 
 template <bool GROUPED, bool GATHER>
-hipError_t launch_fast(const GemmParams& p0, int epi, int grid, int n_col_tiles, hipStream_t s) {
-  const size_t lds = 2 * STAGE_BYTES + 8 * 256;
-  GemmParams p = p0;
-  p.pfd = gemm_pfd();
+hipError_t launch_fast(const GemmParams& p, int epi, int grid, int n_col_tiles, hipStream_t s) {
+  const size_t lds = 2 * STAGE_BYTES;
 #define PSF_L(E)                                                                                  \
   case E: {                                                                                        \
-    auto k = p.pfd > 0 ? gemm_fast_kernel<E, GROUPED, GATHER, 8, true> : gemm_fast_kernel<E, GROUPED, GATHER, 8, false>; \
+    auto k = fast_waves() == 4 ? gemm_fast_kernel<E, GROUPED, GATHER, 4> : gemm_fast_kernel<E, GROUPED, GATHER, 8>; \
     hipError_t e = hipFuncSetAttribute((const void*)k, hipFuncAttributeMaxDynamicSharedMemorySize, \
                                        (int)lds);                                                  \
     if (e != hipSuccess) return e;                                                                 \
-    hipLaunchKernelGGL(k, dim3(grid), dim3(512), lds, s, p, n_col_tiles);                         \
+    hipLaunchKernelGGL(k, dim3(grid), dim3(64 * fast_waves()), lds, s, p, n_col_tiles);            \
     return hipGetLastError();                                                                      \
   }
   switch (epi) {
