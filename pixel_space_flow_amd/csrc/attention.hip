@@ -282,14 +282,23 @@ __global__ __launch_bounds__(256, QB == 1 ? 2 : 1) void attn_v2_kernel(const bf1
     }
   };
 
+  // Per-lane LDS byte offsets of the fragment reads; the stage and the 32-row block offsets are
+  // immediates.  K row r = kb * 32 + lr has kswz(r) = kswz(lr); V^T row r = db * 32 + lr has
+  // ((r >> 1) & 7) = ((lr >> 1) & 7).
+  int koff[D / 16], voff[4];
+#pragma unroll
+  for (int ks = 0; ks < D / 16; ++ks) koff[ks] = lr * KROW + (((ks * 2 + lh) ^ kswz(lr)) << 4);
+#pragma unroll
+  for (int c = 0; c < 4; ++c) voff[c] = KT * KROW + lr * 128 + (((c * 2 + lh) ^ ((lr >> 1) & 7)) << 4);
+  const bf16x2 ones = {static_cast<bf16>(1.0f), static_cast<bf16>(1.0f)};
+
   const int ntiles = (L + KT - 1) / KT;
-  issue(0, 0);
-  for (int t = 0; t < ntiles; ++t) {
+  // one k-tile from LDS stage `stage` (a compile-time constant at every call)
+  auto tile = [&](const int t, const int stage) {
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
-    if (t + 1 < ntiles) issue(t + 1, (t + 1) & 1);
-    const char* Ks = smem + (t & 1) * STAGE;
-    const char* Vs = Ks + KT * KROW;
+    if (t + 1 < ntiles) issue(t + 1, stage ^ 1);
+    const char* S0 = smem + stage * STAGE;
     const int j0 = t * KT;
 
     f32x16 sc[QB][2];
@@ -301,16 +310,16 @@ __global__ __launch_bounds__(256, QB == 1 ? 2 : 1) void attn_v2_kernel(const bf1
         for (int e = 0; e < 16; ++e) sc[qb][kb][e] = 0.f;
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
-      const int r = kb * 32 + lr;
 #pragma unroll
       for (int ks = 0; ks < D / 16; ++ks) {
-        const bf16x8 a = *(const bf16x8*)(Ks + r * KROW + (((ks * 2 + lh) ^ kswz(r)) << 4));
+        const bf16x8 a = *(const bf16x8*)(S0 + kb * 32 * KROW + koff[ks]);
 #pragma unroll
         for (int qb = 0; qb < QB; ++qb)
           sc[qb][kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[qb][ks], sc[qb][kb], 0, 0, 0);
       }
     }
     const bool tail = j0 + KT > L;
+    bf16x8 pb[QB][2][2];
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb) {
       if (tail) {
@@ -339,15 +348,23 @@ __global__ __launch_bounds__(256, QB == 1 ? 2 : 1) void attn_v2_kernel(const bf1
 #pragma unroll
           for (int e = 0; e < 16; ++e) o[qb][i][e] *= alpha;
       }
+      // p = 2^(s log2(e)/sqrt(d) - m): the hardware exp2 (results below 2^-126 flush to zero,
+      // far under the bf16 rounding p gets next).  The row sum accumulates the bf16 p that the
+      // P.V product uses, two at a time with a bf16 dot product against (1, 1).
       const float nm = -m[qb];
       float rs = 0.f;
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-        for (int e = 0; e < 16; ++e) {
-          const float pv = exp2f(fmaf(sc[qb][kb][e], scale_log2, nm));
-          sc[qb][kb][e] = pv;
-          rs += pv;
+        for (int st = 0; st < 2; ++st) {
+#pragma unroll
+          for (int e = 0; e < 8; ++e)
+            pb[qb][kb][st][e] = static_cast<bf16>(__builtin_amdgcn_exp2f(fmaf(sc[qb][kb][st * 8 + e], scale_log2, nm)));
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const bf16x2 pr = {pb[qb][kb][st][2 * e], pb[qb][kb][st][2 * e + 1]};
+            rs = __builtin_amdgcn_fdot2_f32_bf16(pr, ones, rs, false);
+          }
         }
       l[qb] += rs;
     }
@@ -355,21 +372,20 @@ __global__ __launch_bounds__(256, QB == 1 ? 2 : 1) void attn_v2_kernel(const bf1
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
       for (int st = 0; st < 2; ++st) {
-        bf16x8 pb[QB];
-#pragma unroll
-        for (int qb = 0; qb < QB; ++qb)
-#pragma unroll
-          for (int e = 0; e < 8; ++e) pb[qb][e] = static_cast<bf16>(sc[qb][kb][st * 8 + e]);
-        const int ch = kb * 4 + st * 2 + lh;            // 16-byte chunk of keys in permuted order
 #pragma unroll
         for (int db = 0; db < NDB; ++db) {
-          const int r = db * 32 + lr;
-          const bf16x8 av = *(const bf16x8*)(Vs + r * 128 + ((ch ^ ((r >> 1) & 7)) << 4));
+          const bf16x8 av = *(const bf16x8*)(S0 + db * 32 * 128 + voff[kb * 2 + st]);
 #pragma unroll
           for (int qb = 0; qb < QB; ++qb)
-            o[qb][db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, pb[qb], o[qb][db], 0, 0, 0);
+            o[qb][db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, pb[qb][kb][st], o[qb][db], 0, 0, 0);
         }
       }
+  };
+
+  issue(0, 0);
+  for (int t = 0; t < ntiles; t += 2) {
+    tile(t, 0);
+    if (t + 1 < ntiles) tile(t + 1, 1);
   }
 
 #pragma unroll
