@@ -197,6 +197,9 @@ DEVI void dma16_a(__amdgpu_buffer_rsrc_t r, char* lds, uint32_t voff, uint32_t s
   __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_ptr_t)lds, 16, voff, soff, 0, 0);
 }
 
+// Query heads per attention workgroup: 4 when the GQA group size allows, else 2 or 1.
+__host__ __device__ inline int attn_heads_per_wg(int G) { return (G % 4 == 0) ? 4 : ((G % 2 == 0) ? 2 : 1); }
+
 template <int D, int QB>
 __global__ __launch_bounds__(256, QB == 1 ? 2 : 1) void attn_v2_kernel(const bf16* __restrict__ qkv, int64_t ldq,
                                                                      SeqInfo si, int Hq, int Hkv, int Lpad,
@@ -215,23 +218,27 @@ __global__ __launch_bounds__(256, QB == 1 ? 2 : 1) void attn_v2_kernel(const bf1
   // chunks by (r & 15); 128 B rows (K at d = 64, V^T) pair up in a window and use ((r >> 1) & 7).
   auto kswz = [](int r) { return D == 128 ? (r & 15) : ((r >> 1) & 7); };
 
+  // The four waves share one kv head: they cover HPW query heads of its group times 4 / HPW
+  // query blocks, so each K/V tile brought into LDS serves HPW heads.
   const int G = Hq / Hkv;
-  const int total = si.B * Hkv * n_qb * G;
+  const int HPW = attn_heads_per_wg(G);
+  const int n_hg = G / HPW;
+  const int total = si.B * Hkv * n_qb * n_hg;
   const int id = xcd_remap(blockIdx.x, total);
-  const int hh = id % G;
-  int rest = id / G;
+  const int hg = id % n_hg;
+  int rest = id / n_hg;
   const int qbk = rest % n_qb;
   rest /= n_qb;
   const int g = rest % Hkv;
   const int b = rest / Hkv;
-  const int h = g * G + hh;
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int lr = lane & 31, lh = lane >> 5;
+  const int h = g * G + hg * HPW + wave % HPW;
   const int N = si.N;
   const int L = si.plen[b] + N;
-  const int qbase = qbk * (4 * QW) + wave * QW;
+  const int qbase = qbk * ((4 / HPW) * QW) + (wave / HPW) * QW;
 
   bf16x8 qf[QB][D / 16];
 #pragma unroll
@@ -452,8 +459,10 @@ hipError_t attention_bf16(const bf16* qkv, int64_t ldq, const SeqInfo& si, int H
   const float scale_log2 = 1.4426950408889634f / sqrtf((float)d);
   // 4 waves x ATTN_QB*32 queries per workgroup
   constexpr int QB = ATTN_QB;
-  const int n_qb2 = (si.N + 128 * QB - 1) / (128 * QB);
-  const int total2 = si.B * Hkv * n_qb2 * (Hq / Hkv);
+  const int hpw = attn_heads_per_wg(Hq / Hkv);
+  const int qpw = (4 / hpw) * 32 * QB;                  // queries of one head per workgroup
+  const int n_qb2 = (si.N + qpw - 1) / qpw;
+  const int total2 = si.B * Hkv * n_qb2 * (Hq / Hkv / hpw);
   if (d == 128)
     hipLaunchKernelGGL((attn_v2_kernel<128, QB>), dim3(total2), dim3(256), 0, s, qkv, ldq, si, Hq, Hkv, Lpad, Kc, Vt, O, ldo, scale_log2, n_qb2);
   else if (d == 64)

@@ -105,7 +105,8 @@ def test_qknorm_rope(lib, dtype, d, Hq, Hkv, N, plen):
 @pytest.mark.parametrize("dtype", ["bf16", "f32"])
 @pytest.mark.parametrize("d,Hq,Hkv,N,plen", [(128, 8, 2, 200, [37, 0]), (64, 4, 2, 64, [32, 32]),
                                               (128, 4, 4, 130, [400, 5]), (128, 8, 1, 1, [3, 64]),
-                                              (128, 8, 2, 99, [0, 45, 130])])
+                                              (128, 8, 2, 99, [0, 45, 130]), (128, 6, 2, 70, [10, 0]),
+                                              (64, 16, 2, 150, [64, 3])])
 def test_attention(lib, dtype, d, Hq, Hkv, N, plen):
     import torch
     B = len(plen)
