@@ -270,9 +270,9 @@ __global__ __launch_bounds__(256, QB == 1 ? 2 : 1) void attn_v2_kernel(const bf1
   constexpr int VLOADS = D / 8 / 4;                 // wave-loads per wave per tile (V)
   const int vrow_l = lane >> 3, vch_p = lane & 7;
 
-  auto issue = [&](int t, int stage) {
+  // K tile t into the K half of a stage, V^T tile t into the V half
+  auto issue_k = [&](int t, int stage) {
     char* Ks = smem + stage * STAGE;
-    char* Vs = Ks + KT * KROW;
 #pragma unroll
     for (int i = 0; i < KLOADS; ++i) {
       const int r0 = (wave * KLOADS + i) * KRPL;
@@ -280,6 +280,9 @@ __global__ __launch_bounds__(256, QB == 1 ? 2 : 1) void attn_v2_kernel(const bf1
       const int lch = kch_p ^ kswz(row);
       dma16_a(rk, Ks + r0 * KROW, (uint32_t)(row * KROW + lch * 16), (uint32_t)t * KT * KROW);
     }
+  };
+  auto issue_v = [&](int t, int stage) {
+    char* Vs = smem + stage * STAGE + KT * KROW;
 #pragma unroll
     for (int i = 0; i < VLOADS; ++i) {
       const int r0 = (wave * VLOADS + i) * 8;
@@ -300,32 +303,33 @@ __global__ __launch_bounds__(256, QB == 1 ? 2 : 1) void attn_v2_kernel(const bf1
   const bf16x2 ones = {static_cast<bf16>(1.0f), static_cast<bf16>(1.0f)};
 
   const int ntiles = (L + KT - 1) / KT;
-  // one k-tile from LDS stage `stage` (a compile-time constant at every call)
-  auto tile = [&](const int t, const int stage) {
-    __builtin_amdgcn_s_waitcnt(0);
-    __syncthreads();
-    if (t + 1 < ntiles) issue(t + 1, stage ^ 1);
-    const char* S0 = smem + stage * STAGE;
-    const int j0 = t * KT;
 
-    f32x16 sc[QB][2];
+  // Software pipeline across k-tiles: the scores of tile t+1 (K . Q^T MFMAs) are computed while
+  // the softmax of tile t runs on the VALU, then P(t) . V(t) follows.  K therefore runs one tile
+  // ahead of V: K tile t and V tile t both live in stage t & 1, K(t+1) is loaded during tile t-1
+  // and V(t) during tile t-1.
+  f32x16 sc[QB][2], sn[QB][2];
+  auto scores = [&](f32x16 (&dst)[QB][2], const int stage) {
+    const char* K0 = smem + stage * STAGE;
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb)
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-        for (int e = 0; e < 16; ++e) sc[qb][kb][e] = 0.f;
+        for (int e = 0; e < 16; ++e) dst[qb][kb][e] = 0.f;
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
+    for (int ks = 0; ks < D / 16; ++ks)
 #pragma unroll
-      for (int ks = 0; ks < D / 16; ++ks) {
-        const bf16x8 a = *(const bf16x8*)(S0 + kb * 32 * KROW + koff[ks]);
+      for (int kb = 0; kb < 2; ++kb) {
+        const bf16x8 a = *(const bf16x8*)(K0 + kb * 32 * KROW + koff[ks]);
 #pragma unroll
         for (int qb = 0; qb < QB; ++qb)
-          sc[qb][kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[qb][ks], sc[qb][kb], 0, 0, 0);
+          dst[qb][kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[qb][ks], dst[qb][kb], 0, 0, 0);
       }
-    }
-    const bool tail = j0 + KT > L;
+  };
+  // Online softmax of the scores in sc (tile t, keys from j0) and P . V from stage `stage`.
+  auto softmax_pv = [&](const int t, const int stage, const bool tail) {
+    const int j0 = t * KT;
     bf16x8 pb[QB][2][2];
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb) {
@@ -375,6 +379,7 @@ __global__ __launch_bounds__(256, QB == 1 ? 2 : 1) void attn_v2_kernel(const bf1
         }
       l[qb] += rs;
     }
+    const char* S0 = smem + stage * STAGE;
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
@@ -388,12 +393,38 @@ __global__ __launch_bounds__(256, QB == 1 ? 2 : 1) void attn_v2_kernel(const bf1
         }
       }
   };
+  // iteration t (every tile but the last): after the barrier K(t+1) and V(t) have landed and no
+  // wave reads K(t) or V(t-1) any more, so K(t+2) and V(t+1) go into those halves.
+  auto step = [&](const int t, const int stage) {
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+    issue_k(min(t + 2, ntiles - 1), stage);   // past the end: a reload into a half nobody reads
+    issue_v(t + 1, stage ^ 1);
+    scores(sn, stage ^ 1);
+    softmax_pv(t, stage, false);
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb) { sc[qb][0] = sn[qb][0]; sc[qb][1] = sn[qb][1]; }
+  };
 
-  issue(0, 0);
-  for (int t = 0; t < ntiles; t += 2) {
-    tile(t, 0);
-    if (t + 1 < ntiles) tile(t + 1, 1);
+  issue_k(0, 0);
+  issue_v(0, 0);
+  if (ntiles > 1) issue_k(1, 1);
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+  scores(sc, 0);
+  int t = 0;
+  for (; t + 2 < ntiles; t += 2) {
+    step(t, 0);
+    step(t + 1, 1);
   }
+  if (t + 1 < ntiles) {
+    step(t, 0);
+    ++t;
+  }
+  // last tile (the only one that can be partial)
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+  softmax_pv(t, t & 1, t * KT + KT > L);
 
 #pragma unroll
   for (int qb = 0; qb < QB; ++qb) {
