@@ -273,13 +273,22 @@ int run_block(const gen_block_dims& d, const gen_block_weights& w, TH* hidden, c
     }
     HIP_TRY(timed(FAM_QKV, s, [&] { return gemm_any<T>(p, EPI_STORE, s); }));
   }
-  HIP_TRY(qknorm_rope<T>(qkv, QKV, si, Hq, Hkv, hd, (const T*)w.g_q, (const T*)w.g_k, rope, d.rms_eps, s));
-  HIP_TRY(pack_kv<T>(qkv, QKV, si, Hq, Hkv, hd, L.Lpad, Kc, Vt, s));
-  HIP_TRY(timed(FAM_ATTN, s, [&] {
-    if (sizeof(T) == 2)
-      return attention_bf16((const bf16*)qkv, QKV, si, Hq, Hkv, hd, L.Lpad, (const bf16*)Kc, (const bf16*)Vt, (bf16*)attn, QD, s);
-    return attention_f32((const float*)qkv, QKV, si, Hq, Hkv, hd, L.Lpad, (const float*)Kc, (const float*)Vt, (float*)attn, QD, s);
-  }));
+  if (sizeof(T) == 2) {
+    // bf16: the QK-norm and RoPE ride along with the K packing and the attention's Q loads
+    HIP_TRY(pack_kv_knorm((const bf16*)qkv, QKV, si, Hq, Hkv, hd, L.Lpad, (const bf16*)w.g_k, rope, d.rms_eps,
+                          (bf16*)Kc, (bf16*)Vt, s));
+    HIP_TRY(timed(FAM_ATTN, s, [&] {
+      return attention_bf16((const bf16*)qkv, QKV, si, Hq, Hkv, hd, L.Lpad, (const bf16*)Kc, (const bf16*)Vt,
+                            (bf16*)attn, QD, (const bf16*)w.g_q, rope, d.rms_eps, s);
+    }));
+  } else {
+    HIP_TRY(qknorm_rope<T>(qkv, QKV, si, Hq, Hkv, hd, (const T*)w.g_q, (const T*)w.g_k, rope, d.rms_eps, s));
+    HIP_TRY(pack_kv<T>(qkv, QKV, si, Hq, Hkv, hd, L.Lpad, Kc, Vt, s));
+    HIP_TRY(timed(FAM_ATTN, s, [&] {
+      return attention_f32((const float*)qkv, QKV, si, Hq, Hkv, hd, L.Lpad, (const float*)Kc, (const float*)Vt,
+                           (float*)attn, QD, s);
+    }));
+  }
   {
     GemmParams p = gp();
     p.A = attn; p.lda = QD; p.B = w.w_o; p.ldb = QD; p.M = M; p.N = D; p.K = QD;
@@ -660,7 +669,8 @@ int gen_op_attention(const void* qkv, int B, int N, int Hq, int Hkv, int d, cons
   hipStream_t s = (hipStream_t)stream;
   if (dtype == GEN_BF16) {
     HIP_TRY(pack_kv<bf16>((const bf16*)qkv, ld, si, Hq, Hkv, d, Lpad, at<bf16>(workspace, kc), at<bf16>(workspace, vt), s));
-    HIP_TRY(attention_bf16((const bf16*)qkv, ld, si, Hq, Hkv, d, Lpad, at<bf16>(workspace, kc), at<bf16>(workspace, vt), (bf16*)out, (int64_t)Hq * d, s));
+    HIP_TRY(attention_bf16((const bf16*)qkv, ld, si, Hq, Hkv, d, Lpad, at<bf16>(workspace, kc), at<bf16>(workspace, vt),
+                           (bf16*)out, (int64_t)Hq * d, nullptr, nullptr, 0.f, s));
   } else {
     HIP_TRY(pack_kv<float>((const float*)qkv, ld, si, Hq, Hkv, d, Lpad, at<float>(workspace, kc), at<float>(workspace, vt), s));
     HIP_TRY(attention_f32((const float*)qkv, ld, si, Hq, Hkv, d, Lpad, at<float>(workspace, kc), at<float>(workspace, vt), (float*)out, (int64_t)Hq * d, s));

@@ -200,12 +200,16 @@ DEVI void dma16_a(__amdgpu_buffer_rsrc_t r, char* lds, uint32_t voff, uint32_t s
 // Query heads per attention workgroup: 4 when the GQA group size allows, else 2 or 1.
 __host__ __device__ inline int attn_heads_per_wg(int G) { return (G % 4 == 0) ? 4 : ((G % 2 == 0) ? 2 : 1); }
 
-template <int D, int QB>
+// QKN: the q heads in qkv are raw projections; each wave applies the per-head RMSNorm (gain gq)
+// and the rotate-half RoPE (cos/sin table [pos][d/2]) to its queries while loading them.
+template <int D, int QB, bool QKN>
 __global__ __launch_bounds__(256, QB == 1 ? 2 : 1) void attn_v2_kernel(const bf16* __restrict__ qkv, int64_t ldq,
                                                                      SeqInfo si, int Hq, int Hkv, int Lpad,
                                                                      const bf16* __restrict__ Kc,
                                                                      const bf16* __restrict__ Vt, bf16* __restrict__ O,
-                                                                     int64_t ldo, float scale_log2, int n_qb) {
+                                                                     int64_t ldo, float scale_log2, int n_qb,
+                                                                     const bf16* __restrict__ gq,
+                                                                     const float2* __restrict__ table, float eps) {
   constexpr int KT = 64;                  // keys per tile
   constexpr int KROW = D * 2;             // bytes per K row
   constexpr int KCH = D / 8;              // 16-byte chunks per K row
@@ -243,10 +247,47 @@ __global__ __launch_bounds__(256, QB == 1 ? 2 : 1) void attn_v2_kernel(const bf1
   bf16x8 qf[QB][D / 16];
 #pragma unroll
   for (int qb = 0; qb < QB; ++qb) {
-    const int64_t tok = (int64_t)b * N + min(qbase + qb * 32 + lr, N - 1);
+    const int qn = min(qbase + qb * 32 + lr, N - 1);
+    const int64_t tok = (int64_t)b * N + qn;
     const bf16* qp = qkv + tok * ldq + (int64_t)h * D + lh * 8;
 #pragma unroll
     for (int ks = 0; ks < D / 16; ++ks) qf[qb][ks] = *(const bf16x8*)(qp + ks * 16);
+    if (QKN) {
+      // This lane holds elements ks * 16 + lh * 8 + e of its query's head vector (the other half
+      // sits in lane ^ 32); the rotate-half partner of element j < d/2 is j + d/2, i.e. k-step
+      // ks + d/32 of the same lane.
+      float x[D / 16][8];
+      float ss = 0.f;
+#pragma unroll
+      for (int ks = 0; ks < D / 16; ++ks)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          x[ks][e] = static_cast<float>(qf[qb][ks][e]);
+          ss += x[ks][e] * x[ks][e];
+        }
+      ss += __shfl_xor(ss, 32, 64);
+      const float r = 1.0f / sqrtf(ss / (float)D + eps);
+#pragma unroll
+      for (int ks = 0; ks < D / 16; ++ks) {
+        const bf16x8 gg = *(const bf16x8*)(gq + ks * 16 + lh * 8);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) x[ks][e] = x[ks][e] * r * static_cast<float>(gg[e]);
+      }
+      const float2* tb = table + (int64_t)(si.plen[b] + qn) * (D / 2) + lh * 8;
+#pragma unroll
+      for (int ks = 0; ks < D / 32; ++ks)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const float2 cs = tb[ks * 16 + e];
+          const float a = x[ks][e], c = x[ks + D / 32][e];
+          x[ks][e] = a * cs.x - c * cs.y;
+          x[ks + D / 32][e] = c * cs.x + a * cs.y;
+        }
+#pragma unroll
+      for (int ks = 0; ks < D / 16; ++ks)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) qf[qb][ks][e] = static_cast<bf16>(x[ks][e]);
+    }
   }
   f32x16 o[QB][NDB];
 #pragma unroll
@@ -483,7 +524,8 @@ __global__ __launch_bounds__(128) void attn_f32_kernel(const float* __restrict__
 }  // namespace
 
 hipError_t attention_bf16(const bf16* qkv, int64_t ldq, const SeqInfo& si, int Hq, int Hkv, int d, int Lpad,
-                          const bf16* Kc, const bf16* Vt, bf16* O, int64_t ldo, hipStream_t s) {
+                          const bf16* Kc, const bf16* Vt, bf16* O, int64_t ldo, const bf16* gq,
+                          const float2* table, float eps, hipStream_t s) {
   const int n_qb = (si.N + 127) / 128;
   const int total = si.B * Hkv * n_qb * (Hq / Hkv);
   if (total == 0) return hipSuccess;
@@ -494,12 +536,17 @@ hipError_t attention_bf16(const bf16* qkv, int64_t ldq, const SeqInfo& si, int H
   const int qpw = (4 / hpw) * 32 * QB;                  // queries of one head per workgroup
   const int n_qb2 = (si.N + qpw - 1) / qpw;
   const int total2 = si.B * Hkv * n_qb2 * (Hq / Hkv / hpw);
-  if (d == 128)
-    hipLaunchKernelGGL((attn_v2_kernel<128, QB>), dim3(total2), dim3(256), 0, s, qkv, ldq, si, Hq, Hkv, Lpad, Kc, Vt, O, ldo, scale_log2, n_qb2);
-  else if (d == 64)
-    hipLaunchKernelGGL((attn_v2_kernel<64, QB>), dim3(total2), dim3(256), 0, s, qkv, ldq, si, Hq, Hkv, Lpad, Kc, Vt, O, ldo, scale_log2, n_qb2);
-  else
+#define PSF_ATTN(DD, QKN)                                                                              \
+  hipLaunchKernelGGL((attn_v2_kernel<DD, QB, QKN>), dim3(total2), dim3(256), 0, s, qkv, ldq, si, Hq, Hkv, Lpad, Kc, \
+                     Vt, O, ldo, scale_log2, n_qb2, gq, table, eps)
+  if (d == 128) {
+    if (gq) PSF_ATTN(128, true); else PSF_ATTN(128, false);
+  } else if (d == 64) {
+    if (gq) PSF_ATTN(64, true); else PSF_ATTN(64, false);
+  } else {
     return hipErrorInvalidValue;
+  }
+#undef PSF_ATTN
   (void)total;
   return hipGetLastError();
 }

@@ -167,6 +167,57 @@ __global__ __launch_bounds__(256) void pack_k_kernel(const T* __restrict__ qkv, 
   *(u32x4*)(Kc + (((int64_t)b * Hkv + g) * Lpad + j) * d + c * V::N) = v;
 }
 
+// Kc as pack_k_kernel, with each image key RMS-normalised (gain gk) and rotated (RoPE at its
+// packed index j).  One head vector per L = d / 8 lanes (16-byte chunks), as in
+// qknorm_rope_kernel; every lane runs the arithmetic and the row kind picks the stored value.
+template <int D>
+__global__ __launch_bounds__(256) void pack_k_knorm_kernel(const bf16* __restrict__ qkv, int64_t ld, SeqInfo si,
+                                                           int Hq, int Hkv, int Lpad, const bf16* __restrict__ gk,
+                                                           const float2* __restrict__ table, float eps,
+                                                           bf16* __restrict__ Kc, int64_t total) {
+  using V = V16<bf16>;
+  constexpr int L = D / V::N;
+  constexpr int HPW = 64 / L;
+  const int lane = threadIdx.x & 63;
+  const int64_t hv = ((int64_t)blockIdx.x * 4 + (threadIdx.x >> 6)) * HPW + lane / L;
+  const int sub = lane % L;
+  const bool active = hv < total;
+  const int64_t hvc = active ? hv : 0;
+  const int j = (int)(hvc % Lpad);
+  const int64_t bg = hvc / Lpad;
+  const int g = (int)(bg % Hkv), b = (int)(bg / Hkv);
+  const int P = si.plen[b];
+  const int kind = j < P ? 0 : (j < P + si.N ? 1 : 2);     // prefix, image, padding
+  u32x4 raw = {0, 0, 0, 0};
+  if (kind == 0) raw = *(const u32x4*)((const bf16*)si.pk[b] + ((int64_t)j * Hkv + g) * D + sub * V::N);
+  else if (kind == 1) raw = *(const u32x4*)(qkv + ((int64_t)b * si.N + j - P) * ld + (int64_t)(Hq + g) * D + sub * V::N);
+  float x[V::N], gg[V::N];
+  V::unpack(raw, x);
+  V::unpack(*(const u32x4*)(gk + sub * V::N), gg);
+  float ss = 0.f;
+#pragma unroll
+  for (int e = 0; e < V::N; ++e) ss += x[e] * x[e];
+#pragma unroll
+  for (int o = L / 2; o > 0; o >>= 1) ss += __shfl_xor(ss, o, 64);
+  const float r = 1.0f / sqrtf(ss / (float)D + eps);
+#pragma unroll
+  for (int e = 0; e < V::N; ++e) x[e] = x[e] * r * gg[e];
+  float pr[V::N];
+#pragma unroll
+  for (int e = 0; e < V::N; ++e) pr[e] = __shfl_xor(x[e], L / 2, 64);
+  const bool first = sub < L / 2;
+  const int j0 = (sub % (L / 2)) * V::N;
+  const float2* tb = table + (int64_t)(kind == 1 ? j : 0) * (D / 2) + j0;
+  float out[V::N];
+#pragma unroll
+  for (int e = 0; e < V::N; ++e) {
+    const float2 cs = tb[e];
+    out[e] = first ? (x[e] * cs.x - pr[e] * cs.y) : (x[e] * cs.x + pr[e] * cs.y);
+  }
+  if (!active) return;
+  *(u32x4*)(Kc + (((int64_t)b * Hkv + g) * Lpad + j) * D + sub * V::N) = kind == 1 ? V::pack(out) : raw;
+}
+
 // Vt[b][g][dd][j0..j0+8): each lane gathers 8 keys of one head-dim column; a wave's loads
 // of one key row are 64 consecutive elements.
 template <typename T>
@@ -328,6 +379,23 @@ hipError_t pack_kv(const T* qkv, int64_t ld, const SeqInfo& si, int Hq, int Hkv,
   hipLaunchKernelGGL(pack_k_kernel<T>, gk, dim3(256), 0, s, qkv, ld, si, Hq, Hkv, d, Lpad, Kc);
   dim3 gv((d * (Lpad / V16<T>::N) + 255) / 256, Hkv, si.B);
   hipLaunchKernelGGL(pack_vt_kernel<T>, gv, dim3(256), 0, s, qkv, ld, si, Hq, Hkv, d, Lpad, Vt);
+  return hipGetLastError();
+}
+hipError_t pack_kv_knorm(const bf16* qkv, int64_t ld, const SeqInfo& si, int Hq, int Hkv, int d, int Lpad,
+                         const bf16* gk, const float2* table, float eps, bf16* Kc, bf16* Vt, hipStream_t s) {
+  const int64_t total = (int64_t)si.B * Hkv * Lpad;
+  if (total == 0) return hipSuccess;
+  const int L = d / V16<bf16>::N;
+  const int64_t per_block = 4 * (64 / L);
+  const dim3 grid((unsigned)((total + per_block - 1) / per_block));
+  if (d == 128)
+    hipLaunchKernelGGL((pack_k_knorm_kernel<128>), grid, dim3(256), 0, s, qkv, ld, si, Hq, Hkv, Lpad, gk, table, eps, Kc, total);
+  else if (d == 64)
+    hipLaunchKernelGGL((pack_k_knorm_kernel<64>), grid, dim3(256), 0, s, qkv, ld, si, Hq, Hkv, Lpad, gk, table, eps, Kc, total);
+  else
+    return hipErrorInvalidValue;
+  dim3 gv((d * (Lpad / V16<bf16>::N) + 255) / 256, Hkv, si.B);
+  hipLaunchKernelGGL(pack_vt_kernel<bf16>, gv, dim3(256), 0, s, qkv, ld, si, Hq, Hkv, d, Lpad, Vt);
   return hipGetLastError();
 }
 template hipError_t pack_kv<bf16>(const bf16*, int64_t, const SeqInfo&, int, int, int, int, bf16*, bf16*, hipStream_t);
