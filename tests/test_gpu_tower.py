@@ -24,6 +24,8 @@ class GpuTower:
         self.glob = weights_to_dev(self.np_glob, dtype)
         self.np_layers, self.layers_dev, self.layers = [], [], []
         for l in range(w.n_layers):
+            if w.n_layers > 4:
+                log(f"  weights of layer {l}")
             wts = W.layer_weights(w, l, seed, dtype)
             self.np_layers.append(wts)
             dv = weights_to_dev(wts, dtype)
@@ -50,7 +52,12 @@ class GpuTower:
 
     def oracle_tokens(self, x_np, sigma, rows=None):
         w = self.w
-        return O.tower_tokens(x_np, sigma, self.np_glob, lambda l: self.np_layers[l], w.dims, w.n_layers, w.n_br,
+
+        def layer(l):
+            if w.n_layers > 4:
+                log(f"  oracle layer {l}")
+            return self.np_layers[l]
+        return O.tower_tokens(x_np, sigma, self.np_glob, layer, w.dims, w.n_layers, w.n_br,
                               self.np_pk, self.np_pv, np.float32, rows=rows)
 
 
