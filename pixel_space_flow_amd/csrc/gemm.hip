@@ -515,11 +515,18 @@ __global__ __launch_bounds__(64 * NW, 1) void gemm_fast_kernel(GemmParams p, int
         if (kt + 2 < KT) issue(kt + 2, st);
         rd(cur ^ 1, st ^ 1, 0);
       }
+      // the wave that is behind within the tile gets the higher priority, so the two waves of a
+      // SIMD stay level and reach the barrier together
+      if (ks == 0) __builtin_amdgcn_s_setprio(2);
+      else if (ks == 1) __builtin_amdgcn_s_setprio(1);
+      else if (ks == 2) __builtin_amdgcn_s_setprio(0);
+      else __builtin_amdgcn_s_setprio(3);
       __builtin_amdgcn_sched_barrier(0);
       mma(cur);
       __builtin_amdgcn_sched_barrier(0);
     }
   }
+  __builtin_amdgcn_s_setprio(0);
 
   // ---- epilogue through LDS: each wave stages one 32x32 fp32 block at a time, then every lane
   // owns 16 consecutive columns of one row (lanes 2r, 2r+1 cover row r), so global accesses are
@@ -565,6 +572,237 @@ __global__ __launch_bounds__(64 * NW, 1) void gemm_fast_kernel(GemmParams p, int
         const int row = row0 + r;
         const int col0 = (EPI == EPI_SWIGLU) ? tn * (BN / 2) + (wn * (NBW / 2) + (nb >> 1)) * 32 + cc
                                              : tn * BN + wn * (BN / WN) + nb * 32 + cc;
+        const int ncols = (EPI == EPI_SWIGLU) ? p.swiglu_I : p.N;
+        epi_row16<EPI>(p, row, col0, ncols, v);
+      }
+    }
+  }
+}
+
+// bf16 GEMM for the residual and QKV projections: 256 x 256 output tiles, k consumed 32 at a time
+// through a ring of four LDS
+// stages (32 KB each: 256 rows x 64 B of A, the same of B).  8 waves in a 2 x 4 grid, each
+// 128 x 64 (4 x 2 MFMA blocks of 32 x 32, v_mfma_f32_32x32x16_bf16), two waves per SIMD.
+// Operands go global -> LDS by buffer loads that write LDS directly (16 B per lane).  The DMA
+// of each k-tile is split in two halves sent in consecutive k-steps, interleaved with MFMAs, so
+// the vector-memory path sees a steady stream; three k-tiles are in flight while one is read.
+template <int EPI, bool GROUPED, bool GATHER>
+__global__ __launch_bounds__(512, 1) void gemm_k32_kernel(GemmParams p, int n_col_tiles) {
+  constexpr int NBW = 2;                     // 32-column MFMA blocks per wave
+  constexpr int KB = 32;                     // k per stage
+  constexpr int ROWB = KB * 2;               // bytes of one LDS row (64)
+  constexpr int STG = (BM + BN) * ROWB;      // 32 KB
+  constexpr int NST = 4;
+  extern __shared__ __attribute__((aligned(16))) char smem[];
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wm = wave >> 2, wn = wave & 3;
+
+  int tn, row0, rows, expert = 0;
+  if (GROUPED) {
+    const int t = blockIdx.x / n_col_tiles;
+    tn = blockIdx.x - t * n_col_tiles;
+    expert = p.tiles[3 * t];
+    if (expert < 0) return;
+    row0 = p.tiles[3 * t + 1];
+    rows = p.tiles[3 * t + 2];
+  } else {
+    const int n_m = (p.M + BM - 1) / BM;
+    const int n_t = n_m * n_col_tiles;
+    const int id = xcd_remap(blockIdx.x, n_t);
+    const int GROUP = 8;
+    const int per_group = GROUP * n_col_tiles;
+    const int g = id / per_group;
+    const int first_m = g * GROUP;
+    const int gsz = min(n_m - first_m, GROUP);
+    const int r_in = id - g * per_group;
+    tn = r_in / gsz;
+    row0 = (first_m + r_in % gsz) * BM;
+    rows = min(BM, p.M - row0);
+  }
+  // LDS rows are 64 B (4 chunks of 16 B).  ds_read_b128 serves 16 lanes per cycle over a 256 B
+  // (64-bank) window, i.e. four rows; chunk c of row r is stored at c ^ ((r >> 2) & 3), so the 16
+  // rows read together at one logical chunk occupy 16 distinct slots.  One DMA instruction fills
+  // 1 KB = 16 rows: lane l writes row l >> 2, stored chunk l & 3, which holds logical chunk
+  // (l & 3) ^ ((l >> 4) & 3) (the groups start at multiples of 16 rows).
+  const int lrow = lane >> 2;
+  const int lch = (lane & 3) ^ ((lane >> 4) & 3);
+  const uint32_t lda2 = (uint32_t)p.lda * 2, ldb2 = (uint32_t)p.ldb * 2;
+  // wave w sends row groups 2w and 2w + 1 (16 rows each) of both operands
+
+  __amdgpu_buffer_rsrc_t ra;
+  uint32_t avoff[2];
+  if (GATHER) {
+    ra = make_rsrc(p.A, 0x7fffffff);
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const int r = (2 * wave + h) * 16 + lrow;
+      avoff[h] = (uint32_t)p.a_rows[row0 + min(r, rows - 1)] * lda2 + lch * 16;
+    }
+  } else {
+    ra = make_rsrc((const bf16*)p.A + (int64_t)row0 * p.lda, (uint32_t)rows * lda2);
+    avoff[0] = avoff[1] = lrow * lda2 + lch * 16;
+  }
+  const bf16* Bexp = (const bf16*)p.B + (GROUPED ? (int64_t)expert * p.b_expert_stride : 0);
+  __amdgpu_buffer_rsrc_t rb;
+  uint32_t bsoff[2];
+  if (p.bmode == 1) {
+    rb = make_rsrc(Bexp, (uint32_t)(2 * p.swiglu_I) * ldb2);
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const int r0 = (2 * wave + h) * 16;
+      const int nb = r0 >> 5;
+      bsoff[h] = (uint32_t)(((nb & 1) ? p.swiglu_I : 0) + tn * (BN / 2) + (nb >> 1) * 32 + (r0 & 31)) * ldb2;
+    }
+  } else {
+    const int nvalid = min(BN, p.N - tn * BN);
+    rb = make_rsrc(Bexp + (int64_t)tn * BN * p.ldb, (uint32_t)nvalid * ldb2);
+#pragma unroll
+    for (int h = 0; h < 2; ++h) bsoff[h] = (uint32_t)((2 * wave + h) * 16) * ldb2;
+  }
+  const uint32_t bvoff = lrow * ldb2 + lch * 16;
+
+  const int KT = p.K / KB;
+  // Half h of the DMA of k-tile t (row groups 2w + h of A and of B) into stage t % 4.  Tiles past
+  // the end reload the last one into a stage nobody reads again, so every k-step sends the same
+  // number of loads and the vmcnt arithmetic below holds throughout.
+  auto dma_half = [&](int t, int h) {
+    char* As = smem + (t & (NST - 1)) * STG;
+    char* Bs = As + BM * ROWB;
+    const uint32_t kb = (uint32_t)min(t, KT - 1) * ROWB;
+    const int g = 2 * wave + h;
+    if (GATHER)
+      dma16(ra, As + g * 1024, avoff[h], kb);
+    else
+      dma16(ra, As + g * 1024, avoff[h], g * 16 * lda2 + kb);
+    dma16(rb, Bs + g * 1024, bvoff, bsoff[h] + kb);
+  };
+
+  f32x16 acc[4][NBW];
+#pragma unroll
+  for (int a = 0; a < 4; ++a)
+#pragma unroll
+    for (int b = 0; b < NBW; ++b)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) acc[a][b][e] = 0.f;
+
+  const int lr = lane & 31, lh = lane >> 5;
+  const int arow0 = (wm * 128 + lr) * ROWB, brow0 = (wn * 64 + lr) * ROWB;
+  const int sw = (lr >> 2) & 3;
+  bf16x8 fa[2][4], fb[2][NBW];
+  auto rd = [&](int set, int stage, int ks) {
+    const char* As = smem + stage * STG;
+    const char* Bs = As + BM * ROWB;
+    const int ch = ((ks * 2 + lh) ^ sw) << 4;
+    // in the order the MFMAs consume them
+    fa[set][0] = *(const bf16x8*)(As + arow0 + ch);
+#pragma unroll
+    for (int nb = 0; nb < NBW; ++nb) fb[set][nb] = *(const bf16x8*)(Bs + brow0 + nb * 32 * ROWB + ch);
+#pragma unroll
+    for (int mb = 1; mb < 4; ++mb) fa[set][mb] = *(const bf16x8*)(As + arow0 + mb * 32 * ROWB + ch);
+  };
+  auto mma = [&](int set) {
+#pragma unroll
+    for (int mb = 0; mb < 4; ++mb)
+#pragma unroll
+      for (int nb = 0; nb < NBW; ++nb)
+        acc[mb][nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[set][mb], fb[set][nb], acc[mb][nb], 0, 0, 0);
+  };
+  // one k-step: 8 MFMAs, each followed by one of the step's 6 LDS reads, the first two also by
+  // one DMA instruction
+  auto interleave = [&]() {
+#pragma unroll
+    for (int i = 0; i < 6; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // MFMA
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);   // DS read
+      if (i < 2) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);   // VMEM (LDS-DMA)
+    }
+    __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+  };
+  // vmcnt(8) lgkmcnt(0): all but the last 8 loads (the next two k-tiles), every LDS access
+  constexpr int WAIT_TILE = 8 | (7 << 4);
+
+  // Prologue: k-tiles 0-2 whole and the first half of tile 3; wait for tile 0.
+  dma_half(0, 0); dma_half(0, 1);
+  dma_half(1, 0); dma_half(1, 1);
+  dma_half(2, 0); dma_half(2, 1);
+  dma_half(3, 0);
+  __builtin_amdgcn_s_waitcnt(10 | (7 << 4));
+  __builtin_amdgcn_s_barrier();
+  rd(0, 0, 0);
+  // Steady state, k-tile kt in stage kt % 4.  Step 0 sends the second half of tile kt+3; step 1
+  // waits for tile kt+1 (sent at least two k-tiles earlier), meets the other waves (so tile kt's
+  // stage is free and tile kt+1's complete), reads tile kt+1's first fragments and sends the
+  // first half of tile kt+4 into tile kt's stage.
+  for (int kt = 0; kt + 1 < KT; ++kt) {
+    const int st = kt & (NST - 1);
+    // a wave past the barrier runs at the higher priority, so one that is ahead lets its SIMD
+    // partner catch up and the two meet the barrier together
+    __builtin_amdgcn_s_setprio(0);
+    rd(1, st, 1);
+    dma_half(kt + 3, 1);
+    mma(0);
+    interleave();
+    __builtin_amdgcn_sched_barrier(0);
+    __builtin_amdgcn_s_waitcnt(WAIT_TILE);
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_s_setprio(1);
+    rd(0, (kt + 1) & (NST - 1), 0);
+    dma_half(kt + 4, 0);
+    mma(1);
+    interleave();
+    __builtin_amdgcn_sched_barrier(0);
+  }
+  __builtin_amdgcn_s_setprio(0);
+  rd(1, (KT - 1) & (NST - 1), 1);
+  mma(0);
+  mma(1);
+
+  // ---- epilogue through LDS: each wave stages one 32x32 fp32 block at a time, then every lane
+  // owns 16 consecutive columns of one row (lanes 2r, 2r+1 cover row r), so global accesses are
+  // 16-byte vectors and the per-row index math runs once per block.
+  __builtin_amdgcn_s_waitcnt(0);   // the trailing reloads have landed
+  __syncthreads();   // every wave is done with the LDS stages
+  constexpr int TS = 36;                                   // padded fp32 row stride of a staged block
+  float* T0 = (float*)smem + wave * (2 * 32 * TS);
+  float* T1 = T0 + 32 * TS;
+  const int rr = lane >> 1, cc = (lane & 1) * 16;
+#pragma unroll
+  for (int mb = 0; mb < 4; ++mb) {
+#pragma unroll
+    for (int nb = 0; nb < NBW; ++nb) {
+      if (EPI == EPI_SWIGLU && (nb & 1)) continue;       // consumed together with its gate block
+#pragma unroll
+      for (int e = 0; e < 16; ++e) T0[((e >> 2) * 8 + lh * 4 + (e & 3)) * TS + lr] = acc[mb][nb][e];
+      if (EPI == EPI_SWIGLU) {
+#pragma unroll
+        for (int e = 0; e < 16; ++e) T1[((e >> 2) * 8 + lh * 4 + (e & 3)) * TS + lr] = acc[mb][nb + 1][e];
+      }
+      __builtin_amdgcn_s_waitcnt(0xc07f);                   // lgkmcnt(0): staged values written
+      __builtin_amdgcn_wave_barrier();
+      float v[16];
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const float4 f = *(const float4*)(T0 + rr * TS + cc + 4 * q);
+        v[4 * q] = f.x; v[4 * q + 1] = f.y; v[4 * q + 2] = f.z; v[4 * q + 3] = f.w;
+      }
+      if (EPI == EPI_SWIGLU) {
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const float4 f = *(const float4*)(T1 + rr * TS + cc + 4 * q);
+          v[4 * q] = silu_f(v[4 * q]) * f.x;
+          v[4 * q + 1] = silu_f(v[4 * q + 1]) * f.y;
+          v[4 * q + 2] = silu_f(v[4 * q + 2]) * f.z;
+          v[4 * q + 3] = silu_f(v[4 * q + 3]) * f.w;
+        }
+      }
+      __builtin_amdgcn_s_waitcnt(0xc07f);                   // reads done before the next block overwrites
+      __builtin_amdgcn_wave_barrier();
+      const int r = wm * 128 + mb * 32 + rr;
+      if (r < rows) {
+        const int row = row0 + r;
+        const int col0 = (EPI == EPI_SWIGLU) ? tn * (BN / 2) + (wn * (NBW / 2) + (nb >> 1)) * 32 + cc
+                                             : tn * BN + wn * 64 + nb * 32 + cc;
         const int ncols = (EPI == EPI_SWIGLU) ? p.swiglu_I : p.N;
         epi_row16<EPI>(p, row, col0, ncols, v);
       }
@@ -668,6 +906,14 @@ hipError_t launch_fast(const GemmParams& p, int epi, int grid, int n_col_tiles, 
   const size_t lds = 2 * STAGE_BYTES;
 #define PSF_L(E)                                                                                  \
   case E: {                                                                                        \
+    if (E != EPI_SWIGLU) {                                                                         \
+      auto k = gemm_k32_kernel<E, GROUPED, GATHER>;                                                \
+      hipError_t e = hipFuncSetAttribute((const void*)k, hipFuncAttributeMaxDynamicSharedMemorySize, \
+                                         (int)lds);                                                \
+      if (e != hipSuccess) return e;                                                               \
+      hipLaunchKernelGGL(k, dim3(grid), dim3(512), lds, s, p, n_col_tiles);                        \
+      return hipGetLastError();                                                                    \
+    }                                                                                              \
     auto k = fast_waves() == 4 ? gemm_fast_kernel<E, GROUPED, GATHER, 4> : gemm_fast_kernel<E, GROUPED, GATHER, 8>; \
     hipError_t e = hipFuncSetAttribute((const void*)k, hipFuncAttributeMaxDynamicSharedMemorySize, \
                                        (int)lds);                                                  \
