@@ -115,6 +115,40 @@ def make_device_tower(psf, w, seed=0):
     return layers_dev, glob, pk, pv, x
 
 
+def merge_lora_at_load(psf, lw, layers_dev, seed=1):
+    """Draw a rank-r LoRA per layer (A ~ N(0, 0.02), B ~ N(0, 1e-3), seeded device RNG) and fold
+    it into each layer's weights in place with gen_block_lora_merge; returns the merge time (ms)."""
+    import torch
+    d = lw.dims
+    g = torch.Generator(device="cuda")
+    g.manual_seed(seed)
+    D, I, r = d.hidden, d.mlp_intermediate, d.lora_rank
+    qd, kd = d.n_q_heads * d.head_dim, d.n_kv_heads * d.head_dim
+    ins = {"q": D, "k": D, "v": D, "o": qd, "gate": D, "up": D, "down": I}
+    outs = {"q": qd, "k": kd, "v": kd, "o": D, "gate": I, "up": I, "down": D}
+    dims = psf.make_dims(d, psf.GEN_BF16)
+
+    def randn(*shape, std):
+        t = torch.empty(*shape, device="cuda", dtype=torch.float32)
+        t.normal_(0.0, std, generator=g)
+        return t.to(torch.bfloat16)
+    loras = []
+    for lwd in layers_dev:
+        full = dict(lwd)
+        for s in ("q", "k", "v", "o", "gate", "up", "down"):
+            full[f"lora_a_{s}"] = randn(r, ins[s], std=0.02)
+            full[f"lora_b_{s}"] = randn(outs[s], r, std=1e-3)
+        loras.append(full)
+    torch.cuda.synchronize()
+    start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    start.record()
+    for lwd, full in zip(layers_dev, loras):
+        psf.block_lora_merge(dims, psf.make_weights(full), lwd["w_qkv"], lwd["w_o"], lwd["w_gate_up"], lwd["w_down"])
+    stop.record()
+    torch.cuda.synchronize()
+    return start.elapsed_time(stop)
+
+
 def cpu_baseline(w, seed=0):
     """The oracle (numpy fp32, as it stands) on one full-size gen block of the workload (both
     branches, all tokens), scaled to the 36-layer step; the patch embed and head are < 0.3 %
@@ -136,7 +170,7 @@ def cpu_baseline(w, seed=0):
     step_s = dt * w.n_layers
     return {"value": w.batch * w.n_tokens / step_s, "unit": "image tokens/s", "cores": int(threads),
             "kind": "oracle",
-            "sample": (f"one gen block of the workload (2 branches x {w.n_tokens} tokens, prefix {w.prefix_len}) "
+            "sample": (f"one gen block of the workload ({w.batch} x {w.n_tokens} tokens, prefix {w.prefix_len}) "
                        f"in numpy fp32 took {dt:.2f} s; scaled x{w.n_layers} layers"),
             "host": platform.processor() or platform.machine(), "numpy": np.__version__}
 
@@ -181,6 +215,9 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--config", type=int, default=2)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--variant", choices=("cfg", "lora-merged-cfg1"), default="cfg",
+                    help="cfg: the 2048^2 two-branch CFG step (default); lora-merged-cfg1: one branch at "
+                         "1024^2 with cfg 1 and a rank-32 LoRA folded into the weights at load")
     ap.add_argument("--kernel", choices=("gate_up", "attention", "copy"),
                     help="run only this kernel at the workload's shapes, --steps times (for counter runs)")
     args = ap.parse_args()
@@ -194,13 +231,23 @@ def main():
     import workloads as W
 
     w = W.CONFIGS[args.config]
-    assert w.unit == "tower" and not w.dims.is_moe and not w.dims.lora_rank, "bench times the dense CFG tower step"
+    lora_w = None
+    if args.variant == "lora-merged-cfg1":
+        # the 8-step distilled-LoRA fast path: one image, one branch, cfg 1, LoRA fused at load
+        lora_w = W.scaled(W.CONFIGS[3], name="qwen3-8b-tower36-1024px-cfg1-lora-merged", n_img=1, n_br=1,
+                          cfg_scale=1.0, n_steps=8, prefix_cache_samples=0)
+        w = W.scaled(lora_w, dims=W.BlockDims(**{**W.dataclasses.asdict(lora_w.dims), "lora_rank": 0,
+                                                    "lora_alpha": 0.0}))
+    assert w.unit == "tower" and not w.dims.is_moe and not w.dims.lora_rank, "bench times the dense tower step"
     torch.cuda.set_device(0)
     if args.kernel:
         run_kernel_only(psf, w, args.kernel, args.steps)
         return
     dims = psf.make_dims(w.dims, psf.GEN_BF16)
     layers_dev, glob, pk, pv, x = make_device_tower(psf, w)
+    merge_ms = None
+    if lora_w is not None:
+        merge_ms = merge_lora_at_load(psf, lora_w, layers_dev)
     layers = [psf.make_weights(l) for l in layers_dev]
     ws = psf.alloc_workspace(psf.workspace_size(dims, w.n_img, w.n_br, w.n_tokens, w.prefix_len))
     xo = torch.empty_like(x)
@@ -234,7 +281,9 @@ def main():
     gu_tflops = gu_flops / (gu_avg_ms * 1e-3) / 1e12
     props = torch.cuda.get_device_properties(0)
     out = {
-        "metric": "gen-tower image tokens/s per denoise step at 2048^2 CFG; % bf16 MFMA peak",
+        "metric": ("gen-tower image tokens/s per denoise step at 2048^2 CFG; % bf16 MFMA peak" if lora_w is None else
+                   "gen-tower image tokens/s per denoise step at 1024^2, one branch (cfg 1), LoRA merged at load; "
+                   "% bf16 MFMA peak"),
         "value": round(tokens / (ms * 1e-3), 1),
         "unit": "image tokens/s",
         "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
@@ -245,19 +294,24 @@ def main():
                    "image_tokens_per_branch": w.n_tokens, "cfg_branches": w.n_br, "prefix_tokens": w.prefix_len,
                    "hidden": d.hidden, "heads": [d.n_q_heads, d.n_kv_heads, d.head_dim],
                    "mlp_intermediate": d.mlp_intermediate, "cfg_scale": w.cfg_scale, "shift": w.shift,
-                   "t_eps": w.t_eps, "schedule_step": "0 of 50", "global_batch": w.batch, "seq_len": w.n_tokens},
+                   "t_eps": w.t_eps, "schedule_step": f"0 of {w.n_steps}", "global_batch": w.batch, "seq_len": w.n_tokens},
         "pct_bf16_peak": round(100 * tflops / PEAK_BF16_TFLOPS, 2),
         "tflops": round(tflops, 1),
         "step_tflop": round(fl["total"] / 1e12, 3),
         "image_tokens_per_s_per_output_image": round(w.n_tokens / (ms * 1e-3), 1),
-        "roofline": {"kernel": "gate_up SwiGLU GEMM (M=8192, N=2x12288, K=4096)", "bound": "mfma",
+        "roofline": {"kernel": f"gate_up SwiGLU GEMM (M={tokens}, N=2x{d.mlp_intermediate}, K={d.hidden})",
+                     "bound": "mfma",
                      "achieved": round(gu_tflops, 1), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-                     "frac": round(gu_tflops / PEAK_BF16_TFLOPS, 4), "traffic": measured_traffic(),
+                     "frac": round(gu_tflops / PEAK_BF16_TFLOPS, 4),
+                     "traffic": measured_traffic() if lora_w is None else None,
                      "algorithmic_bytes": 2 * (tokens * d.hidden + 2 * d.mlp_intermediate * d.hidden
                                                + tokens * d.mlp_intermediate),
                      "avg_launch_ms": round(gu_avg_ms, 4), "launches_timed": gu_n},
         "device": {"name": props.name, "cus": props.multi_processor_count},
     }
+    if lora_w is not None:
+        out["config"]["lora"] = {"rank": lora_w.dims.lora_rank, "alpha": lora_w.dims.lora_alpha,
+                                 "sites": "q,k,v,o,gate,up,down", "merge_ms_all_layers": round(merge_ms, 3)}
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(W.scaled(w, n_layers=w.n_layers))
     print(json.dumps(out), flush=True)

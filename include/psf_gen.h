@@ -130,6 +130,18 @@ int gen_tower_step(const gen_block_dims* dims, int n_layers, const gen_block_wei
                    const void* const* prefix_k, const void* const* prefix_v, const int* prefix_len,
                    float* x_out, float* x0_out, void* workspace, size_t workspace_bytes, void* stream);
 
+/* Merged-LoRA weights for the fast path in which a LoRA (such as the 8-step distilled one) is
+ * fused into the base weights at load (vllm-omni recipe "SenseNova-U1.5", 8-step distilled LoRA;
+ * DiffSynth-Studio "SenseNova-U1", 快速推理).  For every site s (q, k, v, o, gate, up, down) whose
+ * lora_a/lora_b are set, the site's rows of the base matrix become
+ *   W_s' = W_s + (lora_alpha / lora_rank) lora_b[s] lora_a[s]
+ * summed in float32 and rounded once to dims.dtype; sites without LoRA are copied.  The merged
+ * block then runs with lora_rank = 0 and the four output matrices in place of w_qkv, w_o,
+ * w_gate_up, w_down.  dims.lora_rank must be > 0 (dense block); outputs are device buffers of the
+ * base matrices' shapes, 16-byte aligned, and may equal the inputs (merge in place). */
+int gen_block_lora_merge(const gen_block_dims* dims, const gen_block_weights* w, void* w_qkv_out,
+                         void* w_o_out, void* w_gate_up_out, void* w_down_out, void* stream);
+
 /* CFG mix and shifted-flow Euler update, in place, float32, n elements:
  *   x0g = cfg_scale == 1 ? x0_cond : x0_uncond + cfg_scale (x0_cond - x0_uncond)
  *   x  <- x + (sigma_next - sigma) (x - x0g) / max(sigma, t_eps)

@@ -12,7 +12,7 @@ import numpy as np
 
 __all__ = [
     "shift_sigma", "sigma_schedule", "rms_norm", "rope_cos_sin", "apply_rope", "attention",
-    "silu", "swiglu", "lora_delta", "linear", "route_topk", "moe_mlp", "gen_block",
+    "silu", "swiglu", "lora_delta", "merge_lora", "linear", "route_topk", "moe_mlp", "gen_block",
     "patchify", "unpatchify", "timestep_features", "timestep_embed", "tower_tokens", "tower_x0",
     "cfg_mix", "euler_step", "tower_step", "noisy_sample",
 ]
@@ -117,6 +117,21 @@ def lora_delta(x: np.ndarray, a: np.ndarray, b: np.ndarray, alpha: float, rank: 
     B = lora_up [out, r] ([lilting] lora_down / lora_up / .alpha naming;
     [DiffSynth] 模型训练: targets q/k/v/o/gate/up/down of the gen tower)."""
     return x.dtype.type(alpha / rank) * ((x @ a.T) @ b.T)
+
+
+def merge_lora(wts: Dict[str, np.ndarray], dims) -> Dict[str, np.ndarray]:
+    """Base weights with every LoRA site folded in: W_s + (alpha/rank) B_s A_s on the site's
+    rows (q, k, v rows of w_qkv; w_o; gate, up rows of w_gate_up; w_down).  The fast path of
+    the 8-step distilled LoRA fuses it at load ([U1.5-recipe] 8-step distilled LoRA;
+    [DiffSynth] 快速推理).  Returns a new dict without the lora_* entries."""
+    s = wts["w_qkv"].dtype.type(dims.lora_alpha / dims.lora_rank)
+    delta = {site: s * (wts[f"lora_b_{site}"] @ wts[f"lora_a_{site}"]) for site in ("q", "k", "v", "o", "gate", "up", "down")}
+    out = {k: v for k, v in wts.items() if not k.startswith("lora_")}
+    out["w_qkv"] = wts["w_qkv"] + np.concatenate([delta["q"], delta["k"], delta["v"]])
+    out["w_o"] = wts["w_o"] + delta["o"]
+    out["w_gate_up"] = wts["w_gate_up"] + np.concatenate([delta["gate"], delta["up"]])
+    out["w_down"] = wts["w_down"] + delta["down"]
+    return out
 
 
 def route_topk(u: np.ndarray, w_router: np.ndarray, k: int):

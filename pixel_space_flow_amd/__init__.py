@@ -19,7 +19,7 @@ LORA_SITES = ("q", "k", "v", "o", "gate", "up", "down")
 
 # every symbol declared in include/psf_gen.h
 EXPORTS = ("gen_block_forward", "gen_tower_step", "flow_euler_cfg", "gen_moe_route", "gen_workspace_size",
-           "gen_sigma_schedule", "gen_last_error",
+           "gen_sigma_schedule", "gen_last_error", "gen_block_lora_merge",
            # include/psf_gen_ops.h
            "gen_op_rmsnorm", "gen_op_linear", "gen_op_qknorm_rope", "gen_op_attention", "gen_op_workspace_size",
            "gen_timing_begin", "gen_timing_end")
@@ -61,6 +61,7 @@ def _load():
     lib.gen_tower_step.argtypes = [P(BlockDimsC), i, P(BlockWeightsC), vp, vp, vp, vp, vp, vp, i, i, i, i,
                                    P(f), P(f), f, i, f, P(vp), P(vp), P(i), vp, vp, vp, sz, vp]
     lib.flow_euler_cfg.argtypes = [vp, vp, vp, sz, f, f, f, f, vp]
+    lib.gen_block_lora_merge.argtypes = [P(BlockDimsC), P(BlockWeightsC), vp, vp, vp, vp, vp]
     lib.gen_moe_route.argtypes = [vp, vp, i, i, i, i, i, vp, vp, vp]
     lib.gen_workspace_size.argtypes = [P(BlockDimsC), i, i, i, i]
     lib.gen_workspace_size.restype = sz
@@ -157,6 +158,14 @@ def block_forward(dims: BlockDimsC, weights: BlockWeightsC, hidden, prefix_k, pr
     _check(lib.gen_block_forward(ctypes.byref(dims), ctypes.byref(weights), hidden.data_ptr(), B, N,
                                  _ptr_array(prefix_k), _ptr_array(prefix_v), plen, _ptr(topk_out),
                                  workspace.data_ptr(), workspace.numel() * workspace.element_size(), _stream(stream)))
+
+
+def block_lora_merge(dims: BlockDimsC, weights: BlockWeightsC, w_qkv_out, w_o_out, w_gate_up_out, w_down_out,
+                     stream=None):
+    """Fold each LoRA site of `weights` into the base matrices (outputs may be the inputs)."""
+    _check(lib.gen_block_lora_merge(ctypes.byref(dims), ctypes.byref(weights), w_qkv_out.data_ptr(),
+                                    w_o_out.data_ptr(), w_gate_up_out.data_ptr(), w_down_out.data_ptr(),
+                                    _stream(stream)))
 
 
 def tower_step(dims: BlockDimsC, layers: Sequence[BlockWeightsC], glob: dict, x_t, n_br: int, sigma, sigma_next,

@@ -463,6 +463,39 @@ int gen_block_forward(const gen_block_dims* dims, const gen_block_weights* w, vo
   return rc ? rc : ok();
 }
 
+int gen_block_lora_merge(const gen_block_dims* dims, const gen_block_weights* w, void* w_qkv_out, void* w_o_out,
+                         void* w_gate_up_out, void* w_down_out, void* stream) {
+  int rc = check_dims(dims);
+  if (rc) return rc;
+  if (dims->lora_rank == 0) return fail(GEN_EINVAL, "dims.lora_rank is 0: nothing to merge");
+  if ((rc = check_weights(dims, w, 0))) return rc;
+  void* outs[4] = {w_qkv_out, w_o_out, w_gate_up_out, w_down_out};
+  for (void* o : outs)
+    if (!o || !aligned16(o)) return fail(GEN_EINVAL, "merged weight outputs must be non-NULL and 16-byte aligned");
+  const int D = dims->hidden, hd = dims->head_dim, Hq = dims->n_q_heads, Hkv = dims->n_kv_heads;
+  const int I = dims->mlp_intermediate, r = dims->lora_rank;
+  const float scale = dims->lora_alpha / (float)r;
+  // site s: (matrix, first row, rows, in)
+  const void* mats[4] = {w->w_qkv, w->w_o, w->w_gate_up, w->w_down};
+  const int mat[7] = {0, 0, 0, 1, 2, 2, 3};
+  const int row0[7] = {0, Hq * hd, (Hq + Hkv) * hd, 0, 0, I, 0};
+  const int rows[7] = {Hq * hd, Hkv * hd, Hkv * hd, D, I, I, D};
+  const int ins[7] = {D, D, D, Hq * hd, D, D, I};
+  hipStream_t s = (hipStream_t)stream;
+  for (int site = 0; site < 7; ++site) {
+    const int m = mat[site];
+    const size_t off = (size_t)row0[site] * ins[site];
+    if (dims->dtype == GEN_BF16) {
+      HIP_TRY(lora_merge<bf16>((const bf16*)mats[m] + off, (const bf16*)w->lora_a[site], (const bf16*)w->lora_b[site],
+                               (bf16*)outs[m] + off, rows[site], ins[site], r, scale, s));
+    } else {
+      HIP_TRY(lora_merge<float>((const float*)mats[m] + off, (const float*)w->lora_a[site], (const float*)w->lora_b[site],
+                                (float*)outs[m] + off, rows[site], ins[site], r, scale, s));
+    }
+  }
+  return ok();
+}
+
 int gen_tower_step(const gen_block_dims* dims, int n_layers, const gen_block_weights* layers, const void* w_in,
                    const void* temb_w1, const void* temb_w2, const void* g_final, const void* w_out, const float* x_t,
                    int n_img, int n_br, int H, int W, const float* sigma, const float* sigma_next, float cfg_scale,

@@ -245,6 +245,48 @@ __global__ __launch_bounds__(256) void pack_vt_kernel(const T* __restrict__ qkv,
   *(u32x4*)(Vt + (((int64_t)b * Hkv + g) * d + dd) * Lpad + j0) = V::pack(f);
 }
 
+// ---------------------------------------------------------------- LoRA merge
+// Wo[o, i] = W[o, i] + scale * sum_r B[o, r] A[r, i] for a [64 x 256] tile per workgroup: the
+// 64 rows of B sit in LDS (every lane reads the same entry), each lane owns one column i and
+// keeps 64 fp32 sums; the sum is added to W in fp32 and rounded once.  A == nullptr copies W.
+template <typename T>
+__global__ __launch_bounds__(256) void lora_merge_kernel(const T* __restrict__ W, const T* __restrict__ A,
+                                                         const T* __restrict__ B, T* __restrict__ Wo, int out, int in,
+                                                         int rank, float scale) {
+  __shared__ float Bs[64][129];
+  const int i = blockIdx.x * 256 + threadIdx.x;
+  const int o0 = blockIdx.y * 64;
+  const int nrow = min(64, out - o0);
+  if (A) {
+    for (int t = threadIdx.x; t < 64 * rank; t += 256) {
+      const int o = t / rank, r = t - o * rank;
+      Bs[o][r] = o < nrow ? to_f(B[(int64_t)(o0 + o) * rank + r]) : 0.f;
+    }
+  }
+  __syncthreads();
+  if (i >= in) return;
+  float acc[64];
+#pragma unroll
+  for (int o = 0; o < 64; ++o) acc[o] = 0.f;
+  if (A) {
+    for (int rc = 0; rc < rank; rc += 8) {
+      float a[8];
+#pragma unroll
+      for (int k = 0; k < 8; ++k) a[k] = to_f(A[(int64_t)(rc + k) * in + i]);
+#pragma unroll
+      for (int o = 0; o < 64; ++o)
+#pragma unroll
+        for (int k = 0; k < 8; ++k) acc[o] = fmaf(Bs[o][rc + k], a[k], acc[o]);
+    }
+  }
+#pragma unroll
+  for (int o = 0; o < 64; ++o)
+    if (o < nrow) {
+      const int64_t at = (int64_t)(o0 + o) * in + i;
+      Wo[at] = from_f<T>(fmaf(scale, acc[o], to_f(W[at])));
+    }
+}
+
 // ---------------------------------------------------------------- patchify
 template <typename T>
 __global__ __launch_bounds__(256) void patchify_kernel(const float* __restrict__ x, T* __restrict__ out, int n_img,
@@ -398,6 +440,17 @@ hipError_t pack_kv_knorm(const bf16* qkv, int64_t ld, const SeqInfo& si, int Hq,
   hipLaunchKernelGGL(pack_vt_kernel<bf16>, gv, dim3(256), 0, s, qkv, ld, si, Hq, Hkv, d, Lpad, Vt);
   return hipGetLastError();
 }
+template <typename T>
+hipError_t lora_merge(const T* W, const T* A, const T* B, T* Wo, int out, int in, int rank, float scale,
+                      hipStream_t s) {
+  if (out <= 0 || in <= 0) return hipSuccess;
+  dim3 grid((in + 255) / 256, (out + 63) / 64);
+  hipLaunchKernelGGL(lora_merge_kernel<T>, grid, dim3(256), 0, s, W, A, B, Wo, out, in, rank, scale);
+  return hipGetLastError();
+}
+template hipError_t lora_merge<bf16>(const bf16*, const bf16*, const bf16*, bf16*, int, int, int, float, hipStream_t);
+template hipError_t lora_merge<float>(const float*, const float*, const float*, float*, int, int, int, float, hipStream_t);
+
 template hipError_t pack_kv<bf16>(const bf16*, int64_t, const SeqInfo&, int, int, int, int, bf16*, bf16*, hipStream_t);
 template hipError_t pack_kv<float>(const float*, int64_t, const SeqInfo&, int, int, int, int, float*, float*, hipStream_t);
 

@@ -130,3 +130,16 @@ def test_flow_euler_cfg_rejects_bad_arguments_on_host(psf):
     assert f(4096, 4096, None, 16, 4.0, 1.0, 0.9, 0.02, None) == psf.GEN_EINVAL   # uncond needed for cfg != 1
     assert f(4100, 4096, 4096, 16, 4.0, 1.0, 0.9, 0.02, None) == psf.GEN_EINVAL   # unaligned
     assert f(4096, 4096, 4096, 16, 4.0, 0.0, 0.0, 0.0, None) == psf.GEN_EINVAL    # zero denominator
+
+
+def test_block_lora_merge_rejects_bad_arguments_on_host(psf):
+    f = psf.lib.gen_block_lora_merge
+    d = dims(psf)                                    # lora_rank 0
+    w = fake_weights(psf)
+    assert f(ctypes.byref(d), ctypes.byref(w), 4096, 4096, 4096, 4096, None) == psf.GEN_EINVAL
+    assert "nothing to merge" in psf.last_error()
+    d.lora_rank, d.lora_alpha = 32, 32.0
+    assert f(ctypes.byref(d), ctypes.byref(w), None, 4096, 4096, 4096, None) == psf.GEN_EINVAL
+    assert f(ctypes.byref(d), ctypes.byref(w), 4096, 4100, 4096, 4096, None) == psf.GEN_EINVAL   # unaligned
+    d.lora_rank = 12
+    assert f(ctypes.byref(d), ctypes.byref(w), 4096, 4096, 4096, 4096, None) == psf.GEN_EUNSUPPORTED

@@ -346,6 +346,17 @@ def test_block_lora_equals_merged_weights():
                                rtol=1e-10, atol=1e-10)
 
 
+def test_merge_lora_reproduces_the_unmerged_block():
+    # the oracle's merge, run with LoRA off, against the unmerged LoRA block (itself pinned
+    # above by the hand-written merge and by B = 0)
+    d, wts, h, pk, pv = small_block_case(lora=True)
+    base_d = W.small_dims(hidden=64, n_q_heads=4, n_kv_heads=2, head_dim=16, mlp_intermediate=96)
+    m = O.merge_lora(wts, d)
+    assert not any(k.startswith("lora_") for k in m)
+    np.testing.assert_allclose(O.gen_block(h, m, base_d, pk, pv), O.gen_block(h, wts, d, pk, pv),
+                               rtol=1e-10, atol=1e-10)
+
+
 def test_block_moe_all_experts_equals_dense_mixture_of_identical_experts():
     d = W.small_dims(hidden=64, n_q_heads=4, n_kv_heads=2, head_dim=16, mlp_intermediate=0,
                      n_experts=4, top_k=2, expert_intermediate=48)
