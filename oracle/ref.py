@@ -13,6 +13,7 @@ import numpy as np
 __all__ = [
     "shift_sigma", "sigma_schedule", "rms_norm", "rope_cos_sin", "apply_rope", "attention",
     "silu", "swiglu", "lora_delta", "merge_lora", "linear", "route_topk", "moe_mlp", "gen_block",
+    "causal_attention", "prefix_block", "prefix_tower",
     "patchify", "unpatchify", "timestep_features", "timestep_embed", "tower_tokens", "tower_x0",
     "cfg_mix", "euler_step", "tower_step", "noisy_sample",
 ]
@@ -243,6 +244,78 @@ def gen_block(h: np.ndarray, wts: Dict[str, np.ndarray], dims, prefix_k: Sequenc
             parts.append({"u_post": u2})
     out = np.stack(outs)
     return (out, parts) if return_parts else out
+
+
+# ----------------------------------------------------------------------------- prefix forward
+def causal_attention(q: np.ndarray, k: np.ndarray, v: np.ndarray) -> np.ndarray:
+    """Decoder self-attention of the prompt pass: query t sees keys 0..t only.
+
+    q [T, Hq, d]; k, v [T, Hkv, d] -> [T, Hq, d]; GQA grouping and 1/sqrt(d) as in
+    ``attention``.  The prompt is read by the understanding tower as an ordinary
+    autoregressive decoder ([DiffSynth] 架构说明: the prefix pass yields the
+    past_key_values the image tokens then read)."""
+    T, Hq, d = q.shape
+    G = Hq // k.shape[1]
+    scale = q.dtype.type(1.0 / math.sqrt(d))
+    seen = np.tril(np.ones((T, T), dtype=bool))             # [query, key]
+    out = np.empty_like(q)
+    for h in range(Hq):
+        s = (q[:, h, :] @ k[:, h // G, :].T) * scale
+        s = np.where(seen, s, -np.inf)
+        p = np.exp(s - s.max(axis=1, keepdims=True))
+        out[:, h, :] = (p / p.sum(axis=1, keepdims=True)) @ v[:, h // G, :]
+    return out
+
+
+def prefix_block(h: np.ndarray, wts: Dict[str, np.ndarray], dims):
+    """One block of the prompt pass over h [B, P, D]: the gen block's sequence of steps
+    with positions 0..P-1, no earlier cache and causal attention.  Returns
+    (h_out [B, P, D], K [B, P, Hkv, d], V [B, P, Hkv, d]) where K holds the keys after
+    QK-norm and RoPE: the static prefix-KV cache the gen blocks take as given
+    ([SETUP] static prefix-KV cache; [DiffSynth] 架构说明)."""
+    B, P, D = h.shape
+    Hq, Hkv, hd = dims.n_q_heads, dims.n_kv_heads, dims.head_dim
+    eps, qd, kvd = dims.rms_eps, Hq * hd, Hkv * hd
+    lora, r, alpha = dims.lora_rank > 0, dims.lora_rank, dims.lora_alpha
+
+    def proj(x, wname, site, lo=None, hi=None):
+        w = wts[wname] if lo is None else wts[wname][lo:hi]
+        y = linear(x, w)
+        if lora and f"lora_a_{site}" in wts:
+            y = y + lora_delta(x, wts[f"lora_a_{site}"], wts[f"lora_b_{site}"], alpha, r)
+        return y
+
+    c, s = rope_cos_sin(np.arange(P), hd, dims.rope_theta, h.dtype)
+    outs, Ks, Vs = [], [], []
+    for b in range(B):
+        u = rms_norm(h[b], wts["g_in"], eps)
+        q = apply_rope(rms_norm(proj(u, "w_qkv", "q", 0, qd).reshape(P, Hq, hd), wts["g_q"], eps), c, s)
+        k = apply_rope(rms_norm(proj(u, "w_qkv", "k", qd, qd + kvd).reshape(P, Hkv, hd), wts["g_k"], eps), c, s)
+        v = proj(u, "w_qkv", "v", qd + kvd, qd + 2 * kvd).reshape(P, Hkv, hd)
+        x = h[b] + proj(causal_attention(q, k, v).reshape(P, qd), "w_o", "o")
+        u2 = rms_norm(x, wts["g_post"], eps)
+        if dims.is_moe:
+            x = x + moe_mlp(u2, wts["w_router"], wts["w_exp_gate_up"], wts["w_exp_down"], dims.top_k)
+        else:
+            I = dims.mlp_intermediate
+            x = x + proj(swiglu(proj(u2, "w_gate_up", "gate", 0, I), proj(u2, "w_gate_up", "up", I, 2 * I)),
+                         "w_down", "down")
+        outs.append(x)
+        Ks.append(k)
+        Vs.append(v)
+    return np.stack(outs), np.stack(Ks), np.stack(Vs)
+
+
+def prefix_tower(h: np.ndarray, layer_weights, dims, n_layers: int):
+    """The prompt pass through n_layers blocks: (h_out, [K_l], [V_l]) with one
+    [B, P, Hkv, d] key and value cache per block ([U1-recipe] t2i pipeline: one
+    prefix forward ahead of the denoise loop)."""
+    Ks, Vs = [], []
+    for l in range(n_layers):
+        h, K, V = prefix_block(h, layer_weights(l), dims)
+        Ks.append(K)
+        Vs.append(V)
+    return h, Ks, Vs
 
 
 # ----------------------------------------------------------------------------- tower

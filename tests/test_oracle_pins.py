@@ -376,6 +376,78 @@ def test_block_moe_all_experts_equals_dense_mixture_of_identical_experts():
                                rtol=1e-10, atol=1e-10)
 
 
+# ----------------------------------------------------------------------------- prefix forward
+def sdpa_gqa(q, k, v, causal):
+    G = q.shape[1] // k.shape[1]
+    tq = torch.from_numpy(q).permute(1, 0, 2)[None]
+    tk = torch.from_numpy(k).permute(1, 0, 2).repeat_interleave(G, dim=0)[None]
+    tv = torch.from_numpy(v).permute(1, 0, 2).repeat_interleave(G, dim=0)[None]
+    return F.scaled_dot_product_attention(tq, tk, tv, is_causal=causal)[0].permute(1, 0, 2).numpy()
+
+
+def test_causal_attention_brute_force_and_sdpa():
+    # query t is the unmasked brute force over keys 0..t
+    q, k, v = rnd(6, 4, 8), rnd(6, 2, 8), rnd(6, 2, 8)
+    got = O.causal_attention(q, k, v)
+    for t in range(6):
+        np.testing.assert_allclose(got[t:t + 1], brute_attention(q[t:t + 1], k[:t + 1], v[:t + 1]),
+                                   rtol=1e-12, atol=1e-12)
+    q, k, v = rnd(19, 8, 16), rnd(19, 2, 16), rnd(19, 2, 16)
+    np.testing.assert_allclose(O.causal_attention(q, k, v), sdpa_gqa(q, k, v, True), rtol=1e-10, atol=1e-12)
+
+
+def test_causal_attention_invariants():
+    q, k, v = rnd(7, 2, 8), rnd(7, 1, 8), rnd(7, 1, 8)
+    o = O.causal_attention(q, k, v)
+    np.testing.assert_allclose(o[0], np.broadcast_to(v[0, 0], o[0].shape), rtol=1e-14)   # one key seen
+    np.testing.assert_allclose(o[-1:], O.attention(q[-1:], k, v), rtol=1e-12)           # all keys seen
+    k2, v2 = k.copy(), v.copy()
+    k2[4:], v2[4:] = 5 * rnd(3, 1, 8), 5 * rnd(3, 1, 8)
+    o2 = O.causal_attention(q, k2, v2)
+    assert np.array_equal(o2[:4], o[:4])          # later keys never reach earlier queries
+    assert not np.allclose(o2[4:], o[4:])
+
+
+def small_prefix_case(moe=False, seed=0, n_layers=1):
+    if moe:
+        d = W.small_dims(hidden=64, n_q_heads=4, n_kv_heads=2, head_dim=16, mlp_intermediate=0,
+                         n_experts=4, top_k=2, expert_intermediate=48)
+        base = W.CONFIGS[4]
+    else:
+        d = W.small_dims(hidden=64, n_q_heads=4, n_kv_heads=2, head_dim=16, mlp_intermediate=96)
+        base = W.CONFIGS[0]
+    w = W.scaled(base, dims=d, prefix_len=9, n_layers=n_layers)
+    lw = [{k: v.astype(np.float64) for k, v in W.prefix_layer_weights(w, l, seed, "f32").items()}
+          for l in range(n_layers)]
+    return d, lw, W.prompt_hidden(w, seed, "f32").astype(np.float64)
+
+
+@pytest.mark.parametrize("moe", [False, True])
+def test_prefix_block_token_t_is_a_gen_block_over_the_earlier_cache(moe):
+    # Token t of the prompt pass sees tokens 0..t: it is the (pinned) gen block run on token t
+    # alone, at position t, with the cache of tokens 0..t-1 as its prefix.  This ties the
+    # causal mask, the positions and the cached K (normed, rotated) to the gen block's reading.
+    d, lw, h = small_prefix_case(moe)
+    out, K, V = O.prefix_block(h, lw[0], d)
+    B, P = h.shape[:2]
+    assert K.shape == V.shape == (B, P, d.n_kv_heads, d.head_dim)
+    for t in range(P):
+        g = O.gen_block(h[:, t:t + 1], lw[0], d, [K[b, :t] for b in range(B)], [V[b, :t] for b in range(B)])
+        np.testing.assert_allclose(g[:, 0], out[:, t], rtol=1e-10, atol=1e-10)
+
+
+def test_prefix_tower_last_token_runs_the_gen_blocks_over_its_caches():
+    d, lw, h = small_prefix_case(n_layers=3)
+    out, Ks, Vs = O.prefix_tower(h, lambda l: lw[l], d, 3)
+    B, P = h.shape[:2]
+    for t in (0, P - 1):
+        x = h[:, t:t + 1]
+        for l in range(3):
+            x = O.gen_block(x, lw[l], d, [Ks[l][b, :t] for b in range(B)], [Vs[l][b, :t] for b in range(B)])
+        np.testing.assert_allclose(x[:, 0], out[:, t], rtol=1e-10, atol=1e-10)
+    assert not np.allclose(Ks[1], Ks[0])
+
+
 # ----------------------------------------------------------------------------- patchify / temb
 def test_patchify_bijection_and_conv2d():
     x = rnd(2, 3, 64, 96)

@@ -161,9 +161,10 @@ LORA_A_STD = 0.02
 LORA_B_STD = 1e-3
 
 
-def layer_tensor_specs(d: BlockDims, layer: int):
+def layer_tensor_specs(d: BlockDims, layer: int, tower: str = "L"):
     """(name, shape, kind) of every tensor of one gen block.  Linear weights are
-    [out, in]; the fused gate/up weight stacks gate rows above up rows."""
+    [out, in]; the fused gate/up weight stacks gate rows above up rows.  ``tower``
+    prefixes the names: "L" for the gen tower, "U" for the prompt (prefix) tower."""
     D = d.hidden
     qd, kvd = d.n_q_heads * d.head_dim, d.n_kv_heads * d.head_dim
     specs = [("g_in", (D,), "gain"), ("w_qkv", (d.qkv_out, D), "w"),
@@ -183,7 +184,7 @@ def layer_tensor_specs(d: BlockDims, layer: int):
                 "up": d.mlp_intermediate, "down": D}
         for s in LORA_SITES:
             specs += [(f"lora_a_{s}", (r, ins[s]), "lora_a"), (f"lora_b_{s}", (outs[s], r), "lora_b")]
-    return [(f"L{layer}.{n}", shp, kind) for n, shp, kind in specs]
+    return [(f"{tower}{layer}.{n}", shp, kind) for n, shp, kind in specs]
 
 
 def _draw(config_id, seed, name, shape, kind, D):
@@ -201,10 +202,10 @@ def _draw(config_id, seed, name, shape, kind, D):
 
 
 def layer_weights(w: Workload, layer: int, seed: int = 0, dtype: str = "bf16",
-                  threads: int = 8) -> Dict[str, np.ndarray]:
+                  threads: int = 8, tower: str = "L") -> Dict[str, np.ndarray]:
     """All tensors of gen block ``layer`` as fp32 arrays (bf16-rounded for bf16 runs).
     Keys drop the ``L<layer>.`` prefix."""
-    specs = layer_tensor_specs(w.dims, layer)
+    specs = layer_tensor_specs(w.dims, layer, tower)
 
     def one(spec):
         name, shape, kind = spec
@@ -212,6 +213,24 @@ def layer_weights(w: Workload, layer: int, seed: int = 0, dtype: str = "bf16",
 
     with ThreadPoolExecutor(max(1, threads)) as ex:
         return dict(ex.map(one, specs))
+
+
+def prefix_dims(w: Workload) -> BlockDims:
+    """Block shape of the prompt tower: the gen block's, without LoRA (adapters train the
+    gen tower only)."""
+    return dataclasses.replace(w.dims, lora_rank=0, lora_alpha=0.0)
+
+
+def prefix_layer_weights(w: Workload, layer: int, seed: int = 0, dtype: str = "bf16") -> Dict[str, np.ndarray]:
+    """Weights of prompt-tower block ``layer`` (names ``U<layer>.*``, same distributions)."""
+    return layer_weights(dataclasses.replace(w, dims=prefix_dims(w)), layer, seed, dtype, tower="U")
+
+
+def prompt_hidden(w: Workload, seed: int = 0, dtype: str = "f32") -> np.ndarray:
+    """Embedded prompt [batch, prefix_len, D] ~ N(0, 1): the prompt tower's input, standing in
+    for token embeddings of an encoded prompt (one per sample and CFG branch)."""
+    shp = (w.batch, w.prefix_len, w.dims.hidden)
+    return maybe_bf16(normal(w.config_id, seed, "prompt_hidden", shp), dtype)
 
 
 def prefix_kv(w: Workload, layer: int, sample: int, seed: int = 0, dtype: str = "bf16"):
