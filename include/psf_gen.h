@@ -130,6 +130,24 @@ int gen_tower_step(const gen_block_dims* dims, int n_layers, const gen_block_wei
                    const void* const* prefix_k, const void* const* prefix_v, const int* prefix_len,
                    float* x_out, float* x0_out, void* workspace, size_t workspace_bytes, void* stream);
 
+/* Prefix forward: the prompt pass that writes the static prefix-KV cache the gen tower reads
+ * (DiffSynth-Studio "SenseNova-U1", 架构说明: image tokens attend to the prompt's past key/values;
+ * sensenova-u1-lora-trainer "Setup notes": the prefix cache is computed once and reused).  B prompt
+ * sequences of P tokens each run through n_layers blocks of the same structure as the gen block
+ * (RMSNorm, QKV, per-head RMSNorm + RoPE at positions 0..P-1, attention, O-proj, RMSNorm, MLP)
+ * with CAUSAL attention (token t sees tokens 0..t); the weights are the prompt tower's own.
+ *   hidden     [B, P, D] in dims.hidden_dtype: the embedded prompt in, the last block's output out
+ *   k_cache    HOST [n_layers * B] device pointers, index l*B + b, each [P, Hkv, d] in dims.dtype:
+ *              receives block l's keys after QK-norm and RoPE (the form gen_block_forward takes)
+ *   v_cache    HOST [n_layers * B] device pointers [P, Hkv, d]: block l's values
+ *   topk_idx_out  nullable int32 [n_layers, B*P, top_k] (MoE blocks): the experts each token was
+ *              routed to, as gen_block_forward reports them
+ *   workspace  >= gen_workspace_size(dims, 1, B, P, 0) bytes
+ * Token embedding (the vocabulary lookup) is not part of this call. */
+int gen_prefix_forward(const gen_block_dims* dims, int n_layers, const gen_block_weights* layers,
+                       void* hidden, int B, int P, void* const* k_cache, void* const* v_cache,
+                       int32_t* topk_idx_out, void* workspace, size_t workspace_bytes, void* stream);
+
 /* Merged-LoRA weights for the fast path in which a LoRA (such as the 8-step distilled one) is
  * fused into the base weights at load (vllm-omni recipe "SenseNova-U1.5", 8-step distilled LoRA;
  * DiffSynth-Studio "SenseNova-U1", 快速推理).  For every site s (q, k, v, o, gate, up, down) whose

@@ -267,12 +267,15 @@ def causal_attention(q: np.ndarray, k: np.ndarray, v: np.ndarray) -> np.ndarray:
     return out
 
 
-def prefix_block(h: np.ndarray, wts: Dict[str, np.ndarray], dims):
+def prefix_block(h: np.ndarray, wts: Dict[str, np.ndarray], dims, moe_idx: Optional[np.ndarray] = None,
+                 return_parts: bool = False):
     """One block of the prompt pass over h [B, P, D]: the gen block's sequence of steps
     with positions 0..P-1, no earlier cache and causal attention.  Returns
     (h_out [B, P, D], K [B, P, Hkv, d], V [B, P, Hkv, d]) where K holds the keys after
     QK-norm and RoPE: the static prefix-KV cache the gen blocks take as given
-    ([SETUP] static prefix-KV cache; [DiffSynth] 架构说明)."""
+    ([SETUP] static prefix-KV cache; [DiffSynth] 架构说明).  ``moe_idx`` [B, P, k] and
+    ``return_parts`` (the MLP input u_post per sequence, appended to the tuple) as in
+    ``gen_block``."""
     B, P, D = h.shape
     Hq, Hkv, hd = dims.n_q_heads, dims.n_kv_heads, dims.head_dim
     eps, qd, kvd = dims.rms_eps, Hq * hd, Hkv * hd
@@ -286,7 +289,7 @@ def prefix_block(h: np.ndarray, wts: Dict[str, np.ndarray], dims):
         return y
 
     c, s = rope_cos_sin(np.arange(P), hd, dims.rope_theta, h.dtype)
-    outs, Ks, Vs = [], [], []
+    outs, Ks, Vs, parts = [], [], [], []
     for b in range(B):
         u = rms_norm(h[b], wts["g_in"], eps)
         q = apply_rope(rms_norm(proj(u, "w_qkv", "q", 0, qd).reshape(P, Hq, hd), wts["g_q"], eps), c, s)
@@ -295,7 +298,8 @@ def prefix_block(h: np.ndarray, wts: Dict[str, np.ndarray], dims):
         x = h[b] + proj(causal_attention(q, k, v).reshape(P, qd), "w_o", "o")
         u2 = rms_norm(x, wts["g_post"], eps)
         if dims.is_moe:
-            x = x + moe_mlp(u2, wts["w_router"], wts["w_exp_gate_up"], wts["w_exp_down"], dims.top_k)
+            mi = None if moe_idx is None else moe_idx[b]
+            x = x + moe_mlp(u2, wts["w_router"], wts["w_exp_gate_up"], wts["w_exp_down"], dims.top_k, mi)
         else:
             I = dims.mlp_intermediate
             x = x + proj(swiglu(proj(u2, "w_gate_up", "gate", 0, I), proj(u2, "w_gate_up", "up", I, 2 * I)),
@@ -303,7 +307,9 @@ def prefix_block(h: np.ndarray, wts: Dict[str, np.ndarray], dims):
         outs.append(x)
         Ks.append(k)
         Vs.append(v)
-    return np.stack(outs), np.stack(Ks), np.stack(Vs)
+        parts.append({"u_post": u2})
+    res = (np.stack(outs), np.stack(Ks), np.stack(Vs))
+    return res + (parts,) if return_parts else res
 
 
 def prefix_tower(h: np.ndarray, layer_weights, dims, n_layers: int):

@@ -19,7 +19,7 @@ LORA_SITES = ("q", "k", "v", "o", "gate", "up", "down")
 
 # every symbol declared in include/psf_gen.h
 EXPORTS = ("gen_block_forward", "gen_tower_step", "flow_euler_cfg", "gen_moe_route", "gen_workspace_size",
-           "gen_sigma_schedule", "gen_last_error", "gen_block_lora_merge",
+           "gen_sigma_schedule", "gen_last_error", "gen_block_lora_merge", "gen_prefix_forward",
            # include/psf_gen_ops.h
            "gen_op_rmsnorm", "gen_op_linear", "gen_op_qknorm_rope", "gen_op_attention", "gen_op_workspace_size",
            "gen_timing_begin", "gen_timing_end")
@@ -62,6 +62,7 @@ def _load():
                                    P(f), P(f), f, i, f, P(vp), P(vp), P(i), vp, vp, vp, sz, vp]
     lib.flow_euler_cfg.argtypes = [vp, vp, vp, sz, f, f, f, f, vp]
     lib.gen_block_lora_merge.argtypes = [P(BlockDimsC), P(BlockWeightsC), vp, vp, vp, vp, vp]
+    lib.gen_prefix_forward.argtypes = [P(BlockDimsC), i, P(BlockWeightsC), vp, i, i, P(vp), P(vp), vp, vp, sz, vp]
     lib.gen_moe_route.argtypes = [vp, vp, i, i, i, i, i, vp, vp, vp]
     lib.gen_workspace_size.argtypes = [P(BlockDimsC), i, i, i, i]
     lib.gen_workspace_size.restype = sz
@@ -158,6 +159,19 @@ def block_forward(dims: BlockDimsC, weights: BlockWeightsC, hidden, prefix_k, pr
     _check(lib.gen_block_forward(ctypes.byref(dims), ctypes.byref(weights), hidden.data_ptr(), B, N,
                                  _ptr_array(prefix_k), _ptr_array(prefix_v), plen, _ptr(topk_out),
                                  workspace.data_ptr(), workspace.numel() * workspace.element_size(), _stream(stream)))
+
+
+def prefix_forward(dims: BlockDimsC, layers: Sequence[BlockWeightsC], hidden, k_cache, v_cache, workspace,
+                   topk_out=None, stream=None):
+    """Causal prompt pass over hidden [B, P, D] (in place).  k_cache/v_cache: flat lists of
+    [P, Hkv, d] device tensors indexed l*B + b, filled with each block's keys (normed and
+    rotated) and values.  topk_out: optional int32 [n_layers, B*P, top_k] (MoE)."""
+    B, P = hidden.shape[0], hidden.shape[1]
+    L = len(layers)
+    arr = (BlockWeightsC * max(1, L))(*layers)
+    _check(lib.gen_prefix_forward(ctypes.byref(dims), L, arr, hidden.data_ptr(), B, P, _ptr_array(k_cache),
+                                  _ptr_array(v_cache), _ptr(topk_out), workspace.data_ptr(),
+                                  workspace.numel() * workspace.element_size(), _stream(stream)))
 
 
 def block_lora_merge(dims: BlockDimsC, weights: BlockWeightsC, w_qkv_out, w_o_out, w_gate_up_out, w_down_out,

@@ -243,9 +243,12 @@ void lora_ext(GemmParams& p, const gen_block_dims& d, const gen_block_weights& w
 // With an fp32 residual the O and down projections accumulate into `hidden` in place; with a
 // bf16 residual the mid-block residual lives in the fp32 buffer hmid and `hidden` is rounded
 // once, at the block output.
+// kcache/vcache (prefix forward): per-sequence outputs [N, Hkv, d] receiving this block's normed,
+// rotated keys and its values; attention is then causal.
 template <typename T, typename TH>
 int run_block(const gen_block_dims& d, const gen_block_weights& w, TH* hidden, const SeqInfo& si, void* ws,
-              const Ws& L, int32_t* topk_out, hipStream_t s) {
+              const Ws& L, int32_t* topk_out, hipStream_t s, void* const* kcache = nullptr,
+              void* const* vcache = nullptr) {
   constexpr bool f32res = sizeof(TH) == 4;
   const int B = si.B, N = si.N, M = B * N, D = d.hidden;
   const int Hq = d.n_q_heads, Hkv = d.n_kv_heads, hd = d.head_dim;
@@ -273,20 +276,36 @@ int run_block(const gen_block_dims& d, const gen_block_weights& w, TH* hidden, c
     }
     HIP_TRY(timed(FAM_QKV, s, [&] { return gemm_any<T>(p, EPI_STORE, s); }));
   }
-  if (sizeof(T) == 2) {
+  if (kcache) {
+    // prefix forward: normalise and rotate q, k in place, hand k and v to the cache, causal attention
+    HIP_TRY(qknorm_rope<T>(qkv, QKV, si, Hq, Hkv, hd, (const T*)w.g_q, (const T*)w.g_k, rope, d.rms_eps, s));
+    const size_t row = (size_t)Hkv * hd * sizeof(T), pitch = (size_t)QKV * sizeof(T);
+    for (int b = 0; b < B; ++b) {
+      const T* src = qkv + (size_t)b * N * QKV + QD;
+      HIP_TRY(hipMemcpy2DAsync(kcache[b], row, src, pitch, row, N, hipMemcpyDeviceToDevice, s));
+      HIP_TRY(hipMemcpy2DAsync(vcache[b], row, src + (size_t)Hkv * hd, pitch, row, N, hipMemcpyDeviceToDevice, s));
+    }
+    HIP_TRY(pack_kv<T>(qkv, QKV, si, Hq, Hkv, hd, L.Lpad, Kc, Vt, s));
+    if (sizeof(T) == 2)
+      HIP_TRY(attention_bf16((const bf16*)qkv, QKV, si, Hq, Hkv, hd, L.Lpad, (const bf16*)Kc, (const bf16*)Vt,
+                             (bf16*)attn, QD, nullptr, nullptr, 0.f, true, s));
+    else
+      HIP_TRY(attention_f32((const float*)qkv, QKV, si, Hq, Hkv, hd, L.Lpad, (const float*)Kc, (const float*)Vt,
+                            (float*)attn, QD, true, s));
+  } else if (sizeof(T) == 2) {
     // bf16: the QK-norm and RoPE ride along with the K packing and the attention's Q loads
     HIP_TRY(pack_kv_knorm((const bf16*)qkv, QKV, si, Hq, Hkv, hd, L.Lpad, (const bf16*)w.g_k, rope, d.rms_eps,
                           (bf16*)Kc, (bf16*)Vt, s));
     HIP_TRY(timed(FAM_ATTN, s, [&] {
       return attention_bf16((const bf16*)qkv, QKV, si, Hq, Hkv, hd, L.Lpad, (const bf16*)Kc, (const bf16*)Vt,
-                            (bf16*)attn, QD, (const bf16*)w.g_q, rope, d.rms_eps, s);
+                            (bf16*)attn, QD, (const bf16*)w.g_q, rope, d.rms_eps, false, s);
     }));
   } else {
     HIP_TRY(qknorm_rope<T>(qkv, QKV, si, Hq, Hkv, hd, (const T*)w.g_q, (const T*)w.g_k, rope, d.rms_eps, s));
     HIP_TRY(pack_kv<T>(qkv, QKV, si, Hq, Hkv, hd, L.Lpad, Kc, Vt, s));
     HIP_TRY(timed(FAM_ATTN, s, [&] {
       return attention_f32((const float*)qkv, QKV, si, Hq, Hkv, hd, L.Lpad, (const float*)Kc, (const float*)Vt,
-                           (float*)attn, QD, s);
+                           (float*)attn, QD, false, s);
     }));
   }
   {
@@ -461,6 +480,46 @@ int gen_block_forward(const gen_block_dims* dims, const gen_block_weights* w, vo
   else
     rc = run_block<float, float>(*dims, *w, (float*)hidden, si, workspace, L, topk_idx_out, s);
   return rc ? rc : ok();
+}
+
+int gen_prefix_forward(const gen_block_dims* dims, int n_layers, const gen_block_weights* layers, void* hidden,
+                       int B, int P, void* const* k_cache, void* const* v_cache, int32_t* topk_idx_out,
+                       void* workspace, size_t workspace_bytes, void* stream) {
+  int rc = check_dims(dims);
+  if (rc) return rc;
+  if (n_layers < 1) return fail(GEN_EINVAL, "n_layers %d < 1", n_layers);
+  if (!layers) return fail(GEN_EINVAL, "layers is NULL");
+  for (int l = 0; l < n_layers; ++l)
+    if ((rc = check_weights(dims, &layers[l], l))) return rc;
+  if (!hidden || !aligned16(hidden)) return fail(GEN_EINVAL, "hidden is NULL or not 16-byte aligned");
+  if (B < 1 || P < 1) return fail(GEN_EINVAL, "B=%d and P=%d must be >= 1", B, P);
+  if (B > MAXB) return fail(GEN_EUNSUPPORTED, "B=%d > %d sequences per call", B, MAXB);
+  if (!k_cache || !v_cache) return fail(GEN_EINVAL, "k_cache/v_cache arrays are NULL");
+  for (int i = 0; i < n_layers * B; ++i)
+    if (!k_cache[i] || !v_cache[i] || !aligned16(k_cache[i]) || !aligned16(v_cache[i]))
+      return fail(GEN_EINVAL, "cache pointer %d is NULL or not 16-byte aligned", i);
+  if (!workspace || !aligned16(workspace)) return fail(GEN_EINVAL, "workspace is NULL or not 16-byte aligned");
+  const Ws L = layout(*dims, 1, B, P, 0);
+  if (workspace_bytes < L.total)
+    return fail(GEN_EWORKSPACE, "workspace %zu bytes < %zu required", workspace_bytes, L.total);
+  SeqInfo si{};
+  si.B = B;
+  si.N = P;   // the prompt tokens play the role of the block's own tokens; no earlier cache
+  hipStream_t s = (hipStream_t)stream;
+  HIP_TRY(rope_table(at<float2>(workspace, L.rope), L.n_pos, dims->head_dim, dims->rope_theta, s));
+  for (int l = 0; l < n_layers; ++l) {
+    void* const* kc = k_cache + (size_t)l * B;
+    void* const* vc = v_cache + (size_t)l * B;
+    int32_t* tk = topk_idx_out && dims->n_experts > 0 ? topk_idx_out + (size_t)l * B * P * dims->top_k : nullptr;
+    if (dims->dtype == GEN_BF16 && dims->hidden_dtype == GEN_F32)
+      rc = run_block<bf16, float>(*dims, layers[l], (float*)hidden, si, workspace, L, tk, s, kc, vc);
+    else if (dims->dtype == GEN_BF16)
+      rc = run_block<bf16, bf16>(*dims, layers[l], (bf16*)hidden, si, workspace, L, tk, s, kc, vc);
+    else
+      rc = run_block<float, float>(*dims, layers[l], (float*)hidden, si, workspace, L, tk, s, kc, vc);
+    if (rc) return rc;
+  }
+  return ok();
 }
 
 int gen_block_lora_merge(const gen_block_dims* dims, const gen_block_weights* w, void* w_qkv_out, void* w_o_out,
@@ -703,10 +762,10 @@ int gen_op_attention(const void* qkv, int B, int N, int Hq, int Hkv, int d, cons
   if (dtype == GEN_BF16) {
     HIP_TRY(pack_kv<bf16>((const bf16*)qkv, ld, si, Hq, Hkv, d, Lpad, at<bf16>(workspace, kc), at<bf16>(workspace, vt), s));
     HIP_TRY(attention_bf16((const bf16*)qkv, ld, si, Hq, Hkv, d, Lpad, at<bf16>(workspace, kc), at<bf16>(workspace, vt),
-                           (bf16*)out, (int64_t)Hq * d, nullptr, nullptr, 0.f, s));
+                           (bf16*)out, (int64_t)Hq * d, nullptr, nullptr, 0.f, false, s));
   } else {
     HIP_TRY(pack_kv<float>((const float*)qkv, ld, si, Hq, Hkv, d, Lpad, at<float>(workspace, kc), at<float>(workspace, vt), s));
-    HIP_TRY(attention_f32((const float*)qkv, ld, si, Hq, Hkv, d, Lpad, at<float>(workspace, kc), at<float>(workspace, vt), (float*)out, (int64_t)Hq * d, s));
+    HIP_TRY(attention_f32((const float*)qkv, ld, si, Hq, Hkv, d, Lpad, at<float>(workspace, kc), at<float>(workspace, vt), (float*)out, (int64_t)Hq * d, false, s));
   }
   return ok();
 }

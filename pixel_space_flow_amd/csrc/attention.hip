@@ -1,10 +1,11 @@
-// Prefix + image-token attention of the gen block (grouped-query, no mask, scale 1/sqrt(d)).
+// Prefix + image-token attention of the gen block (grouped-query, scale 1/sqrt(d); no mask, or a
+// causal mask for the prefix forward that builds the prompt cache).
 //
 // Keys/values of one (sequence, kv head) are the static prefix cache followed by the image
 // tokens' own k/v, packed contiguously (K [Lpad, d] and V transposed [d, Lpad]).
 //
-// bf16 path, one workgroup = 4 waves = 128 queries of one q head; each wave owns 32 queries.
-// Per 64-key tile (K and V^T staged in LDS, shared by the 4 waves):
+// bf16 path, one workgroup = 4 waves of 32 queries that share one kv head (up to 4 of its query
+// heads).  Per 64-key tile (K and V^T staged in LDS, shared by the 4 waves):
 //   S^T = K Q^T     v_mfma_f32_32x32x16_bf16, A = K rows from LDS, B = Q^T held in registers.
 //                   A lane then holds 16 scores of ONE query (column lane&31) for keys
 //                   (e/4)*8 + (lane/32)*4 + e%4 of each 32-key block, so the softmax row max
@@ -25,162 +26,8 @@
 namespace psf {
 namespace {
 
-template <int D>
-__global__ __launch_bounds__(256, 2) void attn_bf16_kernel(const bf16* __restrict__ qkv, int64_t ldq, SeqInfo si,
-                                                           int Hq, int Hkv, int Lpad, const bf16* __restrict__ Kc,
-                                                           const bf16* __restrict__ Vt, bf16* __restrict__ O,
-                                                           int64_t ldo, float scale_log2, int n_qb) {
-  constexpr int KT = 64;                 // keys per tile
-  constexpr int KROW = D * 2;            // bytes per K row in LDS
-  constexpr int KCH = D / 8;             // 16-byte chunks per K row
-  constexpr int NDB = D / 32;            // 32-row blocks of the head dim
-  __shared__ __attribute__((aligned(16))) char Ks[KT * KROW];
-  __shared__ __attribute__((aligned(16))) char Vs[D * KT * 2];
-
-  const int G = Hq / Hkv;
-  const int total = si.B * Hkv * n_qb * G;
-  const int id = xcd_remap(blockIdx.x, total);
-  const int hh = id % G;
-  int rest = id / G;
-  const int qb = rest % n_qb;
-  rest /= n_qb;
-  const int g = rest % Hkv;
-  const int b = rest / Hkv;
-  const int h = g * G + hh;
-
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int lr = lane & 31, lh = lane >> 5;
-  const int N = si.N;
-  const int L = si.plen[b] + N;
-  const int query = qb * 128 + wave * 32 + lr;
-  const int64_t tok = (int64_t)b * N + min(query, N - 1);
-
-  // Q^T fragments: lane holds q[query][ks*16 + lh*8 .. +8) for every 16-wide slice of d
-  bf16x8 qf[D / 16];
-  {
-    const bf16* qp = qkv + tok * ldq + (int64_t)h * D + lh * 8;
-#pragma unroll
-    for (int ks = 0; ks < D / 16; ++ks) qf[ks] = *(const bf16x8*)(qp + ks * 16);
-  }
-
-  f32x16 o[NDB];
-#pragma unroll
-  for (int i = 0; i < NDB; ++i)
-#pragma unroll
-    for (int e = 0; e < 16; ++e) o[i][e] = 0.f;
-  float m = -INFINITY, l = 0.f;
-
-  const bf16* Kbase = Kc + ((int64_t)b * Hkv + g) * Lpad * D;
-  const bf16* Vbase = Vt + ((int64_t)b * Hkv + g) * D * Lpad;
-  const int ntiles = (L + KT - 1) / KT;
-
-  for (int t = 0; t < ntiles; ++t) {
-    const int j0 = t * KT;
-    __syncthreads();
-    // K tile: 64 rows x KCH chunks
-#pragma unroll
-    for (int i = 0; i < (KT * KCH) / 256; ++i) {
-      const int c = tid + i * 256;
-      const int r = c / KCH, ch = c % KCH;
-      const u32x4 v = *(const u32x4*)(Kbase + (int64_t)(j0 + r) * D + ch * 8);
-      *(u32x4*)(Ks + r * KROW + ((ch ^ (r & 7)) << 4)) = v;
-    }
-    // V^T tile: D rows x 64 keys (8 chunks of 8 keys per row), stored as swizzled 8-byte units
-#pragma unroll
-    for (int i = 0; i < (D * 8) / 256; ++i) {
-      const int c = tid + i * 256;
-      const int r = c >> 3, ch = c & 7;
-      const u32x4 v = *(const u32x4*)(Vbase + (int64_t)r * Lpad + j0 + ch * 8);
-      const int u0 = (2 * ch) ^ (r & 15), u1 = (2 * ch + 1) ^ (r & 15);
-      *(u32x2*)(Vs + r * 128 + u0 * 8) = u32x2{v[0], v[1]};
-      *(u32x2*)(Vs + r * 128 + u1 * 8) = u32x2{v[2], v[3]};
-    }
-    __syncthreads();
-
-    f32x16 s[2];
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
-#pragma unroll
-      for (int e = 0; e < 16; ++e) s[kb][e] = 0.f;
-      const int r = kb * 32 + lr;
-#pragma unroll
-      for (int ks = 0; ks < D / 16; ++ks) {
-        const bf16x8 a = *(const bf16x8*)(Ks + r * KROW + (((ks * 2 + lh) ^ (r & 7)) << 4));
-        s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[ks], s[kb], 0, 0, 0);
-      }
-    }
-    // scale, mask keys beyond L, tile max
-    float mx = -INFINITY;
-    const bool tail = j0 + KT > L;
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-      for (int e = 0; e < 16; ++e) {
-        float x = s[kb][e] * scale_log2;
-        if (tail) {
-          const int key = j0 + kb * 32 + (e >> 2) * 8 + lh * 4 + (e & 3);
-          if (key >= L) x = -INFINITY;
-        }
-        s[kb][e] = x;
-        mx = fmaxf(mx, x);
-      }
-    mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
-    const float mn = fmaxf(m, mx);
-    const float alpha = exp2f(m - mn);
-    m = mn;
-    float rs = 0.f;
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-      for (int e = 0; e < 16; ++e) {
-        const float p = exp2f(s[kb][e] - mn);
-        s[kb][e] = p;
-        rs += p;
-      }
-    l = l * alpha + rs;
-#pragma unroll
-    for (int i = 0; i < NDB; ++i)
-#pragma unroll
-      for (int e = 0; e < 16; ++e) o[i][e] *= alpha;
-
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-      for (int st = 0; st < 2; ++st) {
-        bf16x8 pb;
-#pragma unroll
-        for (int e = 0; e < 8; ++e) pb[e] = static_cast<bf16>(s[kb][st * 8 + e]);
-        const int u0 = kb * 8 + st * 4 + lh;   // 8-byte unit of keys kb*32 + st*16 + lh*4 .. +4
-#pragma unroll
-        for (int db = 0; db < NDB; ++db) {
-          const int r = db * 32 + lr;
-          const u32x2 lo = *(const u32x2*)(Vs + r * 128 + ((u0 ^ (r & 15)) << 3));
-          const u32x2 hi = *(const u32x2*)(Vs + r * 128 + (((u0 + 2) ^ (r & 15)) << 3));
-          const u32x4 av = {lo[0], lo[1], hi[0], hi[1]};
-          o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, av), pb, o[db], 0, 0, 0);
-        }
-      }
-  }
-
-  const float lt = l + __shfl_xor(l, 32, 64);
-  const float inv = 1.0f / lt;
-  if (query < N) {
-    bf16* op = O + tok * ldo + (int64_t)h * D;
-#pragma unroll
-    for (int db = 0; db < NDB; ++db)
-#pragma unroll
-      for (int e4 = 0; e4 < 4; ++e4) {
-        const int d0 = db * 32 + e4 * 8 + lh * 4;
-        bf16x4 v;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) v[i] = static_cast<bf16>(o[db][e4 * 4 + i] * inv);
-        *(bf16x4*)(op + d0) = v;
-      }
-  }
-}
-
-// ------------------------------------------------------------------ v2
-// One workgroup = 4 waves x QB 32-query blocks of one q head.  K/V tiles of 64 keys come in by
+// ------------------------------------------------------------------ bf16 kernel
+// One workgroup = 4 waves x QB 32-query blocks.  K/V tiles of 64 keys come in by
 // LDS-DMA (buffer loads straight into LDS, double buffered, one barrier per tile).  Every K
 // fragment and V^T fragment read from LDS feeds QB MFMAs.  V^T is packed with the keys of each
 // 16-key group stored in the order [0-3, 8-11, 4-7, 12-15], which is exactly the order in which
@@ -209,7 +56,8 @@ __global__ __launch_bounds__(256, QB == 1 ? 2 : 1) void attn_v2_kernel(const bf1
                                                                      const bf16* __restrict__ Vt, bf16* __restrict__ O,
                                                                      int64_t ldo, float scale_log2, int n_qb,
                                                                      const bf16* __restrict__ gq,
-                                                                     const float2* __restrict__ table, float eps) {
+                                                                     const float2* __restrict__ table, float eps,
+                                                                     int causal) {
   constexpr int KT = 64;                  // keys per tile
   constexpr int KROW = D * 2;             // bytes per K row
   constexpr int KCH = D / 8;              // 16-byte chunks per K row
@@ -343,7 +191,11 @@ __global__ __launch_bounds__(256, QB == 1 ? 2 : 1) void attn_v2_kernel(const bf1
   for (int c = 0; c < 4; ++c) voff[c] = KT * KROW + lr * 128 + (((c * 2 + lh) ^ ((lr >> 1) & 7)) << 4);
   const bf16x2 ones = {static_cast<bf16>(1.0f), static_cast<bf16>(1.0f)};
 
-  const int ntiles = (L + KT - 1) / KT;
+  // causal: query n sees keys j <= P_b + n, so this workgroup needs keys up to its last query
+  const int qwg = (4 / HPW) * QW;
+  const int Lc = causal ? min(L, si.plen[b] + min(N - 1, qbk * qwg + qwg - 1) + 1) : L;
+  const int ntiles = (Lc + KT - 1) / KT;
+  const int myq = si.plen[b] + qbase + lr;               // last key this lane's query may see (causal)
 
   // Software pipeline across k-tiles: the scores of tile t+1 (K . Q^T MFMAs) are computed while
   // the softmax of tile t runs on the VALU, then P(t) . V(t) follows.  K therefore runs one tile
@@ -369,8 +221,10 @@ __global__ __launch_bounds__(256, QB == 1 ? 2 : 1) void attn_v2_kernel(const bf1
       }
   };
   // Online softmax of the scores in sc (tile t, keys from j0) and P . V from stage `stage`.
-  auto softmax_pv = [&](const int t, const int stage, const bool tail) {
+  auto softmax_pv = [&](const int t, const int stage) {
     const int j0 = t * KT;
+    // keys past the sequence end, and for causal rows keys past the query, get probability 0
+    const bool tail = j0 + KT > L || (causal && j0 + KT - 1 > si.plen[b] + qbase);
     bf16x8 pb[QB][2][2];
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb) {
@@ -380,7 +234,7 @@ __global__ __launch_bounds__(256, QB == 1 ? 2 : 1) void attn_v2_kernel(const bf1
 #pragma unroll
           for (int e = 0; e < 16; ++e) {
             const int key = j0 + kb * 32 + (e >> 2) * 8 + lh * 4 + (e & 3);
-            if (key >= L) sc[qb][kb][e] = -INFINITY;
+            if (key >= L || (causal && key > myq + qb * 32)) sc[qb][kb][e] = -INFINITY;
           }
       }
       float mx = -INFINITY;
@@ -442,7 +296,7 @@ __global__ __launch_bounds__(256, QB == 1 ? 2 : 1) void attn_v2_kernel(const bf1
     issue_k(min(t + 2, ntiles - 1), stage);   // past the end: a reload into a half nobody reads
     issue_v(t + 1, stage ^ 1);
     scores(sn, stage ^ 1);
-    softmax_pv(t, stage, false);
+    softmax_pv(t, stage);
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb) { sc[qb][0] = sn[qb][0]; sc[qb][1] = sn[qb][1]; }
   };
@@ -465,7 +319,7 @@ __global__ __launch_bounds__(256, QB == 1 ? 2 : 1) void attn_v2_kernel(const bf1
   // last tile (the only one that can be partial)
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
-  softmax_pv(t, t & 1, t * KT + KT > L);
+  softmax_pv(t, t & 1);
 
 #pragma unroll
   for (int qb = 0; qb < QB; ++qb) {
@@ -492,12 +346,12 @@ template <int D>
 __global__ __launch_bounds__(128) void attn_f32_kernel(const float* __restrict__ qkv, int64_t ldq, SeqInfo si, int Hq,
                                                        int Hkv, int Lpad, const float* __restrict__ Kc,
                                                        const float* __restrict__ Vt, float* __restrict__ O,
-                                                       int64_t ldo, float scale) {
+                                                       int64_t ldo, float scale, int causal) {
   const int b = blockIdx.z, h = blockIdx.y;
   const int n = blockIdx.x * 128 + threadIdx.x;
   if (n >= si.N) return;
   const int g = h / (Hq / Hkv);
-  const int L = si.plen[b] + si.N;
+  const int L = causal ? si.plen[b] + n + 1 : si.plen[b] + si.N;
   const int64_t tok = (int64_t)b * si.N + n;
   float q[D], o[D];
 #pragma unroll
@@ -525,7 +379,7 @@ __global__ __launch_bounds__(128) void attn_f32_kernel(const float* __restrict__
 
 hipError_t attention_bf16(const bf16* qkv, int64_t ldq, const SeqInfo& si, int Hq, int Hkv, int d, int Lpad,
                           const bf16* Kc, const bf16* Vt, bf16* O, int64_t ldo, const bf16* gq,
-                          const float2* table, float eps, hipStream_t s) {
+                          const float2* table, float eps, bool causal, hipStream_t s) {
   const int n_qb = (si.N + 127) / 128;
   const int total = si.B * Hkv * n_qb * (Hq / Hkv);
   if (total == 0) return hipSuccess;
@@ -538,7 +392,7 @@ hipError_t attention_bf16(const bf16* qkv, int64_t ldq, const SeqInfo& si, int H
   const int total2 = si.B * Hkv * n_qb2 * (Hq / Hkv / hpw);
 #define PSF_ATTN(DD, QKN)                                                                              \
   hipLaunchKernelGGL((attn_v2_kernel<DD, QB, QKN>), dim3(total2), dim3(256), 0, s, qkv, ldq, si, Hq, Hkv, Lpad, Kc, \
-                     Vt, O, ldo, scale_log2, n_qb2, gq, table, eps)
+                     Vt, O, ldo, scale_log2, n_qb2, gq, table, eps, causal ? 1 : 0)
   if (d == 128) {
     if (gq) PSF_ATTN(128, true); else PSF_ATTN(128, false);
   } else if (d == 64) {
@@ -552,11 +406,12 @@ hipError_t attention_bf16(const bf16* qkv, int64_t ldq, const SeqInfo& si, int H
 }
 
 hipError_t attention_f32(const float* qkv, int64_t ldq, const SeqInfo& si, int Hq, int Hkv, int d, int Lpad,
-                         const float* Kc, const float* Vt, float* O, int64_t ldo, hipStream_t s) {
+                         const float* Kc, const float* Vt, float* O, int64_t ldo, bool causal, hipStream_t s) {
   dim3 grid((si.N + 127) / 128, Hq, si.B);
   const float scale = 1.0f / sqrtf((float)d);
-  if (d == 128) hipLaunchKernelGGL(attn_f32_kernel<128>, grid, dim3(128), 0, s, qkv, ldq, si, Hq, Hkv, Lpad, Kc, Vt, O, ldo, scale);
-  else if (d == 64) hipLaunchKernelGGL(attn_f32_kernel<64>, grid, dim3(128), 0, s, qkv, ldq, si, Hq, Hkv, Lpad, Kc, Vt, O, ldo, scale);
+  const int c = causal ? 1 : 0;
+  if (d == 128) hipLaunchKernelGGL(attn_f32_kernel<128>, grid, dim3(128), 0, s, qkv, ldq, si, Hq, Hkv, Lpad, Kc, Vt, O, ldo, scale, c);
+  else if (d == 64) hipLaunchKernelGGL(attn_f32_kernel<64>, grid, dim3(128), 0, s, qkv, ldq, si, Hq, Hkv, Lpad, Kc, Vt, O, ldo, scale, c);
   else return hipErrorInvalidValue;
   return hipGetLastError();
 }

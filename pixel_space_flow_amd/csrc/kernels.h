@@ -41,14 +41,14 @@ hipError_t pack_kv(const T* qkv, int64_t ld, const SeqInfo& si, int Hq, int Hkv,
 hipError_t pack_kv_knorm(const bf16* qkv, int64_t ld, const SeqInfo& si, int Hq, int Hkv, int d, int Lpad,
                          const bf16* gk, const float2* table, float eps, bf16* Kc, bf16* Vt, hipStream_t s);
 
-// O[b*N + n, h*d:(h+1)*d] = softmax(q k^T / sqrt(d)) v over the L_b = P_b + N keys of Kc/Vt.
-// With gq non-null the q heads of qkv are raw: per-head RMSNorm (gain gq) and RoPE at position
-// P_b + n are applied to each query as it is loaded.
+// O[b*N + n, h*d:(h+1)*d] = softmax(q k^T / sqrt(d)) v over the L_b = P_b + N keys of Kc/Vt
+// (causal: over keys j <= P_b + n only).  With gq non-null the q heads of qkv are raw: per-head
+// RMSNorm (gain gq) and RoPE at position P_b + n are applied to each query as it is loaded.
 hipError_t attention_bf16(const bf16* qkv, int64_t ldq, const SeqInfo& si, int Hq, int Hkv, int d, int Lpad,
                           const bf16* Kc, const bf16* Vt, bf16* O, int64_t ldo, const bf16* gq,
-                          const float2* table, float eps, hipStream_t s);
+                          const float2* table, float eps, bool causal, hipStream_t s);
 hipError_t attention_f32(const float* qkv, int64_t ldq, const SeqInfo& si, int Hq, int Hkv, int d, int Lpad,
-                         const float* Kc, const float* Vt, float* O, int64_t ldo, hipStream_t s);
+                         const float* Kc, const float* Vt, float* O, int64_t ldo, bool causal, hipStream_t s);
 
 // Wo [out, in] = W + scale B A with A [rank, in], B [out, rank] (rank a multiple of 8, <= 128;
 // fp32 sums, one rounding); A == nullptr copies W.  Wo may equal W.

@@ -143,3 +143,24 @@ def test_block_lora_merge_rejects_bad_arguments_on_host(psf):
     assert f(ctypes.byref(d), ctypes.byref(w), 4096, 4100, 4096, 4096, None) == psf.GEN_EINVAL   # unaligned
     d.lora_rank = 12
     assert f(ctypes.byref(d), ctypes.byref(w), 4096, 4096, 4096, 4096, None) == psf.GEN_EUNSUPPORTED
+
+
+def test_prefix_forward_rejects_bad_arguments_on_host(psf):
+    f = psf.lib.gen_prefix_forward
+    d = dims(psf)
+    lw = (psf.BlockWeightsC * 2)(fake_weights(psf), fake_weights(psf))
+    good = (ctypes.c_void_p * 4)(4096, 4096, 4096, 4096)
+    hole = (ctypes.c_void_p * 4)(4096, 4096, None, 4096)
+
+    def call(n_layers=2, layers=lw, hidden=4096, B=2, P=400, kc=good, vc=good, ws=1 << 30):
+        return f(ctypes.byref(d), n_layers, layers, hidden, B, P, kc, vc, None, 4096, ws, None)
+    assert call(n_layers=0) == psf.GEN_EINVAL
+    assert call(layers=(psf.BlockWeightsC * 2)(fake_weights(psf), psf.BlockWeightsC())) == psf.GEN_EINVAL
+    assert "layer 1" in psf.last_error() or "g_in" in psf.last_error()
+    assert call(hidden=None) == psf.GEN_EINVAL
+    assert call(hidden=4100) == psf.GEN_EINVAL                    # unaligned
+    assert call(P=0) == psf.GEN_EINVAL
+    assert call(B=64) == psf.GEN_EUNSUPPORTED
+    assert call(kc=hole) == psf.GEN_EINVAL                        # every (layer, sequence) slot needed
+    assert call(vc=None) == psf.GEN_EINVAL
+    assert call(ws=64) == psf.GEN_EWORKSPACE
