@@ -149,6 +149,99 @@ def merge_lora_at_load(psf, lw, layers_dev, seed=1):
     return start.elapsed_time(stop)
 
 
+def prefix_flops(w) -> int:
+    """Algorithmic FLOPs of the prompt pass over w.batch prompts of w.prefix_len tokens through
+    w.n_layers blocks; causal attention counts only the visible (query, key) pairs."""
+    d = w.dims
+    B, P, D = w.batch, w.prefix_len, d.hidden
+    M = B * P
+    QD, KV = d.n_q_heads * d.head_dim, d.n_kv_heads * d.head_dim
+    per = 2 * M * D * (QD + 2 * KV) + 4 * B * d.n_q_heads * d.head_dim * (P * (P + 1) // 2) + 2 * M * QD * D
+    per += 2 * M * D * 2 * d.mlp_intermediate + 2 * M * d.mlp_intermediate * D
+    return per * w.n_layers
+
+
+def run_prefix_bench(psf, w, args):
+    """gen_prefix_forward over the cond and uncond prompts (400 tokens each) through the 36-layer
+    prompt tower, writing the per-layer prefix-KV cache: the pass that runs once per request
+    before the denoise loop."""
+    import torch
+    import workloads as W
+    d = W.prefix_dims(w)
+    dims = psf.make_dims(d, psf.GEN_BF16)
+    layers_dev, _, _, _, _ = make_device_tower(psf, W.scaled(w, dims=d), seed=2)
+    layers = [psf.make_weights(l) for l in layers_dev]
+    B, P = w.batch, w.prefix_len
+    g = torch.Generator(device="cuda")
+    g.manual_seed(3)
+    h0 = torch.randn(B, P, d.hidden, device="cuda", generator=g)
+    h = torch.empty_like(h0)
+    shp = (P, d.n_kv_heads, d.head_dim)
+    kc = [torch.empty(shp, device="cuda", dtype=torch.bfloat16) for _ in range(w.n_layers * B)]
+    vc = [torch.empty(shp, device="cuda", dtype=torch.bfloat16) for _ in range(w.n_layers * B)]
+    ws = psf.alloc_workspace(psf.workspace_size(dims, 1, B, P, 0))
+
+    def step():
+        h.copy_(h0)
+        psf.prefix_forward(dims, layers, h, kc, vc, ws)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    psf.timing_begin("gate_up", w.n_layers * args.steps)
+    start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    start.record()
+    for _ in range(args.steps):
+        step()
+    stop.record()
+    torch.cuda.synchronize()
+    ms = start.elapsed_time(stop) / args.steps
+    gu_ms, gu_n = psf.timing_end()
+    gu_avg = gu_ms / max(gu_n, 1)
+    M = B * P
+    gu_tf = 2 * M * d.hidden * 2 * d.mlp_intermediate / (gu_avg * 1e-3) / 1e12
+    tflops = prefix_flops(w) / (ms * 1e-3) / 1e12
+    out = {
+        "metric": "prompt tokens/s through the 36-layer prompt tower writing the prefix-KV cache; % bf16 MFMA peak",
+        "value": round(M / (ms * 1e-3), 1), "unit": "prompt tokens/s",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 3),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": f"qwen3-8b-prompt-tower{w.n_layers}-2x{P}tok", "layers": w.n_layers,
+                   "prompts": B, "prompt_tokens": P, "hidden": d.hidden,
+                   "heads": [d.n_q_heads, d.n_kv_heads, d.head_dim], "mlp_intermediate": d.mlp_intermediate,
+                   "cache_bytes": 2 * w.n_layers * B * P * d.n_kv_heads * d.head_dim * 2},
+        "pct_bf16_peak": round(100 * tflops / PEAK_BF16_TFLOPS, 2), "tflops": round(tflops, 1),
+        "roofline": {"kernel": f"gate_up SwiGLU GEMM (M={M}, N=2x{d.mlp_intermediate}, K={d.hidden})",
+                     "bound": "mfma", "achieved": round(gu_tf, 1), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(gu_tf / PEAK_BF16_TFLOPS, 4), "traffic": None,
+                     "avg_launch_ms": round(gu_avg, 4), "launches_timed": gu_n},
+    }
+    if not args.no_cpu_baseline:
+        import numpy as np
+        import oracle as O
+        wts = W.prefix_layer_weights(w, 0, 0, "bf16")
+        hp = W.prompt_hidden(w, 0, "bf16")
+        t0 = time.perf_counter()
+        O.prefix_block(hp, wts, d)
+        dt = time.perf_counter() - t0
+        out["cpu_baseline"] = {"value": round(M / (dt * w.n_layers), 2), "unit": "prompt tokens/s",
+                               "cores": blas_threads(), "kind": "oracle",
+                               "sample": f"one prompt-tower block ({B} x {P} tokens) in numpy fp32 took "
+                                         f"{dt:.2f} s; scaled x{w.n_layers} layers",
+                               "numpy": np.__version__}
+    print(json.dumps(out), flush=True)
+
+
+def blas_threads() -> int:
+    """Threads numpy's BLAS runs the oracle's products on."""
+    try:
+        from threadpoolctl import threadpool_info
+        return int(max((p.get("num_threads", 1) for p in threadpool_info() if p.get("user_api") == "blas"),
+                       default=1))
+    except Exception:
+        return os.cpu_count() or 1
+
+
 def cpu_baseline(w, seed=0):
     """The oracle (numpy fp32, as it stands) on one full-size gen block of the workload (both
     branches, all tokens), scaled to the 36-layer step; the patch embed and head are < 0.3 %
@@ -156,11 +249,7 @@ def cpu_baseline(w, seed=0):
     import numpy as np
     import oracle as O
     import workloads as W
-    try:
-        from threadpoolctl import threadpool_info
-        threads = max((p.get("num_threads", 1) for p in threadpool_info() if p.get("user_api") == "blas"), default=1)
-    except Exception:
-        threads = os.cpu_count() or 1
+    threads = blas_threads()
     wts = W.layer_weights(w, 0, seed, "bf16")
     h = W.block_hidden(w, seed, "bf16")
     pk, pv = zip(*[W.prefix_kv(w, 0, s, seed, "bf16") for s in range(w.batch)])
@@ -215,9 +304,10 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--config", type=int, default=2)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--variant", choices=("cfg", "lora-merged-cfg1"), default="cfg",
+    ap.add_argument("--variant", choices=("cfg", "lora-merged-cfg1", "prefix"), default="cfg",
                     help="cfg: the 2048^2 two-branch CFG step (default); lora-merged-cfg1: one branch at "
-                         "1024^2 with cfg 1 and a rank-32 LoRA folded into the weights at load")
+                         "1024^2 with cfg 1 and a rank-32 LoRA folded into the weights at load; prefix: the "
+                         "prompt pass that writes the prefix-KV cache (2 prompts x 400 tokens, 36 layers)")
     ap.add_argument("--kernel", choices=("gate_up", "attention", "copy"),
                     help="run only this kernel at the workload's shapes, --steps times (for counter runs)")
     args = ap.parse_args()
@@ -240,6 +330,9 @@ def main():
                                                     "lora_alpha": 0.0}))
     assert w.unit == "tower" and not w.dims.is_moe and not w.dims.lora_rank, "bench times the dense tower step"
     torch.cuda.set_device(0)
+    if args.variant == "prefix":
+        run_prefix_bench(psf, w, args)
+        return
     if args.kernel:
         run_kernel_only(psf, w, args.kernel, args.steps)
         return

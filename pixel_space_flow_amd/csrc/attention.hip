@@ -196,6 +196,8 @@ __global__ __launch_bounds__(256, QB == 1 ? 2 : 1) void attn_v2_kernel(const bf1
   const int Lc = causal ? min(L, si.plen[b] + min(N - 1, qbk * qwg + qwg - 1) + 1) : L;
   const int ntiles = (Lc + KT - 1) / KT;
   const int myq = si.plen[b] + qbase + lr;               // last key this lane's query may see (causal)
+  // tiles below nfull are seen whole by every query of the workgroup: no masking
+  const int nfull = causal ? min(ntiles, (si.plen[b] + qbk * qwg + 1) / KT) : L / KT;
 
   // Software pipeline across k-tiles: the scores of tile t+1 (K . Q^T MFMAs) are computed while
   // the softmax of tile t runs on the VALU, then P(t) . V(t) follows.  K therefore runs one tile
@@ -221,10 +223,11 @@ __global__ __launch_bounds__(256, QB == 1 ? 2 : 1) void attn_v2_kernel(const bf1
       }
   };
   // Online softmax of the scores in sc (tile t, keys from j0) and P . V from stage `stage`.
-  auto softmax_pv = [&](const int t, const int stage) {
+  // masked (a literal at every call): the tile may hold keys past the sequence end or, for causal
+  // rows, past the query; those get probability 0.
+  auto softmax_pv = [&](const int t, const int stage, const bool masked) {
     const int j0 = t * KT;
-    // keys past the sequence end, and for causal rows keys past the query, get probability 0
-    const bool tail = j0 + KT > L || (causal && j0 + KT - 1 > si.plen[b] + qbase);
+    const bool tail = masked && (j0 + KT > L || (causal && j0 + KT - 1 > si.plen[b] + qbase));
     bf16x8 pb[QB][2][2];
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb) {
@@ -290,13 +293,13 @@ __global__ __launch_bounds__(256, QB == 1 ? 2 : 1) void attn_v2_kernel(const bf1
   };
   // iteration t (every tile but the last): after the barrier K(t+1) and V(t) have landed and no
   // wave reads K(t) or V(t-1) any more, so K(t+2) and V(t+1) go into those halves.
-  auto step = [&](const int t, const int stage) {
+  auto step = [&](const int t, const int stage, const bool masked) {
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
     issue_k(min(t + 2, ntiles - 1), stage);   // past the end: a reload into a half nobody reads
     issue_v(t + 1, stage ^ 1);
     scores(sn, stage ^ 1);
-    softmax_pv(t, stage);
+    softmax_pv(t, stage, masked);
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb) { sc[qb][0] = sn[qb][0]; sc[qb][1] = sn[qb][1]; }
   };
@@ -308,18 +311,23 @@ __global__ __launch_bounds__(256, QB == 1 ? 2 : 1) void attn_v2_kernel(const bf1
   __syncthreads();
   scores(sc, 0);
   int t = 0;
-  for (; t + 2 < ntiles; t += 2) {
-    step(t, 0);
-    step(t + 1, 1);
+  for (; t + 2 < ntiles && t + 2 <= nfull; t += 2) {
+    step(t, 0, false);
+    step(t + 1, 1, false);
   }
-  if (t + 1 < ntiles) {
-    step(t, 0);
-    ++t;
-  }
-  // last tile (the only one that can be partial)
+  // The rest but the last: the causal diagonal, or one unpaired full tile.  t is even here and
+  // at most ceil((qwg - 1) / KT) + 1 tiles remain before the last, qwg <= 4 QW queries.
+  constexpr int MAXTAIL = (4 * QW - 1 + KT - 1) / KT + 1;
+#pragma unroll
+  for (int i = 0; i < MAXTAIL; ++i)
+    if (t + 1 < ntiles) {
+      step(t, i & 1, true);
+      ++t;
+    }
+  // last tile
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
-  softmax_pv(t, t & 1);
+  softmax_pv(t, t & 1, true);
 
 #pragma unroll
   for (int qb = 0; qb < QB; ++qb) {
