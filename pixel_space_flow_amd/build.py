@@ -22,19 +22,52 @@ FLAGS = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}",
          "-Wno-unused-result"]
 
 
-def _compile(src: str) -> str:
+RESOURCES = os.path.join(BUILD_DIR, "kernel_resources.txt")
+
+
+def _resources(remarks: str):
+    """(kernel symbol, VGPRs, AGPRs, scratch bytes per lane) from the compiler's
+    kernel-resource-usage remarks."""
+    out, cur = [], None
+    for line in remarks.splitlines():
+        if "remark:" not in line:
+            continue
+        body = line.split("remark:", 1)[1].split("[-Rpass")[0].strip()
+        key, _, val = body.partition(":")
+        val = val.strip()
+        if key == "Function Name":
+            cur = [val, 0, 0, 0]
+            out.append(cur)
+        elif cur is not None and key == "VGPRs":
+            cur[1] = int(val)
+        elif cur is not None and key == "AGPRs":
+            cur[2] = int(val)
+        elif cur is not None and key.startswith("ScratchSize"):
+            cur[3] = int(val)
+    return out
+
+
+def _compile(src: str):
     obj = os.path.join(BUILD_DIR, os.path.splitext(src)[0] + ".o")
     cmd = [HIPCC, *FLAGS, "-x", "hip", "-c", os.path.join(CSRC, src), "-o", obj]
+    if src.endswith(".hip"):
+        cmd.append("-Rpass-analysis=kernel-resource-usage")
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"hipcc failed for {src}:\n{r.stderr}")
-    return obj
+    return obj, _resources(r.stderr)
 
 
 def build(verbose: bool = True) -> str:
     os.makedirs(BUILD_DIR, exist_ok=True)
     with ThreadPoolExecutor(min(len(SOURCES), os.cpu_count() or 4)) as ex:
-        objs = list(ex.map(_compile, SOURCES))
+        done = list(ex.map(_compile, SOURCES))
+    objs = [o for o, _ in done]
+    # per-kernel register and scratch use of this build (a spill shows as scratch > 0)
+    with open(RESOURCES, "w") as f:
+        for _, res in done:
+            for name, v, a, sc in res:
+                f.write(f"{name} vgprs={v} agprs={a} scratch={sc}\n")
     tmp = OUT + ".tmp"
     cmd = [HIPCC, "-shared", "-fPIC", f"--offload-arch={ARCH}", *objs, "-o", tmp]
     r = subprocess.run(cmd, capture_output=True, text=True)
