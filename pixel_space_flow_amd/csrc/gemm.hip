@@ -921,16 +921,17 @@ hipError_t launch_fast(const GemmParams& p, int epi, int grid, int n_col_tiles, 
     hipLaunchKernelGGL(k, dim3(grid), dim3(64 * fast_waves()), lds, s, p, n_col_tiles);            \
     return hipGetLastError();                                                                      \
   }
-  // this kernel serves the LoRA products (the down projection, and block GEMMs with the up
-  // projection as a K extension): block epilogues only, never the embed or head ones
   switch (epi) {
     PSF_L(EPI_STORE)
     PSF_L(EPI_RESID)
     PSF_L(EPI_SWIGLU)
+    PSF_L(EPI_F32_IMG)
+    PSF_L(EPI_BIAS_BCAST)
     PSF_L(EPI_SCALED)
     PSF_L(EPI_RESID_TO_F32)
     PSF_L(EPI_RESID_FROM_F32)
     PSF_L(EPI_RESID_F32)
+    PSF_L(EPI_BIAS_BCAST_F32)
   }
 #undef PSF_L
   return hipErrorInvalidValue;
