@@ -15,7 +15,7 @@ __all__ = [
     "silu", "swiglu", "lora_delta", "merge_lora", "linear", "route_topk", "moe_mlp", "gen_block",
     "causal_attention", "prefix_block", "prefix_tower",
     "patchify", "unpatchify", "timestep_features", "timestep_embed", "tower_tokens", "tower_x0",
-    "cfg_mix", "euler_step", "tower_step", "noisy_sample",
+    "cfg_mix", "dual_cfg_mix", "euler_step", "tower_step", "noisy_sample",
 ]
 
 
@@ -410,6 +410,23 @@ def cfg_mix(x0_cond: np.ndarray, x0_uncond: Optional[np.ndarray], scale: float) 
     return x0_uncond + x0_cond.dtype.type(scale) * (x0_cond - x0_uncond)
 
 
+def dual_cfg_mix(x0_cond: np.ndarray, x0_img: np.ndarray, x0_uncond: Optional[np.ndarray], cfg_scale: float,
+                 img_cfg_scale: float) -> np.ndarray:
+    """Image-edit guidance over three branches ([U1.5-recipe] img2img: cfg_scale steers
+    toward the instruction, img_cfg_scale toward the input image, 1.0 switching image
+    guidance off; the 3-way run uses cond + img_cond + uncond; [DiffSynth] 图像编辑: the
+    negative branch keeps the input image and drops the instruction).  Reading: the
+    pages give no formula, so the nested form is taken
+        x0_u + s_img (x0_i - x0_u) + s_txt (x0_c - x0_i)
+    with cond = prompt + image, img_cond = image without the instruction, uncond =
+    neither.  At s_img = 1 the uncond branch drops out and this is the two-branch
+    guidance of cond against img_cond, the pages' 2-way run."""
+    if x0_uncond is None or img_cfg_scale == 1.0:
+        return cfg_mix(x0_cond, x0_img, cfg_scale)
+    t = x0_cond.dtype.type
+    return x0_uncond + t(img_cfg_scale) * (x0_img - x0_uncond) + t(cfg_scale) * (x0_cond - x0_img)
+
+
 def euler_step(x: np.ndarray, x0: np.ndarray, sigma: float, sigma_next: float, t_eps: float) -> np.ndarray:
     """Flow-matching Euler step from sigma to sigma_next with an x0 prediction.
     Convention x_sigma = (1 - sigma) x0 + sigma eps (sigma = 1 is pure noise), so
@@ -422,9 +439,10 @@ def euler_step(x: np.ndarray, x0: np.ndarray, sigma: float, sigma_next: float, t
 
 
 def tower_step(x_t, k: int, sched: np.ndarray, glob, layer_weights, dims, n_layers, n_br,
-               prefix_k, prefix_v, cfg_scale: float, t_eps: float, dtype=np.float32):
-    """One denoise step k: predict x0 at sigma_k for both branches, mix with CFG,
-    Euler to sigma_{k+1}.  Returns (x_next [n_img,3,H,W], x0 [n_img*n_br,3,H,W])."""
+               prefix_k, prefix_v, cfg_scale: float, t_eps: float, dtype=np.float32, img_cfg_scale: float = 1.0):
+    """One denoise step k: predict x0 at sigma_k for every branch, mix with CFG (two
+    branches: cond, uncond; three: cond, img_cond, uncond with ``dual_cfg_mix``), Euler to
+    sigma_{k+1}.  Returns (x_next [n_img,3,H,W], x0 [n_img*n_br,3,H,W])."""
     n_img = x_t.shape[0]
     sig = [float(sched[k])] * n_img
     x0 = tower_x0(x_t, sig, glob, layer_weights, dims, n_layers, n_br, prefix_k, prefix_v, dtype)
@@ -432,7 +450,10 @@ def tower_step(x_t, k: int, sched: np.ndarray, glob, layer_weights, dims, n_laye
     xs = x_t.astype(dtype)
     outs = []
     for i in range(n_img):
-        g = cfg_mix(x0[i, 0], x0[i, 1] if n_br == 2 else None, cfg_scale)
+        if n_br == 3:
+            g = dual_cfg_mix(x0[i, 0], x0[i, 1], x0[i, 2], cfg_scale, img_cfg_scale)
+        else:
+            g = cfg_mix(x0[i, 0], x0[i, 1] if n_br == 2 else None, cfg_scale)
         outs.append(euler_step(xs[i], g, float(sched[k]), float(sched[k + 1]), t_eps))
     return np.stack(outs), x0.reshape(n_img * n_br, *x0.shape[2:])
 

@@ -489,6 +489,28 @@ def test_cfg_on_x0_equals_cfg_on_velocity():
     np.testing.assert_allclose((x - O.cfg_mix(c, u, 4.0)) / sig, vg, rtol=1e-12, atol=1e-12)
 
 
+def test_dual_cfg_reductions():
+    c, i, u = rnd(3, 8, 8), rnd(3, 8, 8), rnd(3, 8, 8)
+    # image guidance off: the uncond branch drops out, two-branch guidance of cond against img_cond
+    np.testing.assert_allclose(O.dual_cfg_mix(c, i, u, 4.0, 1.0), i + 4.0 * (c - i), rtol=1e-13, atol=1e-13)
+    np.testing.assert_array_equal(O.dual_cfg_mix(c, i, u, 4.0, 1.0), O.dual_cfg_mix(c, i, None, 4.0, 2.0))
+    np.testing.assert_allclose(O.dual_cfg_mix(c, i, u, 1.0, 1.0), c, rtol=1e-14, atol=1e-14)   # no guidance
+    np.testing.assert_allclose(O.dual_cfg_mix(c, i, u, 0.0, 0.0), u, rtol=1e-14, atol=1e-14)
+    # when cond and img_cond agree the text scale has no effect, and the result is image CFG
+    np.testing.assert_allclose(O.dual_cfg_mix(i, i, u, 7.0, 2.5), u + 2.5 * (i - u), rtol=1e-13, atol=1e-13)
+    # the weights on (c, i, u) sum to 1: a common shift of all branches shifts the result
+    np.testing.assert_allclose(O.dual_cfg_mix(c + 2.0, i + 2.0, u + 2.0, 4.0, 2.0),
+                               O.dual_cfg_mix(c, i, u, 4.0, 2.0) + 2.0, rtol=1e-12, atol=1e-12)
+
+
+def test_dual_cfg_on_x0_equals_dual_cfg_on_velocity():
+    x, c, i, u = rnd(3, 8, 8), rnd(3, 8, 8), rnd(3, 8, 8), rnd(3, 8, 8)
+    sig = 0.6
+    vc, vi, vu = ((x - z) / sig for z in (c, i, u))
+    vg = vu + 2.0 * (vi - vu) + 4.0 * (vc - vi)
+    np.testing.assert_allclose((x - O.dual_cfg_mix(c, i, u, 4.0, 2.0)) / sig, vg, rtol=1e-12, atol=1e-12)
+
+
 def test_euler_closed_form_and_perfect_denoiser():
     x0, eps = rnd(50), rnd(50)
     for s, sn in [(1.0, 0.993243), (0.75, 0.0), (0.4, 0.1)]:
@@ -543,6 +565,25 @@ def test_tower_step_composition_and_branches():
     pv2 = [[p[0], p[0]] for p in pv]
     _, x0s = O.tower_step(x, 0, sched, glob, lambda l: lw[l], d, 2, 2, pk2, pv2, 4.0, 0.02, np.float64)
     np.testing.assert_array_equal(x0s[0], x0s[1])
+
+
+def test_tower_step_three_branches_dual_cfg():
+    # each branch is the one-branch tower over its own prefix (lengths differ), in the order
+    # cond, img_cond, uncond, and the update is the Euler step on the dual-guided prediction
+    w, d, glob, lw, _, _, x = tiny_tower(2)
+    lens = (7, 5, 3)
+    pk = [[W.normal(0, 0, f"dual_pk{l}{b}", (lens[b], 1, 16)) for b in range(3)] for l in range(2)]
+    pv = [[W.normal(0, 0, f"dual_pv{l}{b}", (lens[b], 1, 16)) for b in range(3)] for l in range(2)]
+    sched = O.sigma_schedule(2, 3.0)
+    xn, x0 = O.tower_step(x, 0, sched, glob, lambda l: lw[l], d, 2, 3, pk, pv, 4.0, 0.02, np.float64,
+                          img_cfg_scale=2.0)
+    assert x0.shape[0] == 3
+    for b in range(3):
+        one = O.tower_x0(x, [1.0], glob, lambda l: lw[l], d, 2, 1, [[pk[l][b]] for l in range(2)],
+                         [[pv[l][b]] for l in range(2)], np.float64)
+        np.testing.assert_allclose(x0[b], one[0], rtol=1e-12, atol=1e-12)
+    g = O.dual_cfg_mix(x0[0], x0[1], x0[2], 4.0, 2.0)
+    np.testing.assert_allclose(xn[0], O.euler_step(x[0], g, sched[0], sched[1], 0.02), rtol=1e-12, atol=1e-12)
 
 
 # ----------------------------------------------------------------------------- shapes pinned by the pages

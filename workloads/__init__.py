@@ -79,6 +79,8 @@ class Workload:
     unit: str = "tower"      # "tower" (gen_tower_step) or "block" (gen_block_forward)
     prefix_cache_samples: int = 0   # >0: prefixes are drawn from a cache of this many samples
     dtypes: tuple = ("bf16",)
+    img_cfg_scale: float = 1.0       # image guidance of the three-branch (image edit) step
+    branch_prefix: tuple = ()        # per-branch prefix lengths (else prefix_len for every branch)
 
     @property
     def n_tokens(self) -> int:
@@ -87,6 +89,14 @@ class Workload:
     @property
     def batch(self) -> int:
         return self.n_img * self.n_br
+
+    def prefix_len_of(self, sample: int) -> int:
+        """Prefix length of sample = image * n_br + branch."""
+        return self.branch_prefix[sample % self.n_br] if self.branch_prefix else self.prefix_len
+
+    @property
+    def max_prefix(self) -> int:
+        return max(self.branch_prefix) if self.branch_prefix else self.prefix_len
 
 
 QWEN3_8B = dict(hidden=4096, n_q_heads=32, n_kv_heads=8, head_dim=128, mlp_intermediate=12288)
@@ -108,6 +118,19 @@ CONFIGS: Dict[int, Workload] = {
                                                        head_dim=128, n_experts=32, top_k=8,
                                                        expert_intermediate=768),
                 n_layers=1, n_img=1, n_br=2, height=2048, width=2048, prefix_len=400, unit="block"),
+}
+
+
+# Workloads beyond the benchmark configurations above.
+# Image edit with dual guidance: three branches per image in the order cond (edit image +
+# instruction), img_cond (edit image, no instruction), uncond (neither), cfg 4 and image cfg 2
+# as in the pages' 3-way run.  Reading for the prefix lengths (the pages give none): the edit
+# image adds 1024 tokens (a 1024^2 input in 32-pixel patches) to a 400-token text part, so
+# cond and img_cond carry 1424 prefix tokens and uncond the 400-token fixed text.
+VARIANTS: Dict[str, Workload] = {
+    "dual_cfg": Workload(5, "qwen3-8b-tower36-2048px-dual-cfg-edit", BlockDims(**QWEN3_8B), n_layers=36,
+                         n_img=1, n_br=3, height=2048, width=2048, prefix_len=1424, cfg_scale=4.0,
+                         img_cfg_scale=2.0, shift=3.0, n_steps=50, t_eps=0.02, branch_prefix=(1424, 1424, 400)),
 }
 
 
@@ -237,7 +260,7 @@ def prefix_kv(w: Workload, layer: int, sample: int, seed: int = 0, dtype: str = 
     """Static prefix K and V of one (layer, sample): two [P, Hkv, d] arrays, N(0, 1).
     For CFG workloads sample = image * n_br + branch (branch 0 cond, 1 uncond);
     for cache workloads it is the cache slot."""
-    shp = (w.prefix_len, w.dims.n_kv_heads, w.dims.head_dim)
+    shp = (w.prefix_len_of(sample), w.dims.n_kv_heads, w.dims.head_dim)
     k = normal(w.config_id, seed, f"L{layer}.prefix_k.s{sample}", shp)
     v = normal(w.config_id, seed, f"L{layer}.prefix_v.s{sample}", shp)
     return maybe_bf16(k, dtype), maybe_bf16(v, dtype)
