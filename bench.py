@@ -57,13 +57,12 @@ def measured_traffic():
 def step_flops(w) -> dict:
     """Algorithmic FLOPs of one gen_tower_step (2 per multiply-add), by component."""
     d = w.dims
-    B, N, P, D = w.batch, w.n_tokens, w.prefix_len, d.hidden
+    B, N, D = w.batch, w.n_tokens, d.hidden
     M = B * N
     QD, KV = d.n_q_heads * d.head_dim, d.n_kv_heads * d.head_dim
-    L = P + N
     f = {}
     f["qkv"] = 2 * M * D * (QD + 2 * KV)
-    f["attention"] = 4 * B * d.n_q_heads * N * L * d.head_dim
+    f["attention"] = sum(4 * d.n_q_heads * N * (w.prefix_len_of(b) + N) * d.head_dim for b in range(B))
     f["o"] = 2 * M * QD * D
     if d.is_moe:
         f["router"] = 2 * M * D * d.n_experts
@@ -107,9 +106,9 @@ def make_device_tower(psf, w, seed=0):
         layers_dev.append(lw)
     glob = {"w_in": randn(D, 3072, std=0.02), "temb_w1": randn(D, 256, std=0.02), "temb_w2": randn(D, D, std=0.02),
             "g_final": randn(D, std=0.1, mean=1.0), "w_out": randn(3072, D, std=0.02)}
-    shp = (w.prefix_len, d.n_kv_heads, d.head_dim)
-    pk = [randn(*shp) for _ in range(w.n_layers * w.batch)]
-    pv = [randn(*shp) for _ in range(w.n_layers * w.batch)]
+    shp = [(w.prefix_len_of(s), d.n_kv_heads, d.head_dim) for s in range(w.batch)]
+    pk = [randn(*shp[i % w.batch]) for i in range(w.n_layers * w.batch)]
+    pv = [randn(*shp[i % w.batch]) for i in range(w.n_layers * w.batch)]
     x = torch.empty(w.n_img, 3, w.height, w.width, device="cuda")
     x.normal_(0.0, 1.0, generator=g)
     return layers_dev, glob, pk, pv, x
@@ -259,7 +258,8 @@ def cpu_baseline(w, seed=0):
     step_s = dt * w.n_layers
     return {"value": w.batch * w.n_tokens / step_s, "unit": "image tokens/s", "cores": int(threads),
             "kind": "oracle",
-            "sample": (f"one gen block of the workload ({w.batch} x {w.n_tokens} tokens, prefix {w.prefix_len}) "
+            "sample": (f"one gen block of the workload ({w.batch} x {w.n_tokens} tokens, prefix "
+                       f"{list(w.branch_prefix) if w.branch_prefix else w.prefix_len}) "
                        f"in numpy fp32 took {dt:.2f} s; scaled x{w.n_layers} layers"),
             "host": platform.processor() or platform.machine(), "numpy": np.__version__}
 
@@ -304,10 +304,11 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--config", type=int, default=2)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--variant", choices=("cfg", "lora-merged-cfg1", "prefix"), default="cfg",
+    ap.add_argument("--variant", choices=("cfg", "lora-merged-cfg1", "prefix", "dual-cfg"), default="cfg",
                     help="cfg: the 2048^2 two-branch CFG step (default); lora-merged-cfg1: one branch at "
                          "1024^2 with cfg 1 and a rank-32 LoRA folded into the weights at load; prefix: the "
-                         "prompt pass that writes the prefix-KV cache (2 prompts x 400 tokens, 36 layers)")
+                         "prompt pass that writes the prefix-KV cache (2 prompts x 400 tokens, 36 layers); "
+                         "dual-cfg: the 2048^2 image-edit step with three branches (cfg 4, image cfg 2)")
     ap.add_argument("--kernel", choices=("gate_up", "attention", "copy"),
                     help="run only this kernel at the workload's shapes, --steps times (for counter runs)")
     args = ap.parse_args()
@@ -320,7 +321,7 @@ def main():
     import pixel_space_flow_amd as psf
     import workloads as W
 
-    w = W.CONFIGS[args.config]
+    w = W.CONFIGS[args.config] if args.variant != "dual-cfg" else W.VARIANTS["dual_cfg"]
     lora_w = None
     if args.variant == "lora-merged-cfg1":
         # the 8-step distilled-LoRA fast path: one image, one branch, cfg 1, LoRA fused at load
@@ -342,14 +343,14 @@ def main():
     if lora_w is not None:
         merge_ms = merge_lora_at_load(psf, lora_w, layers_dev)
     layers = [psf.make_weights(l) for l in layers_dev]
-    ws = psf.alloc_workspace(psf.workspace_size(dims, w.n_img, w.n_br, w.n_tokens, w.prefix_len))
+    ws = psf.alloc_workspace(psf.workspace_size(dims, w.n_img, w.n_br, w.n_tokens, w.max_prefix))
     xo = torch.empty_like(x)
     sched = psf.sigma_schedule(w.n_steps, w.shift)
-    plen = [w.prefix_len] * w.batch
+    plen = [w.prefix_len_of(s) for s in range(w.batch)]
 
     def step():
         psf.tower_step(dims, layers, glob, x, w.n_br, [sched[0]], [sched[1]], w.cfg_scale, w.t_eps, pk, pv, plen,
-                       xo, ws)
+                       xo, ws, img_cfg_scale=w.img_cfg_scale)
 
     for _ in range(args.warmup):
         step()
@@ -374,9 +375,11 @@ def main():
     gu_tflops = gu_flops / (gu_avg_ms * 1e-3) / 1e12
     props = torch.cuda.get_device_properties(0)
     out = {
-        "metric": ("gen-tower image tokens/s per denoise step at 2048^2 CFG; % bf16 MFMA peak" if lora_w is None else
-                   "gen-tower image tokens/s per denoise step at 1024^2, one branch (cfg 1), LoRA merged at load; "
-                   "% bf16 MFMA peak"),
+        "metric": {"cfg": "gen-tower image tokens/s per denoise step at 2048^2 CFG; % bf16 MFMA peak",
+                   "lora-merged-cfg1": "gen-tower image tokens/s per denoise step at 1024^2, one branch (cfg 1), "
+                                       "LoRA merged at load; % bf16 MFMA peak",
+                   "dual-cfg": "gen-tower image tokens/s per denoise step at 2048^2, image edit with dual guidance "
+                               "(three branches); % bf16 MFMA peak"}[args.variant],
         "value": round(tokens / (ms * 1e-3), 1),
         "unit": "image tokens/s",
         "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
@@ -384,10 +387,12 @@ def main():
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
         "dtype": "bf16", "data": "synthetic",
         "config": {"workload": w.name, "layers": w.n_layers, "image_px": [w.height, w.width],
-                   "image_tokens_per_branch": w.n_tokens, "cfg_branches": w.n_br, "prefix_tokens": w.prefix_len,
+                   "image_tokens_per_branch": w.n_tokens, "cfg_branches": w.n_br,
+                   "prefix_tokens": w.prefix_len if not w.branch_prefix else list(w.branch_prefix),
                    "hidden": d.hidden, "heads": [d.n_q_heads, d.n_kv_heads, d.head_dim],
                    "mlp_intermediate": d.mlp_intermediate, "cfg_scale": w.cfg_scale, "shift": w.shift,
-                   "t_eps": w.t_eps, "schedule_step": f"0 of {w.n_steps}", "global_batch": w.batch, "seq_len": w.n_tokens},
+                   "t_eps": w.t_eps, "schedule_step": f"0 of {w.n_steps}", "global_batch": w.batch, "seq_len": w.n_tokens,
+                   **({"img_cfg_scale": w.img_cfg_scale} if w.n_br == 3 else {})},
         "pct_bf16_peak": round(100 * tflops / PEAK_BF16_TFLOPS, 2),
         "tflops": round(tflops, 1),
         "step_tflop": round(fl["total"] / 1e12, 3),

@@ -104,12 +104,14 @@ int gen_block_forward(const gen_block_dims* dims, const gen_block_weights* w, vo
                       int32_t* topk_idx_out, void* workspace, size_t workspace_bytes, void* stream);
 
 /* One denoise step of the gen tower for n_img images and n_br CFG branches
- * (branch 0 = cond, 1 = uncond):
+ * (two: 0 = cond, 1 = uncond; three, for image edits: 0 = cond, 1 = img_cond, 2 = uncond):
  *   h0  = patchify(x_t) W_in^T + temb(sigma)      (tokens in raster order of 32x32 patches,
  *                                                  features ordered channel, row, column)
  *   h   = n_layers gen blocks, per branch with its own prefix
  *   x0  = unpatchify(RMSNorm(h; g_final) W_out^T) (float32)
  *   x0g = x0_u + cfg_scale (x0_c - x0_u)          (x0_c when n_br == 1 or cfg_scale == 1)
+ *   three branches (dual guidance, as flow_euler_dual_cfg):
+ *   x0g = x0_u + img_cfg_scale (x0_i - x0_u) + cfg_scale (x0_c - x0_i)
  *   x_out = x_t + (sigma_next - sigma) (x_t - x0g) / max(sigma, t_eps)
  * temb = temb_w2 silu(temb_w1 [cos(1000 sigma f), sin(1000 sigma f)]), f_j = 1e4^(-j/128).
  *   layers       HOST [n_layers] weight structs
@@ -117,6 +119,7 @@ int gen_block_forward(const gen_block_dims* dims, const gen_block_weights* w, vo
  *   x_t          [n_img, 3, H, W] float32; H, W multiples of 32
  *   sigma        HOST [n_img]; sigma_next HOST [n_img] or NULL: then x_out receives x0
  *                (n_br must be 1) and no Euler update is made
+ *   img_cfg_scale  image guidance, read only when n_br == 3 (1 switches it off)
  *   cfg_norm     0 ("none"); anything else returns GEN_EUNSUPPORTED
  *   prefix_k/v   HOST [n_layers * n_img * n_br] device pointers, index (l*n_img + i)*n_br + br
  *   prefix_len   HOST [n_img * n_br]
@@ -126,9 +129,10 @@ int gen_block_forward(const gen_block_dims* dims, const gen_block_weights* w, vo
 int gen_tower_step(const gen_block_dims* dims, int n_layers, const gen_block_weights* layers,
                    const void* w_in, const void* temb_w1, const void* temb_w2, const void* g_final,
                    const void* w_out, const float* x_t, int n_img, int n_br, int H, int W,
-                   const float* sigma, const float* sigma_next, float cfg_scale, int cfg_norm, float t_eps,
-                   const void* const* prefix_k, const void* const* prefix_v, const int* prefix_len,
-                   float* x_out, float* x0_out, void* workspace, size_t workspace_bytes, void* stream);
+                   const float* sigma, const float* sigma_next, float cfg_scale, float img_cfg_scale,
+                   int cfg_norm, float t_eps, const void* const* prefix_k, const void* const* prefix_v,
+                   const int* prefix_len, float* x_out, float* x0_out, void* workspace, size_t workspace_bytes,
+                   void* stream);
 
 /* Prefix forward: the prompt pass that writes the static prefix-KV cache the gen tower reads
  * (DiffSynth-Studio "SenseNova-U1", 架构说明: image tokens attend to the prompt's past key/values;
@@ -166,6 +170,19 @@ int gen_block_lora_merge(const gen_block_dims* dims, const gen_block_weights* w,
  * x0_uncond may be NULL only when cfg_scale == 1.  x must not alias x0_cond/x0_uncond. */
 int flow_euler_cfg(float* x, const float* x0_cond, const float* x0_uncond, size_t n, float cfg_scale,
                    float sigma, float sigma_next, float t_eps, void* stream);
+
+/* Dual guidance of an image edit and the Euler update, in place, float32, n elements
+ * (vllm-omni recipe "SenseNova-U1.5", img2img: cfg_scale guides toward the instruction,
+ * img_cfg_scale toward the input image, 1.0 switching image guidance off, the 3-way run using
+ * cond + img_cond + uncond; DiffSynth-Studio "SenseNova-U1", 图像编辑: the negative branch keeps
+ * the image and drops the instruction).  The pages print no formula; the nested form is taken:
+ *   x0g = x0_uncond + img_cfg_scale (x0_img - x0_uncond) + cfg_scale (x0_cond - x0_img)
+ *   x  <- x + (sigma_next - sigma) (x - x0g) / max(sigma, t_eps)
+ * With img_cfg_scale == 1 the uncond branch drops out (x0_img + cfg_scale (x0_cond - x0_img)) and
+ * x0_uncond may be NULL.  x must not alias the predictions. */
+int flow_euler_dual_cfg(float* x, const float* x0_cond, const float* x0_img, const float* x0_uncond, size_t n,
+                        float cfg_scale, float img_cfg_scale, float sigma, float sigma_next, float t_eps,
+                        void* stream);
 
 /* Router of an MoE gen block on its own, for checking routing decisions:
  *   logits = u w_router^T (float32 accumulate), p = softmax(logits), the top_k largest p

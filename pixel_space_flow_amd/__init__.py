@@ -18,7 +18,8 @@ GEN_F32, GEN_BF16 = 0, 1
 LORA_SITES = ("q", "k", "v", "o", "gate", "up", "down")
 
 # every symbol declared in include/psf_gen.h
-EXPORTS = ("gen_block_forward", "gen_tower_step", "flow_euler_cfg", "gen_moe_route", "gen_workspace_size",
+EXPORTS = ("gen_block_forward", "gen_tower_step", "flow_euler_cfg", "flow_euler_dual_cfg", "gen_moe_route",
+           "gen_workspace_size",
            "gen_sigma_schedule", "gen_last_error", "gen_block_lora_merge", "gen_prefix_forward",
            # include/psf_gen_ops.h
            "gen_op_rmsnorm", "gen_op_linear", "gen_op_qknorm_rope", "gen_op_attention", "gen_op_workspace_size",
@@ -59,8 +60,9 @@ def _load():
     P = ctypes.POINTER
     lib.gen_block_forward.argtypes = [P(BlockDimsC), P(BlockWeightsC), vp, i, i, P(vp), P(vp), P(i), vp, vp, sz, vp]
     lib.gen_tower_step.argtypes = [P(BlockDimsC), i, P(BlockWeightsC), vp, vp, vp, vp, vp, vp, i, i, i, i,
-                                   P(f), P(f), f, i, f, P(vp), P(vp), P(i), vp, vp, vp, sz, vp]
+                                   P(f), P(f), f, f, i, f, P(vp), P(vp), P(i), vp, vp, vp, sz, vp]
     lib.flow_euler_cfg.argtypes = [vp, vp, vp, sz, f, f, f, f, vp]
+    lib.flow_euler_dual_cfg.argtypes = [vp, vp, vp, vp, sz, f, f, f, f, f, vp]
     lib.gen_block_lora_merge.argtypes = [P(BlockDimsC), P(BlockWeightsC), vp, vp, vp, vp, vp]
     lib.gen_prefix_forward.argtypes = [P(BlockDimsC), i, P(BlockWeightsC), vp, i, i, P(vp), P(vp), vp, vp, sz, vp]
     lib.gen_moe_route.argtypes = [vp, vp, i, i, i, i, i, vp, vp, vp]
@@ -184,7 +186,7 @@ def block_lora_merge(dims: BlockDimsC, weights: BlockWeightsC, w_qkv_out, w_o_ou
 
 def tower_step(dims: BlockDimsC, layers: Sequence[BlockWeightsC], glob: dict, x_t, n_br: int, sigma, sigma_next,
                cfg_scale: float, t_eps: float, prefix_k, prefix_v, prefix_len, x_out, workspace, x0_out=None,
-               cfg_norm: int = 0, stream=None):
+               cfg_norm: int = 0, stream=None, img_cfg_scale: float = 1.0):
     """glob: w_in, temb_w1, temb_w2, g_final, w_out.  prefix_k/v: flat lists indexed
     (l*n_img + i)*n_br + br.  sigma/sigma_next: per-image host floats (sigma_next None:
     x_out receives x0)."""
@@ -196,7 +198,8 @@ def tower_step(dims: BlockDimsC, layers: Sequence[BlockWeightsC], glob: dict, x_
     plen = (ctypes.c_int * (n_img * n_br))(*prefix_len)
     _check(lib.gen_tower_step(ctypes.byref(dims), L, arr, _ptr(glob["w_in"]), _ptr(glob["temb_w1"]),
                               _ptr(glob["temb_w2"]), _ptr(glob["g_final"]), _ptr(glob["w_out"]), x_t.data_ptr(),
-                              n_img, n_br, H, W, sig, sn, float(cfg_scale), cfg_norm, float(t_eps),
+                              n_img, n_br, H, W, sig, sn, float(cfg_scale), float(img_cfg_scale), cfg_norm,
+                              float(t_eps),
                               _ptr_array(prefix_k), _ptr_array(prefix_v), plen, x_out.data_ptr(), _ptr(x0_out),
                               workspace.data_ptr(), workspace.numel() * workspace.element_size(), _stream(stream)))
 
@@ -205,6 +208,13 @@ def flow_euler_cfg(x, x0_cond, x0_uncond, cfg_scale: float, sigma: float, sigma_
                    stream=None):
     _check(lib.flow_euler_cfg(x.data_ptr(), x0_cond.data_ptr(), _ptr(x0_uncond), x.numel(), float(cfg_scale),
                               float(sigma), float(sigma_next), float(t_eps), _stream(stream)))
+
+
+def flow_euler_dual_cfg(x, x0_cond, x0_img, x0_uncond, cfg_scale: float, img_cfg_scale: float, sigma: float,
+                        sigma_next: float, t_eps: float, stream=None):
+    _check(lib.flow_euler_dual_cfg(x.data_ptr(), x0_cond.data_ptr(), x0_img.data_ptr(), _ptr(x0_uncond), x.numel(),
+                                   float(cfg_scale), float(img_cfg_scale), float(sigma), float(sigma_next),
+                                   float(t_eps), _stream(stream)))
 
 
 def moe_route(u, w_router, top_k: int, idx_out, w_out, dtype: int, stream=None):

@@ -438,7 +438,24 @@ int flow_euler_cfg(float* x, const float* x0_cond, const float* x0_uncond, size_
   if (!std::isfinite(cfg_scale) || !std::isfinite(sigma) || !std::isfinite(sigma_next) || !std::isfinite(t_eps))
     return fail(GEN_EINVAL, "scalars must be finite");
   if (!(std::max(sigma, t_eps) > 0.f)) return fail(GEN_EINVAL, "max(sigma, t_eps) must be > 0");
-  HIP_TRY(cfg_euler(x, x, x0_cond, x0_uncond, n, cfg_scale, sigma, sigma_next, t_eps, (hipStream_t)stream));
+  HIP_TRY(cfg_euler(x, x, x0_cond, nullptr, x0_uncond, n, cfg_scale, 1.0f, sigma, sigma_next, t_eps,
+                    (hipStream_t)stream));
+  return ok();
+}
+
+int flow_euler_dual_cfg(float* x, const float* x0_cond, const float* x0_img, const float* x0_uncond, size_t n,
+                        float cfg_scale, float img_cfg_scale, float sigma, float sigma_next, float t_eps,
+                        void* stream) {
+  if (!x || !x0_cond || !x0_img) return fail(GEN_EINVAL, "x, x0_cond and x0_img must be non-NULL");
+  if (!x0_uncond && img_cfg_scale != 1.0f) return fail(GEN_EINVAL, "x0_uncond is NULL but img_cfg_scale != 1");
+  if (!aligned16(x) || !aligned16(x0_cond) || !aligned16(x0_img) || (x0_uncond && !aligned16(x0_uncond)))
+    return fail(GEN_EINVAL, "pointers must be 16-byte aligned");
+  if (!std::isfinite(cfg_scale) || !std::isfinite(img_cfg_scale) || !std::isfinite(sigma) ||
+      !std::isfinite(sigma_next) || !std::isfinite(t_eps))
+    return fail(GEN_EINVAL, "scalars must be finite");
+  if (!(std::max(sigma, t_eps) > 0.f)) return fail(GEN_EINVAL, "max(sigma, t_eps) must be > 0");
+  HIP_TRY(cfg_euler(x, x, x0_cond, x0_img, x0_uncond, n, cfg_scale, img_cfg_scale, sigma, sigma_next, t_eps,
+                    (hipStream_t)stream));
   return ok();
 }
 
@@ -558,7 +575,8 @@ int gen_block_lora_merge(const gen_block_dims* dims, const gen_block_weights* w,
 int gen_tower_step(const gen_block_dims* dims, int n_layers, const gen_block_weights* layers, const void* w_in,
                    const void* temb_w1, const void* temb_w2, const void* g_final, const void* w_out, const float* x_t,
                    int n_img, int n_br, int H, int W, const float* sigma, const float* sigma_next, float cfg_scale,
-                   int cfg_norm, float t_eps, const void* const* prefix_k, const void* const* prefix_v,
+                   float img_cfg_scale, int cfg_norm, float t_eps, const void* const* prefix_k,
+                   const void* const* prefix_v,
                    const int* prefix_len, float* x_out, float* x0_out, void* workspace, size_t workspace_bytes,
                    void* stream) {
   int rc = check_dims(dims);
@@ -575,13 +593,14 @@ int gen_tower_step(const gen_block_dims* dims, int n_layers, const gen_block_wei
   }
   if (x0_out && !aligned16(x0_out)) return fail(GEN_EINVAL, "x0_out is not 16-byte aligned");
   if (n_img < 1) return fail(GEN_EINVAL, "n_img %d < 1", n_img);
-  if (n_br != 1 && n_br != 2) return fail(GEN_EINVAL, "n_br %d must be 1 or 2", n_br);
+  if (n_br < 1 || n_br > 3) return fail(GEN_EINVAL, "n_br %d must be 1, 2 or 3", n_br);
   if (n_img * n_br > MAXB) return fail(GEN_EUNSUPPORTED, "n_img*n_br = %d > %d", n_img * n_br, MAXB);
   if (H <= 0 || W <= 0 || H % 32 || W % 32) return fail(GEN_EINVAL, "H=%d and W=%d must be positive multiples of 32", H, W);
   if (!sigma) return fail(GEN_EINVAL, "sigma is NULL");
   if (cfg_norm != 0) return fail(GEN_EUNSUPPORTED, "cfg_norm %d: only 0 (\"none\") is supported", cfg_norm);
   if (!sigma_next && n_br != 1) return fail(GEN_EINVAL, "x0-only output (sigma_next NULL) needs n_br == 1");
-  if (!std::isfinite(cfg_scale) || !std::isfinite(t_eps)) return fail(GEN_EINVAL, "cfg_scale and t_eps must be finite");
+  if (!std::isfinite(cfg_scale) || !std::isfinite(img_cfg_scale) || !std::isfinite(t_eps))
+    return fail(GEN_EINVAL, "cfg_scale, img_cfg_scale and t_eps must be finite");
   for (int i = 0; i < n_img; ++i) {
     if (!std::isfinite(sigma[i])) return fail(GEN_EINVAL, "sigma[%d] is not finite", i);
     if (sigma_next) {
@@ -646,10 +665,12 @@ int gen_tower_step(const gen_block_dims* dims, int n_layers, const gen_block_wei
     return ok();
   }
   for (int i = 0; i < n_img; ++i) {
+    // branches of image i: cond, then uncond (two) or img_cond, uncond (three)
     const float* xc = x0 + (size_t)i * n_br * img;
-    const float* xu = n_br == 2 ? xc + img : nullptr;
-    HIP_TRY(cfg_euler(x_out + i * img, x_t + i * img, xc, xu, img, n_br == 2 ? cfg_scale : 1.0f, sigma[i],
-                      sigma_next[i], t_eps, s));
+    const float* xm = n_br == 3 ? xc + img : nullptr;
+    const float* xu = n_br >= 2 ? xc + (size_t)(n_br - 1) * img : nullptr;
+    HIP_TRY(cfg_euler(x_out + i * img, x_t + i * img, xc, xm, xu, img, n_br >= 2 ? cfg_scale : 1.0f,
+                      n_br == 3 ? img_cfg_scale : 1.0f, sigma[i], sigma_next[i], t_eps, s));
   }
   return ok();
 }

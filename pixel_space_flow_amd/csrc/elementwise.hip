@@ -345,20 +345,25 @@ __global__ __launch_bounds__(256) void temb2_kernel(const T* __restrict__ w2, co
 }
 
 // ---------------------------------------------------------------- CFG + Euler
-template <bool MIX>
+// Guided prediction g per pixel, then x' = x + dt (x - g) / den.
+//   MIX 0: g = c;   MIX 1: g = u + s (c - u);   MIX 2 (three branches, c / i / u = cond /
+//   img_cond / uncond): g = u + s_img (i - u) + s (c - i).
+DEVI float guide(int mix, float c, float i, float u, float s, float si) {
+  return mix == 0 ? c : (mix == 1 ? u + s * (c - u) : u + si * (i - u) + s * (c - i));
+}
+template <int MIX>
 __global__ __launch_bounds__(256) void cfg_euler_kernel(float* xo, const float* xi, const float* __restrict__ xc,
-                                                        const float* __restrict__ xu, size_t n, float scale, float dt,
-                                                        float den) {
+                                                        const float* __restrict__ xm, const float* __restrict__ xu,
+                                                        size_t n, float scale, float iscale, float dt, float den) {
   const size_t i = ((size_t)blockIdx.x * 256 + threadIdx.x) * 4;
   if (i + 4 <= n) {
     float4 a = *(const float4*)(xi + i);
     const float4 c = *(const float4*)(xc + i);
-    float4 g = c;
-    if (MIX) {
-      const float4 u = *(const float4*)(xu + i);
-      g = make_float4(u.x + scale * (c.x - u.x), u.y + scale * (c.y - u.y), u.z + scale * (c.z - u.z),
-                      u.w + scale * (c.w - u.w));
-    }
+    float4 m = c, u = c;
+    if (MIX == 2) m = *(const float4*)(xm + i);
+    if (MIX >= 1) u = *(const float4*)(xu + i);
+    const float4 g = make_float4(guide(MIX, c.x, m.x, u.x, scale, iscale), guide(MIX, c.y, m.y, u.y, scale, iscale),
+                                 guide(MIX, c.z, m.z, u.z, scale, iscale), guide(MIX, c.w, m.w, u.w, scale, iscale));
     a.x = a.x + dt * ((a.x - g.x) / den);
     a.y = a.y + dt * ((a.y - g.y) / den);
     a.z = a.z + dt * ((a.z - g.z) / den);
@@ -366,7 +371,7 @@ __global__ __launch_bounds__(256) void cfg_euler_kernel(float* xo, const float* 
     *(float4*)(xo + i) = a;
   } else {
     for (size_t k = i; k < n; ++k) {
-      const float g = MIX ? xu[k] + scale * (xc[k] - xu[k]) : xc[k];
+      const float g = guide(MIX, xc[k], MIX == 2 ? xm[k] : 0.f, MIX >= 1 ? xu[k] : 0.f, scale, iscale);
       xo[k] = xi[k] + dt * ((xi[k] - g) / den);
     }
   }
@@ -476,16 +481,20 @@ hipError_t timestep_embed(const float* sigma_host, const T* w1, const T* w2, flo
 template hipError_t timestep_embed<bf16>(const float*, const bf16*, const bf16*, float*, float*, int, int, hipStream_t);
 template hipError_t timestep_embed<float>(const float*, const float*, const float*, float*, float*, int, int, hipStream_t);
 
-hipError_t cfg_euler(float* xo, const float* x, const float* xc, const float* xu, size_t n, float scale, float sigma,
-                     float sigma_next, float t_eps, hipStream_t s) {
+hipError_t cfg_euler(float* xo, const float* x, const float* xc, const float* xm, const float* xu, size_t n,
+                     float scale, float img_scale, float sigma, float sigma_next, float t_eps, hipStream_t s) {
   if (n == 0) return hipSuccess;
   const float dt = sigma_next - sigma;
   const float den = sigma > t_eps ? sigma : t_eps;
   const unsigned grid = (unsigned)((n + 1023) / 1024);
-  if (xu && scale != 1.0f)
-    hipLaunchKernelGGL(cfg_euler_kernel<true>, dim3(grid), dim3(256), 0, s, xo, x, xc, xu, n, scale, dt, den);
+  if (xm && xu && img_scale != 1.0f)
+    hipLaunchKernelGGL(cfg_euler_kernel<2>, dim3(grid), dim3(256), 0, s, xo, x, xc, xm, xu, n, scale, img_scale, dt, den);
+  else if (xm && scale != 1.0f)   // image guidance off: two-branch guidance of cond against img_cond
+    hipLaunchKernelGGL(cfg_euler_kernel<1>, dim3(grid), dim3(256), 0, s, xo, x, xc, xm, xm, n, scale, 1.0f, dt, den);
+  else if (!xm && xu && scale != 1.0f)
+    hipLaunchKernelGGL(cfg_euler_kernel<1>, dim3(grid), dim3(256), 0, s, xo, x, xc, xu, xu, n, scale, 1.0f, dt, den);
   else
-    hipLaunchKernelGGL(cfg_euler_kernel<false>, dim3(grid), dim3(256), 0, s, xo, x, xc, xu, n, scale, dt, den);
+    hipLaunchKernelGGL(cfg_euler_kernel<0>, dim3(grid), dim3(256), 0, s, xo, x, xc, xc, xc, n, 1.0f, 1.0f, dt, den);
   return hipGetLastError();
 }
 

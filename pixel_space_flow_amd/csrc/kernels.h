@@ -65,10 +65,12 @@ template <typename T>
 hipError_t timestep_embed(const float* sigma_dev, const T* w1, const T* w2, float* h1, float* temb, int n_img, int D,
                           hipStream_t s);
 
-// xo = x + (sn - s) (x - x0g) / max(s, t_eps), x0g the CFG mix (xu may be null iff scale == 1);
-// xo may equal x.
-hipError_t cfg_euler(float* xo, const float* x, const float* xc, const float* xu, size_t n, float scale, float sigma,
-                     float sigma_next, float t_eps, hipStream_t s);
+// xo = x + (sn - s) (x - x0g) / max(s, t_eps) with x0g the guided prediction: xc alone (no
+// other branch, or unit scales), xu + scale (xc - xu) (two branches), or with xm (img_cond, three
+// branches) xu + img_scale (xm - xu) + scale (xc - xm); img_scale 1 or xu null gives
+// xm + scale (xc - xm).  xo may equal x.
+hipError_t cfg_euler(float* xo, const float* x, const float* xc, const float* xm, const float* xu, size_t n,
+                     float scale, float img_scale, float sigma, float sigma_next, float t_eps, hipStream_t s);
 
 // Router: idx/w [T, k]; u [T, D], wr [E, D]
 template <typename T>

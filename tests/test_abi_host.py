@@ -113,11 +113,16 @@ def test_tower_step_rejects_bad_arguments_on_host(psf):
     arr = (ctypes.c_void_p * 2)(4096, 4096)
     pl = (ctypes.c_int * 2)(4, 4)
 
-    def call(H=64, W=64, n_br=2, cfg_norm=0, sigma_next=nxt, x=4096, ws=1 << 30):
+    def call(H=64, W=64, n_br=2, cfg_norm=0, sigma_next=nxt, x=4096, ws=1 << 30, img_cfg=1.0):
         return psf.lib.gen_tower_step(ctypes.byref(d), 1, lw, 4096, 4096, 4096, 4096, 4096, x, 1, n_br, H, W,
-                                      one, sigma_next, 4.0, cfg_norm, 0.02, arr, arr, pl, 4096, None, 4096, ws, None)
+                                      one, sigma_next, 4.0, img_cfg, cfg_norm, 0.02, arr3, arr3, pl3, 4096, None,
+                                      4096, ws, None)
+    arr3 = (ctypes.c_void_p * 3)(4096, 4096, 4096)
+    pl3 = (ctypes.c_int * 3)(4, 4, 4)
     assert call(H=48) == psf.GEN_EINVAL            # not a multiple of 32
-    assert call(n_br=3) == psf.GEN_EINVAL
+    assert call(n_br=4) == psf.GEN_EINVAL
+    assert call(n_br=0) == psf.GEN_EINVAL
+    assert call(n_br=3, img_cfg=float("nan")) == psf.GEN_EINVAL
     assert call(cfg_norm=1) == psf.GEN_EUNSUPPORTED
     assert call(sigma_next=None) == psf.GEN_EINVAL  # x0-only output needs one branch
     assert call(x=None) == psf.GEN_EINVAL
@@ -130,6 +135,15 @@ def test_flow_euler_cfg_rejects_bad_arguments_on_host(psf):
     assert f(4096, 4096, None, 16, 4.0, 1.0, 0.9, 0.02, None) == psf.GEN_EINVAL   # uncond needed for cfg != 1
     assert f(4100, 4096, 4096, 16, 4.0, 1.0, 0.9, 0.02, None) == psf.GEN_EINVAL   # unaligned
     assert f(4096, 4096, 4096, 16, 4.0, 0.0, 0.0, 0.0, None) == psf.GEN_EINVAL    # zero denominator
+
+
+def test_flow_euler_dual_cfg_rejects_bad_arguments_on_host(psf):
+    f = psf.lib.flow_euler_dual_cfg
+    assert f(4096, 4096, None, 4096, 16, 4.0, 2.0, 1.0, 0.9, 0.02, None) == psf.GEN_EINVAL   # img branch needed
+    assert f(4096, 4096, 4096, None, 16, 4.0, 2.0, 1.0, 0.9, 0.02, None) == psf.GEN_EINVAL   # uncond for img cfg != 1
+    assert f(4096, 4096, 4100, 4096, 16, 4.0, 2.0, 1.0, 0.9, 0.02, None) == psf.GEN_EINVAL   # unaligned
+    assert f(4096, 4096, 4096, 4096, 16, float("inf"), 2.0, 1.0, 0.9, 0.02, None) == psf.GEN_EINVAL
+    assert f(4096, 4096, 4096, 4096, 16, 4.0, 2.0, 0.0, 0.0, 0.0, None) == psf.GEN_EINVAL    # zero denominator
 
 
 def test_block_lora_merge_rejects_bad_arguments_on_host(psf):

@@ -158,6 +158,24 @@ def test_flow_euler_cfg(lib):
     np.testing.assert_allclose(host(xd), O.euler_step(x, c, 0.5, 0.25, 0.02), rtol=1e-5, atol=1e-5)
 
 
+def test_flow_euler_dual_cfg(lib):
+    import torch
+    n = 3 * 64 * 64 + 3
+    x, c, i, u = (W.normal(98, 1, t, (n,)) for t in ("x", "c", "i", "u"))
+    for s_txt, s_img, sg, sn in [(4.0, 2.0, 1.0, 0.75), (4.0, 1.0, 0.5, 0.25), (1.0, 1.0, 0.3, 0.0),
+                                 (1.0, 3.0, 0.01, 0.0), (7.5, 1.5, 0.9, 0.8)]:
+        xd = torch.from_numpy(x).cuda()
+        lib.flow_euler_dual_cfg(xd, torch.from_numpy(c).cuda(), torch.from_numpy(i).cuda(),
+                                torch.from_numpy(u).cuda(), s_txt, s_img, sg, sn, 0.02)
+        ref = O.euler_step(x, O.dual_cfg_mix(c, i, u, s_txt, s_img), sg, sn, 0.02)
+        np.testing.assert_allclose(host(xd), ref, rtol=1e-5, atol=1e-5)
+    xd = torch.from_numpy(x).cuda()        # image guidance off: no uncond branch needed
+    lib.flow_euler_dual_cfg(xd, torch.from_numpy(c).cuda(), torch.from_numpy(i).cuda(), None, 4.0, 1.0, 0.5, 0.25,
+                            0.02)
+    np.testing.assert_allclose(host(xd), O.euler_step(x, O.dual_cfg_mix(c, i, None, 4.0, 1.0), 0.5, 0.25, 0.02),
+                               rtol=1e-5, atol=1e-5)
+
+
 @pytest.mark.parametrize("T,D,E,k", [(300, 256, 32, 8), (4096, 2048, 32, 8), (17, 128, 6, 2)])
 def test_moe_route_exact_sets(lib, T, D, E, k):
     import torch

@@ -36,17 +36,17 @@ class GpuTower:
         self.np_pv = [[W.prefix_kv(w, l, s, seed, dtype)[1] for s in slots] for l in range(w.n_layers)]
         self.pk = [dev(p, dtype) for layer in self.np_pk for p in layer]
         self.pv = [dev(p, dtype) for layer in self.np_pv for p in layer]
-        self.plen = [w.prefix_len] * w.batch
-        self.ws = lib.alloc_workspace(lib.workspace_size(self.dims, w.n_img, w.n_br, w.n_tokens, w.prefix_len))
+        self.plen = [w.prefix_len_of(s) for s in slots]
+        self.ws = lib.alloc_workspace(lib.workspace_size(self.dims, w.n_img, w.n_br, w.n_tokens, w.max_prefix))
 
-    def step(self, x_np, sigma, sigma_next, cfg_scale):
+    def step(self, x_np, sigma, sigma_next, cfg_scale, img_cfg_scale=1.0):
         import torch
         w = self.w
         x = torch.from_numpy(np.ascontiguousarray(x_np)).cuda()
         xo = torch.empty_like(x)
         x0 = torch.empty(w.batch, 3, w.height, w.width, device="cuda")
         self.lib.tower_step(self.dims, self.layers, self.glob, x, w.n_br, sigma, sigma_next, cfg_scale, w.t_eps,
-                            self.pk, self.pv, self.plen, xo, self.ws, x0_out=x0)
+                            self.pk, self.pv, self.plen, xo, self.ws, x0_out=x0, img_cfg_scale=img_cfg_scale)
         torch.cuda.synchronize()
         return host(xo), host(x0)
 
@@ -98,7 +98,7 @@ def test_config0_single_branch_cfg1(lib):
 
 def sampled_tower_check(lib, w, x, sigma, sigma_next, n_rows, seed_tag):
     t = GpuTower(lib, w, "bf16")
-    xn, x0 = t.step(x, sigma, sigma_next, w.cfg_scale)
+    xn, x0 = t.step(x, sigma, sigma_next, w.cfg_scale, w.img_cfg_scale)
     rows = np.sort(W.rng(w.config_id, 0, seed_tag).choice(w.n_tokens, n_rows, replace=False))
     ref = t.oracle_tokens(x, sigma, rows=rows)
     got = O.patchify(x0)[:, rows]
@@ -154,3 +154,40 @@ def test_config2_full_tower_36_layers(lib):
     x = W.noise_image(w)
     log("config 2, 36 layers")
     sampled_tower_check(lib, w, x, [sched[0]], [sched[1]], 512, "rows36")
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_dual_cfg_three_branches_two_steps(lib, dtype):
+    """Image-edit guidance: config 0's tower with three branches (cond, img_cond, uncond) whose
+    prefixes differ in length (48, 40, 32), cfg 4 and image cfg 2, over the 2-step schedule."""
+    w = W.scaled(W.CONFIGS[0], n_br=3, img_cfg_scale=2.0, branch_prefix=(48, 40, 32), prefix_len=48)
+    t = GpuTower(lib, w, dtype)
+    sched = O.sigma_schedule(w.n_steps, w.shift)
+    x = W.noise_image(w)
+    cos_min = TOWER_COS if dtype == "bf16" else 0.99999
+    for k in range(w.n_steps):
+        log(f"dual cfg {dtype} step {k}")
+        xn, x0 = t.step(x, [sched[k]], [sched[k + 1]], w.cfg_scale, w.img_cfg_scale)
+        rn, r0 = O.tower_step(x, k, sched, t.np_glob, lambda l: t.np_layers[l], w.dims, w.n_layers, w.n_br,
+                              t.np_pk, t.np_pv, w.cfg_scale, w.t_eps, np.float32, img_cfg_scale=w.img_cfg_scale)
+        cs = [cosine(x0[b], r0[b]) for b in range(w.batch)]
+        cd = cosine(xn - x, rn - x)
+        log(f"  cos x0 per branch {cs}, dx {cd:.6f}")
+        assert min(cs) >= cos_min and cd >= cos_min
+        # the update against the GPU's own three predictions, every pixel
+        g = O.dual_cfg_mix(x0[0], x0[1], x0[2], w.cfg_scale, w.img_cfg_scale)
+        np.testing.assert_allclose(xn[0], O.euler_step(x[0], g, sched[k], sched[k + 1], w.t_eps),
+                                   rtol=1e-5, atol=1e-5)
+        x = xn
+
+
+def test_dual_cfg_width_2048px_one_layer(lib):
+    """The 2048^2 image-edit workload (3 x 4096 tokens, prefixes 1424 / 1424 / 400) at depth 1,
+    the last block and head checked on sampled tokens of every branch."""
+    w = W.scaled(W.VARIANTS["dual_cfg"], n_layers=1)
+    sched = O.sigma_schedule(w.n_steps, w.shift)
+    x = W.noise_image(w)
+    log("dual cfg 2048^2 at depth 1")
+    xn, x0, got, ref = sampled_tower_check(lib, w, x, [sched[0]], [sched[1]], 256, "rows")
+    g = O.dual_cfg_mix(x0[0], x0[1], x0[2], w.cfg_scale, w.img_cfg_scale)
+    np.testing.assert_allclose(xn[0], O.euler_step(x[0], g, sched[0], sched[1], w.t_eps), rtol=1e-5, atol=1e-5)
