@@ -25,6 +25,9 @@ Sources, cited by page title and section:
                  前提にする" (default.yaml section: x0 loss, uniform timestep)
 Where the pages leave a step open, the reading taken is stated at the function.
 
+``backward.py`` holds the gradients of LoRA training with the x0 loss (the
+derivative of each forward step, the block and the tower walked in reverse).
+
 Parity status: every function here is pinned by a CPU test against a closed
 form, a brute-force computation, a library routine or an invariant, except the
 composition of the full tower, which is pinned only through its pinned parts
@@ -32,3 +35,4 @@ composition of the full tower, which is pinned only through its pinned parts
 unpinned beyond composition.
 """
 from .ref import *  # noqa: F401,F403
+from .backward import *  # noqa: F401,F403
