@@ -171,6 +171,52 @@ int gen_block_lora_merge(const gen_block_dims* dims, const gen_block_weights* w,
 int flow_euler_cfg(float* x, const float* x0_cond, const float* x0_uncond, size_t n, float cfg_scale,
                    float sigma, float sigma_next, float t_eps, void* stream);
 
+/* ---- LoRA training (the trainer's step; sensenova-u1-lora-trainer "Setup notes";
+ * lilting.ch "SenseNova U1 8BのLoRA trainer…", default.yaml: x0 loss, uniform timestep, LoRA on
+ * attention and MLP; DiffSynth-Studio "SenseNova-U1", 模型训练: sites q, k, v, o, gate, up, down).
+ * Only the LoRA matrices receive gradients: base weights, norm gains and embedders are frozen.
+ * Dense blocks, bf16 weights, fp32 residual stream (dims.hidden_dtype = GEN_F32), head_dim 128.
+ * Gradient buffers are float32, laid out as the matrices (lora_a [rank, in], lora_b [out, rank]),
+ * and ACCUMULATE (+=): clear them before a step.  Sites without LoRA need no buffers. */
+typedef struct {
+  float* lora_a[7];
+  float* lora_b[7];
+} gen_lora_grads;
+
+/* Workspace bytes for gen_block_backward (0 on invalid arguments). */
+size_t gen_backward_workspace_size(const gen_block_dims* dims, int B, int N, int max_prefix);
+
+/* Backward of one gen block over B sequences of N tokens (their prefixes as in gen_block_forward):
+ *   hidden_in  [B, N, D] float32: the block's input
+ *   d_hidden   [B, N, D] float32: in, dL/d(block output); out, dL/d(block input)
+ *   grads      LoRA gradient buffers (may be NULL when dims.lora_rank == 0)
+ * The block's forward is recomputed inside the call (activations are not kept between calls). */
+int gen_block_backward(const gen_block_dims* dims, const gen_block_weights* w, const float* hidden_in,
+                       float* d_hidden, int B, int N, const void* const* prefix_k, const void* const* prefix_v,
+                       const int* prefix_len, const gen_lora_grads* grads, void* workspace, size_t workspace_bytes,
+                       void* stream);
+
+/* Workspace bytes for gen_tower_lora_train_step (includes every block's saved input). */
+size_t gen_train_workspace_size(const gen_block_dims* dims, int n_layers, int n_img, int n_tokens, int max_prefix);
+
+/* One LoRA training step of the gen tower with the x0 loss, one branch per sample:
+ *   x0_pred = gen_tower_step's x0 at sigma[i] from x_t (no CFG), loss = mean over all pixels of
+ *   (x0_pred - x0)^2, and the gradient of the loss is carried back through the out head, the
+ *   final RMSNorm and every block, accumulating each layer's LoRA gradients into grads[l].
+ *   x_t, x0      [n_img, 3, H, W] float32 (x_t = (1 - t) x0 + t eps is the caller's sample)
+ *   sigma        HOST [n_img]
+ *   prefix_k/v   HOST [n_layers * n_img] device pointers, index l*n_img + i; prefix_len HOST [n_img]
+ *   grads        HOST [n_layers]
+ *   loss         device float32 scalar (written)
+ *   x0_pred_out  nullable [n_img, 3, H, W] float32
+ * No optimizer update is applied. */
+int gen_tower_lora_train_step(const gen_block_dims* dims, int n_layers, const gen_block_weights* layers,
+                              const void* w_in, const void* temb_w1, const void* temb_w2, const void* g_final,
+                              const void* w_out, const float* x_t, const float* x0, int n_img, int H, int W,
+                              const float* sigma, const void* const* prefix_k, const void* const* prefix_v,
+                              const int* prefix_len, const gen_lora_grads* grads, float* loss, float* x0_pred_out,
+                              void* workspace, size_t workspace_bytes, void* stream);
+
 /* Dual guidance of an image edit and the Euler update, in place, float32, n elements
  * (vllm-omni recipe "SenseNova-U1.5", img2img: cfg_scale guides toward the instruction,
  * img_cfg_scale toward the input image, 1.0 switching image guidance off, the 3-way run using

@@ -21,6 +21,7 @@ LORA_SITES = ("q", "k", "v", "o", "gate", "up", "down")
 EXPORTS = ("gen_block_forward", "gen_tower_step", "flow_euler_cfg", "flow_euler_dual_cfg", "gen_moe_route",
            "gen_workspace_size",
            "gen_sigma_schedule", "gen_last_error", "gen_block_lora_merge", "gen_prefix_forward",
+           "gen_backward_workspace_size", "gen_block_backward", "gen_train_workspace_size", "gen_tower_lora_train_step",
            # include/psf_gen_ops.h
            "gen_op_rmsnorm", "gen_op_linear", "gen_op_qknorm_rope", "gen_op_attention", "gen_op_workspace_size",
            "gen_timing_begin", "gen_timing_end")
@@ -47,6 +48,10 @@ class BlockWeightsC(ctypes.Structure):
                [("lora_a", ctypes.c_void_p * 7), ("lora_b", ctypes.c_void_p * 7)]
 
 
+class LoraGradsC(ctypes.Structure):
+    _fields_ = [("lora_a", ctypes.c_void_p * 7), ("lora_b", ctypes.c_void_p * 7)]
+
+
 def _load():
     # torch bundles its own HIP runtime with the same soname (libamdhip64.so.7) as /opt/rocm's.
     # Mapping torch's first makes the library bind to that one runtime, so device pointers and
@@ -64,6 +69,14 @@ def _load():
     lib.flow_euler_cfg.argtypes = [vp, vp, vp, sz, f, f, f, f, vp]
     lib.flow_euler_dual_cfg.argtypes = [vp, vp, vp, vp, sz, f, f, f, f, f, vp]
     lib.gen_block_lora_merge.argtypes = [P(BlockDimsC), P(BlockWeightsC), vp, vp, vp, vp, vp]
+    lib.gen_backward_workspace_size.argtypes = [P(BlockDimsC), i, i, i]
+    lib.gen_backward_workspace_size.restype = sz
+    lib.gen_block_backward.argtypes = [P(BlockDimsC), P(BlockWeightsC), vp, vp, i, i, P(vp), P(vp), P(i),
+                                       P(LoraGradsC), vp, sz, vp]
+    lib.gen_train_workspace_size.argtypes = [P(BlockDimsC), i, i, i, i]
+    lib.gen_train_workspace_size.restype = sz
+    lib.gen_tower_lora_train_step.argtypes = [P(BlockDimsC), i, P(BlockWeightsC), vp, vp, vp, vp, vp, vp, vp, i, i, i,
+                                              P(f), P(vp), P(vp), P(i), P(LoraGradsC), vp, vp, vp, sz, vp]
     lib.gen_prefix_forward.argtypes = [P(BlockDimsC), i, P(BlockWeightsC), vp, i, i, P(vp), P(vp), vp, vp, sz, vp]
     lib.gen_moe_route.argtypes = [vp, vp, i, i, i, i, i, vp, vp, vp]
     lib.gen_workspace_size.argtypes = [P(BlockDimsC), i, i, i, i]
@@ -174,6 +187,59 @@ def prefix_forward(dims: BlockDimsC, layers: Sequence[BlockWeightsC], hidden, k_
     _check(lib.gen_prefix_forward(ctypes.byref(dims), L, arr, hidden.data_ptr(), B, P, _ptr_array(k_cache),
                                   _ptr_array(v_cache), _ptr(topk_out), workspace.data_ptr(),
                                   workspace.numel() * workspace.element_size(), _stream(stream)))
+
+
+def make_lora_grads(g: dict) -> LoraGradsC:
+    """ctypes gradient buffers from a dict of float32 device tensors keyed ``lora_a_<site>`` /
+    ``lora_b_<site>`` (missing sites: NULL)."""
+    c = LoraGradsC()
+    for k, s in enumerate(LORA_SITES):
+        c.lora_a[k] = _ptr(g.get(f"lora_a_{s}"))
+        c.lora_b[k] = _ptr(g.get(f"lora_b_{s}"))
+    return c
+
+
+def backward_workspace_size(dims: BlockDimsC, B: int, N: int, max_prefix: int) -> int:
+    n = lib.gen_backward_workspace_size(ctypes.byref(dims), B, N, max_prefix)
+    if n == 0:
+        raise GenError(GEN_EINVAL, last_error())
+    return n
+
+
+def train_workspace_size(dims: BlockDimsC, n_layers: int, n_img: int, n_tokens: int, max_prefix: int) -> int:
+    n = lib.gen_train_workspace_size(ctypes.byref(dims), n_layers, n_img, n_tokens, max_prefix)
+    if n == 0:
+        raise GenError(GEN_EINVAL, last_error())
+    return n
+
+
+def block_backward(dims: BlockDimsC, weights: BlockWeightsC, hidden_in, d_hidden, prefix_k, prefix_v, prefix_len,
+                   grads: Optional[LoraGradsC], workspace, stream=None):
+    """d_hidden [B, N, D] fp32: in dL/d(out), out dL/d(in); LoRA gradients accumulate into grads."""
+    B, N = hidden_in.shape[0], hidden_in.shape[1]
+    plen = (ctypes.c_int * B)(*prefix_len)
+    _check(lib.gen_block_backward(ctypes.byref(dims), ctypes.byref(weights), hidden_in.data_ptr(), d_hidden.data_ptr(),
+                                  B, N, _ptr_array(prefix_k), _ptr_array(prefix_v), plen,
+                                  ctypes.byref(grads) if grads is not None else None, workspace.data_ptr(),
+                                  workspace.numel() * workspace.element_size(), _stream(stream)))
+
+
+def tower_lora_train_step(dims: BlockDimsC, layers: Sequence[BlockWeightsC], glob: dict, x_t, x0, sigma, prefix_k,
+                          prefix_v, prefix_len, grads: Sequence[LoraGradsC], loss, workspace, x0_pred_out=None,
+                          stream=None):
+    """One LoRA training step (x0 loss): loss (device fp32 scalar) is written, grads[l] accumulate."""
+    n_img, _, H, W = x_t.shape
+    L = len(layers)
+    arr = (BlockWeightsC * L)(*layers)
+    garr = (LoraGradsC * L)(*grads)
+    sig = (ctypes.c_float * n_img)(*sigma)
+    plen = (ctypes.c_int * n_img)(*prefix_len)
+    _check(lib.gen_tower_lora_train_step(ctypes.byref(dims), L, arr, _ptr(glob["w_in"]), _ptr(glob["temb_w1"]),
+                                         _ptr(glob["temb_w2"]), _ptr(glob["g_final"]), _ptr(glob["w_out"]),
+                                         x_t.data_ptr(), x0.data_ptr(), n_img, H, W, sig, _ptr_array(prefix_k),
+                                         _ptr_array(prefix_v), plen, garr, loss.data_ptr(), _ptr(x0_pred_out),
+                                         workspace.data_ptr(), workspace.numel() * workspace.element_size(),
+                                         _stream(stream)))
 
 
 def block_lora_merge(dims: BlockDimsC, weights: BlockWeightsC, w_qkv_out, w_o_out, w_gate_up_out, w_down_out,

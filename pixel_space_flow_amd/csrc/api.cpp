@@ -401,6 +401,274 @@ int check_prefix_ptrs(const SeqInfo& si, int layer) {
   return GEN_OK;
 }
 
+// ------------------------------------------------------------------ training backward (one block)
+// LoRA sites: 0 q, 1 k, 2 v, 3 o, 4 gate, 5 up, 6 down.
+struct Wb {
+  size_t u, qkv_raw, qkv_n, kc, vt, rope, attn, lse, dot, xmid, u2, gu, z, t_qkv, t_o, t_gu, t_down, tp, dyb, dz,
+      dgu, du, dxf, dO, dq, dk, dv, dqkv, wt, xb, bt, part, total;
+  int Lpad, n_pos;
+};
+
+Wb layout_bwd(const gen_block_dims& d, int B, int N, int max_prefix) {
+  Wb w{};
+  const size_t M = (size_t)B * N, D = d.hidden, I = d.mlp_intermediate, r = d.lora_rank;
+  const size_t Hq = d.n_q_heads, Hkv = d.n_kv_heads, hd = d.head_dim;
+  const size_t QD = Hq * hd, KVD = Hkv * hd, QKV = QD + 2 * KVD;
+  w.Lpad = (int)((max_prefix + N + 63) / 64 * 64);
+  w.n_pos = max_prefix + N;
+  size_t o = 0;
+  auto take = [&](size_t bytes) { size_t a = o; o += up(bytes); return a; };
+  w.u = take(M * D * 2);
+  w.qkv_raw = take(M * QKV * 2);
+  w.qkv_n = take(M * QKV * 2);
+  w.kc = take((size_t)B * Hkv * w.Lpad * hd * 2);
+  w.vt = take((size_t)B * Hkv * w.Lpad * hd * 2);
+  w.rope = take((size_t)w.n_pos * (hd / 2) * 8);
+  w.attn = take(M * QD * 2);
+  w.lse = take((size_t)B * Hq * N * 4);
+  w.dot = take((size_t)B * Hq * N * 4);
+  w.xmid = take(M * D * 4);
+  w.u2 = take(M * D * 2);
+  w.gu = take(M * 2 * I * 2);
+  w.z = take(M * I * 2);
+  w.t_qkv = take(M * 3 * r * 2);
+  w.t_o = take(M * r * 2);
+  w.t_gu = take(M * 2 * r * 2);
+  w.t_down = take(M * r * 2);
+  w.tp = take(M * 3 * r * 2);
+  w.dyb = take(M * D * 2);
+  w.dz = take(M * I * 2);
+  w.dgu = take(M * 2 * I * 2);
+  w.du = take(M * D * 2);
+  w.dxf = take(M * D * 4);
+  w.dO = take(M * QD * 2);
+  w.dq = take(M * QD * 4);
+  w.dk = take(M * KVD * 4);
+  w.dv = take(M * KVD * 4);
+  w.dqkv = take(M * QKV * 2);
+  w.wt = take(std::max(std::max(QKV * D, QD * D), std::max(2 * I * D, I * D)) * 2);
+  w.xb = take(std::max(std::max(D, I), QD) * 3 * r * 2);
+  w.bt = take(r * std::max(std::max(QD, D), I) * 2);
+  w.part = take(std::max((size_t)4 << 20, r * std::max(std::max(QD, D), I)) * 4);
+  w.total = o;
+  return w;
+}
+
+struct BackSite {
+  int site;     // LoRA site index
+  int col;      // first column of the site in the gradient dY
+  int out;      // its width (rows of lora_b)
+};
+
+// For the LoRA sites of one base GEMM whose output gradient is dY [M, lddy]:
+//   tp[:, slot r:(slot+1) r] = (alpha/r) dY_site B_site   (dL/d(x A^T), scaled as the forward's t)
+//   xb[:, slot r:(slot+1) r] = A_site^T                    (the up-projection of the K extension)
+// and p gets that K extension, so the base dgrad GEMM also adds sum_site tp_site A_site.
+// Returns the number of sites present (slot order = list order).
+int lora_back(const gen_block_dims& d, const gen_block_weights& w, const BackSite* sites, int ns, const bf16* dY,
+              int lddy, int in, int M, bf16* tp, bf16* xb, bf16* bt, GemmParams& p, int* slot, hipStream_t s) {
+  const int r = d.lora_rank;
+  int n = 0;
+  for (int i = 0; i < ns; ++i) slot[i] = (r > 0 && w.lora_a[sites[i].site]) ? n++ : -1;
+  if (n == 0) return 0;
+  for (int i = 0; i < ns; ++i) {
+    if (slot[i] < 0) continue;
+    const BackSite& st = sites[i];
+    HIP_TRY(transpose_bf16((const bf16*)w.lora_b[st.site], r, bt, st.out, st.out, r, s));
+    GemmParams q = gp();
+    q.A = dY + st.col; q.lda = lddy; q.B = bt; q.ldb = st.out; q.M = M; q.N = r; q.K = st.out;
+    q.C = tp + slot[i] * r; q.ldc = n * r; q.scale = d.lora_alpha / (float)r;
+    HIP_TRY(gemm_bf16(q, EPI_SCALED, s));
+    HIP_TRY(transpose_bf16((const bf16*)w.lora_a[st.site], in, xb + slot[i] * r, n * r, r, in, s));
+  }
+  p.X = tp; p.ldx = n * r; p.xk = n * r; p.xr = n * r;
+  p.XB[0] = xb; p.XB[1] = p.XB[2] = nullptr;
+  p.xsite_end[0] = p.xsite_end[1] = p.xsite_end[2] = p.N;
+  p.xoff[0] = p.xoff[1] = p.xoff[2] = 0;
+  return n;
+}
+
+// Weight gradients of the sites: dB_site += dY_site^T t_site (the forward's scaled x A^T, columns
+// toff[i] of t), dA_site += tp_slot^T x.
+int lora_wgrad(const gen_block_dims& d, const gen_lora_grads& g, const BackSite* sites, int ns, const int* slot, int n,
+               const bf16* dY, int lddy, const bf16* t, int ldt, const int* toff, const bf16* tp, const bf16* x, int in,
+               int M, float* part, hipStream_t s) {
+  const int r = d.lora_rank;
+  for (int i = 0; i < ns; ++i) {
+    if (slot[i] < 0) continue;
+    const int st = sites[i].site;
+    HIP_TRY(wgrad(dY + sites[i].col, lddy, t + toff[i], ldt, M, sites[i].out, r, g.lora_b[st], part, s));
+    HIP_TRY(wgrad(tp + slot[i] * r, n * r, x, in, M, r, in, g.lora_a[st], part, s));
+  }
+  return GEN_OK;
+}
+
+// Gradient of one dense gen block (bf16 operands, fp32 residual).  h: the block input [M, D]
+// fp32; dh: in, dL/d(block output); out, dL/d(block input).  Recomputes the block's forward
+// into the workspace, then walks back through it; LoRA gradients accumulate into g.
+int run_block_bwd(const gen_block_dims& d, const gen_block_weights& w, const float* h, float* dh, const SeqInfo& si,
+                  const gen_lora_grads& g, void* ws, const Wb& L, hipStream_t s) {
+  const int B = si.B, N = si.N, M = B * N, D = d.hidden, I = d.mlp_intermediate, r = d.lora_rank;
+  const int Hq = d.n_q_heads, Hkv = d.n_kv_heads, hd = d.head_dim;
+  const int QD = Hq * hd, KVD = Hkv * hd, QKV = QD + 2 * KVD;
+  const bool lora = r > 0;
+  const float eps = d.rms_eps;
+  bf16* u = at<bf16>(ws, L.u);
+  bf16* qkv_raw = at<bf16>(ws, L.qkv_raw);
+  bf16* qkv_n = at<bf16>(ws, L.qkv_n);
+  bf16* attn = at<bf16>(ws, L.attn);
+  float* lse = at<float>(ws, L.lse);
+  float* xmid = at<float>(ws, L.xmid);
+  bf16* u2 = at<bf16>(ws, L.u2);
+  bf16* gu = at<bf16>(ws, L.gu);
+  bf16* z = at<bf16>(ws, L.z);
+  bf16* t_qkv = at<bf16>(ws, L.t_qkv);
+  bf16* t_o = at<bf16>(ws, L.t_o);
+  bf16* t_gu = at<bf16>(ws, L.t_gu);
+  bf16* t_down = at<bf16>(ws, L.t_down);
+  bf16* tp = at<bf16>(ws, L.tp);
+  bf16* dyb = at<bf16>(ws, L.dyb);
+  bf16* dz = at<bf16>(ws, L.dz);
+  bf16* dgu = at<bf16>(ws, L.dgu);
+  bf16* du = at<bf16>(ws, L.du);
+  float* dxf = at<float>(ws, L.dxf);
+  bf16* dO = at<bf16>(ws, L.dO);
+  bf16* dqkv = at<bf16>(ws, L.dqkv);
+  bf16* wt = at<bf16>(ws, L.wt);
+  bf16* xb = at<bf16>(ws, L.xb);
+  bf16* bt = at<bf16>(ws, L.bt);
+  float* part = at<float>(ws, L.part);
+  const float2* rope = at<float2>(ws, L.rope);
+  HIP_TRY(rope_table(at<float2>(ws, L.rope), L.n_pos, hd, d.rope_theta, s));
+
+  // ---- forward, keeping what the backward reads
+  const int qkv_sites[3] = {0, 1, 2}, qkv_ends[3] = {QD, QD + KVD, QKV};
+  const int o_site[1] = {3}, gu_sites[2] = {4, 5}, gu_ends[2] = {I, 2 * I}, down_site[1] = {6};
+  int off_qkv[3] = {-1, -1, -1}, off_o[1] = {-1}, off_gu[2] = {-1, -1}, off_down[1] = {-1};
+  int ld_qkv = r, ld_o = r, ld_gu = r, ld_down = r;
+  HIP_TRY((rmsnorm<float, bf16>(h, (const bf16*)w.g_in, u, M, D, eps, s)));
+  {
+    GemmParams p = gp();
+    p.A = u; p.lda = D; p.B = w.w_qkv; p.ldb = D; p.M = M; p.N = QKV; p.K = D; p.C = qkv_raw; p.ldc = QKV;
+    if (lora) {
+      HIP_TRY(lora_down<bf16>(d, w, qkv_sites, 3, u, D, M, t_qkv, off_qkv, ld_qkv, s));
+      if (off_qkv[0] >= 0 || off_qkv[1] >= 0 || off_qkv[2] >= 0) lora_ext(p, d, w, qkv_sites, 3, qkv_ends, t_qkv, ld_qkv, off_qkv);
+    }
+    HIP_TRY(gemm_bf16(p, EPI_STORE, s));
+  }
+  HIP_TRY(hipMemcpyAsync(qkv_n, qkv_raw, (size_t)M * QKV * 2, hipMemcpyDeviceToDevice, s));
+  HIP_TRY(qknorm_rope<bf16>(qkv_n, QKV, si, Hq, Hkv, hd, (const bf16*)w.g_q, (const bf16*)w.g_k, rope, eps, s));
+  HIP_TRY(pack_kv<bf16>(qkv_n, QKV, si, Hq, Hkv, hd, L.Lpad, at<bf16>(ws, L.kc), at<bf16>(ws, L.vt), s));
+  HIP_TRY(attention_bf16(qkv_n, QKV, si, Hq, Hkv, hd, L.Lpad, at<bf16>(ws, L.kc), at<bf16>(ws, L.vt), attn, QD,
+                         nullptr, nullptr, 0.f, false, s, lse));
+  {
+    GemmParams p = gp();
+    p.A = attn; p.lda = QD; p.B = w.w_o; p.ldb = QD; p.M = M; p.N = D; p.K = QD;
+    p.C = xmid; p.ldc = D; p.R = h; p.ldr = D;
+    if (lora) {
+      HIP_TRY(lora_down<bf16>(d, w, o_site, 1, attn, QD, M, t_o, off_o, ld_o, s));
+      if (off_o[0] >= 0) lora_ext(p, d, w, o_site, 1, &D, t_o, ld_o, off_o);
+    }
+    HIP_TRY(gemm_bf16(p, EPI_RESID_F32, s));
+  }
+  HIP_TRY((rmsnorm<float, bf16>(xmid, (const bf16*)w.g_post, u2, M, D, eps, s)));
+  {
+    GemmParams p = gp();
+    p.A = u2; p.lda = D; p.B = w.w_gate_up; p.ldb = D; p.M = M; p.N = 2 * I; p.K = D; p.C = gu; p.ldc = 2 * I;
+    if (lora) {
+      HIP_TRY(lora_down<bf16>(d, w, gu_sites, 2, u2, D, M, t_gu, off_gu, ld_gu, s));
+      if (off_gu[0] >= 0 || off_gu[1] >= 0) lora_ext(p, d, w, gu_sites, 2, gu_ends, t_gu, ld_gu, off_gu);
+    }
+    HIP_TRY(gemm_bf16(p, EPI_STORE, s));
+  }
+  HIP_TRY(swiglu_fwd(gu, z, M, I, s));
+  if (lora) HIP_TRY(lora_down<bf16>(d, w, down_site, 1, z, I, M, t_down, off_down, ld_down, s));
+
+  // ---- backward
+  int slot[3], n;
+  HIP_TRY(cast_f32_bf16(dh, dyb, (int64_t)M * D, s));
+  {  // down projection: dz = dy W_down (+ LoRA)
+    const BackSite bs[1] = {{6, 0, D}};
+    GemmParams p = gp();
+    HIP_TRY(transpose_bf16((const bf16*)w.w_down, I, wt, D, D, I, s));
+    p.A = dyb; p.lda = D; p.B = wt; p.ldb = D; p.M = M; p.N = I; p.K = D; p.C = dz; p.ldc = I;
+    n = lora_back(d, w, bs, 1, dyb, D, I, M, tp, xb, bt, p, slot, s);
+    if (n < 0) return n;
+    HIP_TRY(gemm_bf16(p, EPI_STORE, s));
+    if (n > 0) {
+      int rc = lora_wgrad(d, g, bs, 1, slot, n, dyb, D, t_down, ld_down, off_down, tp, z, I, M, part, s);
+      if (rc) return rc;
+    }
+  }
+  HIP_TRY(swiglu_bwd(gu, dz, dgu, M, I, s));
+  {  // gate/up: du2 = dgate W_gate + dup W_up (+ LoRA)
+    const BackSite bs[2] = {{4, 0, I}, {5, I, I}};
+    GemmParams p = gp();
+    HIP_TRY(transpose_bf16((const bf16*)w.w_gate_up, D, wt, 2 * I, 2 * I, D, s));
+    p.A = dgu; p.lda = 2 * I; p.B = wt; p.ldb = 2 * I; p.M = M; p.N = D; p.K = 2 * I; p.C = du; p.ldc = D;
+    n = lora_back(d, w, bs, 2, dgu, 2 * I, D, M, tp, xb, bt, p, slot, s);
+    if (n < 0) return n;
+    HIP_TRY(gemm_bf16(p, EPI_STORE, s));
+    if (n > 0) {
+      int rc = lora_wgrad(d, g, bs, 2, slot, n, dgu, 2 * I, t_gu, ld_gu, off_gu, tp, u2, D, M, part, s);
+      if (rc) return rc;
+    }
+  }
+  HIP_TRY(rmsnorm_bwd(xmid, (const bf16*)w.g_post, du, dh, dxf, M, D, eps, s));
+  HIP_TRY(cast_f32_bf16(dxf, dyb, (int64_t)M * D, s));
+  {  // O projection: dO = dx W_o (+ LoRA)
+    const BackSite bs[1] = {{3, 0, D}};
+    GemmParams p = gp();
+    HIP_TRY(transpose_bf16((const bf16*)w.w_o, QD, wt, D, D, QD, s));
+    p.A = dyb; p.lda = D; p.B = wt; p.ldb = D; p.M = M; p.N = QD; p.K = D; p.C = dO; p.ldc = QD;
+    n = lora_back(d, w, bs, 1, dyb, D, QD, M, tp, xb, bt, p, slot, s);
+    if (n < 0) return n;
+    HIP_TRY(gemm_bf16(p, EPI_STORE, s));
+    if (n > 0) {
+      int rc = lora_wgrad(d, g, bs, 1, slot, n, dyb, D, t_o, ld_o, off_o, tp, attn, QD, M, part, s);
+      if (rc) return rc;
+    }
+  }
+  HIP_TRY(attention_bwd(qkv_n, QKV, si, Hq, Hkv, hd, attn, dO, lse, at<float>(ws, L.dot), at<float>(ws, L.dq),
+                        at<float>(ws, L.dk), at<float>(ws, L.dv), s));
+  HIP_TRY(qknorm_rope_bwd(qkv_raw, QKV, at<float>(ws, L.dq), at<float>(ws, L.dk), at<float>(ws, L.dv), si, Hq, Hkv, hd,
+                          (const bf16*)w.g_q, (const bf16*)w.g_k, rope, eps, dqkv, QKV, s));
+  {  // QKV projection: du = dqkv W_qkv (+ LoRA on q, k, v)
+    const BackSite bs[3] = {{0, 0, QD}, {1, QD, KVD}, {2, QD + KVD, KVD}};
+    GemmParams p = gp();
+    HIP_TRY(transpose_bf16((const bf16*)w.w_qkv, D, wt, QKV, QKV, D, s));
+    p.A = dqkv; p.lda = QKV; p.B = wt; p.ldb = QKV; p.M = M; p.N = D; p.K = QKV; p.C = du; p.ldc = D;
+    n = lora_back(d, w, bs, 3, dqkv, QKV, D, M, tp, xb, bt, p, slot, s);
+    if (n < 0) return n;
+    HIP_TRY(gemm_bf16(p, EPI_STORE, s));
+    if (n > 0) {
+      int rc = lora_wgrad(d, g, bs, 3, slot, n, dqkv, QKV, t_qkv, ld_qkv, off_qkv, tp, u, D, M, part, s);
+      if (rc) return rc;
+    }
+  }
+  HIP_TRY(rmsnorm_bwd(h, (const bf16*)w.g_in, du, dxf, dh, M, D, eps, s));
+  return GEN_OK;
+}
+
+int check_train_dims(const gen_block_dims* d) {
+  int rc = check_dims(d);
+  if (rc) return rc;
+  if (d->dtype != GEN_BF16 || d->hidden_dtype != GEN_F32)
+    return fail(GEN_EUNSUPPORTED, "the backward pass runs with bf16 weights and an fp32 residual stream");
+  if (d->mlp_intermediate <= 0) return fail(GEN_EUNSUPPORTED, "the backward pass covers dense blocks only");
+  if (d->head_dim != 128) return fail(GEN_EUNSUPPORTED, "the attention backward needs head_dim 128");
+  return GEN_OK;
+}
+
+int check_grads(const gen_block_dims* d, const gen_block_weights* w, const gen_lora_grads* g, int layer) {
+  if (d->lora_rank == 0) return GEN_OK;
+  if (!g) return fail(GEN_EINVAL, "layer %d: grads is NULL", layer);
+  for (int s = 0; s < 7; ++s)
+    if (w->lora_a[s] && (!g->lora_a[s] || !g->lora_b[s]))
+      return fail(GEN_EINVAL, "layer %d: LoRA site %d has no gradient buffers", layer, s);
+  return GEN_OK;
+}
+
 }  // namespace
 
 // ==================================================================== exported
@@ -671,6 +939,171 @@ int gen_tower_step(const gen_block_dims* dims, int n_layers, const gen_block_wei
     const float* xu = n_br >= 2 ? xc + (size_t)(n_br - 1) * img : nullptr;
     HIP_TRY(cfg_euler(x_out + i * img, x_t + i * img, xc, xm, xu, img, n_br >= 2 ? cfg_scale : 1.0f,
                       n_br == 3 ? img_cfg_scale : 1.0f, sigma[i], sigma_next[i], t_eps, s));
+  }
+  return ok();
+}
+
+
+// ------------------------------------------------------------------ training backward
+size_t gen_backward_workspace_size(const gen_block_dims* dims, int B, int N, int max_prefix) {
+  if (check_train_dims(dims) != GEN_OK) return 0;
+  if (B < 1 || N < 1 || max_prefix < 0) {
+    fail(GEN_EINVAL, "sizes must be positive");
+    return 0;
+  }
+  g_err.clear();
+  return layout_bwd(*dims, B, N, max_prefix).total;
+}
+
+int gen_block_backward(const gen_block_dims* dims, const gen_block_weights* w, const float* hidden_in, float* d_hidden,
+                       int B, int N, const void* const* prefix_k, const void* const* prefix_v, const int* prefix_len,
+                       const gen_lora_grads* grads, void* workspace, size_t workspace_bytes, void* stream) {
+  int rc = check_train_dims(dims);
+  if (rc) return rc;
+  if ((rc = check_weights(dims, w, 0))) return rc;
+  if ((rc = check_grads(dims, w, grads, 0))) return rc;
+  if (!hidden_in || !d_hidden || !aligned16(hidden_in) || !aligned16(d_hidden))
+    return fail(GEN_EINVAL, "hidden_in/d_hidden NULL or not 16-byte aligned");
+  if (B < 1 || N < 1) return fail(GEN_EINVAL, "B=%d and N=%d must be >= 1", B, N);
+  if (B > MAXB) return fail(GEN_EUNSUPPORTED, "B=%d > %d sequences per call", B, MAXB);
+  int maxp = 0;
+  if ((rc = check_prefix(dims, B, prefix_k, prefix_v, prefix_len, &maxp))) return rc;
+  const SeqInfo si = make_seq(B, N, prefix_k, prefix_v, prefix_len);
+  if ((rc = check_prefix_ptrs(si, 0))) return rc;
+  if (!workspace || !aligned16(workspace)) return fail(GEN_EINVAL, "workspace is NULL or not 16-byte aligned");
+  const Wb L = layout_bwd(*dims, B, N, maxp);
+  if (workspace_bytes < L.total) return fail(GEN_EWORKSPACE, "workspace %zu bytes < %zu required", workspace_bytes, L.total);
+  gen_lora_grads none{};
+  rc = run_block_bwd(*dims, *w, hidden_in, d_hidden, si, grads ? *grads : none, workspace, L, (hipStream_t)stream);
+  return rc ? rc : ok();
+}
+
+namespace {
+constexpr int LOSS_PARTS = 1024;
+struct Wt {
+  size_t fwd, bwd, saved, dh, pred, dpred, dtok, dhn, parts, woutT, total;
+};
+Wt layout_train(const gen_block_dims& d, int n_layers, int n_img, int N, int maxp) {
+  Wt w{};
+  const size_t M = (size_t)n_img * N, D = d.hidden;
+  size_t o = 0;
+  auto take = [&](size_t bytes) { size_t a = o; o += up(bytes); return a; };
+  w.fwd = take(layout(d, n_img, 1, N, maxp).total);
+  w.bwd = take(layout_bwd(d, n_img, N, maxp).total);
+  w.saved = take((size_t)n_layers * M * D * 4);
+  w.dh = take(M * D * 4);
+  w.pred = take(M * 3072 * 4);
+  w.dpred = take(M * 3072 * 4);
+  w.dtok = take(M * 3072 * 2);
+  w.dhn = take(M * D * 2);
+  w.parts = take(LOSS_PARTS * 4);
+  w.woutT = take(3072 * D * 2);
+  w.total = o;
+  return w;
+}
+}  // namespace
+
+size_t gen_train_workspace_size(const gen_block_dims* dims, int n_layers, int n_img, int n_tokens, int max_prefix) {
+  if (check_train_dims(dims) != GEN_OK) return 0;
+  if (n_layers < 1 || n_img < 1 || n_tokens < 1 || max_prefix < 0) {
+    fail(GEN_EINVAL, "sizes must be positive");
+    return 0;
+  }
+  g_err.clear();
+  return layout_train(*dims, n_layers, n_img, n_tokens, max_prefix).total;
+}
+
+int gen_tower_lora_train_step(const gen_block_dims* dims, int n_layers, const gen_block_weights* layers,
+                              const void* w_in, const void* temb_w1, const void* temb_w2, const void* g_final,
+                              const void* w_out, const float* x_t, const float* x0, int n_img, int H, int W,
+                              const float* sigma, const void* const* prefix_k, const void* const* prefix_v,
+                              const int* prefix_len, const gen_lora_grads* grads, float* loss, float* x0_pred_out,
+                              void* workspace, size_t workspace_bytes, void* stream) {
+  int rc = check_train_dims(dims);
+  if (rc) return rc;
+  if (n_layers < 1) return fail(GEN_EINVAL, "n_layers %d < 1", n_layers);
+  if (!layers) return fail(GEN_EINVAL, "layers is NULL");
+  for (int l = 0; l < n_layers; ++l) {
+    if ((rc = check_weights(dims, &layers[l], l))) return rc;
+    if ((rc = check_grads(dims, &layers[l], grads ? &grads[l] : nullptr, l))) return rc;
+  }
+  const void* glob[] = {w_in, temb_w1, temb_w2, g_final, w_out, x_t, x0, loss};
+  const char* gname[] = {"w_in", "temb_w1", "temb_w2", "g_final", "w_out", "x_t", "x0", "loss"};
+  for (int i = 0; i < 8; ++i) {
+    if (!glob[i]) return fail(GEN_EINVAL, "%s is NULL", gname[i]);
+    if (i < 7 && !aligned16(glob[i])) return fail(GEN_EINVAL, "%s is not 16-byte aligned", gname[i]);
+  }
+  if (x0_pred_out && !aligned16(x0_pred_out)) return fail(GEN_EINVAL, "x0_pred_out is not 16-byte aligned");
+  if (n_img < 1) return fail(GEN_EINVAL, "n_img %d < 1", n_img);
+  if (n_img > MAXB) return fail(GEN_EUNSUPPORTED, "n_img = %d > %d", n_img, MAXB);
+  if (H <= 0 || W <= 0 || H % 32 || W % 32) return fail(GEN_EINVAL, "H=%d and W=%d must be positive multiples of 32", H, W);
+  if (!sigma) return fail(GEN_EINVAL, "sigma is NULL");
+  for (int i = 0; i < n_img; ++i)
+    if (!std::isfinite(sigma[i])) return fail(GEN_EINVAL, "sigma[%d] is not finite", i);
+  const int B = n_img, N = (H / 32) * (W / 32), M = B * N, D = dims->hidden;
+  int maxp = 0;
+  if ((rc = check_prefix(dims, B, prefix_k, prefix_v, prefix_len, &maxp))) return rc;
+  for (int l = 0; l < n_layers; ++l) {
+    const SeqInfo si = make_seq(B, N, prefix_k + (size_t)l * B, prefix_v + (size_t)l * B, prefix_len);
+    if ((rc = check_prefix_ptrs(si, l))) return rc;
+  }
+  if (!workspace || !aligned16(workspace)) return fail(GEN_EINVAL, "workspace is NULL or not 16-byte aligned");
+  const Wt T = layout_train(*dims, n_layers, n_img, N, maxp);
+  if (workspace_bytes < T.total) return fail(GEN_EWORKSPACE, "workspace %zu bytes < %zu required", workspace_bytes, T.total);
+
+  hipStream_t s = (hipStream_t)stream;
+  void* fws = at<char>(workspace, T.fwd);
+  const Ws F = layout(*dims, n_img, 1, N, maxp);
+  float* hidden = at<float>(fws, F.hidden);
+  // forward, saving each block's input
+  HIP_TRY(timestep_embed<bf16>(sigma, (const bf16*)temb_w1, (const bf16*)temb_w2, at<float>(fws, F.h1),
+                               at<float>(fws, F.temb), n_img, D, s));
+  HIP_TRY(patchify<bf16>(x_t, at<bf16>(fws, F.patches), n_img, H, W, s));
+  {
+    GemmParams p = gp();
+    p.A = at<bf16>(fws, F.patches); p.lda = 3072; p.B = w_in; p.ldb = 3072; p.M = M; p.N = D; p.K = 3072;
+    p.C = hidden; p.ldc = D; p.bias = at<float>(fws, F.temb); p.rows_per = N; p.n_bcast = 1;
+    HIP_TRY(gemm_bf16(p, EPI_BIAS_BCAST_F32, s));
+  }
+  HIP_TRY(rope_table(at<float2>(fws, F.rope), F.n_pos, dims->head_dim, dims->rope_theta, s));
+  for (int l = 0; l < n_layers; ++l) {
+    HIP_TRY(hipMemcpyAsync(at<float>(workspace, T.saved) + (size_t)l * M * D, hidden, (size_t)M * D * 4,
+                           hipMemcpyDeviceToDevice, s));
+    const SeqInfo si = make_seq(B, N, prefix_k + (size_t)l * B, prefix_v + (size_t)l * B, prefix_len);
+    if ((rc = run_block<bf16, float>(*dims, layers[l], hidden, si, fws, F, nullptr, s))) return rc;
+  }
+  bf16* u = at<bf16>(fws, F.u);
+  HIP_TRY((rmsnorm<float, bf16>(hidden, (const bf16*)g_final, u, M, D, dims->rms_eps, s)));
+  float* pred = x0_pred_out ? x0_pred_out : at<float>(workspace, T.pred);
+  {
+    GemmParams p = gp();
+    p.A = u; p.lda = D; p.B = w_out; p.ldb = D; p.M = M; p.N = 3072; p.K = D;
+    p.C = pred; p.rows_per = N; p.img_H = H; p.img_W = W;
+    HIP_TRY(gemm_bf16(p, EPI_F32_IMG, s));
+  }
+  // loss and its gradient with respect to the prediction, back through the head and final norm
+  float* dpred = at<float>(workspace, T.dpred);
+  HIP_TRY(x0_loss(pred, x0, dpred, at<float>(workspace, T.parts), LOSS_PARTS, loss, (int64_t)M * 3072, s));
+  bf16* dtok = at<bf16>(workspace, T.dtok);
+  HIP_TRY(patchify<bf16>(dpred, dtok, n_img, H, W, s));
+  bf16* woutT = at<bf16>(workspace, T.woutT);
+  HIP_TRY(transpose_bf16((const bf16*)w_out, D, woutT, 3072, 3072, D, s));
+  bf16* dhn = at<bf16>(workspace, T.dhn);
+  {
+    GemmParams p = gp();
+    p.A = dtok; p.lda = 3072; p.B = woutT; p.ldb = 3072; p.M = M; p.N = D; p.K = 3072; p.C = dhn; p.ldc = D;
+    HIP_TRY(gemm_bf16(p, EPI_STORE, s));
+  }
+  float* dh = at<float>(workspace, T.dh);
+  HIP_TRY(rmsnorm_bwd(hidden, (const bf16*)g_final, dhn, nullptr, dh, M, D, dims->rms_eps, s));
+  void* bws = at<char>(workspace, T.bwd);
+  const Wb L = layout_bwd(*dims, n_img, N, maxp);
+  gen_lora_grads none{};
+  for (int l = n_layers - 1; l >= 0; --l) {
+    const SeqInfo si = make_seq(B, N, prefix_k + (size_t)l * B, prefix_v + (size_t)l * B, prefix_len);
+    rc = run_block_bwd(*dims, layers[l], at<float>(workspace, T.saved) + (size_t)l * M * D, dh, si,
+                       grads ? grads[l] : none, bws, L, s);
+    if (rc) return rc;
   }
   return ok();
 }

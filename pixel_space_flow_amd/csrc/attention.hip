@@ -57,7 +57,7 @@ __global__ __launch_bounds__(256, QB == 1 ? 2 : 1) void attn_v2_kernel(const bf1
                                                                      int64_t ldo, float scale_log2, int n_qb,
                                                                      const bf16* __restrict__ gq,
                                                                      const float2* __restrict__ table, float eps,
-                                                                     int causal) {
+                                                                     int causal, float* __restrict__ lse) {
   constexpr int KT = 64;                  // keys per tile
   constexpr int KROW = D * 2;             // bytes per K row
   constexpr int KCH = D / 8;              // 16-byte chunks per K row
@@ -334,6 +334,8 @@ __global__ __launch_bounds__(256, QB == 1 ? 2 : 1) void attn_v2_kernel(const bf1
     const float lt = l[qb] + __shfl_xor(l[qb], 32, 64);
     const float inv = 1.0f / lt;
     const int query = qbase + qb * 32 + lr;
+    // log2-sum-exp of the scaled scores, for the backward pass: p = 2^(s log2(e)/sqrt(d) - lse)
+    if (lse && lh == 0 && query < N) lse[((int64_t)b * Hq + h) * N + query] = m[qb] + __log2f(lt);
     if (query < N) {
       bf16* op = O + ((int64_t)b * N + query) * ldo + (int64_t)h * D;
 #pragma unroll
@@ -387,7 +389,7 @@ __global__ __launch_bounds__(128) void attn_f32_kernel(const float* __restrict__
 
 hipError_t attention_bf16(const bf16* qkv, int64_t ldq, const SeqInfo& si, int Hq, int Hkv, int d, int Lpad,
                           const bf16* Kc, const bf16* Vt, bf16* O, int64_t ldo, const bf16* gq,
-                          const float2* table, float eps, bool causal, hipStream_t s) {
+                          const float2* table, float eps, bool causal, hipStream_t s, float* lse) {
   const int n_qb = (si.N + 127) / 128;
   const int total = si.B * Hkv * n_qb * (Hq / Hkv);
   if (total == 0) return hipSuccess;
@@ -400,7 +402,7 @@ hipError_t attention_bf16(const bf16* qkv, int64_t ldq, const SeqInfo& si, int H
   const int total2 = si.B * Hkv * n_qb2 * (Hq / Hkv / hpw);
 #define PSF_ATTN(DD, QKN)                                                                              \
   hipLaunchKernelGGL((attn_v2_kernel<DD, QB, QKN>), dim3(total2), dim3(256), 0, s, qkv, ldq, si, Hq, Hkv, Lpad, Kc, \
-                     Vt, O, ldo, scale_log2, n_qb2, gq, table, eps, causal ? 1 : 0)
+                     Vt, O, ldo, scale_log2, n_qb2, gq, table, eps, causal ? 1 : 0, lse)
   if (d == 128) {
     if (gq) PSF_ATTN(128, true); else PSF_ATTN(128, false);
   } else if (d == 64) {

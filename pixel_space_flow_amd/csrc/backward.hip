@@ -1,0 +1,570 @@
+// Backward kernels of LoRA training with the x0 loss: the residual-stream gradient goes down the
+// tower through every step of the gen block, and weight gradients are formed for the LoRA
+// matrices only (base weights frozen).  bf16 operands, fp32 accumulation and fp32 gradients of
+// the residual stream.
+//
+//   transpose_kernel       out[c][r] = in[r][c] (frozen weights and LoRA matrices as GEMM operands)
+//   cast_kernel            fp32 -> bf16 (GEMM operands)
+//   rmsnorm_bwd_kernel     out = base + r g dy - x r^3 sum(g dy x) / D, one row per workgroup
+//   swiglu_kernel          z = silu(gate) up, and its backward
+//   qknorm_rope_bwd_kernel gradient through RoPE (the inverse rotation) and the per-head RMSNorm
+//   attn_bwd_dot_kernel    D[q] = sum_i dO[q, i] O[q, i]
+//   attn_bwd_dkdv_kernel   dK, dV of the image keys: one wave per 32 keys, over every query of the
+//                          group's heads, P recomputed from the forward's log-sum-exp
+//   attn_bwd_dq_kernel     dQ: one wave per 32 queries, over every key (prefix and image)
+//   wgrad_kernel           C[n1, n2] += sum_m X[m, n1] Y[m, n2] (LoRA weight gradients), split over m
+//   x0_loss_kernel         squared error partial sums and dL/dx0
+#include "common.h"
+#include "kernels.h"
+
+namespace psf {
+namespace {
+
+// ---------------------------------------------------------------- layout helpers
+__global__ __launch_bounds__(256) void transpose_kernel(const bf16* __restrict__ in, int64_t ldi, bf16* __restrict__ out,
+                                                        int64_t ldo, int R, int C) {
+  __shared__ uint16_t tile[64][66];
+  const int r0 = blockIdx.y * 64, c0 = blockIdx.x * 64;
+  const int tx = threadIdx.x & 63, ty = threadIdx.x >> 6;
+  const uint16_t* src = (const uint16_t*)in;
+  uint16_t* dst = (uint16_t*)out;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    const int r = r0 + ty + 4 * i, c = c0 + tx;
+    tile[ty + 4 * i][tx] = (r < R && c < C) ? src[(int64_t)r * ldi + c] : 0;
+  }
+  __syncthreads();
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    const int c = c0 + ty + 4 * i, r = r0 + tx;
+    if (c < C && r < R) dst[(int64_t)c * ldo + r] = tile[tx][ty + 4 * i];
+  }
+}
+
+__global__ __launch_bounds__(256) void cast_kernel(const float* __restrict__ x, bf16* __restrict__ y, int64_t n) {
+  const int64_t i = ((int64_t)blockIdx.x * 256 + threadIdx.x) * 4;
+  if (i + 4 <= n) {
+    const float4 v = *(const float4*)(x + i);
+    bf16x4 o = {static_cast<bf16>(v.x), static_cast<bf16>(v.y), static_cast<bf16>(v.z), static_cast<bf16>(v.w)};
+    *(bf16x4*)(y + i) = o;
+  } else {
+    for (int64_t k = i; k < n; ++k) y[k] = static_cast<bf16>(x[k]);
+  }
+}
+
+DEVI float block_sum256(float v, float* red) {
+  v = warp_sum(v);
+  const int w = threadIdx.x >> 6;
+  __syncthreads();
+  if ((threadIdx.x & 63) == 0) red[w] = v;
+  __syncthreads();
+  return red[0] + red[1] + red[2] + red[3];
+}
+
+// out[m, :] = base[m, :] + dRMSNorm(x[m, :]; g)^T dy[m, :]   (base may alias out, or be null)
+__global__ __launch_bounds__(256) void rmsnorm_bwd_kernel(const float* __restrict__ x, const bf16* __restrict__ g,
+                                                          const bf16* __restrict__ dy, const float* base,
+                                                          float* out, int D, float eps) {
+  __shared__ float red[4];
+  const int64_t row = blockIdx.x;
+  const float* xr = x + row * D;
+  const bf16* dr = dy + row * D;
+  float ss = 0.f, sgx = 0.f;
+  for (int i = threadIdx.x; i < D; i += 256) {
+    const float xv = xr[i], gd = static_cast<float>(g[i]) * static_cast<float>(dr[i]);
+    ss += xv * xv;
+    sgx += gd * xv;
+  }
+  ss = block_sum256(ss, red);
+  sgx = block_sum256(sgx, red);
+  const float r = 1.0f / sqrtf(ss / (float)D + eps);
+  const float c = r * r * r * sgx / (float)D;
+  for (int i = threadIdx.x; i < D; i += 256) {
+    const float gd = static_cast<float>(g[i]) * static_cast<float>(dr[i]);
+    const float v = r * gd - xr[i] * c;
+    out[row * D + i] = (base ? base[row * D + i] : 0.f) + v;
+  }
+}
+
+// z[m, j] = silu(gu[m, j]) gu[m, I + j]
+__global__ __launch_bounds__(256) void swiglu_kernel(const bf16* __restrict__ gu, bf16* __restrict__ z, int I, int64_t n) {
+  const int64_t t = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (t >= n) return;
+  const int64_t m = t / I;
+  const int j = (int)(t - m * I);
+  const float gt = static_cast<float>(gu[m * 2 * I + j]), up = static_cast<float>(gu[m * 2 * I + I + j]);
+  z[t] = static_cast<bf16>(gt / (1.0f + __expf(-gt)) * up);
+}
+
+// dgu[m, j] = dz up silu'(gate), dgu[m, I + j] = dz silu(gate)
+__global__ __launch_bounds__(256) void swiglu_bwd_kernel(const bf16* __restrict__ gu, const bf16* __restrict__ dz,
+                                                         bf16* __restrict__ dgu, int I, int64_t n) {
+  const int64_t t = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (t >= n) return;
+  const int64_t m = t / I;
+  const int j = (int)(t - m * I);
+  const float gt = static_cast<float>(gu[m * 2 * I + j]), up = static_cast<float>(gu[m * 2 * I + I + j]);
+  const float d = static_cast<float>(dz[t]);
+  const float s = 1.0f / (1.0f + __expf(-gt));
+  dgu[m * 2 * I + j] = static_cast<bf16>(d * up * (s + gt * s * (1.0f - s)));
+  dgu[m * 2 * I + I + j] = static_cast<bf16>(d * gt * s);
+}
+
+// One wave per (token, head) of the q and k heads: lane p < d/2 holds the rotate-half pair
+// (p, p + d/2).  grad (fp32, row stride ldg) is the gradient with respect to the normed and
+// rotated head; raw the head before the norm.  Writes the gradient with respect to raw (bf16)
+// into dqkv; v heads copy their gradient (dv) as it is.
+__global__ __launch_bounds__(256) void qknorm_rope_bwd_kernel(const bf16* __restrict__ raw, int64_t ldr,
+                                                              const float* __restrict__ dq, const float* __restrict__ dk,
+                                                              const float* __restrict__ dv, SeqInfo si, int Hq, int Hkv,
+                                                              int d, const bf16* __restrict__ gq,
+                                                              const bf16* __restrict__ gk,
+                                                              const float2* __restrict__ table, float eps,
+                                                              bf16* __restrict__ dqkv, int64_t ldo, int64_t total) {
+  const int lane = threadIdx.x & 63;
+  const int64_t hv = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (hv >= total) return;
+  const int H = Hq + 2 * Hkv;
+  const int64_t tok = hv / H;
+  const int head = (int)(hv - tok * H);
+  const int b = (int)(tok / si.N), n = (int)(tok - (int64_t)b * si.N);
+  const int half = d / 2;
+  bf16* op = dqkv + tok * ldo + (int64_t)head * d;
+  if (head >= Hq + Hkv) {                       // v: the gradient passes through
+    const float* gp = dv + tok * (int64_t)Hkv * d + (int64_t)(head - Hq - Hkv) * d;
+    for (int i = lane; i < d; i += 64) op[i] = static_cast<bf16>(gp[i]);
+    return;
+  }
+  const bool isq = head < Hq;
+  const float* gp = isq ? dq + tok * (int64_t)Hq * d + (int64_t)head * d : dk + tok * (int64_t)Hkv * d + (int64_t)(head - Hq) * d;
+  const bf16* rp = raw + tok * ldr + (int64_t)head * d;
+  const bf16* g = isq ? gq : gk;
+  const bool act = lane < half;
+  const int p = act ? lane : 0;
+  // inverse rotation of the incoming gradient
+  const float2 cs = table[(int64_t)(si.plen[b] + n) * half + p];
+  const float ga = gp[p], gb = gp[p + half];
+  const float ta = ga * cs.x + gb * cs.y, tb = -ga * cs.y + gb * cs.x;
+  // RMSNorm backward over the head vector
+  const float xa = static_cast<float>(rp[p]), xb = static_cast<float>(rp[p + half]);
+  const float wa = static_cast<float>(g[p]), wb = static_cast<float>(g[p + half]);
+  float ss = act ? xa * xa + xb * xb : 0.f;
+  float sgx = act ? wa * ta * xa + wb * tb * xb : 0.f;
+  ss = warp_sum(ss);
+  sgx = warp_sum(sgx);
+  const float r = 1.0f / sqrtf(ss / (float)d + eps);
+  const float c = r * r * r * sgx / (float)d;
+  if (act) {
+    op[p] = static_cast<bf16>(r * wa * ta - xa * c);
+    op[p + half] = static_cast<bf16>(r * wb * tb - xb * c);
+  }
+}
+
+// D[(b*Hq + h)*N + n] = sum_i dO[tok, h*d + i] O[tok, h*d + i]: one wave per (token, head)
+__global__ __launch_bounds__(256) void attn_bwd_dot_kernel(const bf16* __restrict__ dO, const bf16* __restrict__ O,
+                                                           int64_t ld, int Hq, int d, int N, float* __restrict__ Dq,
+                                                           int64_t total) {
+  const int lane = threadIdx.x & 63;
+  const int64_t hv = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (hv >= total) return;
+  const int64_t tok = hv / Hq;
+  const int h = (int)(hv - tok * Hq);
+  float acc = 0.f;
+  for (int i = lane; i < d; i += 64)
+    acc += static_cast<float>(dO[tok * ld + (int64_t)h * d + i]) * static_cast<float>(O[tok * ld + (int64_t)h * d + i]);
+  acc = warp_sum(acc);
+  if (lane == 0) {
+    const int64_t b = tok / N, n = tok - b * N;
+    Dq[(b * Hq + h) * N + n] = acc;
+  }
+}
+
+// ---------------------------------------------------------------- attention backward
+// Both kernels use v_mfma_f32_32x32x16_bf16.  Operand fragments: lane l holds A[l%32][8(l/32) .. +8]
+// and B[8(l/32) .. +8][l%32] of one 16-deep k-step; the accumulator gives lane l the 16 values
+// C[(e/4)*8 + (l/32)*4 + e%4][l%32].  A product whose k index is the accumulator's row index
+// (P or dS as the B operand) takes the accumulator values e = 8t .. 8t+7 as k-step t, which
+// visits k in the order 16t + (i/4)*8 + (l/32)*4 + i%4; its A operand is read from LDS in that
+// same order.
+DEVI int perm_k(int t, int i, int lh) { return 16 * t + (i >> 2) * 8 + lh * 4 + (i & 3); }
+
+// Row pointer of key j (sequence b, kv head g) in the K or V source: the prefix cache for j < P,
+// the normed (K) or raw (V) image projections in qkv otherwise.
+DEVI const bf16* kv_row(const SeqInfo& si, int b, int g, int j, int Hkv, int d, const bf16* qkv, int64_t ldq,
+                        int col0, bool isv) {
+  const int P = si.plen[b];
+  if (j < P) return (const bf16*)(isv ? si.pv[b] : si.pk[b]) + ((int64_t)j * Hkv + g) * d;
+  return qkv + ((int64_t)b * si.N + (j - P)) * ldq + col0 + (int64_t)g * d;
+}
+
+// dK, dV of the image keys [P + 32 kb, +32) of (sequence b, kv head g).  S = Q K^T per 32
+// queries: A = Q rows (from LDS), B = K rows (registers).  dV^T += dO^T P and dK^T += Q^T dS with
+// the A operands read transposed from LDS.
+template <int D>
+__global__ __launch_bounds__(64) void attn_bwd_dkdv_kernel(const bf16* __restrict__ qkv, int64_t ldq, SeqInfo si,
+                                                           int Hq, int Hkv, const bf16* __restrict__ dO, int64_t ldo,
+                                                           const float* __restrict__ lse, const float* __restrict__ Dq,
+                                                           float scale_log2, float scale, float* __restrict__ dk,
+                                                           float* __restrict__ dv, int n_kb) {
+  constexpr int KS = D / 16, NDB = D / 32;
+  __shared__ __attribute__((aligned(16))) bf16 sq[32][D];
+  __shared__ __attribute__((aligned(16))) bf16 sdo[32][D];
+  const int lane = threadIdx.x, lr = lane & 31, lh = lane >> 5;
+  const int kb = blockIdx.x % n_kb;
+  const int g = (blockIdx.x / n_kb) % Hkv;
+  const int b = blockIdx.x / (n_kb * Hkv);
+  const int N = si.N, P = si.plen[b], G = Hq / Hkv;
+  const int QD = Hq * D;
+  const int key0 = 32 * kb;                          // image key index (token) of row 0
+  const int mykey = key0 + lr;
+  const bool keyok = mykey < N;
+  const int kc = keyok ? mykey : N - 1;
+  bf16x8 kf[KS], vf[KS];
+  {
+    const bf16* kp = qkv + ((int64_t)b * N + kc) * ldq + QD + (int64_t)g * D + lh * 8;
+    const bf16* vp = qkv + ((int64_t)b * N + kc) * ldq + QD + (int64_t)Hkv * D + (int64_t)g * D + lh * 8;
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      kf[ks] = *(const bf16x8*)(kp + ks * 16);
+      vf[ks] = *(const bf16x8*)(vp + ks * 16);
+    }
+  }
+  f32x16 dkT[NDB], dvT[NDB];
+#pragma unroll
+  for (int i = 0; i < NDB; ++i)
+#pragma unroll
+    for (int e = 0; e < 16; ++e) { dkT[i][e] = 0.f; dvT[i][e] = 0.f; }
+  const int nqb = (N + 31) / 32;
+  for (int hi = 0; hi < G; ++hi) {
+    const int h = g * G + hi;
+    const float* lse_h = lse + ((int64_t)b * Hq + h) * N;
+    const float* D_h = Dq + ((int64_t)b * Hq + h) * N;
+    for (int qb = 0; qb < nqb; ++qb) {
+      const int q0 = qb * 32;
+      __syncthreads();
+      // stage the 32 query rows of Q (normed, rotated) and dO of head h
+#pragma unroll
+      for (int c = 0; c < D / 16; ++c) {
+        const int idx = c * 64 + lane;                // 16-byte chunk index over 32 rows x D/8 chunks
+        const int row = idx / (D / 8), ch = idx % (D / 8);
+        const int q = min(q0 + row, N - 1);
+        const int64_t tok = (int64_t)b * N + q;
+        *(bf16x8*)&sq[row][ch * 8] = *(const bf16x8*)(qkv + tok * ldq + (int64_t)h * D + ch * 8);
+        *(bf16x8*)&sdo[row][ch * 8] = *(const bf16x8*)(dO + tok * ldo + (int64_t)h * D + ch * 8);
+      }
+      __syncthreads();
+      f32x16 s, dp;
+#pragma unroll
+      for (int e = 0; e < 16; ++e) { s[e] = 0.f; dp[e] = 0.f; }
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) {
+        const bf16x8 qa = *(const bf16x8*)&sq[lr][ks * 16 + lh * 8];
+        const bf16x8 da = *(const bf16x8*)&sdo[lr][ks * 16 + lh * 8];
+        s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa, kf[ks], s, 0, 0, 0);
+        dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(da, vf[ks], dp, 0, 0, 0);
+      }
+      // P and dS (rows = queries q0 + (e/4)*8 + lh*4 + e%4, column = this lane's key)
+      bf16x8 pf[2], dsf[2];
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        const int q = q0 + (e >> 2) * 8 + lh * 4 + (e & 3);
+        const bool ok = keyok && q < N;
+        const int qc = min(q, N - 1);
+        const float p = ok ? __builtin_amdgcn_exp2f(s[e] * scale_log2 - lse_h[qc]) : 0.f;
+        const float ds = p * (dp[e] - D_h[qc]);
+        pf[e >> 3][e & 7] = static_cast<bf16>(p);
+        dsf[e >> 3][e & 7] = static_cast<bf16>(ds);
+      }
+#pragma unroll
+      for (int t = 0; t < 2; ++t)
+#pragma unroll
+        for (int db = 0; db < NDB; ++db) {
+          bf16x8 at, aq;
+#pragma unroll
+          for (int i = 0; i < 8; ++i) {
+            const int r = perm_k(t, i, lh);
+            at[i] = sdo[r][db * 32 + lr];
+            aq[i] = sq[r][db * 32 + lr];
+          }
+          dvT[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(at, pf[t], dvT[db], 0, 0, 0);
+          dkT[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(aq, dsf[t], dkT[db], 0, 0, 0);
+        }
+    }
+  }
+  if (keyok) {
+    const int64_t tok = (int64_t)b * N + mykey;
+#pragma unroll
+    for (int db = 0; db < NDB; ++db)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        const int dd = db * 32 + (e >> 2) * 8 + lh * 4 + (e & 3);
+        dk[tok * Hkv * D + (int64_t)g * D + dd] = dkT[db][e] * scale;
+        dv[tok * Hkv * D + (int64_t)g * D + dd] = dvT[db][e];
+      }
+  }
+  (void)P;
+}
+
+// dQ of queries [32 qb, +32) of (sequence b, head h) over every key.  S^T = K Q^T: A = K rows,
+// B = Q rows (registers); dP^T = V dO^T likewise; dQ^T += K^T dS^T with K^T read from LDS.
+template <int D>
+__global__ __launch_bounds__(64) void attn_bwd_dq_kernel(const bf16* __restrict__ qkv, int64_t ldq, SeqInfo si, int Hq,
+                                                         int Hkv, const bf16* __restrict__ dO, int64_t ldo,
+                                                         const float* __restrict__ lse, const float* __restrict__ Dq,
+                                                         float scale_log2, float scale, float* __restrict__ dq,
+                                                         int n_qb) {
+  constexpr int KS = D / 16, NDB = D / 32;
+  __shared__ __attribute__((aligned(16))) bf16 sk[32][D];
+  const int lane = threadIdx.x, lr = lane & 31, lh = lane >> 5;
+  const int qb = blockIdx.x % n_qb;
+  const int h = (blockIdx.x / n_qb) % Hq;
+  const int b = blockIdx.x / (n_qb * Hq);
+  const int N = si.N, P = si.plen[b], L = P + N;
+  const int g = h / (Hq / Hkv);
+  const int QD = Hq * D;
+  const int myq = 32 * qb + lr;
+  const bool qok = myq < N;
+  const int64_t tok = (int64_t)b * N + min(myq, N - 1);
+  bf16x8 qf[KS], df[KS];
+#pragma unroll
+  for (int ks = 0; ks < KS; ++ks) {
+    qf[ks] = *(const bf16x8*)(qkv + tok * ldq + (int64_t)h * D + ks * 16 + lh * 8);
+    df[ks] = *(const bf16x8*)(dO + tok * ldo + (int64_t)h * D + ks * 16 + lh * 8);
+  }
+  const float my_lse = lse[((int64_t)b * Hq + h) * N + min(myq, N - 1)];
+  const float my_D = Dq[((int64_t)b * Hq + h) * N + min(myq, N - 1)];
+  f32x16 dqT[NDB];
+#pragma unroll
+  for (int i = 0; i < NDB; ++i)
+#pragma unroll
+    for (int e = 0; e < 16; ++e) dqT[i][e] = 0.f;
+  for (int j0 = 0; j0 < L; j0 += 32) {
+    const int jc = min(j0 + lr, L - 1);
+    const bf16* kp = kv_row(si, b, g, jc, Hkv, D, qkv, ldq, QD, false) + lh * 8;
+    const bf16* vp = kv_row(si, b, g, jc, Hkv, D, qkv, ldq, QD + Hkv * D, true) + lh * 8;
+    bf16x8 kf[KS];
+    f32x16 s, dp;
+#pragma unroll
+    for (int e = 0; e < 16; ++e) { s[e] = 0.f; dp[e] = 0.f; }
+    __syncthreads();
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      kf[ks] = *(const bf16x8*)(kp + ks * 16);
+      const bf16x8 vv = *(const bf16x8*)(vp + ks * 16);
+      *(bf16x8*)&sk[lr][ks * 16 + lh * 8] = kf[ks];
+      s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[ks], qf[ks], s, 0, 0, 0);
+      dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vv, df[ks], dp, 0, 0, 0);
+    }
+    __syncthreads();
+    bf16x8 dsf[2];
+#pragma unroll
+    for (int e = 0; e < 16; ++e) {
+      const int j = j0 + (e >> 2) * 8 + lh * 4 + (e & 3);
+      const float p = (qok && j < L) ? __builtin_amdgcn_exp2f(s[e] * scale_log2 - my_lse) : 0.f;
+      dsf[e >> 3][e & 7] = static_cast<bf16>(p * (dp[e] - my_D));
+    }
+#pragma unroll
+    for (int t = 0; t < 2; ++t)
+#pragma unroll
+      for (int db = 0; db < NDB; ++db) {
+        bf16x8 ak;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) ak[i] = sk[perm_k(t, i, lh)][db * 32 + lr];
+        dqT[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ak, dsf[t], dqT[db], 0, 0, 0);
+      }
+  }
+  if (qok) {
+#pragma unroll
+    for (int db = 0; db < NDB; ++db)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        const int dd = db * 32 + (e >> 2) * 8 + lh * 4 + (e & 3);
+        dq[tok * QD + (int64_t)h * D + dd] = dqT[db][e] * scale;
+      }
+  }
+}
+
+// ---------------------------------------------------------------- LoRA weight gradients
+// Partial[z][n1][n2] = sum over m in split z of X[m, n1] Y[m, n2].  Workgroup tile 64 x 64 of
+// (n1, n2), four waves of 32 x 32; chunks of 64 m are staged in LDS transposed ([n][m], rows
+// padded to 72 so the 16-byte fragment reads stay aligned and spread over banks).
+__global__ __launch_bounds__(256) void wgrad_kernel(const bf16* __restrict__ X, int64_t ldx, const bf16* __restrict__ Y,
+                                                    int64_t ldy, int M, int N1, int N2, int m_per_split,
+                                                    float* __restrict__ part) {
+  __shared__ __attribute__((aligned(16))) bf16 sx[64][72];
+  __shared__ __attribute__((aligned(16))) bf16 sy[64][72];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int lr = lane & 31, lh = lane >> 5;
+  const int n1b = blockIdx.x * 64, n2b = blockIdx.y * 64, z = blockIdx.z;
+  const int m_lo = z * m_per_split, m_hi = min(M, m_lo + m_per_split);
+  const int w1 = (wave >> 1) * 32, w2 = (wave & 1) * 32;
+  f32x16 acc;
+#pragma unroll
+  for (int e = 0; e < 16; ++e) acc[e] = 0.f;
+  for (int m0 = m_lo; m0 < m_hi; m0 += 64) {
+    __syncthreads();
+    // 64 m x 8 chunks of 8 columns, two per thread, for each of X and Y
+#pragma unroll
+    for (int it = 0; it < 2; ++it) {
+      const int idx = it * 256 + tid;
+      const int mm = idx >> 3, ch = idx & 7;
+      const int m = m0 + mm;
+      const int c1 = n1b + ch * 8, c2 = n2b + ch * 8;
+      bf16x8 vx, vy;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) { vx[e] = static_cast<bf16>(0.f); vy[e] = static_cast<bf16>(0.f); }
+      if (m < m_hi && c1 < N1) vx = *(const bf16x8*)(X + (int64_t)m * ldx + c1);
+      if (m < m_hi && c2 < N2) vy = *(const bf16x8*)(Y + (int64_t)m * ldy + c2);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        sx[ch * 8 + e][mm] = vx[e];
+        sy[ch * 8 + e][mm] = vy[e];
+      }
+    }
+    __syncthreads();
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) {
+      const bf16x8 a = *(const bf16x8*)&sx[w1 + lr][ks * 16 + lh * 8];
+      const bf16x8 bb = *(const bf16x8*)&sy[w2 + lr][ks * 16 + lh * 8];
+      acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, bb, acc, 0, 0, 0);
+    }
+  }
+  float* out = part + (int64_t)z * N1 * N2;
+#pragma unroll
+  for (int e = 0; e < 16; ++e) {
+    const int r = n1b + w1 + (e >> 2) * 8 + lh * 4 + (e & 3);
+    const int c = n2b + w2 + lr;
+    if (r < N1 && c < N2) out[(int64_t)r * N2 + c] = acc[e];
+  }
+}
+
+// C[i] += sum_z part[z][i]
+__global__ __launch_bounds__(256) void wgrad_reduce_kernel(const float* __restrict__ part, int splits, int64_t n,
+                                                           float* __restrict__ C) {
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (i >= n) return;
+  float s = 0.f;
+  for (int z = 0; z < splits; ++z) s += part[(int64_t)z * n + i];
+  C[i] += s;
+}
+
+// ---------------------------------------------------------------- x0 loss
+// part[block] = sum of (pred - tgt)^2 over the block's elements; grad = 2 (pred - tgt) / n
+__global__ __launch_bounds__(256) void x0_loss_kernel(const float* __restrict__ pred, const float* __restrict__ tgt,
+                                                      float* __restrict__ grad, float* __restrict__ part, int64_t n) {
+  __shared__ float red[4];
+  float acc = 0.f;
+  const float two_n = 2.0f / (float)n;
+  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (int64_t)gridDim.x * 256) {
+    const float dlt = pred[i] - tgt[i];
+    acc += dlt * dlt;
+    grad[i] = two_n * dlt;
+  }
+  acc = block_sum256(acc, red);
+  if (threadIdx.x == 0) part[blockIdx.x] = acc;
+}
+
+__global__ __launch_bounds__(256) void loss_reduce_kernel(const float* __restrict__ part, int nb, int64_t n,
+                                                          float* __restrict__ loss) {
+  __shared__ float red[4];
+  float acc = 0.f;
+  for (int i = threadIdx.x; i < nb; i += 256) acc += part[i];
+  acc = block_sum256(acc, red);
+  if (threadIdx.x == 0) *loss = acc / (float)n;
+}
+
+}  // namespace
+
+// ==================================================================== launchers
+hipError_t transpose_bf16(const bf16* in, int64_t ldi, bf16* out, int64_t ldo, int R, int C, hipStream_t s) {
+  if (R <= 0 || C <= 0) return hipSuccess;
+  hipLaunchKernelGGL(transpose_kernel, dim3((C + 63) / 64, (R + 63) / 64), dim3(256), 0, s, in, ldi, out, ldo, R, C);
+  return hipGetLastError();
+}
+
+hipError_t cast_f32_bf16(const float* x, bf16* y, int64_t n, hipStream_t s) {
+  if (n <= 0) return hipSuccess;
+  hipLaunchKernelGGL(cast_kernel, dim3((unsigned)((n + 1023) / 1024)), dim3(256), 0, s, x, y, n);
+  return hipGetLastError();
+}
+
+hipError_t rmsnorm_bwd(const float* x, const bf16* g, const bf16* dy, const float* base, float* out, int rows, int D,
+                       float eps, hipStream_t s) {
+  if (rows <= 0) return hipSuccess;
+  hipLaunchKernelGGL(rmsnorm_bwd_kernel, dim3(rows), dim3(256), 0, s, x, g, dy, base, out, D, eps);
+  return hipGetLastError();
+}
+
+hipError_t swiglu_fwd(const bf16* gu, bf16* z, int M, int I, hipStream_t s) {
+  const int64_t n = (int64_t)M * I;
+  if (n <= 0) return hipSuccess;
+  hipLaunchKernelGGL(swiglu_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, gu, z, I, n);
+  return hipGetLastError();
+}
+
+hipError_t swiglu_bwd(const bf16* gu, const bf16* dz, bf16* dgu, int M, int I, hipStream_t s) {
+  const int64_t n = (int64_t)M * I;
+  if (n <= 0) return hipSuccess;
+  hipLaunchKernelGGL(swiglu_bwd_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, gu, dz, dgu, I, n);
+  return hipGetLastError();
+}
+
+hipError_t qknorm_rope_bwd(const bf16* raw, int64_t ldr, const float* dq, const float* dk, const float* dv,
+                           const SeqInfo& si, int Hq, int Hkv, int d, const bf16* gq, const bf16* gk,
+                           const float2* table, float eps, bf16* dqkv, int64_t ldo, hipStream_t s) {
+  const int64_t total = (int64_t)si.B * si.N * (Hq + 2 * Hkv);
+  if (total == 0) return hipSuccess;
+  if (d > 128 || d % 2) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(qknorm_rope_bwd_kernel, dim3((unsigned)((total + 3) / 4)), dim3(256), 0, s, raw, ldr, dq, dk, dv,
+                     si, Hq, Hkv, d, gq, gk, table, eps, dqkv, ldo, total);
+  return hipGetLastError();
+}
+
+hipError_t attention_bwd(const bf16* qkv, int64_t ldq, const SeqInfo& si, int Hq, int Hkv, int d, const bf16* O,
+                         const bf16* dO, const float* lse, float* Dq, float* dq, float* dk, float* dv, hipStream_t s) {
+  const int N = si.N, B = si.B;
+  if (N == 0) return hipSuccess;
+  if (d != 128) return hipErrorInvalidValue;
+  const int64_t QD = (int64_t)Hq * d;
+  const int64_t tot = (int64_t)B * N * Hq;
+  hipLaunchKernelGGL(attn_bwd_dot_kernel, dim3((unsigned)((tot + 3) / 4)), dim3(256), 0, s, dO, O, QD, Hq, d, N, Dq, tot);
+  const float scale = 1.0f / sqrtf((float)d);
+  const float scale_log2 = 1.4426950408889634f * scale;
+  const int nb = (N + 31) / 32;
+  hipLaunchKernelGGL(attn_bwd_dkdv_kernel<128>, dim3(B * Hkv * nb), dim3(64), 0, s, qkv, ldq, si, Hq, Hkv, dO, QD, lse,
+                     (const float*)Dq, scale_log2, scale, dk, dv, nb);
+  hipLaunchKernelGGL(attn_bwd_dq_kernel<128>, dim3(B * Hq * nb), dim3(64), 0, s, qkv, ldq, si, Hq, Hkv, dO, QD, lse,
+                     (const float*)Dq, scale_log2, scale, dq, nb);
+  return hipGetLastError();
+}
+
+int wgrad_splits(int M, int N1, int N2) {
+  const int tiles = ((N1 + 63) / 64) * ((N2 + 63) / 64);
+  int splits = std::max(1, 1024 / std::max(tiles, 1));
+  splits = std::min(splits, std::max(1, (M + 255) / 256));
+  return splits;
+}
+
+hipError_t wgrad(const bf16* X, int64_t ldx, const bf16* Y, int64_t ldy, int M, int N1, int N2, float* C, float* part,
+                 hipStream_t s) {
+  if (M <= 0 || N1 <= 0 || N2 <= 0) return hipSuccess;
+  if (N1 % 8 || N2 % 8 || ldx % 8 || ldy % 8) return hipErrorInvalidValue;
+  const int splits = wgrad_splits(M, N1, N2);
+  const int per = ((M + splits - 1) / splits + 63) / 64 * 64;
+  const int nz = (M + per - 1) / per;
+  hipLaunchKernelGGL(wgrad_kernel, dim3((N1 + 63) / 64, (N2 + 63) / 64, nz), dim3(256), 0, s, X, ldx, Y, ldy, M, N1, N2,
+                     per, part);
+  const int64_t n = (int64_t)N1 * N2;
+  hipLaunchKernelGGL(wgrad_reduce_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, (const float*)part, nz, n, C);
+  return hipGetLastError();
+}
+
+hipError_t x0_loss(const float* pred, const float* tgt, float* grad, float* part, int nparts, float* loss, int64_t n,
+                   hipStream_t s) {
+  if (n <= 0) return hipSuccess;
+  hipLaunchKernelGGL(x0_loss_kernel, dim3(nparts), dim3(256), 0, s, pred, tgt, grad, part, n);
+  hipLaunchKernelGGL(loss_reduce_kernel, dim3(1), dim3(256), 0, s, (const float*)part, nparts, n, loss);
+  return hipGetLastError();
+}
+
+}  // namespace psf

@@ -46,7 +46,7 @@ hipError_t pack_kv_knorm(const bf16* qkv, int64_t ld, const SeqInfo& si, int Hq,
 // RMSNorm (gain gq) and RoPE at position P_b + n are applied to each query as it is loaded.
 hipError_t attention_bf16(const bf16* qkv, int64_t ldq, const SeqInfo& si, int Hq, int Hkv, int d, int Lpad,
                           const bf16* Kc, const bf16* Vt, bf16* O, int64_t ldo, const bf16* gq,
-                          const float2* table, float eps, bool causal, hipStream_t s);
+                          const float2* table, float eps, bool causal, hipStream_t s, float* lse = nullptr);
 hipError_t attention_f32(const float* qkv, int64_t ldq, const SeqInfo& si, int Hq, int Hkv, int d, int Lpad,
                          const float* Kc, const float* Vt, float* O, int64_t ldo, bool causal, hipStream_t s);
 
@@ -71,6 +71,29 @@ hipError_t timestep_embed(const float* sigma_dev, const T* w1, const T* w2, floa
 // xm + scale (xc - xm).  xo may equal x.
 hipError_t cfg_euler(float* xo, const float* x, const float* xc, const float* xm, const float* xu, size_t n,
                      float scale, float img_scale, float sigma, float sigma_next, float t_eps, hipStream_t s);
+
+// ---- training backward (backward.hip)
+hipError_t transpose_bf16(const bf16* in, int64_t ldi, bf16* out, int64_t ldo, int R, int C, hipStream_t s);
+hipError_t cast_f32_bf16(const float* x, bf16* y, int64_t n, hipStream_t s);
+// out = base + (dRMSNorm(x; g))^T dy per row of D (base may alias out or be null)
+hipError_t rmsnorm_bwd(const float* x, const bf16* g, const bf16* dy, const float* base, float* out, int rows, int D,
+                       float eps, hipStream_t s);
+hipError_t swiglu_fwd(const bf16* gu, bf16* z, int M, int I, hipStream_t s);
+hipError_t swiglu_bwd(const bf16* gu, const bf16* dz, bf16* dgu, int M, int I, hipStream_t s);
+// dqkv = gradient with respect to the raw q, k heads (through RoPE and the per-head norm) and v
+hipError_t qknorm_rope_bwd(const bf16* raw, int64_t ldr, const float* dq, const float* dk, const float* dv,
+                           const SeqInfo& si, int Hq, int Hkv, int d, const bf16* gq, const bf16* gk,
+                           const float2* table, float eps, bf16* dqkv, int64_t ldo, hipStream_t s);
+// qkv: normed, rotated q/k and v of the image tokens; O, dO [M, Hq d]; lse [B, Hq, N] (log2 units);
+// Dq scratch [B, Hq, N]; dq [M, Hq d], dk, dv [M, Hkv d] fp32 (image keys only)
+hipError_t attention_bwd(const bf16* qkv, int64_t ldq, const SeqInfo& si, int Hq, int Hkv, int d, const bf16* O,
+                         const bf16* dO, const float* lse, float* Dq, float* dq, float* dk, float* dv, hipStream_t s);
+// C[n1, n2] += sum_m X[m, n1] Y[m, n2]; part: scratch of wgrad_part_floats(M, N1, N2) floats
+int wgrad_splits(int M, int N1, int N2);
+hipError_t wgrad(const bf16* X, int64_t ldx, const bf16* Y, int64_t ldy, int M, int N1, int N2, float* C, float* part,
+                 hipStream_t s);
+hipError_t x0_loss(const float* pred, const float* tgt, float* grad, float* part, int nparts, float* loss, int64_t n,
+                   hipStream_t s);
 
 // Router: idx/w [T, k]; u [T, D], wr [E, D]
 template <typename T>

@@ -178,3 +178,36 @@ def test_prefix_forward_rejects_bad_arguments_on_host(psf):
     assert call(kc=hole) == psf.GEN_EINVAL                        # every (layer, sequence) slot needed
     assert call(vc=None) == psf.GEN_EINVAL
     assert call(ws=64) == psf.GEN_EWORKSPACE
+
+
+def test_training_entry_points_reject_bad_arguments_on_host(psf):
+    d = dims(psf)                     # 8B-shaped dense bf16 block, head_dim 128
+    d.lora_rank, d.lora_alpha = 32, 32.0
+    w = fake_weights(psf)
+    for s in range(7):
+        w.lora_a[s] = 4096
+        w.lora_b[s] = 4096
+    g = psf.LoraGradsC()
+    arr = (ctypes.c_void_p * 2)(4096, 4096)
+    pl = (ctypes.c_int * 2)(4, 4)
+    f = psf.lib.gen_block_backward
+
+    def call(dd=d, ww=w, gg=g, h=4096, dh=4096, B=2, N=64, ws=1 << 34):
+        return f(ctypes.byref(dd), ctypes.byref(ww), h, dh, B, N, arr, arr, pl,
+                 ctypes.byref(gg) if gg is not None else None, 4096, ws, None)
+    assert call() == psf.GEN_EINVAL and "gradient" in psf.last_error()      # LoRA sites without buffers
+    for s in range(7):
+        g.lora_a[s] = 4096
+        g.lora_b[s] = 4096
+    assert call(h=None) == psf.GEN_EINVAL
+    assert call(dh=4100) == psf.GEN_EINVAL                                    # unaligned
+    assert call(B=64) == psf.GEN_EUNSUPPORTED
+    assert call(ws=64) == psf.GEN_EWORKSPACE
+    d64 = dims(psf)
+    d64.head_dim = 64
+    assert call(dd=d64, gg=None) == psf.GEN_EUNSUPPORTED                     # attention backward needs d = 128
+    dm = dims(psf)
+    dm.mlp_intermediate, dm.n_experts, dm.top_k, dm.expert_intermediate = 0, 8, 2, 256
+    assert call(dd=dm, gg=None) == psf.GEN_EUNSUPPORTED                      # dense blocks only
+    assert psf.lib.gen_backward_workspace_size(ctypes.byref(d), 2, 64, 0) > 0
+    assert psf.lib.gen_train_workspace_size(ctypes.byref(d), 0, 1, 64, 0) == 0
