@@ -231,6 +231,101 @@ def run_prefix_bench(psf, w, args):
     print(json.dumps(out), flush=True)
 
 
+def train_flops(w) -> dict:
+    """Algorithmic FLOPs of one LoRA training step (x0 loss, one branch per sample): the forward
+    tower, the backward's data gradients (one product per forward GEMM; four attention products:
+    dV, dP, dQ, dK) and the LoRA weight gradients.  The forward that the backward recomputes per
+    block is not counted."""
+    d = w.dims
+    M, N, D, I, r = w.batch * w.n_tokens, w.n_tokens, d.hidden, d.mlp_intermediate, d.lora_rank
+    QD, KV = d.n_q_heads * d.head_dim, d.n_kv_heads * d.head_dim
+    gemm = 2 * M * D * (QD + 2 * KV) + 2 * M * QD * D + 2 * M * D * 2 * I + 2 * M * I * D
+    attn = sum(4 * d.n_q_heads * N * (w.prefix_len_of(b) + N) * d.head_dim for b in range(w.batch))
+    ins = (D, D, D, QD, D, D, I)
+    outs = (QD, KV, KV, D, I, I, D)
+    lora = sum(2 * M * r * (i + o) for i, o in zip(ins, outs))
+    per_layer_fwd = gemm + attn + lora
+    per_layer_bwd = gemm + 2 * attn + 2 * lora
+    head = 2 * M * D * 3072
+    f = {"forward": per_layer_fwd * w.n_layers + 2 * w.n_img * N * 3072 * D + head,
+         "backward": per_layer_bwd * w.n_layers + head}
+    f["total"] = f["forward"] + f["backward"]
+    return f
+
+
+def run_train_bench(psf, w, args):
+    """One LoRA training step of the 36-layer tower (x0 loss, 4 samples x 1024^2, rank 32 on all
+    seven sites): forward, loss, backward to every layer's LoRA gradients.  Gradients are cleared
+    at the start of each step; no optimizer update."""
+    import torch
+    import workloads as W
+    d = w.dims
+    dims = psf.make_dims(d, psf.GEN_BF16)
+    base = W.scaled(w, dims=W.BlockDims(**{**W.dataclasses.asdict(d), "lora_rank": 0, "lora_alpha": 0.0}))
+    layers_dev, glob, pk, pv, x0 = make_device_tower(psf, base, seed=4)
+    g = torch.Generator(device="cuda")
+    g.manual_seed(5)
+
+    def randn(*shape, std):
+        t = torch.empty(*shape, device="cuda", dtype=torch.float32)
+        t.normal_(0.0, std, generator=g)
+        return t.to(torch.bfloat16)
+    D, I, r = d.hidden, d.mlp_intermediate, d.lora_rank
+    qd, kd = d.n_q_heads * d.head_dim, d.n_kv_heads * d.head_dim
+    ins = {"q": D, "k": D, "v": D, "o": qd, "gate": D, "up": D, "down": I}
+    outs = {"q": qd, "k": kd, "v": kd, "o": D, "gate": I, "up": I, "down": D}
+    grads, gstructs = [], []
+    for lwd in layers_dev:
+        for s_ in ("q", "k", "v", "o", "gate", "up", "down"):
+            lwd[f"lora_a_{s_}"] = randn(r, ins[s_], std=0.02)
+            lwd[f"lora_b_{s_}"] = randn(outs[s_], r, std=0.02)
+        gb = {k: torch.zeros(v.shape, device="cuda") for k, v in lwd.items() if k.startswith("lora_")}
+        grads.append(gb)
+        gstructs.append(psf.make_lora_grads(gb))
+    layers = [psf.make_weights(l) for l in layers_dev]
+    noise = torch.randn(x0.shape, device="cuda", generator=g)
+    t = torch.rand(w.n_img, generator=torch.Generator().manual_seed(6))
+    x_t = (1 - t.view(-1, 1, 1, 1).cuda()) * x0 + t.view(-1, 1, 1, 1).cuda() * noise
+    sig = [float(v) for v in t]
+    plen = [w.prefix_len] * w.batch
+    loss = torch.zeros(1, device="cuda")
+    ws = psf.alloc_workspace(psf.train_workspace_size(dims, w.n_layers, w.n_img, w.n_tokens, w.prefix_len))
+
+    def step():
+        for gb in grads:
+            for v in gb.values():
+                v.zero_()
+        psf.tower_lora_train_step(dims, layers, glob, x_t, x0, sig, pk, pv, plen, gstructs, loss, ws)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    start.record()
+    for _ in range(args.steps):
+        step()
+    stop.record()
+    torch.cuda.synchronize()
+    ms = start.elapsed_time(stop) / args.steps
+    fl = train_flops(w)
+    tokens = w.batch * w.n_tokens
+    tflops = fl["total"] / (ms * 1e-3) / 1e12
+    out = {
+        "metric": "LoRA training step of the 36-layer gen tower (x0 loss, forward + backward to the LoRA "
+                  "gradients): image tokens/s; % bf16 MFMA peak",
+        "value": round(tokens / (ms * 1e-3), 1), "unit": "image tokens/s",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 3),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": w.name, "layers": w.n_layers, "samples": w.n_img, "image_px": [w.height, w.width],
+                   "image_tokens_per_sample": w.n_tokens, "prefix_tokens": w.prefix_len,
+                   "lora": {"rank": r, "alpha": d.lora_alpha, "sites": "q,k,v,o,gate,up,down"},
+                   "loss": float(loss.item())},
+        "pct_bf16_peak": round(100 * tflops / PEAK_BF16_TFLOPS, 2), "tflops": round(tflops, 1),
+        "step_tflop": round(fl["total"] / 1e12, 3),
+    }
+    print(json.dumps(out), flush=True)
+
+
 def blas_threads() -> int:
     """Threads numpy's BLAS runs the oracle's products on."""
     try:
@@ -304,11 +399,12 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--config", type=int, default=2)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--variant", choices=("cfg", "lora-merged-cfg1", "prefix", "dual-cfg"), default="cfg",
+    ap.add_argument("--variant", choices=("cfg", "lora-merged-cfg1", "prefix", "dual-cfg", "lora-train"), default="cfg",
                     help="cfg: the 2048^2 two-branch CFG step (default); lora-merged-cfg1: one branch at "
                          "1024^2 with cfg 1 and a rank-32 LoRA folded into the weights at load; prefix: the "
                          "prompt pass that writes the prefix-KV cache (2 prompts x 400 tokens, 36 layers); "
-                         "dual-cfg: the 2048^2 image-edit step with three branches (cfg 4, image cfg 2)")
+                         "dual-cfg: the 2048^2 image-edit step with three branches (cfg 4, image cfg 2); "
+                         "lora-train: one LoRA training step (4 x 1024^2, rank 32, x0 loss)")
     ap.add_argument("--kernel", choices=("gate_up", "attention", "copy"),
                     help="run only this kernel at the workload's shapes, --steps times (for counter runs)")
     args = ap.parse_args()
@@ -333,6 +429,9 @@ def main():
     torch.cuda.set_device(0)
     if args.variant == "prefix":
         run_prefix_bench(psf, w, args)
+        return
+    if args.variant == "lora-train":
+        run_train_bench(psf, W.scaled(W.CONFIGS[3], prefix_cache_samples=0), args)
         return
     if args.kernel:
         run_kernel_only(psf, w, args.kernel, args.steps)

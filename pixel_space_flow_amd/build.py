@@ -13,7 +13,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 OUT = os.path.join(HERE, "libpsf_gen.so")
 BUILD_DIR = os.path.join(HERE, "_build")
-SOURCES = ["gemm.hip", "attention.hip", "elementwise.hip", "moe.hip", "backward.hip", "api.cpp"]
+SOURCES = ["gemm.hip", "attention.hip", "elementwise.hip", "moe.hip", "backward.hip", "skinny.hip", "api.cpp"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 FLAGS = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}",

@@ -145,7 +145,7 @@ constexpr size_t ALIGN = 256;
 size_t up(size_t x) { return (x + ALIGN - 1) / ALIGN * ALIGN; }
 
 struct Ws {
-  size_t hidden, patches, u, qkv, attn, kc, vt, z, rope, temb, h1, x0, lora_t, hmid;
+  size_t hidden, patches, u, qkv, attn, kc, vt, z, rope, temb, h1, x0, lora_t, hmid, skinny;
   size_t m_idx, m_w, m_counts, m_offsets, m_perm, m_pos, m_tiles, m_z, m_y;
   size_t total;
   int Lpad, max_tiles, n_pos;
@@ -174,6 +174,7 @@ Ws layout(const gen_block_dims& d, int n_img, int n_br, int N, int max_prefix) {
   w.h1 = take((size_t)n_img * D * 4);
   w.x0 = take(B * 3 * (size_t)N * 1024 * 4);
   w.lora_t = take(d.lora_rank > 0 ? M * 3 * d.lora_rank * es : 0);
+  w.skinny = take(d.lora_rank > 0 ? skinny_part_floats((int)M, std::min(3 * d.lora_rank, 128)) * 4 : 0);
   if (d.n_experts > 0) {
     const size_t A = M * d.top_k;
     w.max_tiles = (int)(A / 256 + d.n_experts + 1);
@@ -211,7 +212,7 @@ hipError_t gemm_any(const GemmParams& p, int epi, hipStream_t s) {
 // Returns the number of sites present; fills per-site column offsets (-1 if absent).
 template <typename T>
 hipError_t lora_down(const gen_block_dims& d, const gen_block_weights& w, const int* sites, int ns, const T* x, int K,
-                     int M, T* t, int* off, int& ldt, hipStream_t s) {
+                     int M, T* t, int* off, int& ldt, hipStream_t s, float* part = nullptr) {
   GemmParams p = gp();
   int n = 0;
   for (int i = 0; i < ns; ++i) {
@@ -224,6 +225,7 @@ hipError_t lora_down(const gen_block_dims& d, const gen_block_weights& w, const 
   p.M = M; p.N = n * d.lora_rank; p.K = K;
   p.bmode = 2; p.seg_rows = d.lora_rank;
   p.C = t; p.ldc = ldt; p.scale = d.lora_alpha / (float)d.lora_rank;
+  if (part && p.N <= 128 && K % 64 == 0) return gemm_skinny(p, part, s);
   return gemm_bf16(p, EPI_SCALED, s);
 }
 
@@ -271,7 +273,7 @@ int run_block(const gen_block_dims& d, const gen_block_weights& w, TH* hidden, c
     if (lora) {
       const int sites[3] = {0, 1, 2}, ends[3] = {QD, QD + Hkv * hd, QKV};
       int off[3], ldt;
-      HIP_TRY(lora_down<T>(d, w, sites, 3, u, D, M, lt, off, ldt, s));
+      HIP_TRY(lora_down<T>(d, w, sites, 3, u, D, M, lt, off, ldt, s, at<float>(ws, L.skinny)));
       if (off[0] >= 0 || off[1] >= 0 || off[2] >= 0) lora_ext(p, d, w, sites, 3, ends, lt, ldt, off);
     }
     HIP_TRY(timed(FAM_QKV, s, [&] { return gemm_any<T>(p, EPI_STORE, s); }));
@@ -315,7 +317,7 @@ int run_block(const gen_block_dims& d, const gen_block_weights& w, TH* hidden, c
     if (lora) {
       const int sites[1] = {3}, ends[1] = {D};
       int off[1], ldt;
-      HIP_TRY(lora_down<T>(d, w, sites, 1, attn, QD, M, lt, off, ldt, s));
+      HIP_TRY(lora_down<T>(d, w, sites, 1, attn, QD, M, lt, off, ldt, s, at<float>(ws, L.skinny)));
       if (off[0] >= 0) lora_ext(p, d, w, sites, 1, ends, lt, ldt, off);
     }
     HIP_TRY(timed(FAM_O, s, [&] { return gemm_any<T>(p, f32res ? EPI_RESID_F32 : EPI_RESID_TO_F32, s); }));
@@ -331,7 +333,7 @@ int run_block(const gen_block_dims& d, const gen_block_weights& w, TH* hidden, c
       if (lora) {
         const int sites[2] = {4, 5}, ends[2] = {I, 2 * I};
         int off[2], ldt;
-        HIP_TRY(lora_down<T>(d, w, sites, 2, u, D, M, lt, off, ldt, s));
+        HIP_TRY(lora_down<T>(d, w, sites, 2, u, D, M, lt, off, ldt, s, at<float>(ws, L.skinny)));
         if (off[0] >= 0 || off[1] >= 0) lora_ext(p, d, w, sites, 2, ends, lt, ldt, off);
       }
       HIP_TRY(timed(FAM_GATE_UP, s, [&] { return gemm_any<T>(p, EPI_SWIGLU, s); }));
@@ -343,7 +345,7 @@ int run_block(const gen_block_dims& d, const gen_block_weights& w, TH* hidden, c
       if (lora) {
         const int sites[1] = {6}, ends[1] = {D};
         int off[1], ldt;
-        HIP_TRY(lora_down<T>(d, w, sites, 1, z, I, M, lt, off, ldt, s));
+        HIP_TRY(lora_down<T>(d, w, sites, 1, z, I, M, lt, off, ldt, s, at<float>(ws, L.skinny)));
         if (off[0] >= 0) lora_ext(p, d, w, sites, 1, ends, lt, ldt, off);
       }
       HIP_TRY(timed(FAM_DOWN, s, [&] { return gemm_any<T>(p, f32res ? EPI_RESID_F32 : EPI_RESID_FROM_F32, s); }));
@@ -449,7 +451,8 @@ Wb layout_bwd(const gen_block_dims& d, int B, int N, int max_prefix) {
   w.wt = take(std::max(std::max(QKV * D, QD * D), std::max(2 * I * D, I * D)) * 2);
   w.xb = take(std::max(std::max(D, I), QD) * 3 * r * 2);
   w.bt = take(r * std::max(std::max(QD, D), I) * 2);
-  w.part = take(std::max((size_t)4 << 20, r * std::max(std::max(QD, D), I)) * 4);
+  w.part = take(std::max(std::max((size_t)4 << 20, r * std::max(std::max(QD, D), I)),
+                         r ? skinny_part_floats((int)M, (int)std::min<size_t>(3 * r, 128)) : 0) * 4);
   w.total = o;
   return w;
 }
@@ -466,7 +469,8 @@ struct BackSite {
 // and p gets that K extension, so the base dgrad GEMM also adds sum_site tp_site A_site.
 // Returns the number of sites present (slot order = list order).
 int lora_back(const gen_block_dims& d, const gen_block_weights& w, const BackSite* sites, int ns, const bf16* dY,
-              int lddy, int in, int M, bf16* tp, bf16* xb, bf16* bt, GemmParams& p, int* slot, hipStream_t s) {
+              int lddy, int in, int M, bf16* tp, bf16* xb, bf16* bt, GemmParams& p, int* slot, float* part,
+              hipStream_t s) {
   const int r = d.lora_rank;
   int n = 0;
   for (int i = 0; i < ns; ++i) slot[i] = (r > 0 && w.lora_a[sites[i].site]) ? n++ : -1;
@@ -478,7 +482,8 @@ int lora_back(const gen_block_dims& d, const gen_block_weights& w, const BackSit
     GemmParams q = gp();
     q.A = dY + st.col; q.lda = lddy; q.B = bt; q.ldb = st.out; q.M = M; q.N = r; q.K = st.out;
     q.C = tp + slot[i] * r; q.ldc = n * r; q.scale = d.lora_alpha / (float)r;
-    HIP_TRY(gemm_bf16(q, EPI_SCALED, s));
+    if (r <= 128 && st.out % 64 == 0) HIP_TRY(gemm_skinny(q, part, s));
+    else HIP_TRY(gemm_bf16(q, EPI_SCALED, s));
     HIP_TRY(transpose_bf16((const bf16*)w.lora_a[st.site], in, xb + slot[i] * r, n * r, r, in, s));
   }
   p.X = tp; p.ldx = n * r; p.xk = n * r; p.xr = n * r;
@@ -551,7 +556,7 @@ int run_block_bwd(const gen_block_dims& d, const gen_block_weights& w, const flo
     GemmParams p = gp();
     p.A = u; p.lda = D; p.B = w.w_qkv; p.ldb = D; p.M = M; p.N = QKV; p.K = D; p.C = qkv_raw; p.ldc = QKV;
     if (lora) {
-      HIP_TRY(lora_down<bf16>(d, w, qkv_sites, 3, u, D, M, t_qkv, off_qkv, ld_qkv, s));
+      HIP_TRY(lora_down<bf16>(d, w, qkv_sites, 3, u, D, M, t_qkv, off_qkv, ld_qkv, s, part));
       if (off_qkv[0] >= 0 || off_qkv[1] >= 0 || off_qkv[2] >= 0) lora_ext(p, d, w, qkv_sites, 3, qkv_ends, t_qkv, ld_qkv, off_qkv);
     }
     HIP_TRY(gemm_bf16(p, EPI_STORE, s));
@@ -566,7 +571,7 @@ int run_block_bwd(const gen_block_dims& d, const gen_block_weights& w, const flo
     p.A = attn; p.lda = QD; p.B = w.w_o; p.ldb = QD; p.M = M; p.N = D; p.K = QD;
     p.C = xmid; p.ldc = D; p.R = h; p.ldr = D;
     if (lora) {
-      HIP_TRY(lora_down<bf16>(d, w, o_site, 1, attn, QD, M, t_o, off_o, ld_o, s));
+      HIP_TRY(lora_down<bf16>(d, w, o_site, 1, attn, QD, M, t_o, off_o, ld_o, s, part));
       if (off_o[0] >= 0) lora_ext(p, d, w, o_site, 1, &D, t_o, ld_o, off_o);
     }
     HIP_TRY(gemm_bf16(p, EPI_RESID_F32, s));
@@ -576,13 +581,13 @@ int run_block_bwd(const gen_block_dims& d, const gen_block_weights& w, const flo
     GemmParams p = gp();
     p.A = u2; p.lda = D; p.B = w.w_gate_up; p.ldb = D; p.M = M; p.N = 2 * I; p.K = D; p.C = gu; p.ldc = 2 * I;
     if (lora) {
-      HIP_TRY(lora_down<bf16>(d, w, gu_sites, 2, u2, D, M, t_gu, off_gu, ld_gu, s));
+      HIP_TRY(lora_down<bf16>(d, w, gu_sites, 2, u2, D, M, t_gu, off_gu, ld_gu, s, part));
       if (off_gu[0] >= 0 || off_gu[1] >= 0) lora_ext(p, d, w, gu_sites, 2, gu_ends, t_gu, ld_gu, off_gu);
     }
     HIP_TRY(gemm_bf16(p, EPI_STORE, s));
   }
   HIP_TRY(swiglu_fwd(gu, z, M, I, s));
-  if (lora) HIP_TRY(lora_down<bf16>(d, w, down_site, 1, z, I, M, t_down, off_down, ld_down, s));
+  if (lora) HIP_TRY(lora_down<bf16>(d, w, down_site, 1, z, I, M, t_down, off_down, ld_down, s, part));
 
   // ---- backward
   int slot[3], n;
@@ -592,7 +597,7 @@ int run_block_bwd(const gen_block_dims& d, const gen_block_weights& w, const flo
     GemmParams p = gp();
     HIP_TRY(transpose_bf16((const bf16*)w.w_down, I, wt, D, D, I, s));
     p.A = dyb; p.lda = D; p.B = wt; p.ldb = D; p.M = M; p.N = I; p.K = D; p.C = dz; p.ldc = I;
-    n = lora_back(d, w, bs, 1, dyb, D, I, M, tp, xb, bt, p, slot, s);
+    n = lora_back(d, w, bs, 1, dyb, D, I, M, tp, xb, bt, p, slot, part, s);
     if (n < 0) return n;
     HIP_TRY(gemm_bf16(p, EPI_STORE, s));
     if (n > 0) {
@@ -606,7 +611,7 @@ int run_block_bwd(const gen_block_dims& d, const gen_block_weights& w, const flo
     GemmParams p = gp();
     HIP_TRY(transpose_bf16((const bf16*)w.w_gate_up, D, wt, 2 * I, 2 * I, D, s));
     p.A = dgu; p.lda = 2 * I; p.B = wt; p.ldb = 2 * I; p.M = M; p.N = D; p.K = 2 * I; p.C = du; p.ldc = D;
-    n = lora_back(d, w, bs, 2, dgu, 2 * I, D, M, tp, xb, bt, p, slot, s);
+    n = lora_back(d, w, bs, 2, dgu, 2 * I, D, M, tp, xb, bt, p, slot, part, s);
     if (n < 0) return n;
     HIP_TRY(gemm_bf16(p, EPI_STORE, s));
     if (n > 0) {
@@ -621,7 +626,7 @@ int run_block_bwd(const gen_block_dims& d, const gen_block_weights& w, const flo
     GemmParams p = gp();
     HIP_TRY(transpose_bf16((const bf16*)w.w_o, QD, wt, D, D, QD, s));
     p.A = dyb; p.lda = D; p.B = wt; p.ldb = D; p.M = M; p.N = QD; p.K = D; p.C = dO; p.ldc = QD;
-    n = lora_back(d, w, bs, 1, dyb, D, QD, M, tp, xb, bt, p, slot, s);
+    n = lora_back(d, w, bs, 1, dyb, D, QD, M, tp, xb, bt, p, slot, part, s);
     if (n < 0) return n;
     HIP_TRY(gemm_bf16(p, EPI_STORE, s));
     if (n > 0) {
@@ -638,7 +643,7 @@ int run_block_bwd(const gen_block_dims& d, const gen_block_weights& w, const flo
     GemmParams p = gp();
     HIP_TRY(transpose_bf16((const bf16*)w.w_qkv, D, wt, QKV, QKV, D, s));
     p.A = dqkv; p.lda = QKV; p.B = wt; p.ldb = QKV; p.M = M; p.N = D; p.K = QKV; p.C = du; p.ldc = D;
-    n = lora_back(d, w, bs, 3, dqkv, QKV, D, M, tp, xb, bt, p, slot, s);
+    n = lora_back(d, w, bs, 3, dqkv, QKV, D, M, tp, xb, bt, p, slot, part, s);
     if (n < 0) return n;
     HIP_TRY(gemm_bf16(p, EPI_STORE, s));
     if (n > 0) {

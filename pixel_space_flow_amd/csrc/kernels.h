@@ -4,6 +4,7 @@
 #include <stdint.h>
 #include <hip/hip_runtime.h>
 #include "common.h"
+#include "gemm.h"
 
 namespace psf {
 
@@ -94,6 +95,13 @@ hipError_t wgrad(const bf16* X, int64_t ldx, const bf16* Y, int64_t ldy, int M, 
                  hipStream_t s);
 hipError_t x0_loss(const float* pred, const float* tgt, float* grad, float* part, int nparts, float* loss, int64_t n,
                    hipStream_t s);
+
+// Skinny GEMM (N <= 128, K a multiple of 64; bmode 0 or 2, EPI_SCALED into bf16 C): split over K,
+// partial sums in part (skinny_part_floats(M, N) floats), reduced in a fixed order.
+constexpr int SKINNY_MAX_SPLITS = 16;
+inline size_t skinny_part_floats(int M, int N) { return (size_t)SKINNY_MAX_SPLITS * M * N; }
+int skinny_splits(int M, int K);
+hipError_t gemm_skinny(const GemmParams& p, float* part, hipStream_t s);
 
 // Router: idx/w [T, k]; u [T, D], wr [E, D]
 template <typename T>

@@ -1,0 +1,127 @@
+// Skinny GEMM for the LoRA projections: C[m, n] = scale sum_k A[m, k] B[n, k] with N <= 128 output
+// columns (rank r, or up to three sites of rank r side by side).  A 256 x 256 tile GEMM gives such
+// a product only M/256 workgroups; here one wave owns 32 rows x N columns over one k-range, the
+// k-ranges split K so that about 2048 waves run, and a second pass adds the partial sums in a
+// fixed order (no atomics), scales and rounds once to bf16.
+//
+// Fragments of v_mfma_f32_32x32x16_bf16 come straight from global memory: lane l reads 16 bytes of
+// row (l % 32) at k offset 8 (l / 32), four k-steps per iteration, so each row is read as one
+// contiguous 128-byte piece; the next iteration's loads are issued before this one's MFMAs.
+#include "common.h"
+#include "gemm.h"
+#include "kernels.h"
+
+namespace psf {
+namespace {
+
+template <int NB>
+__global__ __launch_bounds__(64) void skinny_kernel(const bf16* __restrict__ A, int64_t lda, const bf16* __restrict__ B0,
+                                                    const bf16* __restrict__ B1, const bf16* __restrict__ B2,
+                                                    int64_t ldb, int seg_rows, int M, int N, int K, int kchunk,
+                                                    float* __restrict__ part) {
+  const int lane = threadIdx.x, lr = lane & 31, lh = lane >> 5;
+  const int m0 = blockIdx.x * 32, z = blockIdx.y;
+  const int k_lo = z * kchunk, k_hi = min(K, k_lo + kchunk);
+  const bf16* ap = A + (int64_t)min(m0 + lr, M - 1) * lda + lh * 8;
+  const bf16* bp[NB];
+  bool bok[NB];
+#pragma unroll
+  for (int nb = 0; nb < NB; ++nb) {
+    const int n = nb * 32 + lr;
+    bok[nb] = n < N;
+    const int nc = bok[nb] ? n : 0;
+    const int seg = nc / seg_rows;
+    const bf16* base = seg == 0 ? B0 : (seg == 1 ? B1 : B2);
+    bp[nb] = base + (int64_t)(nc - seg * seg_rows) * ldb + lh * 8;
+  }
+  f32x16 acc[NB];
+#pragma unroll
+  for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+    for (int e = 0; e < 16; ++e) acc[nb][e] = 0.f;
+  bf16x8 a[4], b[NB][4], an[4], bn[NB][4];
+  const bf16x8 zero = {};
+  auto load = [&](int k, bf16x8 (&ao)[4], bf16x8 (&bo)[NB][4]) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      ao[i] = *(const bf16x8*)(ap + k + 16 * i);
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb) bo[nb][i] = bok[nb] ? *(const bf16x8*)(bp[nb] + k + 16 * i) : zero;
+    }
+  };
+  if (k_lo < k_hi) load(k_lo, a, b);
+  for (int k = k_lo; k < k_hi; k += 64) {
+    const bool more = k + 64 < k_hi;
+    if (more) load(k + 64, an, bn);
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb) acc[nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[i], b[nb][i], acc[nb], 0, 0, 0);
+    if (more) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        a[i] = an[i];
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb) b[nb][i] = bn[nb][i];
+      }
+    }
+  }
+  float* out = part + (int64_t)z * M * N;
+#pragma unroll
+  for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+    for (int e = 0; e < 16; ++e) {
+      const int m = m0 + (e >> 2) * 8 + lh * 4 + (e & 3), n = nb * 32 + lr;
+      if (m < M && n < N) out[(int64_t)m * N + n] = acc[nb][e];
+    }
+}
+
+// C[m * ldc + n] = bf16(scale * sum_z part[z][m][n])
+__global__ __launch_bounds__(256) void skinny_reduce_kernel(const float* __restrict__ part, int splits, int M, int N,
+                                                            float scale, bf16* __restrict__ C, int64_t ldc) {
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  const int64_t n_all = (int64_t)M * N;
+  if (i >= n_all) return;
+  float s = 0.f;
+  for (int z = 0; z < splits; ++z) s += part[(int64_t)z * n_all + i];
+  const int64_t m = i / N;
+  C[m * ldc + (i - m * N)] = static_cast<bf16>(scale * s);
+}
+
+}  // namespace
+
+int skinny_splits(int M, int K) {
+  const int waves_m = (M + 31) / 32;
+  int splits = (2048 + waves_m - 1) / waves_m;
+  splits = std::min(splits, std::max(1, K / 256));
+  return std::min(std::max(splits, 1), SKINNY_MAX_SPLITS);
+}
+
+hipError_t gemm_skinny(const GemmParams& p, float* part, hipStream_t s) {
+  if (p.M <= 0 || p.N <= 0) return hipSuccess;
+  if (p.N > 128 || p.K % 64 || p.K <= 0) return hipErrorInvalidValue;
+  const bool seg = p.bmode == 2;
+  const bf16* B0 = (const bf16*)(seg ? p.Bs[0] : p.B);
+  const bf16* B1 = seg ? (const bf16*)p.Bs[1] : B0;
+  const bf16* B2 = seg ? (const bf16*)p.Bs[2] : B0;
+  const int seg_rows = seg ? p.seg_rows : 128;
+  const int splits = skinny_splits(p.M, p.K);
+  const int kchunk = (p.K / 64 + splits - 1) / splits * 64;
+  const int nz = (p.K + kchunk - 1) / kchunk;
+  const dim3 grid((p.M + 31) / 32, nz);
+  const int nb = (p.N + 31) / 32;
+#define PSF_SK(NBV)                                                                                      \
+  hipLaunchKernelGGL(skinny_kernel<NBV>, grid, dim3(64), 0, s, (const bf16*)p.A, p.lda, B0, B1, B2, p.ldb, \
+                     seg_rows, p.M, p.N, p.K, kchunk, part)
+  if (nb == 1) PSF_SK(1);
+  else if (nb == 2) PSF_SK(2);
+  else if (nb == 3) PSF_SK(3);
+  else PSF_SK(4);
+#undef PSF_SK
+  const int64_t n = (int64_t)p.M * p.N;
+  hipLaunchKernelGGL(skinny_reduce_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, (const float*)part, nz,
+                     p.M, p.N, p.scale, (bf16*)p.C, p.ldc);
+  return hipGetLastError();
+}
+
+}  // namespace psf
