@@ -145,7 +145,7 @@ constexpr size_t ALIGN = 256;
 size_t up(size_t x) { return (x + ALIGN - 1) / ALIGN * ALIGN; }
 
 struct Ws {
-  size_t hidden, patches, u, qkv, attn, kc, vt, z, rope, temb, h1, x0, lora_t, hmid, skinny;
+  size_t hidden, patches, u, qkv, attn, kc, vt, z, rope, temb, h1, x0, lora_t, hmid, skinny, lora_gu, lora_f32;
   size_t m_idx, m_w, m_counts, m_offsets, m_perm, m_pos, m_tiles, m_z, m_y;
   size_t total;
   int Lpad, max_tiles, n_pos;
@@ -175,6 +175,8 @@ Ws layout(const gen_block_dims& d, int n_img, int n_br, int N, int max_prefix) {
   w.x0 = take(B * 3 * (size_t)N * 1024 * 4);
   w.lora_t = take(d.lora_rank > 0 ? M * 3 * d.lora_rank * es : 0);
   w.skinny = take(d.lora_rank > 0 ? skinny_part_floats((int)M, std::min(3 * d.lora_rank, 128)) * 4 : 0);
+  w.lora_gu = take(d.lora_rank > 0 && d.mlp_intermediate > 0 ? M * 2 * d.mlp_intermediate * es : 0);
+  w.lora_f32 = take(d.lora_rank > 0 ? M * qkv * 4 : 0);
   if (d.n_experts > 0) {
     const size_t A = M * d.top_k;
     w.max_tiles = (int)(A / 256 + d.n_experts + 1);
@@ -241,6 +243,32 @@ void lora_ext(GemmParams& p, const gen_block_dims& d, const gen_block_weights& w
   }
 }
 
+bool lora_all(const gen_block_weights& w, const int* sites, int ns) {
+  for (int i = 0; i < ns; ++i)
+    if (!w.lora_b[sites[i]]) return false;
+  return true;
+}
+
+// LoRA up-projection as low-rank products: columns [ends[i-1], ends[i]) of C (op)= t_i B_i^T with
+// t_i = columns off[i] .. off[i] + r of t.  mode 3 writes fp32 (the base GEMM then adds onto it
+// with the fp32-residual epilogue and rounds the sum once), mode 2 adds into fp32, mode 0 writes
+// bf16 (the SwiGLU epilogue's additive terms).
+hipError_t lora_up(const gen_block_dims& d, const gen_block_weights& w, const int* sites, int ns, const int* ends,
+                   const bf16* t, int ldt, const int* off, void* C, int64_t ldc, int M, int mode, hipStream_t s) {
+  const int r = d.lora_rank;
+  int start = 0;
+  for (int i = 0; i < ns; ++i) {
+    if (off[i] >= 0) {
+      void* c = mode >= 2 ? (void*)((float*)C + start) : (void*)((bf16*)C + start);
+      hipError_t e = gemm_lowrank(t + off[i], ldt, (const bf16*)w.lora_b[sites[i]], r, M, ends[i] - start, r, c, ldc,
+                                  mode, s);
+      if (e != hipSuccess) return e;
+    }
+    start = ends[i];
+  }
+  return hipSuccess;
+}
+
 // T: operand dtype (weights, GEMM/attention inputs); TH: residual-stream dtype of `hidden`.
 // With an fp32 residual the O and down projections accumulate into `hidden` in place; with a
 // bf16 residual the mid-block residual lives in the fp32 buffer hmid and `hidden` is rounded
@@ -270,13 +298,20 @@ int run_block(const gen_block_dims& d, const gen_block_weights& w, TH* hidden, c
     GemmParams p = gp();
     p.A = u; p.lda = D; p.B = w.w_qkv; p.ldb = D; p.M = M; p.N = QKV; p.K = D;
     p.C = qkv; p.ldc = QKV;
+    int epi = EPI_STORE;
     if (lora) {
       const int sites[3] = {0, 1, 2}, ends[3] = {QD, QD + Hkv * hd, QKV};
       int off[3], ldt;
       HIP_TRY(lora_down<T>(d, w, sites, 3, u, D, M, lt, off, ldt, s, at<float>(ws, L.skinny)));
-      if (off[0] >= 0 || off[1] >= 0 || off[2] >= 0) lora_ext(p, d, w, sites, 3, ends, lt, ldt, off);
+      if (lora_all(w, sites, 3)) {
+        float* lf = at<float>(ws, L.lora_f32);
+        HIP_TRY(lora_up(d, w, sites, 3, ends, (const bf16*)lt, ldt, off, lf, QKV, M, 3, s));
+        epi = EPI_RESID_FROM_F32; p.R = lf; p.ldr = QKV;
+      } else if (off[0] >= 0 || off[1] >= 0 || off[2] >= 0) {
+        lora_ext(p, d, w, sites, 3, ends, lt, ldt, off);
+      }
     }
-    HIP_TRY(timed(FAM_QKV, s, [&] { return gemm_any<T>(p, EPI_STORE, s); }));
+    HIP_TRY(timed(FAM_QKV, s, [&] { return gemm_any<T>(p, epi, s); }));
   }
   if (kcache) {
     // prefix forward: normalise and rotate q, k in place, hand k and v to the cache, causal attention
@@ -314,13 +349,12 @@ int run_block(const gen_block_dims& d, const gen_block_weights& w, TH* hidden, c
     GemmParams p = gp();
     p.A = attn; p.lda = QD; p.B = w.w_o; p.ldb = QD; p.M = M; p.N = D; p.K = QD;
     p.C = hmid; p.ldc = D; p.R = hidden; p.ldr = D;
-    if (lora) {
-      const int sites[1] = {3}, ends[1] = {D};
-      int off[1], ldt;
-      HIP_TRY(lora_down<T>(d, w, sites, 1, attn, QD, M, lt, off, ldt, s, at<float>(ws, L.skinny)));
-      if (off[0] >= 0) lora_ext(p, d, w, sites, 1, ends, lt, ldt, off);
-    }
+    const int sites[1] = {3}, ends[1] = {D};
+    int off[1] = {-1}, ldt = 0;
+    if (lora) HIP_TRY(lora_down<T>(d, w, sites, 1, attn, QD, M, lt, off, ldt, s, at<float>(ws, L.skinny)));
     HIP_TRY(timed(FAM_O, s, [&] { return gemm_any<T>(p, f32res ? EPI_RESID_F32 : EPI_RESID_TO_F32, s); }));
+    // the LoRA term accumulates into the fp32 mid-block residual
+    if (off[0] >= 0) HIP_TRY(lora_up(d, w, sites, 1, ends, (const bf16*)lt, ldt, off, hmid, D, M, 2, s));
   }
   HIP_TRY((rmsnorm<float, T>(hmid, (const T*)w.g_post, u, M, D, d.rms_eps, s)));
   if (d.mlp_intermediate > 0) {
@@ -334,7 +368,14 @@ int run_block(const gen_block_dims& d, const gen_block_weights& w, TH* hidden, c
         const int sites[2] = {4, 5}, ends[2] = {I, 2 * I};
         int off[2], ldt;
         HIP_TRY(lora_down<T>(d, w, sites, 2, u, D, M, lt, off, ldt, s, at<float>(ws, L.skinny)));
-        if (off[0] >= 0 || off[1] >= 0) lora_ext(p, d, w, sites, 2, ends, lt, ldt, off);
+        if (lora_all(w, sites, 2)) {
+          // gate and up LoRA terms, added by the SwiGLU epilogue before the activation
+          T* lg = at<T>(ws, L.lora_gu);
+          HIP_TRY(lora_up(d, w, sites, 2, ends, (const bf16*)lt, ldt, off, lg, 2 * I, M, 0, s));
+          p.R = lg; p.ldr = 2 * I;
+        } else if (off[0] >= 0 || off[1] >= 0) {
+          lora_ext(p, d, w, sites, 2, ends, lt, ldt, off);
+        }
       }
       HIP_TRY(timed(FAM_GATE_UP, s, [&] { return gemm_any<T>(p, EPI_SWIGLU, s); }));
     }
@@ -342,13 +383,18 @@ int run_block(const gen_block_dims& d, const gen_block_weights& w, TH* hidden, c
       GemmParams p = gp();
       p.A = z; p.lda = I; p.B = w.w_down; p.ldb = I; p.M = M; p.N = D; p.K = I;
       p.C = hidden; p.ldc = D; p.R = hmid; p.ldr = D;
+      const int sites[1] = {6}, ends[1] = {D};
+      int off[1] = {-1}, ldt = 0;
+      bool post = false;
       if (lora) {
-        const int sites[1] = {6}, ends[1] = {D};
-        int off[1], ldt;
         HIP_TRY(lora_down<T>(d, w, sites, 1, z, I, M, lt, off, ldt, s, at<float>(ws, L.skinny)));
-        if (off[0] >= 0) lora_ext(p, d, w, sites, 1, ends, lt, ldt, off);
+        // fp32 residual: the LoRA term is added after the base GEMM; a bf16 residual keeps the
+        // K extension so that the block output is rounded once
+        if (off[0] >= 0 && f32res) post = true;
+        else if (off[0] >= 0) lora_ext(p, d, w, sites, 1, ends, lt, ldt, off);
       }
       HIP_TRY(timed(FAM_DOWN, s, [&] { return gemm_any<T>(p, f32res ? EPI_RESID_F32 : EPI_RESID_FROM_F32, s); }));
+      if (post) HIP_TRY(lora_up(d, w, sites, 1, ends, (const bf16*)lt, ldt, off, hidden, D, M, 2, s));
     }
   } else {
     const int E = d.n_experts, k = d.top_k, Ie = d.expert_intermediate;
@@ -407,7 +453,7 @@ int check_prefix_ptrs(const SeqInfo& si, int layer) {
 // LoRA sites: 0 q, 1 k, 2 v, 3 o, 4 gate, 5 up, 6 down.
 struct Wb {
   size_t u, qkv_raw, qkv_n, kc, vt, rope, attn, lse, dot, xmid, u2, gu, z, t_qkv, t_o, t_gu, t_down, tp, dyb, dz,
-      dgu, du, dxf, dO, dq, dk, dv, dqkv, wt, xb, bt, part, total;
+      dgu, du, dxf, dO, dq, dk, dv, dqkv, wt, xb, bt, part, lf, total;
   int Lpad, n_pos;
 };
 
@@ -451,6 +497,7 @@ Wb layout_bwd(const gen_block_dims& d, int B, int N, int max_prefix) {
   w.wt = take(std::max(std::max(QKV * D, QD * D), std::max(2 * I * D, I * D)) * 2);
   w.xb = take(std::max(std::max(D, I), QD) * 3 * r * 2);
   w.bt = take(r * std::max(std::max(QD, D), I) * 2);
+  w.lf = take(r ? M * std::max(std::max(QKV, 2 * I), std::max(D, QD)) * 4 : 0);
   w.part = take(std::max(std::max((size_t)4 << 20, r * std::max(std::max(QD, D), I)),
                          r ? skinny_part_floats((int)M, (int)std::min<size_t>(3 * r, 128)) : 0) * 4);
   w.total = o;
@@ -465,12 +512,13 @@ struct BackSite {
 
 // For the LoRA sites of one base GEMM whose output gradient is dY [M, lddy]:
 //   tp[:, slot r:(slot+1) r] = (alpha/r) dY_site B_site   (dL/d(x A^T), scaled as the forward's t)
-//   xb[:, slot r:(slot+1) r] = A_site^T                    (the up-projection of the K extension)
-// and p gets that K extension, so the base dgrad GEMM also adds sum_site tp_site A_site.
-// Returns the number of sites present (slot order = list order).
+//   xb[:, slot r:(slot+1) r] = A_site^T
+// and the fp32 scratch lf receives sum_site tp_site A_site, with p.R = lf: the base dgrad GEMM, run
+// with the fp32-residual epilogue, adds dY W onto it and rounds once.  Returns the number of sites present (slot order =
+// list order); with none, p is untouched and the GEMM runs with a plain store.
 int lora_back(const gen_block_dims& d, const gen_block_weights& w, const BackSite* sites, int ns, const bf16* dY,
               int lddy, int in, int M, bf16* tp, bf16* xb, bf16* bt, GemmParams& p, int* slot, float* part,
-              hipStream_t s) {
+              float* lf, hipStream_t s) {
   const int r = d.lora_rank;
   int n = 0;
   for (int i = 0; i < ns; ++i) slot[i] = (r > 0 && w.lora_a[sites[i].site]) ? n++ : -1;
@@ -486,10 +534,9 @@ int lora_back(const gen_block_dims& d, const gen_block_weights& w, const BackSit
     else HIP_TRY(gemm_bf16(q, EPI_SCALED, s));
     HIP_TRY(transpose_bf16((const bf16*)w.lora_a[st.site], in, xb + slot[i] * r, n * r, r, in, s));
   }
-  p.X = tp; p.ldx = n * r; p.xk = n * r; p.xr = n * r;
-  p.XB[0] = xb; p.XB[1] = p.XB[2] = nullptr;
-  p.xsite_end[0] = p.xsite_end[1] = p.xsite_end[2] = p.N;
-  p.xoff[0] = p.xoff[1] = p.xoff[2] = 0;
+  // sum_site tp_site A_site into the fp32 scratch; the base dgrad GEMM adds onto it and rounds once
+  HIP_TRY(gemm_lowrank(tp, n * r, xb, n * r, M, p.N, n * r, lf, p.N, 3, s));
+  p.R = lf; p.ldr = p.N;
   return n;
 }
 
@@ -543,6 +590,7 @@ int run_block_bwd(const gen_block_dims& d, const gen_block_weights& w, const flo
   bf16* xb = at<bf16>(ws, L.xb);
   bf16* bt = at<bf16>(ws, L.bt);
   float* part = at<float>(ws, L.part);
+  float* lf = at<float>(ws, L.lf);
   const float2* rope = at<float2>(ws, L.rope);
   HIP_TRY(rope_table(at<float2>(ws, L.rope), L.n_pos, hd, d.rope_theta, s));
 
@@ -555,11 +603,17 @@ int run_block_bwd(const gen_block_dims& d, const gen_block_weights& w, const flo
   {
     GemmParams p = gp();
     p.A = u; p.lda = D; p.B = w.w_qkv; p.ldb = D; p.M = M; p.N = QKV; p.K = D; p.C = qkv_raw; p.ldc = QKV;
+    int epi = EPI_STORE;
     if (lora) {
       HIP_TRY(lora_down<bf16>(d, w, qkv_sites, 3, u, D, M, t_qkv, off_qkv, ld_qkv, s, part));
-      if (off_qkv[0] >= 0 || off_qkv[1] >= 0 || off_qkv[2] >= 0) lora_ext(p, d, w, qkv_sites, 3, qkv_ends, t_qkv, ld_qkv, off_qkv);
+      if (lora_all(w, qkv_sites, 3)) {
+        HIP_TRY(lora_up(d, w, qkv_sites, 3, qkv_ends, t_qkv, ld_qkv, off_qkv, lf, QKV, M, 3, s));
+        epi = EPI_RESID_FROM_F32; p.R = lf; p.ldr = QKV;
+      } else if (off_qkv[0] >= 0 || off_qkv[1] >= 0 || off_qkv[2] >= 0) {
+        lora_ext(p, d, w, qkv_sites, 3, qkv_ends, t_qkv, ld_qkv, off_qkv);
+      }
     }
-    HIP_TRY(gemm_bf16(p, EPI_STORE, s));
+    HIP_TRY(gemm_bf16(p, epi, s));
   }
   HIP_TRY(hipMemcpyAsync(qkv_n, qkv_raw, (size_t)M * QKV * 2, hipMemcpyDeviceToDevice, s));
   HIP_TRY(qknorm_rope<bf16>(qkv_n, QKV, si, Hq, Hkv, hd, (const bf16*)w.g_q, (const bf16*)w.g_k, rope, eps, s));
@@ -570,21 +624,25 @@ int run_block_bwd(const gen_block_dims& d, const gen_block_weights& w, const flo
     GemmParams p = gp();
     p.A = attn; p.lda = QD; p.B = w.w_o; p.ldb = QD; p.M = M; p.N = D; p.K = QD;
     p.C = xmid; p.ldc = D; p.R = h; p.ldr = D;
-    if (lora) {
-      HIP_TRY(lora_down<bf16>(d, w, o_site, 1, attn, QD, M, t_o, off_o, ld_o, s, part));
-      if (off_o[0] >= 0) lora_ext(p, d, w, o_site, 1, &D, t_o, ld_o, off_o);
-    }
+    if (lora) HIP_TRY(lora_down<bf16>(d, w, o_site, 1, attn, QD, M, t_o, off_o, ld_o, s, part));
     HIP_TRY(gemm_bf16(p, EPI_RESID_F32, s));
+    if (off_o[0] >= 0) HIP_TRY(lora_up(d, w, o_site, 1, &D, t_o, ld_o, off_o, xmid, D, M, 2, s));
   }
   HIP_TRY((rmsnorm<float, bf16>(xmid, (const bf16*)w.g_post, u2, M, D, eps, s)));
   {
     GemmParams p = gp();
     p.A = u2; p.lda = D; p.B = w.w_gate_up; p.ldb = D; p.M = M; p.N = 2 * I; p.K = D; p.C = gu; p.ldc = 2 * I;
+    int epi = EPI_STORE;
     if (lora) {
       HIP_TRY(lora_down<bf16>(d, w, gu_sites, 2, u2, D, M, t_gu, off_gu, ld_gu, s, part));
-      if (off_gu[0] >= 0 || off_gu[1] >= 0) lora_ext(p, d, w, gu_sites, 2, gu_ends, t_gu, ld_gu, off_gu);
+      if (lora_all(w, gu_sites, 2)) {
+        HIP_TRY(lora_up(d, w, gu_sites, 2, gu_ends, t_gu, ld_gu, off_gu, lf, 2 * I, M, 3, s));
+        epi = EPI_RESID_FROM_F32; p.R = lf; p.ldr = 2 * I;
+      } else if (off_gu[0] >= 0 || off_gu[1] >= 0) {
+        lora_ext(p, d, w, gu_sites, 2, gu_ends, t_gu, ld_gu, off_gu);
+      }
     }
-    HIP_TRY(gemm_bf16(p, EPI_STORE, s));
+    HIP_TRY(gemm_bf16(p, epi, s));
   }
   HIP_TRY(swiglu_fwd(gu, z, M, I, s));
   if (lora) HIP_TRY(lora_down<bf16>(d, w, down_site, 1, z, I, M, t_down, off_down, ld_down, s, part));
@@ -597,9 +655,9 @@ int run_block_bwd(const gen_block_dims& d, const gen_block_weights& w, const flo
     GemmParams p = gp();
     HIP_TRY(transpose_bf16((const bf16*)w.w_down, I, wt, D, D, I, s));
     p.A = dyb; p.lda = D; p.B = wt; p.ldb = D; p.M = M; p.N = I; p.K = D; p.C = dz; p.ldc = I;
-    n = lora_back(d, w, bs, 1, dyb, D, I, M, tp, xb, bt, p, slot, part, s);
+    n = lora_back(d, w, bs, 1, dyb, D, I, M, tp, xb, bt, p, slot, part, lf, s);
     if (n < 0) return n;
-    HIP_TRY(gemm_bf16(p, EPI_STORE, s));
+    HIP_TRY(gemm_bf16(p, n > 0 ? EPI_RESID_FROM_F32 : EPI_STORE, s));
     if (n > 0) {
       int rc = lora_wgrad(d, g, bs, 1, slot, n, dyb, D, t_down, ld_down, off_down, tp, z, I, M, part, s);
       if (rc) return rc;
@@ -611,9 +669,9 @@ int run_block_bwd(const gen_block_dims& d, const gen_block_weights& w, const flo
     GemmParams p = gp();
     HIP_TRY(transpose_bf16((const bf16*)w.w_gate_up, D, wt, 2 * I, 2 * I, D, s));
     p.A = dgu; p.lda = 2 * I; p.B = wt; p.ldb = 2 * I; p.M = M; p.N = D; p.K = 2 * I; p.C = du; p.ldc = D;
-    n = lora_back(d, w, bs, 2, dgu, 2 * I, D, M, tp, xb, bt, p, slot, part, s);
+    n = lora_back(d, w, bs, 2, dgu, 2 * I, D, M, tp, xb, bt, p, slot, part, lf, s);
     if (n < 0) return n;
-    HIP_TRY(gemm_bf16(p, EPI_STORE, s));
+    HIP_TRY(gemm_bf16(p, n > 0 ? EPI_RESID_FROM_F32 : EPI_STORE, s));
     if (n > 0) {
       int rc = lora_wgrad(d, g, bs, 2, slot, n, dgu, 2 * I, t_gu, ld_gu, off_gu, tp, u2, D, M, part, s);
       if (rc) return rc;
@@ -626,9 +684,9 @@ int run_block_bwd(const gen_block_dims& d, const gen_block_weights& w, const flo
     GemmParams p = gp();
     HIP_TRY(transpose_bf16((const bf16*)w.w_o, QD, wt, D, D, QD, s));
     p.A = dyb; p.lda = D; p.B = wt; p.ldb = D; p.M = M; p.N = QD; p.K = D; p.C = dO; p.ldc = QD;
-    n = lora_back(d, w, bs, 1, dyb, D, QD, M, tp, xb, bt, p, slot, part, s);
+    n = lora_back(d, w, bs, 1, dyb, D, QD, M, tp, xb, bt, p, slot, part, lf, s);
     if (n < 0) return n;
-    HIP_TRY(gemm_bf16(p, EPI_STORE, s));
+    HIP_TRY(gemm_bf16(p, n > 0 ? EPI_RESID_FROM_F32 : EPI_STORE, s));
     if (n > 0) {
       int rc = lora_wgrad(d, g, bs, 1, slot, n, dyb, D, t_o, ld_o, off_o, tp, attn, QD, M, part, s);
       if (rc) return rc;
@@ -643,9 +701,9 @@ int run_block_bwd(const gen_block_dims& d, const gen_block_weights& w, const flo
     GemmParams p = gp();
     HIP_TRY(transpose_bf16((const bf16*)w.w_qkv, D, wt, QKV, QKV, D, s));
     p.A = dqkv; p.lda = QKV; p.B = wt; p.ldb = QKV; p.M = M; p.N = D; p.K = QKV; p.C = du; p.ldc = D;
-    n = lora_back(d, w, bs, 3, dqkv, QKV, D, M, tp, xb, bt, p, slot, part, s);
+    n = lora_back(d, w, bs, 3, dqkv, QKV, D, M, tp, xb, bt, p, slot, part, lf, s);
     if (n < 0) return n;
-    HIP_TRY(gemm_bf16(p, EPI_STORE, s));
+    HIP_TRY(gemm_bf16(p, n > 0 ? EPI_RESID_FROM_F32 : EPI_STORE, s));
     if (n > 0) {
       int rc = lora_wgrad(d, g, bs, 3, slot, n, dqkv, QKV, t_qkv, ld_qkv, off_qkv, tp, u, D, M, part, s);
       if (rc) return rc;

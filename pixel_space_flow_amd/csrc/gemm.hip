@@ -556,14 +556,38 @@ __global__ __launch_bounds__(64 * NW, 1) void gemm_fast_kernel(GemmParams p, int
         v[4 * q] = f.x; v[4 * q + 1] = f.y; v[4 * q + 2] = f.z; v[4 * q + 3] = f.w;
       }
       if (EPI == EPI_SWIGLU) {
+        float u[16];
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
           const float4 f = *(const float4*)(T1 + rr * TS + cc + 4 * q);
-          v[4 * q] = silu_f(v[4 * q]) * f.x;
-          v[4 * q + 1] = silu_f(v[4 * q + 1]) * f.y;
-          v[4 * q + 2] = silu_f(v[4 * q + 2]) * f.z;
-          v[4 * q + 3] = silu_f(v[4 * q + 3]) * f.w;
+          u[4 * q] = f.x; u[4 * q + 1] = f.y; u[4 * q + 2] = f.z; u[4 * q + 3] = f.w;
         }
+        // optional bf16 terms added before the activation (the LoRA up-projection): R holds the
+        // gate term at column j and the up term at column swiglu_I + j
+        const int rsw = wm * 128 + mb * 32 + rr;
+        const int csw = tn * (BN / 2) + (wn * (NBW / 2) + (nb >> 1)) * 32 + cc;
+        if (p.R && rsw < rows) {
+          const bf16* rg = (const bf16*)p.R + (int64_t)(row0 + rsw) * p.ldr + csw;
+          const bf16* ru = rg + p.swiglu_I;
+          if (csw + 16 <= p.swiglu_I) {
+#pragma unroll
+            for (int h2 = 0; h2 < 2; ++h2) {
+              const bf16x8 a = *(const bf16x8*)(rg + 8 * h2), b = *(const bf16x8*)(ru + 8 * h2);
+#pragma unroll
+              for (int j = 0; j < 8; ++j) {
+                v[8 * h2 + j] += static_cast<float>(a[j]);
+                u[8 * h2 + j] += static_cast<float>(b[j]);
+              }
+            }
+          } else {
+            for (int j = 0; j < 16 && csw + j < p.swiglu_I; ++j) {
+              v[j] += static_cast<float>(rg[j]);
+              u[j] += static_cast<float>(ru[j]);
+            }
+          }
+        }
+#pragma unroll
+        for (int j = 0; j < 16; ++j) v[j] = silu_f(v[j]) * u[j];
       }
       __builtin_amdgcn_s_waitcnt(0xc07f);                   // reads done before the next block overwrites
       __builtin_amdgcn_wave_barrier();
@@ -787,14 +811,38 @@ __global__ __launch_bounds__(512, 1) void gemm_k32_kernel(GemmParams p, int n_co
         v[4 * q] = f.x; v[4 * q + 1] = f.y; v[4 * q + 2] = f.z; v[4 * q + 3] = f.w;
       }
       if (EPI == EPI_SWIGLU) {
+        float u[16];
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
           const float4 f = *(const float4*)(T1 + rr * TS + cc + 4 * q);
-          v[4 * q] = silu_f(v[4 * q]) * f.x;
-          v[4 * q + 1] = silu_f(v[4 * q + 1]) * f.y;
-          v[4 * q + 2] = silu_f(v[4 * q + 2]) * f.z;
-          v[4 * q + 3] = silu_f(v[4 * q + 3]) * f.w;
+          u[4 * q] = f.x; u[4 * q + 1] = f.y; u[4 * q + 2] = f.z; u[4 * q + 3] = f.w;
         }
+        // optional bf16 terms added before the activation (the LoRA up-projection): R holds the
+        // gate term at column j and the up term at column swiglu_I + j
+        const int rsw = wm * 128 + mb * 32 + rr;
+        const int csw = tn * (BN / 2) + (wn * (NBW / 2) + (nb >> 1)) * 32 + cc;
+        if (p.R && rsw < rows) {
+          const bf16* rg = (const bf16*)p.R + (int64_t)(row0 + rsw) * p.ldr + csw;
+          const bf16* ru = rg + p.swiglu_I;
+          if (csw + 16 <= p.swiglu_I) {
+#pragma unroll
+            for (int h2 = 0; h2 < 2; ++h2) {
+              const bf16x8 a = *(const bf16x8*)(rg + 8 * h2), b = *(const bf16x8*)(ru + 8 * h2);
+#pragma unroll
+              for (int j = 0; j < 8; ++j) {
+                v[8 * h2 + j] += static_cast<float>(a[j]);
+                u[8 * h2 + j] += static_cast<float>(b[j]);
+              }
+            }
+          } else {
+            for (int j = 0; j < 16 && csw + j < p.swiglu_I; ++j) {
+              v[j] += static_cast<float>(rg[j]);
+              u[j] += static_cast<float>(ru[j]);
+            }
+          }
+        }
+#pragma unroll
+        for (int j = 0; j < 16; ++j) v[j] = silu_f(v[j]) * u[j];
       }
       __builtin_amdgcn_s_waitcnt(0xc07f);                   // reads done before the next block overwrites
       __builtin_amdgcn_wave_barrier();

@@ -102,6 +102,10 @@ constexpr int SKINNY_MAX_SPLITS = 16;
 inline size_t skinny_part_floats(int M, int N) { return (size_t)SKINNY_MAX_SPLITS * M * N; }
 int skinny_splits(int M, int K);
 hipError_t gemm_skinny(const GemmParams& p, float* part, hipStream_t s);
+// Low-rank product C (op)= X Y^T, K a multiple of 8 (LoRA up-projection): mode 0 C bf16 = acc,
+// 1 C bf16 = bf16(C + acc), 2 C fp32 += acc, 3 C fp32 = acc.
+hipError_t gemm_lowrank(const bf16* X, int64_t ldx, const bf16* Y, int64_t ldy, int M, int N, int K, void* C,
+                        int64_t ldc, int mode, hipStream_t s);
 
 // Router: idx/w [T, k]; u [T, D], wr [E, D]
 template <typename T>

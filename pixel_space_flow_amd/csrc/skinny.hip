@@ -1,4 +1,6 @@
-// Skinny GEMM for the LoRA projections: C[m, n] = scale sum_k A[m, k] B[n, k] with N <= 128 output
+// Skinny and low-rank GEMMs of the LoRA projections.
+//
+// Skinny GEMM (the down-projections): C[m, n] = scale sum_k A[m, k] B[n, k] with N <= 128 output
 // columns (rank r, or up to three sites of rank r side by side).  A 256 x 256 tile GEMM gives such
 // a product only M/256 workgroups; here one wave owns 32 rows x N columns over one k-range, the
 // k-ranges split K so that about 2048 waves run, and a second pass adds the partial sums in a
@@ -88,7 +90,84 @@ __global__ __launch_bounds__(256) void skinny_reduce_kernel(const float* __restr
   C[m * ldc + (i - m * N)] = static_cast<bf16>(scale * s);
 }
 
+// Low-rank product C (op)= X Y^T with a short k (the LoRA up-projection, k = rank or a few ranks):
+// X [M, K], Y [N, K] row-major, K a multiple of 8.  Workgroup tile 128 x 128, four waves of
+// 64 x 64 (2 x 2 blocks of 32 x 32); fragments straight from global memory.
+//   MODE 0: C bf16 = acc;   MODE 1: C bf16 = bf16(C + acc);   MODE 2: C fp32 += acc;   MODE 3: C fp32 = acc
+template <int MODE>
+__global__ __launch_bounds__(256) void lowrank_kernel(const bf16* __restrict__ X, int64_t ldx,
+                                                      const bf16* __restrict__ Y, int64_t ldy, int M, int N, int K,
+                                                      void* C, int64_t ldc) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, lr = lane & 31, lh = lane >> 5;
+  const int m0 = blockIdx.y * 128 + (wave >> 1) * 64, n0 = blockIdx.x * 128 + (wave & 1) * 64;
+  f32x16 acc[2][2];
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.f;
+  const bf16* xp[2];
+  const bf16* yp[2];
+  bool yok[2];
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    xp[i] = X + (int64_t)min(m0 + 32 * i + lr, M - 1) * ldx + lh * 8;
+    const int n = n0 + 32 * i + lr;
+    yok[i] = n < N;
+    yp[i] = Y + (int64_t)(yok[i] ? n : 0) * ldy + lh * 8;
+  }
+  const bf16x8 zero = {};
+  for (int k = 0; k < K; k += 16) {
+    const bool kok = k + lh * 8 < K;              // K a multiple of 8: the last half k-step may be empty
+    bf16x8 a[2], b[2];
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      a[i] = kok ? *(const bf16x8*)(xp[i] + k) : zero;
+      b[i] = (kok && yok[i]) ? *(const bf16x8*)(yp[i] + k) : zero;
+    }
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+      for (int j = 0; j < 2; ++j) acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[i], b[j], acc[i][j], 0, 0, 0);
+  }
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      const int n = n0 + 32 * j + lr;
+      if (n >= N) continue;
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        const int m = m0 + 32 * i + (e >> 2) * 8 + lh * 4 + (e & 3);
+        if (m >= M) continue;
+        if (MODE == 2) {
+          float* c = (float*)C + (int64_t)m * ldc + n;
+          *c += acc[i][j][e];
+        } else if (MODE == 3) {
+          ((float*)C)[(int64_t)m * ldc + n] = acc[i][j][e];
+        } else {
+          bf16* c = (bf16*)C + (int64_t)m * ldc + n;
+          *c = static_cast<bf16>(MODE == 1 ? static_cast<float>(*c) + acc[i][j][e] : acc[i][j][e]);
+        }
+      }
+    }
+}
+
 }  // namespace
+
+hipError_t gemm_lowrank(const bf16* X, int64_t ldx, const bf16* Y, int64_t ldy, int M, int N, int K, void* C,
+                        int64_t ldc, int mode, hipStream_t s) {
+  if (M <= 0 || N <= 0) return hipSuccess;
+  if (K <= 0 || K % 8 || ldx % 8 || ldy % 8) return hipErrorInvalidValue;
+  const dim3 grid((N + 127) / 128, (M + 127) / 128);
+  if (mode == 0) hipLaunchKernelGGL(lowrank_kernel<0>, grid, dim3(256), 0, s, X, ldx, Y, ldy, M, N, K, C, ldc);
+  else if (mode == 1) hipLaunchKernelGGL(lowrank_kernel<1>, grid, dim3(256), 0, s, X, ldx, Y, ldy, M, N, K, C, ldc);
+  else if (mode == 2) hipLaunchKernelGGL(lowrank_kernel<2>, grid, dim3(256), 0, s, X, ldx, Y, ldy, M, N, K, C, ldc);
+  else if (mode == 3) hipLaunchKernelGGL(lowrank_kernel<3>, grid, dim3(256), 0, s, X, ldx, Y, ldy, M, N, K, C, ldc);
+  else return hipErrorInvalidValue;
+  return hipGetLastError();
+}
 
 int skinny_splits(int M, int K) {
   const int waves_m = (M + 31) / 32;
