@@ -9,8 +9,9 @@
 //   swiglu_kernel          z = silu(gate) up, and its backward
 //   qknorm_rope_bwd_kernel gradient through RoPE (the inverse rotation) and the per-head RMSNorm
 //   attn_bwd_dot_kernel    D[q] = sum_i dO[q, i] O[q, i]
-//   attn_bwd_dkdv_kernel   dK, dV of the image keys: one wave per 32 keys, over every query of the
-//                          group's heads, P recomputed from the forward's log-sum-exp
+//   attn_bwd_dkdv_kernel   dK, dV of the image keys: four waves of 32 keys share each staged Q/dO
+//                          block, over every query of the group's heads; P recomputed from the
+//                          forward's log-sum-exp
 //   attn_bwd_dq_kernel     dQ: one wave per 32 queries, over every key (prefix and image)
 //   wgrad_kernel           C[n1, n2] += sum_m X[m, n1] Y[m, n2] (LoRA weight gradients), split over m
 //   x0_loss_kernel         squared error partial sums and dL/dx0
@@ -197,26 +198,28 @@ DEVI const bf16* kv_row(const SeqInfo& si, int b, int g, int j, int Hkv, int d, 
   return qkv + ((int64_t)b * si.N + (j - P)) * ldq + col0 + (int64_t)g * d;
 }
 
-// dK, dV of the image keys [P + 32 kb, +32) of (sequence b, kv head g).  S = Q K^T per 32
-// queries: A = Q rows (from LDS), B = K rows (registers).  dV^T += dO^T P and dK^T += Q^T dS with
-// the A operands read transposed from LDS.
+// dK, dV of the image keys of (sequence b, kv head g): a workgroup of four waves covers 128 keys,
+// wave w the 32 keys [128 kb + 32 w, +32).  Per 32-query block of each head of the group the
+// workgroup stages Q (normed, rotated) and dO in LDS once for its four waves; S = Q K^T takes A =
+// Q rows from LDS and B = the wave's K rows (registers); dV^T += dO^T P and dK^T += Q^T dS read
+// their A operands transposed from LDS.
 template <int D>
-__global__ __launch_bounds__(64) void attn_bwd_dkdv_kernel(const bf16* __restrict__ qkv, int64_t ldq, SeqInfo si,
-                                                           int Hq, int Hkv, const bf16* __restrict__ dO, int64_t ldo,
-                                                           const float* __restrict__ lse, const float* __restrict__ Dq,
-                                                           float scale_log2, float scale, float* __restrict__ dk,
-                                                           float* __restrict__ dv, int n_kb) {
+__global__ __launch_bounds__(256) void attn_bwd_dkdv_kernel(const bf16* __restrict__ qkv, int64_t ldq, SeqInfo si,
+                                                            int Hq, int Hkv, const bf16* __restrict__ dO, int64_t ldo,
+                                                            const float* __restrict__ lse, const float* __restrict__ Dq,
+                                                            float scale_log2, float scale, float* __restrict__ dk,
+                                                            float* __restrict__ dv, int n_kb) {
   constexpr int KS = D / 16, NDB = D / 32;
   __shared__ __attribute__((aligned(16))) bf16 sq[32][D];
   __shared__ __attribute__((aligned(16))) bf16 sdo[32][D];
-  const int lane = threadIdx.x, lr = lane & 31, lh = lane >> 5;
+  __shared__ float slse[32], sD[32];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, lr = lane & 31, lh = lane >> 5;
   const int kb = blockIdx.x % n_kb;
   const int g = (blockIdx.x / n_kb) % Hkv;
   const int b = blockIdx.x / (n_kb * Hkv);
-  const int N = si.N, P = si.plen[b], G = Hq / Hkv;
+  const int N = si.N, G = Hq / Hkv;
   const int QD = Hq * D;
-  const int key0 = 32 * kb;                          // image key index (token) of row 0
-  const int mykey = key0 + lr;
+  const int mykey = 128 * kb + 32 * wave + lr;        // image key index (token) of this lane's column
   const bool keyok = mykey < N;
   const int kc = keyok ? mykey : N - 1;
   bf16x8 kf[KS], vf[KS];
@@ -242,38 +245,39 @@ __global__ __launch_bounds__(64) void attn_bwd_dkdv_kernel(const bf16* __restric
     for (int qb = 0; qb < nqb; ++qb) {
       const int q0 = qb * 32;
       __syncthreads();
-      // stage the 32 query rows of Q (normed, rotated) and dO of head h
+      // 32 rows x D/8 chunks of 16 bytes, for each of Q and dO, over the 256 threads
 #pragma unroll
-      for (int c = 0; c < D / 16; ++c) {
-        const int idx = c * 64 + lane;                // 16-byte chunk index over 32 rows x D/8 chunks
+      for (int c = 0; c < D / 64; ++c) {
+        const int idx = c * 256 + tid;
         const int row = idx / (D / 8), ch = idx % (D / 8);
-        const int q = min(q0 + row, N - 1);
-        const int64_t tok = (int64_t)b * N + q;
+        const int64_t tok = (int64_t)b * N + min(q0 + row, N - 1);
         *(bf16x8*)&sq[row][ch * 8] = *(const bf16x8*)(qkv + tok * ldq + (int64_t)h * D + ch * 8);
         *(bf16x8*)&sdo[row][ch * 8] = *(const bf16x8*)(dO + tok * ldo + (int64_t)h * D + ch * 8);
       }
+      if (tid < 32) {
+        slse[tid] = lse_h[min(q0 + tid, N - 1)];
+        sD[tid] = D_h[min(q0 + tid, N - 1)];
+      }
       __syncthreads();
-      f32x16 s, dp;
+      f32x16 sv, dp;
 #pragma unroll
-      for (int e = 0; e < 16; ++e) { s[e] = 0.f; dp[e] = 0.f; }
+      for (int e = 0; e < 16; ++e) { sv[e] = 0.f; dp[e] = 0.f; }
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks) {
         const bf16x8 qa = *(const bf16x8*)&sq[lr][ks * 16 + lh * 8];
         const bf16x8 da = *(const bf16x8*)&sdo[lr][ks * 16 + lh * 8];
-        s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa, kf[ks], s, 0, 0, 0);
+        sv = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa, kf[ks], sv, 0, 0, 0);
         dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(da, vf[ks], dp, 0, 0, 0);
       }
       // P and dS (rows = queries q0 + (e/4)*8 + lh*4 + e%4, column = this lane's key)
       bf16x8 pf[2], dsf[2];
 #pragma unroll
       for (int e = 0; e < 16; ++e) {
-        const int q = q0 + (e >> 2) * 8 + lh * 4 + (e & 3);
-        const bool ok = keyok && q < N;
-        const int qc = min(q, N - 1);
-        const float p = ok ? __builtin_amdgcn_exp2f(s[e] * scale_log2 - lse_h[qc]) : 0.f;
-        const float ds = p * (dp[e] - D_h[qc]);
-        pf[e >> 3][e & 7] = static_cast<bf16>(p);
-        dsf[e >> 3][e & 7] = static_cast<bf16>(ds);
+        const int qr = (e >> 2) * 8 + lh * 4 + (e & 3);
+        const bool ok = keyok && q0 + qr < N;
+        const float pr = ok ? __builtin_amdgcn_exp2f(sv[e] * scale_log2 - slse[qr]) : 0.f;
+        pf[e >> 3][e & 7] = static_cast<bf16>(pr);
+        dsf[e >> 3][e & 7] = static_cast<bf16>(pr * (dp[e] - sD[qr]));
       }
 #pragma unroll
       for (int t = 0; t < 2; ++t)
@@ -302,7 +306,6 @@ __global__ __launch_bounds__(64) void attn_bwd_dkdv_kernel(const bf16* __restric
         dv[tok * Hkv * D + (int64_t)g * D + dd] = dvT[db][e];
       }
   }
-  (void)P;
 }
 
 // dQ of queries [32 qb, +32) of (sequence b, head h) over every key.  S^T = K Q^T: A = K rows,
@@ -530,11 +533,11 @@ hipError_t attention_bwd(const bf16* qkv, int64_t ldq, const SeqInfo& si, int Hq
   hipLaunchKernelGGL(attn_bwd_dot_kernel, dim3((unsigned)((tot + 3) / 4)), dim3(256), 0, s, dO, O, QD, Hq, d, N, Dq, tot);
   const float scale = 1.0f / sqrtf((float)d);
   const float scale_log2 = 1.4426950408889634f * scale;
-  const int nb = (N + 31) / 32;
-  hipLaunchKernelGGL(attn_bwd_dkdv_kernel<128>, dim3(B * Hkv * nb), dim3(64), 0, s, qkv, ldq, si, Hq, Hkv, dO, QD, lse,
-                     (const float*)Dq, scale_log2, scale, dk, dv, nb);
-  hipLaunchKernelGGL(attn_bwd_dq_kernel<128>, dim3(B * Hq * nb), dim3(64), 0, s, qkv, ldq, si, Hq, Hkv, dO, QD, lse,
-                     (const float*)Dq, scale_log2, scale, dq, nb);
+  const int nkb = (N + 127) / 128, nqb = (N + 31) / 32;
+  hipLaunchKernelGGL(attn_bwd_dkdv_kernel<128>, dim3(B * Hkv * nkb), dim3(256), 0, s, qkv, ldq, si, Hq, Hkv, dO, QD,
+                     lse, (const float*)Dq, scale_log2, scale, dk, dv, nkb);
+  hipLaunchKernelGGL(attn_bwd_dq_kernel<128>, dim3(B * Hq * nqb), dim3(64), 0, s, qkv, ldq, si, Hq, Hkv, dO, QD, lse,
+                     (const float*)Dq, scale_log2, scale, dq, nqb);
   return hipGetLastError();
 }
 
