@@ -300,6 +300,7 @@ def run_train_bench(psf, w, args):
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
+    psf.timing_begin("gate_up", w.n_layers * args.steps)
     start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     start.record()
     for _ in range(args.steps):
@@ -307,6 +308,10 @@ def run_train_bench(psf, w, args):
     stop.record()
     torch.cuda.synchronize()
     ms = start.elapsed_time(stop) / args.steps
+    gu_ms, gu_n = psf.timing_end()
+    gu_avg = gu_ms / max(gu_n, 1)
+    M_ = w.batch * w.n_tokens
+    gu_tf = 2 * M_ * d.hidden * 2 * d.mlp_intermediate / (gu_avg * 1e-3) / 1e12
     fl = train_flops(w)
     tokens = w.batch * w.n_tokens
     tflops = fl["total"] / (ms * 1e-3) / 1e12
@@ -322,6 +327,11 @@ def run_train_bench(psf, w, args):
                    "loss": float(loss.item())},
         "pct_bf16_peak": round(100 * tflops / PEAK_BF16_TFLOPS, 2), "tflops": round(tflops, 1),
         "step_tflop": round(fl["total"] / 1e12, 3),
+        "roofline": {"kernel": f"forward gate_up SwiGLU GEMM with its LoRA terms (M={M_}, N=2x{d.mlp_intermediate}, "
+                               f"K={d.hidden})",
+                     "bound": "mfma", "achieved": round(gu_tf, 1), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(gu_tf / PEAK_BF16_TFLOPS, 4), "traffic": None,
+                     "avg_launch_ms": round(gu_avg, 4), "launches_timed": gu_n},
     }
     print(json.dumps(out), flush=True)
 

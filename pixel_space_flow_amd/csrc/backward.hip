@@ -22,23 +22,49 @@ namespace psf {
 namespace {
 
 // ---------------------------------------------------------------- layout helpers
+// 64 x 64 tiles: rows come in as 16-byte pieces (8 columns), go out as 16-byte pieces of the
+// transposed rows; LDS rows padded by 8 elements keep the 16-byte writes aligned.  C and ldi,
+// ldo must be multiples of 8 for the vector path; other shapes use element accesses.
 __global__ __launch_bounds__(256) void transpose_kernel(const bf16* __restrict__ in, int64_t ldi, bf16* __restrict__ out,
                                                         int64_t ldo, int R, int C) {
-  __shared__ uint16_t tile[64][66];
+  __shared__ __attribute__((aligned(16))) uint16_t tile[64][72];
   const int r0 = blockIdx.y * 64, c0 = blockIdx.x * 64;
-  const int tx = threadIdx.x & 63, ty = threadIdx.x >> 6;
+  const int tid = threadIdx.x;
   const uint16_t* src = (const uint16_t*)in;
   uint16_t* dst = (uint16_t*)out;
+  const bool vec = (C % 8 == 0) && (R % 8 == 0) && (ldi % 8 == 0) && (ldo % 8 == 0);
 #pragma unroll
-  for (int i = 0; i < 16; ++i) {
-    const int r = r0 + ty + 4 * i, c = c0 + tx;
-    tile[ty + 4 * i][tx] = (r < R && c < C) ? src[(int64_t)r * ldi + c] : 0;
+  for (int i = 0; i < 2; ++i) {
+    const int rr = tid / 8 + 32 * i, cc = (tid % 8) * 8;
+    const int r = r0 + rr, c = c0 + cc;
+    if (vec) {
+      u32x4 v = {0, 0, 0, 0};
+      if (r < R && c < C) v = *(const u32x4*)(src + (int64_t)r * ldi + c);
+      *(u32x4*)&tile[rr][cc] = v;
+    } else {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) tile[rr][cc + e] = (r < R && c + e < C) ? src[(int64_t)r * ldi + c + e] : 0;
+    }
   }
   __syncthreads();
 #pragma unroll
-  for (int i = 0; i < 16; ++i) {
-    const int c = c0 + ty + 4 * i, r = r0 + tx;
-    if (c < C && r < R) dst[(int64_t)c * ldo + r] = tile[tx][ty + 4 * i];
+  for (int i = 0; i < 2; ++i) {
+    const int oc = tid / 8 + 32 * i, orr = (tid % 8) * 8;   // output row = input column c0 + oc
+    const int c = c0 + oc, r = r0 + orr;
+    if (c >= C) continue;
+    if (vec) {
+      if (r < R) {
+        uint16_t v[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) v[e] = tile[orr + e][oc];
+        u32x4 w;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) w[e] = (uint32_t)v[2 * e] | ((uint32_t)v[2 * e + 1] << 16);
+        *(u32x4*)(dst + (int64_t)c * ldo + r) = w;
+      }
+    } else {
+      for (int e = 0; e < 8 && r + e < R; ++e) dst[(int64_t)c * ldo + r + e] = tile[orr + e][oc];
+    }
   }
 }
 
