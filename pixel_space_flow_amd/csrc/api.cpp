@@ -146,6 +146,7 @@ size_t up(size_t x) { return (x + ALIGN - 1) / ALIGN * ALIGN; }
 
 struct Ws {
   size_t hidden, patches, u, qkv, attn, kc, vt, z, rope, temb, h1, x0, lora_t, hmid, skinny, lora_gu, lora_f32;
+  size_t splitk, splitk_floats;
   size_t m_idx, m_w, m_counts, m_offsets, m_perm, m_pos, m_tiles, m_z, m_y;
   size_t total;
   int Lpad, max_tiles, n_pos;
@@ -177,6 +178,9 @@ Ws layout(const gen_block_dims& d, int n_img, int n_br, int N, int max_prefix) {
   w.skinny = take(d.lora_rank > 0 ? skinny_part_floats((int)M, std::min(3 * d.lora_rank, 128)) * 4 : 0);
   w.lora_gu = take(d.lora_rank > 0 && d.mlp_intermediate > 0 ? M * 2 * d.mlp_intermediate * es : 0);
   w.lora_f32 = take(d.lora_rank > 0 ? M * qkv * 4 : 0);
+  // split-K partial products for small token counts (few row tiles leave CUs idle)
+  w.splitk_floats = M <= 2048 ? 4 * M * std::max(qkv, D) : 0;
+  w.splitk = take(w.splitk_floats * 4);
   if (d.n_experts > 0) {
     const size_t A = M * d.top_k;
     w.max_tiles = (int)(A / 256 + d.n_experts + 1);
@@ -298,6 +302,7 @@ int run_block(const gen_block_dims& d, const gen_block_weights& w, TH* hidden, c
     GemmParams p = gp();
     p.A = u; p.lda = D; p.B = w.w_qkv; p.ldb = D; p.M = M; p.N = QKV; p.K = D;
     p.C = qkv; p.ldc = QKV;
+    p.part = L.splitk_floats ? at<float>(ws, L.splitk) : nullptr; p.part_floats = L.splitk_floats;
     int epi = EPI_STORE;
     if (lora) {
       const int sites[3] = {0, 1, 2}, ends[3] = {QD, QD + Hkv * hd, QKV};
@@ -349,6 +354,7 @@ int run_block(const gen_block_dims& d, const gen_block_weights& w, TH* hidden, c
     GemmParams p = gp();
     p.A = attn; p.lda = QD; p.B = w.w_o; p.ldb = QD; p.M = M; p.N = D; p.K = QD;
     p.C = hmid; p.ldc = D; p.R = hidden; p.ldr = D;
+    p.part = L.splitk_floats ? at<float>(ws, L.splitk) : nullptr; p.part_floats = L.splitk_floats;
     const int sites[1] = {3}, ends[1] = {D};
     int off[1] = {-1}, ldt = 0;
     if (lora) HIP_TRY(lora_down<T>(d, w, sites, 1, attn, QD, M, lt, off, ldt, s, at<float>(ws, L.skinny)));
@@ -383,6 +389,7 @@ int run_block(const gen_block_dims& d, const gen_block_weights& w, TH* hidden, c
       GemmParams p = gp();
       p.A = z; p.lda = I; p.B = w.w_down; p.ldb = I; p.M = M; p.N = D; p.K = I;
       p.C = hidden; p.ldc = D; p.R = hmid; p.ldr = D;
+      p.part = L.splitk_floats ? at<float>(ws, L.splitk) : nullptr; p.part_floats = L.splitk_floats;
       const int sites[1] = {6}, ends[1] = {D};
       int off[1] = {-1}, ldt = 0;
       bool post = false;

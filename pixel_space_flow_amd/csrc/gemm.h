@@ -16,6 +16,7 @@ enum GemmEpi {
   EPI_RESID_FROM_F32 = 7,  // C (bf16) = R (fp32) + acc     block output
   EPI_RESID_F32 = 8,       // C (fp32) = R (fp32) + acc     fp32 residual stream (may alias)
   EPI_BIAS_BCAST_F32 = 9,  // as EPI_BIAS_BCAST with an fp32 C
+  EPI_PARTIAL_F32 = 10,    // C (fp32) = acc over one k-range of a split-K launch (C + split * M * ldc)
 };
 
 struct GemmParams {
@@ -38,6 +39,9 @@ struct GemmParams {
   int img_H, img_W;                  // EPI_F32_IMG: images of img_H x img_W pixels, rows_per tokens each
   // grouped GEMM (MoE experts): tiles[3*t] = expert, first row, rows
   const int* tiles; int max_tiles; int64_t b_expert_stride;
+  // split-K for grids that leave CUs idle (few row tiles): scratch for ksplit fp32 partial
+  // products; without it (part == nullptr) the GEMM runs unsplit
+  int ksplit; float* part; size_t part_floats;
 };
 
 // Launchers (return hipError_t of the launch).

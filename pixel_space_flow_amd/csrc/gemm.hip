@@ -343,7 +343,7 @@ DEVI void epi_row16(const GemmParams& p, int row, int col0, int ncols, float* v)
     for (int j = 0; j < 16; ++j) v[j] *= p.scale;
   }
   // output
-  if (EPI == EPI_RESID_TO_F32 || EPI == EPI_RESID_F32) {
+  if (EPI == EPI_RESID_TO_F32 || EPI == EPI_RESID_F32 || EPI == EPI_PARTIAL_F32) {
     float* C = (float*)p.C + (int64_t)row * p.ldc + col0;
     if (full) {
 #pragma unroll
@@ -622,7 +622,7 @@ __global__ __launch_bounds__(512, 1) void gemm_k32_kernel(GemmParams p, int n_co
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wave >> 2, wn = wave & 3;
 
-  int tn, row0, rows, expert = 0;
+  int tn, row0, rows, expert = 0, split = 0;
   if (GROUPED) {
     const int t = blockIdx.x / n_col_tiles;
     tn = blockIdx.x - t * n_col_tiles;
@@ -633,7 +633,9 @@ __global__ __launch_bounds__(512, 1) void gemm_k32_kernel(GemmParams p, int n_co
   } else {
     const int n_m = (p.M + BM - 1) / BM;
     const int n_t = n_m * n_col_tiles;
-    const int id = xcd_remap(blockIdx.x, n_t);
+    const int idall = xcd_remap(blockIdx.x, n_t * max(p.ksplit, 1));
+    split = idall / n_t;                               // k-range of a split-K launch (else 0)
+    const int id = idall - split * n_t;
     const int GROUP = 8;
     const int per_group = GROUP * n_col_tiles;
     const int g = id / per_group;
@@ -644,6 +646,7 @@ __global__ __launch_bounds__(512, 1) void gemm_k32_kernel(GemmParams p, int n_co
     row0 = (first_m + r_in % gsz) * BM;
     rows = min(BM, p.M - row0);
   }
+  if (EPI == EPI_PARTIAL_F32) p.C = (float*)p.C + (int64_t)split * p.M * p.ldc;
   // LDS rows are 64 B (4 chunks of 16 B).  ds_read_b128 serves 16 lanes per cycle over a 256 B
   // (64-bank) window, i.e. four rows; chunk c of row r is stored at c ^ ((r >> 2) & 3), so the 16
   // rows read together at one logical chunk occupy 16 distinct slots.  One DMA instruction fills
@@ -686,14 +689,15 @@ __global__ __launch_bounds__(512, 1) void gemm_k32_kernel(GemmParams p, int n_co
   }
   const uint32_t bvoff = lrow * ldb2 + lch * 16;
 
-  const int KT = p.K / KB;
+  const int KT = p.K / KB / max(p.ksplit, 1);
+  const uint32_t kofs = (uint32_t)(split * KT) * ROWB;   // byte offset of this launch's k-range
   // Half h of the DMA of k-tile t (row groups 2w + h of A and of B) into stage t % 4.  Tiles past
   // the end reload the last one into a stage nobody reads again, so every k-step sends the same
   // number of loads and the vmcnt arithmetic below holds throughout.
   auto dma_half = [&](int t, int h) {
     char* As = smem + (t & (NST - 1)) * STG;
     char* Bs = As + BM * ROWB;
-    const uint32_t kb = (uint32_t)min(t, KT - 1) * ROWB;
+    const uint32_t kb = (uint32_t)min(t, KT - 1) * ROWB + kofs;
     const int g = 2 * wave + h;
     if (GATHER)
       dma16(ra, As + g * 1024, avoff[h], kb);
@@ -980,6 +984,7 @@ hipError_t launch_fast(const GemmParams& p, int epi, int grid, int n_col_tiles, 
     PSF_L(EPI_RESID_FROM_F32)
     PSF_L(EPI_RESID_F32)
     PSF_L(EPI_BIAS_BCAST_F32)
+    PSF_L(EPI_PARTIAL_F32)
   }
 #undef PSF_L
   return hipErrorInvalidValue;
@@ -1014,10 +1019,69 @@ hipError_t launch_bf16(const GemmParams& p, int epi, int grid, int n_col_tiles, 
 
 }  // namespace
 
+// Split-K: the sum of the ksplit fp32 partial products goes through the requested epilogue.
+template <int EPI>
+__global__ __launch_bounds__(256) void splitk_reduce_kernel(GemmParams p, int ks) {
+  const int64_t i = ((int64_t)blockIdx.x * 256 + threadIdx.x) * 4;
+  const int64_t total = (int64_t)p.M * p.N;
+  if (i >= total) return;
+  const int64_t m = i / p.N;
+  const int n = (int)(i - m * p.N);                  // N is a multiple of 4: a float4 stays in one row
+  float4 a = *(const float4*)(p.part + i);
+  for (int z = 1; z < ks; ++z) {
+    const float4 b = *(const float4*)(p.part + (int64_t)z * total + i);
+    a.x += b.x; a.y += b.y; a.z += b.z; a.w += b.w;
+  }
+  float v[4] = {a.x, a.y, a.z, a.w};
+  if (EPI == EPI_SCALED)
+    for (int j = 0; j < 4; ++j) v[j] *= p.scale;
+  if (EPI == EPI_RESID || EPI == EPI_RESID_TO_F32)
+    for (int j = 0; j < 4; ++j) v[j] += static_cast<float>(((const bf16*)p.R)[m * p.ldr + n + j]);
+  if (EPI == EPI_RESID_F32 || EPI == EPI_RESID_FROM_F32)
+    for (int j = 0; j < 4; ++j) v[j] += ((const float*)p.R)[m * p.ldr + n + j];
+  if (EPI == EPI_RESID_F32 || EPI == EPI_RESID_TO_F32) {
+    for (int j = 0; j < 4; ++j) ((float*)p.C)[m * p.ldc + n + j] = v[j];
+  } else {
+    for (int j = 0; j < 4; ++j) ((bf16*)p.C)[m * p.ldc + n + j] = static_cast<bf16>(v[j]);
+  }
+}
+
+// Number of k-ranges for a plain GEMM whose row x column tiles leave most CUs idle (0 = unsplit).
+int splitk_choice(const GemmParams& p, int epi, int tiles) {
+  if (!p.part || p.X || p.bmode != 0 || p.a_rows || p.N % 4) return 0;
+  if (epi != EPI_STORE && epi != EPI_RESID && epi != EPI_SCALED && epi != EPI_RESID_F32 && epi != EPI_RESID_TO_F32 &&
+      epi != EPI_RESID_FROM_F32)
+    return 0;
+  if (tiles >= 160) return 0;
+  for (int ks = 4; ks >= 2; --ks) {
+    if (p.K % (32 * ks) || p.K / ks < 512) continue;
+    if ((size_t)ks * p.M * p.N > p.part_floats) continue;
+    return ks;
+  }
+  return 0;
+}
+
 hipError_t gemm_bf16(const GemmParams& p, int epi, hipStream_t s) {
   if (p.M <= 0) return hipSuccess;
   const int n_cols = (epi == EPI_SWIGLU) ? (p.swiglu_I + BN / 2 - 1) / (BN / 2) : (p.N + BN - 1) / BN;
   const int n_m = (p.M + BM - 1) / BM;
+  if (const int ks = splitk_choice(p, epi, n_m * n_cols)) {
+    GemmParams q = p;
+    q.ksplit = ks; q.C = p.part; q.ldc = p.N;
+    hipError_t e = launch_fast<false, false>(q, EPI_PARTIAL_F32, n_m * n_cols * ks, n_cols, s);
+    if (e != hipSuccess) return e;
+    const int64_t n4 = ((int64_t)p.M * p.N + 3) / 4;
+    const dim3 grid((unsigned)((n4 + 255) / 256));
+    switch (epi) {
+      case EPI_STORE: hipLaunchKernelGGL(splitk_reduce_kernel<EPI_STORE>, grid, dim3(256), 0, s, p, ks); break;
+      case EPI_RESID: hipLaunchKernelGGL(splitk_reduce_kernel<EPI_RESID>, grid, dim3(256), 0, s, p, ks); break;
+      case EPI_SCALED: hipLaunchKernelGGL(splitk_reduce_kernel<EPI_SCALED>, grid, dim3(256), 0, s, p, ks); break;
+      case EPI_RESID_F32: hipLaunchKernelGGL(splitk_reduce_kernel<EPI_RESID_F32>, grid, dim3(256), 0, s, p, ks); break;
+      case EPI_RESID_TO_F32: hipLaunchKernelGGL(splitk_reduce_kernel<EPI_RESID_TO_F32>, grid, dim3(256), 0, s, p, ks); break;
+      default: hipLaunchKernelGGL(splitk_reduce_kernel<EPI_RESID_FROM_F32>, grid, dim3(256), 0, s, p, ks); break;
+    }
+    return hipGetLastError();
+  }
   if (p.X && p.xk > 0) return launch_bf16<false, true>(p, epi, n_m * n_cols, n_cols, s);
   if (p.bmode == 2) return launch_bf16<false, false>(p, epi, n_m * n_cols, n_cols, s);
   if (p.a_rows) return launch_fast<false, true>(p, epi, n_m * n_cols, n_cols, s);
