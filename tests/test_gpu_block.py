@@ -186,3 +186,26 @@ def test_block_determinism(lib):
     a = run_gpu_block(lib, w, wts, h, pk, pv, "bf16")
     b = run_gpu_block(lib, w, wts, h, pk, pv, "bf16")
     assert np.array_equal(a, b)
+
+
+def test_split_k_ragged_rows(lib):
+    """Few row tiles (3 x 99 = 297 tokens of the 8B block): the QKV, O and down projections split K
+    four ways; ragged rows, prefixes of different lengths (one empty)."""
+    import torch
+    w = W.scaled(W.CONFIGS[1], height=32 * 9, width=32 * 11, prefix_len=0, n_br=3)
+    d = w.dims
+    wts = W.layer_weights(w, 0, 4, "bf16")
+    h = W.block_hidden(w, 4, "bf16")
+    lens = [400, 0, 37]
+    pk = [W.maybe_bf16(W.normal(1, 4, f"spk{b}", (lens[b], d.n_kv_heads, d.head_dim)), "bf16") for b in range(3)]
+    pv = [W.maybe_bf16(W.normal(1, 4, f"spv{b}", (lens[b], d.n_kv_heads, d.head_dim)), "bf16") for b in range(3)]
+    log(f"split-K block: B=3 N={h.shape[1]} prefixes {lens}")
+    dims = lib.make_dims(d, lib.GEN_BF16)
+    hd = dev(h, "f32")
+    ws = lib.alloc_workspace(lib.workspace_size(dims, 1, 3, h.shape[1], max(lens)))
+    wd = weights_to_dev(wts, "bf16")
+    pkd = [dev(p, "bf16") if p.size else None for p in pk]
+    pvd = [dev(p, "bf16") if p.size else None for p in pv]
+    lib.block_forward(dims, lib.make_weights(wd), hd, pkd, pvd, lens, ws)
+    torch.cuda.synchronize()
+    check(host(hd), O.gen_block(h, wts, d, pk, pv), h, BLOCK_TOL, "split-K ragged")
