@@ -10,9 +10,10 @@
 //   qknorm_rope_bwd_kernel gradient through RoPE (the inverse rotation) and the per-head RMSNorm
 //   attn_bwd_dot_kernel    D[q] = sum_i dO[q, i] O[q, i]
 //   attn_bwd_dkdv_kernel   dK, dV of the image keys: four waves of 32 keys share each staged Q/dO
-//                          block, over every query of the group's heads; P recomputed from the
-//                          forward's log-sum-exp
-//   attn_bwd_dq_kernel     dQ: one wave per 32 queries, over every key (prefix and image)
+//                          block (double buffered), over every query of the group's heads; P
+//                          recomputed from the forward's log-sum-exp
+//   attn_bwd_dq_kernel     dQ: four waves (query heads of one kv head) share each staged K/V tile
+//                          (double buffered), over every key (prefix and image)
 //   wgrad_kernel           C[n1, n2] += sum_m X[m, n1] Y[m, n2] (LoRA weight gradients), split over m
 //   x0_loss_kernel         squared error partial sums and dL/dx0
 #include "common.h"
@@ -213,7 +214,32 @@ __global__ __launch_bounds__(256) void attn_bwd_dot_kernel(const bf16* __restric
 // (P or dS as the B operand) takes the accumulator values e = 8t .. 8t+7 as k-step t, which
 // visits k in the order 16t + (i/4)*8 + (l/32)*4 + i%4; its A operand is read from LDS in that
 // same order.
-DEVI int perm_k(int t, int i, int lh) { return 16 * t + (i >> 2) * 8 + lh * 4 + (i & 3); }
+//
+// Staged [32][128] bf16 tiles (Q and dO, or K) keep rows of 16 chunks of 16 bytes; logical chunk c
+// of row r sits at c ^ f(r), f(r) = 4 (r & 3) + ((r >> 2) & 3).  A row read (16 lanes, 16
+// consecutive rows, one chunk each) then meets 16 distinct chunks, and a transposed read (16
+// lanes, 4 consecutive rows, 32 bytes of each) meets 4 disjoint chunk pairs: no bank conflicts.
+DEVI int tile_off(int r, int c) { return r * 128 + ((((c >> 3) ^ ((r & 3) << 2) ^ ((r >> 2) & 3))) << 3) + (c & 7); }
+
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) s16x4* lds_s16x4;
+
+// A operand of k-step t, column block db (32 columns), from a staged tile read transposed:
+// lane l gets tile[16t + (i/4)*8 + (l/32)*4 + i%4][32 db + l%32] for i = 0..7.  ds_read_tr16_b64 hands lane j
+// of each 16-lane group element j%4 of the 8-byte pieces addressed by lanes 4k + j/4, k = 0..3; so
+// lane j addresses row 16t + 8h + 4(l/32) + j/4, columns 32 db + 16 ((l/16) & 1) + 4 (j%4) .. +3,
+// and the two reads (h = 0, 1) give slots 0-3 and 4-7.
+DEVI bf16x8 tile_tr(const bf16* tile, int t, int db, int lane) {
+  const int j = lane & 15, lh = lane >> 5;
+  const int c = db * 32 + ((lane >> 4) & 1) * 16 + 4 * (j & 3);
+  const int r0 = 16 * t + 4 * lh + (j >> 2);
+  const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4)(tile + tile_off(r0, c)));
+  const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4)(tile + tile_off(r0 + 8, c)));
+  const s16x4 x[2] = {lo, hi};
+  bf16x8 f;
+  __builtin_memcpy(&f, x, 16);
+  return f;
+}
 
 // Row pointer of key j (sequence b, kv head g) in the K or V source: the prefix cache for j < P,
 // the normed (K) or raw (V) image projections in qkv otherwise.
@@ -225,20 +251,22 @@ DEVI const bf16* kv_row(const SeqInfo& si, int b, int g, int j, int Hkv, int d, 
 }
 
 // dK, dV of the image keys of (sequence b, kv head g): a workgroup of four waves covers 128 keys,
-// wave w the 32 keys [128 kb + 32 w, +32).  Per 32-query block of each head of the group the
-// workgroup stages Q (normed, rotated) and dO in LDS once for its four waves; S = Q K^T takes A =
-// Q rows from LDS and B = the wave's K rows (registers); dV^T += dO^T P and dK^T += Q^T dS read
-// their A operands transposed from LDS.
+// wave w the 32 keys [128 kb + 32 w, +32).  The workgroup walks the 32-query blocks of every head
+// of the group; each block's Q (normed, rotated), dO, log-sum-exp and D are staged once in LDS for
+// the four waves (two stages: the next block is loaded into registers while this one is used).
+// S = Q K^T takes A = Q rows from LDS and B = the wave's K rows (registers); dV^T += dO^T P and
+// dK^T += Q^T dS read their A operands transposed from LDS.
 template <int D>
 __global__ __launch_bounds__(256) void attn_bwd_dkdv_kernel(const bf16* __restrict__ qkv, int64_t ldq, SeqInfo si,
                                                             int Hq, int Hkv, const bf16* __restrict__ dO, int64_t ldo,
                                                             const float* __restrict__ lse, const float* __restrict__ Dq,
                                                             float scale_log2, float scale, float* __restrict__ dk,
                                                             float* __restrict__ dv, int n_kb) {
+  static_assert(D == 128, "staged tiles are 32 x 128");
   constexpr int KS = D / 16, NDB = D / 32;
-  __shared__ __attribute__((aligned(16))) bf16 sq[32][D];
-  __shared__ __attribute__((aligned(16))) bf16 sdo[32][D];
-  __shared__ float slse[32], sD[32];
+  __shared__ __attribute__((aligned(16))) bf16 sq[2][32 * D];
+  __shared__ __attribute__((aligned(16))) bf16 sdo[2][32 * D];
+  __shared__ float slse[2][32], sD[2][32];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, lr = lane & 31, lh = lane >> 5;
   const int kb = blockIdx.x % n_kb;
   const int g = (blockIdx.x / n_kb) % Hkv;
@@ -263,63 +291,77 @@ __global__ __launch_bounds__(256) void attn_bwd_dkdv_kernel(const bf16* __restri
   for (int i = 0; i < NDB; ++i)
 #pragma unroll
     for (int e = 0; e < 16; ++e) { dkT[i][e] = 0.f; dvT[i][e] = 0.f; }
-  const int nqb = (N + 31) / 32;
-  for (int hi = 0; hi < G; ++hi) {
-    const int h = g * G + hi;
-    const float* lse_h = lse + ((int64_t)b * Hq + h) * N;
-    const float* D_h = Dq + ((int64_t)b * Hq + h) * N;
-    for (int qb = 0; qb < nqb; ++qb) {
-      const int q0 = qb * 32;
-      __syncthreads();
-      // 32 rows x D/8 chunks of 16 bytes, for each of Q and dO, over the 256 threads
+  const int nqb = (N + 31) / 32, nblk = G * nqb;
+
+  // staging of block it = (head g G + it / nqb, queries 32 (it % nqb) ..): thread tid moves chunks
+  // tid and tid + 256 of Q and of dO (row = chunk / 16); threads 0-31 the lse, 32-63 the D values
+  bf16x8 rq[2], rd[2];
+  float rs = 0.f;
+  auto fetch = [&](int it) {
+    const int h = g * G + it / nqb, q0 = (it % nqb) * 32;
 #pragma unroll
-      for (int c = 0; c < D / 64; ++c) {
-        const int idx = c * 256 + tid;
-        const int row = idx / (D / 8), ch = idx % (D / 8);
-        const int64_t tok = (int64_t)b * N + min(q0 + row, N - 1);
-        *(bf16x8*)&sq[row][ch * 8] = *(const bf16x8*)(qkv + tok * ldq + (int64_t)h * D + ch * 8);
-        *(bf16x8*)&sdo[row][ch * 8] = *(const bf16x8*)(dO + tok * ldo + (int64_t)h * D + ch * 8);
-      }
-      if (tid < 32) {
-        slse[tid] = lse_h[min(q0 + tid, N - 1)];
-        sD[tid] = D_h[min(q0 + tid, N - 1)];
-      }
-      __syncthreads();
-      f32x16 sv, dp;
-#pragma unroll
-      for (int e = 0; e < 16; ++e) { sv[e] = 0.f; dp[e] = 0.f; }
-#pragma unroll
-      for (int ks = 0; ks < KS; ++ks) {
-        const bf16x8 qa = *(const bf16x8*)&sq[lr][ks * 16 + lh * 8];
-        const bf16x8 da = *(const bf16x8*)&sdo[lr][ks * 16 + lh * 8];
-        sv = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa, kf[ks], sv, 0, 0, 0);
-        dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(da, vf[ks], dp, 0, 0, 0);
-      }
-      // P and dS (rows = queries q0 + (e/4)*8 + lh*4 + e%4, column = this lane's key)
-      bf16x8 pf[2], dsf[2];
-#pragma unroll
-      for (int e = 0; e < 16; ++e) {
-        const int qr = (e >> 2) * 8 + lh * 4 + (e & 3);
-        const bool ok = keyok && q0 + qr < N;
-        const float pr = ok ? __builtin_amdgcn_exp2f(sv[e] * scale_log2 - slse[qr]) : 0.f;
-        pf[e >> 3][e & 7] = static_cast<bf16>(pr);
-        dsf[e >> 3][e & 7] = static_cast<bf16>(pr * (dp[e] - sD[qr]));
-      }
-#pragma unroll
-      for (int t = 0; t < 2; ++t)
-#pragma unroll
-        for (int db = 0; db < NDB; ++db) {
-          bf16x8 at, aq;
-#pragma unroll
-          for (int i = 0; i < 8; ++i) {
-            const int r = perm_k(t, i, lh);
-            at[i] = sdo[r][db * 32 + lr];
-            aq[i] = sq[r][db * 32 + lr];
-          }
-          dvT[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(at, pf[t], dvT[db], 0, 0, 0);
-          dkT[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(aq, dsf[t], dkT[db], 0, 0, 0);
-        }
+    for (int c = 0; c < 2; ++c) {
+      const int idx = c * 256 + tid, row = idx >> 4, ch = idx & 15;
+      const int64_t tok = (int64_t)b * N + min(q0 + row, N - 1);
+      rq[c] = *(const bf16x8*)(qkv + tok * ldq + (int64_t)h * D + ch * 8);
+      rd[c] = *(const bf16x8*)(dO + tok * ldo + (int64_t)h * D + ch * 8);
     }
+    if (tid < 64) {
+      const int64_t o = ((int64_t)b * Hq + h) * N + min(q0 + (tid & 31), N - 1);
+      rs = tid < 32 ? lse[o] : Dq[o];
+    }
+  };
+  auto stage = [&](int st) {
+#pragma unroll
+    for (int c = 0; c < 2; ++c) {
+      const int idx = c * 256 + tid, row = idx >> 4, ch = idx & 15;
+      *(bf16x8*)&sq[st][tile_off(row, ch * 8)] = rq[c];
+      *(bf16x8*)&sdo[st][tile_off(row, ch * 8)] = rd[c];
+    }
+    if (tid < 32) slse[st][tid] = rs;
+    else if (tid < 64) sD[st][tid - 32] = rs;
+  };
+  fetch(0);
+  stage(0);
+  if (nblk > 1) fetch(1);
+  __syncthreads();
+  for (int it = 0; it < nblk; ++it) {
+    const int st = it & 1;
+    const int q0 = (it % nqb) * 32;
+    if (it + 1 < nblk) {
+      stage(st ^ 1);                     // every wave left stage st ^ 1 at the last barrier
+      if (it + 2 < nblk) fetch(it + 2);
+    }
+    const bf16* Qs = sq[st];
+    const bf16* Ds = sdo[st];
+    f32x16 sv, dp;
+#pragma unroll
+    for (int e = 0; e < 16; ++e) { sv[e] = 0.f; dp[e] = 0.f; }
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      const bf16x8 qa = *(const bf16x8*)&Qs[tile_off(lr, ks * 16 + lh * 8)];
+      const bf16x8 da = *(const bf16x8*)&Ds[tile_off(lr, ks * 16 + lh * 8)];
+      sv = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa, kf[ks], sv, 0, 0, 0);
+      dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(da, vf[ks], dp, 0, 0, 0);
+    }
+    // P and dS (rows = queries q0 + (e/4)*8 + lh*4 + e%4, column = this lane's key)
+    bf16x8 pf[2], dsf[2];
+#pragma unroll
+    for (int e = 0; e < 16; ++e) {
+      const int qr = (e >> 2) * 8 + lh * 4 + (e & 3);
+      const bool ok = keyok && q0 + qr < N;
+      const float pr = ok ? __builtin_amdgcn_exp2f(sv[e] * scale_log2 - slse[st][qr]) : 0.f;
+      pf[e >> 3][e & 7] = static_cast<bf16>(pr);
+      dsf[e >> 3][e & 7] = static_cast<bf16>(pr * (dp[e] - sD[st][qr]));
+    }
+#pragma unroll
+    for (int t = 0; t < 2; ++t)
+#pragma unroll
+      for (int db = 0; db < NDB; ++db) {
+        dvT[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tile_tr(Ds, t, db, lane), pf[t], dvT[db], 0, 0, 0);
+        dkT[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tile_tr(Qs, t, db, lane), dsf[t], dkT[db], 0, 0, 0);
+      }
+    __syncthreads();
   }
   if (keyok) {
     const int64_t tok = (int64_t)b * N + mykey;
@@ -334,24 +376,32 @@ __global__ __launch_bounds__(256) void attn_bwd_dkdv_kernel(const bf16* __restri
   }
 }
 
-// dQ of queries [32 qb, +32) of (sequence b, head h) over every key.  S^T = K Q^T: A = K rows,
-// B = Q rows (registers); dP^T = V dO^T likewise; dQ^T += K^T dS^T with K^T read from LDS.
+// dQ over every key (prefix and image).  A workgroup of four waves shares one (sequence b, kv head
+// g): wave w takes head g G + hg hpw + w % hpw and the 32 queries of block qg (4 / hpw) + w / hpw,
+// hpw = the heads per workgroup (4, 2 or 1 as the group size allows).  Tiles of 32 keys of K and V
+// are staged once in LDS for the four waves (two stages: the next tile is loaded into registers
+// while this one is used).  S^T = K Q^T and dP^T = V dO^T take A = K or V rows from LDS and B = the
+// wave's Q or dO rows (registers); dQ^T += K^T dS^T reads K^T transposed from LDS.
 template <int D>
-__global__ __launch_bounds__(64) void attn_bwd_dq_kernel(const bf16* __restrict__ qkv, int64_t ldq, SeqInfo si, int Hq,
-                                                         int Hkv, const bf16* __restrict__ dO, int64_t ldo,
-                                                         const float* __restrict__ lse, const float* __restrict__ Dq,
-                                                         float scale_log2, float scale, float* __restrict__ dq,
-                                                         int n_qb) {
+__global__ __launch_bounds__(256) void attn_bwd_dq_kernel(const bf16* __restrict__ qkv, int64_t ldq, SeqInfo si, int Hq,
+                                                          int Hkv, const bf16* __restrict__ dO, int64_t ldo,
+                                                          const float* __restrict__ lse, const float* __restrict__ Dq,
+                                                          float scale_log2, float scale, float* __restrict__ dq,
+                                                          int hpw, int n_qg) {
+  static_assert(D == 128, "staged tiles are 32 x 128");
   constexpr int KS = D / 16, NDB = D / 32;
-  __shared__ __attribute__((aligned(16))) bf16 sk[32][D];
-  const int lane = threadIdx.x, lr = lane & 31, lh = lane >> 5;
-  const int qb = blockIdx.x % n_qb;
-  const int h = (blockIdx.x / n_qb) % Hq;
-  const int b = blockIdx.x / (n_qb * Hq);
+  __shared__ __attribute__((aligned(16))) bf16 sk[2][32 * D];
+  __shared__ __attribute__((aligned(16))) bf16 sv[2][32 * D];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, lr = lane & 31, lh = lane >> 5;
+  const int G = Hq / Hkv, n_hg = G / hpw;
+  const int qg = blockIdx.x % n_qg;
+  const int hg = (blockIdx.x / n_qg) % n_hg;
+  const int g = (blockIdx.x / (n_qg * n_hg)) % Hkv;
+  const int b = blockIdx.x / (n_qg * n_hg * Hkv);
   const int N = si.N, P = si.plen[b], L = P + N;
-  const int g = h / (Hq / Hkv);
+  const int h = g * G + hg * hpw + wave % hpw;
   const int QD = Hq * D;
-  const int myq = 32 * qb + lr;
+  const int myq = (qg * (4 / hpw) + wave / hpw) * 32 + lr;
   const bool qok = myq < N;
   const int64_t tok = (int64_t)b * N + min(myq, N - 1);
   bf16x8 qf[KS], df[KS];
@@ -367,24 +417,49 @@ __global__ __launch_bounds__(64) void attn_bwd_dq_kernel(const bf16* __restrict_
   for (int i = 0; i < NDB; ++i)
 #pragma unroll
     for (int e = 0; e < 16; ++e) dqT[i][e] = 0.f;
-  for (int j0 = 0; j0 < L; j0 += 32) {
-    const int jc = min(j0 + lr, L - 1);
-    const bf16* kp = kv_row(si, b, g, jc, Hkv, D, qkv, ldq, QD, false) + lh * 8;
-    const bf16* vp = kv_row(si, b, g, jc, Hkv, D, qkv, ldq, QD + Hkv * D, true) + lh * 8;
-    bf16x8 kf[KS];
+
+  // staging of key tile t (keys 32 t ..): thread tid moves chunks tid and tid + 256 of K and of V
+  const int ntile = (L + 31) / 32;
+  bf16x8 rk[2], rv[2];
+  auto fetch = [&](int t) {
+#pragma unroll
+    for (int c = 0; c < 2; ++c) {
+      const int idx = c * 256 + tid, row = idx >> 4, ch = idx & 15;
+      const int j = min(32 * t + row, L - 1);
+      rk[c] = *(const bf16x8*)(kv_row(si, b, g, j, Hkv, D, qkv, ldq, QD, false) + ch * 8);
+      rv[c] = *(const bf16x8*)(kv_row(si, b, g, j, Hkv, D, qkv, ldq, QD + Hkv * D, true) + ch * 8);
+    }
+  };
+  auto stage = [&](int st) {
+#pragma unroll
+    for (int c = 0; c < 2; ++c) {
+      const int idx = c * 256 + tid, row = idx >> 4, ch = idx & 15;
+      *(bf16x8*)&sk[st][tile_off(row, ch * 8)] = rk[c];
+      *(bf16x8*)&sv[st][tile_off(row, ch * 8)] = rv[c];
+    }
+  };
+  fetch(0);
+  stage(0);
+  if (ntile > 1) fetch(1);
+  __syncthreads();
+  for (int t = 0; t < ntile; ++t) {
+    const int st = t & 1, j0 = 32 * t;
+    if (t + 1 < ntile) {
+      stage(st ^ 1);                     // every wave left stage st ^ 1 at the last barrier
+      if (t + 2 < ntile) fetch(t + 2);
+    }
+    const bf16* Ks = sk[st];
+    const bf16* Vs = sv[st];
     f32x16 s, dp;
 #pragma unroll
     for (int e = 0; e < 16; ++e) { s[e] = 0.f; dp[e] = 0.f; }
-    __syncthreads();
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
-      kf[ks] = *(const bf16x8*)(kp + ks * 16);
-      const bf16x8 vv = *(const bf16x8*)(vp + ks * 16);
-      *(bf16x8*)&sk[lr][ks * 16 + lh * 8] = kf[ks];
-      s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[ks], qf[ks], s, 0, 0, 0);
-      dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vv, df[ks], dp, 0, 0, 0);
+      const bf16x8 ka = *(const bf16x8*)&Ks[tile_off(lr, ks * 16 + lh * 8)];
+      const bf16x8 va = *(const bf16x8*)&Vs[tile_off(lr, ks * 16 + lh * 8)];
+      s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, qf[ks], s, 0, 0, 0);
+      dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, df[ks], dp, 0, 0, 0);
     }
-    __syncthreads();
     bf16x8 dsf[2];
 #pragma unroll
     for (int e = 0; e < 16; ++e) {
@@ -393,14 +468,11 @@ __global__ __launch_bounds__(64) void attn_bwd_dq_kernel(const bf16* __restrict_
       dsf[e >> 3][e & 7] = static_cast<bf16>(p * (dp[e] - my_D));
     }
 #pragma unroll
-    for (int t = 0; t < 2; ++t)
+    for (int tk = 0; tk < 2; ++tk)
 #pragma unroll
-      for (int db = 0; db < NDB; ++db) {
-        bf16x8 ak;
-#pragma unroll
-        for (int i = 0; i < 8; ++i) ak[i] = sk[perm_k(t, i, lh)][db * 32 + lr];
-        dqT[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ak, dsf[t], dqT[db], 0, 0, 0);
-      }
+      for (int db = 0; db < NDB; ++db)
+        dqT[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tile_tr(Ks, tk, db, lane), dsf[tk], dqT[db], 0, 0, 0);
+    __syncthreads();
   }
   if (qok) {
 #pragma unroll
@@ -562,8 +634,10 @@ hipError_t attention_bwd(const bf16* qkv, int64_t ldq, const SeqInfo& si, int Hq
   const int nkb = (N + 127) / 128, nqb = (N + 31) / 32;
   hipLaunchKernelGGL(attn_bwd_dkdv_kernel<128>, dim3(B * Hkv * nkb), dim3(256), 0, s, qkv, ldq, si, Hq, Hkv, dO, QD,
                      lse, (const float*)Dq, scale_log2, scale, dk, dv, nkb);
-  hipLaunchKernelGGL(attn_bwd_dq_kernel<128>, dim3(B * Hq * nqb), dim3(64), 0, s, qkv, ldq, si, Hq, Hkv, dO, QD, lse,
-                     (const float*)Dq, scale_log2, scale, dq, nqb);
+  const int G = Hq / Hkv, hpw = (G % 4 == 0) ? 4 : ((G % 2 == 0) ? 2 : 1);
+  const int nqg = (nqb + 4 / hpw - 1) / (4 / hpw);
+  hipLaunchKernelGGL(attn_bwd_dq_kernel<128>, dim3(B * Hkv * (G / hpw) * nqg), dim3(256), 0, s, qkv, ldq, si, Hq, Hkv,
+                     dO, QD, lse, (const float*)Dq, scale_log2, scale, dq, hpw, nqg);
   return hipGetLastError();
 }
 

@@ -89,6 +89,29 @@ def test_block_backward_small_ragged(lib, rank):
         check_grads(gt, rg, "small")
 
 
+@pytest.mark.parametrize("heads", [(4, 4), (8, 1), (6, 2)])
+def test_block_backward_group_sizes(lib, heads):
+    """GQA group sizes 1, 8 and 3 (the attention backward puts 1, 4 or 1 query heads of a kv head
+    in one workgroup), ragged token count, prefixes of 40 and 0 tokens."""
+    hq, hkv = heads
+    d = W.small_dims(hidden=256, n_q_heads=hq, n_kv_heads=hkv, head_dim=128, mlp_intermediate=512,
+                     lora_rank=8, lora_alpha=16.0)
+    w = W.scaled(W.CONFIGS[3], dims=d, height=32 * 7, width=32 * 11, prefix_len=40, n_img=2, n_br=1,
+                 prefix_cache_samples=0)
+    wts = strong_lora(W.layer_weights(w, 0, 2, "bf16"))
+    h = W.block_hidden(w, 2, "bf16")
+    pk, pv = zip(*[W.prefix_kv(w, 0, b, 2, "bf16") for b in range(2)])
+    pk, pv = [pk[0], pk[1][:0]], [pv[0], pv[1][:0]]
+    dy = W.normal(3, 2, "dy", h.shape)
+    log(f"block backward Hq={hq} Hkv={hkv}: B=2 N={w.n_tokens} prefixes 40/0")
+    got, gt = run_block_bwd(lib, d, wts, h, pk, pv, dy)
+    ref, rg = O.gen_block_bwd(h, wts, d, pk, pv, dy)
+    e, c = rel_max_err(got, ref), cosine(got, ref)
+    log(f"  dh: max|err|/RMS {e:.3e}, cos {c:.6f}")
+    assert e <= DH_TOL
+    check_grads(gt, rg, f"Hq {hq} Hkv {hkv}")
+
+
 def test_block_backward_8b_lora_block(lib):
     """The 8B LoRA training block: 4 samples x 1024 tokens, 400-token prefixes, rank 32."""
     w = W.scaled(W.CONFIGS[3], n_layers=1)
