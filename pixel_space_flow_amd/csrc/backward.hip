@@ -19,6 +19,8 @@
 #include "common.h"
 #include "kernels.h"
 
+#include <type_traits>
+
 namespace psf {
 namespace {
 
@@ -224,22 +226,39 @@ DEVI int tile_off(int r, int c) { return r * 128 + ((((c >> 3) ^ ((r & 3) << 2) 
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) s16x4* lds_s16x4;
 
+// A lane's element offsets into a staged tile, fixed for the whole kernel.  Row r adds r * 128 and
+// the swizzle only flips bits 3-6 (the chunk), so the offsets of other k-steps and column blocks
+// are these with constant bits XOR-ed in or 2048 (16 rows) added:
+//   rd:       row l%32, logical chunk l/32; chunk 2 ks + l/32 is at rd ^ (ks << 4)
+//   tr0, tr1: the transposed reads below for t = 0, column block 0; for (t, db) they are at
+//             (tr ^ (db << 5)) + 2048 t
+struct TileLane { int rd, tr0, tr1; };
+DEVI TileLane tile_lane(int lane) {
+  const int lr = lane & 31, lh = lane >> 5, j = lane & 15;
+  const int c = ((lane >> 4) & 1) * 16 + 4 * (j & 3), r0 = 4 * lh + (j >> 2);
+  return {tile_off(lr, lh * 8), tile_off(r0, c), tile_off(r0 + 8, c)};
+}
+
+// A or B operand of k-step ks from a staged tile's rows: lane l gets tile[l%32][16 ks + 8 (l/32) .. +8].
+DEVI bf16x8 tile_row(const bf16* tile, const TileLane& tl, int ks) {
+  return *(const bf16x8*)(tile + (tl.rd ^ (ks << 4)));
+}
+
 // A operand of k-step t, column block db (32 columns), from a staged tile read transposed:
-// lane l gets tile[16t + (i/4)*8 + (l/32)*4 + i%4][32 db + l%32] for i = 0..7.  ds_read_tr16_b64 hands lane j
-// of each 16-lane group element j%4 of the 8-byte pieces addressed by lanes 4k + j/4, k = 0..3; so
-// lane j addresses row 16t + 8h + 4(l/32) + j/4, columns 32 db + 16 ((l/16) & 1) + 4 (j%4) .. +3,
-// and the two reads (h = 0, 1) give slots 0-3 and 4-7.
-DEVI bf16x8 tile_tr(const bf16* tile, int t, int db, int lane) {
-  const int j = lane & 15, lh = lane >> 5;
-  const int c = db * 32 + ((lane >> 4) & 1) * 16 + 4 * (j & 3);
-  const int r0 = 16 * t + 4 * lh + (j >> 2);
-  const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4)(tile + tile_off(r0, c)));
-  const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4)(tile + tile_off(r0 + 8, c)));
+// lane l gets tile[16t + (i/4)*8 + (l/32)*4 + i%4][32 db + l%32] for i = 0..7.  ds_read_tr16_b64 hands
+// lane j of each 16-lane group element j%4 of the 8-byte pieces addressed by lanes 4k + j/4,
+// k = 0..3; so lane j addresses row 16t + 8h + 4(l/32) + j/4, columns 32 db + 16 ((l/16) & 1) +
+// 4 (j%4) .. +3, and the two reads (h = 0, 1) give slots 0-3 and 4-7.
+DEVI bf16x8 tile_tr(const bf16* tile, const TileLane& tl, int t, int db) {
+  const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4)(tile + ((tl.tr0 ^ (db << 5)) + 2048 * t)));
+  const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4)(tile + ((tl.tr1 ^ (db << 5)) + 2048 * t)));
   const s16x4 x[2] = {lo, hi};
   bf16x8 f;
   __builtin_memcpy(&f, x, 16);
   return f;
 }
+
+template <int V> using Int = std::integral_constant<int, V>;
 
 // Row pointer of key j (sequence b, kv head g) in the K or V source: the prefix cache for j < P,
 // the normed (K) or raw (V) image projections in qkv otherwise.
@@ -321,12 +340,10 @@ __global__ __launch_bounds__(256) void attn_bwd_dkdv_kernel(const bf16* __restri
     if (tid < 32) slse[st][tid] = rs;
     else if (tid < 64) sD[st][tid - 32] = rs;
   };
-  fetch(0);
-  stage(0);
-  if (nblk > 1) fetch(1);
-  __syncthreads();
-  for (int it = 0; it < nblk; ++it) {
-    const int st = it & 1;
+  const TileLane tl = tile_lane(lane);
+  // block it in stage ST (a constant, so the stage's LDS address folds into the instructions)
+  auto body = [&](int it, auto stc) {
+    constexpr int st = decltype(stc)::value;
     const int q0 = (it % nqb) * 32;
     if (it + 1 < nblk) {
       stage(st ^ 1);                     // every wave left stage st ^ 1 at the last barrier
@@ -339,29 +356,44 @@ __global__ __launch_bounds__(256) void attn_bwd_dkdv_kernel(const bf16* __restri
     for (int e = 0; e < 16; ++e) { sv[e] = 0.f; dp[e] = 0.f; }
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
-      const bf16x8 qa = *(const bf16x8*)&Qs[tile_off(lr, ks * 16 + lh * 8)];
-      const bf16x8 da = *(const bf16x8*)&Ds[tile_off(lr, ks * 16 + lh * 8)];
-      sv = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa, kf[ks], sv, 0, 0, 0);
-      dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(da, vf[ks], dp, 0, 0, 0);
+      sv = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tile_row(Qs, tl, ks), kf[ks], sv, 0, 0, 0);
+      dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tile_row(Ds, tl, ks), vf[ks], dp, 0, 0, 0);
     }
-    // P and dS (rows = queries q0 + (e/4)*8 + lh*4 + e%4, column = this lane's key)
+    // P and dS (rows = queries q0 + (e/4)*8 + lh*4 + e%4, column = this lane's key).  Lanes of
+    // keys past N produce columns that are never stored; rows past N (a ragged last block) are
+    // zeroed so that they add nothing to the valid keys.
+    float4 ls[4], dd[4];
+#pragma unroll
+    for (int a = 0; a < 4; ++a) {
+      ls[a] = *(const float4*)&slse[st][a * 8 + lh * 4];
+      dd[a] = *(const float4*)&sD[st][a * 8 + lh * 4];
+    }
+    const bool full = q0 + 32 <= N;
     bf16x8 pf[2], dsf[2];
 #pragma unroll
     for (int e = 0; e < 16; ++e) {
-      const int qr = (e >> 2) * 8 + lh * 4 + (e & 3);
-      const bool ok = keyok && q0 + qr < N;
-      const float pr = ok ? __builtin_amdgcn_exp2f(sv[e] * scale_log2 - slse[st][qr]) : 0.f;
+      const float lv = ls[e >> 2][e & 3], dv_ = dd[e >> 2][e & 3];
+      float pr = __builtin_amdgcn_exp2f(sv[e] * scale_log2 - lv);
+      if (!full && q0 + (e >> 2) * 8 + lh * 4 + (e & 3) >= N) pr = 0.f;
       pf[e >> 3][e & 7] = static_cast<bf16>(pr);
-      dsf[e >> 3][e & 7] = static_cast<bf16>(pr * (dp[e] - sD[st][qr]));
+      dsf[e >> 3][e & 7] = static_cast<bf16>(pr * (dp[e] - dv_));
     }
 #pragma unroll
     for (int t = 0; t < 2; ++t)
 #pragma unroll
       for (int db = 0; db < NDB; ++db) {
-        dvT[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tile_tr(Ds, t, db, lane), pf[t], dvT[db], 0, 0, 0);
-        dkT[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tile_tr(Qs, t, db, lane), dsf[t], dkT[db], 0, 0, 0);
+        dvT[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tile_tr(Ds, tl, t, db), pf[t], dvT[db], 0, 0, 0);
+        dkT[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tile_tr(Qs, tl, t, db), dsf[t], dkT[db], 0, 0, 0);
       }
     __syncthreads();
+  };
+  fetch(0);
+  stage(0);
+  if (nblk > 1) fetch(1);
+  __syncthreads();
+  for (int it = 0; it < nblk; it += 2) {
+    body(it, Int<0>{});
+    if (it + 1 < nblk) body(it + 1, Int<1>{});
   }
   if (keyok) {
     const int64_t tok = (int64_t)b * N + mykey;
@@ -383,7 +415,7 @@ __global__ __launch_bounds__(256) void attn_bwd_dkdv_kernel(const bf16* __restri
 // while this one is used).  S^T = K Q^T and dP^T = V dO^T take A = K or V rows from LDS and B = the
 // wave's Q or dO rows (registers); dQ^T += K^T dS^T reads K^T transposed from LDS.
 template <int D>
-__global__ __launch_bounds__(256) void attn_bwd_dq_kernel(const bf16* __restrict__ qkv, int64_t ldq, SeqInfo si, int Hq,
+__global__ __launch_bounds__(256, 2) void attn_bwd_dq_kernel(const bf16* __restrict__ qkv, int64_t ldq, SeqInfo si, int Hq,
                                                           int Hkv, const bf16* __restrict__ dO, int64_t ldo,
                                                           const float* __restrict__ lse, const float* __restrict__ Dq,
                                                           float scale_log2, float scale, float* __restrict__ dq,
@@ -438,12 +470,11 @@ __global__ __launch_bounds__(256) void attn_bwd_dq_kernel(const bf16* __restrict
       *(bf16x8*)&sv[st][tile_off(row, ch * 8)] = rv[c];
     }
   };
-  fetch(0);
-  stage(0);
-  if (ntile > 1) fetch(1);
-  __syncthreads();
-  for (int t = 0; t < ntile; ++t) {
-    const int st = t & 1, j0 = 32 * t;
+  const TileLane tl = tile_lane(lane);
+  // key tile t in stage ST (a constant, so the stage's LDS address folds into the instructions)
+  auto body = [&](int t, auto stc) {
+    constexpr int st = decltype(stc)::value;
+    const int j0 = 32 * t;
     if (t + 1 < ntile) {
       stage(st ^ 1);                     // every wave left stage st ^ 1 at the last barrier
       if (t + 2 < ntile) fetch(t + 2);
@@ -455,24 +486,33 @@ __global__ __launch_bounds__(256) void attn_bwd_dq_kernel(const bf16* __restrict
     for (int e = 0; e < 16; ++e) { s[e] = 0.f; dp[e] = 0.f; }
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
-      const bf16x8 ka = *(const bf16x8*)&Ks[tile_off(lr, ks * 16 + lh * 8)];
-      const bf16x8 va = *(const bf16x8*)&Vs[tile_off(lr, ks * 16 + lh * 8)];
-      s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, qf[ks], s, 0, 0, 0);
-      dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, df[ks], dp, 0, 0, 0);
+      s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tile_row(Ks, tl, ks), qf[ks], s, 0, 0, 0);
+      dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tile_row(Vs, tl, ks), df[ks], dp, 0, 0, 0);
     }
+    // lanes of queries past N produce columns that are never stored; keys past L (a ragged last
+    // tile) are zeroed
+    const bool full = j0 + 32 <= L;
     bf16x8 dsf[2];
 #pragma unroll
     for (int e = 0; e < 16; ++e) {
-      const int j = j0 + (e >> 2) * 8 + lh * 4 + (e & 3);
-      const float p = (qok && j < L) ? __builtin_amdgcn_exp2f(s[e] * scale_log2 - my_lse) : 0.f;
+      float p = __builtin_amdgcn_exp2f(s[e] * scale_log2 - my_lse);
+      if (!full && j0 + (e >> 2) * 8 + lh * 4 + (e & 3) >= L) p = 0.f;
       dsf[e >> 3][e & 7] = static_cast<bf16>(p * (dp[e] - my_D));
     }
 #pragma unroll
     for (int tk = 0; tk < 2; ++tk)
 #pragma unroll
       for (int db = 0; db < NDB; ++db)
-        dqT[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tile_tr(Ks, tk, db, lane), dsf[tk], dqT[db], 0, 0, 0);
+        dqT[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tile_tr(Ks, tl, tk, db), dsf[tk], dqT[db], 0, 0, 0);
     __syncthreads();
+  };
+  fetch(0);
+  stage(0);
+  if (ntile > 1) fetch(1);
+  __syncthreads();
+  for (int t = 0; t < ntile; t += 2) {
+    body(t, Int<0>{});
+    if (t + 1 < ntile) body(t + 1, Int<1>{});
   }
   if (qok) {
 #pragma unroll
