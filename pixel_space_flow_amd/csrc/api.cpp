@@ -253,6 +253,21 @@ bool lora_all(const gen_block_weights& w, const int* sites, int ns) {
   return true;
 }
 
+// The LoRA up-projection as the K extension of the 32-deep ring GEMM when its shape allows (the
+// low-rank term then joins the base product's fp32 accumulators, with no scratch round trip);
+// false leaves p unchanged.
+bool try_k32_ext(GemmParams& p, int epi, const gen_block_dims& d, const gen_block_weights& w, const int* sites,
+                 int ns, const int* ends, const void* t, int ldt, const int* off) {
+  bool any = false;
+  for (int i = 0; i < ns; ++i) any = any || off[i] >= 0;
+  if (!any) return false;
+  GemmParams q = p;
+  lora_ext(q, d, w, sites, ns, ends, t, ldt, off);
+  if (!k32_ext_ok(q, epi)) return false;
+  p = q;
+  return true;
+}
+
 // LoRA up-projection as low-rank products: columns [ends[i-1], ends[i]) of C (op)= t_i B_i^T with
 // t_i = columns off[i] .. off[i] + r of t.  mode 3 writes fp32 (the base GEMM then adds onto it
 // with the fp32-residual epilogue and rounds the sum once), mode 2 adds into fp32, mode 0 writes
@@ -308,7 +323,8 @@ int run_block(const gen_block_dims& d, const gen_block_weights& w, TH* hidden, c
       const int sites[3] = {0, 1, 2}, ends[3] = {QD, QD + Hkv * hd, QKV};
       int off[3], ldt;
       HIP_TRY(lora_down<T>(d, w, sites, 3, u, D, M, lt, off, ldt, s, at<float>(ws, L.skinny)));
-      if (lora_all(w, sites, 3)) {
+      if (sizeof(T) == 2 && try_k32_ext(p, EPI_STORE, d, w, sites, 3, ends, lt, ldt, off)) {
+      } else if (lora_all(w, sites, 3)) {
         float* lf = at<float>(ws, L.lora_f32);
         HIP_TRY(lora_up(d, w, sites, 3, ends, (const bf16*)lt, ldt, off, lf, QKV, M, 3, s));
         epi = EPI_RESID_FROM_F32; p.R = lf; p.ldr = QKV;
@@ -357,10 +373,15 @@ int run_block(const gen_block_dims& d, const gen_block_weights& w, TH* hidden, c
     p.part = L.splitk_floats ? at<float>(ws, L.splitk) : nullptr; p.part_floats = L.splitk_floats;
     const int sites[1] = {3}, ends[1] = {D};
     int off[1] = {-1}, ldt = 0;
-    if (lora) HIP_TRY(lora_down<T>(d, w, sites, 1, attn, QD, M, lt, off, ldt, s, at<float>(ws, L.skinny)));
-    HIP_TRY(timed(FAM_O, s, [&] { return gemm_any<T>(p, f32res ? EPI_RESID_F32 : EPI_RESID_TO_F32, s); }));
-    // the LoRA term accumulates into the fp32 mid-block residual
-    if (off[0] >= 0) HIP_TRY(lora_up(d, w, sites, 1, ends, (const bf16*)lt, ldt, off, hmid, D, M, 2, s));
+    const int epi = f32res ? EPI_RESID_F32 : EPI_RESID_TO_F32;
+    bool ext = false;
+    if (lora) {
+      HIP_TRY(lora_down<T>(d, w, sites, 1, attn, QD, M, lt, off, ldt, s, at<float>(ws, L.skinny)));
+      ext = sizeof(T) == 2 && try_k32_ext(p, epi, d, w, sites, 1, ends, lt, ldt, off);
+    }
+    HIP_TRY(timed(FAM_O, s, [&] { return gemm_any<T>(p, epi, s); }));
+    // otherwise the LoRA term accumulates into the fp32 mid-block residual
+    if (off[0] >= 0 && !ext) HIP_TRY(lora_up(d, w, sites, 1, ends, (const bf16*)lt, ldt, off, hmid, D, M, 2, s));
   }
   HIP_TRY((rmsnorm<float, T>(hmid, (const T*)w.g_post, u, M, D, d.rms_eps, s)));
   if (d.mlp_intermediate > 0) {
@@ -393,14 +414,20 @@ int run_block(const gen_block_dims& d, const gen_block_weights& w, TH* hidden, c
       const int sites[1] = {6}, ends[1] = {D};
       int off[1] = {-1}, ldt = 0;
       bool post = false;
+      const int epi = f32res ? EPI_RESID_F32 : EPI_RESID_FROM_F32;
       if (lora) {
         HIP_TRY(lora_down<T>(d, w, sites, 1, z, I, M, lt, off, ldt, s, at<float>(ws, L.skinny)));
-        // fp32 residual: the LoRA term is added after the base GEMM; a bf16 residual keeps the
-        // K extension so that the block output is rounded once
-        if (off[0] >= 0 && f32res) post = true;
-        else if (off[0] >= 0) lora_ext(p, d, w, sites, 1, ends, lt, ldt, off);
+        // the K extension of the ring kernel where it applies; otherwise with an fp32 residual the
+        // LoRA term is added after the base GEMM, and a bf16 residual keeps the K extension of the
+        // register-staged kernel so that the block output is rounded once
+        if (off[0] >= 0 && sizeof(T) == 2 && try_k32_ext(p, epi, d, w, sites, 1, ends, lt, ldt, off)) {
+        } else if (off[0] >= 0 && f32res) {
+          post = true;
+        } else if (off[0] >= 0) {
+          lora_ext(p, d, w, sites, 1, ends, lt, ldt, off);
+        }
       }
-      HIP_TRY(timed(FAM_DOWN, s, [&] { return gemm_any<T>(p, f32res ? EPI_RESID_F32 : EPI_RESID_FROM_F32, s); }));
+      HIP_TRY(timed(FAM_DOWN, s, [&] { return gemm_any<T>(p, epi, s); }));
       if (post) HIP_TRY(lora_up(d, w, sites, 1, ends, (const bf16*)lt, ldt, off, hidden, D, M, 2, s));
     }
   } else {
@@ -541,7 +568,20 @@ int lora_back(const gen_block_dims& d, const gen_block_weights& w, const BackSit
     else HIP_TRY(gemm_bf16(q, EPI_SCALED, s));
     HIP_TRY(transpose_bf16((const bf16*)w.lora_a[st.site], in, xb + slot[i] * r, n * r, r, in, s));
   }
-  // sum_site tp_site A_site into the fp32 scratch; the base dgrad GEMM adds onto it and rounds once
+  // sum_site tp_site A_site: as the K extension of the base dgrad GEMM ([tp | ...] against
+  // [A_site^T | ...]), or into the fp32 scratch that the base GEMM adds onto; either way the sum is
+  // rounded once
+  GemmParams q = p;
+  q.X = tp; q.ldx = n * r; q.xk = n * r; q.xr = n * r;
+  for (int i = 0; i < 3; ++i) {
+    q.XB[i] = i == 0 ? xb : nullptr;
+    q.xoff[i] = 0;
+    q.xsite_end[i] = p.N;
+  }
+  if (k32_ext_ok(q, EPI_STORE)) {
+    p = q;
+    return n;
+  }
   HIP_TRY(gemm_lowrank(tp, n * r, xb, n * r, M, p.N, n * r, lf, p.N, 3, s));
   p.R = lf; p.ldr = p.N;
   return n;
@@ -613,7 +653,8 @@ int run_block_bwd(const gen_block_dims& d, const gen_block_weights& w, const flo
     int epi = EPI_STORE;
     if (lora) {
       HIP_TRY(lora_down<bf16>(d, w, qkv_sites, 3, u, D, M, t_qkv, off_qkv, ld_qkv, s, part));
-      if (lora_all(w, qkv_sites, 3)) {
+      if (try_k32_ext(p, EPI_STORE, d, w, qkv_sites, 3, qkv_ends, t_qkv, ld_qkv, off_qkv)) {
+      } else if (lora_all(w, qkv_sites, 3)) {
         HIP_TRY(lora_up(d, w, qkv_sites, 3, qkv_ends, t_qkv, ld_qkv, off_qkv, lf, QKV, M, 3, s));
         epi = EPI_RESID_FROM_F32; p.R = lf; p.ldr = QKV;
       } else if (off_qkv[0] >= 0 || off_qkv[1] >= 0 || off_qkv[2] >= 0) {
@@ -631,9 +672,13 @@ int run_block_bwd(const gen_block_dims& d, const gen_block_weights& w, const flo
     GemmParams p = gp();
     p.A = attn; p.lda = QD; p.B = w.w_o; p.ldb = QD; p.M = M; p.N = D; p.K = QD;
     p.C = xmid; p.ldc = D; p.R = h; p.ldr = D;
-    if (lora) HIP_TRY(lora_down<bf16>(d, w, o_site, 1, attn, QD, M, t_o, off_o, ld_o, s, part));
+    bool ext = false;
+    if (lora) {
+      HIP_TRY(lora_down<bf16>(d, w, o_site, 1, attn, QD, M, t_o, off_o, ld_o, s, part));
+      ext = try_k32_ext(p, EPI_RESID_F32, d, w, o_site, 1, &D, t_o, ld_o, off_o);
+    }
     HIP_TRY(gemm_bf16(p, EPI_RESID_F32, s));
-    if (off_o[0] >= 0) HIP_TRY(lora_up(d, w, o_site, 1, &D, t_o, ld_o, off_o, xmid, D, M, 2, s));
+    if (off_o[0] >= 0 && !ext) HIP_TRY(lora_up(d, w, o_site, 1, &D, t_o, ld_o, off_o, xmid, D, M, 2, s));
   }
   HIP_TRY((rmsnorm<float, bf16>(xmid, (const bf16*)w.g_post, u2, M, D, eps, s)));
   {
@@ -642,7 +687,8 @@ int run_block_bwd(const gen_block_dims& d, const gen_block_weights& w, const flo
     int epi = EPI_STORE;
     if (lora) {
       HIP_TRY(lora_down<bf16>(d, w, gu_sites, 2, u2, D, M, t_gu, off_gu, ld_gu, s, part));
-      if (lora_all(w, gu_sites, 2)) {
+      if (try_k32_ext(p, EPI_STORE, d, w, gu_sites, 2, gu_ends, t_gu, ld_gu, off_gu)) {
+      } else if (lora_all(w, gu_sites, 2)) {
         HIP_TRY(lora_up(d, w, gu_sites, 2, gu_ends, t_gu, ld_gu, off_gu, lf, 2 * I, M, 3, s));
         epi = EPI_RESID_FROM_F32; p.R = lf; p.ldr = 2 * I;
       } else if (off_gu[0] >= 0 || off_gu[1] >= 0) {
@@ -664,7 +710,7 @@ int run_block_bwd(const gen_block_dims& d, const gen_block_weights& w, const flo
     p.A = dyb; p.lda = D; p.B = wt; p.ldb = D; p.M = M; p.N = I; p.K = D; p.C = dz; p.ldc = I;
     n = lora_back(d, w, bs, 1, dyb, D, I, M, tp, xb, bt, p, slot, part, lf, s);
     if (n < 0) return n;
-    HIP_TRY(gemm_bf16(p, n > 0 ? EPI_RESID_FROM_F32 : EPI_STORE, s));
+    HIP_TRY(gemm_bf16(p, p.R ? EPI_RESID_FROM_F32 : EPI_STORE, s));
     if (n > 0) {
       int rc = lora_wgrad(d, g, bs, 1, slot, n, dyb, D, t_down, ld_down, off_down, tp, z, I, M, part, s);
       if (rc) return rc;
@@ -678,7 +724,7 @@ int run_block_bwd(const gen_block_dims& d, const gen_block_weights& w, const flo
     p.A = dgu; p.lda = 2 * I; p.B = wt; p.ldb = 2 * I; p.M = M; p.N = D; p.K = 2 * I; p.C = du; p.ldc = D;
     n = lora_back(d, w, bs, 2, dgu, 2 * I, D, M, tp, xb, bt, p, slot, part, lf, s);
     if (n < 0) return n;
-    HIP_TRY(gemm_bf16(p, n > 0 ? EPI_RESID_FROM_F32 : EPI_STORE, s));
+    HIP_TRY(gemm_bf16(p, p.R ? EPI_RESID_FROM_F32 : EPI_STORE, s));
     if (n > 0) {
       int rc = lora_wgrad(d, g, bs, 2, slot, n, dgu, 2 * I, t_gu, ld_gu, off_gu, tp, u2, D, M, part, s);
       if (rc) return rc;
@@ -693,7 +739,7 @@ int run_block_bwd(const gen_block_dims& d, const gen_block_weights& w, const flo
     p.A = dyb; p.lda = D; p.B = wt; p.ldb = D; p.M = M; p.N = QD; p.K = D; p.C = dO; p.ldc = QD;
     n = lora_back(d, w, bs, 1, dyb, D, QD, M, tp, xb, bt, p, slot, part, lf, s);
     if (n < 0) return n;
-    HIP_TRY(gemm_bf16(p, n > 0 ? EPI_RESID_FROM_F32 : EPI_STORE, s));
+    HIP_TRY(gemm_bf16(p, p.R ? EPI_RESID_FROM_F32 : EPI_STORE, s));
     if (n > 0) {
       int rc = lora_wgrad(d, g, bs, 1, slot, n, dyb, D, t_o, ld_o, off_o, tp, attn, QD, M, part, s);
       if (rc) return rc;
@@ -710,7 +756,7 @@ int run_block_bwd(const gen_block_dims& d, const gen_block_weights& w, const flo
     p.A = dqkv; p.lda = QKV; p.B = wt; p.ldb = QKV; p.M = M; p.N = D; p.K = QKV; p.C = du; p.ldc = D;
     n = lora_back(d, w, bs, 3, dqkv, QKV, D, M, tp, xb, bt, p, slot, part, lf, s);
     if (n < 0) return n;
-    HIP_TRY(gemm_bf16(p, n > 0 ? EPI_RESID_FROM_F32 : EPI_STORE, s));
+    HIP_TRY(gemm_bf16(p, p.R ? EPI_RESID_FROM_F32 : EPI_STORE, s));
     if (n > 0) {
       int rc = lora_wgrad(d, g, bs, 3, slot, n, dqkv, QKV, t_qkv, ld_qkv, off_qkv, tp, u, D, M, part, s);
       if (rc) return rc;

@@ -48,5 +48,8 @@ struct GemmParams {
 hipError_t gemm_bf16(const GemmParams& p, int epi, hipStream_t s);
 hipError_t gemm_bf16_grouped(const GemmParams& p, int epi, int n_col_tiles, hipStream_t s);
 hipError_t gemm_f32(const GemmParams& p, int epi, hipStream_t s);
+// True when gemm_bf16 runs a K-extended launch (p.X set) on the 32-deep ring kernel: extension
+// width, rank and site column offsets multiples of 32, site boundaries multiples of 16, plain B.
+bool k32_ext_ok(const GemmParams& p, int epi);
 
 }  // namespace psf

@@ -610,7 +610,10 @@ __global__ __launch_bounds__(64 * NW, 1) void gemm_fast_kernel(GemmParams p, int
 // Operands go global -> LDS by buffer loads that write LDS directly (16 B per lane).  The DMA
 // of each k-tile is split in two halves sent in consecutive k-steps, interleaved with MFMAs, so
 // the vector-memory path sees a steady stream; three k-tiles are in flight while one is read.
-template <int EPI, bool GROUPED, bool GATHER>
+// EXT: the LoRA up-projection as xk / 32 more k-tiles after the K / 32 of A and B: A rows from X,
+// B rows from the up-projection of the site that owns the 16 output columns of each row group,
+// zero (out-of-range loads) outside that site's xr-wide slice of X's columns.
+template <int EPI, bool GROUPED, bool GATHER, bool EXT = false>
 __global__ __launch_bounds__(512, 1) void gemm_k32_kernel(GemmParams p, int n_col_tiles) {
   constexpr int NBW = 2;                     // 32-column MFMA blocks per wave
   constexpr int KB = 32;                     // k per stage
@@ -689,16 +692,46 @@ __global__ __launch_bounds__(512, 1) void gemm_k32_kernel(GemmParams p, int n_co
   }
   const uint32_t bvoff = lrow * ldb2 + lch * 16;
 
-  const int KT = p.K / KB / max(p.ksplit, 1);
-  const uint32_t kofs = (uint32_t)(split * KT) * ROWB;   // byte offset of this launch's k-range
+  const int KTM = p.K / KB / max(p.ksplit, 1);            // k-tiles of A B^T in this launch
+  const int KT = KTM + (EXT ? p.xk / KB : 0);
+  const uint32_t kofs = (uint32_t)(split * KTM) * ROWB;  // byte offset of this launch's k-range
+  // K extension: X rows of the tile, and per row group of this wave its site's up-projection rows
+  __amdgpu_buffer_rsrc_t rx, rbx[2];
+  uint32_t xvoff = 0, bxvoff = 0, ldx2 = 0;
+  int bx_lo[2] = {0, 0}, bx_hi[2] = {0, 0};
+  if (EXT) {
+    ldx2 = (uint32_t)p.ldx * 2;
+    rx = make_rsrc((const bf16*)p.X + (int64_t)row0 * p.ldx, (uint32_t)rows * ldx2);
+    xvoff = lrow * ldx2 + lch * 16;
+    bxvoff = lrow * (uint32_t)p.xr * 2 + lch * 16;
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const int col = b_row_outcol(p, tn, (2 * wave + h) * 16);
+      const int site = col < p.xsite_end[0] ? 0 : (col < p.xsite_end[1] ? 1 : 2);
+      const int start = site == 0 ? 0 : p.xsite_end[site - 1];
+      const int nrow = min(16, min(p.xsite_end[site], (p.bmode == 1 ? 2 * p.swiglu_I : p.N)) - col);
+      const bf16* xb = (const bf16*)p.XB[site];
+      rbx[h] = make_rsrc(xb ? xb + (int64_t)(col - start) * p.xr : p.X, (xb && nrow > 0) ? (uint32_t)nrow * p.xr * 2 : 0u);
+      bx_lo[h] = p.xoff[site];                        // X columns [lo, hi) belong to this site
+      bx_hi[h] = p.xoff[site] + p.xr;
+    }
+  }
   // Half h of the DMA of k-tile t (row groups 2w + h of A and of B) into stage t % 4.  Tiles past
   // the end reload the last one into a stage nobody reads again, so every k-step sends the same
   // number of loads and the vmcnt arithmetic below holds throughout.
   auto dma_half = [&](int t, int h) {
     char* As = smem + (t & (NST - 1)) * STG;
     char* Bs = As + BM * ROWB;
-    const uint32_t kb = (uint32_t)min(t, KT - 1) * ROWB + kofs;
+    const int tt = min(t, KT - 1);
     const int g = 2 * wave + h;
+    if (EXT && tt >= KTM) {
+      const int k0 = (tt - KTM) * KB;                 // X column of this extension k-tile
+      dma16(rx, As + g * 1024, xvoff, g * 16 * ldx2 + k0 * 2);
+      const bool in = k0 >= bx_lo[h] && k0 < bx_hi[h];
+      dma16(rbx[h], Bs + g * 1024, bxvoff, in ? (uint32_t)(k0 - bx_lo[h]) * 2 : 0x40000000u);
+      return;
+    }
+    const uint32_t kb = (uint32_t)tt * ROWB + kofs;
     if (GATHER)
       dma16(ra, As + g * 1024, avoff[h], kb);
     else
@@ -990,6 +1023,30 @@ hipError_t launch_fast(const GemmParams& p, int epi, int grid, int n_col_tiles, 
   return hipErrorInvalidValue;
 }
 
+// The 32-deep ring kernel with the K extension (plain B, no row gather): residual and store
+// epilogues.
+hipError_t launch_k32_ext(const GemmParams& p, int epi, int grid, int n_col_tiles, hipStream_t s) {
+  const size_t lds = 2 * STAGE_BYTES;
+#define PSF_L(E)                                                                                  \
+  case E: {                                                                                        \
+    auto k = gemm_k32_kernel<E, false, false, true>;                                               \
+    hipError_t e = hipFuncSetAttribute((const void*)k, hipFuncAttributeMaxDynamicSharedMemorySize, \
+                                       (int)lds);                                                  \
+    if (e != hipSuccess) return e;                                                                 \
+    hipLaunchKernelGGL(k, dim3(grid), dim3(512), lds, s, p, n_col_tiles);                          \
+    return hipGetLastError();                                                                      \
+  }
+  switch (epi) {
+    PSF_L(EPI_STORE)
+    PSF_L(EPI_RESID)
+    PSF_L(EPI_RESID_TO_F32)
+    PSF_L(EPI_RESID_FROM_F32)
+    PSF_L(EPI_RESID_F32)
+  }
+#undef PSF_L
+  return hipErrorInvalidValue;
+}
+
 template <bool GROUPED, bool EXT>
 hipError_t launch_bf16(const GemmParams& p, int epi, int grid, int n_col_tiles, hipStream_t s) {
   const size_t lds = 2 * STAGE_BYTES;
@@ -1046,6 +1103,18 @@ __global__ __launch_bounds__(256) void splitk_reduce_kernel(GemmParams p, int ks
   }
 }
 
+bool k32_ext_ok(const GemmParams& p, int epi) {
+  if (!p.X || p.xk <= 0 || p.xk % 32 || p.xr <= 0 || p.xr % 32 || p.ldx % 8 || p.bmode != 0 || p.a_rows) return false;
+  if (epi != EPI_STORE && epi != EPI_RESID && epi != EPI_RESID_TO_F32 && epi != EPI_RESID_FROM_F32 &&
+      epi != EPI_RESID_F32)
+    return false;
+  for (int i = 0; i < 3; ++i)
+    if (p.xoff[i] % 32 || p.xoff[i] < 0 || (p.XB[i] && p.xoff[i] + p.xr > p.xk)) return false;
+  for (int i = 0; i < 2; ++i)
+    if (p.xsite_end[i] % 16) return false;       // every 16-row group of B lies in one site
+  return true;
+}
+
 // Number of k-ranges for a plain GEMM whose row x column tiles leave most CUs idle (0 = unsplit).
 int splitk_choice(const GemmParams& p, int epi, int tiles) {
   if (!p.part || p.X || p.bmode != 0 || p.a_rows || p.N % 4) return 0;
@@ -1082,7 +1151,10 @@ hipError_t gemm_bf16(const GemmParams& p, int epi, hipStream_t s) {
     }
     return hipGetLastError();
   }
-  if (p.X && p.xk > 0) return launch_bf16<false, true>(p, epi, n_m * n_cols, n_cols, s);
+  if (p.X && p.xk > 0) {
+    if (k32_ext_ok(p, epi)) return launch_k32_ext(p, epi, n_m * n_cols, n_cols, s);
+    return launch_bf16<false, true>(p, epi, n_m * n_cols, n_cols, s);
+  }
   if (p.bmode == 2) return launch_bf16<false, false>(p, epi, n_m * n_cols, n_cols, s);
   if (p.a_rows) return launch_fast<false, true>(p, epi, n_m * n_cols, n_cols, s);
   return launch_fast<false, false>(p, epi, n_m * n_cols, n_cols, s);

@@ -167,9 +167,10 @@ def test_lora_strong_adapter_delta(lib):
 
 
 def test_lora_zero_up_is_bitwise_base(lib):
+    """Zero up-projections leave the block bitwise equal to the base block.  At 4 x 1024 tokens every
+    projection has enough tiles to run unsplit with or without the LoRA K extension, so both
+    runs add their products in the same order."""
     w, wts, h, pk, pv = lora_case()
-    h = h[:, :256]
-    w = W.scaled(w, height=512, width=512)
     zero = dict(wts)
     for s in W.LORA_SITES:
         zero[f"lora_b_{s}"] = np.zeros_like(wts[f"lora_b_{s}"])
