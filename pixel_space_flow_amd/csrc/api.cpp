@@ -395,7 +395,8 @@ int run_block(const gen_block_dims& d, const gen_block_weights& w, TH* hidden, c
         const int sites[2] = {4, 5}, ends[2] = {I, 2 * I};
         int off[2], ldt;
         HIP_TRY(lora_down<T>(d, w, sites, 2, u, D, M, lt, off, ldt, s, at<float>(ws, L.skinny)));
-        if (lora_all(w, sites, 2)) {
+        if (sizeof(T) == 2 && try_k32_ext(p, EPI_SWIGLU, d, w, sites, 2, ends, lt, ldt, off)) {
+        } else if (lora_all(w, sites, 2)) {
           // gate and up LoRA terms, added by the SwiGLU epilogue before the activation
           T* lg = at<T>(ws, L.lora_gu);
           HIP_TRY(lora_up(d, w, sites, 2, ends, (const bf16*)lt, ldt, off, lg, 2 * I, M, 0, s));

@@ -49,7 +49,8 @@ hipError_t gemm_bf16(const GemmParams& p, int epi, hipStream_t s);
 hipError_t gemm_bf16_grouped(const GemmParams& p, int epi, int n_col_tiles, hipStream_t s);
 hipError_t gemm_f32(const GemmParams& p, int epi, hipStream_t s);
 // True when gemm_bf16 runs a K-extended launch (p.X set) on the 32-deep ring kernel: extension
-// width, rank and site column offsets multiples of 32, site boundaries multiples of 16, plain B.
+// width, rank and site column offsets multiples of 32, site boundaries multiples of 16, a plain B
+// (or the interleaved gate/up B with the SwiGLU epilogue).
 bool k32_ext_ok(const GemmParams& p, int epi);
 
 }  // namespace psf

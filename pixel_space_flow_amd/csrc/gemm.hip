@@ -1023,8 +1023,8 @@ hipError_t launch_fast(const GemmParams& p, int epi, int grid, int n_col_tiles, 
   return hipErrorInvalidValue;
 }
 
-// The 32-deep ring kernel with the K extension (plain B, no row gather): residual and store
-// epilogues.
+// The 32-deep ring kernel with the K extension (no row gather): residual and store epilogues on a
+// plain B, the SwiGLU epilogue on the interleaved gate/up B.
 hipError_t launch_k32_ext(const GemmParams& p, int epi, int grid, int n_col_tiles, hipStream_t s) {
   const size_t lds = 2 * STAGE_BYTES;
 #define PSF_L(E)                                                                                  \
@@ -1039,6 +1039,7 @@ hipError_t launch_k32_ext(const GemmParams& p, int epi, int grid, int n_col_tile
   switch (epi) {
     PSF_L(EPI_STORE)
     PSF_L(EPI_RESID)
+    PSF_L(EPI_SWIGLU)
     PSF_L(EPI_RESID_TO_F32)
     PSF_L(EPI_RESID_FROM_F32)
     PSF_L(EPI_RESID_F32)
@@ -1104,10 +1105,13 @@ __global__ __launch_bounds__(256) void splitk_reduce_kernel(GemmParams p, int ks
 }
 
 bool k32_ext_ok(const GemmParams& p, int epi) {
-  if (!p.X || p.xk <= 0 || p.xk % 32 || p.xr <= 0 || p.xr % 32 || p.ldx % 8 || p.bmode != 0 || p.a_rows) return false;
-  if (epi != EPI_STORE && epi != EPI_RESID && epi != EPI_RESID_TO_F32 && epi != EPI_RESID_FROM_F32 &&
-      epi != EPI_RESID_F32)
+  if (!p.X || p.xk <= 0 || p.xk % 32 || p.xr <= 0 || p.xr % 32 || p.ldx % 8 || p.a_rows) return false;
+  if (epi == EPI_SWIGLU) {
+    if (p.bmode != 1 || p.swiglu_I % 16) return false;
+  } else if (p.bmode != 0 || (epi != EPI_STORE && epi != EPI_RESID && epi != EPI_RESID_TO_F32 &&
+                              epi != EPI_RESID_FROM_F32 && epi != EPI_RESID_F32)) {
     return false;
+  }
   for (int i = 0; i < 3; ++i)
     if (p.xoff[i] % 32 || p.xoff[i] < 0 || (p.XB[i] && p.xoff[i] + p.xr > p.xk)) return false;
   for (int i = 0; i < 2; ++i)
