@@ -250,9 +250,10 @@ __global__ __launch_bounds__(NT, 1) void gemm_bf16_kernel(GemmParams p, int n_co
 }
 
 // ------------------------------------------------------------------ fast path
-// Same tile, wave layout, LDS layout and epilogues as gemm_bf16_kernel, but the global->LDS
-// copy uses gfx950's buffer loads straight into LDS (16 bytes per lane): no staging VGPRs and
-// no ds_write instructions, which leaves registers for the MFMA fragments.  One load
+// Same 256 x 256 x 64 tile and epilogues as gemm_bf16_kernel, but the global->LDS copy uses
+// gfx950's buffer loads straight into LDS (16 bytes per lane): no staging VGPRs and no ds_write
+// instructions, which leaves registers for the MFMA fragments; the products are
+// v_mfma_f32_16x16x32_bf16 blocks (one instruction per 32-deep half of the tile).  One load
 // instruction of a wave fills 8 consecutive LDS rows (1 KiB); lane l lands at base + 16 l,
 // i.e. row l/8, physical chunk l%8, so it fetches logical chunk (l%8) ^ (l/8) of its row and
 // the XOR swizzle comes out of the address arithmetic.  Buffer resources cover only the
@@ -369,6 +370,7 @@ template <int EPI, bool GROUPED, bool GATHER, int NW>
 __global__ __launch_bounds__(64 * NW, 1) void gemm_fast_kernel(GemmParams p, int n_col_tiles) {
   // NW = 4: 2 x 2 waves of 128 x 128 (one wave per SIMD); NW = 8: 2 x 4 waves of 128 x 64 (two
   // waves per SIMD, so one wave's DMA issue or barrier wait is covered by the other's MFMAs).
+  // Each wave tile is a grid of 16 x 16 blocks of v_mfma_f32_16x16x32_bf16.
   constexpr int WN = NW / 2;                 // waves along n
   constexpr int NBW = (BN / WN) / 32;        // 32-column MFMA blocks per wave (4 or 2)
   constexpr int GPW = 32 / NW;               // 8-row load groups per wave per operand
@@ -459,72 +461,94 @@ __global__ __launch_bounds__(64 * NW, 1) void gemm_fast_kernel(GemmParams p, int
     }
   };
 
-  f32x16 acc[4][NBW];
+  constexpr int NB16 = 2 * NBW;               // 16-column MFMA blocks per wave (8 or 4)
+  f32x4 acc[8][NB16];
 #pragma unroll
-  for (int a = 0; a < 4; ++a)
+  for (int a = 0; a < 8; ++a)
 #pragma unroll
-    for (int b = 0; b < NBW; ++b)
+    for (int b = 0; b < NB16; ++b)
 #pragma unroll
-      for (int e = 0; e < 16; ++e) acc[a][b][e] = 0.f;
+      for (int e = 0; e < 4; ++e) acc[a][b][e] = 0.f;
 
   const int KT = p.K / BK;
-  const int lr = lane & 31, lh = lane >> 5;
-  // LDS byte offsets of this lane's fragment rows (chunk XOR folded in per k-step below)
-  const int arow0 = (wm * 128 + lr) * (BK * 2), brow0 = (wn * (BN / WN) + lr) * (BK * 2);
-  const int sw = (lr >> 1) & 7;   // the same for all 4 blocks: their rows differ by multiples of 32
-
-  // Software pipeline.  Two register sets of fragments: the reads for k-step ks+1 are issued
-  // before the 16 MFMAs of step ks.  In the last step of a tile every wave waits for its
-  // outstanding LDS-DMA and LDS reads and meets the others at the barrier: the next tile's
-  // stage is then complete and this tile's stage is free, so the DMA of tile kt+2 goes out,
-  // the next tile's first fragments are read, and the last 16 MFMAs hide both.  The
-  // sched_barrier(0) fences keep the compiler from moving reads next to their MFMAs.
-  bf16x8 fa[2][4], fb[2][NBW];
-  auto rd = [&](int set, int stage, int ks) {
+  // 16x16x32 fragments (v_mfma_f32_16x16x32_bf16): lane l holds row l % 16 of a 16-row block and
+  // logical chunk 4 ks + l / 16 of the 32-deep half ks of the 64-deep tile
+  const int r16 = lane & 15, c16 = lane >> 4;
+  const int sw = (r16 >> 1) & 7;              // the same for all blocks: their rows differ by 16
+  const int arow0 = (wm * 128 + r16) * (BK * 2), brow0 = (wn * (BN / WN) + r16) * (BK * 2);
+  bf16x8 fal[4], fah[4], fb[NB16];
+  auto rd_a = [&](bf16x8 (&f)[4], int stage, int ks, int half) {
     const char* As = smem + stage * STAGE_BYTES;
-    const char* Bs = As + BM * BK * 2;
-    const int ch = ((ks * 2 + lh) ^ sw) << 4;
+    const int ch = ((4 * ks + c16) ^ sw) << 4;
 #pragma unroll
-    for (int mb = 0; mb < 4; ++mb) fa[set][mb] = *(const bf16x8*)(As + arow0 + mb * 32 * (BK * 2) + ch);
-#pragma unroll
-    for (int nb = 0; nb < NBW; ++nb) fb[set][nb] = *(const bf16x8*)(Bs + brow0 + nb * 32 * (BK * 2) + ch);
+    for (int i = 0; i < 4; ++i) f[i] = *(const bf16x8*)(As + arow0 + (half * 4 + i) * 16 * (BK * 2) + ch);
   };
-  auto mma = [&](int set) {
+  auto rd_b = [&](int stage, int ks) {
+    const char* Bs = smem + stage * STAGE_BYTES + BM * BK * 2;
+    const int ch = ((4 * ks + c16) ^ sw) << 4;
 #pragma unroll
-    for (int mb = 0; mb < 4; ++mb)
+    for (int nb = 0; nb < NB16; ++nb) fb[nb] = *(const bf16x8*)(Bs + brow0 + nb * 16 * (BK * 2) + ch);
+  };
+  auto mma = [&](const bf16x8 (&fa)[4], int half) {
 #pragma unroll
-      for (int nb = 0; nb < NBW; ++nb)
-        acc[mb][nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[set][mb], fb[set][nb], acc[mb][nb], 0, 0, 0);
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int nb = 0; nb < NB16; ++nb)
+        acc[half * 4 + i][nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fa[i], fb[nb], acc[half * 4 + i][nb], 0, 0, 0);
+  };
+  // MFMAs in pairs, an LDS read after each of the first nds pairs
+  auto interleave = [&](int nds) {
+#pragma unroll
+    for (int i = 0; i < 2 * NB16; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);   // MFMA
+      if (i < nds) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);   // DS read
+    }
   };
 
+  // Software pipeline over the four half-steps of a tile (32-deep half ks, wave-tile rows
+  // 0-63 or 64-127): the fragments of the next half-step are read while this one's MFMAs run;
+  // B fragments after the last MFMA on the previous ones.  In the last half-step every wave waits
+  // for its LDS-DMA and meets the others, so the next tile's stage is complete and this tile's
+  // stage is free for the DMA of tile kt+2.
   issue(0, 0);
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
   if (KT > 1) issue(1, 1);
-  rd(0, 0, 0);
+  rd_a(fal, 0, 0, 0);
+  rd_b(0, 0);
   for (int kt = 0; kt < KT; ++kt) {
     const int st = kt & 1;
-#pragma unroll
-    for (int ks = 0; ks < BK / 16; ++ks) {
-      const int cur = ks & 1;
-      if (ks + 1 < BK / 16) {
-        rd(cur ^ 1, st, ks + 1);
-      } else if (kt + 1 < KT) {
-        __builtin_amdgcn_s_waitcnt(0);
-        __syncthreads();
-        if (kt + 2 < KT) issue(kt + 2, st);
-        rd(cur ^ 1, st ^ 1, 0);
-      }
-      // the wave that is behind within the tile gets the higher priority, so the two waves of a
-      // SIMD stay level and reach the barrier together
-      if (ks == 0) __builtin_amdgcn_s_setprio(2);
-      else if (ks == 1) __builtin_amdgcn_s_setprio(1);
-      else if (ks == 2) __builtin_amdgcn_s_setprio(0);
-      else __builtin_amdgcn_s_setprio(3);
-      __builtin_amdgcn_sched_barrier(0);
-      mma(cur);
-      __builtin_amdgcn_sched_barrier(0);
+    // half-step 0: rows 0-63 of k 0-31
+    __builtin_amdgcn_s_setprio(2);
+    rd_a(fah, st, 0, 1);
+    mma(fal, 0);
+    interleave(4);
+    __builtin_amdgcn_sched_barrier(0);
+    // half-step 1: rows 64-127 of k 0-31
+    __builtin_amdgcn_s_setprio(1);
+    rd_a(fal, st, 1, 0);
+    mma(fah, 1);
+    interleave(4);
+    __builtin_amdgcn_sched_barrier(0);
+    rd_b(st, 1);
+    // half-step 2: rows 0-63 of k 32-63
+    __builtin_amdgcn_s_setprio(0);
+    rd_a(fah, st, 1, 1);
+    mma(fal, 0);
+    interleave(4);
+    __builtin_amdgcn_sched_barrier(0);
+    // half-step 3: rows 64-127 of k 32-63
+    __builtin_amdgcn_s_setprio(3);
+    if (kt + 1 < KT) {
+      __builtin_amdgcn_s_waitcnt(0);
+      __syncthreads();
+      if (kt + 2 < KT) issue(kt + 2, st);
+      rd_a(fal, st ^ 1, 0, 0);
     }
+    mma(fah, 1);
+    interleave(4);
+    __builtin_amdgcn_sched_barrier(0);
+    if (kt + 1 < KT) rd_b(st ^ 1, 0);
   }
   __builtin_amdgcn_s_setprio(0);
 
@@ -542,10 +566,16 @@ __global__ __launch_bounds__(64 * NW, 1) void gemm_fast_kernel(GemmParams p, int
     for (int nb = 0; nb < NBW; ++nb) {
       if (EPI == EPI_SWIGLU && (nb & 1)) continue;       // consumed together with its gate block
 #pragma unroll
-      for (int e = 0; e < 16; ++e) T0[((e >> 2) * 8 + lh * 4 + (e & 3)) * TS + lr] = acc[mb][nb][e];
+      for (int q = 0; q < 4; ++q)
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          T0[((q >> 1) * 16 + 4 * c16 + e) * TS + (q & 1) * 16 + r16] = acc[2 * mb + (q >> 1)][2 * nb + (q & 1)][e];
       if (EPI == EPI_SWIGLU) {
 #pragma unroll
-        for (int e = 0; e < 16; ++e) T1[((e >> 2) * 8 + lh * 4 + (e & 3)) * TS + lr] = acc[mb][nb + 1][e];
+        for (int q = 0; q < 4; ++q)
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+            T1[((q >> 1) * 16 + 4 * c16 + e) * TS + (q & 1) * 16 + r16] = acc[2 * mb + (q >> 1)][2 * (nb + 1) + (q & 1)][e];
       }
       __builtin_amdgcn_s_waitcnt(0xc07f);                   // lgkmcnt(0): staged values written
       __builtin_amdgcn_wave_barrier();
@@ -606,7 +636,8 @@ __global__ __launch_bounds__(64 * NW, 1) void gemm_fast_kernel(GemmParams p, int
 // bf16 GEMM for the residual and QKV projections: 256 x 256 output tiles, k consumed 32 at a time
 // through a ring of four LDS
 // stages (32 KB each: 256 rows x 64 B of A, the same of B).  8 waves in a 2 x 4 grid, each
-// 128 x 64 (4 x 2 MFMA blocks of 32 x 32, v_mfma_f32_32x32x16_bf16), two waves per SIMD.
+// 128 x 64 (8 x 4 MFMA blocks of 16 x 16, v_mfma_f32_16x16x32_bf16: one instruction takes the
+// whole 32-deep k-tile), two waves per SIMD.
 // Operands go global -> LDS by buffer loads that write LDS directly (16 B per lane).  The DMA
 // of each k-tile is split in two halves sent in consecutive k-steps, interleaved with MFMAs, so
 // the vector-memory path sees a steady stream; three k-tiles are in flight while one is read.
@@ -739,85 +770,81 @@ __global__ __launch_bounds__(512, 1) void gemm_k32_kernel(GemmParams p, int n_co
     dma16(rb, Bs + g * 1024, bvoff, bsoff[h] + kb);
   };
 
-  f32x16 acc[4][NBW];
+  f32x4 acc[8][4];
 #pragma unroll
-  for (int a = 0; a < 4; ++a)
+  for (int a = 0; a < 8; ++a)
 #pragma unroll
-    for (int b = 0; b < NBW; ++b)
+    for (int b = 0; b < 4; ++b)
 #pragma unroll
-      for (int e = 0; e < 16; ++e) acc[a][b][e] = 0.f;
+      for (int e = 0; e < 4; ++e) acc[a][b][e] = 0.f;
 
-  const int lr = lane & 31, lh = lane >> 5;
-  const int arow0 = (wm * 128 + lr) * ROWB, brow0 = (wn * 64 + lr) * ROWB;
-  const int sw = (lr >> 2) & 3;
-  bf16x8 fa[2][4], fb[2][NBW];
-  auto rd = [&](int set, int stage, int ks) {
+  // 16x16x32 fragments: lane l holds row (l % 16) of a 16-row block, logical chunk l / 16
+  const int r16 = lane & 15, c16 = lane >> 4;
+  const int sw = (r16 >> 2) & 3;                  // rows of all blocks differ by multiples of 16
+  const int aoff = (wm * 128 + r16) * ROWB + ((c16 ^ sw) << 4);
+  const int boff = (wn * 64 + r16) * ROWB + ((c16 ^ sw) << 4);
+  bf16x8 fal[4], fah[4], fb[4];
+  auto rd_a = [&](bf16x8 (&f)[4], int stage, int half) {
     const char* As = smem + stage * STG;
-    const char* Bs = As + BM * ROWB;
-    const int ch = ((ks * 2 + lh) ^ sw) << 4;
-    // in the order the MFMAs consume them
-    fa[set][0] = *(const bf16x8*)(As + arow0 + ch);
 #pragma unroll
-    for (int nb = 0; nb < NBW; ++nb) fb[set][nb] = *(const bf16x8*)(Bs + brow0 + nb * 32 * ROWB + ch);
-#pragma unroll
-    for (int mb = 1; mb < 4; ++mb) fa[set][mb] = *(const bf16x8*)(As + arow0 + mb * 32 * ROWB + ch);
+    for (int i = 0; i < 4; ++i) f[i] = *(const bf16x8*)(As + aoff + (half * 4 + i) * 16 * ROWB);
   };
-  auto mma = [&](int set) {
+  auto rd_b = [&](bf16x8 (&f)[4], int stage) {
+    const char* Bs = smem + stage * STG + BM * ROWB;
 #pragma unroll
-    for (int mb = 0; mb < 4; ++mb)
-#pragma unroll
-      for (int nb = 0; nb < NBW; ++nb)
-        acc[mb][nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[set][mb], fb[set][nb], acc[mb][nb], 0, 0, 0);
+    for (int i = 0; i < 4; ++i) f[i] = *(const bf16x8*)(Bs + boff + i * 16 * ROWB);
   };
-  // one k-step: 8 MFMAs, each followed by one of the step's 6 LDS reads, the first two also by
-  // one DMA instruction
-  auto interleave = [&]() {
+  auto mma = [&](const bf16x8 (&fa)[4], const bf16x8 (&fbb)[4], int half) {
 #pragma unroll
-    for (int i = 0; i < 6; ++i) {
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // MFMA
-      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);   // DS read
-      if (i < 2) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);   // VMEM (LDS-DMA)
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int nb = 0; nb < 4; ++nb)
+        acc[half * 4 + i][nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fa[i], fbb[nb], acc[half * 4 + i][nb], 0, 0, 0);
+  };
+  // 16 MFMAs in pairs, an LDS read after each of the first nds pairs, a DMA after the first two
+  auto interleave = [&](int nds) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);   // MFMA
+      if (i < nds) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);   // DS read
+      if (i < 2) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);     // VMEM (LDS-DMA)
     }
-    __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
   };
-  // vmcnt(8) lgkmcnt(0): all but the last 8 loads (the next two k-tiles), every LDS access
   constexpr int WAIT_TILE = 8 | (7 << 4);
 
-  // Prologue: k-tiles 0-2 whole and the first half of tile 3; wait for tile 0.
   dma_half(0, 0); dma_half(0, 1);
   dma_half(1, 0); dma_half(1, 1);
   dma_half(2, 0); dma_half(2, 1);
   dma_half(3, 0);
   __builtin_amdgcn_s_waitcnt(10 | (7 << 4));
   __builtin_amdgcn_s_barrier();
-  rd(0, 0, 0);
-  // Steady state, k-tile kt in stage kt % 4.  Step 0 sends the second half of tile kt+3; step 1
-  // waits for tile kt+1 (sent at least two k-tiles earlier), meets the other waves (so tile kt's
-  // stage is free and tile kt+1's complete), reads tile kt+1's first fragments and sends the
-  // first half of tile kt+4 into tile kt's stage.
+  rd_a(fal, 0, 0);
+  rd_b(fb, 0);
+  // k-tile kt: the MFMAs of rows 0-63 of the wave tile while the fragments of rows 64-127 are
+  // read; past the barrier, rows 64-127 while tile kt+1's rows 0-63 are read; tile kt+1's B
+  // fragments are read once the last MFMA on tile kt's B has been issued.
   for (int kt = 0; kt + 1 < KT; ++kt) {
     const int st = kt & (NST - 1);
-    // a wave past the barrier runs at the higher priority, so one that is ahead lets its SIMD
-    // partner catch up and the two meet the barrier together
     __builtin_amdgcn_s_setprio(0);
-    rd(1, st, 1);
+    rd_a(fah, st, 1);
     dma_half(kt + 3, 1);
-    mma(0);
-    interleave();
+    mma(fal, fb, 0);
+    interleave(4);
     __builtin_amdgcn_sched_barrier(0);
     __builtin_amdgcn_s_waitcnt(WAIT_TILE);
     __builtin_amdgcn_s_barrier();
     __builtin_amdgcn_s_setprio(1);
-    rd(0, (kt + 1) & (NST - 1), 0);
+    rd_a(fal, (kt + 1) & (NST - 1), 0);
     dma_half(kt + 4, 0);
-    mma(1);
-    interleave();
+    mma(fah, fb, 1);
+    interleave(4);
     __builtin_amdgcn_sched_barrier(0);
+    rd_b(fb, (kt + 1) & (NST - 1));
   }
   __builtin_amdgcn_s_setprio(0);
-  rd(1, (KT - 1) & (NST - 1), 1);
-  mma(0);
-  mma(1);
+  rd_a(fah, (KT - 1) & (NST - 1), 1);
+  mma(fal, fb, 0);
+  mma(fah, fb, 1);
 
   // ---- epilogue through LDS: each wave stages one 32x32 fp32 block at a time, then every lane
   // owns 16 consecutive columns of one row (lanes 2r, 2r+1 cover row r), so global accesses are
@@ -834,10 +861,16 @@ __global__ __launch_bounds__(512, 1) void gemm_k32_kernel(GemmParams p, int n_co
     for (int nb = 0; nb < NBW; ++nb) {
       if (EPI == EPI_SWIGLU && (nb & 1)) continue;       // consumed together with its gate block
 #pragma unroll
-      for (int e = 0; e < 16; ++e) T0[((e >> 2) * 8 + lh * 4 + (e & 3)) * TS + lr] = acc[mb][nb][e];
+      for (int q = 0; q < 4; ++q)
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          T0[((q >> 1) * 16 + 4 * c16 + e) * TS + (q & 1) * 16 + r16] = acc[2 * mb + (q >> 1)][2 * nb + (q & 1)][e];
       if (EPI == EPI_SWIGLU) {
 #pragma unroll
-        for (int e = 0; e < 16; ++e) T1[((e >> 2) * 8 + lh * 4 + (e & 3)) * TS + lr] = acc[mb][nb + 1][e];
+        for (int q = 0; q < 4; ++q)
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+            T1[((q >> 1) * 16 + 4 * c16 + e) * TS + (q & 1) * 16 + r16] = acc[2 * mb + (q >> 1)][2 * (nb + 1) + (q & 1)][e];
       }
       __builtin_amdgcn_s_waitcnt(0xc07f);                   // lgkmcnt(0): staged values written
       __builtin_amdgcn_wave_barrier();
