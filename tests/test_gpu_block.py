@@ -166,6 +166,32 @@ def test_lora_strong_adapter_delta(lib):
     assert c > 0.999
 
 
+def test_lora_partial_sites(lib):
+    """LoRA on q, v, up and down only (k, o and gate without adapters): the GEMMs' K extension
+    reads zeros for the columns of the sites without one.  Strong up-projections as above; the
+    GPU's LoRA delta must match the oracle's."""
+    from gpu_helpers import cosine
+    w, wts, h, pk, pv = lora_case()
+    h = h[:2, :512]
+    w = W.scaled(w, n_img=2, height=512, width=1024)
+    pk, pv = pk[:2], pv[:2]
+    part = {k: v for k, v in wts.items() if not (k.startswith("lora_") and k.split("_")[-1] in ("k", "o", "gate"))}
+    for s in ("q", "v", "up", "down"):
+        part[f"lora_b_{s}"] = W.maybe_bf16(W.normal(3, 1, f"partial_b_{s}", wts[f"lora_b_{s}"].shape, 0.05), "bf16")
+    assert sorted(k for k in part if k.startswith("lora_a")) == ["lora_a_down", "lora_a_q", "lora_a_up", "lora_a_v"]
+    base_d = W.BlockDims(**{**W.dataclasses.asdict(w.dims), "lora_rank": 0, "lora_alpha": 0.0})
+    base_w = {k: v for k, v in wts.items() if not k.startswith("lora")}
+    got = run_gpu_block(lib, w, part, h, pk, pv, "bf16")
+    gbase = run_gpu_block(lib, W.scaled(w, dims=base_d), base_w, h, pk, pv, "bf16")
+    rows = np.arange(3, 512, 7)
+    ref = O.gen_block(h, part, w.dims, pk, pv, rows=rows)
+    base = O.gen_block(h, base_w, base_d, pk, pv, rows=rows)
+    check(got[:, rows], ref, h[:, rows], BLOCK_TOL, "partial-site LoRA block")
+    c = cosine(got[:, rows] - gbase[:, rows], ref - base)
+    log(f"  LoRA delta cosine {c:.5f}")
+    assert c > 0.999
+
+
 def test_lora_zero_up_is_bitwise_base(lib):
     """Zero up-projections leave the block bitwise equal to the base block.  At 4 x 1024 tokens every
     projection has enough tiles to run unsplit with or without the LoRA K extension, so both

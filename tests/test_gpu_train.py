@@ -112,6 +112,28 @@ def test_block_backward_group_sizes(lib, heads):
     check_grads(gt, rg, f"Hq {hq} Hkv {hkv}")
 
 
+def test_block_backward_rank32_partial_sites(lib):
+    """Rank 32 (the base GEMMs take the LoRA terms as their K extension) with adapters on q, v, o
+    and up only: dh and the gradients of the four adapters."""
+    d = small_dims(32)
+    w = W.scaled(W.CONFIGS[3], dims=d, height=32 * 7, width=32 * 11, prefix_len=40, n_img=2, n_br=1,
+                 prefix_cache_samples=0)
+    full = strong_lora(W.layer_weights(w, 0, 4, "bf16"))
+    wts = {k: v for k, v in full.items() if not (k.startswith("lora_") and k.split("_")[-1] in ("k", "gate", "down"))}
+    h = W.block_hidden(w, 4, "bf16")
+    pk, pv = zip(*[W.prefix_kv(w, 0, b, 4, "bf16") for b in range(2)])
+    pk, pv = [pk[0], pk[1][:17]], [pv[0], pv[1][:17]]
+    dy = W.normal(3, 4, "dy", h.shape)
+    log(f"block backward rank 32, sites q v o up: B=2 N={w.n_tokens} prefixes 40/17")
+    got, gt = run_block_bwd(lib, d, wts, h, pk, pv, dy)
+    ref, rg = O.gen_block_bwd(h, wts, d, pk, pv, dy)
+    assert sorted(rg) == sorted(k for k in wts if k.startswith("lora_"))
+    e, c = rel_max_err(got, ref), cosine(got, ref)
+    log(f"  dh: max|err|/RMS {e:.3e}, cos {c:.6f}")
+    assert e <= DH_TOL
+    check_grads(gt, rg, "rank 32 partial")
+
+
 def test_block_backward_8b_lora_block(lib):
     """The 8B LoRA training block: 4 samples x 1024 tokens, 400-token prefixes, rank 32."""
     w = W.scaled(W.CONFIGS[3], n_layers=1)
