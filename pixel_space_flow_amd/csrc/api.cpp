@@ -533,7 +533,7 @@ Wb layout_bwd(const gen_block_dims& d, int B, int N, int max_prefix) {
   w.xb = take(std::max(std::max(D, I), QD) * 3 * r * 2);
   w.bt = take(r * std::max(std::max(QD, D), I) * 2);
   w.lf = take(r ? M * std::max(std::max(QKV, 2 * I), std::max(D, QD)) * 4 : 0);
-  w.part = take(std::max(std::max((size_t)4 << 20, r * std::max(std::max(QD, D), I)),
+  w.part = take(std::max(std::max((size_t)WGRAD_PART_FLOATS, r * std::max(std::max(QD, D), I)),
                          r ? skinny_part_floats((int)M, (int)std::min<size_t>(3 * r, 128)) : 0) * 4);
   w.total = o;
   return w;

@@ -579,6 +579,98 @@ __global__ __launch_bounds__(256) void wgrad_kernel(const bf16* __restrict__ X, 
   }
 }
 
+// Partial sums of a LoRA weight gradient whose one side is the rank (R <= 128 columns, "Small")
+// and whose other side is a projection width ("Big", NB columns): over the m-range of split z,
+//   BIGX:  part[z][c][j] = sum_m Big[m][c] Small[m][j]   (C = X^T Y with X = Big, N1 = NB, N2 = R)
+//   !BIGX: part[z][j][c] = sum_m Small[m][j] Big[m][c]   (X = Small, Y = Big, N1 = R, N2 = NB)
+// A workgroup streams 128 Big columns (32 per wave) over its m-range in 32-row tiles staged in LDS
+// (two stages, the next tile loaded into registers under this one's MFMAs); both operands are
+// read transposed (k = m) from the staged tiles, and the MFMA operand order puts the Big column
+// on the accumulator's lane axis so the partial stores are 128-byte rows.
+template <bool BIGX>
+__global__ __launch_bounds__(256) void wgrad_lr_kernel(const bf16* __restrict__ Big, int64_t ldb,
+                                                       const bf16* __restrict__ Small, int64_t lds, int M, int NB,
+                                                       int R, int m_per_split, float* __restrict__ part) {
+  __shared__ __attribute__((aligned(16))) bf16 sb[2][32 * 128];
+  __shared__ __attribute__((aligned(16))) bf16 ss[2][32 * 128];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, lr = lane & 31, lh = lane >> 5;
+  const int c0 = blockIdx.x * 128, z = blockIdx.y;
+  const int m_lo = z * m_per_split, m_hi = min(M, m_lo + m_per_split);
+  const int nchunk = (m_hi - m_lo + 31) / 32;
+  const int NJ = (R + 31) / 32;
+  const TileLane tl = tile_lane(lane);
+  f32x16 acc[4];
+#pragma unroll
+  for (int jb = 0; jb < 4; ++jb)
+#pragma unroll
+    for (int e = 0; e < 16; ++e) acc[jb][e] = 0.f;
+  // thread tid moves 16-byte chunks tid and tid + 256 of each tile (row = chunk / 16)
+  bf16x8 rb[2], rs[2];
+  const bf16x8 zero = {};
+  auto fetch = [&](int ch) {
+#pragma unroll
+    for (int c = 0; c < 2; ++c) {
+      const int idx = c * 256 + tid, row = idx >> 4, col = (idx & 15) * 8;
+      const int m = m_lo + ch * 32 + row;
+      rb[c] = (m < m_hi && c0 + col < NB) ? *(const bf16x8*)(Big + (int64_t)m * ldb + c0 + col) : zero;
+      rs[c] = (m < m_hi && col < R) ? *(const bf16x8*)(Small + (int64_t)m * lds + col) : zero;
+    }
+  };
+  auto stage = [&](int st) {
+#pragma unroll
+    for (int c = 0; c < 2; ++c) {
+      const int idx = c * 256 + tid, row = idx >> 4, col = (idx & 15) * 8;
+      *(bf16x8*)&sb[st][tile_off(row, col)] = rb[c];
+      *(bf16x8*)&ss[st][tile_off(row, col)] = rs[c];
+    }
+  };
+  auto body = [&](int ch, auto stc) {
+    constexpr int st = decltype(stc)::value;
+    if (ch + 1 < nchunk) {
+      stage(st ^ 1);                     // every wave left stage st ^ 1 at the last barrier
+      if (ch + 2 < nchunk) fetch(ch + 2);
+    }
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+      const bf16x8 bigf = tile_tr(sb[st], tl, t, wave);
+#pragma unroll
+      for (int jb = 0; jb < 4; ++jb) {
+        if (jb >= NJ) continue;
+        const bf16x8 smf = tile_tr(ss[st], tl, t, jb);
+        acc[jb] = BIGX ? __builtin_amdgcn_mfma_f32_32x32x16_bf16(bigf, smf, acc[jb], 0, 0, 0)
+                       : __builtin_amdgcn_mfma_f32_32x32x16_bf16(smf, bigf, acc[jb], 0, 0, 0);
+      }
+    }
+    __syncthreads();
+  };
+  if (nchunk > 0) {
+    fetch(0);
+    stage(0);
+    if (nchunk > 1) fetch(1);
+    __syncthreads();
+    for (int ch = 0; ch < nchunk; ch += 2) {
+      body(ch, Int<0>{});
+      if (ch + 1 < nchunk) body(ch + 1, Int<1>{});
+    }
+  }
+  // accumulator of block jb: BIGX rows c = c0 + 32 wave + (e/4)*8 + lh*4 + e%4, lanes j = 32 jb + lr;
+  // otherwise rows j = 32 jb + (e/4)*8 + lh*4 + e%4, lanes c = c0 + 32 wave + lr
+  float* out = part + (int64_t)z * NB * R;
+#pragma unroll
+  for (int jb = 0; jb < 4; ++jb) {
+    if (jb >= NJ) continue;
+#pragma unroll
+    for (int e = 0; e < 16; ++e) {
+      const int row = (e >> 2) * 8 + lh * 4 + (e & 3);
+      const int c = c0 + 32 * wave + (BIGX ? row : lr), j = 32 * jb + (BIGX ? lr : row);
+      if (j < R && c < NB) {
+        if (BIGX) out[(int64_t)c * R + j] = acc[jb][e];
+        else out[(int64_t)j * NB + c] = acc[jb][e];
+      }
+    }
+  }
+}
+
 // C[i] += sum_z part[z][i]
 __global__ __launch_bounds__(256) void wgrad_reduce_kernel(const float* __restrict__ part, int splits, int64_t n,
                                                            float* __restrict__ C) {
@@ -692,12 +784,30 @@ hipError_t wgrad(const bf16* X, int64_t ldx, const bf16* Y, int64_t ldy, int M, 
                  hipStream_t s) {
   if (M <= 0 || N1 <= 0 || N2 <= 0) return hipSuccess;
   if (N1 % 8 || N2 % 8 || ldx % 8 || ldy % 8) return hipErrorInvalidValue;
+  const int64_t n = (int64_t)N1 * N2;
+  const int R = std::min(N1, N2), NB = std::max(N1, N2);
+  if (R <= 128) {
+    // one side is the rank: stream the other side in 128-column blocks, about 512 workgroups,
+    // the partial products within WGRAD_PART_FLOATS
+    const int nblk = (NB + 127) / 128;
+    int splits = std::max(1, 512 / nblk);
+    splits = std::min(splits, std::max(1, (M + 127) / 128));
+    splits = (int)std::min<int64_t>(splits, std::max<int64_t>(1, WGRAD_PART_FLOATS / n));
+    const int per = ((M + splits - 1) / splits + 31) / 32 * 32;
+    const int nz = (M + per - 1) / per;
+    if (N1 >= N2)
+      hipLaunchKernelGGL(wgrad_lr_kernel<true>, dim3(nblk, nz), dim3(256), 0, s, X, ldx, Y, ldy, M, NB, R, per, part);
+    else
+      hipLaunchKernelGGL(wgrad_lr_kernel<false>, dim3(nblk, nz), dim3(256), 0, s, Y, ldy, X, ldx, M, NB, R, per, part);
+    hipLaunchKernelGGL(wgrad_reduce_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, (const float*)part, nz, n,
+                       C);
+    return hipGetLastError();
+  }
   const int splits = wgrad_splits(M, N1, N2);
   const int per = ((M + splits - 1) / splits + 63) / 64 * 64;
   const int nz = (M + per - 1) / per;
   hipLaunchKernelGGL(wgrad_kernel, dim3((N1 + 63) / 64, (N2 + 63) / 64, nz), dim3(256), 0, s, X, ldx, Y, ldy, M, N1, N2,
                      per, part);
-  const int64_t n = (int64_t)N1 * N2;
   hipLaunchKernelGGL(wgrad_reduce_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, (const float*)part, nz, n, C);
   return hipGetLastError();
 }

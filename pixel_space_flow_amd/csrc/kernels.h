@@ -89,7 +89,8 @@ hipError_t qknorm_rope_bwd(const bf16* raw, int64_t ldr, const float* dq, const 
 // Dq scratch [B, Hq, N]; dq [M, Hq d], dk, dv [M, Hkv d] fp32 (image keys only)
 hipError_t attention_bwd(const bf16* qkv, int64_t ldq, const SeqInfo& si, int Hq, int Hkv, int d, const bf16* O,
                          const bf16* dO, const float* lse, float* Dq, float* dq, float* dk, float* dv, hipStream_t s);
-// C[n1, n2] += sum_m X[m, n1] Y[m, n2]; part: scratch of wgrad_part_floats(M, N1, N2) floats
+// C[n1, n2] += sum_m X[m, n1] Y[m, n2]; part: scratch of at least WGRAD_PART_FLOATS floats
+constexpr int64_t WGRAD_PART_FLOATS = (int64_t)4 << 20;
 int wgrad_splits(int M, int N1, int N2);
 hipError_t wgrad(const bf16* X, int64_t ldx, const bf16* Y, int64_t ldy, int M, int N1, int N2, float* C, float* part,
                  hipStream_t s);
