@@ -1019,12 +1019,14 @@ int fast_waves() {
   return w;
 }
 
+// The 64-deep kernel for SwiGLU and for plain launches up to 8192 deep; the 32-deep ring kernel
+// for longer k (the down projection), split-K partial products and the expert GEMMs.
 template <bool GROUPED, bool GATHER>
 hipError_t launch_fast(const GemmParams& p, int epi, int grid, int n_col_tiles, hipStream_t s) {
   const size_t lds = 2 * STAGE_BYTES;
 #define PSF_L(E)                                                                                  \
   case E: {                                                                                        \
-    if (E != EPI_SWIGLU) {                                                                         \
+    if (E != EPI_SWIGLU && (E == EPI_PARTIAL_F32 || GROUPED || GATHER || p.K >= 8192)) {           \
       auto k = gemm_k32_kernel<E, GROUPED, GATHER>;                                                \
       hipError_t e = hipFuncSetAttribute((const void*)k, hipFuncAttributeMaxDynamicSharedMemorySize, \
                                          (int)lds);                                                \
