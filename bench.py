@@ -327,7 +327,8 @@ def run_train_bench(psf, w, args):
                    "loss": float(loss.item())},
         "pct_bf16_peak": round(100 * tflops / PEAK_BF16_TFLOPS, 2), "tflops": round(tflops, 1),
         "step_tflop": round(fl["total"] / 1e12, 3),
-        "roofline": {"kernel": f"forward gate_up SwiGLU GEMM with its LoRA terms (M={M_}, N=2x{d.mlp_intermediate}, "
+        "roofline": {"kernel": f"forward gate_up GEMM with its LoRA terms, gate and up kept for the backward "
+                               f"(M={M_}, N=2x{d.mlp_intermediate}, "
                                f"K={d.hidden})",
                      "bound": "mfma", "achieved": round(gu_tf, 1), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                      "frac": round(gu_tf / PEAK_BF16_TFLOPS, 4), "traffic": None,

@@ -235,6 +235,13 @@ hipError_t lora_down(const gen_block_dims& d, const gen_block_weights& w, const 
   return gemm_bf16(p, EPI_SCALED, s);
 }
 
+// The column offsets (and row pitch) that lora_down gives the sites listed, without computing t.
+void lora_offsets(const gen_block_dims& d, const gen_block_weights& w, const int* sites, int ns, int* off, int& ldt) {
+  int n = 0;
+  for (int i = 0; i < ns; ++i) off[i] = w.lora_a[sites[i]] ? (n++) * d.lora_rank : -1;
+  ldt = std::max(n, 1) * d.lora_rank;
+}
+
 // Attach the LoRA up-projection of the given sites as a K extension of p.
 void lora_ext(GemmParams& p, const gen_block_dims& d, const gen_block_weights& w, const int* sites, int ns,
               const int* site_end, const void* t, int ldt, const int* off) {
@@ -486,30 +493,22 @@ int check_prefix_ptrs(const SeqInfo& si, int layer) {
 
 // ------------------------------------------------------------------ training backward (one block)
 // LoRA sites: 0 q, 1 k, 2 v, 3 o, 4 gate, 5 up, 6 down.
-struct Wb {
-  size_t u, qkv_raw, qkv_n, kc, vt, rope, attn, lse, dot, xmid, u2, gu, z, t_qkv, t_o, t_gu, t_down, tp, dyb, dz,
-      dgu, du, dxf, dO, dq, dk, dv, dqkv, wt, xb, bt, part, lf, total;
-  int Lpad, n_pos;
+// What the backward of one block reads from its forward (one slot per block).
+struct Wact {
+  size_t u, qkv_raw, qkv_n, attn, lse, xmid, u2, gu, z, t_qkv, t_o, t_gu, t_down, total;
 };
 
-Wb layout_bwd(const gen_block_dims& d, int B, int N, int max_prefix) {
-  Wb w{};
+Wact layout_act(const gen_block_dims& d, int B, int N) {
+  Wact w{};
   const size_t M = (size_t)B * N, D = d.hidden, I = d.mlp_intermediate, r = d.lora_rank;
-  const size_t Hq = d.n_q_heads, Hkv = d.n_kv_heads, hd = d.head_dim;
-  const size_t QD = Hq * hd, KVD = Hkv * hd, QKV = QD + 2 * KVD;
-  w.Lpad = (int)((max_prefix + N + 63) / 64 * 64);
-  w.n_pos = max_prefix + N;
+  const size_t QD = (size_t)d.n_q_heads * d.head_dim, QKV = QD + 2 * (size_t)d.n_kv_heads * d.head_dim;
   size_t o = 0;
   auto take = [&](size_t bytes) { size_t a = o; o += up(bytes); return a; };
   w.u = take(M * D * 2);
   w.qkv_raw = take(M * QKV * 2);
   w.qkv_n = take(M * QKV * 2);
-  w.kc = take((size_t)B * Hkv * w.Lpad * hd * 2);
-  w.vt = take((size_t)B * Hkv * w.Lpad * hd * 2);
-  w.rope = take((size_t)w.n_pos * (hd / 2) * 8);
   w.attn = take(M * QD * 2);
-  w.lse = take((size_t)B * Hq * N * 4);
-  w.dot = take((size_t)B * Hq * N * 4);
+  w.lse = take((size_t)B * d.n_q_heads * N * 4);
   w.xmid = take(M * D * 4);
   w.u2 = take(M * D * 2);
   w.gu = take(M * 2 * I * 2);
@@ -518,6 +517,32 @@ Wb layout_bwd(const gen_block_dims& d, int B, int N, int max_prefix) {
   w.t_o = take(M * r * 2);
   w.t_gu = take(M * 2 * r * 2);
   w.t_down = take(M * r * 2);
+  w.total = o;
+  return w;
+}
+
+// Scratch of the block backward; with_act: also one activation slot (gen_block_backward).
+struct Wb {
+  size_t act, kc, vt, rope, dot, tp, dyb, dz, dgu, du, dxf, dO, dq, dk, dv, dqkv, wt, xb, bt, part, lf, total;
+  Wact A;
+  int Lpad, n_pos;
+};
+
+Wb layout_bwd(const gen_block_dims& d, int B, int N, int max_prefix, bool with_act = true) {
+  Wb w{};
+  const size_t M = (size_t)B * N, D = d.hidden, I = d.mlp_intermediate, r = d.lora_rank;
+  const size_t Hq = d.n_q_heads, Hkv = d.n_kv_heads, hd = d.head_dim;
+  const size_t QD = Hq * hd, KVD = Hkv * hd, QKV = QD + 2 * KVD;
+  w.Lpad = (int)((max_prefix + N + 63) / 64 * 64);
+  w.n_pos = max_prefix + N;
+  w.A = layout_act(d, B, N);
+  size_t o = 0;
+  auto take = [&](size_t bytes) { size_t a = o; o += up(bytes); return a; };
+  w.act = take(with_act ? w.A.total : 0);
+  w.kc = take((size_t)B * Hkv * w.Lpad * hd * 2);
+  w.vt = take((size_t)B * Hkv * w.Lpad * hd * 2);
+  w.rope = take((size_t)w.n_pos * (hd / 2) * 8);
+  w.dot = take((size_t)B * Hq * N * 4);
   w.tp = take(M * 3 * r * 2);
   w.dyb = take(M * D * 2);
   w.dz = take(M * I * 2);
@@ -603,46 +628,34 @@ int lora_wgrad(const gen_block_dims& d, const gen_lora_grads& g, const BackSite*
   return GEN_OK;
 }
 
-// Gradient of one dense gen block (bf16 operands, fp32 residual).  h: the block input [M, D]
-// fp32; dh: in, dL/d(block output); out, dL/d(block input).  Recomputes the block's forward
-// into the workspace, then walks back through it; LoRA gradients accumulate into g.
-int run_block_bwd(const gen_block_dims& d, const gen_block_weights& w, const float* h, float* dh, const SeqInfo& si,
-                  const gen_lora_grads& g, void* ws, const Wb& L, hipStream_t s) {
+// Forward of one dense gen block for training (bf16 operands, fp32 residual): keeps in the
+// activation slot `act` what block_train_bwd reads; with h_out, also writes the block output
+// h_out = h + attention + MLP (fp32).  Scratch in ws (layout L).
+int block_train_fwd(const gen_block_dims& d, const gen_block_weights& w, const float* h, float* h_out,
+                    const SeqInfo& si, void* act, void* ws, const Wb& L, hipStream_t s) {
   const int B = si.B, N = si.N, M = B * N, D = d.hidden, I = d.mlp_intermediate, r = d.lora_rank;
   const int Hq = d.n_q_heads, Hkv = d.n_kv_heads, hd = d.head_dim;
   const int QD = Hq * hd, KVD = Hkv * hd, QKV = QD + 2 * KVD;
   const bool lora = r > 0;
   const float eps = d.rms_eps;
-  bf16* u = at<bf16>(ws, L.u);
-  bf16* qkv_raw = at<bf16>(ws, L.qkv_raw);
-  bf16* qkv_n = at<bf16>(ws, L.qkv_n);
-  bf16* attn = at<bf16>(ws, L.attn);
-  float* lse = at<float>(ws, L.lse);
-  float* xmid = at<float>(ws, L.xmid);
-  bf16* u2 = at<bf16>(ws, L.u2);
-  bf16* gu = at<bf16>(ws, L.gu);
-  bf16* z = at<bf16>(ws, L.z);
-  bf16* t_qkv = at<bf16>(ws, L.t_qkv);
-  bf16* t_o = at<bf16>(ws, L.t_o);
-  bf16* t_gu = at<bf16>(ws, L.t_gu);
-  bf16* t_down = at<bf16>(ws, L.t_down);
-  bf16* tp = at<bf16>(ws, L.tp);
-  bf16* dyb = at<bf16>(ws, L.dyb);
-  bf16* dz = at<bf16>(ws, L.dz);
-  bf16* dgu = at<bf16>(ws, L.dgu);
-  bf16* du = at<bf16>(ws, L.du);
-  float* dxf = at<float>(ws, L.dxf);
-  bf16* dO = at<bf16>(ws, L.dO);
-  bf16* dqkv = at<bf16>(ws, L.dqkv);
-  bf16* wt = at<bf16>(ws, L.wt);
-  bf16* xb = at<bf16>(ws, L.xb);
-  bf16* bt = at<bf16>(ws, L.bt);
+  bf16* u = at<bf16>(act, L.A.u);
+  bf16* qkv_raw = at<bf16>(act, L.A.qkv_raw);
+  bf16* qkv_n = at<bf16>(act, L.A.qkv_n);
+  bf16* attn = at<bf16>(act, L.A.attn);
+  float* lse = at<float>(act, L.A.lse);
+  float* xmid = at<float>(act, L.A.xmid);
+  bf16* u2 = at<bf16>(act, L.A.u2);
+  bf16* gu = at<bf16>(act, L.A.gu);
+  bf16* z = at<bf16>(act, L.A.z);
+  bf16* t_qkv = at<bf16>(act, L.A.t_qkv);
+  bf16* t_o = at<bf16>(act, L.A.t_o);
+  bf16* t_gu = at<bf16>(act, L.A.t_gu);
+  bf16* t_down = at<bf16>(act, L.A.t_down);
   float* part = at<float>(ws, L.part);
   float* lf = at<float>(ws, L.lf);
   const float2* rope = at<float2>(ws, L.rope);
   HIP_TRY(rope_table(at<float2>(ws, L.rope), L.n_pos, hd, d.rope_theta, s));
 
-  // ---- forward, keeping what the backward reads
   const int qkv_sites[3] = {0, 1, 2}, qkv_ends[3] = {QD, QD + KVD, QKV};
   const int o_site[1] = {3}, gu_sites[2] = {4, 5}, gu_ends[2] = {I, 2 * I}, down_site[1] = {6};
   int off_qkv[3] = {-1, -1, -1}, off_o[1] = {-1}, off_gu[2] = {-1, -1}, off_down[1] = {-1};
@@ -696,10 +709,69 @@ int run_block_bwd(const gen_block_dims& d, const gen_block_weights& w, const flo
         lora_ext(p, d, w, gu_sites, 2, gu_ends, t_gu, ld_gu, off_gu);
       }
     }
-    HIP_TRY(gemm_bf16(p, epi, s));
+    HIP_TRY(timed(FAM_GATE_UP, s, [&] { return gemm_bf16(p, epi, s); }));
   }
   HIP_TRY(swiglu_fwd(gu, z, M, I, s));
   if (lora) HIP_TRY(lora_down<bf16>(d, w, down_site, 1, z, I, M, t_down, off_down, ld_down, s, part));
+
+  if (h_out) {  // down projection onto the mid-block residual: the block output
+    GemmParams p = gp();
+    p.A = z; p.lda = I; p.B = w.w_down; p.ldb = I; p.M = M; p.N = D; p.K = I;
+    p.C = h_out; p.ldc = D; p.R = xmid; p.ldr = D;
+    bool ext = false;
+    if (off_down[0] >= 0) ext = try_k32_ext(p, EPI_RESID_F32, d, w, down_site, 1, &D, t_down, ld_down, off_down);
+    HIP_TRY(gemm_bf16(p, EPI_RESID_F32, s));
+    if (off_down[0] >= 0 && !ext) HIP_TRY(lora_up(d, w, down_site, 1, &D, t_down, ld_down, off_down, h_out, D, M, 2, s));
+  }
+  return GEN_OK;
+}
+
+// Gradient of one dense gen block from the activations block_train_fwd kept in `act`.  h: the
+// block input [M, D] fp32; dh: in, dL/d(block output); out, dL/d(block input).  LoRA gradients
+// accumulate into g.
+int block_train_bwd(const gen_block_dims& d, const gen_block_weights& w, const float* h, float* dh,
+                    const SeqInfo& si, const gen_lora_grads& g, void* act, void* ws, const Wb& L, hipStream_t s) {
+  const int B = si.B, N = si.N, M = B * N, D = d.hidden, I = d.mlp_intermediate, r = d.lora_rank;
+  const int Hq = d.n_q_heads, Hkv = d.n_kv_heads, hd = d.head_dim;
+  const int QD = Hq * hd, KVD = Hkv * hd, QKV = QD + 2 * KVD;
+  const bool lora = r > 0;
+  const float eps = d.rms_eps;
+  bf16* u = at<bf16>(act, L.A.u);
+  bf16* qkv_raw = at<bf16>(act, L.A.qkv_raw);
+  bf16* qkv_n = at<bf16>(act, L.A.qkv_n);
+  bf16* attn = at<bf16>(act, L.A.attn);
+  float* lse = at<float>(act, L.A.lse);
+  float* xmid = at<float>(act, L.A.xmid);
+  bf16* u2 = at<bf16>(act, L.A.u2);
+  bf16* gu = at<bf16>(act, L.A.gu);
+  bf16* z = at<bf16>(act, L.A.z);
+  bf16* t_qkv = at<bf16>(act, L.A.t_qkv);
+  bf16* t_o = at<bf16>(act, L.A.t_o);
+  bf16* t_gu = at<bf16>(act, L.A.t_gu);
+  bf16* t_down = at<bf16>(act, L.A.t_down);
+  float* part = at<float>(ws, L.part);
+  float* lf = at<float>(ws, L.lf);
+  const float2* rope = at<float2>(ws, L.rope);
+  bf16* tp = at<bf16>(ws, L.tp);
+  bf16* dyb = at<bf16>(ws, L.dyb);
+  bf16* dz = at<bf16>(ws, L.dz);
+  bf16* dgu = at<bf16>(ws, L.dgu);
+  bf16* du = at<bf16>(ws, L.du);
+  float* dxf = at<float>(ws, L.dxf);
+  bf16* dO = at<bf16>(ws, L.dO);
+  bf16* dqkv = at<bf16>(ws, L.dqkv);
+  bf16* wt = at<bf16>(ws, L.wt);
+  bf16* xb = at<bf16>(ws, L.xb);
+  bf16* bt = at<bf16>(ws, L.bt);
+  const int qkv_sites[3] = {0, 1, 2};
+  const int o_site[1] = {3}, gu_sites[2] = {4, 5}, down_site[1] = {6};
+  int off_qkv[3], off_o[1], off_gu[2], off_down[1];
+  int ld_qkv, ld_o, ld_gu, ld_down;
+  lora_offsets(d, w, qkv_sites, 3, off_qkv, ld_qkv);
+  lora_offsets(d, w, o_site, 1, off_o, ld_o);
+  lora_offsets(d, w, gu_sites, 2, off_gu, ld_gu);
+  lora_offsets(d, w, down_site, 1, off_down, ld_down);
+  (void)lse; (void)xmid; (void)eps; (void)lora;
 
   // ---- backward
   int slot[3], n;
@@ -765,6 +837,16 @@ int run_block_bwd(const gen_block_dims& d, const gen_block_weights& w, const flo
   }
   HIP_TRY(rmsnorm_bwd(h, (const bf16*)w.g_in, du, dxf, dh, M, D, eps, s));
   return GEN_OK;
+}
+
+// Gradient of one dense gen block: its training forward into the workspace's activation slot,
+// then the backward from there.
+int run_block_bwd(const gen_block_dims& d, const gen_block_weights& w, const float* h, float* dh, const SeqInfo& si,
+                  const gen_lora_grads& g, void* ws, const Wb& L, hipStream_t s) {
+  void* act = at<char>(ws, L.act);
+  const int rc = block_train_fwd(d, w, h, nullptr, si, act, ws, L, s);
+  if (rc) return rc;
+  return block_train_bwd(d, w, h, dh, si, g, act, ws, L, s);
 }
 
 int check_train_dims(const gen_block_dims* d) {
@@ -1098,7 +1180,7 @@ int gen_block_backward(const gen_block_dims* dims, const gen_block_weights* w, c
 namespace {
 constexpr int LOSS_PARTS = 1024;
 struct Wt {
-  size_t fwd, bwd, saved, dh, pred, dpred, dtok, dhn, parts, woutT, total;
+  size_t fwd, bwd, saved, acts, act_stride, dh, pred, dpred, dtok, dhn, parts, woutT, total;
 };
 Wt layout_train(const gen_block_dims& d, int n_layers, int n_img, int N, int maxp) {
   Wt w{};
@@ -1106,8 +1188,10 @@ Wt layout_train(const gen_block_dims& d, int n_layers, int n_img, int N, int max
   size_t o = 0;
   auto take = [&](size_t bytes) { size_t a = o; o += up(bytes); return a; };
   w.fwd = take(layout(d, n_img, 1, N, maxp).total);
-  w.bwd = take(layout_bwd(d, n_img, N, maxp).total);
+  w.bwd = take(layout_bwd(d, n_img, N, maxp, false).total);
   w.saved = take((size_t)n_layers * M * D * 4);
+  w.act_stride = up(layout_act(d, n_img, N).total);
+  w.acts = take((size_t)n_layers * w.act_stride);
   w.dh = take(M * D * 4);
   w.pred = take(M * 3072 * 4);
   w.dpred = take(M * 3072 * 4);
@@ -1182,12 +1266,17 @@ int gen_tower_lora_train_step(const gen_block_dims* dims, int n_layers, const ge
     p.C = hidden; p.ldc = D; p.bias = at<float>(fws, F.temb); p.rows_per = N; p.n_bcast = 1;
     HIP_TRY(gemm_bf16(p, EPI_BIAS_BCAST_F32, s));
   }
-  HIP_TRY(rope_table(at<float2>(fws, F.rope), F.n_pos, dims->head_dim, dims->rope_theta, s));
+  // the blocks' training forwards: block l reads its input from saved[l], keeps its activations
+  // in slot l and writes its output into saved[l + 1] (the last one into hidden)
+  void* bws = at<char>(workspace, T.bwd);
+  const Wb L = layout_bwd(*dims, n_img, N, maxp, false);
+  float* saved = at<float>(workspace, T.saved);
+  HIP_TRY(hipMemcpyAsync(saved, hidden, (size_t)M * D * 4, hipMemcpyDeviceToDevice, s));
   for (int l = 0; l < n_layers; ++l) {
-    HIP_TRY(hipMemcpyAsync(at<float>(workspace, T.saved) + (size_t)l * M * D, hidden, (size_t)M * D * 4,
-                           hipMemcpyDeviceToDevice, s));
     const SeqInfo si = make_seq(B, N, prefix_k + (size_t)l * B, prefix_v + (size_t)l * B, prefix_len);
-    if ((rc = run_block<bf16, float>(*dims, layers[l], hidden, si, fws, F, nullptr, s))) return rc;
+    float* out = l + 1 < n_layers ? saved + (size_t)(l + 1) * M * D : hidden;
+    void* act = at<char>(workspace, T.acts + (size_t)l * T.act_stride);
+    if ((rc = block_train_fwd(*dims, layers[l], saved + (size_t)l * M * D, out, si, act, bws, L, s))) return rc;
   }
   bf16* u = at<bf16>(fws, F.u);
   HIP_TRY((rmsnorm<float, bf16>(hidden, (const bf16*)g_final, u, M, D, dims->rms_eps, s)));
@@ -1213,13 +1302,11 @@ int gen_tower_lora_train_step(const gen_block_dims* dims, int n_layers, const ge
   }
   float* dh = at<float>(workspace, T.dh);
   HIP_TRY(rmsnorm_bwd(hidden, (const bf16*)g_final, dhn, nullptr, dh, M, D, dims->rms_eps, s));
-  void* bws = at<char>(workspace, T.bwd);
-  const Wb L = layout_bwd(*dims, n_img, N, maxp);
   gen_lora_grads none{};
   for (int l = n_layers - 1; l >= 0; --l) {
     const SeqInfo si = make_seq(B, N, prefix_k + (size_t)l * B, prefix_v + (size_t)l * B, prefix_len);
-    rc = run_block_bwd(*dims, layers[l], at<float>(workspace, T.saved) + (size_t)l * M * D, dh, si,
-                       grads ? grads[l] : none, bws, L, s);
+    void* act = at<char>(workspace, T.acts + (size_t)l * T.act_stride);
+    rc = block_train_bwd(*dims, layers[l], saved + (size_t)l * M * D, dh, si, grads ? grads[l] : none, act, bws, L, s);
     if (rc) return rc;
   }
   return ok();
