@@ -366,11 +366,14 @@ DEVI void epi_row16(const GemmParams& p, int row, int col0, int ncols, float* v)
   }
 }
 
-template <int EPI, bool GROUPED, bool GATHER, int NW>
+template <int EPI, bool GROUPED, bool GATHER, int NW, bool EXT = false>
 __global__ __launch_bounds__(64 * NW, 1) void gemm_fast_kernel(GemmParams p, int n_col_tiles) {
   // NW = 4: 2 x 2 waves of 128 x 128 (one wave per SIMD); NW = 8: 2 x 4 waves of 128 x 64 (two
   // waves per SIMD, so one wave's DMA issue or barrier wait is covered by the other's MFMAs).
   // Each wave tile is a grid of 16 x 16 blocks of v_mfma_f32_16x16x32_bf16.
+  // EXT: the LoRA up-projection as ceil(xk / 64) more k-tiles after the K / 64 of A and B: A rows
+  // from X, B rows from the up-projection of the site that owns each 8-row group of B; a 16-byte
+  // chunk outside X's xk columns or outside the site's xr-wide slice of them loads as zeros.
   constexpr int WN = NW / 2;                 // waves along n
   constexpr int NBW = (BN / WN) / 32;        // 32-column MFMA blocks per wave (4 or 2)
   constexpr int GPW = 32 / NW;               // 8-row load groups per wave per operand
@@ -446,9 +449,43 @@ __global__ __launch_bounds__(64 * NW, 1) void gemm_fast_kernel(GemmParams p, int
   }
   const uint32_t bvoff0 = lrow * ldb2 + lch0 * 16, bvoff1 = lrow * ldb2 + lch1 * 16;
 
+  const int KTM = p.K / BK;                      // k-tiles of A B^T
+  const int KT = KTM + (EXT ? (p.xk + BK - 1) / BK : 0);
+  // K extension: X rows of the tile, and per 8-row group of B its site's up-projection rows
+  __amdgpu_buffer_rsrc_t rx, rbx[EXT ? GPW : 1];
+  uint32_t ldx2 = 0;
+  int bx_lo[EXT ? GPW : 1], bx_hi[EXT ? GPW : 1];
+  if (EXT) {
+    ldx2 = (uint32_t)p.ldx * 2;
+    rx = make_rsrc((const bf16*)p.X + (int64_t)row0 * p.ldx, (uint32_t)rows * ldx2);
+#pragma unroll
+    for (int i = 0; i < GPW; ++i) {
+      const int col = b_row_outcol(p, tn, (wave * GPW + i) * 8);
+      const int site = col < p.xsite_end[0] ? 0 : (col < p.xsite_end[1] ? 1 : 2);
+      const int start = site == 0 ? 0 : p.xsite_end[site - 1];
+      const int nrow = min(8, min(p.xsite_end[site], (p.bmode == 1 ? 2 * p.swiglu_I : p.N)) - col);
+      const bf16* xb = (const bf16*)p.XB[site];
+      rbx[i] = make_rsrc(xb ? xb + (int64_t)(col - start) * p.xr : p.X, (xb && nrow > 0) ? (uint32_t)nrow * p.xr * 2 : 0u);
+      bx_lo[i] = p.xoff[site];                     // X columns [lo, hi) belong to this site
+      bx_hi[i] = p.xoff[site] + p.xr;
+    }
+  }
+
   auto issue = [&](int kt, int stage) {
     char* As = smem + stage * STAGE_BYTES;
     char* Bs = As + BM * BK * 2;
+    if (EXT && kt >= KTM) {
+      const int k0 = (kt - KTM) * BK;              // X column of this extension k-tile
+#pragma unroll
+      for (int i = 0; i < GPW; ++i) {
+        const int grp = wave * GPW + i;
+        const int c = k0 + ((i & 1) ? lch1 : lch0) * 8;   // X column of this lane's chunk
+        dma16(rx, As + grp * 1024, c < p.xk ? lrow * ldx2 + (uint32_t)c * 2 : 0x40000000u, grp * 8 * ldx2);
+        const bool in = c >= bx_lo[i] && c < bx_hi[i];
+        dma16(rbx[i], Bs + grp * 1024, in ? (uint32_t)(lrow * p.xr + c - bx_lo[i]) * 2 : 0x40000000u, 0);
+      }
+      return;
+    }
     const uint32_t kb = (uint32_t)kt * (BK * 2);
 #pragma unroll
     for (int i = 0; i < GPW; ++i) {
@@ -470,7 +507,6 @@ __global__ __launch_bounds__(64 * NW, 1) void gemm_fast_kernel(GemmParams p, int
 #pragma unroll
       for (int e = 0; e < 4; ++e) acc[a][b][e] = 0.f;
 
-  const int KT = p.K / BK;
   // 16x16x32 fragments (v_mfma_f32_16x16x32_bf16): lane l holds row l % 16 of a 16-row block and
   // logical chunk 4 ks + l / 16 of the 32-deep half ks of the 64-deep tile
   const int r16 = lane & 15, c16 = lane >> 4;
@@ -1083,6 +1119,30 @@ hipError_t launch_k32_ext(const GemmParams& p, int epi, int grid, int n_col_tile
   return hipErrorInvalidValue;
 }
 
+// The 64-deep kernel with the K extension (no row gather), for launches up to 8192 deep.
+hipError_t launch_fast_ext(const GemmParams& p, int epi, int grid, int n_col_tiles, hipStream_t s) {
+  const size_t lds = 2 * STAGE_BYTES;
+#define PSF_L(E)                                                                                  \
+  case E: {                                                                                        \
+    auto k = gemm_fast_kernel<E, false, false, 8, true>;                                           \
+    hipError_t e = hipFuncSetAttribute((const void*)k, hipFuncAttributeMaxDynamicSharedMemorySize, \
+                                       (int)lds);                                                  \
+    if (e != hipSuccess) return e;                                                                 \
+    hipLaunchKernelGGL(k, dim3(grid), dim3(512), lds, s, p, n_col_tiles);                          \
+    return hipGetLastError();                                                                      \
+  }
+  switch (epi) {
+    PSF_L(EPI_STORE)
+    PSF_L(EPI_RESID)
+    PSF_L(EPI_SWIGLU)
+    PSF_L(EPI_RESID_TO_F32)
+    PSF_L(EPI_RESID_FROM_F32)
+    PSF_L(EPI_RESID_F32)
+  }
+#undef PSF_L
+  return hipErrorInvalidValue;
+}
+
 template <bool GROUPED, bool EXT>
 hipError_t launch_bf16(const GemmParams& p, int epi, int grid, int n_col_tiles, hipStream_t s) {
   const size_t lds = 2 * STAGE_BYTES;
@@ -1191,7 +1251,10 @@ hipError_t gemm_bf16(const GemmParams& p, int epi, hipStream_t s) {
     return hipGetLastError();
   }
   if (p.X && p.xk > 0) {
-    if (k32_ext_ok(p, epi)) return launch_k32_ext(p, epi, n_m * n_cols, n_cols, s);
+    if (k32_ext_ok(p, epi)) {
+      if (p.K < 8192 && p.K % BK == 0) return launch_fast_ext(p, epi, n_m * n_cols, n_cols, s);
+      return launch_k32_ext(p, epi, n_m * n_cols, n_cols, s);
+    }
     return launch_bf16<false, true>(p, epi, n_m * n_cols, n_cols, s);
   }
   if (p.bmode == 2) return launch_bf16<false, false>(p, epi, n_m * n_cols, n_cols, s);
