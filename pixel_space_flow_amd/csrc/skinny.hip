@@ -2,13 +2,15 @@
 //
 // Skinny GEMM (the down-projections): C[m, n] = scale sum_k A[m, k] B[n, k] with N <= 128 output
 // columns (rank r, or up to three sites of rank r side by side).  A 256 x 256 tile GEMM gives such
-// a product only M/256 workgroups; here one wave owns 32 rows x N columns over one k-range, the
-// k-ranges split K so that about 2048 waves run, and a second pass adds the partial sums in a
-// fixed order (no atomics), scales and rounds once to bf16.
+// a product only M/256 workgroups; here one wave owns 32 rows x N columns over one k-range (four
+// waves of consecutive row blocks per workgroup share the k-range, so their B loads meet in the
+// L1 cache), the k-ranges split K so that about 2048 waves run, and a second pass adds the
+// partial sums in a fixed order (no atomics), scales and rounds once to bf16.
 //
-// Fragments of v_mfma_f32_32x32x16_bf16 come straight from global memory: lane l reads 16 bytes of
-// row (l % 32) at k offset 8 (l / 32), four k-steps per iteration, so each row is read as one
-// contiguous 128-byte piece; the next iteration's loads are issued before this one's MFMAs.
+// Per 64-deep step a wave loads its 32 A rows as whole 128-byte rows (8 rows per instruction),
+// passes them through LDS into the v_mfma_f32_32x32x16_bf16 fragment layout (lane l: row l % 32,
+// k offset 8 (l / 32)), and takes its B fragments straight from global memory in that layout; the
+// next step's loads are issued before this one's MFMAs.
 #include "common.h"
 #include "gemm.h"
 #include "kernels.h"
@@ -17,14 +19,20 @@ namespace psf {
 namespace {
 
 template <int NB>
-__global__ __launch_bounds__(64) void skinny_kernel(const bf16* __restrict__ A, int64_t lda, const bf16* __restrict__ B0,
-                                                    const bf16* __restrict__ B1, const bf16* __restrict__ B2,
-                                                    int64_t ldb, int seg_rows, int M, int N, int K, int kchunk,
-                                                    float* __restrict__ part) {
-  const int lane = threadIdx.x, lr = lane & 31, lh = lane >> 5;
-  const int m0 = blockIdx.x * 32, z = blockIdx.y;
+__global__ __launch_bounds__(256) void skinny_kernel(const bf16* __restrict__ A, int64_t lda, const bf16* __restrict__ B0,
+                                                     const bf16* __restrict__ B1, const bf16* __restrict__ B2,
+                                                     int64_t ldb, int seg_rows, int M, int N, int K, int kchunk,
+                                                     float* __restrict__ part) {
+  __shared__ __attribute__((aligned(16))) char sa[4][32 * 128];   // one 32-row x 64-deep A step per wave
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, lr = lane & 31, lh = lane >> 5;
+  const int m0 = blockIdx.x * 128 + w * 32, z = blockIdx.y;
+  if (m0 >= M) return;                          // no workgroup barrier below
   const int k_lo = z * kchunk, k_hi = min(K, k_lo + kchunk);
-  const bf16* ap = A + (int64_t)min(m0 + lr, M - 1) * lda + lh * 8;
+  char* my = sa[w];
+  // A: load i brings rows 8i .. 8i + 7, lane l the 16-byte chunk l % 8 of row 8i + l / 8
+  const bf16* ap[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) ap[i] = A + (int64_t)min(m0 + i * 8 + (lane >> 3), M - 1) * lda + (lane & 7) * 8;
   const bf16* bp[NB];
   bool bok[NB];
 #pragma unroll
@@ -46,7 +54,7 @@ __global__ __launch_bounds__(64) void skinny_kernel(const bf16* __restrict__ A, 
   auto load = [&](int k, bf16x8 (&ao)[4], bf16x8 (&bo)[NB][4]) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      ao[i] = *(const bf16x8*)(ap + k + 16 * i);
+      ao[i] = *(const bf16x8*)(ap[i] + k);
 #pragma unroll
       for (int nb = 0; nb < NB; ++nb) bo[nb][i] = bok[nb] ? *(const bf16x8*)(bp[nb] + k + 16 * i) : zero;
     }
@@ -54,11 +62,23 @@ __global__ __launch_bounds__(64) void skinny_kernel(const bf16* __restrict__ A, 
   if (k_lo < k_hi) load(k_lo, a, b);
   for (int k = k_lo; k < k_hi; k += 64) {
     const bool more = k + 64 < k_hi;
+    // the wave's A rows through LDS (chunk c of row r stored at c ^ (r & 7)), read back as
+    // fragments: lane l takes row l % 32 at k offset 16 i + 8 (l / 32)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int r = i * 8 + (lane >> 3);
+      *(bf16x8*)(my + r * 128 + (((lane & 7) ^ (r & 7)) << 4)) = a[i];
+    }
+    __builtin_amdgcn_wave_barrier();
+    bf16x8 fa[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) fa[i] = *(const bf16x8*)(my + lr * 128 + (((2 * i + lh) ^ (lr & 7)) << 4));
+    __builtin_amdgcn_wave_barrier();
     if (more) load(k + 64, an, bn);
 #pragma unroll
     for (int i = 0; i < 4; ++i)
 #pragma unroll
-      for (int nb = 0; nb < NB; ++nb) acc[nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[i], b[nb][i], acc[nb], 0, 0, 0);
+      for (int nb = 0; nb < NB; ++nb) acc[nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[i], b[nb][i], acc[nb], 0, 0, 0);
     if (more) {
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
@@ -170,8 +190,8 @@ hipError_t gemm_lowrank(const bf16* X, int64_t ldx, const bf16* Y, int64_t ldy, 
 }
 
 int skinny_splits(int M, int K) {
-  const int waves_m = (M + 31) / 32;
-  int splits = (2048 + waves_m - 1) / waves_m;
+  const int groups_m = (M + 31) / 32;
+  int splits = (2048 + groups_m - 1) / groups_m;
   splits = std::min(splits, std::max(1, K / 256));
   return std::min(std::max(splits, 1), SKINNY_MAX_SPLITS);
 }
@@ -187,10 +207,10 @@ hipError_t gemm_skinny(const GemmParams& p, float* part, hipStream_t s) {
   const int splits = skinny_splits(p.M, p.K);
   const int kchunk = (p.K / 64 + splits - 1) / splits * 64;
   const int nz = (p.K + kchunk - 1) / kchunk;
-  const dim3 grid((p.M + 31) / 32, nz);
+  const dim3 grid((p.M + 127) / 128, nz);
   const int nb = (p.N + 31) / 32;
 #define PSF_SK(NBV)                                                                                      \
-  hipLaunchKernelGGL(skinny_kernel<NBV>, grid, dim3(64), 0, s, (const bf16*)p.A, p.lda, B0, B1, B2, p.ldb, \
+  hipLaunchKernelGGL(skinny_kernel<NBV>, grid, dim3(256), 0, s, (const bf16*)p.A, p.lda, B0, B1, B2, p.ldb, \
                      seg_rows, p.M, p.N, p.K, kchunk, part)
   if (nb == 1) PSF_SK(1);
   else if (nb == 2) PSF_SK(2);
