@@ -623,8 +623,18 @@ int lora_wgrad(const gen_block_dims& d, const gen_lora_grads& g, const BackSite*
     if (slot[i] < 0) continue;
     const int st = sites[i].site;
     HIP_TRY(wgrad(dY + sites[i].col, lddy, t + toff[i], ldt, M, sites[i].out, r, g.lora_b[st], part, s));
-    HIP_TRY(wgrad(tp + slot[i] * r, n * r, x, in, M, r, in, g.lora_a[st], part, s));
   }
+  // the A gradients of the sites sharing the input x: one pass over x with their dT side by side
+  // (slot order), the row blocks of the product going to the sites' gradients
+  if (n >= 2 && n * r <= 128) {
+    float* dst[3] = {nullptr, nullptr, nullptr};
+    for (int i = 0; i < ns; ++i)
+      if (slot[i] >= 0) dst[slot[i]] = g.lora_a[sites[i].site];
+    HIP_TRY(wgrad_seg(tp, n * r, x, in, M, n * r, in, r, dst, part, s));
+    return GEN_OK;
+  }
+  for (int i = 0; i < ns; ++i)
+    if (slot[i] >= 0) HIP_TRY(wgrad(tp + slot[i] * r, n * r, x, in, M, r, in, g.lora_a[sites[i].site], part, s));
   return GEN_OK;
 }
 
@@ -730,7 +740,8 @@ int block_train_fwd(const gen_block_dims& d, const gen_block_weights& w, const f
 // block input [M, D] fp32; dh: in, dL/d(block output); out, dL/d(block input).  LoRA gradients
 // accumulate into g.
 int block_train_bwd(const gen_block_dims& d, const gen_block_weights& w, const float* h, float* dh,
-                    const SeqInfo& si, const gen_lora_grads& g, void* act, void* ws, const Wb& L, hipStream_t s) {
+                    const SeqInfo& si, const gen_lora_grads& g, void* act, void* ws, const Wb& L, hipStream_t s,
+                    bool dyb_ready) {
   const int B = si.B, N = si.N, M = B * N, D = d.hidden, I = d.mlp_intermediate, r = d.lora_rank;
   const int Hq = d.n_q_heads, Hkv = d.n_kv_heads, hd = d.head_dim;
   const int QD = Hq * hd, KVD = Hkv * hd, QKV = QD + 2 * KVD;
@@ -775,7 +786,7 @@ int block_train_bwd(const gen_block_dims& d, const gen_block_weights& w, const f
 
   // ---- backward
   int slot[3], n;
-  HIP_TRY(cast_f32_bf16(dh, dyb, (int64_t)M * D, s));
+  if (!dyb_ready) HIP_TRY(cast_f32_bf16(dh, dyb, (int64_t)M * D, s));
   {  // down projection: dz = dy W_down (+ LoRA)
     const BackSite bs[1] = {{6, 0, D}};
     GemmParams p = gp();
@@ -803,8 +814,7 @@ int block_train_bwd(const gen_block_dims& d, const gen_block_weights& w, const f
       if (rc) return rc;
     }
   }
-  HIP_TRY(rmsnorm_bwd(xmid, (const bf16*)w.g_post, du, dh, dxf, M, D, eps, s));
-  HIP_TRY(cast_f32_bf16(dxf, dyb, (int64_t)M * D, s));
+  HIP_TRY(rmsnorm_bwd(xmid, (const bf16*)w.g_post, du, dh, dxf, M, D, eps, s, dyb));
   {  // O projection: dO = dx W_o (+ LoRA)
     const BackSite bs[1] = {{3, 0, D}};
     GemmParams p = gp();
@@ -835,7 +845,8 @@ int block_train_bwd(const gen_block_dims& d, const gen_block_weights& w, const f
       if (rc) return rc;
     }
   }
-  HIP_TRY(rmsnorm_bwd(h, (const bf16*)w.g_in, du, dxf, dh, M, D, eps, s));
+  // dL/d(block input), and its bf16 copy in dyb for the next block down the tower
+  HIP_TRY(rmsnorm_bwd(h, (const bf16*)w.g_in, du, dxf, dh, M, D, eps, s, dyb));
   return GEN_OK;
 }
 
@@ -846,7 +857,7 @@ int run_block_bwd(const gen_block_dims& d, const gen_block_weights& w, const flo
   void* act = at<char>(ws, L.act);
   const int rc = block_train_fwd(d, w, h, nullptr, si, act, ws, L, s);
   if (rc) return rc;
-  return block_train_bwd(d, w, h, dh, si, g, act, ws, L, s);
+  return block_train_bwd(d, w, h, dh, si, g, act, ws, L, s, false);
 }
 
 int check_train_dims(const gen_block_dims* d) {
@@ -1301,12 +1312,13 @@ int gen_tower_lora_train_step(const gen_block_dims* dims, int n_layers, const ge
     HIP_TRY(gemm_bf16(p, EPI_STORE, s));
   }
   float* dh = at<float>(workspace, T.dh);
-  HIP_TRY(rmsnorm_bwd(hidden, (const bf16*)g_final, dhn, nullptr, dh, M, D, dims->rms_eps, s));
+  HIP_TRY(rmsnorm_bwd(hidden, (const bf16*)g_final, dhn, nullptr, dh, M, D, dims->rms_eps, s, at<bf16>(bws, L.dyb)));
   gen_lora_grads none{};
   for (int l = n_layers - 1; l >= 0; --l) {
     const SeqInfo si = make_seq(B, N, prefix_k + (size_t)l * B, prefix_v + (size_t)l * B, prefix_len);
     void* act = at<char>(workspace, T.acts + (size_t)l * T.act_stride);
-    rc = block_train_bwd(*dims, layers[l], saved + (size_t)l * M * D, dh, si, grads ? grads[l] : none, act, bws, L, s);
+    rc = block_train_bwd(*dims, layers[l], saved + (size_t)l * M * D, dh, si, grads ? grads[l] : none, act, bws, L, s,
+                         true);
     if (rc) return rc;
   }
   return ok();

@@ -116,6 +116,48 @@ __global__ __launch_bounds__(256) void rmsnorm_bwd_kernel(const float* __restric
   }
 }
 
+// The same for D a multiple of 4: four columns per thread (16-byte x, base and out, 8-byte g and
+// dy); outb, when set, receives bf16(out) as well.
+__global__ __launch_bounds__(256) void rmsnorm_bwd4_kernel(const float* __restrict__ x, const bf16* __restrict__ g,
+                                                           const bf16* __restrict__ dy, const float* base, float* out,
+                                                           bf16* __restrict__ outb, int D, float eps) {
+  __shared__ float red[4];
+  const int64_t row = blockIdx.x;
+  const float* xr = x + row * D;
+  const bf16* dr = dy + row * D;
+  float ss = 0.f, sgx = 0.f;
+  for (int i = threadIdx.x * 4; i < D; i += 1024) {
+    const f32x4 xv = *(const f32x4*)(xr + i);
+    const bf16x4 gv = *(const bf16x4*)(g + i), dv = *(const bf16x4*)(dr + i);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const float gd = static_cast<float>(gv[e]) * static_cast<float>(dv[e]);
+      ss += xv[e] * xv[e];
+      sgx += gd * xv[e];
+    }
+  }
+  ss = block_sum256(ss, red);
+  sgx = block_sum256(sgx, red);
+  const float r = 1.0f / sqrtf(ss / (float)D + eps);
+  const float c = r * r * r * sgx / (float)D;
+  for (int i = threadIdx.x * 4; i < D; i += 1024) {
+    const f32x4 xv = *(const f32x4*)(xr + i);
+    const bf16x4 gv = *(const bf16x4*)(g + i), dv = *(const bf16x4*)(dr + i);
+    f32x4 b = {0.f, 0.f, 0.f, 0.f};
+    if (base) b = *(const f32x4*)(base + row * D + i);
+    f32x4 o;
+    bf16x4 ob;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const float gd = static_cast<float>(gv[e]) * static_cast<float>(dv[e]);
+      o[e] = b[e] + (r * gd - xv[e] * c);
+      ob[e] = static_cast<bf16>(o[e]);
+    }
+    *(f32x4*)(out + row * D + i) = o;
+    if (outb) *(bf16x4*)(outb + row * D + i) = ob;
+  }
+}
+
 // z[m, j] = silu(gu[m, j]) gu[m, I + j]
 __global__ __launch_bounds__(256) void swiglu_kernel(const bf16* __restrict__ gu, bf16* __restrict__ z, int I, int64_t n) {
   const int64_t t = (int64_t)blockIdx.x * 256 + threadIdx.x;
@@ -720,6 +762,18 @@ __global__ __launch_bounds__(256) void wgrad_reduce_kernel(const float* __restri
   C[i] += s;
 }
 
+// The same with the rows of C in blocks of seg elements (seg_rows rows), block k added into Ck.
+__global__ __launch_bounds__(256) void wgrad_reduce_seg_kernel(const float* __restrict__ part, int splits, int64_t n,
+                                                               int64_t seg, float* C0, float* C1, float* C2) {
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (i >= n) return;
+  float s = 0.f;
+  for (int z = 0; z < splits; ++z) s += part[(int64_t)z * n + i];
+  const int k = (int)(i / seg);
+  float* C = k == 0 ? C0 : (k == 1 ? C1 : C2);
+  C[i - k * seg] += s;
+}
+
 // ---------------------------------------------------------------- x0 loss
 // part[block] = sum of (pred - tgt)^2 over the block's elements; grad = 2 (pred - tgt) / n
 __global__ __launch_bounds__(256) void x0_loss_kernel(const float* __restrict__ pred, const float* __restrict__ tgt,
@@ -760,14 +814,24 @@ hipError_t cast_f32_bf16(const float* x, bf16* y, int64_t n, hipStream_t s) {
   return hipGetLastError();
 }
 
+static bool aligned16(const void* p) { return ((uintptr_t)p & 15) == 0; }
+
 hipError_t rmsnorm_bwd(const float* x, const bf16* g, const bf16* dy, const float* base, float* out, int rows, int D,
-                       float eps, hipStream_t s) {
+                       float eps, hipStream_t s, bf16* outb) {
   if (rows <= 0) return hipSuccess;
+  if (D % 4 == 0 && aligned16(x) && aligned16(out) && (!base || aligned16(base)) && ((uintptr_t)g & 7) == 0 &&
+      ((uintptr_t)dy & 7) == 0 && ((uintptr_t)outb & 7) == 0) {
+    hipLaunchKernelGGL(rmsnorm_bwd4_kernel, dim3(rows), dim3(256), 0, s, x, g, dy, base, out, outb, D, eps);
+    return hipGetLastError();
+  }
   hipLaunchKernelGGL(rmsnorm_bwd_kernel, dim3(rows), dim3(256), 0, s, x, g, dy, base, out, D, eps);
+  if (outb) {
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    return cast_f32_bf16(out, outb, (int64_t)rows * D, s);
+  }
   return hipGetLastError();
 }
-
-static bool aligned16(const void* p) { return ((uintptr_t)p & 15) == 0; }
 
 hipError_t swiglu_fwd(const bf16* gu, bf16* z, int M, int I, hipStream_t s) {
   const int64_t n = (int64_t)M * I;
@@ -831,25 +895,45 @@ int wgrad_splits(int M, int N1, int N2) {
   return splits;
 }
 
+// One side is the rank: stream the other side in 128-column blocks, about 512 workgroups, the
+// partial products [nz, N1, N2] within WGRAD_PART_FLOATS.  Returns nz.
+static int wgrad_lr_launch(const bf16* X, int64_t ldx, const bf16* Y, int64_t ldy, int M, int N1, int N2, float* part,
+                           hipStream_t s) {
+  const int64_t n = (int64_t)N1 * N2;
+  const int R = std::min(N1, N2), NB = std::max(N1, N2);
+  const int nblk = (NB + 127) / 128;
+  int splits = std::max(1, 512 / nblk);
+  splits = std::min(splits, std::max(1, (M + 127) / 128));
+  splits = (int)std::min<int64_t>(splits, std::max<int64_t>(1, WGRAD_PART_FLOATS / n));
+  const int per = ((M + splits - 1) / splits + 31) / 32 * 32;
+  const int nz = (M + per - 1) / per;
+  if (N1 >= N2)
+    hipLaunchKernelGGL(wgrad_lr_kernel<true>, dim3(nblk, nz), dim3(256), 0, s, X, ldx, Y, ldy, M, NB, R, per, part);
+  else
+    hipLaunchKernelGGL(wgrad_lr_kernel<false>, dim3(nblk, nz), dim3(256), 0, s, Y, ldy, X, ldx, M, NB, R, per, part);
+  return nz;
+}
+
+hipError_t wgrad_seg(const bf16* X, int64_t ldx, const bf16* Y, int64_t ldy, int M, int N1, int N2, int seg_rows,
+                     float* const* C, float* part, hipStream_t s) {
+  if (M <= 0 || N1 <= 0 || N2 <= 0) return hipSuccess;
+  if (N1 % 8 || N2 % 8 || ldx % 8 || ldy % 8 || N1 > 128 || seg_rows <= 0 || N1 % seg_rows || N1 / seg_rows > 3)
+    return hipErrorInvalidValue;
+  const int64_t n = (int64_t)N1 * N2;
+  const int nz = wgrad_lr_launch(X, ldx, Y, ldy, M, N1, N2, part, s);
+  const int ns = N1 / seg_rows;
+  hipLaunchKernelGGL(wgrad_reduce_seg_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, (const float*)part, nz,
+                     n, (int64_t)seg_rows * N2, C[0], ns > 1 ? C[1] : C[0], ns > 2 ? C[2] : C[0]);
+  return hipGetLastError();
+}
+
 hipError_t wgrad(const bf16* X, int64_t ldx, const bf16* Y, int64_t ldy, int M, int N1, int N2, float* C, float* part,
                  hipStream_t s) {
   if (M <= 0 || N1 <= 0 || N2 <= 0) return hipSuccess;
   if (N1 % 8 || N2 % 8 || ldx % 8 || ldy % 8) return hipErrorInvalidValue;
   const int64_t n = (int64_t)N1 * N2;
-  const int R = std::min(N1, N2), NB = std::max(N1, N2);
-  if (R <= 128) {
-    // one side is the rank: stream the other side in 128-column blocks, about 512 workgroups,
-    // the partial products within WGRAD_PART_FLOATS
-    const int nblk = (NB + 127) / 128;
-    int splits = std::max(1, 512 / nblk);
-    splits = std::min(splits, std::max(1, (M + 127) / 128));
-    splits = (int)std::min<int64_t>(splits, std::max<int64_t>(1, WGRAD_PART_FLOATS / n));
-    const int per = ((M + splits - 1) / splits + 31) / 32 * 32;
-    const int nz = (M + per - 1) / per;
-    if (N1 >= N2)
-      hipLaunchKernelGGL(wgrad_lr_kernel<true>, dim3(nblk, nz), dim3(256), 0, s, X, ldx, Y, ldy, M, NB, R, per, part);
-    else
-      hipLaunchKernelGGL(wgrad_lr_kernel<false>, dim3(nblk, nz), dim3(256), 0, s, Y, ldy, X, ldx, M, NB, R, per, part);
+  if (std::min(N1, N2) <= 128) {
+    const int nz = wgrad_lr_launch(X, ldx, Y, ldy, M, N1, N2, part, s);
     hipLaunchKernelGGL(wgrad_reduce_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, (const float*)part, nz, n,
                        C);
     return hipGetLastError();

@@ -76,9 +76,10 @@ hipError_t cfg_euler(float* xo, const float* x, const float* xc, const float* xm
 // ---- training backward (backward.hip)
 hipError_t transpose_bf16(const bf16* in, int64_t ldi, bf16* out, int64_t ldo, int R, int C, hipStream_t s);
 hipError_t cast_f32_bf16(const float* x, bf16* y, int64_t n, hipStream_t s);
-// out = base + (dRMSNorm(x; g))^T dy per row of D (base may alias out or be null)
+// out = base + (dRMSNorm(x; g))^T dy per row of D (base may alias out or be null); outb, when set,
+// also receives bf16(out)
 hipError_t rmsnorm_bwd(const float* x, const bf16* g, const bf16* dy, const float* base, float* out, int rows, int D,
-                       float eps, hipStream_t s);
+                       float eps, hipStream_t s, bf16* outb = nullptr);
 hipError_t swiglu_fwd(const bf16* gu, bf16* z, int M, int I, hipStream_t s);
 hipError_t swiglu_bwd(const bf16* gu, const bf16* dz, bf16* dgu, int M, int I, hipStream_t s);
 // dqkv = gradient with respect to the raw q, k heads (through RoPE and the per-head norm) and v
@@ -94,6 +95,10 @@ constexpr int64_t WGRAD_PART_FLOATS = (int64_t)4 << 20;
 int wgrad_splits(int M, int N1, int N2);
 hipError_t wgrad(const bf16* X, int64_t ldx, const bf16* Y, int64_t ldy, int M, int N1, int N2, float* C, float* part,
                  hipStream_t s);
+// As wgrad with N1 <= 128 split into up to three blocks of seg_rows rows, block k added into C[k]
+// ([seg_rows, N2] each)
+hipError_t wgrad_seg(const bf16* X, int64_t ldx, const bf16* Y, int64_t ldy, int M, int N1, int N2, int seg_rows,
+                     float* const* C, float* part, hipStream_t s);
 hipError_t x0_loss(const float* pred, const float* tgt, float* grad, float* part, int nparts, float* loss, int64_t n,
                    hipStream_t s);
 
