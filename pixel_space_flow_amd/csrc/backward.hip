@@ -271,6 +271,77 @@ __global__ __launch_bounds__(256) void qknorm_rope_bwd_kernel(const bf16* __rest
   }
 }
 
+// The same for d = 128: 16 lanes per (token, head), four heads per wave; lane j holds the rotation
+// pairs 4j .. 4j + 3 (elements 4j .. 4j + 3 and 64 + 4j .. 64 + 4j + 3), 16-byte gradient loads.
+__global__ __launch_bounds__(256) void qknorm_rope_bwd128_kernel(const bf16* __restrict__ raw, int64_t ldr,
+                                                                 const float* __restrict__ dq, const float* __restrict__ dk,
+                                                                 const float* __restrict__ dv, SeqInfo si, int Hq, int Hkv,
+                                                                 const bf16* __restrict__ gq, const bf16* __restrict__ gk,
+                                                                 const float2* __restrict__ table, float eps,
+                                                                 bf16* __restrict__ dqkv, int64_t ldo, int64_t total) {
+  constexpr int d = 128, half = 64;
+  const int lane = threadIdx.x & 63, j = lane & 15;
+  const int64_t hv = (int64_t)blockIdx.x * 16 + (threadIdx.x >> 4);
+  const bool valid = hv < total;                 // no early return: the reductions use all 64 lanes
+  const int H = Hq + 2 * Hkv;
+  const int64_t hvc = valid ? hv : 0;
+  const int64_t tok = hvc / H;
+  const int head = (int)(hvc - tok * H);
+  const int b = (int)(tok / si.N), n = (int)(tok - (int64_t)b * si.N);
+  bf16* op = dqkv + tok * ldo + (int64_t)head * d;
+  const int p0 = 4 * j;
+  if (head >= Hq + Hkv) {                        // v: the gradient passes through (uniform per 16 lanes)
+    const float* gp = dv + tok * (int64_t)Hkv * d + (int64_t)(head - Hq - Hkv) * d + 8 * j;
+    const f32x4 a = *(const f32x4*)gp, c = *(const f32x4*)(gp + 4);
+    bf16x8 o;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) { o[e] = static_cast<bf16>(a[e]); o[4 + e] = static_cast<bf16>(c[e]); }
+    if (valid) *(bf16x8*)(op + 8 * j) = o;
+  }
+  const bool isq = head < Hq, isk = !isq && head < Hq + Hkv;
+  float ss = 0.f, sgx = 0.f;
+  f32x4 ta, tb, xa, xb, wa, wb;
+  if (isq || isk) {
+    const float* gp = isq ? dq + tok * (int64_t)Hq * d + (int64_t)head * d : dk + tok * (int64_t)Hkv * d + (int64_t)(head - Hq) * d;
+    const bf16* rp = raw + tok * ldr + (int64_t)head * d;
+    const bf16* g = isq ? gq : gk;
+    const f32x4 ga = *(const f32x4*)(gp + p0), gb = *(const f32x4*)(gp + half + p0);
+    const bf16x4 ra = *(const bf16x4*)(rp + p0), rb = *(const bf16x4*)(rp + half + p0);
+    const bf16x4 va = *(const bf16x4*)(g + p0), vb = *(const bf16x4*)(g + half + p0);
+    const float2* cs = table + (int64_t)(si.plen[b] + n) * half + p0;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const float2 c = cs[e];
+      // inverse rotation of the incoming gradient
+      ta[e] = ga[e] * c.x + gb[e] * c.y;
+      tb[e] = -ga[e] * c.y + gb[e] * c.x;
+      xa[e] = static_cast<float>(ra[e]);
+      xb[e] = static_cast<float>(rb[e]);
+      wa[e] = static_cast<float>(va[e]);
+      wb[e] = static_cast<float>(vb[e]);
+      ss += xa[e] * xa[e] + xb[e] * xb[e];
+      sgx += wa[e] * ta[e] * xa[e] + wb[e] * tb[e] * xb[e];
+    }
+  }
+#pragma unroll
+  for (int o = 8; o > 0; o >>= 1) {              // sums over the 16 lanes of this head
+    ss += __shfl_xor(ss, o, 64);
+    sgx += __shfl_xor(sgx, o, 64);
+  }
+  if (valid && (isq || isk)) {
+    const float r = 1.0f / sqrtf(ss / (float)d + eps);
+    const float c = r * r * r * sgx / (float)d;
+    bf16x4 oa, ob;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      oa[e] = static_cast<bf16>(r * wa[e] * ta[e] - xa[e] * c);
+      ob[e] = static_cast<bf16>(r * wb[e] * tb[e] - xb[e] * c);
+    }
+    *(bf16x4*)(op + p0) = oa;
+    *(bf16x4*)(op + half + p0) = ob;
+  }
+}
+
 // D[(b*Hq + h)*N + n] = sum_i dO[tok, h*d + i] O[tok, h*d + i]: one wave per (token, head)
 __global__ __launch_bounds__(256) void attn_bwd_dot_kernel(const bf16* __restrict__ dO, const bf16* __restrict__ O,
                                                            int64_t ld, int Hq, int d, int N, float* __restrict__ Dq,
@@ -774,6 +845,29 @@ __global__ __launch_bounds__(256) void wgrad_reduce_seg_kernel(const float* __re
   C[i - k * seg] += s;
 }
 
+// The same for d = 128: 16 lanes per (token, head) with 16-byte loads, four heads per wave.
+__global__ __launch_bounds__(256) void attn_bwd_dot128_kernel(const bf16* __restrict__ dO, const bf16* __restrict__ O,
+                                                              int64_t ld, int Hq, int N, float* __restrict__ Dq,
+                                                              int64_t total) {
+  const int lane = threadIdx.x & 63, j = lane & 15;
+  const int64_t hv = (int64_t)blockIdx.x * 16 + (threadIdx.x >> 4);
+  const bool valid = hv < total;
+  const int64_t hvc = valid ? hv : 0;
+  const int64_t tok = hvc / Hq;
+  const int h = (int)(hvc - tok * Hq);
+  const bf16x8 a = *(const bf16x8*)(dO + tok * ld + (int64_t)h * 128 + 8 * j);
+  const bf16x8 c = *(const bf16x8*)(O + tok * ld + (int64_t)h * 128 + 8 * j);
+  float acc = 0.f;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) acc += static_cast<float>(a[e]) * static_cast<float>(c[e]);
+#pragma unroll
+  for (int o = 8; o > 0; o >>= 1) acc += __shfl_xor(acc, o, 64);
+  if (valid && j == 0) {
+    const int64_t b = tok / N, n = tok - b * N;
+    Dq[(b * Hq + h) * N + n] = acc;
+  }
+}
+
 // ---------------------------------------------------------------- x0 loss
 // part[block] = sum of (pred - tgt)^2 over the block's elements; grad = 2 (pred - tgt) / n
 __global__ __launch_bounds__(256) void x0_loss_kernel(const float* __restrict__ pred, const float* __restrict__ tgt,
@@ -863,8 +957,15 @@ hipError_t qknorm_rope_bwd(const bf16* raw, int64_t ldr, const float* dq, const 
   const int64_t total = (int64_t)si.B * si.N * (Hq + 2 * Hkv);
   if (total == 0) return hipSuccess;
   if (d > 128 || d % 2) return hipErrorInvalidValue;
-  hipLaunchKernelGGL(qknorm_rope_bwd_kernel, dim3((unsigned)((total + 3) / 4)), dim3(256), 0, s, raw, ldr, dq, dk, dv,
-                     si, Hq, Hkv, d, gq, gk, table, eps, dqkv, ldo, total);
+  const bool vec = d == 128 && ldr % 8 == 0 && ldo % 8 == 0 && ((uintptr_t)raw & 15) == 0 && ((uintptr_t)dqkv & 15) == 0 &&
+                   ((uintptr_t)dq & 15) == 0 && ((uintptr_t)dk & 15) == 0 && ((uintptr_t)dv & 15) == 0 &&
+                   ((uintptr_t)gq & 7) == 0 && ((uintptr_t)gk & 7) == 0;
+  if (vec)
+    hipLaunchKernelGGL(qknorm_rope_bwd128_kernel, dim3((unsigned)((total + 15) / 16)), dim3(256), 0, s, raw, ldr, dq, dk,
+                       dv, si, Hq, Hkv, gq, gk, table, eps, dqkv, ldo, total);
+  else
+    hipLaunchKernelGGL(qknorm_rope_bwd_kernel, dim3((unsigned)((total + 3) / 4)), dim3(256), 0, s, raw, ldr, dq, dk, dv,
+                       si, Hq, Hkv, d, gq, gk, table, eps, dqkv, ldo, total);
   return hipGetLastError();
 }
 
@@ -875,7 +976,10 @@ hipError_t attention_bwd(const bf16* qkv, int64_t ldq, const SeqInfo& si, int Hq
   if (d != 128) return hipErrorInvalidValue;
   const int64_t QD = (int64_t)Hq * d;
   const int64_t tot = (int64_t)B * N * Hq;
-  hipLaunchKernelGGL(attn_bwd_dot_kernel, dim3((unsigned)((tot + 3) / 4)), dim3(256), 0, s, dO, O, QD, Hq, d, N, Dq, tot);
+  if (QD % 8 == 0 && ((uintptr_t)dO & 15) == 0 && ((uintptr_t)O & 15) == 0)
+    hipLaunchKernelGGL(attn_bwd_dot128_kernel, dim3((unsigned)((tot + 15) / 16)), dim3(256), 0, s, dO, O, QD, Hq, N, Dq, tot);
+  else
+    hipLaunchKernelGGL(attn_bwd_dot_kernel, dim3((unsigned)((tot + 3) / 4)), dim3(256), 0, s, dO, O, QD, Hq, d, N, Dq, tot);
   const float scale = 1.0f / sqrtf((float)d);
   const float scale_log2 = 1.4426950408889634f * scale;
   const int nkb = (N + 127) / 128, nqb = (N + 31) / 32;
