@@ -555,8 +555,8 @@ Wb layout_bwd(const gen_block_dims& d, int B, int N, int max_prefix, bool with_a
   w.dv = take(M * KVD * 4);
   w.dqkv = take(M * QKV * 2);
   w.wt = take(std::max(std::max(QKV * D, QD * D), std::max(2 * I * D, I * D)) * 2);
-  w.xb = take(std::max(std::max(D, I), QD) * 3 * r * 2);
-  w.bt = take(r * std::max(std::max(QD, D), I) * 2);
+  w.xb = take(((size_t)D * 3 + QD + (size_t)D * 2 + I) * r * 2);   // A^T of the qkv, o, gate/up, down groups
+  w.bt = take((size_t)r * (QKV + D + 2 * I + D) * 2);               // B^T of every site
   w.lf = take(r ? M * std::max(std::max(QKV, 2 * I), std::max(D, QD)) * 4 : 0);
   w.part = take(std::max(std::max((size_t)WGRAD_PART_FLOATS, r * std::max(std::max(QD, D), I)),
                          r ? skinny_part_floats((int)M, (int)std::min<size_t>(3 * r, 128)) : 0) * 4);
@@ -578,7 +578,7 @@ struct BackSite {
 // list order); with none, p is untouched and the GEMM runs with a plain store.
 int lora_back(const gen_block_dims& d, const gen_block_weights& w, const BackSite* sites, int ns, const bf16* dY,
               int lddy, int in, int M, bf16* tp, bf16* xb, bf16* bt, GemmParams& p, int* slot, float* part,
-              float* lf, hipStream_t s) {
+              float* lf, hipStream_t s, const bf16* const* bts = nullptr) {
   const int r = d.lora_rank;
   int n = 0;
   for (int i = 0; i < ns; ++i) slot[i] = (r > 0 && w.lora_a[sites[i].site]) ? n++ : -1;
@@ -586,13 +586,13 @@ int lora_back(const gen_block_dims& d, const gen_block_weights& w, const BackSit
   for (int i = 0; i < ns; ++i) {
     if (slot[i] < 0) continue;
     const BackSite& st = sites[i];
-    HIP_TRY(transpose_bf16((const bf16*)w.lora_b[st.site], r, bt, st.out, st.out, r, s));
+    if (!bts) HIP_TRY(transpose_bf16((const bf16*)w.lora_b[st.site], r, bt, st.out, st.out, r, s));
     GemmParams q = gp();
-    q.A = dY + st.col; q.lda = lddy; q.B = bt; q.ldb = st.out; q.M = M; q.N = r; q.K = st.out;
+    q.A = dY + st.col; q.lda = lddy; q.B = bts ? bts[i] : bt; q.ldb = st.out; q.M = M; q.N = r; q.K = st.out;
     q.C = tp + slot[i] * r; q.ldc = n * r; q.scale = d.lora_alpha / (float)r;
     if (r <= 128 && st.out % 64 == 0) HIP_TRY(gemm_skinny(q, part, s));
     else HIP_TRY(gemm_bf16(q, EPI_SCALED, s));
-    HIP_TRY(transpose_bf16((const bf16*)w.lora_a[st.site], in, xb + slot[i] * r, n * r, r, in, s));
+    if (!bts) HIP_TRY(transpose_bf16((const bf16*)w.lora_a[st.site], in, xb + slot[i] * r, n * r, r, in, s));
   }
   // sum_site tp_site A_site: as the K extension of the base dgrad GEMM ([tp | ...] against
   // [A_site^T | ...]), or into the fp32 scratch that the base GEMM adds onto; either way the sum is
@@ -785,6 +785,41 @@ int block_train_bwd(const gen_block_dims& d, const gen_block_weights& w, const f
   (void)lse; (void)xmid; (void)eps; (void)lora;
 
   // ---- backward
+  // every site's B^T and each site group's A^T block in one launch: B^T [r, out] per site, A^T of
+  // a group [in, sites x r] with the present sites side by side (lora_back's slot order)
+  const bf16* bts_down[1] = {nullptr};
+  const bf16* bts_gu[2] = {nullptr, nullptr};
+  const bf16* bts_o[1] = {nullptr};
+  const bf16* bts_qkv[3] = {nullptr, nullptr, nullptr};
+  bf16* xb_qkv = xb;
+  bf16* xb_o = xb_qkv + (size_t)D * 3 * r;
+  bf16* xb_gu = xb_o + (size_t)QD * r;
+  bf16* xb_down = xb_gu + (size_t)D * 2 * r;
+  if (lora) {
+    TransposeJob jobs[TRANSPOSE_MAX_JOBS];
+    int nj = 0;
+    bf16* btp = bt;
+    auto group = [&](const int* sites, const int* outs, int ns, int in, bf16* xbg, const bf16** bts) {
+      int present = 0;
+      for (int i = 0; i < ns; ++i) present += w.lora_a[sites[i]] ? 1 : 0;
+      int slotn = 0;
+      for (int i = 0; i < ns; ++i) {
+        if (!w.lora_a[sites[i]]) continue;
+        jobs[nj++] = {(const bf16*)w.lora_b[sites[i]], r, btp, outs[i], outs[i], r};
+        bts[i] = btp;
+        btp += (size_t)r * outs[i];
+        jobs[nj++] = {(const bf16*)w.lora_a[sites[i]], in, xbg + slotn * r, present * r, r, in};
+        ++slotn;
+      }
+    };
+    const int s_down[1] = {6}, o_down[1] = {D}, s_gu[2] = {4, 5}, o_gu[2] = {I, I}, s_o[1] = {3}, o_o[1] = {D};
+    const int s_qkv[3] = {0, 1, 2}, o_qkv[3] = {QD, KVD, KVD};
+    group(s_down, o_down, 1, I, xb_down, bts_down);
+    group(s_gu, o_gu, 2, D, xb_gu, bts_gu);
+    group(s_o, o_o, 1, QD, xb_o, bts_o);
+    group(s_qkv, o_qkv, 3, D, xb_qkv, bts_qkv);
+    HIP_TRY(transpose_many(jobs, nj, s));
+  }
   int slot[3], n;
   if (!dyb_ready) HIP_TRY(cast_f32_bf16(dh, dyb, (int64_t)M * D, s));
   {  // down projection: dz = dy W_down (+ LoRA)
@@ -792,7 +827,7 @@ int block_train_bwd(const gen_block_dims& d, const gen_block_weights& w, const f
     GemmParams p = gp();
     HIP_TRY(transpose_bf16((const bf16*)w.w_down, I, wt, D, D, I, s));
     p.A = dyb; p.lda = D; p.B = wt; p.ldb = D; p.M = M; p.N = I; p.K = D; p.C = dz; p.ldc = I;
-    n = lora_back(d, w, bs, 1, dyb, D, I, M, tp, xb, bt, p, slot, part, lf, s);
+    n = lora_back(d, w, bs, 1, dyb, D, I, M, tp, xb_down, bt, p, slot, part, lf, s, bts_down);
     if (n < 0) return n;
     HIP_TRY(gemm_bf16(p, p.R ? EPI_RESID_FROM_F32 : EPI_STORE, s));
     if (n > 0) {
@@ -806,7 +841,7 @@ int block_train_bwd(const gen_block_dims& d, const gen_block_weights& w, const f
     GemmParams p = gp();
     HIP_TRY(transpose_bf16((const bf16*)w.w_gate_up, D, wt, 2 * I, 2 * I, D, s));
     p.A = dgu; p.lda = 2 * I; p.B = wt; p.ldb = 2 * I; p.M = M; p.N = D; p.K = 2 * I; p.C = du; p.ldc = D;
-    n = lora_back(d, w, bs, 2, dgu, 2 * I, D, M, tp, xb, bt, p, slot, part, lf, s);
+    n = lora_back(d, w, bs, 2, dgu, 2 * I, D, M, tp, xb_gu, bt, p, slot, part, lf, s, bts_gu);
     if (n < 0) return n;
     HIP_TRY(gemm_bf16(p, p.R ? EPI_RESID_FROM_F32 : EPI_STORE, s));
     if (n > 0) {
@@ -820,7 +855,7 @@ int block_train_bwd(const gen_block_dims& d, const gen_block_weights& w, const f
     GemmParams p = gp();
     HIP_TRY(transpose_bf16((const bf16*)w.w_o, QD, wt, D, D, QD, s));
     p.A = dyb; p.lda = D; p.B = wt; p.ldb = D; p.M = M; p.N = QD; p.K = D; p.C = dO; p.ldc = QD;
-    n = lora_back(d, w, bs, 1, dyb, D, QD, M, tp, xb, bt, p, slot, part, lf, s);
+    n = lora_back(d, w, bs, 1, dyb, D, QD, M, tp, xb_o, bt, p, slot, part, lf, s, bts_o);
     if (n < 0) return n;
     HIP_TRY(gemm_bf16(p, p.R ? EPI_RESID_FROM_F32 : EPI_STORE, s));
     if (n > 0) {
@@ -837,7 +872,7 @@ int block_train_bwd(const gen_block_dims& d, const gen_block_weights& w, const f
     GemmParams p = gp();
     HIP_TRY(transpose_bf16((const bf16*)w.w_qkv, D, wt, QKV, QKV, D, s));
     p.A = dqkv; p.lda = QKV; p.B = wt; p.ldb = QKV; p.M = M; p.N = D; p.K = QKV; p.C = du; p.ldc = D;
-    n = lora_back(d, w, bs, 3, dqkv, QKV, D, M, tp, xb, bt, p, slot, part, lf, s);
+    n = lora_back(d, w, bs, 3, dqkv, QKV, D, M, tp, xb_qkv, bt, p, slot, part, lf, s, bts_qkv);
     if (n < 0) return n;
     HIP_TRY(gemm_bf16(p, p.R ? EPI_RESID_FROM_F32 : EPI_STORE, s));
     if (n > 0) {

@@ -28,10 +28,8 @@ namespace {
 // 64 x 64 tiles: rows come in as 16-byte pieces (8 columns), go out as 16-byte pieces of the
 // transposed rows; LDS rows padded by 8 elements keep the 16-byte writes aligned.  C and ldi,
 // ldo must be multiples of 8 for the vector path; other shapes use element accesses.
-__global__ __launch_bounds__(256) void transpose_kernel(const bf16* __restrict__ in, int64_t ldi, bf16* __restrict__ out,
-                                                        int64_t ldo, int R, int C) {
-  __shared__ __attribute__((aligned(16))) uint16_t tile[64][72];
-  const int r0 = blockIdx.y * 64, c0 = blockIdx.x * 64;
+DEVI void transpose_tile(const bf16* __restrict__ in, int64_t ldi, bf16* __restrict__ out, int64_t ldo, int R, int C,
+                         int r0, int c0, uint16_t (&tile)[64][72]) {
   const int tid = threadIdx.x;
   const uint16_t* src = (const uint16_t*)in;
   uint16_t* dst = (uint16_t*)out;
@@ -69,6 +67,31 @@ __global__ __launch_bounds__(256) void transpose_kernel(const bf16* __restrict__
       for (int e = 0; e < 8 && r + e < R; ++e) dst[(int64_t)c * ldo + r + e] = tile[orr + e][oc];
     }
   }
+}
+
+__global__ __launch_bounds__(256) void transpose_kernel(const bf16* __restrict__ in, int64_t ldi, bf16* __restrict__ out,
+                                                        int64_t ldo, int R, int C) {
+  __shared__ __attribute__((aligned(16))) uint16_t tile[64][72];
+  transpose_tile(in, ldi, out, ldo, R, C, blockIdx.y * 64, blockIdx.x * 64, tile);
+}
+
+// Several small transposes in one launch: workgroup b takes tile b - start[j] of job j
+// (start[j] <= b < start[j + 1]), tiles of a job in row-major order over its 64 x 64 grid.
+struct TransposeJobs {
+  const bf16* in[TRANSPOSE_MAX_JOBS];
+  bf16* out[TRANSPOSE_MAX_JOBS];
+  int64_t ldi[TRANSPOSE_MAX_JOBS], ldo[TRANSPOSE_MAX_JOBS];
+  int R[TRANSPOSE_MAX_JOBS], C[TRANSPOSE_MAX_JOBS];
+  int start[TRANSPOSE_MAX_JOBS + 1];
+  int n;
+};
+__global__ __launch_bounds__(256) void transpose_many_kernel(TransposeJobs jb) {
+  __shared__ __attribute__((aligned(16))) uint16_t tile[64][72];
+  const int b = blockIdx.x;
+  int j = 0;
+  while (j + 1 < jb.n && b >= jb.start[j + 1]) ++j;
+  const int t = b - jb.start[j], ct = (jb.C[j] + 63) / 64;
+  transpose_tile(jb.in[j], jb.ldi[j], jb.out[j], jb.ldo[j], jb.R[j], jb.C[j], (t / ct) * 64, (t % ct) * 64, tile);
 }
 
 __global__ __launch_bounds__(256) void cast_kernel(const float* __restrict__ x, bf16* __restrict__ y, int64_t n) {
@@ -899,6 +922,24 @@ __global__ __launch_bounds__(256) void loss_reduce_kernel(const float* __restric
 hipError_t transpose_bf16(const bf16* in, int64_t ldi, bf16* out, int64_t ldo, int R, int C, hipStream_t s) {
   if (R <= 0 || C <= 0) return hipSuccess;
   hipLaunchKernelGGL(transpose_kernel, dim3((C + 63) / 64, (R + 63) / 64), dim3(256), 0, s, in, ldi, out, ldo, R, C);
+  return hipGetLastError();
+}
+
+hipError_t transpose_many(const TransposeJob* jobs, int n, hipStream_t s) {
+  if (n <= 0) return hipSuccess;
+  if (n > TRANSPOSE_MAX_JOBS) return hipErrorInvalidValue;
+  TransposeJobs jb{};
+  int tiles = 0;
+  for (int i = 0; i < n; ++i) {
+    jb.in[i] = jobs[i].in; jb.out[i] = jobs[i].out; jb.ldi[i] = jobs[i].ldi; jb.ldo[i] = jobs[i].ldo;
+    jb.R[i] = jobs[i].R; jb.C[i] = jobs[i].C;
+    jb.start[i] = tiles;
+    tiles += ((jobs[i].R + 63) / 64) * ((jobs[i].C + 63) / 64);
+  }
+  jb.start[n] = tiles;
+  jb.n = n;
+  if (tiles == 0) return hipSuccess;
+  hipLaunchKernelGGL(transpose_many_kernel, dim3(tiles), dim3(256), 0, s, jb);
   return hipGetLastError();
 }
 

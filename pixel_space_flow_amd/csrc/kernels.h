@@ -75,6 +75,13 @@ hipError_t cfg_euler(float* xo, const float* x, const float* xc, const float* xm
 
 // ---- training backward (backward.hip)
 hipError_t transpose_bf16(const bf16* in, int64_t ldi, bf16* out, int64_t ldo, int R, int C, hipStream_t s);
+// out [C, R] (row pitch ldo) = in [R, C]^T (row pitch ldi) for up to TRANSPOSE_MAX_JOBS matrices in
+// one launch
+constexpr int TRANSPOSE_MAX_JOBS = 16;
+struct TransposeJob {
+  const bf16* in; int64_t ldi; bf16* out; int64_t ldo; int R, C;
+};
+hipError_t transpose_many(const TransposeJob* jobs, int n, hipStream_t s);
 hipError_t cast_f32_bf16(const float* x, bf16* y, int64_t n, hipStream_t s);
 // out = base + (dRMSNorm(x; g))^T dy per row of D (base may alias out or be null); outb, when set,
 // also receives bf16(out)
