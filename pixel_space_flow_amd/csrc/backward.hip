@@ -3,18 +3,23 @@
 // matrices only (base weights frozen).  bf16 operands, fp32 accumulation and fp32 gradients of
 // the residual stream.
 //
-//   transpose_kernel       out[c][r] = in[r][c] (frozen weights and LoRA matrices as GEMM operands)
+//   transpose_kernel       out[c][r] = in[r][c] (frozen weights as GEMM operands); transpose_many_kernel
+//                          the same for up to 16 small matrices in one launch (the LoRA matrices)
 //   cast_kernel            fp32 -> bf16 (GEMM operands)
 //   rmsnorm_bwd_kernel     out = base + r g dy - x r^3 sum(g dy x) / D, one row per workgroup
-//   swiglu_kernel          z = silu(gate) up, and its backward
+//                          (rmsnorm_bwd4_kernel: 16-byte accesses, optionally a bf16 copy of out)
+//   swiglu_kernel          z = silu(gate) up, and its backward (swiglu8_*: eight columns per thread)
 //   qknorm_rope_bwd_kernel gradient through RoPE (the inverse rotation) and the per-head RMSNorm
-//   attn_bwd_dot_kernel    D[q] = sum_i dO[q, i] O[q, i]
+//                          (qknorm_rope_bwd128_kernel: head_dim 128, 16 lanes per head)
+//   attn_bwd_dot_kernel    D[q] = sum_i dO[q, i] O[q, i] (attn_bwd_dot128_kernel: 16 lanes per head)
 //   attn_bwd_dkdv_kernel   dK, dV of the image keys: four waves of 32 keys share each staged Q/dO
 //                          block (double buffered), over every query of the group's heads; P
 //                          recomputed from the forward's log-sum-exp
 //   attn_bwd_dq_kernel     dQ: four waves (query heads of one kv head) share each staged K/V tile
 //                          (double buffered), over every key (prefix and image)
-//   wgrad_kernel           C[n1, n2] += sum_m X[m, n1] Y[m, n2] (LoRA weight gradients), split over m
+//   wgrad_kernel           C[n1, n2] += sum_m X[m, n1] Y[m, n2] (LoRA weight gradients), split over m;
+//                          wgrad_lr_kernel when one side is the rank; wgrad_reduce(_seg)_kernel add
+//                          the split partial sums in a fixed order
 //   x0_loss_kernel         squared error partial sums and dL/dx0
 #include "common.h"
 #include "kernels.h"
