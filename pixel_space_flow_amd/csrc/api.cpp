@@ -583,6 +583,16 @@ int lora_back(const gen_block_dims& d, const gen_block_weights& w, const BackSit
   int n = 0;
   for (int i = 0; i < ns; ++i) slot[i] = (r > 0 && w.lora_a[sites[i].site]) ? n++ : -1;
   if (n == 0) return 0;
+  // every site of a group present at rank 32, side by side from column 0 of dY: one block-diagonal
+  // skinny product reads dY once for all of them
+  bool diag = bts && r == 32 && n == ns && ns >= 2;
+  int outs[3] = {0, 0, 0}, col = 0;
+  for (int i = 0; i < ns && diag; ++i) {
+    diag = sites[i].col == col && sites[i].out % 64 == 0;
+    outs[i] = sites[i].out;
+    col += sites[i].out;
+  }
+  if (diag) HIP_TRY(gemm_skinny_diag(dY, lddy, M, bts, outs, ns, d.lora_alpha / (float)r, tp, n * r, part, s));
   for (int i = 0; i < ns; ++i) {
     if (slot[i] < 0) continue;
     const BackSite& st = sites[i];
@@ -590,7 +600,8 @@ int lora_back(const gen_block_dims& d, const gen_block_weights& w, const BackSit
     GemmParams q = gp();
     q.A = dY + st.col; q.lda = lddy; q.B = bts ? bts[i] : bt; q.ldb = st.out; q.M = M; q.N = r; q.K = st.out;
     q.C = tp + slot[i] * r; q.ldc = n * r; q.scale = d.lora_alpha / (float)r;
-    if (r <= 128 && st.out % 64 == 0) HIP_TRY(gemm_skinny(q, part, s));
+    if (diag) {
+    } else if (r <= 128 && st.out % 64 == 0) HIP_TRY(gemm_skinny(q, part, s));
     else HIP_TRY(gemm_bf16(q, EPI_SCALED, s));
     if (!bts) HIP_TRY(transpose_bf16((const bf16*)w.lora_a[st.site], in, xb + slot[i] * r, n * r, r, in, s));
   }

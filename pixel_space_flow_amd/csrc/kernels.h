@@ -115,6 +115,11 @@ constexpr int SKINNY_MAX_SPLITS = 16;
 inline size_t skinny_part_floats(int M, int N) { return (size_t)SKINNY_MAX_SPLITS * M * N; }
 int skinny_splits(int M, int K);
 hipError_t gemm_skinny(const GemmParams& p, float* part, hipStream_t s);
+// C [M, 32 ns] (pitch ldc) = scale A B^T with a block-diagonal B: output columns 32 i .. 32 i + 31
+// take B[i] [32, outs[i]] (pitch outs[i]) against A's columns of site i (sites side by side from
+// column 0, outs[i] multiples of 64); A read once.  part: skinny_part_floats(M, 32 ns) floats.
+hipError_t gemm_skinny_diag(const bf16* A, int64_t lda, int M, const bf16* const* B, const int* outs, int ns, float scale,
+                           bf16* C, int64_t ldc, float* part, hipStream_t s);
 // Low-rank product C (op)= X Y^T, K a multiple of 8 (LoRA up-projection): mode 0 C bf16 = acc,
 // 1 C bf16 = bf16(C + acc), 2 C fp32 += acc, 3 C fp32 = acc.
 hipError_t gemm_lowrank(const bf16* X, int64_t ldx, const bf16* Y, int64_t ldy, int M, int N, int K, void* C,

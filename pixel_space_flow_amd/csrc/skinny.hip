@@ -18,11 +18,15 @@
 namespace psf {
 namespace {
 
-template <int NB>
+// DIAG: block-diagonal B, one 32-column block per site: block nb takes B_nb (pitch ldb, ldb1,
+// ldb2) over the k-range of its site only ([0, kb1), [kb1, kb2), [kb2, K)), so one pass over A's
+// rows serves sites that read different column ranges of A.
+template <int NB, bool DIAG = false>
 __global__ __launch_bounds__(256) void skinny_kernel(const bf16* __restrict__ A, int64_t lda, const bf16* __restrict__ B0,
                                                      const bf16* __restrict__ B1, const bf16* __restrict__ B2,
                                                      int64_t ldb, int seg_rows, int M, int N, int K, int kchunk,
-                                                     float* __restrict__ part) {
+                                                     float* __restrict__ part, int64_t ldb1 = 0, int64_t ldb2 = 0,
+                                                     int kb1 = 0, int kb2 = 0) {
   __shared__ __attribute__((aligned(16))) char sa[4][32 * 128];   // one 32-row x 64-deep A step per wave
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, lr = lane & 31, lh = lane >> 5;
   const int m0 = blockIdx.x * 128 + w * 32, z = blockIdx.y;
@@ -35,14 +39,23 @@ __global__ __launch_bounds__(256) void skinny_kernel(const bf16* __restrict__ A,
   for (int i = 0; i < 4; ++i) ap[i] = A + (int64_t)min(m0 + i * 8 + (lane >> 3), M - 1) * lda + (lane & 7) * 8;
   const bf16* bp[NB];
   bool bok[NB];
+  int klo[NB], khi[NB];                         // DIAG: k-range of block nb's site
 #pragma unroll
   for (int nb = 0; nb < NB; ++nb) {
     const int n = nb * 32 + lr;
     bok[nb] = n < N;
     const int nc = bok[nb] ? n : 0;
-    const int seg = nc / seg_rows;
-    const bf16* base = seg == 0 ? B0 : (seg == 1 ? B1 : B2);
-    bp[nb] = base + (int64_t)(nc - seg * seg_rows) * ldb + lh * 8;
+    if (DIAG) {
+      klo[nb] = nb == 0 ? 0 : (nb == 1 ? kb1 : kb2);
+      khi[nb] = nb == 0 ? (NB > 1 ? kb1 : K) : (nb == 1 ? (NB > 2 ? kb2 : K) : K);
+      const bf16* base = nb == 0 ? B0 : (nb == 1 ? B1 : B2);
+      const int64_t pitch = nb == 0 ? ldb : (nb == 1 ? ldb1 : ldb2);
+      bp[nb] = base + (int64_t)(nc - nb * 32) * pitch + lh * 8;   // row of the site's B, k from klo
+    } else {
+      const int seg = nc / seg_rows;
+      const bf16* base = seg == 0 ? B0 : (seg == 1 ? B1 : B2);
+      bp[nb] = base + (int64_t)(nc - seg * seg_rows) * ldb + lh * 8;
+    }
   }
   f32x16 acc[NB];
 #pragma unroll
@@ -56,7 +69,12 @@ __global__ __launch_bounds__(256) void skinny_kernel(const bf16* __restrict__ A,
     for (int i = 0; i < 4; ++i) {
       ao[i] = *(const bf16x8*)(ap[i] + k);
 #pragma unroll
-      for (int nb = 0; nb < NB; ++nb) bo[nb][i] = bok[nb] ? *(const bf16x8*)(bp[nb] + k + 16 * i) : zero;
+      for (int nb = 0; nb < NB; ++nb) {
+        if (DIAG)
+          bo[nb][i] = (bok[nb] && k >= klo[nb] && k < khi[nb]) ? *(const bf16x8*)(bp[nb] + (k - klo[nb]) + 16 * i) : zero;
+        else
+          bo[nb][i] = bok[nb] ? *(const bf16x8*)(bp[nb] + k + 16 * i) : zero;
+      }
     }
   };
   if (k_lo < k_hi) load(k_lo, a, b);
@@ -220,6 +238,39 @@ hipError_t gemm_skinny(const GemmParams& p, float* part, hipStream_t s) {
   const int64_t n = (int64_t)p.M * p.N;
   hipLaunchKernelGGL(skinny_reduce_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, (const float*)part, nz,
                      p.M, p.N, p.scale, (bf16*)p.C, p.ldc);
+  return hipGetLastError();
+}
+
+hipError_t gemm_skinny_diag(const bf16* A, int64_t lda, int M, const bf16* const* B, const int* outs, int ns, float scale,
+                           bf16* C, int64_t ldc, float* part, hipStream_t s) {
+  if (M <= 0) return hipSuccess;
+  if (ns < 1 || ns > 3) return hipErrorInvalidValue;
+  int K = 0;
+  for (int i = 0; i < ns; ++i) {
+    if (outs[i] <= 0 || outs[i] % 64) return hipErrorInvalidValue;
+    K += outs[i];
+  }
+  const int kb1 = outs[0], kb2 = ns > 2 ? outs[0] + outs[1] : K;
+  const int N = 32 * ns;
+  const int splits = skinny_splits(M, K);
+  const int kchunk = (K / 64 + splits - 1) / splits * 64;
+  const int nz = (K + kchunk - 1) / kchunk;
+  const dim3 grid((M + 127) / 128, nz);
+  const bf16* B1 = ns > 1 ? B[1] : B[0];
+  const bf16* B2 = ns > 2 ? B[2] : B[0];
+  const int64_t l1 = ns > 1 ? outs[1] : outs[0], l2 = ns > 2 ? outs[2] : outs[0];
+  if (ns == 1)
+    hipLaunchKernelGGL((skinny_kernel<1, true>), grid, dim3(256), 0, s, A, lda, B[0], B1, B2, (int64_t)outs[0], 32, M, N, K,
+                       kchunk, part, l1, l2, kb1, kb2);
+  else if (ns == 2)
+    hipLaunchKernelGGL((skinny_kernel<2, true>), grid, dim3(256), 0, s, A, lda, B[0], B1, B2, (int64_t)outs[0], 32, M, N, K,
+                       kchunk, part, l1, l2, kb1, kb2);
+  else
+    hipLaunchKernelGGL((skinny_kernel<3, true>), grid, dim3(256), 0, s, A, lda, B[0], B1, B2, (int64_t)outs[0], 32, M, N, K,
+                       kchunk, part, l1, l2, kb1, kb2);
+  const int64_t n = (int64_t)M * N;
+  hipLaunchKernelGGL(skinny_reduce_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, (const float*)part, nz, M, N,
+                     scale, C, ldc);
   return hipGetLastError();
 }
 
