@@ -653,7 +653,7 @@ int lora_wgrad(const gen_block_dims& d, const gen_lora_grads& g, const BackSite*
 // activation slot `act` what block_train_bwd reads; with h_out, also writes the block output
 // h_out = h + attention + MLP (fp32).  Scratch in ws (layout L).
 int block_train_fwd(const gen_block_dims& d, const gen_block_weights& w, const float* h, float* h_out,
-                    const SeqInfo& si, void* act, void* ws, const Wb& L, hipStream_t s) {
+                    const SeqInfo& si, void* act, void* ws, const Wb& L, hipStream_t s, bool rope_ready = false) {
   const int B = si.B, N = si.N, M = B * N, D = d.hidden, I = d.mlp_intermediate, r = d.lora_rank;
   const int Hq = d.n_q_heads, Hkv = d.n_kv_heads, hd = d.head_dim;
   const int QD = Hq * hd, KVD = Hkv * hd, QKV = QD + 2 * KVD;
@@ -675,7 +675,7 @@ int block_train_fwd(const gen_block_dims& d, const gen_block_weights& w, const f
   float* part = at<float>(ws, L.part);
   float* lf = at<float>(ws, L.lf);
   const float2* rope = at<float2>(ws, L.rope);
-  HIP_TRY(rope_table(at<float2>(ws, L.rope), L.n_pos, hd, d.rope_theta, s));
+  if (!rope_ready) HIP_TRY(rope_table(at<float2>(ws, L.rope), L.n_pos, hd, d.rope_theta, s));
 
   const int qkv_sites[3] = {0, 1, 2}, qkv_ends[3] = {QD, QD + KVD, QKV};
   const int o_site[1] = {3}, gu_sites[2] = {4, 5}, gu_ends[2] = {I, 2 * I}, down_site[1] = {6};
@@ -684,7 +684,7 @@ int block_train_fwd(const gen_block_dims& d, const gen_block_weights& w, const f
   HIP_TRY((rmsnorm<float, bf16>(h, (const bf16*)w.g_in, u, M, D, eps, s)));
   {
     GemmParams p = gp();
-    p.A = u; p.lda = D; p.B = w.w_qkv; p.ldb = D; p.M = M; p.N = QKV; p.K = D; p.C = qkv_raw; p.ldc = QKV;
+    p.A = u; p.lda = D; p.B = w.w_qkv; p.ldb = D; p.M = M; p.N = QKV; p.K = D; p.C = qkv_n; p.ldc = QKV;
     int epi = EPI_STORE;
     if (lora) {
       HIP_TRY(lora_down<bf16>(d, w, qkv_sites, 3, u, D, M, t_qkv, off_qkv, ld_qkv, s, part));
@@ -698,8 +698,8 @@ int block_train_fwd(const gen_block_dims& d, const gen_block_weights& w, const f
     }
     HIP_TRY(gemm_bf16(p, epi, s));
   }
-  HIP_TRY(hipMemcpyAsync(qkv_n, qkv_raw, (size_t)M * QKV * 2, hipMemcpyDeviceToDevice, s));
-  HIP_TRY(qknorm_rope<bf16>(qkv_n, QKV, si, Hq, Hkv, hd, (const bf16*)w.g_q, (const bf16*)w.g_k, rope, eps, s));
+  // q and k normed and rotated in place; their raw values (all the backward needs of them) to qkv_raw
+  HIP_TRY(qknorm_rope<bf16>(qkv_n, QKV, si, Hq, Hkv, hd, (const bf16*)w.g_q, (const bf16*)w.g_k, rope, eps, s, qkv_raw));
   HIP_TRY(pack_kv<bf16>(qkv_n, QKV, si, Hq, Hkv, hd, L.Lpad, at<bf16>(ws, L.kc), at<bf16>(ws, L.vt), s));
   HIP_TRY(attention_bf16(qkv_n, QKV, si, Hq, Hkv, hd, L.Lpad, at<bf16>(ws, L.kc), at<bf16>(ws, L.vt), attn, QD,
                          nullptr, nullptr, 0.f, false, s, lse));
@@ -1333,7 +1333,7 @@ int gen_tower_lora_train_step(const gen_block_dims* dims, int n_layers, const ge
     const SeqInfo si = make_seq(B, N, prefix_k + (size_t)l * B, prefix_v + (size_t)l * B, prefix_len);
     float* out = l + 1 < n_layers ? saved + (size_t)(l + 1) * M * D : hidden;
     void* act = at<char>(workspace, T.acts + (size_t)l * T.act_stride);
-    if ((rc = block_train_fwd(*dims, layers[l], saved + (size_t)l * M * D, out, si, act, bws, L, s))) return rc;
+    if ((rc = block_train_fwd(*dims, layers[l], saved + (size_t)l * M * D, out, si, act, bws, L, s, l > 0))) return rc;
   }
   bf16* u = at<bf16>(fws, F.u);
   HIP_TRY((rmsnorm<float, bf16>(hidden, (const bf16*)g_final, u, M, D, dims->rms_eps, s)));

@@ -108,7 +108,8 @@ __global__ void rope_table_kernel(float2* table, int n_pos, int half, double the
 template <typename T, int D>
 __global__ __launch_bounds__(256) void qknorm_rope_kernel(T* __restrict__ qkv, int64_t ld, SeqInfo si, int Hq, int Hkv,
                                                           const T* __restrict__ gq, const T* __restrict__ gk,
-                                                          const float2* __restrict__ table, float eps, int64_t total) {
+                                                          const float2* __restrict__ table, float eps, int64_t total,
+                                                          T* __restrict__ raw_out) {
   using V = V16<T>;
   constexpr int L = D / V::N;
   constexpr int HPW = 64 / L;
@@ -125,7 +126,9 @@ __global__ __launch_bounds__(256) void qknorm_rope_kernel(T* __restrict__ qkv, i
   T* p = qkv + tok * ld + (int64_t)head * D + sub * V::N;
   const T* g = (head < Hq ? gq : gk) + sub * V::N;
   float x[V::N], gg[V::N];
-  V::unpack(*(const u32x4*)p, x);
+  const u32x4 raw = *(const u32x4*)p;
+  if (raw_out && active) *(u32x4*)(raw_out + tok * ld + (int64_t)head * D + sub * V::N) = raw;   // pre-norm copy
+  V::unpack(raw, x);
   V::unpack(*(const u32x4*)g, gg);
   float ss = 0.f;
 #pragma unroll
@@ -404,19 +407,19 @@ hipError_t rope_table(float2* table, int n_pos, int head_dim, float theta, hipSt
 
 template <typename T>
 hipError_t qknorm_rope(T* qkv, int64_t ld, const SeqInfo& si, int Hq, int Hkv, int d, const T* gq, const T* gk,
-                       const float2* table, float eps, hipStream_t s) {
+                       const float2* table, float eps, hipStream_t s, T* raw_out) {
   const int64_t total = (int64_t)si.B * si.N * (Hq + Hkv);
   if (total == 0) return hipSuccess;
   const int L = d / V16<T>::N;
   const int64_t per_block = 4 * (64 / L);
   const dim3 grid((unsigned)((total + per_block - 1) / per_block));
-  if (d == 128) hipLaunchKernelGGL((qknorm_rope_kernel<T, 128>), grid, dim3(256), 0, s, qkv, ld, si, Hq, Hkv, gq, gk, table, eps, total);
-  else if (d == 64) hipLaunchKernelGGL((qknorm_rope_kernel<T, 64>), grid, dim3(256), 0, s, qkv, ld, si, Hq, Hkv, gq, gk, table, eps, total);
+  if (d == 128) hipLaunchKernelGGL((qknorm_rope_kernel<T, 128>), grid, dim3(256), 0, s, qkv, ld, si, Hq, Hkv, gq, gk, table, eps, total, raw_out);
+  else if (d == 64) hipLaunchKernelGGL((qknorm_rope_kernel<T, 64>), grid, dim3(256), 0, s, qkv, ld, si, Hq, Hkv, gq, gk, table, eps, total, raw_out);
   else return hipErrorInvalidValue;
   return hipGetLastError();
 }
-template hipError_t qknorm_rope<bf16>(bf16*, int64_t, const SeqInfo&, int, int, int, const bf16*, const bf16*, const float2*, float, hipStream_t);
-template hipError_t qknorm_rope<float>(float*, int64_t, const SeqInfo&, int, int, int, const float*, const float*, const float2*, float, hipStream_t);
+template hipError_t qknorm_rope<bf16>(bf16*, int64_t, const SeqInfo&, int, int, int, const bf16*, const bf16*, const float2*, float, hipStream_t, bf16*);
+template hipError_t qknorm_rope<float>(float*, int64_t, const SeqInfo&, int, int, int, const float*, const float*, const float2*, float, hipStream_t, float*);
 
 template <typename T>
 hipError_t pack_kv(const T* qkv, int64_t ld, const SeqInfo& si, int Hq, int Hkv, int d, int Lpad, T* Kc, T* Vt,

@@ -27,8 +27,9 @@ hipError_t rope_table(float2* table, int n_pos, int head_dim, float theta, hipSt
 // In place on the q and k heads of qkv [B*N, ld]: per-head RMSNorm (gain g_q / g_k) then
 // rotate-half RoPE at position plen[b] + n.
 template <typename T>
+// raw_out (nullable, pitch ld): receives the q and k heads as they were before the norm.
 hipError_t qknorm_rope(T* qkv, int64_t ld, const SeqInfo& si, int Hq, int Hkv, int d, const T* gq, const T* gk,
-                       const float2* table, float eps, hipStream_t s);
+                       const float2* table, float eps, hipStream_t s, T* raw_out = nullptr);
 
 // Pack keys and transposed values of every (sequence, kv head) contiguously:
 //   Kc[b][g][j][:] = j < P_b ? prefix K : (j < P_b + N ? k of token j - P_b : 0)     [B, Hkv, Lpad, d]
