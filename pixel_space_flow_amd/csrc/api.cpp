@@ -630,10 +630,25 @@ int lora_wgrad(const gen_block_dims& d, const gen_lora_grads& g, const BackSite*
                const bf16* dY, int lddy, const bf16* t, int ldt, const int* toff, const bf16* tp, const bf16* x, int in,
                int M, float* part, hipStream_t s) {
   const int r = d.lora_rank;
-  for (int i = 0; i < ns; ++i) {
-    if (slot[i] < 0) continue;
-    const int st = sites[i].site;
-    HIP_TRY(wgrad(dY + sites[i].col, lddy, t + toff[i], ldt, M, sites[i].out, r, g.lora_b[st], part, s));
+  // B gradients: a complete group whose sites sit side by side in dY and in t as one block-diagonal
+  // pass, else site by site
+  bool diag = n == ns && ns >= 2;
+  int outs[3] = {0, 0, 0}, col = 0;
+  float* dstb[3] = {nullptr, nullptr, nullptr};
+  for (int i = 0; i < ns && diag; ++i) {
+    diag = sites[i].col == col && sites[i].out % 128 == 0 && toff[i] == i * r;
+    outs[i] = sites[i].out;
+    dstb[i] = g.lora_b[sites[i].site];
+    col += sites[i].out;
+  }
+  if (diag) {
+    HIP_TRY(wgrad_diag(dY, lddy, t, ldt, M, outs, ns, r, dstb, part, s));
+  } else {
+    for (int i = 0; i < ns; ++i) {
+      if (slot[i] < 0) continue;
+      const int st = sites[i].site;
+      HIP_TRY(wgrad(dY + sites[i].col, lddy, t + toff[i], ldt, M, sites[i].out, r, g.lora_b[st], part, s));
+    }
   }
   // the A gradients of the sites sharing the input x: one pass over x with their dT side by side
   // (slot order), the row blocks of the product going to the sites' gradients

@@ -770,11 +770,14 @@ __global__ __launch_bounds__(256) void wgrad_kernel(const bf16* __restrict__ X, 
 template <bool BIGX>
 __global__ __launch_bounds__(256) void wgrad_lr_kernel(const bf16* __restrict__ Big, int64_t ldb,
                                                        const bf16* __restrict__ Small, int64_t lds, int M, int NB,
-                                                       int R, int m_per_split, float* __restrict__ part) {
+                                                       int R, int m_per_split, float* __restrict__ part, int bseg1,
+                                                       int bseg2, int sm_step) {
   __shared__ __attribute__((aligned(16))) bf16 sb[2][32 * 128];
   __shared__ __attribute__((aligned(16))) bf16 ss[2][32 * 128];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, lr = lane & 31, lh = lane >> 5;
   const int c0 = blockIdx.x * 128, z = blockIdx.y;
+  // block-diagonal use: Big columns from bseg1 (bseg2) on pair with the next sm_step Small columns
+  Small += (c0 >= bseg2 ? 2 : (c0 >= bseg1 ? 1 : 0)) * sm_step;
   const int m_lo = z * m_per_split, m_hi = min(M, m_lo + m_per_split);
   const int nchunk = (m_hi - m_lo + 31) / 32;
   const int NJ = (R + 31) / 32;
@@ -861,16 +864,17 @@ __global__ __launch_bounds__(256) void wgrad_reduce_kernel(const float* __restri
   C[i] += s;
 }
 
-// The same with the rows of C in blocks of seg elements (seg_rows rows), block k added into Ck.
+// The same with C in three pieces: elements [0, e1) added into C0, [e1, e2) into C1, the rest
+// into C2 (each piece from its own start).
 __global__ __launch_bounds__(256) void wgrad_reduce_seg_kernel(const float* __restrict__ part, int splits, int64_t n,
-                                                               int64_t seg, float* C0, float* C1, float* C2) {
+                                                               int64_t e1, int64_t e2, float* C0, float* C1, float* C2) {
   const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
   if (i >= n) return;
   float s = 0.f;
   for (int z = 0; z < splits; ++z) s += part[(int64_t)z * n + i];
-  const int k = (int)(i / seg);
-  float* C = k == 0 ? C0 : (k == 1 ? C1 : C2);
-  C[i - k * seg] += s;
+  if (i < e1) C0[i] += s;
+  else if (i < e2) C1[i - e1] += s;
+  else C2[i - e2] += s;
 }
 
 // The same for d = 128: 16 lanes per (token, head) with 16-byte loads, four heads per wave.
@@ -1048,7 +1052,7 @@ int wgrad_splits(int M, int N1, int N2) {
 // One side is the rank: stream the other side in 128-column blocks, about 512 workgroups, the
 // partial products [nz, N1, N2] within WGRAD_PART_FLOATS.  Returns nz.
 static int wgrad_lr_launch(const bf16* X, int64_t ldx, const bf16* Y, int64_t ldy, int M, int N1, int N2, float* part,
-                           hipStream_t s) {
+                           hipStream_t s, int bseg1 = 1 << 30, int bseg2 = 1 << 30, int sm_step = 0) {
   const int64_t n = (int64_t)N1 * N2;
   const int R = std::min(N1, N2), NB = std::max(N1, N2);
   const int nblk = (NB + 127) / 128;
@@ -1058,9 +1062,11 @@ static int wgrad_lr_launch(const bf16* X, int64_t ldx, const bf16* Y, int64_t ld
   const int per = ((M + splits - 1) / splits + 31) / 32 * 32;
   const int nz = (M + per - 1) / per;
   if (N1 >= N2)
-    hipLaunchKernelGGL(wgrad_lr_kernel<true>, dim3(nblk, nz), dim3(256), 0, s, X, ldx, Y, ldy, M, NB, R, per, part);
+    hipLaunchKernelGGL(wgrad_lr_kernel<true>, dim3(nblk, nz), dim3(256), 0, s, X, ldx, Y, ldy, M, NB, R, per, part, bseg1,
+                       bseg2, sm_step);
   else
-    hipLaunchKernelGGL(wgrad_lr_kernel<false>, dim3(nblk, nz), dim3(256), 0, s, Y, ldy, X, ldx, M, NB, R, per, part);
+    hipLaunchKernelGGL(wgrad_lr_kernel<false>, dim3(nblk, nz), dim3(256), 0, s, Y, ldy, X, ldx, M, NB, R, per, part, bseg1,
+                       bseg2, sm_step);
   return nz;
 }
 
@@ -1072,8 +1078,28 @@ hipError_t wgrad_seg(const bf16* X, int64_t ldx, const bf16* Y, int64_t ldy, int
   const int64_t n = (int64_t)N1 * N2;
   const int nz = wgrad_lr_launch(X, ldx, Y, ldy, M, N1, N2, part, s);
   const int ns = N1 / seg_rows;
+  const int64_t seg = (int64_t)seg_rows * N2;
   hipLaunchKernelGGL(wgrad_reduce_seg_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, (const float*)part, nz,
-                     n, (int64_t)seg_rows * N2, C[0], ns > 1 ? C[1] : C[0], ns > 2 ? C[2] : C[0]);
+                     n, seg, ns > 2 ? 2 * seg : n, C[0], ns > 1 ? C[1] : C[0], ns > 2 ? C[2] : C[0]);
+  return hipGetLastError();
+}
+
+hipError_t wgrad_diag(const bf16* X, int64_t ldx, const bf16* Y, int64_t ldy, int M, const int* outs, int ns, int r,
+                      float* const* C, float* part, hipStream_t s) {
+  if (M <= 0) return hipSuccess;
+  if (ns < 1 || ns > 3 || r <= 0 || r > 128 || r % 8 || ldx % 8 || ldy % 8) return hipErrorInvalidValue;
+  int N1 = 0;
+  for (int i = 0; i < ns; ++i) {
+    if (outs[i] <= 0 || outs[i] % 128) return hipErrorInvalidValue;
+    N1 += outs[i];
+  }
+  if (N1 < r) return hipErrorInvalidValue;
+  const int b1 = outs[0], b2 = ns > 2 ? outs[0] + outs[1] : (1 << 30);
+  const int64_t n = (int64_t)N1 * r;
+  const int nz = wgrad_lr_launch(X, ldx, Y, ldy, M, N1, r, part, s, ns > 1 ? b1 : (1 << 30), b2, r);
+  const int64_t e1 = ns > 1 ? (int64_t)b1 * r : n, e2 = ns > 2 ? (int64_t)b2 * r : n;
+  hipLaunchKernelGGL(wgrad_reduce_seg_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, (const float*)part, nz,
+                     n, e1, e2, C[0], ns > 1 ? C[1] : C[0], ns > 2 ? C[2] : C[0]);
   return hipGetLastError();
 }
 

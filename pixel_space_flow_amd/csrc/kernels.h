@@ -107,6 +107,11 @@ hipError_t wgrad(const bf16* X, int64_t ldx, const bf16* Y, int64_t ldy, int M, 
 // ([seg_rows, N2] each)
 hipError_t wgrad_seg(const bf16* X, int64_t ldx, const bf16* Y, int64_t ldy, int M, int N1, int N2, int seg_rows,
                      float* const* C, float* part, hipStream_t s);
+// Block-diagonal B gradients of up to three sites side by side: C[i] [outs[i], r] += sum_m
+// X[m, site i's columns]^T Y[m, r i .. r i + r - 1] in one pass (X's sites from column 0, outs[i]
+// multiples of 128, Y the sites' down-projections side by side).
+hipError_t wgrad_diag(const bf16* X, int64_t ldx, const bf16* Y, int64_t ldy, int M, const int* outs, int ns, int r,
+                      float* const* C, float* part, hipStream_t s);
 hipError_t x0_loss(const float* pred, const float* tgt, float* grad, float* part, int nparts, float* loss, int64_t n,
                    hipStream_t s);
 
