@@ -279,7 +279,15 @@ def run_train_bench(psf, w, args):
         for s_ in ("q", "k", "v", "o", "gate", "up", "down"):
             lwd[f"lora_a_{s_}"] = randn(r, ins[s_], std=0.02)
             lwd[f"lora_b_{s_}"] = randn(outs[s_], r, std=0.02)
-        gb = {k: torch.zeros(v.shape, device="cuda") for k, v in lwd.items() if k.startswith("lora_")}
+    # every layer's LoRA gradients as views of one flat buffer, cleared by one fill per step
+    shapes = [[(k, v.shape) for k, v in lwd.items() if k.startswith("lora_")] for lwd in layers_dev]
+    flat = torch.zeros(sum(sh.numel() for layer in shapes for _, sh in layer), device="cuda")
+    off = 0
+    for layer in shapes:
+        gb = {}
+        for k, sh in layer:
+            gb[k] = flat[off:off + sh.numel()].view(sh)
+            off += sh.numel()
         grads.append(gb)
         gstructs.append(psf.make_lora_grads(gb))
     layers = [psf.make_weights(l) for l in layers_dev]
@@ -292,9 +300,7 @@ def run_train_bench(psf, w, args):
     ws = psf.alloc_workspace(psf.train_workspace_size(dims, w.n_layers, w.n_img, w.n_tokens, w.prefix_len))
 
     def step():
-        for gb in grads:
-            for v in gb.values():
-                v.zero_()
+        flat.zero_()
         psf.tower_lora_train_step(dims, layers, glob, x_t, x0, sig, pk, pv, plen, gstructs, loss, ws)
 
     for _ in range(args.warmup):
