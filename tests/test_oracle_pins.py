@@ -471,6 +471,48 @@ def test_timestep_features():
     np.testing.assert_allclose(ang1[1:] / ang1[:-1], math.exp(-math.log(1e4) / 128), rtol=1e-9)
 
 
+def _torch_temb(sigma: float, w1: np.ndarray, w2: np.ndarray) -> np.ndarray:
+    """The timestep embedder built from torch-CPU modules in fp64: sinusoidal features of
+    1000 sigma (cos half, then sin half), Linear(256 -> D, no bias), SiLU, Linear(D -> D, no bias)."""
+    D, F_ = w1.shape
+    half = F_ // 2
+    freqs = torch.exp(-math.log(10000.0) * torch.arange(half, dtype=torch.float64) / half)
+    a = 1000.0 * sigma * freqs
+    feat = torch.cat([torch.cos(a), torch.sin(a)])[None]
+    l1 = torch.nn.Linear(F_, D, bias=False).double()
+    l2 = torch.nn.Linear(D, D, bias=False).double()
+    with torch.no_grad():
+        l1.weight.copy_(torch.from_numpy(w1))
+        l2.weight.copy_(torch.from_numpy(w2))
+        return l2(F.silu(l1(feat)))[0].numpy()
+
+
+@pytest.mark.parametrize("D", [256, 384])
+def test_timestep_embed_matches_torch_modules(D):
+    # catches W1 and W2 swapped, SiLU moved after W2 (or dropped), a transposed weight, a bias
+    w1, w2 = rnd(D, 256, scale=0.5), rnd(D, D, scale=0.5)
+    for sigma in (0.0, 0.25, 0.993243, 1.0):
+        np.testing.assert_allclose(O.timestep_embed(sigma, w1, w2), _torch_temb(sigma, w1, w2), rtol=1e-10, atol=1e-12)
+
+
+def test_timestep_embed_pin_catches_planted_mistakes():
+    # mistakes planted in copies of the oracle's composition must fail the torch pin at D = 256,
+    # where W1 [D, 256] and W2 [D, D] have the same shape and a swap would run without error
+    D = 256
+    w1, w2 = rnd(D, 256, scale=0.5), rnd(D, D, scale=0.5)
+    feat = lambda s: O.timestep_features(s, 256, np.float64)[None]   # noqa: E731
+    planted = {
+        "W1/W2 swapped": lambda s: O.linear(O.silu(O.linear(feat(s), w2)), w1)[0],
+        "SiLU after W2": lambda s: O.silu(O.linear(O.linear(feat(s), w1), w2))[0],
+        "SiLU dropped": lambda s: O.linear(O.linear(feat(s), w1), w2)[0],
+        "W1 transposed": lambda s: O.linear(O.silu(O.linear(feat(s), w1.T)), w2)[0],
+    }
+    for name, fn in planted.items():
+        got, ref = fn(0.5), _torch_temb(0.5, w1, w2)
+        assert not np.allclose(got, ref, rtol=1e-6, atol=1e-8), f"planted mistake not caught: {name}"
+    np.testing.assert_allclose(O.timestep_embed(0.5, w1, w2), _torch_temb(0.5, w1, w2), rtol=1e-10, atol=1e-12)
+
+
 # ----------------------------------------------------------------------------- cfg / euler
 def test_cfg_special_cases_and_linearity():
     c, u = rnd(3, 8, 8), rnd(3, 8, 8)
