@@ -239,7 +239,9 @@ int flow_euler_dual_cfg(float* x, const float* x0_cond, const float* x0_img, con
  *   logits = u w_router^T (float32 accumulate), p = softmax(logits), the top_k largest p
  *   (ties to the lower expert index), weights p / sum over the top_k.
  *   u [T, D] and w_router [E, D] in `dtype`; idx_out [T, top_k] int32 and w_out [T, top_k]
- *   float32, both in descending-probability order.  E <= 64, top_k <= E. */
+ *   float32, both in descending-probability order.  D a positive multiple of 64, E <= 64,
+ *   top_k <= E; otherwise GEN_EINVAL.  (Inside gen_block_forward the router reads the fp32
+ *   mid-block residual and applies the post-attention RMSNorm itself, all in float32.) */
 int gen_moe_route(const void* u, const void* w_router, int T, int D, int E, int top_k, int dtype,
                   int32_t* idx_out, float* w_out, void* stream);
 

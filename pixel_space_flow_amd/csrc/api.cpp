@@ -88,7 +88,6 @@ int check_dims(const gen_block_dims* d) {
     if (d->expert_intermediate <= 0 || d->expert_intermediate % 64)
       return fail(GEN_EINVAL, "expert_intermediate %d must be a positive multiple of 64", d->expert_intermediate);
     if (d->dtype != GEN_BF16) return fail(GEN_EUNSUPPORTED, "expert MLP runs in bf16 only");
-    if (d->hidden > 4096) return fail(GEN_EUNSUPPORTED, "router supports hidden <= 4096");
   }
   if (d->lora_rank < 0) return fail(GEN_EINVAL, "lora_rank %d < 0", d->lora_rank);
   if (d->lora_rank > 0) {
@@ -147,7 +146,7 @@ size_t up(size_t x) { return (x + ALIGN - 1) / ALIGN * ALIGN; }
 struct Ws {
   size_t hidden, patches, u, qkv, attn, kc, vt, z, rope, temb, h1, x0, lora_t, hmid, skinny, lora_gu, lora_f32;
   size_t splitk, splitk_floats;
-  size_t m_idx, m_w, m_counts, m_offsets, m_perm, m_pos, m_tiles, m_z, m_y;
+  size_t m_idx, m_w, m_counts, m_offsets, m_perm, m_pos, m_tiles, m_z, m_y, m_lrank, m_blkcnt, m_blkoff;
   size_t total;
   int Lpad, max_tiles, n_pos;
 };
@@ -193,6 +192,9 @@ Ws layout(const gen_block_dims& d, int n_img, int n_br, int N, int max_prefix) {
     w.m_tiles = take((size_t)w.max_tiles * 3 * 4);
     w.m_z = take(A * d.expert_intermediate * es);
     w.m_y = take(A * D * es);
+    w.m_lrank = take(A * 4);
+    w.m_blkcnt = take((size_t)moe_route_blocks((int)M) * d.n_experts * 4);
+    w.m_blkoff = take((size_t)moe_route_blocks((int)M) * d.n_experts * 4);
   }
   w.total = o;
   return w;
@@ -447,8 +449,14 @@ int run_block(const gen_block_dims& d, const gen_block_weights& w, TH* hidden, c
     int* tiles = at<int>(ws, L.m_tiles);
     bf16* zp = at<bf16>(ws, L.m_z);
     bf16* yp = at<bf16>(ws, L.m_y);
-    HIP_TRY(moe_route<bf16>((const bf16*)u, (const bf16*)w.w_router, M, D, E, k, idx, wt, s));
-    HIP_TRY(moe_sort(idx, M, k, E, at<int>(ws, L.m_counts), at<int>(ws, L.m_offsets), perm, pos, tiles, L.max_tiles, 256, s));
+    // routed from the fp32 mid-block residual through the post-attention norm, in fp32 (the
+    // expert GEMMs take the bf16 copy u)
+    int* lrank = at<int>(ws, L.m_lrank);
+    int* blkcnt = at<int>(ws, L.m_blkcnt);
+    HIP_TRY((moe_route<float, bf16>(hmid, (const bf16*)w.g_post, d.rms_eps, (const bf16*)w.w_router, M, D, E, k, idx,
+                                    wt, lrank, blkcnt, s)));
+    HIP_TRY(moe_sort(idx, lrank, blkcnt, at<int>(ws, L.m_blkoff), M, k, E, at<int>(ws, L.m_counts),
+                     at<int>(ws, L.m_offsets), perm, pos, tiles, L.max_tiles, 256, s));
     {
       GemmParams p = gp();
       p.A = u; p.lda = D; p.a_rows = perm; p.B = w.w_exp_gate_up; p.ldb = D; p.N = 2 * Ie; p.K = D; p.M = M * k;
@@ -1001,11 +1009,15 @@ int flow_euler_dual_cfg(float* x, const float* x0_cond, const float* x0_img, con
 int gen_moe_route(const void* u, const void* w_router, int T, int D, int E, int top_k, int dtype, int32_t* idx_out,
                   float* w_out, void* stream) {
   if (!u || !w_router || !idx_out || !w_out) return fail(GEN_EINVAL, "NULL pointer argument");
-  if (T < 0 || D <= 0 || D > 4096 || E < 1 || E > 64 || top_k < 1 || top_k > E)
-    return fail(GEN_EINVAL, "bad sizes T=%d D=%d E=%d top_k=%d", T, D, E, top_k);
+  if (T < 0 || D <= 0 || D % 64 || E < 1 || E > 64 || top_k < 1 || top_k > E)
+    return fail(GEN_EINVAL, "bad sizes T=%d D=%d (a positive multiple of 64) E=%d top_k=%d", T, D, E, top_k);
   hipStream_t s = (hipStream_t)stream;
-  if (dtype == GEN_BF16) HIP_TRY(moe_route<bf16>((const bf16*)u, (const bf16*)w_router, T, D, E, top_k, idx_out, w_out, s));
-  else if (dtype == GEN_F32) HIP_TRY(moe_route<float>((const float*)u, (const float*)w_router, T, D, E, top_k, idx_out, w_out, s));
+  if (dtype == GEN_BF16)
+    HIP_TRY((moe_route<bf16, bf16>((const bf16*)u, nullptr, 0.f, (const bf16*)w_router, T, D, E, top_k, idx_out, w_out,
+                                   nullptr, nullptr, s)));
+  else if (dtype == GEN_F32)
+    HIP_TRY((moe_route<float, float>((const float*)u, nullptr, 0.f, (const float*)w_router, T, D, E, top_k, idx_out,
+                                     w_out, nullptr, nullptr, s)));
   else return fail(GEN_EINVAL, "bad dtype %d", dtype);
   return ok();
 }

@@ -131,14 +131,22 @@ hipError_t gemm_skinny_diag(const bf16* A, int64_t lda, int M, const bf16* const
 hipError_t gemm_lowrank(const bf16* X, int64_t ldx, const bf16* Y, int64_t ldy, int M, int N, int K, void* C,
                         int64_t ldc, int mode, hipStream_t s);
 
-// Router: idx/w [T, k]; u [T, D], wr [E, D]
-template <typename T>
-hipError_t moe_route(const T* u, const T* wr, int T_, int D, int E, int k, int* idx, float* w, hipStream_t s);
+// Router over x [T, D] (D a multiple of 64), wr [E, D] (E <= 64): logits of rmsnorm(x; g, eps)
+// when g is non-null (x the fp32 residual, everything in fp32), of x itself otherwise; softmax,
+// top-k (ties to the lower index), weights renormalised over the k -> idx/w [T, k].  With lrank
+// (and blkcnt, moe_route_blocks(T) x E ints) it also writes each assignment's stable rank among
+// its router workgroup's assignments of the same expert, and those per-expert counts.
+template <typename Tx, typename Tw>
+hipError_t moe_route(const Tx* x, const Tw* g, float eps, const Tw* wr, int T_, int D, int E, int k, int* idx, float* w,
+                     int* lrank, int* blkcnt, hipStream_t s);
+int moe_route_blocks(int T_);
 
-// Counting sort of the T*k assignments by expert (stable in token order), tile table for the
-// grouped GEMM (BM-row tiles), and each assignment's position in the sorted order.
-hipError_t moe_sort(const int* idx, int T_, int k, int E, int* counts, int* offsets, int* perm_tok, int* pos_of,
-                    int* tiles, int max_tiles, int bm, hipStream_t s);
+// Counting sort of the T*k assignments by expert (stable in token order) from the router's
+// ranks and counts (blkoff: scratch of moe_route_blocks(T) x E ints), tile table for the grouped
+// GEMM (bm-row tiles), and each assignment's position in the sorted order.
+hipError_t moe_sort(const int* idx, const int* lrank, const int* blkcnt, int* blkoff, int T_, int k, int E,
+                    int* counts, int* offsets, int* perm_tok, int* pos_of, int* tiles, int max_tiles, int bm,
+                    hipStream_t s);
 
 // h[t, :] = bf16(r[t, :] + sum_j w[t, j] y[pos_of[t*k + j], :])   (fp32 residual r, fixed j order)
 template <typename TH>

@@ -1,117 +1,233 @@
-// Routed expert MLP support for the A3B gen block: softmax router with top-k and
-// renormalised weights, a deterministic counting sort of (token, slot) assignments by
-// expert with the grouped-GEMM tile table, and the fixed-order weighted combine.
+// Routed expert MLP support for the A3B gen block: softmax router (fp32, from the fp32 residual
+// through the post-attention RMSNorm) with top-k and renormalised weights, a deterministic
+// counting sort of (token, slot) assignments by expert with the grouped-GEMM tile table, and the
+// fixed-order weighted combine.
 // No floating-point atomics anywhere: results are bitwise reproducible.
+#include <climits>
+
 #include "common.h"
 #include "kernels.h"
 
 namespace psf {
 namespace {
 
-// One wave per token; lane e computes expert e's logit from the token row staged in LDS.
-// Selection is by logit (the softmax is monotone), ties to the lower expert index.
-template <typename T>
-__global__ __launch_bounds__(256) void route_kernel(const T* __restrict__ u, const T* __restrict__ wr, int T_, int D,
-                                                    int E, int k, int* __restrict__ idx, float* __restrict__ w) {
-  extern __shared__ float urow_all[];
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  const int t = blockIdx.x * 4 + wave;
-  float* urow = urow_all + wave * D;
-  const int tc = min(t, T_ - 1);
-  for (int i = lane; i < D; i += 64) urow[i] = to_f(u[(int64_t)tc * D + i]);
-  __syncthreads();
-  float logit = -INFINITY;
-  if (lane < E) {
-    float acc = 0.f;
-    const T* wrow = wr + (int64_t)lane * D;
-    for (int i = 0; i < D; ++i) acc += to_f(wrow[i]) * urow[i];
-    logit = acc;
-  }
-  const float mx = warp_max(logit);
-  const float ex = lane < E ? expf(logit - mx) : 0.f;
-  const float z = warp_sum(ex);
-  const float p = ex / z;
-  // top-k by repeated wave argmax of the logit (lower index wins ties)
-  float key = lane < E ? logit : -INFINITY;
-  float selsum = 0.f;
-  int my_rank = -1;
-  for (int j = 0; j < k; ++j) {
-    float bv = key;
-    int bi = lane;
-#pragma unroll
-    for (int o = 32; o > 0; o >>= 1) {
-      const float ov = __shfl_xor(bv, o, 64);
-      const int oi = __shfl_xor(bi, o, 64);
-      if (ov > bv || (ov == bv && oi < bi)) { bv = ov; bi = oi; }
-    }
-    if (lane == bi) { my_rank = j; key = -INFINITY; }
-    selsum += __shfl(p, bi, 64);
-  }
-  if (t < T_ && my_rank >= 0) {
-    idx[(int64_t)t * k + my_rank] = lane;
-    w[(int64_t)t * k + my_rank] = p / selsum;
-  }
-}
+// Router over a tile of RT tokens per workgroup.  With a gain g the logits are those of the
+// RMS-normalised row, computed in one pass over x in fp32:
+//   logit[t, e] = rs_t sum_c x[t, c] (g[c] w[e, c]),  rs_t = 1 / sqrt(mean_c x[t, c]^2 + eps)
+// (g == nullptr: logit = sum_c x[t, c] w[e, c], x already normalised).  64-column chunks of x
+// and of g w are staged in LDS as fp32; thread (tq, eq) accumulates tokens tq + 16 i (i < 4)
+// against experts eq + 16 j (j < EJ).  Then one wave per token: softmax, top-k by repeated wave
+// argmax of the logit (the softmax is monotone; ties to the lower expert index), weights
+// renormalised over the k, and each assignment's stable rank among the workgroup's assignments
+// of the same expert (assignment order t k + slot) with the workgroup's per-expert counts, so
+// that the sort needs no second pass over the assignments.
+constexpr int RT = 64;          // tokens per router workgroup
+constexpr int RCH = 64;         // columns per staged chunk
+constexpr int RST = RCH + 4;    // padded fp32 row stride (272 B: 16 consecutive rows hit 16 distinct 16-byte slots)
 
-// Single workgroup: integer histogram, exclusive scan + tile table, then a stable rank
-// pass over chunks of 1024 assignments (per-expert ballots inside each wave, exclusive
-// scan over the 16 waves, running per-expert base across chunks).
-__global__ __launch_bounds__(1024) void sort_kernel(const int* __restrict__ idx, int n, int E, int k, int bm,
-                                                    int max_tiles, int* __restrict__ counts,
-                                                    int* __restrict__ offsets, int* __restrict__ perm_tok,
-                                                    int* __restrict__ pos_of, int* __restrict__ tiles) {
-  __shared__ int cnt[64], base[64], tot[64], wcnt[16][64];
+template <typename Tx, typename Tw, int EJ>
+__global__ __launch_bounds__(256) void route_kernel(const Tx* __restrict__ x, const Tw* __restrict__ g, float eps,
+                                                    const Tw* __restrict__ wr, int T_, int D, int E, int k,
+                                                    int* __restrict__ idx, float* __restrict__ w,
+                                                    int* __restrict__ lrank, int* __restrict__ blkcnt) {
+  __shared__ __attribute__((aligned(16))) float xs[RT * RST];
+  __shared__ __attribute__((aligned(16))) float gw[16 * EJ * RST];
+  __shared__ float lg[RT * 65];
+  __shared__ float rs[RT];
+  __shared__ int sel[RT * 64];
+  __shared__ int cnt[64], wtot[4][64];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  if (tid < 64) cnt[tid] = 0;
-  __syncthreads();
-  for (int a = tid; a < n; a += 1024) atomicAdd(&cnt[idx[a]], 1);
-  __syncthreads();
-  if (tid == 0) {
-    int s = 0, ts = 0;
-    for (int e = 0; e < E; ++e) {
-      base[e] = s;
-      offsets[e] = s;
-      counts[e] = cnt[e];
-      for (int r = 0; r < cnt[e]; r += bm) {
-        if (ts < max_tiles) {
-          tiles[3 * ts] = e;
-          tiles[3 * ts + 1] = s + r;
-          tiles[3 * ts + 2] = min(bm, cnt[e] - r);
-        }
-        ++ts;
-      }
-      s += cnt[e];
+  const int tq = tid & 15, eq = tid >> 4;
+  const int t0 = blockIdx.x * RT;
+  float acc[4][EJ];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < EJ; ++j) acc[i][j] = 0.f;
+  float ss[4] = {0.f, 0.f, 0.f, 0.f};
+  for (int c0 = 0; c0 < D; c0 += RCH) {
+    // stage x: row (tid >> 4) + 16 i, columns 4 tq .. 4 tq + 3 (fp32 in LDS)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int r = eq + 16 * i;
+      const int t = min(t0 + r, T_ - 1);
+      const Tx* src = x + (int64_t)t * D + c0 + 4 * tq;
+      float f[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) f[e] = to_f(src[e]);
+      ss[i] += f[0] * f[0] + f[1] * f[1] + f[2] * f[2] + f[3] * f[3];
+      *(float4*)(xs + r * RST + 4 * tq) = make_float4(f[0], f[1], f[2], f[3]);
     }
-    offsets[E] = s;
-    for (int i = ts; i < max_tiles; ++i) tiles[3 * i] = -1;
-  }
-  __syncthreads();
-  const uint64_t lt_mask = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
-  for (int c0 = 0; c0 < n; c0 += 1024) {
-    const int a = c0 + tid;
-    const int e = a < n ? idx[a] : -1;
-    int rank = 0;
-    for (int x = 0; x < E; ++x) {
-      const uint64_t bal = __ballot(e == x);
-      if (e == x) rank = __popcll(bal & lt_mask);
-      if (lane == 0) wcnt[wave][x] = __popcll(bal);
+    // stage g w for experts eq + 16 j
+#pragma unroll
+    for (int j = 0; j < EJ; ++j) {
+      const int e = eq + 16 * j;
+      float f[4] = {0.f, 0.f, 0.f, 0.f};
+      if (e < E) {
+        const Tw* src = wr + (int64_t)e * D + c0 + 4 * tq;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) f[q] = g ? to_f(g[c0 + 4 * tq + q]) * to_f(src[q]) : to_f(src[q]);
+      }
+      *(float4*)(gw + e * RST + 4 * tq) = make_float4(f[0], f[1], f[2], f[3]);
     }
     __syncthreads();
-    if (tid < E) {
-      int s = 0;
-      for (int w2 = 0; w2 < 16; ++w2) { const int c = wcnt[w2][tid]; wcnt[w2][tid] = s; s += c; }
-      tot[tid] = s;
+#pragma unroll 4
+    for (int c = 0; c < RCH; c += 4) {
+      float4 xv[4], wv[EJ];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) xv[i] = *(const float4*)(xs + (tq + 16 * i) * RST + c);
+#pragma unroll
+      for (int j = 0; j < EJ; ++j) wv[j] = *(const float4*)(gw + (eq + 16 * j) * RST + c);
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < EJ; ++j) {
+          float a = acc[i][j];
+          a = fmaf(xv[i].x, wv[j].x, a);
+          a = fmaf(xv[i].y, wv[j].y, a);
+          a = fmaf(xv[i].z, wv[j].z, a);
+          a = fmaf(xv[i].w, wv[j].w, a);
+          acc[i][j] = a;
+        }
+    }
+    __syncthreads();
+  }
+  // row sums of squares: the 16 lanes of a row group are consecutive
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    float v = ss[i];
+#pragma unroll
+    for (int o = 8; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
+    if (tq == 0) rs[eq + 16 * i] = g ? 1.0f / sqrtf(v / (float)D + eps) : 1.0f;
+  }
+  if (tid < 64) cnt[tid] = 0;
+  __syncthreads();
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < EJ; ++j)
+      if (eq + 16 * j < E) lg[(tq + 16 * i) * 65 + eq + 16 * j] = acc[i][j] * rs[tq + 16 * i];
+  __syncthreads();
+  // one wave per token: softmax, top-k, renormalised weights
+  for (int r = wave; r < RT; r += 4) {
+    const int t = t0 + r;
+    const float logit = lane < E ? lg[r * 65 + lane] : -INFINITY;
+    const float mx = warp_max(logit);
+    const float ex = lane < E ? expf(logit - mx) : 0.f;
+    const float p = ex / warp_sum(ex);
+    // selection key: the logit's order as a signed integer (NaN lowest among the experts, an
+    // expert already taken and the lanes past E below every expert), so that the k rounds always
+    // pick k distinct experts
+    int key = INT_MIN;
+    if (lane < E) {
+      const int b = __float_as_int(logit);
+      key = __builtin_isnan(logit) ? INT_MIN + 1 : max(b >= 0 ? b : b ^ 0x7fffffff, INT_MIN + 1);
+    }
+    float selsum = 0.f;
+    int my_rank = -1;
+    for (int j = 0; j < k; ++j) {
+      int bv = key, bi = lane;
+#pragma unroll
+      for (int o = 32; o > 0; o >>= 1) {
+        const int ov = __shfl_xor(bv, o, 64);
+        const int oi = __shfl_xor(bi, o, 64);
+        if (ov > bv || (ov == bv && oi < bi)) { bv = ov; bi = oi; }
+      }
+      if (lane == bi) { my_rank = j; key = INT_MIN; }
+      selsum += __shfl(p, bi, 64);
+    }
+    if (my_rank >= 0) sel[r * k + my_rank] = t < T_ ? lane : -1;
+    if (t < T_ && my_rank >= 0) {
+      idx[(int64_t)t * k + my_rank] = lane;
+      w[(int64_t)t * k + my_rank] = p / selsum;
+    }
+  }
+  if (!lrank) return;
+  __syncthreads();
+  // stable rank of each assignment among this workgroup's assignments of its expert, in chunks of
+  // 256 assignments: per-expert ballots inside each wave, prefix over the 4 waves, running counts
+  const int n = RT * k;
+  const uint64_t lt_mask = lane == 0 ? 0ull : (~0ull >> (64 - lane));
+  for (int a0 = 0; a0 < n; a0 += 256) {
+    const int a = a0 + tid;
+    const int e = a < n ? sel[a] : -1;
+    int rank = 0;
+    for (int xe = 0; xe < E; ++xe) {
+      const uint64_t bal = __ballot(e == xe);
+      if (e == xe) rank = __popcll(bal & lt_mask);
+      if (lane == 0) wtot[wave][xe] = __popcll(bal);
     }
     __syncthreads();
     if (e >= 0) {
-      const int pos = base[e] + wcnt[wave][e] + rank;
-      perm_tok[pos] = a / k;
-      pos_of[a] = pos;
+      int before = cnt[e];
+      for (int w2 = 0; w2 < wave; ++w2) before += wtot[w2][e];
+      lrank[(int64_t)t0 * k + a] = before + rank;
     }
     __syncthreads();
-    if (tid < E) base[tid] += tot[tid];
+    if (tid < E) cnt[tid] += wtot[0][tid] + wtot[1][tid] + wtot[2][tid] + wtot[3][tid];
     __syncthreads();
   }
+  if (tid < E) blkcnt[(int64_t)blockIdx.x * E + tid] = cnt[tid];
+}
+
+// One workgroup: per-expert totals and, for every router workgroup b, the first sorted position of
+// its assignments of expert e: off[b][e] = offsets[e] + sum_{b' < b} blkcnt[b'][e].  16 threads per
+// expert, each over a contiguous range of workgroups; then the grouped-GEMM tile table.
+__global__ __launch_bounds__(1024) void moe_scan_kernel(const int* __restrict__ blkcnt, int nblk, int E, int bm,
+                                                        int max_tiles, int* __restrict__ blkoff,
+                                                        int* __restrict__ counts, int* __restrict__ offsets,
+                                                        int* __restrict__ tiles) {
+  __shared__ int part[16][64], base[65];
+  const int tid = threadIdx.x, e = tid & 63, q = tid >> 6;
+  const int per = (nblk + 15) / 16, b0 = q * per, b1 = min(nblk, b0 + per);
+  int s = 0;
+  if (e < E)
+    for (int b = b0; b < b1; ++b) s += blkcnt[(int64_t)b * E + e];
+  part[q][e] = s;
+  __syncthreads();
+  if (tid == 0) {
+    int o = 0, ts = 0;
+    for (int x = 0; x < E; ++x) {
+      int c = 0;
+      for (int qq = 0; qq < 16; ++qq) c += part[qq][x];
+      base[x] = o;
+      offsets[x] = o;
+      counts[x] = c;
+      for (int r = 0; r < c; r += bm) {
+        if (ts < max_tiles) {
+          tiles[3 * ts] = x;
+          tiles[3 * ts + 1] = o + r;
+          tiles[3 * ts + 2] = min(bm, c - r);
+        }
+        ++ts;
+      }
+      o += c;
+    }
+    offsets[E] = o;
+    for (int i = ts; i < max_tiles; ++i) tiles[3 * i] = -1;
+  }
+  __syncthreads();
+  if (e < E) {
+    int run = base[e];
+    for (int qq = 0; qq < q; ++qq) run += part[qq][e];
+    for (int b = b0; b < b1; ++b) {
+      blkoff[(int64_t)b * E + e] = run;
+      run += blkcnt[(int64_t)b * E + e];
+    }
+  }
+}
+
+// Sorted position of every assignment a = t k + slot: its router workgroup's first position for
+// the expert plus its stable rank there; perm_tok lists the tokens in sorted order.
+__global__ __launch_bounds__(256) void moe_scatter_kernel(const int* __restrict__ idx, const int* __restrict__ lrank,
+                                                          const int* __restrict__ blkoff, int n, int k, int E,
+                                                          int* __restrict__ perm_tok, int* __restrict__ pos_of) {
+  const int a = blockIdx.x * 256 + threadIdx.x;
+  if (a >= n) return;
+  const int t = a / k;
+  const int pos = blkoff[(int64_t)(t / RT) * E + idx[a]] + lrank[a];
+  pos_of[a] = pos;
+  perm_tok[pos] = t;
 }
 
 template <typename TH>
@@ -137,20 +253,36 @@ __global__ __launch_bounds__(256) void combine_kernel(TH* __restrict__ h, const 
 
 }  // namespace
 
-template <typename T>
-hipError_t moe_route(const T* u, const T* wr, int T_, int D, int E, int k, int* idx, float* w, hipStream_t s) {
+template <typename Tx, typename Tw>
+hipError_t moe_route(const Tx* x, const Tw* g, float eps, const Tw* wr, int T_, int D, int E, int k, int* idx, float* w,
+                     int* lrank, int* blkcnt, hipStream_t s) {
   if (T_ <= 0) return hipSuccess;
-  const size_t lds = 4 * (size_t)D * sizeof(float);
-  hipLaunchKernelGGL(route_kernel<T>, dim3((T_ + 3) / 4), dim3(256), lds, s, u, wr, T_, D, E, k, idx, w);
+  const dim3 grid((T_ + RT - 1) / RT);
+  if (E <= 32)
+    hipLaunchKernelGGL((route_kernel<Tx, Tw, 2>), grid, dim3(256), 0, s, x, g, eps, wr, T_, D, E, k, idx, w, lrank, blkcnt);
+  else
+    hipLaunchKernelGGL((route_kernel<Tx, Tw, 4>), grid, dim3(256), 0, s, x, g, eps, wr, T_, D, E, k, idx, w, lrank, blkcnt);
   return hipGetLastError();
 }
-template hipError_t moe_route<bf16>(const bf16*, const bf16*, int, int, int, int, int*, float*, hipStream_t);
-template hipError_t moe_route<float>(const float*, const float*, int, int, int, int, int*, float*, hipStream_t);
+template hipError_t moe_route<float, bf16>(const float*, const bf16*, float, const bf16*, int, int, int, int, int*,
+                                           float*, int*, int*, hipStream_t);
+template hipError_t moe_route<bf16, bf16>(const bf16*, const bf16*, float, const bf16*, int, int, int, int, int*,
+                                          float*, int*, int*, hipStream_t);
+template hipError_t moe_route<float, float>(const float*, const float*, float, const float*, int, int, int, int, int*,
+                                            float*, int*, int*, hipStream_t);
 
-hipError_t moe_sort(const int* idx, int T_, int k, int E, int* counts, int* offsets, int* perm_tok, int* pos_of,
-                    int* tiles, int max_tiles, int bm, hipStream_t s) {
-  hipLaunchKernelGGL(sort_kernel, dim3(1), dim3(1024), 0, s, idx, T_ * k, E, k, bm, max_tiles, counts, offsets,
-                     perm_tok, pos_of, tiles);
+int moe_route_blocks(int T_) { return (T_ + RT - 1) / RT; }
+
+hipError_t moe_sort(const int* idx, const int* lrank, const int* blkcnt, int* blkoff, int T_, int k, int E,
+                    int* counts, int* offsets, int* perm_tok, int* pos_of, int* tiles, int max_tiles, int bm,
+                    hipStream_t s) {
+  const int nblk = moe_route_blocks(T_);
+  hipLaunchKernelGGL(moe_scan_kernel, dim3(1), dim3(1024), 0, s, blkcnt, nblk, E, bm, max_tiles, blkoff, counts,
+                     offsets, tiles);
+  const int n = T_ * k;
+  if (n > 0)
+    hipLaunchKernelGGL(moe_scatter_kernel, dim3((n + 255) / 256), dim3(256), 0, s, idx, lrank, blkoff, n, k, E,
+                       perm_tok, pos_of);
   return hipGetLastError();
 }
 

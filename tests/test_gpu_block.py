@@ -94,34 +94,43 @@ def test_bf16_residual_stream(lib, cfg):
     assert worst <= 1.0
 
 
-def test_config4_moe_block_sampled_rows(lib):
-    """A3B MoE block at full size (2 x 4096 tokens, 32 experts top-8).  The GPU's routed sets
-    must equal the oracle's except where the oracle's 8th/9th logit gap is below what the
-    bf16 residual stream can resolve; the output is compared on 512 sampled tokens per branch
-    with the oracle routed through the GPU's sets."""
+MOE_TIE_TOL = 1e-2   # router logits: top-8 sets may differ only where the 8th/9th logit gap is below this
+
+
+def test_config4_moe_block_all_tokens(lib):
+    """A3B MoE block at full size (2 x 4096 tokens, 32 experts top-8).  The GPU routes in fp32 from
+    the fp32 mid-block residual, as the oracle does; its top-8 set must equal the oracle's for every
+    token whose oracle 8th/9th logit gap is at least 1e-2 (both sets are correct at a closer
+    tie).  The output is compared on every token: against the oracle's own block where the sets
+    agree, and against the oracle re-run with the GPU's set on the tokens routed differently."""
     w = W.CONFIGS[4]
     d = w.dims
-    log("config 4: MoE block")
+    log("config 4: MoE block, every token")
     wts, h, pk, pv = block_inputs(w, 0, 0, "bf16")
     got, gidx = run_gpu_block(lib, w, wts, h, pk, pv, "bf16", topk=True)
-    rows = np.sort(W.rng(4, 0, "rows").choice(w.n_tokens, 512, replace=False))
-    ref_own, parts = O.gen_block(h, wts, d, pk, pv, rows=rows, return_parts=True)
-    tie_tol = 5e-2
-    mism = 0
-    near = 0
+    ref, parts = O.gen_block(h, wts, d, pk, pv, return_parts=True)
+    mism, near, worst_gap = [], 0, 0.0
     for b in range(h.shape[0]):
         logits = parts[b]["u_post"].astype(np.float64) @ wts["w_router"].T.astype(np.float64)
         srt = np.sort(logits, axis=1)[:, ::-1]
         gap = srt[:, d.top_k - 1] - srt[:, d.top_k]
         oidx = np.argsort(-logits, axis=1, kind="stable")[:, :d.top_k]
-        for i, t in enumerate(rows):
-            if set(gidx[b, t]) != set(oidx[i]):
-                mism += 1
-                assert gap[i] < tie_tol, f"token {t} routed differently with gap {gap[i]}"
-            near += int(gap[i] < tie_tol)
-    log(f"  routing: {mism} sampled tokens differ, {near} near-ties (gap < {tie_tol})")
-    ref = O.gen_block(h, wts, d, pk, pv, rows=rows, moe_idx=gidx.astype(np.int64))
-    check(got[:, rows], ref, h[:, rows], BLOCK_TOL, "config 4 (GPU routing)")
+        diff = [t for t in range(h.shape[1]) if set(gidx[b, t]) != set(oidx[t])]
+        for t in diff:
+            worst_gap = max(worst_gap, float(gap[t]))
+            assert gap[t] < MOE_TIE_TOL, f"branch {b} token {t} routed differently with gap {gap[t]}"
+        mism.append(diff)
+        near += int((gap < MOE_TIE_TOL).sum())
+    log(f"  routing: {sum(map(len, mism))} of {h.shape[0] * h.shape[1]} tokens differ (largest oracle gap among "
+        f"them {worst_gap:.2e}), {near} near-ties (gap < {MOE_TIE_TOL})")
+    want = ref.copy()
+    for b, diff in enumerate(mism):
+        if diff:
+            rows = np.array(diff)
+            rr = O.gen_block(h[b:b + 1], wts, d, pk[b:b + 1], pv[b:b + 1], rows=rows,
+                             moe_idx=gidx[b:b + 1].astype(np.int64))
+            want[b, rows] = rr[0]
+    check(got, want, h, BLOCK_TOL, "config 4 (every token)")
 
 
 def lora_case():

@@ -65,10 +65,11 @@ def run_prefix(lib, d, layer_wts, h, dtype):
     return host(hd), K, V, topk
 
 
-def check_routing(gidx, parts, wts, d, what, tie_tol=5e-2):
-    """The GPU's expert sets equal the oracle's except at near-ties of the 8th/9th router logit
-    (gap below what the bf16 MLP input can resolve)."""
+def check_routing(gidx, parts, wts, d, what, tie_tol=1e-2):
+    """The GPU's expert sets equal the oracle's on every token except at near-ties of the 8th/9th
+    router logit (gap below 1e-2, where both sets are correct)."""
     mism = near = 0
+    worst = 0.0
     for b in range(gidx.shape[0]):
         logits = parts[b]["u_post"].astype(np.float64) @ wts["w_router"].T.astype(np.float64)
         srt = np.sort(logits, axis=1)[:, ::-1]
@@ -77,9 +78,11 @@ def check_routing(gidx, parts, wts, d, what, tie_tol=5e-2):
         for t in range(gidx.shape[1]):
             if set(gidx[b, t]) != set(oidx[t]):
                 mism += 1
+                worst = max(worst, float(gap[t]))
                 assert gap[t] < tie_tol, f"{what}: token {t} routed differently with gap {gap[t]}"
         near += int((gap < tie_tol).sum())
-    log(f"  {what}: routing {mism} tokens differ, {near} near-ties (gap < {tie_tol})")
+    log(f"  {what}: routing {mism} tokens differ (largest oracle gap among them {worst:.2e}), "
+        f"{near} near-ties (gap < {tie_tol})")
 
 
 def check_layer(got, ref, h_in, dtype, what):
