@@ -52,6 +52,10 @@ def bf16_faithful(got: np.ndarray, ref: np.ndarray, slack: float = 1.05) -> floa
 BLOCK_TOL = 2e-2          # max abs error <= 2e-2 x RMS(reference) per block (bf16 runs)
 BLOCK_TOL_F32 = 1e-4      # fp32 runs: only summation order differs
 TOWER_COS = 0.999         # cosine similarity after the full tower
+# Looser bars where the arithmetic of a correct bf16 implementation needs them; each is derived
+# from the rounding model in tests/precision_model.py by tests/test_tolerance_derivations.py:
+PREFIX_TOL = 2.5e-2       # prompt-pass block (its first tokens attend to a handful of keys)
+DH_TOL = 4e-2             # residual-stream gradient of the training block backward
 
 
 def weights_to_dev(wts: dict, dtype: str) -> dict:

@@ -7,17 +7,18 @@ import pytest
 
 import oracle as O
 import workloads as W
-from gpu_helpers import cosine, dev, host, log, rel_max_err, rms, weights_to_dev
+from gpu_helpers import DH_TOL, cosine, dev, host, log, rel_max_err, rms, weights_to_dev
 
 pytestmark = pytest.mark.gpu
 
 # Gradients through a bf16 block: the oracle runs in fp32 on the same bf16-rounded inputs.  The
-# backward rounds twice as many operands to bf16 as the forward (the recomputed activations, then
-# dy, dz, dgate/dup, du2, dx, dO, P and dS in the attention products, dqkv, du).  Emulating exactly
-# those roundings on the CPU (bf16 round-to-nearest-even, fp32 elsewhere) at the 8B LoRA block
-# shape gives max |dh err| = 2.93e-2 RMS; the bar is 4e-2 RMS.  A LoRA weight gradient is a sum
-# over every token, so it is checked by cosine >= 0.999 and max |err| <= 3e-2 max |ref|.
-DH_TOL = 4e-2
+# backward rounds about twice as many operands to bf16 as the forward (the saved activations, then
+# dy, dz, dgate/dup, du2, the residual gradient, dO, P and dS in the attention products, dqkv,
+# du).  The bar for dh is DH_TOL = 4e-2 RMS; the rounding model of tests/precision_model.py at the
+# 8B LoRA block shape gives the error a correct bf16 backward shows, and
+# test_tolerance_derivations.py::test_backward_dh_tolerance checks that DH_TOL sits above it with a
+# margin.  A LoRA weight gradient is a sum over every token, so it is checked by cosine >= 0.999
+# and max |err| <= 3e-2 max |ref|.
 G_COS = 0.999
 G_TOL = 3e-2
 

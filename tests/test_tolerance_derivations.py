@@ -1,0 +1,67 @@
+"""Where a GPU parity bar differs from the plain 2e-2 per-block one, the arithmetic decides it.
+
+Each test runs the numpy rounding model of the bf16 path (``precision_model``) and the fp32
+oracle on the same seeded inputs at the shape the GPU test uses, and checks the bar against the
+error the model shows:
+  - the prompt-pass block bar PREFIX_TOL (2.5e-2) sits above the modelled error with a margin;
+  - the training backward's dh bar DH_TOL (4e-2) likewise;
+  - the fp32 residual stream (reading R16 of the design notes): with it the modelled 8B gen
+    block stays inside 2e-2, while a residual rounded to bf16 at the middle and the end of the
+    block does not, which is why the residual stays fp32.
+CPU only; each test takes seconds to a minute.
+"""
+import numpy as np
+
+import oracle as O
+import workloads as W
+from gpu_helpers import BLOCK_TOL, DH_TOL, PREFIX_TOL, log
+from precision_model import gen_block_bf16, gen_block_bwd_bf16, rel_max_err
+
+MARGIN = 1.15   # a bar must exceed the modelled error by at least 15 %
+
+
+def test_prefix_tolerance():
+    """The 8B prompt block over 2 prompts of 400 tokens (test_prefix_qwen3_8b_block_400_tokens)."""
+    w = W.CONFIGS[1]
+    d = W.prefix_dims(w)
+    wts = W.prefix_layer_weights(w, 0, 0, "bf16")
+    h = W.prompt_hidden(w, 0, "bf16")
+    ref = O.prefix_block(h, wts, d)[0]
+    got = gen_block_bf16(h, wts, d, None, None, causal=True)
+    e = rel_max_err(got, ref)
+    log(f"prompt block, rounding model vs oracle: max|err|/RMS = {e:.3e} (bar {PREFIX_TOL})")
+    assert e * MARGIN <= PREFIX_TOL
+
+
+def test_fp32_residual_reading():
+    """The 8B gen block over 2 x 1024 tokens, prefix 400 (config 1)."""
+    w = W.CONFIGS[1]
+    wts = W.layer_weights(w, 0, 0, "bf16")
+    h = W.block_hidden(w, 0, "bf16")
+    pk, pv = zip(*[W.prefix_kv(w, 0, s, 0, "bf16") for s in range(w.batch)])
+    ref = O.gen_block(h, wts, w.dims, list(pk), list(pv))
+    e32 = rel_max_err(gen_block_bf16(h, wts, w.dims, pk, pv, residual="f32"), ref)
+    e16 = rel_max_err(gen_block_bf16(h, wts, w.dims, pk, pv, residual="bf16_both"), ref)
+    log(f"8B block, rounding model vs oracle: fp32 residual {e32:.3e}, bf16 mid-block and output {e16:.3e} "
+        f"(bar {BLOCK_TOL})")
+    assert e32 * MARGIN <= BLOCK_TOL
+    assert e16 > BLOCK_TOL
+
+
+def test_backward_dh_tolerance():
+    """The 8B LoRA training block (4 x 1024 tokens, prefixes from the cache, rank 32, adapters at
+    the size training reaches) as in test_block_backward_8b_lora_block."""
+    w = W.scaled(W.CONFIGS[3], n_layers=1)
+    d = w.dims
+    wts = W.layer_weights(w, 0, 0, "bf16")
+    for s in W.LORA_SITES:
+        wts[f"lora_b_{s}"] = W.round_bf16(wts[f"lora_b_{s}"] * 100.0)
+    h = W.maybe_bf16(W.normal(3, 0, "train_hidden", (w.n_img, w.n_tokens, d.hidden)), "bf16")
+    slots = W.cache_slots(w, 0)
+    pk, pv = zip(*[W.prefix_kv(w, 0, s, 0, "bf16") for s in slots])
+    dy = W.normal(3, 0, "train_dy", h.shape, 1e-3)
+    ref, _ = O.gen_block_bwd(h, wts, d, list(pk), list(pv), dy)
+    got = gen_block_bwd_bf16(h, wts, d, list(pk), list(pv), dy)
+    e = rel_max_err(got, ref)
+    log(f"8B LoRA block backward, rounding model vs oracle: dh max|err|/RMS = {e:.3e} (bar {DH_TOL})")
+    assert np.isfinite(e) and e * MARGIN <= DH_TOL
