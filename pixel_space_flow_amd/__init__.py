@@ -11,7 +11,9 @@ import os
 from typing import Optional, Sequence
 
 HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(HERE, "libpsf_gen.so")
+# PSF_GEN_LIB names another build of the same library (the host-only sanitizer build that the
+# CPU tests of the argument checks load); by default the in-tree HIP build
+LIB_PATH = os.environ.get("PSF_GEN_LIB") or os.path.join(HERE, "libpsf_gen.so")
 
 GEN_OK, GEN_EINVAL, GEN_EUNSUPPORTED, GEN_EWORKSPACE, GEN_EHIP = 0, -1, -2, -3, -4
 GEN_F32, GEN_BF16 = 0, 1

@@ -79,6 +79,63 @@ def build(verbose: bool = True) -> str:
     return OUT
 
 
+SAN_DIR = os.path.join(BUILD_DIR, "host_asan")
+SAN_OUT = os.path.join(BUILD_DIR, "libpsf_gen_host_asan.so")
+# the host pass instrumented with AddressSanitizer and UndefinedBehaviorSanitizer; the device code
+# is built as usual (no GPU sanitizer)
+SAN_FLAGS = ["-O1", "-g", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}",
+             "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+             "-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fsanitize=undefined",
+             "-Xarch_host", "-fno-sanitize-recover=undefined", "-Xarch_host", "-fno-omit-frame-pointer",
+             "-Wno-unused-result"]
+
+
+def _sources_stamp(flags) -> str:
+    import hashlib
+    h = hashlib.sha256(" ".join(flags).encode())
+    for f in sorted(os.listdir(CSRC)):
+        h.update(f.encode())
+        h.update(open(os.path.join(CSRC, f), "rb").read())
+    h.update(open(os.path.join(HERE, "..", "include", "psf_gen.h"), "rb").read())
+    h.update(open(os.path.join(HERE, "..", "include", "psf_gen_ops.h"), "rb").read())
+    return h.hexdigest()
+
+
+def build_host_sanitized(verbose: bool = True) -> str:
+    """The library with its host code (the C ABI, argument validation, workspace layout,
+    launchers) built with AddressSanitizer and UndefinedBehaviorSanitizer, for the CPU tests of
+    the host-side checks; rebuilt only when a source changed.  Load it with clang's ASan runtime
+    preloaded (libclang_rt.asan-x86_64.so)."""
+    stamp = _sources_stamp(SAN_FLAGS)
+    stamp_file = SAN_OUT + ".stamp"
+    if os.path.exists(SAN_OUT) and os.path.exists(stamp_file) and open(stamp_file).read() == stamp:
+        return SAN_OUT
+    os.makedirs(SAN_DIR, exist_ok=True)
+
+    def one(src):
+        obj = os.path.join(SAN_DIR, os.path.splitext(src)[0] + ".o")
+        cmd = [HIPCC, *SAN_FLAGS, "-x", "hip", "-c", os.path.join(CSRC, src), "-o", obj]
+        r = subprocess.run(cmd, capture_output=True, text=True)
+        if r.returncode != 0:
+            raise RuntimeError(f"hipcc (sanitized host) failed for {src}:\n{r.stderr}")
+        return obj
+    with ThreadPoolExecutor(min(len(SOURCES), os.cpu_count() or 4)) as ex:
+        objs = list(ex.map(one, SOURCES))
+    cmd = [HIPCC, "-shared", "-fPIC", f"--offload-arch={ARCH}", "-Xarch_host", "-fsanitize=address",
+           "-Xarch_host", "-fsanitize=undefined", "-Xarch_host", "-shared-libasan", *objs, "-o", SAN_OUT]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"link (sanitized host) failed:\n{r.stderr}")
+    with open(stamp_file, "w") as f:
+        f.write(stamp)
+    if verbose:
+        print(f"built {SAN_OUT}")
+    return SAN_OUT
+
+
 if __name__ == "__main__":
-    build()
+    if len(sys.argv) > 1 and sys.argv[1] == "host-asan":
+        build_host_sanitized()
+    else:
+        build()
     sys.exit(0)
