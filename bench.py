@@ -440,19 +440,24 @@ def cpu_baseline(w, seed=0):
 
 def run_kernel_only(psf, w, which: str, reps: int):
     """One kernel family of the step at the workload's shapes, `reps` launches (rocprofv3 counter
-    runs); "copy" is a plain 256 MiB device copy used to calibrate the byte counters."""
+    runs): the gate/up + SwiGLU GEMM, the down and O projections onto an fp32 residual, the QKV
+    GEMM, the attention; "copy" is a plain 256 MiB device copy used to calibrate the byte
+    counters."""
     import torch
     d = w.dims
     M, D, I = w.batch * w.n_tokens, d.hidden, d.mlp_intermediate
     bf = torch.bfloat16
     g = torch.Generator(device="cuda")
     g.manual_seed(0)
-    if which == "gate_up":
-        x = torch.randn(M, D, device="cuda", generator=g).to(bf)
-        wt = (0.02 * torch.randn(2 * I, D, device="cuda", generator=g)).to(bf)
-        y = torch.empty(M, I, device="cuda", dtype=bf)
+    if which in ("gate_up", "down", "o", "qkv"):
+        QD = d.n_q_heads * d.head_dim
+        K, N, epi, ydt = {"gate_up": (D, I, 2, bf), "down": (I, D, 3, torch.float32), "o": (QD, D, 3, torch.float32),
+                          "qkv": (D, d.qkv_out, 0, bf)}[which]
+        x = torch.randn(M, K, device="cuda", generator=g).to(bf)
+        wt = (0.02 * torch.randn(2 * N if epi == 2 else N, K, device="cuda", generator=g)).to(bf)
+        y = torch.zeros(M, N, device="cuda", dtype=ydt)
         for _ in range(reps):
-            psf.op_linear(x, wt, y, None, 2)
+            psf.op_linear(x, wt, y, None, epi)
     elif which == "attention":
         Hq, Hkv, hd, P, N = d.n_q_heads, d.n_kv_heads, d.head_dim, w.prefix_len, w.n_tokens
         qkv = torch.randn(M, (Hq + 2 * Hkv) * hd, device="cuda", generator=g).to(bf)
@@ -641,7 +646,7 @@ def main():
                          "prompt pass that writes the prefix-KV cache (2 prompts x 400 tokens, 36 layers); "
                          "dual-cfg: the 2048^2 image-edit step with three branches (cfg 4, image cfg 2); "
                          "lora-train: one LoRA training step (4 x 1024^2, rank 32, x0 loss)")
-    ap.add_argument("--kernel", choices=("gate_up", "attention", "copy"),
+    ap.add_argument("--kernel", choices=("gate_up", "down", "o", "qkv", "attention", "copy"),
                     help="run only this kernel at the workload's shapes, --steps times (for counter runs)")
     args = ap.parse_args()
     if args.gpus != 1:

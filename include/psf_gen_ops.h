@@ -31,7 +31,9 @@ int gen_op_rmsnorm(const void* x, const void* g, void* y, int rows, int D, float
 /* Linear layer y = x w^T with an epilogue, x [M, K], K % 64 == 0:
  *   epi 0: y [M, N] = x w^T,               w [N, K]
  *   epi 1: y [M, N] = resid + x w^T,       w [N, K], resid [M, N] (may equal y)
- *   epi 2: y [M, N] = silu(x wg^T) * (x wu^T), w [2N, K] = gate rows then up rows */
+ *   epi 2: y [M, N] = silu(x wg^T) * (x wu^T), w [2N, K] = gate rows then up rows
+ *   epi 3: y [M, N] float32 += x w^T (dtype GEN_BF16 only; resid ignored): the O and down
+ *          projections onto the block's fp32 residual stream */
 int gen_op_linear(const void* x, const void* w, void* y, const void* resid, int M, int N, int K, int epi, int dtype,
                   void* stream);
 

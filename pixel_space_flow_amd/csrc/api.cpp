@@ -1442,7 +1442,8 @@ int gen_op_linear(const void* x, const void* w, void* y, const void* resid, int 
   if (check_dtype(dtype)) return GEN_EINVAL;
   if (!x || !w || !y || !aligned16(x) || !aligned16(w) || !aligned16(y)) return fail(GEN_EINVAL, "NULL or unaligned pointer");
   if (M < 0 || N <= 0 || K <= 0 || K % 64) return fail(GEN_EINVAL, "M %d N %d K %d (K must be a positive multiple of 64)", M, N, K);
-  if (epi < 0 || epi > 2) return fail(GEN_EINVAL, "epi %d not in 0..2", epi);
+  if (epi < 0 || epi > 3) return fail(GEN_EINVAL, "epi %d not in 0..3", epi);
+  if (epi == 3 && dtype != GEN_BF16) return fail(GEN_EUNSUPPORTED, "epi 3 needs dtype GEN_BF16");
   if (epi == 1 && !resid) return fail(GEN_EINVAL, "epi 1 needs resid");
   if (epi == 2 && N % 8) return fail(GEN_EINVAL, "epi 2 needs N %% 8 == 0");
   GemmParams p = gp();
@@ -1451,6 +1452,7 @@ int gen_op_linear(const void* x, const void* w, void* y, const void* resid, int 
   if (epi == 0) { p.N = N; p.ldc = N; }
   if (epi == 1) { p.N = N; p.ldc = N; p.R = resid; p.ldr = N; e = EPI_RESID; }
   if (epi == 2) { p.N = 2 * N; p.ldc = N; p.bmode = 1; p.swiglu_I = N; e = EPI_SWIGLU; }
+  if (epi == 3) { p.N = N; p.ldc = N; p.R = y; p.ldr = N; e = EPI_RESID_F32; }
   hipStream_t s = (hipStream_t)stream;
   if (dtype == GEN_BF16) HIP_TRY(gemm_bf16(p, e, s));
   else HIP_TRY(gemm_f32(p, e, s));

@@ -15,13 +15,13 @@ namespace {
 // RMS-normalised row, computed in one pass over x in fp32:
 //   logit[t, e] = rs_t sum_c x[t, c] (g[c] w[e, c]),  rs_t = 1 / sqrt(mean_c x[t, c]^2 + eps)
 // (g == nullptr: logit = sum_c x[t, c] w[e, c], x already normalised).  64-column chunks of x
-// and of g w are staged in LDS as fp32; thread (tq, eq) accumulates tokens tq + 16 i (i < 4)
-// against experts eq + 16 j (j < EJ).  Then one wave per token: softmax, top-k by repeated wave
-// argmax of the logit (the softmax is monotone; ties to the lower expert index), weights
-// renormalised over the k, and each assignment's stable rank among the workgroup's assignments
-// of the same expert (assignment order t k + slot) with the workgroup's per-expert counts, so
-// that the sort needs no second pass over the assignments.
-constexpr int RT = 64;          // tokens per router workgroup
+// and of g w are staged in LDS as fp32; thread (t, eq) accumulates token t = tid % 16 against
+// experts eq + 16 j (eq = tid / 16, j < EJ).  Then one wave per token: softmax, top-k by
+// repeated wave argmax of the logit (the softmax is monotone; ties to the lower expert index),
+// weights renormalised over the k, and each assignment's stable rank among the workgroup's
+// assignments of the same expert (assignment order t k + slot) with the workgroup's per-expert
+// counts, so that the sort needs no second pass over the assignments.
+constexpr int RT = 16;          // tokens per router workgroup
 constexpr int RCH = 64;         // columns per staged chunk
 constexpr int RST = RCH + 4;    // padded fp32 row stride (272 B: 16 consecutive rows hit 16 distinct 16-byte slots)
 
@@ -39,26 +39,21 @@ __global__ __launch_bounds__(256) void route_kernel(const Tx* __restrict__ x, co
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int tq = tid & 15, eq = tid >> 4;
   const int t0 = blockIdx.x * RT;
-  float acc[4][EJ];
+  float acc[EJ];
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
-#pragma unroll
-    for (int j = 0; j < EJ; ++j) acc[i][j] = 0.f;
-  float ss[4] = {0.f, 0.f, 0.f, 0.f};
+  for (int j = 0; j < EJ; ++j) acc[j] = 0.f;
+  float ss = 0.f;
+  // staging roles: x row eq (16 rows x 16 chunks of 4 columns); g w rows eq + 16 j
+  const int xr = min(t0 + eq, T_ - 1);
   for (int c0 = 0; c0 < D; c0 += RCH) {
-    // stage x: row (tid >> 4) + 16 i, columns 4 tq .. 4 tq + 3 (fp32 in LDS)
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int r = eq + 16 * i;
-      const int t = min(t0 + r, T_ - 1);
-      const Tx* src = x + (int64_t)t * D + c0 + 4 * tq;
+    {
+      const Tx* src = x + (int64_t)xr * D + c0 + 4 * tq;
       float f[4];
 #pragma unroll
       for (int e = 0; e < 4; ++e) f[e] = to_f(src[e]);
-      ss[i] += f[0] * f[0] + f[1] * f[1] + f[2] * f[2] + f[3] * f[3];
-      *(float4*)(xs + r * RST + 4 * tq) = make_float4(f[0], f[1], f[2], f[3]);
+      ss += f[0] * f[0] + f[1] * f[1] + f[2] * f[2] + f[3] * f[3];
+      *(float4*)(xs + eq * RST + 4 * tq) = make_float4(f[0], f[1], f[2], f[3]);
     }
-    // stage g w for experts eq + 16 j
 #pragma unroll
     for (int j = 0; j < EJ; ++j) {
       const int e = eq + 16 * j;
@@ -73,40 +68,29 @@ __global__ __launch_bounds__(256) void route_kernel(const Tx* __restrict__ x, co
     __syncthreads();
 #pragma unroll 4
     for (int c = 0; c < RCH; c += 4) {
-      float4 xv[4], wv[EJ];
+      const float4 xv = *(const float4*)(xs + tq * RST + c);
 #pragma unroll
-      for (int i = 0; i < 4; ++i) xv[i] = *(const float4*)(xs + (tq + 16 * i) * RST + c);
-#pragma unroll
-      for (int j = 0; j < EJ; ++j) wv[j] = *(const float4*)(gw + (eq + 16 * j) * RST + c);
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int j = 0; j < EJ; ++j) {
-          float a = acc[i][j];
-          a = fmaf(xv[i].x, wv[j].x, a);
-          a = fmaf(xv[i].y, wv[j].y, a);
-          a = fmaf(xv[i].z, wv[j].z, a);
-          a = fmaf(xv[i].w, wv[j].w, a);
-          acc[i][j] = a;
-        }
+      for (int j = 0; j < EJ; ++j) {
+        const float4 wv = *(const float4*)(gw + (eq + 16 * j) * RST + c);
+        float a = acc[j];
+        a = fmaf(xv.x, wv.x, a);
+        a = fmaf(xv.y, wv.y, a);
+        a = fmaf(xv.z, wv.z, a);
+        a = fmaf(xv.w, wv.w, a);
+        acc[j] = a;
+      }
     }
     __syncthreads();
   }
-  // row sums of squares: the 16 lanes of a row group are consecutive
+  // row sums of squares of row eq: its 16 staging lanes are consecutive
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    float v = ss[i];
-#pragma unroll
-    for (int o = 8; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
-    if (tq == 0) rs[eq + 16 * i] = g ? 1.0f / sqrtf(v / (float)D + eps) : 1.0f;
-  }
+  for (int o = 8; o > 0; o >>= 1) ss += __shfl_xor(ss, o, 64);
+  if (tq == 0) rs[eq] = g ? 1.0f / sqrtf(ss / (float)D + eps) : 1.0f;
   if (tid < 64) cnt[tid] = 0;
   __syncthreads();
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
-#pragma unroll
-    for (int j = 0; j < EJ; ++j)
-      if (eq + 16 * j < E) lg[(tq + 16 * i) * 65 + eq + 16 * j] = acc[i][j] * rs[tq + 16 * i];
+  for (int j = 0; j < EJ; ++j)
+    if (eq + 16 * j < E) lg[tq * 65 + eq + 16 * j] = acc[j] * rs[tq];
   __syncthreads();
   // one wave per token: softmax, top-k, renormalised weights
   for (int r = wave; r < RT; r += 4) {
@@ -172,17 +156,20 @@ __global__ __launch_bounds__(256) void route_kernel(const Tx* __restrict__ x, co
 
 // One workgroup: per-expert totals and, for every router workgroup b, the first sorted position of
 // its assignments of expert e: off[b][e] = offsets[e] + sum_{b' < b} blkcnt[b'][e].  16 threads per
-// expert, each over a contiguous range of workgroups; then the grouped-GEMM tile table.
+// expert, each over a contiguous range of workgroups; then the grouped-GEMM tile table, each
+// expert's tiles written by its own thread.
 __global__ __launch_bounds__(1024) void moe_scan_kernel(const int* __restrict__ blkcnt, int nblk, int E, int bm,
                                                         int max_tiles, int* __restrict__ blkoff,
                                                         int* __restrict__ counts, int* __restrict__ offsets,
                                                         int* __restrict__ tiles) {
-  __shared__ int part[16][64], base[65];
+  __shared__ int part[16][64], base[65], tbase[65];
   const int tid = threadIdx.x, e = tid & 63, q = tid >> 6;
-  const int per = (nblk + 15) / 16, b0 = q * per, b1 = min(nblk, b0 + per);
+  const int per = (nblk + 15) / 16, b0 = min(nblk, q * per), b1 = min(nblk, b0 + per);
   int s = 0;
-  if (e < E)
+  if (e < E) {
+#pragma unroll 8
     for (int b = b0; b < b1; ++b) s += blkcnt[(int64_t)b * E + e];
+  }
   part[q][e] = s;
   __syncthreads();
   if (tid == 0) {
@@ -191,22 +178,27 @@ __global__ __launch_bounds__(1024) void moe_scan_kernel(const int* __restrict__ 
       int c = 0;
       for (int qq = 0; qq < 16; ++qq) c += part[qq][x];
       base[x] = o;
-      offsets[x] = o;
-      counts[x] = c;
-      for (int r = 0; r < c; r += bm) {
-        if (ts < max_tiles) {
-          tiles[3 * ts] = x;
-          tiles[3 * ts + 1] = o + r;
-          tiles[3 * ts + 2] = min(bm, c - r);
-        }
-        ++ts;
-      }
+      tbase[x] = ts;
       o += c;
+      ts += (c + bm - 1) / bm;
     }
-    offsets[E] = o;
-    for (int i = ts; i < max_tiles; ++i) tiles[3 * i] = -1;
+    base[E] = o;
+    tbase[E] = ts;
   }
   __syncthreads();
+  if (e < E && q == 0) {
+    const int c = base[e + 1] - base[e];
+    counts[e] = c;
+    offsets[e] = base[e];
+    if (e == E - 1) offsets[E] = base[E];
+    for (int r = 0, ts = tbase[e]; r < c; r += bm, ++ts)
+      if (ts < max_tiles) {
+        tiles[3 * ts] = e;
+        tiles[3 * ts + 1] = base[e] + r;
+        tiles[3 * ts + 2] = min(bm, c - r);
+      }
+  }
+  for (int i = tbase[E] + tid; i < max_tiles; i += 1024) tiles[3 * i] = -1;
   if (e < E) {
     int run = base[e];
     for (int qq = 0; qq < q; ++qq) run += part[qq][e];

@@ -25,7 +25,10 @@ def bf(x: np.ndarray) -> np.ndarray:
     return W.round_bf16(np.asarray(x, np.float32))
 
 
-def _attention_bf16(q, K, V, causal_offset=None):
+POINTS = ("u", "qkv", "qk", "p", "o", "u2", "z")   # the forward's bf16 rounding points
+
+
+def _attention_bf16(q, K, V, causal_offset=None, round_p=True, round_o=True):
     """Attention as the MFMA kernel computes it: q, K, V bf16; scores accumulated in fp32; the
     probabilities exp(s - rowmax) rounded to bf16 before the P.V product; the row sum taken over
     the rounded probabilities; output rounded to bf16.  causal_offset: query t sees keys
@@ -41,28 +44,34 @@ def _attention_bf16(q, K, V, causal_offset=None):
         s = (q[:, h] @ K[:, h // G].T) * sc
         if mask is not None:
             s = np.where(mask, s, -np.inf)
-        p = bf(np.exp(s - s.max(axis=1, keepdims=True)))
+        p = np.exp(s - s.max(axis=1, keepdims=True))
+        if round_p:
+            p = bf(p)
         out[:, h] = (p @ V[:, h // G]) / p.sum(axis=1, keepdims=True)
-    return bf(out)
+    return bf(out) if round_o else out
 
 
-def _proj(x, w, wts, site, scale):
+def _proj(x, w, wts, site, scale, round_t=True):
     """bf16 GEMM with the LoRA up-projection joined to its fp32 accumulators: the down-projection
     t = bf16(scale x A^T) is rounded once (the skinny kernel's bf16 output); returns fp32."""
     y = x @ w.T
     if f"lora_a_{site}" in wts:
-        t = bf(np.float32(scale) * (x @ wts[f"lora_a_{site}"].T))
+        t = np.float32(scale) * (x @ wts[f"lora_a_{site}"].T)
+        t = bf(t) if round_t else t
         y = y + t @ wts[f"lora_b_{site}"].T
     return y
 
 
 def gen_block_bf16(h: np.ndarray, wts: Dict[str, np.ndarray], dims, prefix_k: Sequence[np.ndarray],
-                   prefix_v: Sequence[np.ndarray], residual: str = "f32", causal: bool = False):
+                   prefix_v: Sequence[np.ndarray], residual: str = "f32", causal: bool = False,
+                   exact=()):
     """Model of the bf16 block (dense), in the order of ``oracle.gen_block``.
 
     residual: "f32" (the residual stream kept in fp32), "bf16_out" (the block output rounded
     once, the mid-block residual fp32), "bf16_both" (mid-block residual and output rounded).
-    causal: the prompt pass (no prefix, query t sees keys 0..t, positions from 0)."""
+    causal: the prompt pass (no prefix, query t sees keys 0..t, positions from 0).
+    exact: rounding points of POINTS left out (kept fp32), to measure what each one costs."""
+    r = {pt: (lambda x: x) if pt in exact else bf for pt in POINTS}
     B, N, D = h.shape
     Hq, Hkv, hd = dims.n_q_heads, dims.n_kv_heads, dims.head_dim
     eps, I = dims.rms_eps, dims.mlp_intermediate
@@ -73,26 +82,27 @@ def gen_block_bf16(h: np.ndarray, wts: Dict[str, np.ndarray], dims, prefix_k: Se
     for b in range(B):
         hb = h[b].astype(np.float32)
         P = 0 if causal else prefix_k[b].shape[0]
-        u = bf(O.rms_norm(hb, wts["g_in"], eps))
-        q_raw = bf(_proj(u, wq, wts, "q", sc)).reshape(N, Hq, hd)
-        k_raw = bf(_proj(u, wk, wts, "k", sc)).reshape(N, Hkv, hd)
-        v = bf(_proj(u, wv, wts, "v", sc)).reshape(N, Hkv, hd)
+        u = r["u"](O.rms_norm(hb, wts["g_in"], eps))
+        q_raw = r["qkv"](_proj(u, wq, wts, "q", sc)).reshape(N, Hq, hd)
+        k_raw = r["qkv"](_proj(u, wk, wts, "k", sc)).reshape(N, Hkv, hd)
+        v = r["qkv"](_proj(u, wv, wts, "v", sc)).reshape(N, Hkv, hd)
         c, s = O.rope_cos_sin(P + np.arange(N), hd, dims.rope_theta, np.float32)
-        q = bf(O.apply_rope(O.rms_norm(q_raw, wts["g_q"], eps), c, s))
-        k = bf(O.apply_rope(O.rms_norm(k_raw, wts["g_k"], eps), c, s))
+        q = r["qk"](O.apply_rope(O.rms_norm(q_raw, wts["g_q"], eps), c, s))
+        k = r["qk"](O.apply_rope(O.rms_norm(k_raw, wts["g_k"], eps), c, s))
+        rp, ro = "p" not in exact, "o" not in exact
         if causal:
-            o = _attention_bf16(q, k, v, causal_offset=0)
+            o = _attention_bf16(q, k, v, causal_offset=0, round_p=rp, round_o=ro)
         else:
             K = np.concatenate([prefix_k[b].astype(np.float32), k])
             V = np.concatenate([prefix_v[b].astype(np.float32), v])
-            o = _attention_bf16(q, K, V)
+            o = _attention_bf16(q, K, V, round_p=rp, round_o=ro)
         x = hb + _proj(o.reshape(N, qd), wts["w_o"], wts, "o", sc)
         if residual == "bf16_both":
             x = bf(x)
-        u2 = bf(O.rms_norm(x, wts["g_post"], eps))
+        u2 = r["u2"](O.rms_norm(x, wts["g_post"], eps))
         gate = _proj(u2, wts["w_gate_up"][:I], wts, "gate", sc)
         up = _proj(u2, wts["w_gate_up"][I:], wts, "up", sc)
-        z = bf(O.swiglu(gate, up))
+        z = r["z"](O.swiglu(gate, up))
         y = x + _proj(z, wts["w_down"], wts, "down", sc)
         outs.append(bf(y) if residual != "f32" else y)
     return np.stack(outs)
