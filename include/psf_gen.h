@@ -103,6 +103,20 @@ int gen_block_forward(const gen_block_dims* dims, const gen_block_weights* w, vo
                       const void* const* prefix_k, const void* const* prefix_v, const int* prefix_len,
                       int32_t* topk_idx_out, void* workspace, size_t workspace_bytes, void* stream);
 
+/* gen_block_forward for callers that cannot allocate (code under HIP graph capture, tight serving
+ * loops, harnesses that forbid hipMalloc): the same computation, with the workspace taken from a
+ * device array inside the library instead of an argument.  The array holds
+ * PSF_GEN_NOALLOC_SCRATCH_BYTES (128 MiB) on every GPU the library runs on, until the process
+ * ends; a call whose workspace (gen_workspace_size(dims, 1, B, N, max prefix_len)) exceeds it
+ * returns GEN_EWORKSPACE with nothing launched.  The call allocates nothing.  Every call on one GPU
+ * uses that GPU's single array: calls that overlap on one GPU (other streams, other threads)
+ * race and must be serialised by the caller.  Arguments and errors otherwise as
+ * gen_block_forward. */
+#define PSF_GEN_NOALLOC_SCRATCH_BYTES ((size_t)128 << 20)
+int gen_block_forward_noalloc(const gen_block_dims* dims, const gen_block_weights* w, void* hidden, int B, int N,
+                              const void* const* prefix_k, const void* const* prefix_v, const int* prefix_len,
+                              int32_t* topk_idx_out, void* stream);
+
 /* One denoise step of the gen tower for n_img images and n_br CFG branches
  * (two: 0 = cond, 1 = uncond; three, for image edits: 0 = cond, 1 = img_cond, 2 = uncond):
  *   h0  = patchify(x_t) W_in^T + temb(sigma)      (tokens in raster order of 32x32 patches,

@@ -20,7 +20,7 @@ GEN_F32, GEN_BF16 = 0, 1
 LORA_SITES = ("q", "k", "v", "o", "gate", "up", "down")
 
 # every symbol declared in include/psf_gen.h
-EXPORTS = ("gen_block_forward", "gen_tower_step", "flow_euler_cfg", "flow_euler_dual_cfg", "gen_moe_route",
+EXPORTS = ("gen_block_forward", "gen_block_forward_noalloc", "gen_tower_step", "flow_euler_cfg", "flow_euler_dual_cfg", "gen_moe_route",
            "gen_workspace_size",
            "gen_sigma_schedule", "gen_last_error", "gen_block_lora_merge", "gen_prefix_forward",
            "gen_backward_workspace_size", "gen_block_backward", "gen_train_workspace_size", "gen_tower_lora_train_step",
@@ -66,6 +66,7 @@ def _load():
     vp, i, f, sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_size_t
     P = ctypes.POINTER
     lib.gen_block_forward.argtypes = [P(BlockDimsC), P(BlockWeightsC), vp, i, i, P(vp), P(vp), P(i), vp, vp, sz, vp]
+    lib.gen_block_forward_noalloc.argtypes = [P(BlockDimsC), P(BlockWeightsC), vp, i, i, P(vp), P(vp), P(i), vp, vp]
     lib.gen_tower_step.argtypes = [P(BlockDimsC), i, P(BlockWeightsC), vp, vp, vp, vp, vp, vp, i, i, i, i,
                                    P(f), P(f), f, f, i, f, P(vp), P(vp), P(i), vp, vp, vp, sz, vp]
     lib.flow_euler_cfg.argtypes = [vp, vp, vp, sz, f, f, f, f, vp]
@@ -93,7 +94,7 @@ def _load():
     lib.gen_op_workspace_size.restype = sz
     lib.gen_timing_begin.argtypes = [i, i]
     lib.gen_timing_end.argtypes = [P(ctypes.c_double), P(i)]
-    for n in ("gen_block_forward", "gen_tower_step", "flow_euler_cfg", "gen_moe_route", "gen_sigma_schedule",
+    for n in ("gen_block_forward", "gen_block_forward_noalloc", "gen_tower_step", "flow_euler_cfg", "gen_moe_route", "gen_sigma_schedule",
               "gen_op_rmsnorm", "gen_op_linear", "gen_op_qknorm_rope", "gen_op_attention",
               "gen_timing_begin", "gen_timing_end"):
         getattr(lib, n).restype = i
@@ -176,6 +177,20 @@ def block_forward(dims: BlockDimsC, weights: BlockWeightsC, hidden, prefix_k, pr
     _check(lib.gen_block_forward(ctypes.byref(dims), ctypes.byref(weights), hidden.data_ptr(), B, N,
                                  _ptr_array(prefix_k), _ptr_array(prefix_v), plen, _ptr(topk_out),
                                  workspace.data_ptr(), workspace.numel() * workspace.element_size(), _stream(stream)))
+
+
+def block_forward_noalloc(dims: BlockDimsC, weights: BlockWeightsC, hidden, prefix_k, prefix_v, prefix_len,
+                          topk_out=None, stream=None):
+    """gen_block_forward without a workspace argument: the library's own per-GPU scratch array
+    (NOALLOC_SCRATCH_BYTES) serves instead; nothing is allocated."""
+    B, N = hidden.shape[0], hidden.shape[1]
+    plen = (ctypes.c_int * B)(*prefix_len)
+    _check(lib.gen_block_forward_noalloc(ctypes.byref(dims), ctypes.byref(weights), hidden.data_ptr(), B, N,
+                                         _ptr_array(prefix_k), _ptr_array(prefix_v), plen, _ptr(topk_out),
+                                         _stream(stream)))
+
+
+NOALLOC_SCRATCH_BYTES = 128 << 20
 
 
 def prefix_forward(dims: BlockDimsC, layers: Sequence[BlockWeightsC], hidden, k_cache, v_cache, workspace,

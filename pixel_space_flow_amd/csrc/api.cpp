@@ -13,6 +13,23 @@
 #include "gemm.h"
 #include "kernels.h"
 
+#include <mutex>
+
+// Scratch of gen_block_forward_noalloc (for callers that cannot allocate): a file-scope device
+// array, one copy on every GPU the library runs on, held until the process ends.  Host code
+// never passes its name to a kernel or a copy: the array's device address is looked up once per
+// device (hipGetSymbolAddress, that device current) and only that address is used.
+static __device__ __align__(256) char scratch[PSF_GEN_NOALLOC_SCRATCH_BYTES];
+
+namespace {
+constexpr int MAX_DEVICES = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[MAX_DEVICES] = {};
+}  // namespace
+
+// The current device's address of `scratch` (looked up on the first call on that device).
+static int noalloc_scratch(void** out);
+
 using namespace psf;
 
 namespace {
@@ -950,6 +967,59 @@ int check_grads(const gen_block_dims* d, const gen_block_weights* w, const gen_l
 
 }  // namespace
 
+int noalloc_scratch(void** out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return fail(GEN_EHIP, "hipGetDevice: %s", hipGetErrorString(e));
+  if (dev < 0 || dev >= MAX_DEVICES) return fail(GEN_EUNSUPPORTED, "device %d >= %d", dev, MAX_DEVICES);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || !p) return fail(GEN_EHIP, "hipGetSymbolAddress(scratch): %s", hipGetErrorString(e));
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return GEN_OK;
+}
+
+namespace {
+
+// gen_block_forward over a caller workspace, or (noalloc) over this GPU's copy of `scratch`.
+int block_forward_ws(const gen_block_dims* dims, const gen_block_weights* w, void* hidden, int B, int N,
+                     const void* const* prefix_k, const void* const* prefix_v, const int* prefix_len,
+                     int32_t* topk_idx_out, void* workspace, size_t workspace_bytes, void* stream, bool noalloc) {
+  int rc = check_dims(dims);
+  if (rc) return rc;
+  if ((rc = check_weights(dims, w, 0))) return rc;
+  if (!hidden || !aligned16(hidden)) return fail(GEN_EINVAL, "hidden is NULL or not 16-byte aligned");
+  if (B < 1 || N < 1) return fail(GEN_EINVAL, "B=%d and N=%d must be >= 1", B, N);
+  if (B > MAXB) return fail(GEN_EUNSUPPORTED, "B=%d > %d sequences per call", B, MAXB);
+  int maxp = 0;
+  if ((rc = check_prefix(dims, B, prefix_k, prefix_v, prefix_len, &maxp))) return rc;
+  const SeqInfo si = make_seq(B, N, prefix_k, prefix_v, prefix_len);
+  if ((rc = check_prefix_ptrs(si, 0))) return rc;
+  if (!workspace || !aligned16(workspace)) return fail(GEN_EINVAL, "workspace is NULL or not 16-byte aligned");
+  const Ws L = layout(*dims, 1, B, N, maxp);
+  if (workspace_bytes < L.total) {
+    if (noalloc)
+      return fail(GEN_EWORKSPACE, "this call needs %zu bytes of scratch; the allocation-free entry point holds %zu "
+                  "(use gen_block_forward with a workspace)", L.total, workspace_bytes);
+    return fail(GEN_EWORKSPACE, "workspace %zu bytes < %zu required", workspace_bytes, L.total);
+  }
+  hipStream_t s = (hipStream_t)stream;
+  HIP_TRY(rope_table(at<float2>(workspace, L.rope), L.n_pos, dims->head_dim, dims->rope_theta, s));
+  if (dims->dtype == GEN_BF16 && dims->hidden_dtype == GEN_F32)
+    rc = run_block<bf16, float>(*dims, *w, (float*)hidden, si, workspace, L, topk_idx_out, s);
+  else if (dims->dtype == GEN_BF16)
+    rc = run_block<bf16, bf16>(*dims, *w, (bf16*)hidden, si, workspace, L, topk_idx_out, s);
+  else
+    rc = run_block<float, float>(*dims, *w, (float*)hidden, si, workspace, L, topk_idx_out, s);
+  return rc ? rc : ok();
+}
+
+}  // namespace
+
 // ==================================================================== exported
 extern "C" {
 
@@ -1025,29 +1095,18 @@ int gen_moe_route(const void* u, const void* w_router, int T, int D, int E, int 
 int gen_block_forward(const gen_block_dims* dims, const gen_block_weights* w, void* hidden, int B, int N,
                       const void* const* prefix_k, const void* const* prefix_v, const int* prefix_len,
                       int32_t* topk_idx_out, void* workspace, size_t workspace_bytes, void* stream) {
-  int rc = check_dims(dims);
+  return block_forward_ws(dims, w, hidden, B, N, prefix_k, prefix_v, prefix_len, topk_idx_out, workspace,
+                          workspace_bytes, stream, false);
+}
+
+int gen_block_forward_noalloc(const gen_block_dims* dims, const gen_block_weights* w, void* hidden, int B, int N,
+                              const void* const* prefix_k, const void* const* prefix_v, const int* prefix_len,
+                              int32_t* topk_idx_out, void* stream) {
+  void* ptr = nullptr;
+  const int rc = noalloc_scratch(&ptr);
   if (rc) return rc;
-  if ((rc = check_weights(dims, w, 0))) return rc;
-  if (!hidden || !aligned16(hidden)) return fail(GEN_EINVAL, "hidden is NULL or not 16-byte aligned");
-  if (B < 1 || N < 1) return fail(GEN_EINVAL, "B=%d and N=%d must be >= 1", B, N);
-  if (B > MAXB) return fail(GEN_EUNSUPPORTED, "B=%d > %d sequences per call", B, MAXB);
-  int maxp = 0;
-  if ((rc = check_prefix(dims, B, prefix_k, prefix_v, prefix_len, &maxp))) return rc;
-  const SeqInfo si = make_seq(B, N, prefix_k, prefix_v, prefix_len);
-  if ((rc = check_prefix_ptrs(si, 0))) return rc;
-  if (!workspace || !aligned16(workspace)) return fail(GEN_EINVAL, "workspace is NULL or not 16-byte aligned");
-  const Ws L = layout(*dims, 1, B, N, maxp);
-  if (workspace_bytes < L.total)
-    return fail(GEN_EWORKSPACE, "workspace %zu bytes < %zu required", workspace_bytes, L.total);
-  hipStream_t s = (hipStream_t)stream;
-  HIP_TRY(rope_table(at<float2>(workspace, L.rope), L.n_pos, dims->head_dim, dims->rope_theta, s));
-  if (dims->dtype == GEN_BF16 && dims->hidden_dtype == GEN_F32)
-    rc = run_block<bf16, float>(*dims, *w, (float*)hidden, si, workspace, L, topk_idx_out, s);
-  else if (dims->dtype == GEN_BF16)
-    rc = run_block<bf16, bf16>(*dims, *w, (bf16*)hidden, si, workspace, L, topk_idx_out, s);
-  else
-    rc = run_block<float, float>(*dims, *w, (float*)hidden, si, workspace, L, topk_idx_out, s);
-  return rc ? rc : ok();
+  return block_forward_ws(dims, w, hidden, B, N, prefix_k, prefix_v, prefix_len, topk_idx_out, ptr,
+                          PSF_GEN_NOALLOC_SCRATCH_BYTES, stream, true);
 }
 
 int gen_prefix_forward(const gen_block_dims* dims, int n_layers, const gen_block_weights* layers, void* hidden,
