@@ -160,6 +160,14 @@ int check_prefix(const gen_block_dims* d, int B, const void* const* pk, const vo
 constexpr size_t ALIGN = 256;
 size_t up(size_t x) { return (x + ALIGN - 1) / ALIGN * ALIGN; }
 
+// Row pitch (elements) of the SwiGLU output z, the down projection's A operand.  GEMM operand rows
+// whose pitch is an odd multiple of 8 KiB above 8 KiB (24 KiB at I = 12288 in bf16) load measurably
+// slower than rows 128 bytes longer, so such rows get 64 elements of padding.
+int z_pitch(int I, size_t es) {
+  const size_t b = (size_t)I * es;
+  return (b > 8192 && b % 8192 == 0 && (b / 8192) % 2 == 1) ? I + (int)(128 / es) : I;
+}
+
 struct Ws {
   size_t hidden, patches, u, qkv, attn, kc, vt, z, rope, temb, h1, x0, lora_t, hmid, skinny, lora_gu, lora_f32;
   size_t splitk, splitk_floats;
@@ -185,7 +193,7 @@ Ws layout(const gen_block_dims& d, int n_img, int n_br, int N, int max_prefix) {
   w.attn = take(M * d.n_q_heads * d.head_dim * es);
   w.kc = take(B * d.n_kv_heads * w.Lpad * d.head_dim * es);
   w.vt = take(B * d.n_kv_heads * w.Lpad * d.head_dim * es);
-  w.z = take(d.mlp_intermediate > 0 ? M * d.mlp_intermediate * es : 0);
+  w.z = take(d.mlp_intermediate > 0 ? M * (size_t)z_pitch(d.mlp_intermediate, es) * es : 0);
   w.rope = take((size_t)w.n_pos * (d.head_dim / 2) * sizeof(float) * 2);
   w.temb = take((size_t)n_img * D * 4);
   w.h1 = take((size_t)n_img * D * 4);
@@ -237,7 +245,7 @@ hipError_t gemm_any(const GemmParams& p, int epi, hipStream_t s) {
 // Returns the number of sites present; fills per-site column offsets (-1 if absent).
 template <typename T>
 hipError_t lora_down(const gen_block_dims& d, const gen_block_weights& w, const int* sites, int ns, const T* x, int K,
-                     int M, T* t, int* off, int& ldt, hipStream_t s, float* part = nullptr) {
+                     int M, T* t, int* off, int& ldt, hipStream_t s, float* part = nullptr, int ldx = 0) {
   GemmParams p = gp();
   int n = 0;
   for (int i = 0; i < ns; ++i) {
@@ -246,7 +254,7 @@ hipError_t lora_down(const gen_block_dims& d, const gen_block_weights& w, const 
   }
   ldt = std::max(n, 1) * d.lora_rank;
   if (n == 0) return hipSuccess;
-  p.A = x; p.lda = K; p.B = p.Bs[0]; p.ldb = K;
+  p.A = x; p.lda = ldx ? ldx : K; p.B = p.Bs[0]; p.ldb = K;
   p.M = M; p.N = n * d.lora_rank; p.K = K;
   p.bmode = 2; p.seg_rows = d.lora_rank;
   p.C = t; p.ldc = ldt; p.scale = d.lora_alpha / (float)d.lora_rank;
@@ -412,11 +420,12 @@ int run_block(const gen_block_dims& d, const gen_block_weights& w, TH* hidden, c
   HIP_TRY((rmsnorm<float, T>(hmid, (const T*)w.g_post, u, M, D, d.rms_eps, s)));
   if (d.mlp_intermediate > 0) {
     const int I = d.mlp_intermediate;
+    const int LZ = z_pitch(I, sizeof(T));
     T* z = at<T>(ws, L.z);
     {
       GemmParams p = gp();
       p.A = u; p.lda = D; p.B = w.w_gate_up; p.ldb = D; p.M = M; p.N = 2 * I; p.K = D;
-      p.bmode = 1; p.swiglu_I = I; p.C = z; p.ldc = I;
+      p.bmode = 1; p.swiglu_I = I; p.C = z; p.ldc = LZ;
       if (lora) {
         const int sites[2] = {4, 5}, ends[2] = {I, 2 * I};
         int off[2], ldt;
@@ -435,7 +444,7 @@ int run_block(const gen_block_dims& d, const gen_block_weights& w, TH* hidden, c
     }
     {
       GemmParams p = gp();
-      p.A = z; p.lda = I; p.B = w.w_down; p.ldb = I; p.M = M; p.N = D; p.K = I;
+      p.A = z; p.lda = LZ; p.B = w.w_down; p.ldb = I; p.M = M; p.N = D; p.K = I;
       p.C = hidden; p.ldc = D; p.R = hmid; p.ldr = D;
       p.part = L.splitk_floats ? at<float>(ws, L.splitk) : nullptr; p.part_floats = L.splitk_floats;
       const int sites[1] = {6}, ends[1] = {D};
@@ -443,7 +452,7 @@ int run_block(const gen_block_dims& d, const gen_block_weights& w, TH* hidden, c
       bool post = false;
       const int epi = f32res ? EPI_RESID_F32 : EPI_RESID_FROM_F32;
       if (lora) {
-        HIP_TRY(lora_down<T>(d, w, sites, 1, z, I, M, lt, off, ldt, s, at<float>(ws, L.skinny)));
+        HIP_TRY(lora_down<T>(d, w, sites, 1, z, I, M, lt, off, ldt, s, at<float>(ws, L.skinny), LZ));
         // the K extension of the ring kernel where it applies; otherwise with an fp32 residual the
         // LoRA term is added after the base GEMM, and a bf16 residual keeps the K extension of the
         // register-staged kernel so that the block output is rounded once

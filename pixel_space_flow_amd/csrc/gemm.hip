@@ -552,7 +552,10 @@ __global__ __launch_bounds__(64 * NW, 1) void gemm_fast_kernel(GemmParams p, int
   if (KT > 1) issue(1, 1);
   rd_a(fal, 0, 0, 0);
   rd_b(0, 0);
-  for (int kt = 0; kt < KT; ++kt) {
+  // every k-tile but the last: the body has no branches (the DMA of the tile two ahead reloads
+  // the last tile into the free stage when it runs past the end)
+  int kt = 0;
+  for (; kt + 1 < KT; ++kt) {
     const int st = kt & 1;
     // half-step 0: rows 0-63 of k 0-31
     __builtin_amdgcn_s_setprio(2);
@@ -575,22 +578,32 @@ __global__ __launch_bounds__(64 * NW, 1) void gemm_fast_kernel(GemmParams p, int
     __builtin_amdgcn_sched_barrier(0);
     // half-step 3: rows 64-127 of k 32-63
     __builtin_amdgcn_s_setprio(3);
-    if (kt + 1 < KT) {
-      __builtin_amdgcn_s_waitcnt(0);
-      __syncthreads();
-      if (kt + 2 < KT) issue(kt + 2, st);
-      rd_a(fal, st ^ 1, 0, 0);
-    }
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+    issue(min(kt + 2, KT - 1), st);
+    rd_a(fal, st ^ 1, 0, 0);
     mma(fah, 1);
     interleave(4);
     __builtin_amdgcn_sched_barrier(0);
-    if (kt + 1 < KT) rd_b(st ^ 1, 0);
+    rd_b(st ^ 1, 0);
+  }
+  {
+    const int st = kt & 1;
+    rd_a(fah, st, 0, 1);
+    mma(fal, 0);
+    rd_a(fal, st, 1, 0);
+    mma(fah, 1);
+    rd_b(st, 1);
+    rd_a(fah, st, 1, 1);
+    mma(fal, 0);
+    mma(fah, 1);
   }
   __builtin_amdgcn_s_setprio(0);
 
   // ---- epilogue through LDS: each wave stages one 32x32 fp32 block at a time, then every lane
   // owns 16 consecutive columns of one row (lanes 2r, 2r+1 cover row r), so global accesses are
   // 16-byte vectors and the per-row index math runs once per block.
+  __builtin_amdgcn_s_waitcnt(0);   // a trailing reload of the last tile has landed
   __syncthreads();   // every wave is done with the LDS stages
   constexpr int TS = 36;                                   // padded fp32 row stride of a staged block
   float* T0 = (float*)smem + wave * (2 * 32 * TS);

@@ -14,16 +14,34 @@ namespace {
 // Router over a tile of RT tokens per workgroup.  With a gain g the logits are those of the
 // RMS-normalised row, computed in one pass over x in fp32:
 //   logit[t, e] = rs_t sum_c x[t, c] (g[c] w[e, c]),  rs_t = 1 / sqrt(mean_c x[t, c]^2 + eps)
-// (g == nullptr: logit = sum_c x[t, c] w[e, c], x already normalised).  64-column chunks of x
-// and of g w are staged in LDS as fp32; thread (t, eq) accumulates token t = tid % 16 against
-// experts eq + 16 j (eq = tid / 16, j < EJ).  Then one wave per token: softmax, top-k by
-// repeated wave argmax of the logit (the softmax is monotone; ties to the lower expert index),
-// weights renormalised over the k, and each assignment's stable rank among the workgroup's
-// assignments of the same expert (assignment order t k + slot) with the workgroup's per-expert
-// counts, so that the sort needs no second pass over the assignments.
+// (g == nullptr: logit = sum_c x[t, c] w[e, c], x already normalised).  256-column chunks of x
+// and of g w are staged in LDS as fp32, the next chunk's values loaded into registers while the
+// current one is consumed; thread (t, eq) accumulates token t = tid % 16 against experts
+// eq + 16 j (eq = tid / 16, j < EJ).  Then one wave per token: softmax, top-k by repeated wave
+// argmax of the logit (the softmax is monotone; ties to the lower expert index), weights
+// renormalised over the k, and each assignment's stable rank among the workgroup's assignments
+// of the same expert (assignment order t k + slot) with the workgroup's per-expert counts, so
+// that the sort needs no second pass over the assignments.
 constexpr int RT = 16;          // tokens per router workgroup
-constexpr int RCH = 64;         // columns per staged chunk
-constexpr int RST = RCH + 4;    // padded fp32 row stride (272 B: 16 consecutive rows hit 16 distinct 16-byte slots)
+constexpr int RCH = 256;        // columns per staged chunk
+constexpr int RST = RCH + 4;    // padded fp32 row stride (1040 B: 16 consecutive rows hit 16 distinct 16-byte slots)
+
+// 16 consecutive elements (16-byte aligned) as floats
+DEVI void load16(const float* p, float* f) {
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const float4 v = *(const float4*)(p + 4 * q);
+    f[4 * q] = v.x; f[4 * q + 1] = v.y; f[4 * q + 2] = v.z; f[4 * q + 3] = v.w;
+  }
+}
+DEVI void load16(const bf16* p, float* f) {
+#pragma unroll
+  for (int q = 0; q < 2; ++q) {
+    const bf16x8 v = *(const bf16x8*)(p + 8 * q);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) f[8 * q + e] = static_cast<float>(v[e]);
+  }
+}
 
 template <typename Tx, typename Tw, int EJ>
 __global__ __launch_bounds__(256) void route_kernel(const Tx* __restrict__ x, const Tw* __restrict__ g, float eps,
@@ -43,30 +61,46 @@ __global__ __launch_bounds__(256) void route_kernel(const Tx* __restrict__ x, co
 #pragma unroll
   for (int j = 0; j < EJ; ++j) acc[j] = 0.f;
   float ss = 0.f;
-  // staging roles: x row eq (16 rows x 16 chunks of 4 columns); g w rows eq + 16 j
-  const int xr = min(t0 + eq, T_ - 1);
-  for (int c0 = 0; c0 < D; c0 += RCH) {
-    {
-      const Tx* src = x + (int64_t)xr * D + c0 + 4 * tq;
-      float f[4];
+  // staging roles: x row eq and g w rows eq + 16 j, columns 16 tq .. 16 tq + 15 of each chunk
+  const Tx* xrow = x + (int64_t)min(t0 + eq, T_ - 1) * D + 16 * tq;
+  float xn[16], wn[EJ][16], gn[16];
+  // a thread's 16 columns lie wholly inside or wholly past D (D is a multiple of 16); past it
+  // they stage as zeros
+  auto fetch = [&](int c0) {
+    const bool in = c0 + 16 * tq < D;
+    if (in) load16(xrow + c0, xn);
+    else
 #pragma unroll
-      for (int e = 0; e < 4; ++e) f[e] = to_f(src[e]);
-      ss += f[0] * f[0] + f[1] * f[1] + f[2] * f[2] + f[3] * f[3];
-      *(float4*)(xs + eq * RST + 4 * tq) = make_float4(f[0], f[1], f[2], f[3]);
-    }
+      for (int q = 0; q < 16; ++q) xn[q] = 0.f;
+    if (g && in) load16(g + c0 + 16 * tq, gn);
 #pragma unroll
     for (int j = 0; j < EJ; ++j) {
       const int e = eq + 16 * j;
-      float f[4] = {0.f, 0.f, 0.f, 0.f};
-      if (e < E) {
-        const Tw* src = wr + (int64_t)e * D + c0 + 4 * tq;
+      if (e < E && in) load16(wr + (int64_t)e * D + c0 + 16 * tq, wn[j]);
+      else
 #pragma unroll
-        for (int q = 0; q < 4; ++q) f[q] = g ? to_f(g[c0 + 4 * tq + q]) * to_f(src[q]) : to_f(src[q]);
-      }
-      *(float4*)(gw + e * RST + 4 * tq) = make_float4(f[0], f[1], f[2], f[3]);
+        for (int q = 0; q < 16; ++q) wn[j][q] = 0.f;
+    }
+  };
+  fetch(0);
+  for (int c0 = 0; c0 < D; c0 += RCH) {
+#pragma unroll
+    for (int q = 0; q < 16; ++q) ss += xn[q] * xn[q];
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+      *(float4*)(xs + eq * RST + 16 * tq + 4 * q) = make_float4(xn[4 * q], xn[4 * q + 1], xn[4 * q + 2], xn[4 * q + 3]);
+#pragma unroll
+    for (int j = 0; j < EJ; ++j) {
+      float f[16];
+#pragma unroll
+      for (int q = 0; q < 16; ++q) f[q] = g ? gn[q] * wn[j][q] : wn[j][q];
+#pragma unroll
+      for (int q = 0; q < 4; ++q)
+        *(float4*)(gw + (eq + 16 * j) * RST + 16 * tq + 4 * q) = make_float4(f[4 * q], f[4 * q + 1], f[4 * q + 2], f[4 * q + 3]);
     }
     __syncthreads();
-#pragma unroll 4
+    if (c0 + RCH < D) fetch(c0 + RCH);      // the next chunk's loads run under this chunk's FMAs
+#pragma unroll 8
     for (int c = 0; c < RCH; c += 4) {
       const float4 xv = *(const float4*)(xs + tq * RST + c);
 #pragma unroll
