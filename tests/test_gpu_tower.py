@@ -102,19 +102,47 @@ def guided(x0s, w):
     return O.cfg_mix(x0s[0], x0s[1] if w.n_br == 2 else None, w.cfg_scale)
 
 
+def cfg_amplification(ref_br, w):
+    """How much the guidance mix magnifies independent errors of the branch predictions:
+    |sum_b c_b e_b| / |x0g| for errors e_b of equal size |x0_b| eps and no correlation, relative to
+    eps, i.e. sqrt(sum_b c_b^2 |x0_b|^2) / |x0g| with c_b the mix coefficients (cfg s on two
+    branches: s and 1 - s)."""
+    if w.n_br == 3:
+        s, si = w.cfg_scale, w.img_cfg_scale
+        coef = (s, si - s, 1.0 - si)            # cond, img_cond, uncond
+    elif w.n_br == 2:
+        coef = (w.cfg_scale, 1.0 - w.cfg_scale)
+    else:
+        coef = (1.0,)
+    g = guided(ref_br, w)
+    num = np.sqrt(sum(c * c * np.sum(np.asarray(r, np.float64) ** 2) for c, r in zip(coef, ref_br)))
+    return float(num / np.linalg.norm(np.asarray(g, np.float64)))
+
+
 def sampled_tower_check(lib, w, x, sigma, sigma_next, n_rows, seed_tag):
     """One GPU tower step against the oracle on sampled tokens (the last block and the head run
-    on those tokens only; every earlier block on all of them): each branch's x0, the guided x0
-    and the Euler update dx = x_next - x_t, all at cosine >= 0.999."""
+    on those tokens only; every earlier block on all of them).
+
+    Each branch's x0 must meet the tower bar, cosine >= 0.999.  The guided x0 and the Euler update
+    dx = x_next - x_t are checked against that bar carried through the guidance mix: with branch
+    errors of relative size eps the mix of scale s leaves an error of about A eps on the guided
+    prediction (A = cfg_amplification, 4.8 at the 2048^2 CFG workload), i.e. 1 - cos grows by A^2,
+    and dx = (sigma' - sigma)/sigma (x_t - x0g) carries the guided error scaled by
+    |x0g| / |x_t - x0g|.  So: 1 - cos(guided) <= A^2 (1 - 0.999), and, as a consistency check, no
+    more than 1.5 A^2 times the branches' own 1 - cos; likewise for dx with A |x0g| / |x_t - x0g|.
+    (The rounding model of the bf16 path reproduces the measured guided and dx cosines at the full
+    workload, see tests/precision_full_tower.py.)"""
     t = GpuTower(lib, w, "bf16")
     xn, x0 = t.step(x, sigma, sigma_next, w.cfg_scale, w.img_cfg_scale)
     rows = np.sort(W.rng(w.config_id, 0, seed_tag).choice(w.n_tokens, n_rows, replace=False))
     ref = t.oracle_tokens(x, sigma, rows=rows)
     got = O.patchify(x0)[:, rows]
+    br_gap = []
     for b in range(w.batch):
         c, e = cosine(got[b], ref[b]), rel_max_err(got[b], ref[b])
         log(f"  branch {b}: cos {c:.6f}, max|err|/RMS {e:.3e}")
         assert c >= TOWER_COS
+        br_gap.append(1.0 - c)
     xt = O.patchify(x)[:, rows]
     xnt = O.patchify(xn)[:, rows]
     for i in range(w.n_img):
@@ -122,8 +150,13 @@ def sampled_tower_check(lib, w, x, sigma, sigma_next, n_rows, seed_tag):
         g_got, g_ref = guided(got[br], w), guided(ref[br], w)
         dx_ref = O.euler_step(xt[i], g_ref, sigma[i], sigma_next[i], w.t_eps) - xt[i]
         cg, cd = cosine(g_got, g_ref), cosine(xnt[i] - xt[i], dx_ref)
-        log(f"  image {i}: guided x0 cos {cg:.6f} (max|err|/RMS {rel_max_err(g_got, g_ref):.3e}), dx cos {cd:.6f}")
-        assert cg >= TOWER_COS and cd >= TOWER_COS
+        A = cfg_amplification(ref[br], w)
+        Ad = A * np.linalg.norm(g_ref) / np.linalg.norm(xt[i].astype(np.float64) - g_ref)
+        eb = max(br_gap[br])
+        log(f"  image {i}: guided x0 cos {cg:.6f} (bar {1 - A * A * (1 - TOWER_COS):.6f}, amplification {A:.2f}), "
+            f"dx cos {cd:.6f} (bar {1 - Ad * Ad * (1 - TOWER_COS):.6f})")
+        assert 1.0 - cg <= A * A * (1.0 - TOWER_COS) and 1.0 - cg <= 1.5 * A * A * eb + 1e-7
+        assert 1.0 - cd <= Ad * Ad * (1.0 - TOWER_COS) and 1.0 - cd <= 1.5 * Ad * Ad * eb + 1e-7
     return xn, x0, got, ref
 
 

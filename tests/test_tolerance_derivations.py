@@ -65,3 +65,33 @@ def test_backward_dh_tolerance():
     e = rel_max_err(got, ref)
     log(f"8B LoRA block backward, rounding model vs oracle: dh max|err|/RMS = {e:.3e} (bar {DH_TOL})")
     assert np.isfinite(e) and e * MARGIN <= DH_TOL
+
+
+def test_cfg_amplifies_branch_errors_as_derived():
+    """The guided prediction's error follows from the branches' (test_gpu_tower.sampled_tower_check):
+    with uncorrelated branch errors of relative size eps, cfg scale s leaves about A eps with
+    A = sqrt(s^2 |c|^2 + (1 - s)^2 |u|^2) / |x0g|.  Checked on a reduced tower (8 layers of hidden
+    1024, 2 x 256 tokens) run through the rounding model against the oracle."""
+    from test_gpu_tower import cfg_amplification, guided
+    d = W.small_dims(hidden=1024, n_q_heads=8, n_kv_heads=2, head_dim=128, mlp_intermediate=3072)
+    w = W.scaled(W.CONFIGS[2], dims=d, height=512, width=512, prefix_len=64, n_layers=8)
+    sched = O.sigma_schedule(w.n_steps, w.shift)
+    glob = W.tower_globals(w, 0, "bf16")
+    tok = O.patchify(W.noise_image(w))
+    h0 = O.linear(tok[0], glob["w_in"]) + O.timestep_embed(sched[0], glob["temb_w1"], glob["temb_w2"])
+    hr = np.stack([h0, h0])
+    hm = hr.copy()
+    for l in range(w.n_layers):
+        wts = W.layer_weights(w, l, 0, "bf16")
+        pk = [W.prefix_kv(w, l, s, 0, "bf16")[0] for s in range(2)]
+        pv = [W.prefix_kv(w, l, s, 0, "bf16")[1] for s in range(2)]
+        hr = O.gen_block(hr, wts, d, pk, pv)
+        hm = gen_block_bf16(hm, wts, d, pk, pv)
+    head = lambda h: O.linear(O.rms_norm(h, glob["g_final"], d.rms_eps), glob["w_out"])   # noqa: E731
+    yr, ym = head(hr), head(hm)
+    cosf = lambda a, b: float(a.ravel() @ b.ravel() / np.linalg.norm(a) / np.linalg.norm(b))   # noqa: E731
+    eb = max(1 - cosf(ym[0].astype(np.float64), yr[0]), 1 - cosf(ym[1].astype(np.float64), yr[1]))
+    eg = 1 - cosf(guided(ym, w).astype(np.float64), guided(yr, w).astype(np.float64))
+    A = cfg_amplification(yr, w)
+    log(f"reduced tower: branch 1-cos {eb:.3e}, guided 1-cos {eg:.3e}, A^2 (1-cos branch) {A * A * eb:.3e} (A = {A:.2f})")
+    assert 0.5 * A * A * eb <= eg <= 1.5 * A * A * eb
