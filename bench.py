@@ -88,6 +88,19 @@ def step_flops(w) -> dict:
     return out
 
 
+def down_pitch(I: int) -> int:
+    """Row pitch (elements) the benches give w_down: dense unless a dense bf16 row is a multiple of
+    8 KiB (I = 12288), then I + 64, the layout the library streams fastest (gen_block_weights
+    ld_down)."""
+    return I + 64 if (2 * I) % 8192 == 0 else I
+
+
+def down_weight(randn, D: int, I: int, std: float):
+    """w_down [D, I] as a view of a [D, down_pitch(I)] allocation, and its pitch."""
+    ld = down_pitch(I)
+    return randn(D, ld, std=std)[:, :I], ld
+
+
 def make_device_tower(psf, w, seed=0):
     """Random-init tower weights and prefixes on the GPU (torch's seeded device RNG)."""
     import torch
@@ -108,7 +121,8 @@ def make_device_tower(psf, w, seed=0):
         lw = {"g_in": randn(D, std=0.1, mean=1.0), "w_qkv": randn(QKV, D, std=0.02),
               "g_q": randn(d.head_dim, std=0.1, mean=1.0), "g_k": randn(d.head_dim, std=0.1, mean=1.0),
               "w_o": randn(D, d.n_q_heads * d.head_dim, std=0.02), "g_post": randn(D, std=0.1, mean=1.0),
-              "w_gate_up": randn(2 * I, D, std=0.02), "w_down": randn(D, I, std=0.02)}
+              "w_gate_up": randn(2 * I, D, std=0.02)}
+        lw["w_down"], lw["ld_down"] = down_weight(randn, D, I, 0.02)
         layers_dev.append(lw)
     glob = {"w_in": randn(D, 3072, std=0.02), "temb_w1": randn(D, 256, std=0.02), "temb_w2": randn(D, D, std=0.02),
             "g_final": randn(D, std=0.1, mean=1.0), "w_out": randn(3072, D, std=0.02)}
@@ -440,7 +454,8 @@ def cpu_baseline(w, seed=0):
 
 def run_kernel_only(psf, w, which: str, reps: int):
     """One kernel family of the step at the workload's shapes, `reps` launches (rocprofv3 counter
-    runs): the gate/up + SwiGLU GEMM, the down and O projections onto an fp32 residual, the QKV
+    runs): the gate/up + SwiGLU GEMM, the down (rows at the tower's w_down pitch) and O
+    projections onto an fp32 residual, the QKV
     GEMM, the attention; "copy" is a plain 256 MiB device copy used to calibrate the byte
     counters."""
     import torch
@@ -453,8 +468,13 @@ def run_kernel_only(psf, w, which: str, reps: int):
         QD = d.n_q_heads * d.head_dim
         K, N, epi, ydt = {"gate_up": (D, I, 2, bf), "down": (I, D, 3, torch.float32), "o": (QD, D, 3, torch.float32),
                           "qkv": (D, d.qkv_out, 0, bf)}[which]
-        x = torch.randn(M, K, device="cuda", generator=g).to(bf)
-        wt = (0.02 * torch.randn(2 * N if epi == 2 else N, K, device="cuda", generator=g)).to(bf)
+        # the down projection with both operands' rows at the tower's padded pitch: the op takes
+        # dense rows, so the pad columns are computed as zeros (0.5 % more FLOPs at I = 12288)
+        Kp = down_pitch(K) if which == "down" else K
+        x = torch.zeros(M, Kp, device="cuda", dtype=bf)
+        x[:, :K] = torch.randn(M, K, device="cuda", generator=g).to(bf)
+        wt = torch.zeros(2 * N if epi == 2 else N, Kp, device="cuda", dtype=bf)
+        wt[:, :K] = (0.02 * torch.randn(wt.shape[0], K, device="cuda", generator=g)).to(bf)
         y = torch.zeros(M, N, device="cuda", dtype=ydt)
         for _ in range(reps):
             psf.op_linear(x, wt, y, None, epi)
@@ -497,7 +517,8 @@ def make_device_block(psf, w, seed=0):
         lw.update(w_router=randn(E, D, std=D ** -0.5), w_exp_gate_up=randn(E, 2 * Ie, D, std=0.02),
                   w_exp_down=randn(E, D, Ie, std=0.02))
     else:
-        lw.update(w_gate_up=randn(2 * d.mlp_intermediate, D, std=0.02), w_down=randn(D, d.mlp_intermediate, std=0.02))
+        lw.update(w_gate_up=randn(2 * d.mlp_intermediate, D, std=0.02))
+        lw["w_down"], lw["ld_down"] = down_weight(randn, D, d.mlp_intermediate, 0.02)
     shp = (w.prefix_len, d.n_kv_heads, d.head_dim)
     pk = [randn(*shp) for _ in range(w.batch)]
     pv = [randn(*shp) for _ in range(w.batch)]

@@ -47,7 +47,7 @@ class BlockDimsC(ctypes.Structure):
 class BlockWeightsC(ctypes.Structure):
     _fields_ = [(n, ctypes.c_void_p) for n in ("g_in", "w_qkv", "g_q", "g_k", "w_o", "g_post", "w_gate_up",
                                                 "w_down", "w_router", "w_exp_gate_up", "w_exp_down")] + \
-               [("lora_a", ctypes.c_void_p * 7), ("lora_b", ctypes.c_void_p * 7)]
+               [("lora_a", ctypes.c_void_p * 7), ("lora_b", ctypes.c_void_p * 7), ("ld_down", ctypes.c_int)]
 
 
 class LoraGradsC(ctypes.Structure):
@@ -128,13 +128,15 @@ def _ptr(t) -> Optional[int]:
 
 def make_weights(w: dict) -> BlockWeightsC:
     """ctypes weights from a dict of device tensors keyed by gen_block_weights field names
-    (LoRA: ``lora_a_<site>`` / ``lora_b_<site>``)."""
+    (LoRA: ``lora_a_<site>`` / ``lora_b_<site>``; ``ld_down``: the row pitch of w_down in
+    elements, an int, absent or 0 for dense rows)."""
     c = BlockWeightsC()
     for n, _ in BlockWeightsC._fields_[:11]:
         setattr(c, n, _ptr(w.get(n)))
     for k, s in enumerate(LORA_SITES):
         c.lora_a[k] = _ptr(w.get(f"lora_a_{s}"))
         c.lora_b[k] = _ptr(w.get(f"lora_b_{s}"))
+    c.ld_down = int(w.get("ld_down", 0) or 0)
     return c
 
 

@@ -127,6 +127,9 @@ int check_weights(const gen_block_dims* d, const gen_block_weights* w, int layer
   if (d->mlp_intermediate > 0) {
     if (!w->w_gate_up || !w->w_down) return fail(GEN_EINVAL, "layer %d: w_gate_up/w_down is NULL", layer);
     if (!aligned16(w->w_gate_up) || !aligned16(w->w_down)) return fail(GEN_EINVAL, "layer %d: MLP weights not 16-byte aligned", layer);
+    if (w->ld_down != 0 && (w->ld_down < d->mlp_intermediate || w->ld_down % 8))
+      return fail(GEN_EINVAL, "layer %d: ld_down %d must be 0 or a multiple of 8 >= mlp_intermediate %d", layer,
+                  w->ld_down, d->mlp_intermediate);
   } else {
     if (!w->w_router || !w->w_exp_gate_up || !w->w_exp_down) return fail(GEN_EINVAL, "layer %d: expert weights are NULL", layer);
     if (!aligned16(w->w_exp_gate_up) || !aligned16(w->w_exp_down)) return fail(GEN_EINVAL, "layer %d: expert weights not 16-byte aligned", layer);
@@ -232,6 +235,11 @@ GemmParams gp() {
   std::memset(&p, 0, sizeof p);
   p.scale = 1.f;
   return p;
+}
+
+// Row pitch of w_down in elements (dense rows unless the caller set one).
+int ld_down_of(const gen_block_dims& d, const gen_block_weights& w) {
+  return w.ld_down > 0 ? w.ld_down : d.mlp_intermediate;
 }
 
 // ------------------------------------------------------------------ one gen block
@@ -444,7 +452,7 @@ int run_block(const gen_block_dims& d, const gen_block_weights& w, TH* hidden, c
     }
     {
       GemmParams p = gp();
-      p.A = z; p.lda = LZ; p.B = w.w_down; p.ldb = I; p.M = M; p.N = D; p.K = I;
+      p.A = z; p.lda = LZ; p.B = w.w_down; p.ldb = ld_down_of(d, w); p.M = M; p.N = D; p.K = I;
       p.C = hidden; p.ldc = D; p.R = hmid; p.ldr = D;
       p.part = L.splitk_floats ? at<float>(ws, L.splitk) : nullptr; p.part_floats = L.splitk_floats;
       const int sites[1] = {6}, ends[1] = {D};
@@ -786,7 +794,7 @@ int block_train_fwd(const gen_block_dims& d, const gen_block_weights& w, const f
 
   if (h_out) {  // down projection onto the mid-block residual: the block output
     GemmParams p = gp();
-    p.A = z; p.lda = I; p.B = w.w_down; p.ldb = I; p.M = M; p.N = D; p.K = I;
+    p.A = z; p.lda = I; p.B = w.w_down; p.ldb = ld_down_of(d, w); p.M = M; p.N = D; p.K = I;
     p.C = h_out; p.ldc = D; p.R = xmid; p.ldr = D;
     bool ext = false;
     if (off_down[0] >= 0) ext = try_k32_ext(p, EPI_RESID_F32, d, w, down_site, 1, &D, t_down, ld_down, off_down);
@@ -885,7 +893,7 @@ int block_train_bwd(const gen_block_dims& d, const gen_block_weights& w, const f
   {  // down projection: dz = dy W_down (+ LoRA)
     const BackSite bs[1] = {{6, 0, D}};
     GemmParams p = gp();
-    HIP_TRY(transpose_bf16((const bf16*)w.w_down, I, wt, D, D, I, s));
+    HIP_TRY(transpose_bf16((const bf16*)w.w_down, ld_down_of(d, w), wt, D, D, I, s));
     p.A = dyb; p.lda = D; p.B = wt; p.ldb = D; p.M = M; p.N = I; p.K = D; p.C = dz; p.ldc = I;
     n = lora_back(d, w, bs, 1, dyb, D, I, M, tp, xb_down, bt, p, slot, part, lf, s, bts_down);
     if (n < 0) return n;
@@ -1179,13 +1187,14 @@ int gen_block_lora_merge(const gen_block_dims* dims, const gen_block_weights* w,
   hipStream_t s = (hipStream_t)stream;
   for (int site = 0; site < 7; ++site) {
     const int m = mat[site];
-    const size_t off = (size_t)row0[site] * ins[site];
+    const int64_t ld = m == 3 ? ld_down_of(*dims, *w) : ins[site];   // w_down_out keeps w_down's pitch
+    const size_t off = (size_t)row0[site] * ld;
     if (dims->dtype == GEN_BF16) {
       HIP_TRY(lora_merge<bf16>((const bf16*)mats[m] + off, (const bf16*)w->lora_a[site], (const bf16*)w->lora_b[site],
-                               (bf16*)outs[m] + off, rows[site], ins[site], r, scale, s));
+                               (bf16*)outs[m] + off, rows[site], ins[site], ld, r, scale, s));
     } else {
       HIP_TRY(lora_merge<float>((const float*)mats[m] + off, (const float*)w->lora_a[site], (const float*)w->lora_b[site],
-                                (float*)outs[m] + off, rows[site], ins[site], r, scale, s));
+                                (float*)outs[m] + off, rows[site], ins[site], ld, r, scale, s));
     }
   }
   return ok();

@@ -1068,14 +1068,24 @@ int fast_waves() {
   return w;
 }
 
-// The 64-deep kernel for SwiGLU and for plain launches up to 8192 deep; the 32-deep ring kernel
-// for longer k (the down projection), split-K partial products and the expert GEMMs.
+// Long-k launches (8192 deep or more) whose A or B rows sit at a multiple of 8 KiB apart (a
+// dense bf16 row of 12288) fetch the 256 rows of a tile from few memory channels; the ring
+// kernel's 64-byte row slices tolerate that better than the 64-deep kernel's 128-byte ones.  With
+// both pitches off such multiples (rows padded by 128 B) the 64-deep kernel is the faster.
+bool long_k_ring(const GemmParams& p) {
+  const auto aliased = [](int64_t ld) { return ((ld * 2) & 8191) == 0; };
+  return p.K >= 8192 && (aliased(p.lda) || aliased(p.ldb));
+}
+
+// The 64-deep kernel for SwiGLU and for plain launches but long-k ones with aliased row pitches;
+// the 32-deep ring kernel for those, split-K partial products and the expert GEMMs.
 template <bool GROUPED, bool GATHER>
 hipError_t launch_fast(const GemmParams& p, int epi, int grid, int n_col_tiles, hipStream_t s) {
   const size_t lds = 2 * STAGE_BYTES;
+  const bool ring = GROUPED || GATHER || long_k_ring(p);
 #define PSF_L(E)                                                                                  \
   case E: {                                                                                        \
-    if (E != EPI_SWIGLU && (E == EPI_PARTIAL_F32 || GROUPED || GATHER || p.K >= 8192)) {           \
+    if (E != EPI_SWIGLU && (E == EPI_PARTIAL_F32 || ring)) {                                       \
       auto k = gemm_k32_kernel<E, GROUPED, GATHER>;                                                \
       hipError_t e = hipFuncSetAttribute((const void*)k, hipFuncAttributeMaxDynamicSharedMemorySize, \
                                          (int)lds);                                                \
@@ -1132,7 +1142,7 @@ hipError_t launch_k32_ext(const GemmParams& p, int epi, int grid, int n_col_tile
   return hipErrorInvalidValue;
 }
 
-// The 64-deep kernel with the K extension (no row gather), for launches up to 8192 deep.
+// The 64-deep kernel with the K extension (no row gather), where long_k_ring does not apply.
 hipError_t launch_fast_ext(const GemmParams& p, int epi, int grid, int n_col_tiles, hipStream_t s) {
   const size_t lds = 2 * STAGE_BYTES;
 #define PSF_L(E)                                                                                  \
@@ -1265,7 +1275,7 @@ hipError_t gemm_bf16(const GemmParams& p, int epi, hipStream_t s) {
   }
   if (p.X && p.xk > 0) {
     if (k32_ext_ok(p, epi)) {
-      if (p.K < 8192 && p.K % BK == 0) return launch_fast_ext(p, epi, n_m * n_cols, n_cols, s);
+      if (!long_k_ring(p) && p.K % BK == 0) return launch_fast_ext(p, epi, n_m * n_cols, n_cols, s);
       return launch_k32_ext(p, epi, n_m * n_cols, n_cols, s);
     }
     return launch_bf16<false, true>(p, epi, n_m * n_cols, n_cols, s);

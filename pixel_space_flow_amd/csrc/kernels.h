@@ -55,7 +55,7 @@ hipError_t attention_f32(const float* qkv, int64_t ldq, const SeqInfo& si, int H
 // Wo [out, in] = W + scale B A with A [rank, in], B [out, rank] (rank a multiple of 8, <= 128;
 // fp32 sums, one rounding); A == nullptr copies W.  Wo may equal W.
 template <typename T>
-hipError_t lora_merge(const T* W, const T* A, const T* B, T* Wo, int out, int in, int rank, float scale,
+hipError_t lora_merge(const T* W, const T* A, const T* B, T* Wo, int out, int in, int64_t ldw, int rank, float scale,
                       hipStream_t s);
 
 // patches[(i*N + t), f] from x [n_img, 3, H, W] (32x32 patches, raster tokens, (c, iy, ix) features)

@@ -103,6 +103,10 @@ def test_block_forward_rejects_bad_arguments_on_host(psf):
     d5 = dims(psf)
     d5.n_experts = 32
     assert call_block(psf, d5, w) == psf.GEN_EINVAL                        # dense and MoE at once
+    w6 = fake_weights(psf)
+    for ld in (d.mlp_intermediate - 8, d.mlp_intermediate + 4, -64):
+        w6.ld_down = ld
+        assert call_block(psf, d, w6) == psf.GEN_EINVAL and "ld_down" in psf.last_error()   # bad w_down pitch
 
 
 def test_tower_step_rejects_bad_arguments_on_host(psf):
