@@ -5,6 +5,7 @@ oracle on the same seeded inputs at the shape the GPU test uses, and checks the 
 error the model shows:
   - the prompt-pass block bar PREFIX_TOL (2.5e-2) sits above the modelled error with a margin;
   - the training backward's dh bar DH_TOL (4e-2) likewise;
+  - the bf16-residual mode's bar, the block bar plus one output rounding (2^-8 |y|) per element;
   - the fp32 residual stream (reading R16 of the design notes): with it the modelled 8B gen
     block stays inside 2e-2, while a residual rounded to bf16 at the middle and the end of the
     block does not, which is why the residual stays fp32.
@@ -46,6 +47,24 @@ def test_fp32_residual_reading():
         f"(bar {BLOCK_TOL})")
     assert e32 * MARGIN <= BLOCK_TOL
     assert e16 > BLOCK_TOL
+
+
+def test_bf16_residual_bound():
+    """The bf16-residual mode (hidden_dtype bf16, test_bf16_residual_stream): the block output is
+    rounded to bf16 once more, which moves each element by at most half a bf16 ulp, 2^-8 |y|.  Its
+    bar is therefore the block bar plus that rounding, per element: 2e-2 RMS(y) + 2^-8 |y|.  The
+    rounding model of the 8B block with the output rounded (mid-block residual fp32) stays inside
+    it with the margin."""
+    w = W.CONFIGS[1]
+    wts = W.layer_weights(w, 0, 0, "bf16")
+    h = W.block_hidden(w, 0, "bf16")
+    pk, pv = zip(*[W.prefix_kv(w, 0, s, 0, "bf16") for s in range(w.batch)])
+    ref = O.gen_block(h, wts, w.dims, list(pk), list(pv)).astype(np.float64)
+    got = gen_block_bf16(h, wts, w.dims, pk, pv, residual="bf16_out").astype(np.float64)
+    bound = BLOCK_TOL * np.sqrt(np.mean(ref ** 2)) + 2.0 ** -8 * np.abs(ref)
+    worst = float(np.max(np.abs(got - ref) / bound))
+    log(f"8B block, output rounded to bf16, rounding model vs oracle: worst |err| / (2e-2 RMS + 2^-8 |y|) = {worst:.3f}")
+    assert worst * MARGIN <= 1.0
 
 
 def test_backward_dh_tolerance():
