@@ -212,15 +212,27 @@ __global__ __launch_bounds__(256, QB == 1 ? 2 : 1) void attn_v2_kernel(const bf1
       for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
         for (int e = 0; e < 16; ++e) dst[qb][kb][e] = 0.f;
+    // K fragments (ks, kb) in order f = 2 ks + kb through a ring of FR registers: FR reads are in
+    // flight ahead of each MFMA, so the LDS latency hides under the MFMAs before it
+    constexpr int NF = D / 8, FR = 4;
+    auto rd = [&](const int f) { return *(const bf16x8*)(K0 + (f & 1) * 32 * KROW + koff[f >> 1]); };
+    bf16x8 a[FR];
 #pragma unroll
-    for (int ks = 0; ks < D / 16; ++ks)
+    for (int f = 0; f < FR; ++f) a[f] = rd(f);
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
-        const bf16x8 a = *(const bf16x8*)(K0 + kb * 32 * KROW + koff[ks]);
+    for (int f = 0; f < NF; ++f) {
 #pragma unroll
-        for (int qb = 0; qb < QB; ++qb)
-          dst[qb][kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[qb][ks], dst[qb][kb], 0, 0, 0);
-      }
+      for (int qb = 0; qb < QB; ++qb)
+        dst[qb][f & 1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[f % FR], qf[qb][f >> 1], dst[qb][f & 1], 0, 0, 0);
+      if (f + FR < NF) a[f % FR] = rd(f + FR);
+    }
+    // keep that order: the scheduler would otherwise sink each read next to its MFMA
+    __builtin_amdgcn_sched_group_barrier(0x100, FR, 1);                  // DS reads
+#pragma unroll
+    for (int f = 0; f < NF; ++f) {
+      __builtin_amdgcn_sched_group_barrier(0x008, QB, 1);                // MFMA
+      if (f + FR < NF) __builtin_amdgcn_sched_group_barrier(0x100, 1, 1);
+    }
   };
   // Online softmax of the scores in sc (tile t, keys from j0) and P . V from stage `stage`.
   // masked (a literal at every call): the tile may hold keys past the sequence end or, for causal
@@ -278,18 +290,26 @@ __global__ __launch_bounds__(256, QB == 1 ? 2 : 1) void attn_v2_kernel(const bf1
       l[qb] += rs;
     }
     const char* S0 = smem + stage * STAGE;
+    // V^T fragments (kb, st, db) in order f = (2 kb + st) NDB + db through a ring of FR registers
+    constexpr int NF = 4 * NDB, FR = 4;
+    auto rd = [&](const int f) { return *(const bf16x8*)(S0 + (f % NDB) * 32 * 128 + voff[f / NDB]); };
+    bf16x8 av[FR];
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
+    for (int f = 0; f < FR; ++f) av[f] = rd(f);
 #pragma unroll
-      for (int st = 0; st < 2; ++st) {
+    for (int f = 0; f < NF; ++f) {
+      const int ks = f / NDB, db = f % NDB;       // ks = 2 kb + st
 #pragma unroll
-        for (int db = 0; db < NDB; ++db) {
-          const bf16x8 av = *(const bf16x8*)(S0 + db * 32 * 128 + voff[kb * 2 + st]);
+      for (int qb = 0; qb < QB; ++qb)
+        o[qb][db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av[f % FR], pb[qb][ks >> 1][ks & 1], o[qb][db], 0, 0, 0);
+      if (f + FR < NF) av[f % FR] = rd(f + FR);
+    }
+    __builtin_amdgcn_sched_group_barrier(0x100, FR, 2);                  // DS reads
 #pragma unroll
-          for (int qb = 0; qb < QB; ++qb)
-            o[qb][db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, pb[qb][kb][st], o[qb][db], 0, 0, 0);
-        }
-      }
+    for (int f = 0; f < NF; ++f) {
+      __builtin_amdgcn_sched_group_barrier(0x008, QB, 2);                // MFMA
+      if (f + FR < NF) __builtin_amdgcn_sched_group_barrier(0x100, 1, 2);
+    }
   };
   // iteration t (every tile but the last): after the barrier K(t+1) and V(t) have landed and no
   // wave reads K(t) or V(t-1) any more, so K(t+2) and V(t+1) go into those halves.
