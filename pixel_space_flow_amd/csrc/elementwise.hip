@@ -248,6 +248,49 @@ __global__ __launch_bounds__(256) void pack_vt_kernel(const T* __restrict__ qkv,
   *(u32x4*)(Vt + (((int64_t)b * Hkv + g) * d + dd) * Lpad + j0) = V::pack(f);
 }
 
+// bf16 V^T of one (sequence, kv head, 64-key tile) through LDS: the tile's key rows come in as
+// 16-byte vectors (prefix rows from the cache, image rows from qkv, zeros past the end), the V^T
+// rows go out as 16-byte vectors, each 16-key group in the order [0-3, 8-11, 4-7, 12-15] as in
+// pack_vt_kernel.  Lpad is a multiple of 64.
+template <int D>
+__global__ __launch_bounds__(256) void pack_vt_tile_kernel(const bf16* __restrict__ qkv, int64_t ld, SeqInfo si,
+                                                           int Hq, int Hkv, int Lpad, bf16* __restrict__ Vt) {
+  constexpr int CPR = D / 8;                // 16-byte chunks per key row
+  constexpr int RS = D + 8;                 // padded LDS row (elements)
+  __shared__ __attribute__((aligned(16))) bf16 tile[64 * RS];
+  const int b = blockIdx.z, g = blockIdx.y, j0 = blockIdx.x * 64;
+  const int P = si.plen[b], N = si.N;
+  for (int i = threadIdx.x; i < 64 * CPR; i += 256) {
+    const int r = i / CPR, c = i - r * CPR;
+    const int j = j0 + r;
+    u32x4 v = {0, 0, 0, 0};
+    if (j < P) v = *(const u32x4*)((const bf16*)si.pv[b] + ((int64_t)j * Hkv + g) * D + c * 8);
+    else if (j < P + N) v = *(const u32x4*)(qkv + ((int64_t)b * N + j - P) * ld + (int64_t)(Hq + Hkv + g) * D + c * 8);
+    *(u32x4*)(tile + r * RS + c * 8) = v;
+  }
+  __syncthreads();
+  for (int i = threadIdx.x; i < D * 8; i += 256) {
+    const int dd = i >> 3, kc = i & 7;
+    bf16x8 e;
+#pragma unroll
+    for (int q = 0; q < 8; ++q) {
+      const int pos = kc * 8 + q;
+      const int j = (pos & ~15) | (((pos >> 2) & 1) << 3) | (((pos >> 3) & 1) << 2) | (pos & 3);
+      e[q] = tile[j * RS + dd];
+    }
+    *(bf16x8*)(Vt + (((int64_t)b * Hkv + g) * D + dd) * Lpad + j0 + kc * 8) = e;
+  }
+}
+
+hipError_t pack_vt_bf16(const bf16* qkv, int64_t ld, const SeqInfo& si, int Hq, int Hkv, int d, int Lpad, bf16* Vt,
+                        hipStream_t s) {
+  const dim3 grid(Lpad / 64, Hkv, si.B);
+  if (d == 128) hipLaunchKernelGGL((pack_vt_tile_kernel<128>), grid, dim3(256), 0, s, qkv, ld, si, Hq, Hkv, Lpad, Vt);
+  else if (d == 64) hipLaunchKernelGGL((pack_vt_tile_kernel<64>), grid, dim3(256), 0, s, qkv, ld, si, Hq, Hkv, Lpad, Vt);
+  else return hipErrorInvalidValue;
+  return hipGetLastError();
+}
+
 // ---------------------------------------------------------------- LoRA merge
 // Wo[o, i] = W[o, i] + scale * sum_r B[o, r] A[r, i] for a [64 x 256] tile per workgroup: the
 // 64 rows of B sit in LDS (every lane reads the same entry), each lane owns one column i and
@@ -428,6 +471,11 @@ hipError_t pack_kv(const T* qkv, int64_t ld, const SeqInfo& si, int Hq, int Hkv,
   const int cpr = d / V16<T>::N;
   dim3 gk((Lpad * cpr + 255) / 256, Hkv, si.B);
   hipLaunchKernelGGL(pack_k_kernel<T>, gk, dim3(256), 0, s, qkv, ld, si, Hq, Hkv, d, Lpad, Kc);
+  if (sizeof(T) == 2) {
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    return pack_vt_bf16((const bf16*)qkv, ld, si, Hq, Hkv, d, Lpad, (bf16*)Vt, s);
+  }
   dim3 gv((d * (Lpad / V16<T>::N) + 255) / 256, Hkv, si.B);
   hipLaunchKernelGGL(pack_vt_kernel<T>, gv, dim3(256), 0, s, qkv, ld, si, Hq, Hkv, d, Lpad, Vt);
   return hipGetLastError();
@@ -445,9 +493,9 @@ hipError_t pack_kv_knorm(const bf16* qkv, int64_t ld, const SeqInfo& si, int Hq,
     hipLaunchKernelGGL((pack_k_knorm_kernel<64>), grid, dim3(256), 0, s, qkv, ld, si, Hq, Hkv, Lpad, gk, table, eps, Kc, total);
   else
     return hipErrorInvalidValue;
-  dim3 gv((d * (Lpad / V16<bf16>::N) + 255) / 256, Hkv, si.B);
-  hipLaunchKernelGGL(pack_vt_kernel<bf16>, gv, dim3(256), 0, s, qkv, ld, si, Hq, Hkv, d, Lpad, Vt);
-  return hipGetLastError();
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  return pack_vt_bf16(qkv, ld, si, Hq, Hkv, d, Lpad, Vt, s);
 }
 template <typename T>
 hipError_t lora_merge(const T* W, const T* A, const T* B, T* Wo, int out, int in, int64_t ldw, int rank, float scale,
