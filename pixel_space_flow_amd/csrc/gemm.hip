@@ -16,6 +16,11 @@ namespace {
 
 constexpr int BM = 256, BN = 256, BK = 64, NT = 256;
 constexpr int STAGE_BYTES = (BM + BN) * BK * 2;  // 64 KiB per stage
+// The 64-deep kernel keeps its operands apart in LDS: two A stages, then three B stages (the
+// weights, whose loads come from HBM and have the longer latency, run two k-tiles ahead).
+constexpr int FAST_ASZ = BM * BK * 2;             // 32 KiB
+constexpr int FAST_BSZ = BN * BK * 2;             // 32 KiB
+constexpr int FAST_LDS = 2 * FAST_ASZ + 3 * FAST_BSZ;   // 160 KiB
 
 DEVI int swz(int row, int chunk) { return row * (BK * 2) + ((chunk ^ (row & 7)) << 4); }
 
@@ -471,9 +476,9 @@ __global__ __launch_bounds__(64 * NW, 1) void gemm_fast_kernel(GemmParams p, int
     }
   }
 
-  auto issue = [&](int kt, int stage) {
-    char* As = smem + stage * STAGE_BYTES;
-    char* Bs = As + BM * BK * 2;
+  // DMA of k-tile kt: A into A stage sa, B into B stage sb (each GPW loads per wave)
+  auto issue_a = [&](int kt, int sa) {
+    char* As = smem + sa * FAST_ASZ;
     if (EXT && kt >= KTM) {
       const int k0 = (kt - KTM) * BK;              // X column of this extension k-tile
 #pragma unroll
@@ -481,8 +486,6 @@ __global__ __launch_bounds__(64 * NW, 1) void gemm_fast_kernel(GemmParams p, int
         const int grp = wave * GPW + i;
         const int c = k0 + ((i & 1) ? lch1 : lch0) * 8;   // X column of this lane's chunk
         dma16(rx, As + grp * 1024, c < p.xk ? lrow * ldx2 + (uint32_t)c * 2 : 0x40000000u, grp * 8 * ldx2);
-        const bool in = c >= bx_lo[i] && c < bx_hi[i];
-        dma16(rbx[i], Bs + grp * 1024, in ? (uint32_t)(lrow * p.xr + c - bx_lo[i]) * 2 : 0x40000000u, 0);
       }
       return;
     }
@@ -494,6 +497,25 @@ __global__ __launch_bounds__(64 * NW, 1) void gemm_fast_kernel(GemmParams p, int
         dma16(ra, As + grp * 1024, avoff[i], kb);
       else
         dma16(ra, As + grp * 1024, avoff[i & 1], grp * 8 * lda2 + kb);
+    }
+  };
+  auto issue_b = [&](int kt, int sb) {
+    char* Bs = smem + 2 * FAST_ASZ + sb * FAST_BSZ;
+    if (EXT && kt >= KTM) {
+      const int k0 = (kt - KTM) * BK;
+#pragma unroll
+      for (int i = 0; i < GPW; ++i) {
+        const int grp = wave * GPW + i;
+        const int c = k0 + ((i & 1) ? lch1 : lch0) * 8;
+        const bool in = c >= bx_lo[i] && c < bx_hi[i];
+        dma16(rbx[i], Bs + grp * 1024, in ? (uint32_t)(lrow * p.xr + c - bx_lo[i]) * 2 : 0x40000000u, 0);
+      }
+      return;
+    }
+    const uint32_t kb = (uint32_t)kt * (BK * 2);
+#pragma unroll
+    for (int i = 0; i < GPW; ++i) {
+      const int grp = wave * GPW + i;
       dma16(rb, Bs + grp * 1024, (i & 1) ? bvoff1 : bvoff0, bsoff[i] + kb);
     }
   };
@@ -514,13 +536,13 @@ __global__ __launch_bounds__(64 * NW, 1) void gemm_fast_kernel(GemmParams p, int
   const int arow0 = (wm * 128 + r16) * (BK * 2), brow0 = (wn * (BN / WN) + r16) * (BK * 2);
   bf16x8 fal[4], fah[4], fb[NB16];
   auto rd_a = [&](bf16x8 (&f)[4], int stage, int ks, int half) {
-    const char* As = smem + stage * STAGE_BYTES;
+    const char* As = smem + stage * FAST_ASZ;
     const int ch = ((4 * ks + c16) ^ sw) << 4;
 #pragma unroll
     for (int i = 0; i < 4; ++i) f[i] = *(const bf16x8*)(As + arow0 + (half * 4 + i) * 16 * (BK * 2) + ch);
   };
-  auto rd_b = [&](int stage, int ks) {
-    const char* Bs = smem + stage * STAGE_BYTES + BM * BK * 2;
+  auto rd_b = [&](int stage, int ks) {          // stage: B stage 0-2
+    const char* Bs = smem + 2 * FAST_ASZ + stage * FAST_BSZ;
     const int ch = ((4 * ks + c16) ^ sw) << 4;
 #pragma unroll
     for (int nb = 0; nb < NB16; ++nb) fb[nb] = *(const bf16x8*)(Bs + brow0 + nb * 16 * (BK * 2) + ch);
@@ -544,19 +566,27 @@ __global__ __launch_bounds__(64 * NW, 1) void gemm_fast_kernel(GemmParams p, int
   // Software pipeline over the four half-steps of a tile (32-deep half ks, wave-tile rows
   // 0-63 or 64-127): the fragments of the next half-step are read while this one's MFMAs run;
   // B fragments after the last MFMA on the previous ones.  In the last half-step every wave waits
-  // for its LDS-DMA and meets the others, so the next tile's stage is complete and this tile's
-  // stage is free for the DMA of tile kt+2.
-  issue(0, 0);
+  // for the loads of tile kt+1 and meets the others, so tile kt+1 is complete and tile kt's A
+  // stage and B stage are free: the DMA of A(kt+2) and of B(kt+3) goes into them.  A runs one
+  // tile ahead of its use, B two; the wait leaves the newest GPW loads, B(kt+2), in flight.
+  constexpr int VM_N = GPW;
+  constexpr int VM_B_IN_FLIGHT = (VM_N & 15) | ((VM_N >> 4) << 14) | (7 << 4) | (15 << 8);
+  issue_a(0, 0);
+  issue_b(0, 0);
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
-  if (KT > 1) issue(1, 1);
+  // tiles past the end reload the last tile into a stage nobody reads again, so every issue sends
+  // the same number of loads and the vmcnt arithmetic holds throughout
+  issue_a(min(1, KT - 1), 1);
+  issue_b(min(1, KT - 1), 1);
+  issue_b(min(2, KT - 1), 2);
   rd_a(fal, 0, 0, 0);
   rd_b(0, 0);
-  // every k-tile but the last: the body has no branches (the DMA of the tile two ahead reloads
-  // the last tile into the free stage when it runs past the end)
-  int kt = 0;
+  // every k-tile but the last: the body has no branches
+  int kt = 0, sb = 0;                           // sb: B stage of tile kt (kt mod 3)
   for (; kt + 1 < KT; ++kt) {
     const int st = kt & 1;
+    const int sb1 = sb == 2 ? 0 : sb + 1;
     // half-step 0: rows 0-63 of k 0-31
     __builtin_amdgcn_s_setprio(2);
     rd_a(fah, st, 0, 1);
@@ -569,7 +599,7 @@ __global__ __launch_bounds__(64 * NW, 1) void gemm_fast_kernel(GemmParams p, int
     mma(fah, 1);
     interleave(4);
     __builtin_amdgcn_sched_barrier(0);
-    rd_b(st, 1);
+    rd_b(sb, 1);
     // half-step 2: rows 0-63 of k 32-63
     __builtin_amdgcn_s_setprio(0);
     rd_a(fah, st, 1, 1);
@@ -578,14 +608,17 @@ __global__ __launch_bounds__(64 * NW, 1) void gemm_fast_kernel(GemmParams p, int
     __builtin_amdgcn_sched_barrier(0);
     // half-step 3: rows 64-127 of k 32-63
     __builtin_amdgcn_s_setprio(3);
-    __builtin_amdgcn_s_waitcnt(0);
-    __syncthreads();
-    issue(min(kt + 2, KT - 1), st);
+    __builtin_amdgcn_s_waitcnt(VM_B_IN_FLIGHT);
+    __builtin_amdgcn_s_waitcnt(0xc07f);          // and this wave's LDS reads of tile kt
+    __builtin_amdgcn_s_barrier();
+    issue_a(min(kt + 2, KT - 1), st);
+    issue_b(min(kt + 3, KT - 1), sb);
     rd_a(fal, st ^ 1, 0, 0);
     mma(fah, 1);
     interleave(4);
     __builtin_amdgcn_sched_barrier(0);
-    rd_b(st ^ 1, 0);
+    rd_b(sb1, 0);
+    sb = sb1;
   }
   {
     const int st = kt & 1;
@@ -593,7 +626,7 @@ __global__ __launch_bounds__(64 * NW, 1) void gemm_fast_kernel(GemmParams p, int
     mma(fal, 0);
     rd_a(fal, st, 1, 0);
     mma(fah, 1);
-    rd_b(st, 1);
+    rd_b(sb, 1);
     rd_a(fah, st, 1, 1);
     mma(fal, 0);
     mma(fah, 1);
@@ -1095,9 +1128,9 @@ hipError_t launch_fast(const GemmParams& p, int epi, int grid, int n_col_tiles, 
     }                                                                                              \
     auto k = fast_waves() == 4 ? gemm_fast_kernel<E, GROUPED, GATHER, 4> : gemm_fast_kernel<E, GROUPED, GATHER, 8>; \
     hipError_t e = hipFuncSetAttribute((const void*)k, hipFuncAttributeMaxDynamicSharedMemorySize, \
-                                       (int)lds);                                                  \
+                                       FAST_LDS);                                                  \
     if (e != hipSuccess) return e;                                                                 \
-    hipLaunchKernelGGL(k, dim3(grid), dim3(64 * fast_waves()), lds, s, p, n_col_tiles);            \
+    hipLaunchKernelGGL(k, dim3(grid), dim3(64 * fast_waves()), FAST_LDS, s, p, n_col_tiles);       \
     return hipGetLastError();                                                                      \
   }
   switch (epi) {
@@ -1144,7 +1177,7 @@ hipError_t launch_k32_ext(const GemmParams& p, int epi, int grid, int n_col_tile
 
 // The 64-deep kernel with the K extension (no row gather), where long_k_ring does not apply.
 hipError_t launch_fast_ext(const GemmParams& p, int epi, int grid, int n_col_tiles, hipStream_t s) {
-  const size_t lds = 2 * STAGE_BYTES;
+  const size_t lds = FAST_LDS;
 #define PSF_L(E)                                                                                  \
   case E: {                                                                                        \
     auto k = gemm_fast_kernel<E, false, false, 8, true>;                                           \
