@@ -534,20 +534,20 @@ __global__ __launch_bounds__(64 * NW, 1) void gemm_fast_kernel(GemmParams p, int
   const int r16 = lane & 15, c16 = lane >> 4;
   const int sw = (r16 >> 1) & 7;              // the same for all blocks: their rows differ by 16
   const int arow0 = (wm * 128 + r16) * (BK * 2), brow0 = (wn * (BN / WN) + r16) * (BK * 2);
-  bf16x8 fal[4], fah[4], fb[NB16];
+  bf16x8 fal[4], fah[4], fb0[NB16], fb1[NB16];   // B fragments of the two 32-deep halves
   auto rd_a = [&](bf16x8 (&f)[4], int stage, int ks, int half) {
     const char* As = smem + stage * FAST_ASZ;
     const int ch = ((4 * ks + c16) ^ sw) << 4;
 #pragma unroll
     for (int i = 0; i < 4; ++i) f[i] = *(const bf16x8*)(As + arow0 + (half * 4 + i) * 16 * (BK * 2) + ch);
   };
-  auto rd_b = [&](int stage, int ks) {          // stage: B stage 0-2
+  auto rd_b = [&](bf16x8 (&f)[NB16], int stage, int ks) {   // stage: B stage 0-2
     const char* Bs = smem + 2 * FAST_ASZ + stage * FAST_BSZ;
     const int ch = ((4 * ks + c16) ^ sw) << 4;
 #pragma unroll
-    for (int nb = 0; nb < NB16; ++nb) fb[nb] = *(const bf16x8*)(Bs + brow0 + nb * 16 * (BK * 2) + ch);
+    for (int nb = 0; nb < NB16; ++nb) f[nb] = *(const bf16x8*)(Bs + brow0 + nb * 16 * (BK * 2) + ch);
   };
-  auto mma = [&](const bf16x8 (&fa)[4], int half) {
+  auto mma = [&](const bf16x8 (&fa)[4], const bf16x8 (&fb)[NB16], int half) {
 #pragma unroll
     for (int i = 0; i < 4; ++i)
 #pragma unroll
@@ -564,11 +564,13 @@ __global__ __launch_bounds__(64 * NW, 1) void gemm_fast_kernel(GemmParams p, int
   };
 
   // Software pipeline over the four half-steps of a tile (32-deep half ks, wave-tile rows
-  // 0-63 or 64-127): the fragments of the next half-step are read while this one's MFMAs run;
-  // B fragments after the last MFMA on the previous ones.  In the last half-step every wave waits
-  // for the loads of tile kt+1 and meets the others, so tile kt+1 is complete and tile kt's A
-  // stage and B stage are free: the DMA of A(kt+2) and of B(kt+3) goes into them.  A runs one
-  // tile ahead of its use, B two; the wait leaves the newest GPW loads, B(kt+2), in flight.
+  // 0-63 or 64-127): the A fragments of the next half-step are read while this one's MFMAs run;
+  // the B fragments of the tile's second half (fb1) at its first half-step, those of the next
+  // tile's first half (fb0) right after the last half-step's barrier, so no half-step starts by
+  // waiting for LDS.  In the last half-step every wave waits for the loads of tile kt+1 and meets
+  // the others, so tile kt+1 is complete and tile kt's A stage and B stage are free: the DMA of
+  // A(kt+2) and of B(kt+3) goes into them.  A runs one tile ahead of its use, B (the weights, whose
+  // loads carry most of the latency) two; the wait leaves the newest GPW loads, B(kt+2), in flight.
   constexpr int VM_N = GPW;
   constexpr int VM_B_IN_FLIGHT = (VM_N & 15) | ((VM_N >> 4) << 14) | (7 << 4) | (15 << 8);
   issue_a(0, 0);
@@ -581,7 +583,7 @@ __global__ __launch_bounds__(64 * NW, 1) void gemm_fast_kernel(GemmParams p, int
   issue_b(min(1, KT - 1), 1);
   issue_b(min(2, KT - 1), 2);
   rd_a(fal, 0, 0, 0);
-  rd_b(0, 0);
+  rd_b(fb0, 0, 0);
   // every k-tile but the last: the body has no branches
   int kt = 0, sb = 0;                           // sb: B stage of tile kt (kt mod 3)
   for (; kt + 1 < KT; ++kt) {
@@ -590,20 +592,20 @@ __global__ __launch_bounds__(64 * NW, 1) void gemm_fast_kernel(GemmParams p, int
     // half-step 0: rows 0-63 of k 0-31
     __builtin_amdgcn_s_setprio(2);
     rd_a(fah, st, 0, 1);
-    mma(fal, 0);
-    interleave(4);
+    rd_b(fb1, sb, 1);
+    mma(fal, fb0, 0);
+    interleave(8);
     __builtin_amdgcn_sched_barrier(0);
     // half-step 1: rows 64-127 of k 0-31
     __builtin_amdgcn_s_setprio(1);
     rd_a(fal, st, 1, 0);
-    mma(fah, 1);
+    mma(fah, fb0, 1);
     interleave(4);
     __builtin_amdgcn_sched_barrier(0);
-    rd_b(sb, 1);
     // half-step 2: rows 0-63 of k 32-63
     __builtin_amdgcn_s_setprio(0);
     rd_a(fah, st, 1, 1);
-    mma(fal, 0);
+    mma(fal, fb1, 0);
     interleave(4);
     __builtin_amdgcn_sched_barrier(0);
     // half-step 3: rows 64-127 of k 32-63
@@ -614,22 +616,22 @@ __global__ __launch_bounds__(64 * NW, 1) void gemm_fast_kernel(GemmParams p, int
     issue_a(min(kt + 2, KT - 1), st);
     issue_b(min(kt + 3, KT - 1), sb);
     rd_a(fal, st ^ 1, 0, 0);
-    mma(fah, 1);
-    interleave(4);
+    rd_b(fb0, sb1, 0);
+    mma(fah, fb1, 1);
+    interleave(8);
     __builtin_amdgcn_sched_barrier(0);
-    rd_b(sb1, 0);
     sb = sb1;
   }
   {
     const int st = kt & 1;
     rd_a(fah, st, 0, 1);
-    mma(fal, 0);
+    rd_b(fb1, sb, 1);
+    mma(fal, fb0, 0);
     rd_a(fal, st, 1, 0);
-    mma(fah, 1);
-    rd_b(sb, 1);
+    mma(fah, fb0, 1);
     rd_a(fah, st, 1, 1);
-    mma(fal, 0);
-    mma(fah, 1);
+    mma(fal, fb1, 0);
+    mma(fah, fb1, 1);
   }
   __builtin_amdgcn_s_setprio(0);
 
