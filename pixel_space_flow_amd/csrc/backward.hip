@@ -193,7 +193,7 @@ __global__ __launch_bounds__(256) void swiglu_kernel(const bf16* __restrict__ gu
   const int64_t m = t / I;
   const int j = (int)(t - m * I);
   const float gt = static_cast<float>(gu[m * 2 * I + j]), up = static_cast<float>(gu[m * 2 * I + I + j]);
-  z[t] = static_cast<bf16>(gt / (1.0f + __expf(-gt)) * up);
+  z[t] = static_cast<bf16>(silu_f(gt) * up);
 }
 
 // The same for I a multiple of 8: eight columns per thread, 16-byte loads and stores.
@@ -208,7 +208,7 @@ __global__ __launch_bounds__(256) void swiglu8_kernel(const bf16* __restrict__ g
 #pragma unroll
   for (int e = 0; e < 8; ++e) {
     const float gt = static_cast<float>(g[e]), up = static_cast<float>(u[e]);
-    o[e] = static_cast<bf16>(gt / (1.0f + __expf(-gt)) * up);
+    o[e] = static_cast<bf16>(silu_f(gt) * up);
   }
   *(bf16x8*)(z + t * 8) = o;
 }

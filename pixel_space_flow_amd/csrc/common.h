@@ -40,4 +40,8 @@ DEVI int xcd_remap(int id, int n) {
   return (id & 7) * q + (id >> 3);
 }
 
-DEVI float silu_f(float x) { return x / (1.0f + __expf(-x)); }
+// silu(x) = x sigmoid(x).  The reciprocal is v_rcp_f32 (1 ulp) rather than an IEEE division,
+// whose scale / fma / fixup sequence costs several times as many instructions; the result is
+// rounded to bf16 by every caller.  1 + e^-x >= 1, so no denormal reaches the reciprocal;
+// x = -inf gives NaN as the division would (-inf * 0).
+DEVI float silu_f(float x) { return x * __builtin_amdgcn_rcpf(1.0f + __expf(-x)); }

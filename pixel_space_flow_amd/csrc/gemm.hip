@@ -371,6 +371,90 @@ DEVI void epi_row16(const GemmParams& p, int row, int col0, int ncols, float* v)
   }
 }
 
+// Epilogue of 4 consecutive columns [col0, col0+4) of one output row, straight from the
+// accumulators (col0 is a multiple of 4; leading dimensions are multiples of 8, so the vector
+// accesses are aligned).  Residual inputs come in through rin, loaded by the caller ahead of time.
+template <int EPI>
+DEVI void epi_row4_store(const GemmParams& p, int row, int col0, int ncols, const float* v) {
+  const bool full = col0 + 4 <= ncols;
+  if (EPI == EPI_F32_IMG) {
+    const int img = row / p.rows_per, t = row - img * p.rows_per;
+    const int pw = p.img_W >> 5;
+    const int py = t / pw, px = t - py * pw;
+    const int c = col0 >> 10, iy = (col0 >> 5) & 31, ix = col0 & 31;
+    float* out = (float*)p.C + (((int64_t)img * 3 + c) * p.img_H + py * 32 + iy) * p.img_W + px * 32 + ix;
+    if (full) *(float4*)out = make_float4(v[0], v[1], v[2], v[3]);
+    else for (int j = 0; j < 4 && col0 + j < ncols; ++j) out[j] = v[j];
+    return;
+  }
+  if (EPI == EPI_BIAS_BCAST || EPI == EPI_BIAS_BCAST_F32) {
+    const int img = row / p.rows_per, t = row - img * p.rows_per;
+    const float* bias = p.bias + (int64_t)img * p.N + col0;
+    float x[4];
+    for (int j = 0; j < 4; ++j) x[j] = v[j] + ((col0 + j < ncols) ? bias[j] : 0.f);
+    for (int br = 0; br < p.n_bcast; ++br) {
+      const int64_t o = ((int64_t)(img * p.n_bcast + br) * p.rows_per + t) * p.ldc + col0;
+      if (EPI == EPI_BIAS_BCAST_F32) {
+        float* C = (float*)p.C + o;
+        if (full) *(float4*)C = make_float4(x[0], x[1], x[2], x[3]);
+        else for (int j = 0; j < 4 && col0 + j < ncols; ++j) C[j] = x[j];
+      } else {
+        bf16* C = (bf16*)p.C + o;
+        if (full) {
+          bf16x4 a;
+#pragma unroll
+          for (int j = 0; j < 4; ++j) a[j] = from_f<bf16>(x[j]);
+          *(bf16x4*)C = a;
+        } else {
+          for (int j = 0; j < 4 && col0 + j < ncols; ++j) C[j] = from_f<bf16>(x[j]);
+        }
+      }
+    }
+    return;
+  }
+  if (EPI == EPI_RESID_TO_F32 || EPI == EPI_RESID_F32 || EPI == EPI_PARTIAL_F32) {
+    float* C = (float*)p.C + (int64_t)row * p.ldc + col0;
+    if (full) *(float4*)C = make_float4(v[0], v[1], v[2], v[3]);
+    else for (int j = 0; j < 4 && col0 + j < ncols; ++j) C[j] = v[j];
+  } else {
+    bf16* C = (bf16*)p.C + (int64_t)row * p.ldc + col0;
+    if (full) {
+      bf16x4 a;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) a[j] = from_f<bf16>(v[j]);
+      *(bf16x4*)C = a;
+    } else {
+      for (int j = 0; j < 4 && col0 + j < ncols; ++j) C[j] = from_f<bf16>(v[j]);
+    }
+  }
+}
+
+// The residual term of 4 consecutive columns as fp32 (zero for epilogues without one).
+template <int EPI>
+DEVI f32x4 epi_row4_resid(const GemmParams& p, int row, int col0, int ncols) {
+  f32x4 r = {0.f, 0.f, 0.f, 0.f};
+  const bool full = col0 + 4 <= ncols;
+  if (EPI == EPI_RESID || EPI == EPI_RESID_TO_F32) {
+    const bf16* R = (const bf16*)p.R + (int64_t)row * p.ldr + col0;
+    if (full) {
+      const bf16x4 a = *(const bf16x4*)R;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) r[j] = static_cast<float>(a[j]);
+    } else {
+      for (int j = 0; j < 4 && col0 + j < ncols; ++j) r[j] = to_f(R[j]);
+    }
+  } else if (EPI == EPI_RESID_FROM_F32 || EPI == EPI_RESID_F32) {
+    const float* R = (const float*)p.R + (int64_t)row * p.ldr + col0;
+    if (full) {
+      const float4 f = *(const float4*)R;
+      r[0] = f.x; r[1] = f.y; r[2] = f.z; r[3] = f.w;
+    } else {
+      for (int j = 0; j < 4 && col0 + j < ncols; ++j) r[j] = R[j];
+    }
+  }
+  return r;
+}
+
 template <int EPI, bool GROUPED, bool GATHER, int NW, bool EXT = false>
 __global__ __launch_bounds__(64 * NW, 1) void gemm_fast_kernel(GemmParams p, int n_col_tiles) {
   // NW = 4: 2 x 2 waves of 128 x 128 (one wave per SIMD); NW = 8: 2 x 4 waves of 128 x 64 (two
@@ -530,7 +614,10 @@ __global__ __launch_bounds__(64 * NW, 1) void gemm_fast_kernel(GemmParams p, int
       for (int e = 0; e < 4; ++e) acc[a][b][e] = 0.f;
 
   // 16x16x32 fragments (v_mfma_f32_16x16x32_bf16): lane l holds row l % 16 of a 16-row block and
-  // logical chunk 4 ks + l / 16 of the 32-deep half ks of the 64-deep tile
+  // logical chunk 4 ks + l / 16 of the 32-deep half ks of the 64-deep tile.  The B fragment goes
+  // in as the instruction's first operand, so the product block comes out transposed: lane l
+  // holds output row l % 16, columns 4 (l / 16) .. 4 (l / 16) + 3, which the epilogue stores
+  // straight from the accumulators.
   const int r16 = lane & 15, c16 = lane >> 4;
   const int sw = (r16 >> 1) & 7;              // the same for all blocks: their rows differ by 16
   const int arow0 = (wm * 128 + r16) * (BK * 2), brow0 = (wn * (BN / WN) + r16) * (BK * 2);
@@ -552,7 +639,7 @@ __global__ __launch_bounds__(64 * NW, 1) void gemm_fast_kernel(GemmParams p, int
     for (int i = 0; i < 4; ++i)
 #pragma unroll
       for (int nb = 0; nb < NB16; ++nb)
-        acc[half * 4 + i][nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fa[i], fb[nb], acc[half * 4 + i][nb], 0, 0, 0);
+        acc[half * 4 + i][nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fb[nb], fa[i], acc[half * 4 + i][nb], 0, 0, 0);
   };
   // MFMAs in pairs, an LDS read after each of the first nds pairs
   auto interleave = [&](int nds) {
@@ -635,83 +722,73 @@ __global__ __launch_bounds__(64 * NW, 1) void gemm_fast_kernel(GemmParams p, int
   }
   __builtin_amdgcn_s_setprio(0);
 
-  // ---- epilogue through LDS: each wave stages one 32x32 fp32 block at a time, then every lane
-  // owns 16 consecutive columns of one row (lanes 2r, 2r+1 cover row r), so global accesses are
-  // 16-byte vectors and the per-row index math runs once per block.
-  __builtin_amdgcn_s_waitcnt(0);   // a trailing reload of the last tile has landed
-  __syncthreads();   // every wave is done with the LDS stages
-  constexpr int TS = 36;                                   // padded fp32 row stride of a staged block
-  float* T0 = (float*)smem + wave * (2 * 32 * TS);
-  float* T1 = T0 + 32 * TS;
-  const int rr = lane >> 1, cc = (lane & 1) * 16;
+  // ---- epilogue straight from the accumulators: block (a, b) of lane l is output row
+  // wm*128 + 16a + l%16, columns 16b + 4(l/16) .. +3 of the wave's slice, stored as one 8- or
+  // 16-byte vector.  The residual rows of block row a+1 are loaded before block row a is stored
+  // (R may alias C: the two never touch the same element), rows past the tile's end read the last
+  // valid row and store nothing.
+  __builtin_amdgcn_s_waitcnt(0);   // the trailing reloads of the last tile have landed in LDS
+  if (EPI == EPI_SWIGLU) {
+    // gate block b (b/2 even) and its up block b+2 hold the same output columns
 #pragma unroll
-  for (int mb = 0; mb < 4; ++mb) {
+    for (int a = 0; a < 8; ++a) {
+      const int r = wm * 128 + a * 16 + r16;
+      if (r >= rows) continue;
+      const int row = row0 + r;
 #pragma unroll
-    for (int nb = 0; nb < NBW; ++nb) {
-      if (EPI == EPI_SWIGLU && (nb & 1)) continue;       // consumed together with its gate block
+      for (int b = 0; b < NB16; ++b) {
+        if ((b >> 1) & 1) continue;
+        const int col = tn * (BN / 2) + ((wn * NBW + (b >> 1)) >> 1) * 32 + (b & 1) * 16 + 4 * c16;
+        float v[4], u[4];
 #pragma unroll
-      for (int q = 0; q < 4; ++q)
-#pragma unroll
-        for (int e = 0; e < 4; ++e)
-          T0[((q >> 1) * 16 + 4 * c16 + e) * TS + (q & 1) * 16 + r16] = acc[2 * mb + (q >> 1)][2 * nb + (q & 1)][e];
-      if (EPI == EPI_SWIGLU) {
-#pragma unroll
-        for (int q = 0; q < 4; ++q)
-#pragma unroll
-          for (int e = 0; e < 4; ++e)
-            T1[((q >> 1) * 16 + 4 * c16 + e) * TS + (q & 1) * 16 + r16] = acc[2 * mb + (q >> 1)][2 * (nb + 1) + (q & 1)][e];
-      }
-      __builtin_amdgcn_s_waitcnt(0xc07f);                   // lgkmcnt(0): staged values written
-      __builtin_amdgcn_wave_barrier();
-      float v[16];
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const float4 f = *(const float4*)(T0 + rr * TS + cc + 4 * q);
-        v[4 * q] = f.x; v[4 * q + 1] = f.y; v[4 * q + 2] = f.z; v[4 * q + 3] = f.w;
-      }
-      if (EPI == EPI_SWIGLU) {
-        float u[16];
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          const float4 f = *(const float4*)(T1 + rr * TS + cc + 4 * q);
-          u[4 * q] = f.x; u[4 * q + 1] = f.y; u[4 * q + 2] = f.z; u[4 * q + 3] = f.w;
-        }
+        for (int e = 0; e < 4; ++e) { v[e] = acc[a][b][e]; u[e] = acc[a][b + 2][e]; }
         // optional bf16 terms added before the activation (the LoRA up-projection): R holds the
         // gate term at column j and the up term at column swiglu_I + j
-        const int rsw = wm * 128 + mb * 32 + rr;
-        const int csw = tn * (BN / 2) + (wn * (NBW / 2) + (nb >> 1)) * 32 + cc;
-        if (p.R && rsw < rows) {
-          const bf16* rg = (const bf16*)p.R + (int64_t)(row0 + rsw) * p.ldr + csw;
+        if (p.R) {
+          const bf16* rg = (const bf16*)p.R + (int64_t)row * p.ldr + col;
           const bf16* ru = rg + p.swiglu_I;
-          if (csw + 16 <= p.swiglu_I) {
+          if (col + 4 <= p.swiglu_I) {
+            const bf16x4 ga = *(const bf16x4*)rg, ua = *(const bf16x4*)ru;
 #pragma unroll
-            for (int h2 = 0; h2 < 2; ++h2) {
-              const bf16x8 a = *(const bf16x8*)(rg + 8 * h2), b = *(const bf16x8*)(ru + 8 * h2);
-#pragma unroll
-              for (int j = 0; j < 8; ++j) {
-                v[8 * h2 + j] += static_cast<float>(a[j]);
-                u[8 * h2 + j] += static_cast<float>(b[j]);
-              }
-            }
+            for (int e = 0; e < 4; ++e) { v[e] += static_cast<float>(ga[e]); u[e] += static_cast<float>(ua[e]); }
           } else {
-            for (int j = 0; j < 16 && csw + j < p.swiglu_I; ++j) {
-              v[j] += static_cast<float>(rg[j]);
-              u[j] += static_cast<float>(ru[j]);
+            for (int e = 0; e < 4 && col + e < p.swiglu_I; ++e) {
+              v[e] += static_cast<float>(rg[e]);
+              u[e] += static_cast<float>(ru[e]);
             }
           }
         }
 #pragma unroll
-        for (int j = 0; j < 16; ++j) v[j] = silu_f(v[j]) * u[j];
+        for (int e = 0; e < 4; ++e) v[e] = silu_f(v[e]) * u[e];
+        epi_row4_store<EPI>(p, row, col, p.swiglu_I, v);
       }
-      __builtin_amdgcn_s_waitcnt(0xc07f);                   // reads done before the next block overwrites
-      __builtin_amdgcn_wave_barrier();
-      const int r = wm * 128 + mb * 32 + rr;
-      if (r < rows) {
-        const int row = row0 + r;
-        const int col0 = (EPI == EPI_SWIGLU) ? tn * (BN / 2) + (wn * (NBW / 2) + (nb >> 1)) * 32 + cc
-                                             : tn * BN + wn * (BN / WN) + nb * 32 + cc;
-        const int ncols = (EPI == EPI_SWIGLU) ? p.swiglu_I : p.N;
-        epi_row16<EPI>(p, row, col0, ncols, v);
+    }
+  } else {
+    constexpr bool HAS_R = EPI == EPI_RESID || EPI == EPI_RESID_TO_F32 || EPI == EPI_RESID_FROM_F32 ||
+                           EPI == EPI_RESID_F32;
+    const int colw = tn * BN + wn * (BN / WN) + 4 * c16;
+    f32x4 rn[NB16];
+    auto load_r = [&](int a) {
+      const int row = row0 + min(wm * 128 + a * 16 + r16, rows - 1);
+#pragma unroll
+      for (int b = 0; b < NB16; ++b) rn[b] = epi_row4_resid<EPI>(p, row, colw + 16 * b, p.N);
+    };
+    load_r(0);
+#pragma unroll
+    for (int a = 0; a < 8; ++a) {
+      f32x4 rc[NB16];
+#pragma unroll
+      for (int b = 0; b < NB16; ++b) rc[b] = rn[b];
+      if (a + 1 < 8) load_r(a + 1);
+      const int r = wm * 128 + a * 16 + r16;
+      if (r >= rows) continue;
+#pragma unroll
+      for (int b = 0; b < NB16; ++b) {
+        float v[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          v[e] = EPI == EPI_SCALED ? acc[a][b][e] * p.scale : HAS_R ? acc[a][b][e] + rc[b][e] : acc[a][b][e];
+        epi_row4_store<EPI>(p, row0 + r, colw + 16 * b, p.N, v);
       }
     }
   }
