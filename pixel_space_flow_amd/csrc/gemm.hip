@@ -455,6 +455,36 @@ DEVI f32x4 epi_row4_resid(const GemmParams& p, int row, int col0, int ncols) {
   return r;
 }
 
+// Two 16-column blocks b, b+1 of one 16-row group, 4 columns of each per lane (lane l: columns
+// 4 (l/16) .. +3 of both blocks), rounded to bf16.  Lanes of the 16-lane rows 1 and 3 hand their
+// block-b columns to rows 0 and 2 and take those rows' block-(b+1) columns (v_permlane16_swap), so
+// lane l ends with 8 consecutive columns: those of block b + (l/16) % 2 from column 8 ((l/16) / 2),
+// i.e. at offset coff from block b's first column.  Every lane of the wave must execute it.
+DEVI bf16x8 pair_to_8(const float* v0, const float* v1, int c16, int& coff) {
+  bf16x4 a0, a1;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) { a0[e] = from_f<bf16>(v0[e]); a1[e] = from_f<bf16>(v1[e]); }
+  u32x2 w0 = __builtin_bit_cast(u32x2, a0), w1 = __builtin_bit_cast(u32x2, a1);
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const auto r = __builtin_amdgcn_permlane16_swap(w0[i], w1[i], false, false);
+    w0[i] = r[0];
+    w1[i] = r[1];
+  }
+  coff = (c16 & 1) * 16 + (c16 >> 1) * 8;
+  const u32x4 o = {w0[0], w0[1], w1[0], w1[1]};
+  return __builtin_bit_cast(bf16x8, o);
+}
+
+// 8 consecutive bf16 columns [col, col+8) of row pointer C (at col), the valid ones below ncols.
+DEVI void store8_bf16(bf16* C, int col, int ncols, bf16x8 o) {
+  if (col + 8 <= ncols) {
+    *(bf16x8*)C = o;
+  } else {
+    for (int j = 0; j < 8 && col + j < ncols; ++j) C[j] = o[j];
+  }
+}
+
 template <int EPI, bool GROUPED, bool GATHER, int NW, bool EXT = false>
 __global__ __launch_bounds__(64 * NW, 1) void gemm_fast_kernel(GemmParams p, int n_col_tiles) {
   // NW = 4: 2 x 2 waves of 128 x 128 (one wave per SIMD); NW = 8: 2 x 4 waves of 128 x 64 (two
@@ -723,49 +753,59 @@ __global__ __launch_bounds__(64 * NW, 1) void gemm_fast_kernel(GemmParams p, int
   __builtin_amdgcn_s_setprio(0);
 
   // ---- epilogue straight from the accumulators: block (a, b) of lane l is output row
-  // wm*128 + 16a + l%16, columns 16b + 4(l/16) .. +3 of the wave's slice, stored as one 8- or
-  // 16-byte vector.  The residual rows of block row a+1 are loaded before block row a is stored
-  // (R may alias C: the two never touch the same element), rows past the tile's end read the last
-  // valid row and store nothing.
+  // wm*128 + 16a + l%16, columns 16b + 4(l/16) .. +3 of the wave's slice.  bf16 outputs of block
+  // pairs (b, b+1) are exchanged between lanes into 8 consecutive columns and stored as 16 bytes
+  // per lane; fp32 outputs as 16 bytes per lane straight away.  The residual rows of block row a+1
+  // are loaded before block row a is stored (R may alias C: the two never touch the same element);
+  // rows past the tile's end read the last valid row and store nothing.
   __builtin_amdgcn_s_waitcnt(0);   // the trailing reloads of the last tile have landed in LDS
   if (EPI == EPI_SWIGLU) {
-    // gate block b (b/2 even) and its up block b+2 hold the same output columns
+    // gate block b (b/2 even) and its up block b+2 hold the same output columns; gate blocks come
+    // in pairs b, b+1 (b even)
 #pragma unroll
     for (int a = 0; a < 8; ++a) {
       const int r = wm * 128 + a * 16 + r16;
-      if (r >= rows) continue;
+      const bool rok = r < rows;
       const int row = row0 + r;
 #pragma unroll
-      for (int b = 0; b < NB16; ++b) {
+      for (int b = 0; b < NB16; b += 2) {
         if ((b >> 1) & 1) continue;
-        const int col = tn * (BN / 2) + ((wn * NBW + (b >> 1)) >> 1) * 32 + (b & 1) * 16 + 4 * c16;
-        float v[4], u[4];
+        const int colp = tn * (BN / 2) + ((wn * NBW + (b >> 1)) >> 1) * 32;   // first column of the pair
+        float v[2][4];
 #pragma unroll
-        for (int e = 0; e < 4; ++e) { v[e] = acc[a][b][e]; u[e] = acc[a][b + 2][e]; }
-        // optional bf16 terms added before the activation (the LoRA up-projection): R holds the
-        // gate term at column j and the up term at column swiglu_I + j
-        if (p.R) {
-          const bf16* rg = (const bf16*)p.R + (int64_t)row * p.ldr + col;
-          const bf16* ru = rg + p.swiglu_I;
-          if (col + 4 <= p.swiglu_I) {
-            const bf16x4 ga = *(const bf16x4*)rg, ua = *(const bf16x4*)ru;
+        for (int h = 0; h < 2; ++h) {
+          const int col = colp + h * 16 + 4 * c16;
+          float u[4];
 #pragma unroll
-            for (int e = 0; e < 4; ++e) { v[e] += static_cast<float>(ga[e]); u[e] += static_cast<float>(ua[e]); }
-          } else {
-            for (int e = 0; e < 4 && col + e < p.swiglu_I; ++e) {
-              v[e] += static_cast<float>(rg[e]);
-              u[e] += static_cast<float>(ru[e]);
+          for (int e = 0; e < 4; ++e) { v[h][e] = acc[a][b + h][e]; u[e] = acc[a][b + h + 2][e]; }
+          // optional bf16 terms added before the activation (the LoRA up-projection): R holds the
+          // gate term at column j and the up term at column swiglu_I + j
+          if (p.R && rok) {
+            const bf16* rg = (const bf16*)p.R + (int64_t)row * p.ldr + col;
+            const bf16* ru = rg + p.swiglu_I;
+            if (col + 4 <= p.swiglu_I) {
+              const bf16x4 ga = *(const bf16x4*)rg, ua = *(const bf16x4*)ru;
+#pragma unroll
+              for (int e = 0; e < 4; ++e) { v[h][e] += static_cast<float>(ga[e]); u[e] += static_cast<float>(ua[e]); }
+            } else {
+              for (int e = 0; e < 4 && col + e < p.swiglu_I; ++e) {
+                v[h][e] += static_cast<float>(rg[e]);
+                u[e] += static_cast<float>(ru[e]);
+              }
             }
           }
-        }
 #pragma unroll
-        for (int e = 0; e < 4; ++e) v[e] = silu_f(v[e]) * u[e];
-        epi_row4_store<EPI>(p, row, col, p.swiglu_I, v);
+          for (int e = 0; e < 4; ++e) v[h][e] = silu_f(v[h][e]) * u[e];
+        }
+        int coff;
+        const bf16x8 o = pair_to_8(v[0], v[1], c16, coff);
+        if (rok) store8_bf16((bf16*)p.C + (int64_t)row * p.ldc + colp + coff, colp + coff, p.swiglu_I, o);
       }
     }
   } else {
     constexpr bool HAS_R = EPI == EPI_RESID || EPI == EPI_RESID_TO_F32 || EPI == EPI_RESID_FROM_F32 ||
                            EPI == EPI_RESID_F32;
+    constexpr bool PAIR = EPI == EPI_STORE || EPI == EPI_RESID || EPI == EPI_SCALED || EPI == EPI_RESID_FROM_F32;
     const int colw = tn * BN + wn * (BN / WN) + 4 * c16;
     f32x4 rn[NB16];
     auto load_r = [&](int a) {
@@ -781,14 +821,24 @@ __global__ __launch_bounds__(64 * NW, 1) void gemm_fast_kernel(GemmParams p, int
       for (int b = 0; b < NB16; ++b) rc[b] = rn[b];
       if (a + 1 < 8) load_r(a + 1);
       const int r = wm * 128 + a * 16 + r16;
-      if (r >= rows) continue;
+      const bool rok = r < rows;
+      float v[NB16][4];
 #pragma unroll
-      for (int b = 0; b < NB16; ++b) {
-        float v[4];
+      for (int b = 0; b < NB16; ++b)
 #pragma unroll
         for (int e = 0; e < 4; ++e)
-          v[e] = EPI == EPI_SCALED ? acc[a][b][e] * p.scale : HAS_R ? acc[a][b][e] + rc[b][e] : acc[a][b][e];
-        epi_row4_store<EPI>(p, row0 + r, colw + 16 * b, p.N, v);
+          v[b][e] = EPI == EPI_SCALED ? acc[a][b][e] * p.scale : HAS_R ? acc[a][b][e] + rc[b][e] : acc[a][b][e];
+      if (PAIR) {
+#pragma unroll
+        for (int b = 0; b < NB16; b += 2) {
+          const int colp = tn * BN + wn * (BN / WN) + 16 * b;
+          int coff;
+          const bf16x8 o = pair_to_8(v[b], v[b + 1], c16, coff);
+          if (rok) store8_bf16((bf16*)p.C + (int64_t)(row0 + r) * p.ldc + colp + coff, colp + coff, p.N, o);
+        }
+      } else if (rok) {
+#pragma unroll
+        for (int b = 0; b < NB16; ++b) epi_row4_store<EPI>(p, row0 + r, colw + 16 * b, p.N, v[b]);
       }
     }
   }

@@ -63,6 +63,31 @@ def test_linear(lib, dtype, M, N, K, epi):
         assert err <= BLOCK_TOL_F32
 
 
+@pytest.mark.parametrize("M,N,K", [(2000, 8104, 1024), (2000, 8104, 512), (2000, 9000, 256), (600, 4000, 64)])
+def test_linear_swiglu_many_tiles(lib, M, N, K):
+    """SwiGLU launches with more 256 x 128 output tiles than the chip has CUs (512, and 568: an
+    uneven number per CU), so one workgroup runs several tiles and a tile's outputs are stored
+    while the next tile's first k-tiles load; with K = 512 and 256 the k range is too short to
+    carry all of them, with K = 64 a single k-tile carries none.  Ragged last rows (2000 = 7 x 256
+    + 208) and columns (8104 = 63 x 128 + 40).  Sampled rows, among them every tile's first and
+    last, against the oracle at the bf16 rounding bound."""
+    import torch
+    log(f"linear swiglu M={M} N={N} K={K}")
+    x = rnd(f"sx{M}{K}", (M, K), 1.0)
+    w = rnd(f"sw{N}{K}", (2 * N, K), 0.05)
+    y = dev(np.full((M, N), np.nan, np.float32), "bf16")
+    lib.op_linear(dev(x, "bf16"), dev(w, "bf16"), y, None, 2)
+    torch.cuda.synchronize()
+    got = host(y)
+    assert np.isfinite(got).all()                      # every output written
+    rows = sorted(set([r for t in range(0, M, 256) for r in (t, min(t + 255, M - 1))] +
+                      list(np.random.default_rng(M + N + K).integers(0, M, 24))))
+    ref = O.swiglu(O.linear(x[rows], w[:N]), O.linear(x[rows], w[N:]))
+    f = bf16_faithful(got[rows], ref)
+    log(f"  {len(rows)} rows: bf16-rounding units={f:.3f}")
+    assert f <= 1.0
+
+
 def test_linear_resid_in_place(lib):
     import torch
     M, N, K = 260, 256, 192
