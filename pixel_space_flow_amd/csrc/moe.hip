@@ -14,33 +14,29 @@ namespace {
 // Router over a tile of RT tokens per workgroup.  With a gain g the logits are those of the
 // RMS-normalised row, computed in one pass over x in fp32:
 //   logit[t, e] = rs_t sum_c x[t, c] (g[c] w[e, c]),  rs_t = 1 / sqrt(mean_c x[t, c]^2 + eps)
-// (g == nullptr: logit = sum_c x[t, c] w[e, c], x already normalised).  256-column chunks of x
-// and of g w are staged in LDS as fp32, the next chunk's values loaded into registers while the
-// current one is consumed; thread (t, eq) accumulates token t = tid % 16 against experts
-// eq + 16 j (eq = tid / 16, j < EJ).  Then one wave per token: softmax, top-k by repeated wave
-// argmax of the logit (the softmax is monotone; ties to the lower expert index), weights
-// renormalised over the k, and each assignment's stable rank among the workgroup's assignments
-// of the same expert (assignment order t k + slot) with the workgroup's per-expert counts, so
-// that the sort needs no second pass over the assignments.
+// (g == nullptr: logit = sum_c x[t, c] w[e, c], x already normalised).  The contraction runs on
+// the fp32 matrix instruction v_mfma_f32_16x16x4_f32 (fp32 products and sums): the four waves
+// take contiguous quarters of the D columns, each wave a 16-token x 16-expert block per expert
+// block j (EJ blocks), with lane l holding token l % 16 of A and expert 16 j + l % 16 of B for the
+// columns 4 (l / 16) + q of each 16-column group (the same column order on both operands, so the
+// sum is the plain dot product in another order); x, g and w come in by batches of column
+// groups.  The four quarters' partial sums meet in LDS and are added in a fixed order.  Then one
+// wave per token: softmax, the top-k by rank (ties to the lower expert index; the softmax is
+// monotone, so the order of the logits is that of the probabilities), weights renormalised over
+// the k, and each assignment's stable rank among the workgroup's assignments of the same expert
+// (assignment order t k + slot) with the workgroup's per-expert counts, so that the sort needs no
+// second pass over the assignments.
 constexpr int RT = 16;          // tokens per router workgroup
-constexpr int RCH = 256;        // columns per staged chunk
-constexpr int RST = RCH + 4;    // padded fp32 row stride (1040 B: 16 consecutive rows hit 16 distinct 16-byte slots)
 
-// 16 consecutive elements (16-byte aligned) as floats
-DEVI void load16(const float* p, float* f) {
-#pragma unroll
-  for (int q = 0; q < 4; ++q) {
-    const float4 v = *(const float4*)(p + 4 * q);
-    f[4 * q] = v.x; f[4 * q + 1] = v.y; f[4 * q + 2] = v.z; f[4 * q + 3] = v.w;
-  }
+// 4 consecutive elements (aligned to their size) as floats
+DEVI void load4(const float* p, float* f) {
+  const float4 v = *(const float4*)p;
+  f[0] = v.x; f[1] = v.y; f[2] = v.z; f[3] = v.w;
 }
-DEVI void load16(const bf16* p, float* f) {
+DEVI void load4(const bf16* p, float* f) {
+  const bf16x4 v = *(const bf16x4*)p;
 #pragma unroll
-  for (int q = 0; q < 2; ++q) {
-    const bf16x8 v = *(const bf16x8*)(p + 8 * q);
-#pragma unroll
-    for (int e = 0; e < 8; ++e) f[8 * q + e] = static_cast<float>(v[e]);
-  }
+  for (int e = 0; e < 4; ++e) f[e] = static_cast<float>(v[e]);
 }
 
 template <typename Tx, typename Tw, int EJ>
@@ -48,116 +44,117 @@ __global__ __launch_bounds__(256) void route_kernel(const Tx* __restrict__ x, co
                                                     const Tw* __restrict__ wr, int T_, int D, int E, int k,
                                                     int* __restrict__ idx, float* __restrict__ w,
                                                     int* __restrict__ lrank, int* __restrict__ blkcnt) {
-  __shared__ __attribute__((aligned(16))) float xs[RT * RST];
-  __shared__ __attribute__((aligned(16))) float gw[16 * EJ * RST];
+  __shared__ float part[4][RT][65];
+  __shared__ float ssw[4][RT];
   __shared__ float lg[RT * 65];
   __shared__ float rs[RT];
   __shared__ int sel[RT * 64];
+  __shared__ float psel[RT * 64];
   __shared__ int cnt[64], wtot[4][64];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int tq = tid & 15, eq = tid >> 4;
+  const int li = lane & 15, kq = lane >> 4;
   const int t0 = blockIdx.x * RT;
-  float acc[EJ];
+  // D is a multiple of 64: each wave owns D / 64 groups of 16 columns, from column c_begin
+  const int ng = D / 64;
+  const int c_begin = wave * ng * 16 + 4 * kq;
+  const Tx* xrow = x + (int64_t)min(t0 + li, T_ - 1) * D + c_begin;   // rows past T_ read row T_ - 1
+  const Tw* grow = g ? g + c_begin : nullptr;
+  const Tw* wrow[EJ];
+  bool wok[EJ];
 #pragma unroll
-  for (int j = 0; j < EJ; ++j) acc[j] = 0.f;
-  float ss = 0.f;
-  // staging roles: x row eq and g w rows eq + 16 j, columns 16 tq .. 16 tq + 15 of each chunk
-  const Tx* xrow = x + (int64_t)min(t0 + eq, T_ - 1) * D + 16 * tq;
-  float xn[16], wn[EJ][16], gn[16];
-  // a thread's 16 columns lie wholly inside or wholly past D (D is a multiple of 16); past it
-  // they stage as zeros
-  auto fetch = [&](int c0) {
-    const bool in = c0 + 16 * tq < D;
-    if (in) load16(xrow + c0, xn);
-    else
-#pragma unroll
-      for (int q = 0; q < 16; ++q) xn[q] = 0.f;
-    if (g && in) load16(g + c0 + 16 * tq, gn);
-#pragma unroll
-    for (int j = 0; j < EJ; ++j) {
-      const int e = eq + 16 * j;
-      if (e < E && in) load16(wr + (int64_t)e * D + c0 + 16 * tq, wn[j]);
-      else
-#pragma unroll
-        for (int q = 0; q < 16; ++q) wn[j][q] = 0.f;
-    }
-  };
-  fetch(0);
-  for (int c0 = 0; c0 < D; c0 += RCH) {
-#pragma unroll
-    for (int q = 0; q < 16; ++q) ss += xn[q] * xn[q];
-#pragma unroll
-    for (int q = 0; q < 4; ++q)
-      *(float4*)(xs + eq * RST + 16 * tq + 4 * q) = make_float4(xn[4 * q], xn[4 * q + 1], xn[4 * q + 2], xn[4 * q + 3]);
-#pragma unroll
-    for (int j = 0; j < EJ; ++j) {
-      float f[16];
-#pragma unroll
-      for (int q = 0; q < 16; ++q) f[q] = g ? gn[q] * wn[j][q] : wn[j][q];
-#pragma unroll
-      for (int q = 0; q < 4; ++q)
-        *(float4*)(gw + (eq + 16 * j) * RST + 16 * tq + 4 * q) = make_float4(f[4 * q], f[4 * q + 1], f[4 * q + 2], f[4 * q + 3]);
-    }
-    __syncthreads();
-    if (c0 + RCH < D) fetch(c0 + RCH);      // the next chunk's loads run under this chunk's FMAs
-#pragma unroll 8
-    for (int c = 0; c < RCH; c += 4) {
-      const float4 xv = *(const float4*)(xs + tq * RST + c);
-#pragma unroll
-      for (int j = 0; j < EJ; ++j) {
-        const float4 wv = *(const float4*)(gw + (eq + 16 * j) * RST + c);
-        float a = acc[j];
-        a = fmaf(xv.x, wv.x, a);
-        a = fmaf(xv.y, wv.y, a);
-        a = fmaf(xv.z, wv.z, a);
-        a = fmaf(xv.w, wv.w, a);
-        acc[j] = a;
-      }
-    }
-    __syncthreads();
+  for (int j = 0; j < EJ; ++j) {
+    const int e = 16 * j + li;
+    wok[j] = e < E;
+    wrow[j] = wr + (int64_t)(wok[j] ? e : 0) * D + c_begin;           // experts past E contribute zero
   }
-  // row sums of squares of row eq: its 16 staging lanes are consecutive
+  auto fetch = [&](int off, float (&xo)[4], float (&go)[4], float (&wo)[EJ][4]) {
+    load4(xrow + off, xo);
+    if (g) load4(grow + off, go);
 #pragma unroll
-  for (int o = 8; o > 0; o >>= 1) ss += __shfl_xor(ss, o, 64);
-  if (tq == 0) rs[eq] = g ? 1.0f / sqrtf(ss / (float)D + eps) : 1.0f;
-  if (tid < 64) cnt[tid] = 0;
-  __syncthreads();
+    for (int j = 0; j < EJ; ++j) load4(wrow[j] + off, wo[j]);
+  };
+  f32x4 acc[EJ];
+#pragma unroll
+  for (int j = 0; j < EJ; ++j) acc[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+  float ss = 0.f;
+  // batches of NB column groups: all of a batch's loads are issued before its first product, so
+  // one memory latency is paid per batch rather than per group
+  constexpr int NB = EJ <= 2 ? 8 : 4;
+  for (int i0 = 0; i0 < ng; i0 += NB) {
+    float xb[NB][4], gb[NB][4], wb[NB][EJ][4];
+#pragma unroll
+    for (int u = 0; u < NB; ++u)
+      if (i0 + u < ng) fetch(16 * (i0 + u), xb[u], gb[u], wb[u]);
+#pragma unroll
+    for (int u = 0; u < NB; ++u)
+      if (i0 + u < ng) {
+#pragma unroll
+        for (int q = 0; q < 4; ++q) ss += xb[u][q] * xb[u][q];
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+#pragma unroll
+          for (int j = 0; j < EJ; ++j) {
+            const float bw = wok[j] ? (g ? gb[u][q] * wb[u][j][q] : wb[u][j][q]) : 0.f;
+            acc[j] = __builtin_amdgcn_mfma_f32_16x16x4f32(xb[u][q], bw, acc[j], 0, 0, 0);
+          }
+      }
+  }
+  // lanes li + 16 kq (kq = 0..3) hold partial sums of squares of token li
+  ss += __shfl_xor(ss, 16, 64);
+  ss += __shfl_xor(ss, 32, 64);
+  if (kq == 0) ssw[wave][li] = ss;
+  // block j of lane l: tokens 4 (l / 16) + r, expert 16 j + l % 16
 #pragma unroll
   for (int j = 0; j < EJ; ++j)
-    if (eq + 16 * j < E) lg[tq * 65 + eq + 16 * j] = acc[j] * rs[tq];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) part[wave][4 * kq + r][16 * j + li] = acc[j][r];
+  if (tid < 64) cnt[tid] = 0;
   __syncthreads();
-  // one wave per token: softmax, top-k, renormalised weights
+  if (tid < RT) {
+    const float tot = ssw[0][tid] + ssw[1][tid] + ssw[2][tid] + ssw[3][tid];
+    rs[tid] = g ? 1.0f / sqrtf(tot / (float)D + eps) : 1.0f;
+  }
+  __syncthreads();
+  for (int i = tid; i < RT * 64; i += 256) {
+    const int tk = i >> 6, e = i & 63;
+    if (e < E) lg[tk * 65 + e] = (((part[0][tk][e] + part[1][tk][e]) + part[2][tk][e]) + part[3][tk][e]) * rs[tk];
+  }
+  __syncthreads();
+  // one wave per token, lane e for expert e: every lane reads the token's E logits from LDS (the
+  // same address across the wave, a broadcast) and finds in-lane the max, the softmax denominator
+  // and its own expert's rank: the number of experts before it in the order "larger logit first,
+  // ties to the lower index" (NaN below every number).  The top-k are the ranks below k; the
+  // weights are renormalised by the sum of the k probabilities taken in rank order.
+  auto order_key = [](float v) {
+    const int b = __float_as_int(v);
+    return __builtin_isnan(v) ? INT_MIN + 1 : max(b >= 0 ? b : b ^ 0x7fffffff, INT_MIN + 1);
+  };
   for (int r = wave; r < RT; r += 4) {
     const int t = t0 + r;
-    const float logit = lane < E ? lg[r * 65 + lane] : -INFINITY;
-    const float mx = warp_max(logit);
-    const float ex = lane < E ? expf(logit - mx) : 0.f;
-    const float p = ex / warp_sum(ex);
-    // selection key: the logit's order as a signed integer (NaN lowest among the experts, an
-    // expert already taken and the lanes past E below every expert), so that the k rounds always
-    // pick k distinct experts
-    int key = INT_MIN;
-    if (lane < E) {
-      const int b = __float_as_int(logit);
-      key = __builtin_isnan(logit) ? INT_MIN + 1 : max(b >= 0 ? b : b ^ 0x7fffffff, INT_MIN + 1);
+    const float* lr = lg + r * 65;
+    const float logit = lane < E ? lr[lane] : 0.f;
+    const int key = order_key(logit);
+    float mx = -INFINITY;
+    int rank = 0;
+    for (int e = 0; e < E; ++e) {
+      const float v = lr[e];
+      mx = fmaxf(mx, v);
+      const int ke = order_key(v);
+      rank += (ke > key || (ke == key && e < lane)) ? 1 : 0;
     }
+    float den = 0.f;
+    for (int e = 0; e < E; ++e) den += expf(lr[e] - mx);
+    const float p = expf(logit - mx) / den;
+    const bool chosen = lane < E && rank < k;
+    if (chosen) psel[r * 64 + rank] = p;
+    __builtin_amdgcn_s_waitcnt(0xc07f);       // this wave's LDS writes, read back below by other lanes
+    __builtin_amdgcn_wave_barrier();
     float selsum = 0.f;
-    int my_rank = -1;
-    for (int j = 0; j < k; ++j) {
-      int bv = key, bi = lane;
-#pragma unroll
-      for (int o = 32; o > 0; o >>= 1) {
-        const int ov = __shfl_xor(bv, o, 64);
-        const int oi = __shfl_xor(bi, o, 64);
-        if (ov > bv || (ov == bv && oi < bi)) { bv = ov; bi = oi; }
-      }
-      if (lane == bi) { my_rank = j; key = INT_MIN; }
-      selsum += __shfl(p, bi, 64);
-    }
-    if (my_rank >= 0) sel[r * k + my_rank] = t < T_ ? lane : -1;
-    if (t < T_ && my_rank >= 0) {
-      idx[(int64_t)t * k + my_rank] = lane;
-      w[(int64_t)t * k + my_rank] = p / selsum;
+    for (int j = 0; j < k; ++j) selsum += psel[r * 64 + j];
+    if (chosen) sel[r * k + rank] = t < T_ ? lane : -1;
+    if (t < T_ && chosen) {
+      idx[(int64_t)t * k + rank] = lane;
+      w[(int64_t)t * k + rank] = p / selsum;
     }
   }
   if (!lrank) return;
