@@ -1239,12 +1239,13 @@ bool long_k_ring(const GemmParams& p) {
   return p.K >= 8192 && (aliased(p.lda) || aliased(p.ldb));
 }
 
-// The 64-deep kernel for SwiGLU and for plain launches but long-k ones with aliased row pitches;
-// the 32-deep ring kernel for those, split-K partial products and the expert GEMMs.
+// The 64-deep kernel for SwiGLU, for the grouped expert GEMMs and for plain launches but long-k
+// ones with aliased row pitches; the 32-deep ring kernel for those, split-K partial products and
+// row-gathered launches outside the expert groups.
 template <bool GROUPED, bool GATHER>
 hipError_t launch_fast(const GemmParams& p, int epi, int grid, int n_col_tiles, hipStream_t s) {
   const size_t lds = 2 * STAGE_BYTES;
-  const bool ring = GROUPED || GATHER || long_k_ring(p);
+  const bool ring = (GATHER && !GROUPED) || long_k_ring(p);
 #define PSF_L(E)                                                                                  \
   case E: {                                                                                        \
     if (E != EPI_SWIGLU && (E == EPI_PARTIAL_F32 || ring)) {                                       \
