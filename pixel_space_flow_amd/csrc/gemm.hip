@@ -1400,19 +1400,43 @@ bool k32_ext_ok(const GemmParams& p, int epi) {
   return true;
 }
 
-// Number of k-ranges for a plain GEMM whose row x column tiles leave most CUs idle (0 = unsplit).
+// Compute units of the current device (one workgroup of the fast GEMMs per CU).
+int device_cus() {
+  static const int n = [] {
+    int dev = 0, v = 0;
+    if (hipGetDevice(&dev) != hipSuccess || hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+      return 256;
+    return v > 0 ? v : 256;
+  }();
+  return n;
+}
+
+// Number of k-ranges for a plain GEMM whose row x column tiles leave CUs idle (0 = unsplit): the
+// split (1, 2 or 4) with the least estimated time, counted in k-columns that one round of tiles
+// streams: rounds x K / ks for the products, plus, for a split, the fp32 partials written and read
+// back (8 ks M N bytes) at the same rate (a 64-deep k-tile takes ~1.5 us, HBM moves ~5 TB/s, so
+// ~117 KB of partials cost as much as one k-column).  A split that adds a round of tiles never
+// pays; one that fills idle CUs does unless its partials outweigh the depth it saves.
 int splitk_choice(const GemmParams& p, int epi, int tiles) {
   if (!p.part || p.X || p.bmode != 0 || p.a_rows || p.N % 4) return 0;
   if (epi != EPI_STORE && epi != EPI_RESID && epi != EPI_SCALED && epi != EPI_RESID_F32 && epi != EPI_RESID_TO_F32 &&
       epi != EPI_RESID_FROM_F32)
     return 0;
-  if (tiles >= 160) return 0;
-  for (int ks = 4; ks >= 2; --ks) {
+  const int n_cu = device_cus();
+  if (tiles >= n_cu) return 0;
+  double best = (double)p.K;                       // unsplit: one round
+  int best_ks = 0;
+  for (int ks = 2; ks <= 4; ks *= 2) {
     if (p.K % (32 * ks) || p.K / ks < 512) continue;
     if ((size_t)ks * p.M * p.N > p.part_floats) continue;
-    return ks;
+    const double rounds = (double)((tiles * ks + n_cu - 1) / n_cu);
+    const double cost = rounds * (p.K / ks) + 8.0 * ks * (double)p.M * p.N / 117000.0;
+    if (cost < best) {
+      best = cost;
+      best_ks = ks;
+    }
   }
-  return 0;
+  return best_ks;
 }
 
 hipError_t gemm_bf16(const GemmParams& p, int epi, hipStream_t s) {
