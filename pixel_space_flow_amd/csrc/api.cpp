@@ -379,12 +379,8 @@ int run_block(const gen_block_dims& d, const gen_block_weights& w, TH* hidden, c
   if (kcache) {
     // prefix forward: normalise and rotate q, k in place, hand k and v to the cache, causal attention
     HIP_TRY(qknorm_rope<T>(qkv, QKV, si, Hq, Hkv, hd, (const T*)w.g_q, (const T*)w.g_k, rope, d.rms_eps, s));
-    const size_t row = (size_t)Hkv * hd * sizeof(T), pitch = (size_t)QKV * sizeof(T);
-    for (int b = 0; b < B; ++b) {
-      const T* src = qkv + (size_t)b * N * QKV + QD;
-      HIP_TRY(hipMemcpy2DAsync(kcache[b], row, src, pitch, row, N, hipMemcpyDeviceToDevice, s));
-      HIP_TRY(hipMemcpy2DAsync(vcache[b], row, src + (size_t)Hkv * hd, pitch, row, N, hipMemcpyDeviceToDevice, s));
-    }
+    // the cache pointers are 16-byte aligned (checked at the boundary)
+    HIP_TRY(kv_cache_write<T>(qkv, QKV, QD, N, Hkv * hd, B, kcache, vcache, s));
     HIP_TRY(pack_kv<T>(qkv, QKV, si, Hq, Hkv, hd, L.Lpad, Kc, Vt, s));
     if (sizeof(T) == 2)
       HIP_TRY(attention_bf16((const bf16*)qkv, QKV, si, Hq, Hkv, hd, L.Lpad, (const bf16*)Kc, (const bf16*)Vt,

@@ -424,6 +424,26 @@ __global__ __launch_bounds__(256) void cfg_euler_kernel(float* xo, const float* 
   }
 }
 
+struct KVCacheOut {
+  void* k[MAXB];
+  void* v[MAXB];
+};
+
+// grid (chunk blocks, B, 2): z = 0 copies the keys, z = 1 the values of sequence y
+template <typename T>
+__global__ __launch_bounds__(256) void kv_cache_write_kernel(const T* __restrict__ qkv, int64_t ld, int QD, int N,
+                                                             int row_elems, KVCacheOut out) {
+  constexpr int V = 16 / sizeof(T);
+  const int cpr = row_elems / V;
+  const int64_t c = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (c >= (int64_t)N * cpr) return;
+  const int b = blockIdx.y, which = blockIdx.z;
+  const int n = (int)(c / cpr), ch = (int)(c - (int64_t)n * cpr);
+  const T* src = qkv + ((int64_t)b * N + n) * ld + QD + which * row_elems + ch * V;
+  T* dst = (T*)(which ? out.v[b] : out.k[b]) + (int64_t)n * row_elems + ch * V;
+  *(u32x4*)dst = *(const u32x4*)src;
+}
+
 }  // namespace
 
 // ================================================================== launchers
@@ -464,6 +484,25 @@ hipError_t qknorm_rope(T* qkv, int64_t ld, const SeqInfo& si, int Hq, int Hkv, i
 }
 template hipError_t qknorm_rope<bf16>(bf16*, int64_t, const SeqInfo&, int, int, int, const bf16*, const bf16*, const float2*, float, hipStream_t, bf16*);
 template hipError_t qknorm_rope<float>(float*, int64_t, const SeqInfo&, int, int, int, const float*, const float*, const float2*, float, hipStream_t, float*);
+
+template <typename T>
+hipError_t kv_cache_write(const T* qkv, int64_t ld, int QD, int N, int row_elems, int B, void* const* kcache,
+                          void* const* vcache, hipStream_t s) {
+  constexpr int V = 16 / sizeof(T);
+  if (B <= 0 || N <= 0) return hipSuccess;
+  if (B > MAXB || row_elems % V || QD % V || ld % V) return hipErrorInvalidValue;
+  KVCacheOut out;
+  for (int b = 0; b < B; ++b) {
+    out.k[b] = kcache[b];
+    out.v[b] = vcache[b];
+  }
+  const int64_t chunks = (int64_t)N * (row_elems / V);
+  hipLaunchKernelGGL(kv_cache_write_kernel<T>, dim3((unsigned)((chunks + 255) / 256), B, 2), dim3(256), 0, s, qkv, ld,
+                     QD, N, row_elems, out);
+  return hipGetLastError();
+}
+template hipError_t kv_cache_write<bf16>(const bf16*, int64_t, int, int, int, int, void* const*, void* const*, hipStream_t);
+template hipError_t kv_cache_write<float>(const float*, int64_t, int, int, int, int, void* const*, void* const*, hipStream_t);
 
 template <typename T>
 hipError_t pack_kv(const T* qkv, int64_t ld, const SeqInfo& si, int Hq, int Hkv, int d, int Lpad, T* Kc, T* Vt,

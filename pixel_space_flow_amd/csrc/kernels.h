@@ -34,6 +34,14 @@ hipError_t qknorm_rope(T* qkv, int64_t ld, const SeqInfo& si, int Hq, int Hkv, i
 // Pack keys and transposed values of every (sequence, kv head) contiguously:
 //   Kc[b][g][j][:] = j < P_b ? prefix K : (j < P_b + N ? k of token j - P_b : 0)     [B, Hkv, Lpad, d]
 //   Vt[b][g][:][j] = same for V, transposed                                          [B, Hkv, d, Lpad]
+// The prompt pass's hand-off to the caller's cache: for every sequence b, the rows of qkv hold
+// q (QD columns), then k and v (row_elems = Hkv d columns each); k goes to kcache[b] and v to
+// vcache[b], each [N, Hkv, d] dense.  One launch, 16 bytes per thread; every pointer must be
+// 16-byte aligned.
+template <typename T>
+hipError_t kv_cache_write(const T* qkv, int64_t ld, int QD, int N, int row_elems, int B, void* const* kcache,
+                          void* const* vcache, hipStream_t s);
+
 template <typename T>
 hipError_t pack_kv(const T* qkv, int64_t ld, const SeqInfo& si, int Hq, int Hkv, int d, int Lpad, T* Kc, T* Vt,
                    hipStream_t s);
