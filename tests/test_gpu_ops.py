@@ -201,15 +201,19 @@ def test_flow_euler_dual_cfg(lib):
                                rtol=1e-5, atol=1e-5)
 
 
-@pytest.mark.parametrize("T,D,E,k", [(300, 256, 32, 8), (4096, 2048, 32, 8), (17, 128, 6, 2)])
-def test_moe_route_exact_sets(lib, T, D, E, k):
+# experts up to 32 run one instance of the router, 33-64 another (four 16-expert blocks); D = 64
+# gives each of the router's four waves a single 16-column group
+@pytest.mark.parametrize("T,D,E,k,dt", [(300, 256, 32, 8, "bf16"), (4096, 2048, 32, 8, "bf16"), (17, 128, 6, 2, "bf16"),
+                                        (300, 256, 64, 8, "bf16"), (33, 64, 40, 4, "bf16"),
+                                        (300, 512, 48, 6, "f32"), (4096, 2048, 32, 8, "f32")])
+def test_moe_route_exact_sets(lib, T, D, E, k, dt):
     import torch
-    log(f"route T={T} D={D} E={E} k={k}")
-    u = rnd(f"ru{T}{D}", (T, D))
-    wr = rnd(f"rw{E}{D}", (E, D), 1.0 / np.sqrt(D))
+    log(f"route T={T} D={D} E={E} k={k} {dt}")
+    u = rnd(f"ru{T}{D}", (T, D), dtype=dt)
+    wr = rnd(f"rw{E}{D}", (E, D), 1.0 / np.sqrt(D), dtype=dt)
     idx = torch.empty(T, k, dtype=torch.int32, device="cuda")
     wt = torch.empty(T, k, dtype=torch.float32, device="cuda")
-    lib.moe_route(dev(u, "bf16"), dev(wr, "bf16"), k, idx, wt, lib.GEN_BF16)
+    lib.moe_route(dev(u, dt), dev(wr, dt), k, idx, wt, lib.GEN_BF16 if dt == "bf16" else lib.GEN_F32)
     gi, gw = idx.cpu().numpy(), wt.cpu().numpy()
     ridx, rw, p = O.route_topk(u.astype(np.float64), wr.astype(np.float64), k)
     srt = np.sort(p, axis=1)[:, ::-1]
