@@ -171,6 +171,12 @@ int z_pitch(int I, size_t es) {
   return (b > 8192 && b % 8192 == 0 && (b / 8192) % 2 == 1) ? I + (int)(128 / es) : I;
 }
 
+// Row pitch (bf16 elements) of the training path's long-k GEMM operands (the SwiGLU output z and
+// the gate/up gradient with the transposed gate/up weight): rows a multiple of 8 KiB apart get 64
+// elements of padding, so those products run on the 64-deep kernel at a pitch that loads at full
+// speed.
+int train_pitch(int n) { return ((size_t)n * 2) % 8192 == 0 ? n + 64 : n; }
+
 struct Ws {
   size_t hidden, patches, u, qkv, attn, kc, vt, z, rope, temb, h1, x0, lora_t, hmid, skinny, lora_gu, lora_f32;
   size_t splitk, splitk_floats;
@@ -550,7 +556,7 @@ Wact layout_act(const gen_block_dims& d, int B, int N) {
   w.xmid = take(M * D * 4);
   w.u2 = take(M * D * 2);
   w.gu = take(M * 2 * I * 2);
-  w.z = take(M * I * 2);
+  w.z = take(M * (size_t)train_pitch((int)I) * 2);
   w.t_qkv = take(M * 3 * r * 2);
   w.t_o = take(M * r * 2);
   w.t_gu = take(M * 2 * r * 2);
@@ -584,7 +590,7 @@ Wb layout_bwd(const gen_block_dims& d, int B, int N, int max_prefix, bool with_a
   w.tp = take(M * 3 * r * 2);
   w.dyb = take(M * D * 2);
   w.dz = take(M * I * 2);
-  w.dgu = take(M * 2 * I * 2);
+  w.dgu = take(M * (size_t)train_pitch((int)(2 * I)) * 2);
   w.du = take(M * D * 2);
   w.dxf = take(M * D * 4);
   w.dO = take(M * QD * 2);
@@ -592,7 +598,7 @@ Wb layout_bwd(const gen_block_dims& d, int B, int N, int max_prefix, bool with_a
   w.dk = take(M * KVD * 4);
   w.dv = take(M * KVD * 4);
   w.dqkv = take(M * QKV * 2);
-  w.wt = take(std::max(std::max(QKV * D, QD * D), std::max(2 * I * D, I * D)) * 2);
+  w.wt = take(std::max(std::max(QKV * D, QD * D), std::max((size_t)train_pitch((int)(2 * I)) * D, I * D)) * 2);
   w.xb = take(((size_t)D * 3 + QD + (size_t)D * 2 + I) * r * 2);   // A^T of the qkv, o, gate/up, down groups
   w.bt = take((size_t)r * (QKV + D + 2 * I + D) * 2);               // B^T of every site
   w.lf = take(r ? M * std::max(std::max(QKV, 2 * I), std::max(D, QD)) * 4 : 0);
@@ -666,8 +672,9 @@ int lora_back(const gen_block_dims& d, const gen_block_weights& w, const BackSit
 // toff[i] of t), dA_site += tp_slot^T x.
 int lora_wgrad(const gen_block_dims& d, const gen_lora_grads& g, const BackSite* sites, int ns, const int* slot, int n,
                const bf16* dY, int lddy, const bf16* t, int ldt, const int* toff, const bf16* tp, const bf16* x, int in,
-               int M, float* part, hipStream_t s) {
+               int M, float* part, hipStream_t s, int ldx = 0) {
   const int r = d.lora_rank;
+  if (ldx == 0) ldx = in;                        // row pitch of x (in columns are used)
   // B gradients: a complete group whose sites sit side by side in dY and in t as one block-diagonal
   // pass, else site by site
   bool diag = n == ns && ns >= 2;
@@ -694,11 +701,11 @@ int lora_wgrad(const gen_block_dims& d, const gen_lora_grads& g, const BackSite*
     float* dst[3] = {nullptr, nullptr, nullptr};
     for (int i = 0; i < ns; ++i)
       if (slot[i] >= 0) dst[slot[i]] = g.lora_a[sites[i].site];
-    HIP_TRY(wgrad_seg(tp, n * r, x, in, M, n * r, in, r, dst, part, s));
+    HIP_TRY(wgrad_seg(tp, n * r, x, ldx, M, n * r, in, r, dst, part, s));
     return GEN_OK;
   }
   for (int i = 0; i < ns; ++i)
-    if (slot[i] >= 0) HIP_TRY(wgrad(tp + slot[i] * r, n * r, x, in, M, r, in, g.lora_a[sites[i].site], part, s));
+    if (slot[i] >= 0) HIP_TRY(wgrad(tp + slot[i] * r, n * r, x, ldx, M, r, in, g.lora_a[sites[i].site], part, s));
   return GEN_OK;
 }
 
@@ -785,12 +792,13 @@ int block_train_fwd(const gen_block_dims& d, const gen_block_weights& w, const f
     }
     HIP_TRY(timed(FAM_GATE_UP, s, [&] { return gemm_bf16(p, epi, s); }));
   }
-  HIP_TRY(swiglu_fwd(gu, z, M, I, s));
-  if (lora) HIP_TRY(lora_down<bf16>(d, w, down_site, 1, z, I, M, t_down, off_down, ld_down, s, part));
+  const int LZ = train_pitch(I);
+  HIP_TRY(swiglu_fwd(gu, z, LZ, M, I, s));
+  if (lora) HIP_TRY(lora_down<bf16>(d, w, down_site, 1, z, I, M, t_down, off_down, ld_down, s, part, LZ));
 
   if (h_out) {  // down projection onto the mid-block residual: the block output
     GemmParams p = gp();
-    p.A = z; p.lda = I; p.B = w.w_down; p.ldb = ld_down_of(d, w); p.M = M; p.N = D; p.K = I;
+    p.A = z; p.lda = LZ; p.B = w.w_down; p.ldb = ld_down_of(d, w); p.M = M; p.N = D; p.K = I;
     p.C = h_out; p.ldc = D; p.R = xmid; p.ldr = D;
     bool ext = false;
     if (off_down[0] >= 0) ext = try_k32_ext(p, EPI_RESID_F32, d, w, down_site, 1, &D, t_down, ld_down, off_down);
@@ -895,21 +903,23 @@ int block_train_bwd(const gen_block_dims& d, const gen_block_weights& w, const f
     if (n < 0) return n;
     HIP_TRY(gemm_bf16(p, p.R ? EPI_RESID_FROM_F32 : EPI_STORE, s));
     if (n > 0) {
-      int rc = lora_wgrad(d, g, bs, 1, slot, n, dyb, D, t_down, ld_down, off_down, tp, z, I, M, part, s);
+      int rc = lora_wgrad(d, g, bs, 1, slot, n, dyb, D, t_down, ld_down, off_down, tp, z, I, M, part, s,
+                          train_pitch(I));
       if (rc) return rc;
     }
   }
-  HIP_TRY(swiglu_bwd(gu, dz, dgu, M, I, s));
+  const int LG = train_pitch(2 * I);
+  HIP_TRY(swiglu_bwd(gu, dz, dgu, LG, M, I, s));
   {  // gate/up: du2 = dgate W_gate + dup W_up (+ LoRA)
     const BackSite bs[2] = {{4, 0, I}, {5, I, I}};
     GemmParams p = gp();
-    HIP_TRY(transpose_bf16((const bf16*)w.w_gate_up, D, wt, 2 * I, 2 * I, D, s));
-    p.A = dgu; p.lda = 2 * I; p.B = wt; p.ldb = 2 * I; p.M = M; p.N = D; p.K = 2 * I; p.C = du; p.ldc = D;
-    n = lora_back(d, w, bs, 2, dgu, 2 * I, D, M, tp, xb_gu, bt, p, slot, part, lf, s, bts_gu);
+    HIP_TRY(transpose_bf16((const bf16*)w.w_gate_up, D, wt, LG, 2 * I, D, s));
+    p.A = dgu; p.lda = LG; p.B = wt; p.ldb = LG; p.M = M; p.N = D; p.K = 2 * I; p.C = du; p.ldc = D;
+    n = lora_back(d, w, bs, 2, dgu, LG, D, M, tp, xb_gu, bt, p, slot, part, lf, s, bts_gu);
     if (n < 0) return n;
     HIP_TRY(gemm_bf16(p, p.R ? EPI_RESID_FROM_F32 : EPI_STORE, s));
     if (n > 0) {
-      int rc = lora_wgrad(d, g, bs, 2, slot, n, dgu, 2 * I, t_gu, ld_gu, off_gu, tp, u2, D, M, part, s);
+      int rc = lora_wgrad(d, g, bs, 2, slot, n, dgu, LG, t_gu, ld_gu, off_gu, tp, u2, D, M, part, s);
       if (rc) return rc;
     }
   }

@@ -186,18 +186,20 @@ __global__ __launch_bounds__(256) void rmsnorm_bwd4_kernel(const float* __restri
   }
 }
 
-// z[m, j] = silu(gu[m, j]) gu[m, I + j]
-__global__ __launch_bounds__(256) void swiglu_kernel(const bf16* __restrict__ gu, bf16* __restrict__ z, int I, int64_t n) {
+// z[m, j] = silu(gu[m, j]) gu[m, I + j]  (z rows ldz apart)
+__global__ __launch_bounds__(256) void swiglu_kernel(const bf16* __restrict__ gu, bf16* __restrict__ z, int64_t ldz, int I,
+                                                     int64_t n) {
   const int64_t t = (int64_t)blockIdx.x * 256 + threadIdx.x;
   if (t >= n) return;
   const int64_t m = t / I;
   const int j = (int)(t - m * I);
   const float gt = static_cast<float>(gu[m * 2 * I + j]), up = static_cast<float>(gu[m * 2 * I + I + j]);
-  z[t] = static_cast<bf16>(silu_f(gt) * up);
+  z[m * ldz + j] = static_cast<bf16>(silu_f(gt) * up);
 }
 
 // The same for I a multiple of 8: eight columns per thread, 16-byte loads and stores.
-__global__ __launch_bounds__(256) void swiglu8_kernel(const bf16* __restrict__ gu, bf16* __restrict__ z, int I, int64_t n8) {
+__global__ __launch_bounds__(256) void swiglu8_kernel(const bf16* __restrict__ gu, bf16* __restrict__ z, int64_t ldz, int I,
+                                                      int64_t n8) {
   const int64_t t = (int64_t)blockIdx.x * 256 + threadIdx.x;
   if (t >= n8) return;
   const int I8 = I >> 3;
@@ -210,12 +212,12 @@ __global__ __launch_bounds__(256) void swiglu8_kernel(const bf16* __restrict__ g
     const float gt = static_cast<float>(g[e]), up = static_cast<float>(u[e]);
     o[e] = static_cast<bf16>(silu_f(gt) * up);
   }
-  *(bf16x8*)(z + t * 8) = o;
+  *(bf16x8*)(z + m * ldz + j) = o;
 }
 
-// dgu[m, j] = dz up silu'(gate), dgu[m, I + j] = dz silu(gate)
+// dgu[m, j] = dz up silu'(gate), dgu[m, I + j] = dz silu(gate)  (dgu rows ldg apart)
 __global__ __launch_bounds__(256) void swiglu_bwd_kernel(const bf16* __restrict__ gu, const bf16* __restrict__ dz,
-                                                         bf16* __restrict__ dgu, int I, int64_t n) {
+                                                         bf16* __restrict__ dgu, int64_t ldg, int I, int64_t n) {
   const int64_t t = (int64_t)blockIdx.x * 256 + threadIdx.x;
   if (t >= n) return;
   const int64_t m = t / I;
@@ -223,13 +225,13 @@ __global__ __launch_bounds__(256) void swiglu_bwd_kernel(const bf16* __restrict_
   const float gt = static_cast<float>(gu[m * 2 * I + j]), up = static_cast<float>(gu[m * 2 * I + I + j]);
   const float d = static_cast<float>(dz[t]);
   const float s = 1.0f / (1.0f + __expf(-gt));
-  dgu[m * 2 * I + j] = static_cast<bf16>(d * up * (s + gt * s * (1.0f - s)));
-  dgu[m * 2 * I + I + j] = static_cast<bf16>(d * gt * s);
+  dgu[m * ldg + j] = static_cast<bf16>(d * up * (s + gt * s * (1.0f - s)));
+  dgu[m * ldg + I + j] = static_cast<bf16>(d * gt * s);
 }
 
 // The same for I a multiple of 8: eight columns per thread, 16-byte loads and stores.
 __global__ __launch_bounds__(256) void swiglu8_bwd_kernel(const bf16* __restrict__ gu, const bf16* __restrict__ dz,
-                                                          bf16* __restrict__ dgu, int I, int64_t n8) {
+                                                          bf16* __restrict__ dgu, int64_t ldg, int I, int64_t n8) {
   const int64_t t = (int64_t)blockIdx.x * 256 + threadIdx.x;
   if (t >= n8) return;
   const int I8 = I >> 3;
@@ -245,8 +247,8 @@ __global__ __launch_bounds__(256) void swiglu8_bwd_kernel(const bf16* __restrict
     og[e] = static_cast<bf16>(d * up * (sg + gt * sg * (1.0f - sg)));
     ou[e] = static_cast<bf16>(d * gt * sg);
   }
-  *(bf16x8*)(dgu + m * 2 * I + j) = og;
-  *(bf16x8*)(dgu + m * 2 * I + I + j) = ou;
+  *(bf16x8*)(dgu + m * ldg + j) = og;
+  *(bf16x8*)(dgu + m * ldg + I + j) = ou;
 }
 
 // One wave per (token, head) of the q and k heads: lane p < d/2 holds the rotate-half pair
@@ -977,26 +979,28 @@ hipError_t rmsnorm_bwd(const float* x, const bf16* g, const bf16* dy, const floa
   return hipGetLastError();
 }
 
-hipError_t swiglu_fwd(const bf16* gu, bf16* z, int M, int I, hipStream_t s) {
+hipError_t swiglu_fwd(const bf16* gu, bf16* z, int64_t ldz, int M, int I, hipStream_t s) {
   const int64_t n = (int64_t)M * I;
   if (n <= 0) return hipSuccess;
-  if (I % 8 == 0 && aligned16(gu) && aligned16(z)) {
+  if (ldz < I) return hipErrorInvalidValue;
+  if (I % 8 == 0 && ldz % 8 == 0 && aligned16(gu) && aligned16(z)) {
     const int64_t n8 = n / 8;
-    hipLaunchKernelGGL(swiglu8_kernel, dim3((unsigned)((n8 + 255) / 256)), dim3(256), 0, s, gu, z, I, n8);
+    hipLaunchKernelGGL(swiglu8_kernel, dim3((unsigned)((n8 + 255) / 256)), dim3(256), 0, s, gu, z, ldz, I, n8);
   } else {
-    hipLaunchKernelGGL(swiglu_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, gu, z, I, n);
+    hipLaunchKernelGGL(swiglu_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, gu, z, ldz, I, n);
   }
   return hipGetLastError();
 }
 
-hipError_t swiglu_bwd(const bf16* gu, const bf16* dz, bf16* dgu, int M, int I, hipStream_t s) {
+hipError_t swiglu_bwd(const bf16* gu, const bf16* dz, bf16* dgu, int64_t ldg, int M, int I, hipStream_t s) {
   const int64_t n = (int64_t)M * I;
   if (n <= 0) return hipSuccess;
-  if (I % 8 == 0 && aligned16(gu) && aligned16(dz) && aligned16(dgu)) {
+  if (ldg < 2 * (int64_t)I) return hipErrorInvalidValue;
+  if (I % 8 == 0 && ldg % 8 == 0 && aligned16(gu) && aligned16(dz) && aligned16(dgu)) {
     const int64_t n8 = n / 8;
-    hipLaunchKernelGGL(swiglu8_bwd_kernel, dim3((unsigned)((n8 + 255) / 256)), dim3(256), 0, s, gu, dz, dgu, I, n8);
+    hipLaunchKernelGGL(swiglu8_bwd_kernel, dim3((unsigned)((n8 + 255) / 256)), dim3(256), 0, s, gu, dz, dgu, ldg, I, n8);
   } else {
-    hipLaunchKernelGGL(swiglu_bwd_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, gu, dz, dgu, I, n);
+    hipLaunchKernelGGL(swiglu_bwd_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, gu, dz, dgu, ldg, I, n);
   }
   return hipGetLastError();
 }

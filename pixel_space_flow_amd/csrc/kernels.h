@@ -96,8 +96,10 @@ hipError_t cast_f32_bf16(const float* x, bf16* y, int64_t n, hipStream_t s);
 // also receives bf16(out)
 hipError_t rmsnorm_bwd(const float* x, const bf16* g, const bf16* dy, const float* base, float* out, int rows, int D,
                        float eps, hipStream_t s, bf16* outb = nullptr);
-hipError_t swiglu_fwd(const bf16* gu, bf16* z, int M, int I, hipStream_t s);
-hipError_t swiglu_bwd(const bf16* gu, const bf16* dz, bf16* dgu, int M, int I, hipStream_t s);
+// z = silu(gate) up over gu = [gate | up] (rows 2 I); z rows ldz apart
+hipError_t swiglu_fwd(const bf16* gu, bf16* z, int64_t ldz, int M, int I, hipStream_t s);
+// dgu = [dgate | dup] of z = silu(gate) up (dz rows I, dgu rows ldg apart)
+hipError_t swiglu_bwd(const bf16* gu, const bf16* dz, bf16* dgu, int64_t ldg, int M, int I, hipStream_t s);
 // dqkv = gradient with respect to the raw q, k heads (through RoPE and the per-head norm) and v
 hipError_t qknorm_rope_bwd(const bf16* raw, int64_t ldr, const float* dq, const float* dk, const float* dv,
                            const SeqInfo& si, int Hq, int Hkv, int d, const bf16* gq, const bf16* gk,
