@@ -501,7 +501,7 @@ __global__ __launch_bounds__(64 * NW, 1) void gemm_fast_kernel(GemmParams p, int
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wave / WN, wn = wave % WN;
 
-  int tn, row0, rows, expert = 0;
+  int tn, row0, rows, expert = 0, split = 0;
   if (GROUPED) {
     const int t = blockIdx.x / n_col_tiles;
     tn = blockIdx.x - t * n_col_tiles;
@@ -512,7 +512,9 @@ __global__ __launch_bounds__(64 * NW, 1) void gemm_fast_kernel(GemmParams p, int
   } else {
     const int n_m = (p.M + BM - 1) / BM;
     const int n_t = n_m * n_col_tiles;
-    const int id = xcd_remap(blockIdx.x, n_t);
+    const int idall = xcd_remap(blockIdx.x, n_t * max(p.ksplit, 1));
+    split = idall / n_t;                               // k-range of a split-K launch (else 0)
+    const int id = idall - split * n_t;
     const int GROUP = 8;
     const int per_group = GROUP * n_col_tiles;
     const int g = id / per_group;
@@ -568,8 +570,10 @@ __global__ __launch_bounds__(64 * NW, 1) void gemm_fast_kernel(GemmParams p, int
   }
   const uint32_t bvoff0 = lrow * ldb2 + lch0 * 16, bvoff1 = lrow * ldb2 + lch1 * 16;
 
-  const int KTM = p.K / BK;                      // k-tiles of A B^T
+  const int KTM = p.K / BK / max(p.ksplit, 1);  // k-tiles of A B^T in this launch's k-range
   const int KT = KTM + (EXT ? (p.xk + BK - 1) / BK : 0);
+  const uint32_t kofs = (uint32_t)(split * KTM) * (BK * 2);   // byte offset of the k-range
+  if (EPI == EPI_PARTIAL_F32) p.C = (float*)p.C + (int64_t)split * p.M * p.ldc;
   // K extension: X rows of the tile, and per 8-row group of B its site's up-projection rows
   __amdgpu_buffer_rsrc_t rx, rbx[EXT ? GPW : 1];
   uint32_t ldx2 = 0;
@@ -603,7 +607,7 @@ __global__ __launch_bounds__(64 * NW, 1) void gemm_fast_kernel(GemmParams p, int
       }
       return;
     }
-    const uint32_t kb = (uint32_t)kt * (BK * 2);
+    const uint32_t kb = (uint32_t)kt * (BK * 2) + kofs;
 #pragma unroll
     for (int i = 0; i < GPW; ++i) {
       const int grp = wave * GPW + i;
@@ -626,7 +630,7 @@ __global__ __launch_bounds__(64 * NW, 1) void gemm_fast_kernel(GemmParams p, int
       }
       return;
     }
-    const uint32_t kb = (uint32_t)kt * (BK * 2);
+    const uint32_t kb = (uint32_t)kt * (BK * 2) + kofs;
 #pragma unroll
     for (int i = 0; i < GPW; ++i) {
       const int grp = wave * GPW + i;
@@ -1239,16 +1243,17 @@ bool long_k_ring(const GemmParams& p) {
   return p.K >= 8192 && (aliased(p.lda) || aliased(p.ldb));
 }
 
-// The 64-deep kernel for SwiGLU, for the grouped expert GEMMs and for plain launches but long-k
-// ones with aliased row pitches; the 32-deep ring kernel for those, split-K partial products and
-// row-gathered launches outside the expert groups.
+// The 64-deep kernel for SwiGLU, for the grouped expert GEMMs, for split-K partial products whose
+// k-ranges are whole 64-deep tiles and for plain launches but long-k ones with aliased row pitches;
+// the 32-deep ring kernel for those, the other split-K products and row-gathered launches outside
+// the expert groups.
 template <bool GROUPED, bool GATHER>
 hipError_t launch_fast(const GemmParams& p, int epi, int grid, int n_col_tiles, hipStream_t s) {
   const size_t lds = 2 * STAGE_BYTES;
   const bool ring = (GATHER && !GROUPED) || long_k_ring(p);
 #define PSF_L(E)                                                                                  \
   case E: {                                                                                        \
-    if (E != EPI_SWIGLU && (E == EPI_PARTIAL_F32 || ring)) {                                       \
+    if (E != EPI_SWIGLU && (ring || (E == EPI_PARTIAL_F32 && (p.K / max(p.ksplit, 1)) % BK))) {   \
       auto k = gemm_k32_kernel<E, GROUPED, GATHER>;                                                \
       hipError_t e = hipFuncSetAttribute((const void*)k, hipFuncAttributeMaxDynamicSharedMemorySize, \
                                          (int)lds);                                                \
