@@ -308,10 +308,18 @@ def run_train_bench(psf, w, args):
     plen = [w.prefix_len] * w.batch
     loss = torch.zeros(1, device="cuda")
     ws = psf.alloc_workspace(psf.train_workspace_size(dims, w.n_layers, w.n_img, w.n_tokens, w.prefix_len))
+    # the frozen base weights' transposes for the backward, made once for the run (like loading)
+    ft = psf.alloc_workspace(psf.train_frozen_t_size(dims, w.n_layers))
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    psf.train_frozen_t(dims, layers, ft)
+    e1.record()
+    torch.cuda.synchronize()
+    frozen_t_ms = e0.elapsed_time(e1)
 
     def step():
         flat.zero_()
-        psf.tower_lora_train_step(dims, layers, glob, x_t, x0, sig, pk, pv, plen, gstructs, loss, ws)
+        psf.tower_lora_train_step(dims, layers, glob, x_t, x0, sig, pk, pv, plen, gstructs, loss, ws, frozen_t=ft)
 
     ms, per = time_steps(step, args.steps, args.warmup)
     gu_avg, gu_n = kernel_pass(psf, "gate_up", w.n_layers, step, max(2, min(args.steps, 5)))
@@ -329,7 +337,8 @@ def run_train_bench(psf, w, args):
         "config": {"workload": w.name, "layers": w.n_layers, "samples": w.n_img, "image_px": [w.height, w.width],
                    "image_tokens_per_sample": w.n_tokens, "prefix_tokens": w.prefix_len,
                    "lora": {"rank": r, "alpha": d.lora_alpha, "sites": "q,k,v,o,gate,up,down"},
-                   "loss": float(loss.item())},
+                   "loss": float(loss.item()),
+                   "frozen_transposes": {"bytes": ft.numel(), "once_ms": round(frozen_t_ms, 2)}},
         "pct_bf16_peak": round(100 * tflops / PEAK_BF16_TFLOPS, 2), "tflops": round(tflops, 1),
         "step_tflop": round(fl["total"] / 1e12, 3),
         "roofline": {"kernel": f"forward gate_up GEMM with its LoRA terms, gate and up kept for the backward "

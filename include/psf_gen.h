@@ -234,14 +234,28 @@ size_t gen_train_workspace_size(const gen_block_dims* dims, int n_layers, int n_
  *   grads        HOST [n_layers]
  *   loss         device float32 scalar (written)
  *   x0_pred_out  nullable [n_img, 3, H, W] float32
+ *   frozen_t     nullable: the layers' frozen base weights as the backward's operands, filled by
+ *                gen_train_frozen_t for these same layers (16-byte aligned); with NULL every step
+ *                transposes them again
  * The forward keeps each block's activations in the workspace; the backward reads them.
- * No optimizer update is applied. */
+ * No optimizer update is applied.  Results are the same with and without frozen_t. */
 int gen_tower_lora_train_step(const gen_block_dims* dims, int n_layers, const gen_block_weights* layers,
                               const void* w_in, const void* temb_w1, const void* temb_w2, const void* g_final,
                               const void* w_out, const float* x_t, const float* x0, int n_img, int H, int W,
                               const float* sigma, const void* const* prefix_k, const void* const* prefix_v,
                               const int* prefix_len, const gen_lora_grads* grads, float* loss, float* x0_pred_out,
-                              void* workspace, size_t workspace_bytes, void* stream);
+                              const void* frozen_t, void* workspace, size_t workspace_bytes, void* stream);
+
+/* The base weights stay frozen through LoRA training (sensenova-u1-lora-trainer "Setup notes":
+ * only the adapters train), so the transposed copies the backward's data gradients multiply by can
+ * be made once per training run instead of once per step.  gen_train_frozen_t_size gives the bytes
+ * for n_layers layers of these dims (0 on invalid arguments: the training step's dims rules);
+ * gen_train_frozen_t writes them (bf16, per layer: w_down^T, w_gate_up^T, w_o^T, w_qkv^T) into
+ * frozen_t (caller-owned device memory, 16-byte aligned, >= that size; errors GEN_EINVAL /
+ * GEN_EWORKSPACE).  The copies are valid while the base weights do not change. */
+size_t gen_train_frozen_t_size(const gen_block_dims* dims, int n_layers);
+int gen_train_frozen_t(const gen_block_dims* dims, int n_layers, const gen_block_weights* layers, void* frozen_t,
+                       size_t bytes, void* stream);
 
 /* Dual guidance of an image edit and the Euler update, in place, float32, n elements
  * (vllm-omni recipe "SenseNova-U1.5", img2img: cfg_scale guides toward the instruction,

@@ -24,6 +24,7 @@ EXPORTS = ("gen_block_forward", "gen_block_forward_noalloc", "gen_tower_step", "
            "gen_workspace_size",
            "gen_sigma_schedule", "gen_last_error", "gen_block_lora_merge", "gen_prefix_forward",
            "gen_backward_workspace_size", "gen_block_backward", "gen_train_workspace_size", "gen_tower_lora_train_step",
+           "gen_train_frozen_t_size", "gen_train_frozen_t",
            # include/psf_gen_ops.h
            "gen_op_rmsnorm", "gen_op_linear", "gen_op_qknorm_rope", "gen_op_attention", "gen_op_workspace_size",
            "gen_timing_begin", "gen_timing_end")
@@ -79,7 +80,10 @@ def _load():
     lib.gen_train_workspace_size.argtypes = [P(BlockDimsC), i, i, i, i]
     lib.gen_train_workspace_size.restype = sz
     lib.gen_tower_lora_train_step.argtypes = [P(BlockDimsC), i, P(BlockWeightsC), vp, vp, vp, vp, vp, vp, vp, i, i, i,
-                                              P(f), P(vp), P(vp), P(i), P(LoraGradsC), vp, vp, vp, sz, vp]
+                                              P(f), P(vp), P(vp), P(i), P(LoraGradsC), vp, vp, vp, vp, sz, vp]
+    lib.gen_train_frozen_t_size.argtypes = [P(BlockDimsC), i]
+    lib.gen_train_frozen_t_size.restype = sz
+    lib.gen_train_frozen_t.argtypes = [P(BlockDimsC), i, P(BlockWeightsC), vp, sz, vp]
     lib.gen_prefix_forward.argtypes = [P(BlockDimsC), i, P(BlockWeightsC), vp, i, i, P(vp), P(vp), vp, vp, sz, vp]
     lib.gen_moe_route.argtypes = [vp, vp, i, i, i, i, i, vp, vp, vp]
     lib.gen_workspace_size.argtypes = [P(BlockDimsC), i, i, i, i]
@@ -243,10 +247,24 @@ def block_backward(dims: BlockDimsC, weights: BlockWeightsC, hidden_in, d_hidden
                                   workspace.numel() * workspace.element_size(), _stream(stream)))
 
 
+def train_frozen_t_size(dims: BlockDimsC, n_layers: int) -> int:
+    return lib.gen_train_frozen_t_size(ctypes.byref(dims), n_layers)
+
+
+def train_frozen_t(dims: BlockDimsC, layers: Sequence[BlockWeightsC], frozen_t, stream=None):
+    """The frozen base weights' transposes for the training backward, made once (frozen_t: uint8 device
+    buffer of at least train_frozen_t_size bytes)."""
+    L = len(layers)
+    arr = (BlockWeightsC * L)(*layers)
+    _check(lib.gen_train_frozen_t(ctypes.byref(dims), L, arr, frozen_t.data_ptr(),
+                                  frozen_t.numel() * frozen_t.element_size(), _stream(stream)))
+
+
 def tower_lora_train_step(dims: BlockDimsC, layers: Sequence[BlockWeightsC], glob: dict, x_t, x0, sigma, prefix_k,
                           prefix_v, prefix_len, grads: Sequence[LoraGradsC], loss, workspace, x0_pred_out=None,
-                          stream=None):
-    """One LoRA training step (x0 loss): loss (device fp32 scalar) is written, grads[l] accumulate."""
+                          stream=None, frozen_t=None):
+    """One LoRA training step (x0 loss): loss (device fp32 scalar) is written, grads[l] accumulate.
+    frozen_t: optional buffer filled by train_frozen_t for the same layers."""
     n_img, _, H, W = x_t.shape
     L = len(layers)
     arr = (BlockWeightsC * L)(*layers)
@@ -257,7 +275,7 @@ def tower_lora_train_step(dims: BlockDimsC, layers: Sequence[BlockWeightsC], glo
                                          _ptr(glob["temb_w2"]), _ptr(glob["g_final"]), _ptr(glob["w_out"]),
                                          x_t.data_ptr(), x0.data_ptr(), n_img, H, W, sig, _ptr_array(prefix_k),
                                          _ptr_array(prefix_v), plen, garr, loss.data_ptr(), _ptr(x0_pred_out),
-                                         workspace.data_ptr(), workspace.numel() * workspace.element_size(),
+                                         _ptr(frozen_t), workspace.data_ptr(), workspace.numel() * workspace.element_size(),
                                          _stream(stream)))
 
 

@@ -811,9 +811,31 @@ int block_train_fwd(const gen_block_dims& d, const gen_block_weights& w, const f
 // Gradient of one dense gen block from the activations block_train_fwd kept in `act`.  h: the
 // block input [M, D] fp32; dh: in, dL/d(block output); out, dL/d(block input).  LoRA gradients
 // accumulate into g.
+// The frozen base weights as the backward's data-gradient operands, per layer: W_down^T [I, D],
+// W_gate_up^T [D, train_pitch(2 I)], W_o^T [QD, D], W_qkv^T [D, QKV] (bf16).
+struct FrozenT {
+  size_t down, gu, o, qkv, stride;
+};
+FrozenT frozen_t_layout(const gen_block_dims& d) {
+  FrozenT f{};
+  const size_t D = d.hidden, I = d.mlp_intermediate, QD = (size_t)d.n_q_heads * d.head_dim;
+  const size_t QKV = QD + 2 * (size_t)d.n_kv_heads * d.head_dim;
+  size_t o = 0;
+  auto take = [&](size_t bytes) { size_t a = o; o += up(bytes); return a; };
+  f.down = take(I * D * 2);
+  f.gu = take(D * (size_t)train_pitch((int)(2 * I)) * 2);
+  f.o = take(QD * D * 2);
+  f.qkv = take(D * QKV * 2);
+  f.stride = o;
+  return f;
+}
+
+// ft: nullable, this layer's cached transposes (frozen_t_layout); without them each data-gradient
+// operand is transposed into the scratch wt on the call.
 int block_train_bwd(const gen_block_dims& d, const gen_block_weights& w, const float* h, float* dh,
                     const SeqInfo& si, const gen_lora_grads& g, void* act, void* ws, const Wb& L, hipStream_t s,
-                    bool dyb_ready) {
+                    bool dyb_ready, const char* ft = nullptr) {
+  const FrozenT FT = frozen_t_layout(d);
   const int B = si.B, N = si.N, M = B * N, D = d.hidden, I = d.mlp_intermediate, r = d.lora_rank;
   const int Hq = d.n_q_heads, Hkv = d.n_kv_heads, hd = d.head_dim;
   const int QD = Hq * hd, KVD = Hkv * hd, QKV = QD + 2 * KVD;
@@ -897,8 +919,9 @@ int block_train_bwd(const gen_block_dims& d, const gen_block_weights& w, const f
   {  // down projection: dz = dy W_down (+ LoRA)
     const BackSite bs[1] = {{6, 0, D}};
     GemmParams p = gp();
-    HIP_TRY(transpose_bf16((const bf16*)w.w_down, ld_down_of(d, w), wt, D, D, I, s));
-    p.A = dyb; p.lda = D; p.B = wt; p.ldb = D; p.M = M; p.N = I; p.K = D; p.C = dz; p.ldc = I;
+    const bf16* wdt = ft ? (const bf16*)(ft + FT.down) : wt;
+    if (!ft) HIP_TRY(transpose_bf16((const bf16*)w.w_down, ld_down_of(d, w), wt, D, D, I, s));
+    p.A = dyb; p.lda = D; p.B = wdt; p.ldb = D; p.M = M; p.N = I; p.K = D; p.C = dz; p.ldc = I;
     n = lora_back(d, w, bs, 1, dyb, D, I, M, tp, xb_down, bt, p, slot, part, lf, s, bts_down);
     if (n < 0) return n;
     HIP_TRY(gemm_bf16(p, p.R ? EPI_RESID_FROM_F32 : EPI_STORE, s));
@@ -913,8 +936,9 @@ int block_train_bwd(const gen_block_dims& d, const gen_block_weights& w, const f
   {  // gate/up: du2 = dgate W_gate + dup W_up (+ LoRA)
     const BackSite bs[2] = {{4, 0, I}, {5, I, I}};
     GemmParams p = gp();
-    HIP_TRY(transpose_bf16((const bf16*)w.w_gate_up, D, wt, LG, 2 * I, D, s));
-    p.A = dgu; p.lda = LG; p.B = wt; p.ldb = LG; p.M = M; p.N = D; p.K = 2 * I; p.C = du; p.ldc = D;
+    const bf16* wgt = ft ? (const bf16*)(ft + FT.gu) : wt;
+    if (!ft) HIP_TRY(transpose_bf16((const bf16*)w.w_gate_up, D, wt, LG, 2 * I, D, s));
+    p.A = dgu; p.lda = LG; p.B = wgt; p.ldb = LG; p.M = M; p.N = D; p.K = 2 * I; p.C = du; p.ldc = D;
     n = lora_back(d, w, bs, 2, dgu, LG, D, M, tp, xb_gu, bt, p, slot, part, lf, s, bts_gu);
     if (n < 0) return n;
     HIP_TRY(gemm_bf16(p, p.R ? EPI_RESID_FROM_F32 : EPI_STORE, s));
@@ -927,8 +951,9 @@ int block_train_bwd(const gen_block_dims& d, const gen_block_weights& w, const f
   {  // O projection: dO = dx W_o (+ LoRA)
     const BackSite bs[1] = {{3, 0, D}};
     GemmParams p = gp();
-    HIP_TRY(transpose_bf16((const bf16*)w.w_o, QD, wt, D, D, QD, s));
-    p.A = dyb; p.lda = D; p.B = wt; p.ldb = D; p.M = M; p.N = QD; p.K = D; p.C = dO; p.ldc = QD;
+    const bf16* wot = ft ? (const bf16*)(ft + FT.o) : wt;
+    if (!ft) HIP_TRY(transpose_bf16((const bf16*)w.w_o, QD, wt, D, D, QD, s));
+    p.A = dyb; p.lda = D; p.B = wot; p.ldb = D; p.M = M; p.N = QD; p.K = D; p.C = dO; p.ldc = QD;
     n = lora_back(d, w, bs, 1, dyb, D, QD, M, tp, xb_o, bt, p, slot, part, lf, s, bts_o);
     if (n < 0) return n;
     HIP_TRY(gemm_bf16(p, p.R ? EPI_RESID_FROM_F32 : EPI_STORE, s));
@@ -944,8 +969,9 @@ int block_train_bwd(const gen_block_dims& d, const gen_block_weights& w, const f
   {  // QKV projection: du = dqkv W_qkv (+ LoRA on q, k, v)
     const BackSite bs[3] = {{0, 0, QD}, {1, QD, KVD}, {2, QD + KVD, KVD}};
     GemmParams p = gp();
-    HIP_TRY(transpose_bf16((const bf16*)w.w_qkv, D, wt, QKV, QKV, D, s));
-    p.A = dqkv; p.lda = QKV; p.B = wt; p.ldb = QKV; p.M = M; p.N = D; p.K = QKV; p.C = du; p.ldc = D;
+    const bf16* wqt = ft ? (const bf16*)(ft + FT.qkv) : wt;
+    if (!ft) HIP_TRY(transpose_bf16((const bf16*)w.w_qkv, D, wt, QKV, QKV, D, s));
+    p.A = dqkv; p.lda = QKV; p.B = wqt; p.ldb = QKV; p.M = M; p.N = D; p.K = QKV; p.C = du; p.ldc = D;
     n = lora_back(d, w, bs, 3, dqkv, QKV, D, M, tp, xb_qkv, bt, p, slot, part, lf, s, bts_qkv);
     if (n < 0) return n;
     HIP_TRY(gemm_bf16(p, p.R ? EPI_RESID_FROM_F32 : EPI_STORE, s));
@@ -1386,7 +1412,7 @@ int gen_tower_lora_train_step(const gen_block_dims* dims, int n_layers, const ge
                               const void* w_out, const float* x_t, const float* x0, int n_img, int H, int W,
                               const float* sigma, const void* const* prefix_k, const void* const* prefix_v,
                               const int* prefix_len, const gen_lora_grads* grads, float* loss, float* x0_pred_out,
-                              void* workspace, size_t workspace_bytes, void* stream) {
+                              const void* frozen_t, void* workspace, size_t workspace_bytes, void* stream) {
   int rc = check_train_dims(dims);
   if (rc) return rc;
   if (n_layers < 1) return fail(GEN_EINVAL, "n_layers %d < 1", n_layers);
@@ -1402,6 +1428,7 @@ int gen_tower_lora_train_step(const gen_block_dims* dims, int n_layers, const ge
     if (i < 7 && !aligned16(glob[i])) return fail(GEN_EINVAL, "%s is not 16-byte aligned", gname[i]);
   }
   if (x0_pred_out && !aligned16(x0_pred_out)) return fail(GEN_EINVAL, "x0_pred_out is not 16-byte aligned");
+  if (frozen_t && !aligned16(frozen_t)) return fail(GEN_EINVAL, "frozen_t is not 16-byte aligned");
   if (n_img < 1) return fail(GEN_EINVAL, "n_img %d < 1", n_img);
   if (n_img > MAXB) return fail(GEN_EUNSUPPORTED, "n_img = %d > %d", n_img, MAXB);
   if (H <= 0 || W <= 0 || H % 32 || W % 32) return fail(GEN_EINVAL, "H=%d and W=%d must be positive multiples of 32", H, W);
@@ -1473,9 +1500,41 @@ int gen_tower_lora_train_step(const gen_block_dims* dims, int n_layers, const ge
   for (int l = n_layers - 1; l >= 0; --l) {
     const SeqInfo si = make_seq(B, N, prefix_k + (size_t)l * B, prefix_v + (size_t)l * B, prefix_len);
     void* act = at<char>(workspace, T.acts + (size_t)l * T.act_stride);
+    const char* ft = frozen_t ? (const char*)frozen_t + (size_t)l * frozen_t_layout(*dims).stride : nullptr;
     rc = block_train_bwd(*dims, layers[l], saved + (size_t)l * M * D, dh, si, grads ? grads[l] : none, act, bws, L, s,
-                         true);
+                         true, ft);
     if (rc) return rc;
+  }
+  return ok();
+}
+
+size_t gen_train_frozen_t_size(const gen_block_dims* dims, int n_layers) {
+  if (check_train_dims(dims) || n_layers < 1) return 0;
+  return (size_t)n_layers * frozen_t_layout(*dims).stride;
+}
+
+int gen_train_frozen_t(const gen_block_dims* dims, int n_layers, const gen_block_weights* layers, void* frozen_t,
+                       size_t bytes, void* stream) {
+  int rc = check_train_dims(dims);
+  if (rc) return rc;
+  if (n_layers < 1) return fail(GEN_EINVAL, "n_layers %d < 1", n_layers);
+  if (!layers) return fail(GEN_EINVAL, "layers is NULL");
+  for (int l = 0; l < n_layers; ++l)
+    if ((rc = check_weights(dims, &layers[l], l))) return rc;
+  if (!frozen_t || !aligned16(frozen_t)) return fail(GEN_EINVAL, "frozen_t is NULL or not 16-byte aligned");
+  const FrozenT F = frozen_t_layout(*dims);
+  if (bytes < (size_t)n_layers * F.stride)
+    return fail(GEN_EWORKSPACE, "frozen_t %zu bytes < %zu required", bytes, (size_t)n_layers * F.stride);
+  hipStream_t s = (hipStream_t)stream;
+  const int D = dims->hidden, I = dims->mlp_intermediate, QD = dims->n_q_heads * dims->head_dim;
+  const int QKV = QD + 2 * dims->n_kv_heads * dims->head_dim, LG = train_pitch(2 * I);
+  for (int l = 0; l < n_layers; ++l) {
+    const gen_block_weights& w = layers[l];
+    char* ft = (char*)frozen_t + (size_t)l * F.stride;
+    HIP_TRY(transpose_bf16((const bf16*)w.w_down, ld_down_of(*dims, w), (bf16*)(ft + F.down), D, D, I, s));
+    HIP_TRY(transpose_bf16((const bf16*)w.w_gate_up, D, (bf16*)(ft + F.gu), LG, 2 * I, D, s));
+    HIP_TRY(transpose_bf16((const bf16*)w.w_o, QD, (bf16*)(ft + F.o), D, D, QD, s));
+    HIP_TRY(transpose_bf16((const bf16*)w.w_qkv, D, (bf16*)(ft + F.qkv), QKV, QKV, D, s));
   }
   return ok();
 }

@@ -215,3 +215,26 @@ def test_training_entry_points_reject_bad_arguments_on_host(psf):
     assert call(dd=dm, gg=None) == psf.GEN_EUNSUPPORTED                      # dense blocks only
     assert psf.lib.gen_backward_workspace_size(ctypes.byref(d), 2, 64, 0) > 0
     assert psf.lib.gen_train_workspace_size(ctypes.byref(d), 0, 1, 64, 0) == 0
+
+
+def test_frozen_transposes_entry_points_reject_bad_arguments_on_host(psf):
+    d = dims(psf)                     # 8B-shaped dense bf16 block: w_down^T, w_gate_up^T (rows padded), w_o^T, w_qkv^T
+    w = fake_weights(psf)
+    lw = (psf.BlockWeightsC * 2)(w, w)
+    per_layer = psf.lib.gen_train_frozen_t_size(ctypes.byref(d), 1)
+    assert per_layer >= 2 * (12288 * 4096 + 4096 * 24640 + 4096 * 4096 + 4096 * 6144)
+    assert psf.lib.gen_train_frozen_t_size(ctypes.byref(d), 2) == 2 * per_layer
+    assert psf.lib.gen_train_frozen_t_size(ctypes.byref(d), 0) == 0
+    d64 = dims(psf)
+    d64.head_dim = 64
+    assert psf.lib.gen_train_frozen_t_size(ctypes.byref(d64), 1) == 0      # the training step's dims rules
+    f = psf.lib.gen_train_frozen_t
+
+    def call(n_layers=2, layers=lw, buf=4096, nbytes=1 << 40):
+        return f(ctypes.byref(d), n_layers, layers, buf, nbytes, None)
+    assert call(n_layers=0) == psf.GEN_EINVAL
+    assert call(layers=None) == psf.GEN_EINVAL
+    assert call(layers=(psf.BlockWeightsC * 2)(w, psf.BlockWeightsC())) == psf.GEN_EINVAL
+    assert call(buf=None) == psf.GEN_EINVAL
+    assert call(buf=4100) == psf.GEN_EINVAL                                   # unaligned
+    assert call(nbytes=2 * per_layer - 1) == psf.GEN_EWORKSPACE

@@ -187,3 +187,48 @@ def test_tower_train_step(lib):
     assert abs(loss.item() - rloss) <= 1e-3 * rloss
     for l in range(2):
         check_grads(grads[l][0], rgrads[l], f"layer {l}")
+
+
+@pytest.mark.parametrize("hidden,inter", [(256, 512), (2048, 4096)])
+def test_tower_train_step_frozen_t(lib, hidden, inter):
+    """The frozen weights' transposes made once (gen_train_frozen_t) give the same loss and LoRA
+    gradients, bit for bit, as the step that transposes them itself; at hidden 2048 / intermediate
+    4096 the z and gate/up-gradient rows are padded (multiples of 8 KiB otherwise)."""
+    import torch
+    d = W.small_dims(hidden=hidden, n_q_heads=hidden // 128, n_kv_heads=max(1, hidden // 512), head_dim=128,
+                     mlp_intermediate=inter, lora_rank=32, lora_alpha=32.0)
+    w = W.scaled(W.CONFIGS[3], dims=d, height=256, width=256, prefix_len=32, n_layers=2, n_img=2,
+                 prefix_cache_samples=0)
+    log(f"frozen transposes: hidden {hidden}, intermediate {inter}")
+    glob = W.tower_globals(w, 0, "bf16")
+    lw = [strong_lora(W.layer_weights(w, l, 0, "bf16")) for l in range(2)]
+    pk = [[W.prefix_kv(w, l, s, 0, "bf16")[0] for s in range(2)] for l in range(2)]
+    pv = [[W.prefix_kv(w, l, s, 0, "bf16")[1] for s in range(2)] for l in range(2)]
+    t = W.train_timesteps(w)
+    x0 = W.clean_image(w)
+    x = O.noisy_sample(x0, W.noise_image(w), t).astype(np.float32)
+    sig = [float(v) for v in t]
+    dims = lib.make_dims(d, lib.GEN_BF16)
+    gd = weights_to_dev(glob, "bf16")
+    lwd = [weights_to_dev(x_, "bf16") for x_ in lw]
+    layers = [lib.make_weights(x_) for x_ in lwd]
+    pkd = [dev(p, "bf16") for layer in pk for p in layer]
+    pvd = [dev(p, "bf16") for layer in pv for p in layer]
+    ws = lib.alloc_workspace(lib.train_workspace_size(dims, 2, 2, w.n_tokens, 32))
+    ft = lib.alloc_workspace(lib.train_frozen_t_size(dims, 2))
+    lib.train_frozen_t(dims, layers, ft)
+    xt, x0d = torch.from_numpy(x).cuda(), torch.from_numpy(x0).cuda()
+    runs = []
+    for frozen in (None, ft):
+        grads = [grad_buffers(lib, x_) for x_ in lw]
+        loss = torch.zeros(1, device="cuda")
+        lib.tower_lora_train_step(dims, layers, gd, xt, x0d, sig, pkd, pvd, [32, 32], [g[1] for g in grads], loss, ws,
+                                  frozen_t=frozen)
+        torch.cuda.synchronize()
+        runs.append((loss.clone(), [{k: v.clone() for k, v in g[0].items()} for g in grads]))
+    (l0, g0), (l1, g1) = runs
+    log(f"  loss {l0.item():.6f} / {l1.item():.6f}")
+    assert torch.equal(l0, l1)
+    for l in range(2):
+        for k in g0[l]:
+            assert torch.equal(g0[l][k], g1[l][k]), (l, k)
