@@ -170,57 +170,6 @@ __global__ __launch_bounds__(256) void pack_k_kernel(const T* __restrict__ qkv, 
   *(u32x4*)(Kc + (((int64_t)b * Hkv + g) * Lpad + j) * d + c * V::N) = v;
 }
 
-// Kc as pack_k_kernel, with each image key RMS-normalised (gain gk) and rotated (RoPE at its
-// packed index j).  One head vector per L = d / 8 lanes (16-byte chunks), as in
-// qknorm_rope_kernel; every lane runs the arithmetic and the row kind picks the stored value.
-template <int D>
-__global__ __launch_bounds__(256) void pack_k_knorm_kernel(const bf16* __restrict__ qkv, int64_t ld, SeqInfo si,
-                                                           int Hq, int Hkv, int Lpad, const bf16* __restrict__ gk,
-                                                           const float2* __restrict__ table, float eps,
-                                                           bf16* __restrict__ Kc, int64_t total) {
-  using V = V16<bf16>;
-  constexpr int L = D / V::N;
-  constexpr int HPW = 64 / L;
-  const int lane = threadIdx.x & 63;
-  const int64_t hv = ((int64_t)blockIdx.x * 4 + (threadIdx.x >> 6)) * HPW + lane / L;
-  const int sub = lane % L;
-  const bool active = hv < total;
-  const int64_t hvc = active ? hv : 0;
-  const int j = (int)(hvc % Lpad);
-  const int64_t bg = hvc / Lpad;
-  const int g = (int)(bg % Hkv), b = (int)(bg / Hkv);
-  const int P = si.plen[b];
-  const int kind = j < P ? 0 : (j < P + si.N ? 1 : 2);     // prefix, image, padding
-  u32x4 raw = {0, 0, 0, 0};
-  if (kind == 0) raw = *(const u32x4*)((const bf16*)si.pk[b] + ((int64_t)j * Hkv + g) * D + sub * V::N);
-  else if (kind == 1) raw = *(const u32x4*)(qkv + ((int64_t)b * si.N + j - P) * ld + (int64_t)(Hq + g) * D + sub * V::N);
-  float x[V::N], gg[V::N];
-  V::unpack(raw, x);
-  V::unpack(*(const u32x4*)(gk + sub * V::N), gg);
-  float ss = 0.f;
-#pragma unroll
-  for (int e = 0; e < V::N; ++e) ss += x[e] * x[e];
-#pragma unroll
-  for (int o = L / 2; o > 0; o >>= 1) ss += __shfl_xor(ss, o, 64);
-  const float r = 1.0f / sqrtf(ss / (float)D + eps);
-#pragma unroll
-  for (int e = 0; e < V::N; ++e) x[e] = x[e] * r * gg[e];
-  float pr[V::N];
-#pragma unroll
-  for (int e = 0; e < V::N; ++e) pr[e] = __shfl_xor(x[e], L / 2, 64);
-  const bool first = sub < L / 2;
-  const int j0 = (sub % (L / 2)) * V::N;
-  const float2* tb = table + (int64_t)(kind == 1 ? j : 0) * (D / 2) + j0;
-  float out[V::N];
-#pragma unroll
-  for (int e = 0; e < V::N; ++e) {
-    const float2 cs = tb[e];
-    out[e] = first ? (x[e] * cs.x - pr[e] * cs.y) : (x[e] * cs.x + pr[e] * cs.y);
-  }
-  if (!active) return;
-  *(u32x4*)(Kc + (((int64_t)b * Hkv + g) * Lpad + j) * D + sub * V::N) = kind == 1 ? V::pack(out) : raw;
-}
-
 // Vt[b][g][dd][j0..j0+8): each lane gathers 8 keys of one head-dim column; a wave's loads
 // of one key row are 64 consecutive elements.
 template <typename T>
@@ -260,6 +209,78 @@ __global__ __launch_bounds__(256) void pack_vt_tile_kernel(const bf16* __restric
   __shared__ __attribute__((aligned(16))) bf16 tile[64 * RS];
   const int b = blockIdx.z, g = blockIdx.y, j0 = blockIdx.x * 64;
   const int P = si.plen[b], N = si.N;
+  for (int i = threadIdx.x; i < 64 * CPR; i += 256) {
+    const int r = i / CPR, c = i - r * CPR;
+    const int j = j0 + r;
+    u32x4 v = {0, 0, 0, 0};
+    if (j < P) v = *(const u32x4*)((const bf16*)si.pv[b] + ((int64_t)j * Hkv + g) * D + c * 8);
+    else if (j < P + N) v = *(const u32x4*)(qkv + ((int64_t)b * N + j - P) * ld + (int64_t)(Hq + Hkv + g) * D + c * 8);
+    *(u32x4*)(tile + r * RS + c * 8) = v;
+  }
+  __syncthreads();
+  for (int i = threadIdx.x; i < D * 8; i += 256) {
+    const int dd = i >> 3, kc = i & 7;
+    bf16x8 e;
+#pragma unroll
+    for (int q = 0; q < 8; ++q) {
+      const int pos = kc * 8 + q;
+      const int j = (pos & ~15) | (((pos >> 2) & 1) << 3) | (((pos >> 3) & 1) << 2) | (pos & 3);
+      e[q] = tile[j * RS + dd];
+    }
+    *(bf16x8*)(Vt + (((int64_t)b * Hkv + g) * D + dd) * Lpad + j0 + kc * 8) = e;
+  }
+}
+
+// K and V^T of one (sequence, kv head, 64-key tile) in one workgroup.  K as pack_k_kernel, with each
+// image key RMS-normalised (gain gk) and rotated (RoPE at its packed index j): one key row per L =
+// d / 8 lanes (16-byte chunks), as in qknorm_rope_kernel, every lane running the arithmetic and the
+// row kind picking the stored value; then V^T as pack_vt_tile_kernel.
+template <int D>
+__global__ __launch_bounds__(256) void pack_kv_knorm_tile_kernel(const bf16* __restrict__ qkv, int64_t ld, SeqInfo si,
+                                                                 int Hq, int Hkv, int Lpad, const bf16* __restrict__ gk,
+                                                                 const float2* __restrict__ table, float eps,
+                                                                 bf16* __restrict__ Kc, bf16* __restrict__ Vt) {
+  using V = V16<bf16>;
+  constexpr int L = D / V::N;               // lanes per key row
+  constexpr int RPP = 256 / L;              // key rows per pass
+  constexpr int CPR = D / 8;
+  constexpr int RS = D + 8;
+  __shared__ __attribute__((aligned(16))) bf16 tile[64 * RS];
+  const int b = blockIdx.z, g = blockIdx.y, j0 = blockIdx.x * 64;
+  const int P = si.plen[b], N = si.N;
+  const int lane = threadIdx.x & 63, sub = lane % L;
+  float gg[V::N];
+  V::unpack(*(const u32x4*)(gk + sub * V::N), gg);
+  for (int r0 = 0; r0 < 64; r0 += RPP) {
+    const int j = j0 + r0 + threadIdx.x / L;
+    const int kind = j < P ? 0 : (j < P + N ? 1 : 2);      // prefix, image, padding
+    u32x4 raw = {0, 0, 0, 0};
+    if (kind == 0) raw = *(const u32x4*)((const bf16*)si.pk[b] + ((int64_t)j * Hkv + g) * D + sub * V::N);
+    else if (kind == 1) raw = *(const u32x4*)(qkv + ((int64_t)b * N + j - P) * ld + (int64_t)(Hq + g) * D + sub * V::N);
+    float x[V::N];
+    V::unpack(raw, x);
+    float ss = 0.f;
+#pragma unroll
+    for (int e = 0; e < V::N; ++e) ss += x[e] * x[e];
+#pragma unroll
+    for (int o = L / 2; o > 0; o >>= 1) ss += __shfl_xor(ss, o, 64);
+    const float r = 1.0f / sqrtf(ss / (float)D + eps);
+#pragma unroll
+    for (int e = 0; e < V::N; ++e) x[e] = x[e] * r * gg[e];
+    float pr[V::N];
+#pragma unroll
+    for (int e = 0; e < V::N; ++e) pr[e] = __shfl_xor(x[e], L / 2, 64);
+    const bool first = sub < L / 2;
+    const int jj = (sub % (L / 2)) * V::N;
+    const float2* tb = table + (int64_t)(kind == 1 ? j : 0) * (D / 2) + jj;
+    float out[V::N];
+#pragma unroll
+    for (int e = 0; e < V::N; ++e) {
+      const float2 cs = tb[e];
+      out[e] = first ? (x[e] * cs.x - pr[e] * cs.y) : (x[e] * cs.x + pr[e] * cs.y);
+    }
+    *(u32x4*)(Kc + (((int64_t)b * Hkv + g) * Lpad + j) * D + sub * V::N) = kind == 1 ? V::pack(out) : raw;
+  }
   for (int i = threadIdx.x; i < 64 * CPR; i += 256) {
     const int r = i / CPR, c = i - r * CPR;
     const int j = j0 + r;
@@ -521,20 +542,15 @@ hipError_t pack_kv(const T* qkv, int64_t ld, const SeqInfo& si, int Hq, int Hkv,
 }
 hipError_t pack_kv_knorm(const bf16* qkv, int64_t ld, const SeqInfo& si, int Hq, int Hkv, int d, int Lpad,
                          const bf16* gk, const float2* table, float eps, bf16* Kc, bf16* Vt, hipStream_t s) {
-  const int64_t total = (int64_t)si.B * Hkv * Lpad;
-  if (total == 0) return hipSuccess;
-  const int L = d / V16<bf16>::N;
-  const int64_t per_block = 4 * (64 / L);
-  const dim3 grid((unsigned)((total + per_block - 1) / per_block));
+  if ((int64_t)si.B * Hkv * Lpad == 0) return hipSuccess;
+  const dim3 g2(Lpad / 64, Hkv, si.B);
   if (d == 128)
-    hipLaunchKernelGGL((pack_k_knorm_kernel<128>), grid, dim3(256), 0, s, qkv, ld, si, Hq, Hkv, Lpad, gk, table, eps, Kc, total);
+    hipLaunchKernelGGL((pack_kv_knorm_tile_kernel<128>), g2, dim3(256), 0, s, qkv, ld, si, Hq, Hkv, Lpad, gk, table, eps, Kc, Vt);
   else if (d == 64)
-    hipLaunchKernelGGL((pack_k_knorm_kernel<64>), grid, dim3(256), 0, s, qkv, ld, si, Hq, Hkv, Lpad, gk, table, eps, Kc, total);
+    hipLaunchKernelGGL((pack_kv_knorm_tile_kernel<64>), g2, dim3(256), 0, s, qkv, ld, si, Hq, Hkv, Lpad, gk, table, eps, Kc, Vt);
   else
     return hipErrorInvalidValue;
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  return pack_vt_bf16(qkv, ld, si, Hq, Hkv, d, Lpad, Vt, s);
+  return hipGetLastError();
 }
 template <typename T>
 hipError_t lora_merge(const T* W, const T* A, const T* B, T* Wo, int out, int in, int64_t ldw, int rank, float scale,
@@ -590,3 +606,4 @@ hipError_t cfg_euler(float* xo, const float* x, const float* xc, const float* xm
 }
 
 }  // namespace psf
+
