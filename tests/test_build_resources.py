@@ -33,5 +33,5 @@ def test_no_kernel_spills_to_scratch():
 
 def test_hot_kernels_are_in_the_table():
     names = " ".join(n for n, _ in table_rows())
-    for k in ("attn_v2_kernel", "gemm_k32_kernel", "gemm_fast_kernel", "pack_k_knorm_kernel", "route_kernel"):
+    for k in ("attn_v2_kernel", "gemm_k32_kernel", "gemm_fast_kernel", "pack_kv_knorm_tile_kernel", "route_kernel"):
         assert k in names, k
